@@ -1,0 +1,165 @@
+"""Dense attention and the compensated block-sparse rule, fp64.
+
+The rule follows PISA ("PISA: Piecewise Sparse Attention Is Wiser for
+Efficient Diffusion Transformers", section 2, "Algorithme Central"): for a
+query t of query block a,
+
+    o_t = N_t / D_t
+    D_t = sum_{j in E} sum_n e^{s q.k_n}                      exact blocks
+        + sum_{j in M} sum_n e^{s l~_tn}                      skim blocks
+        + [c >= 0] sum_{j in U} n_j e^{s q.k_bar_j}           zeroth order
+    N_t = sum_{j in E} sum_n e^{s q.k_n} v_n
+        + sum_{j in M} sum_n p~_tn v~_n 2^{e_v(j)}
+        + [c >= 0] sum_{j in U} n_j e^{s q.k_bar_j} v_bar_j
+        + [c == 1] sum_{j in U} e^{s q.k_bar_j} s (q^T H_j)
+
+with s the softmax scale, E the exactly computed key blocks, M the fp8 skim
+blocks (Triage's low-precision tier), U every other block, n_j the block's
+valid key count, k_bar_j / v_bar_j its exact means and H_j = sum_n
+(k_n - k_bar_j) v_n^T.  The zeroth-order term is PISA's alpha_{t,j} times the
+block's value sum (alpha_{t,j} = exp(q_t k_bar_j^T)), which equals SVG-EAR's
+centroid replacement ("SVG-EAR ...", section 2A) of all n_j keys and values
+by their means.  The first-order term is PISA's with the per-block matrix
+H_j in place of the global mean H_bar; its denominator share is zero because
+sum_n (k_n - k_bar_j) = 0 for the exact mean.  Every approximation sits
+inside the one normalisation D_t, as PISA's "Coherence de Normalisation"
+asks.
+
+Skim tile (a, j) emulation (the fp8 reading of Triage's fast tier):
+q~, k~, v~ are the per-block scaled e4m3 copies with exponents e_q(a),
+e_k(j), e_v(j); l~_tn = (q~_t . k~_n) 2^{e_q(a) + e_k(j)}; with
+L_tn = s l~_tn log2(e) and c_t = ceil(max_n L_tn) for the tile,
+p~_tn = 2^{c_t - 8} e4m3(2^{8 + L_tn - c_t}).  The denominator takes the
+unquantised weights.
+"""
+
+import math
+
+import numpy as np
+
+from . import e4m3
+
+BLK = 64
+LOG2E = 1.0 / math.log(2.0)
+
+
+def dense_attention(q, k, v, N: int, scale: float):
+    """softmax(scale * q k^T) v over the N valid tokens, fp64.
+
+    Returns (O [B,H,N_pad,d], lse [B,H,N_pad]); pad rows are 0.
+    """
+    B, H, Np, d = q.shape
+    O = np.zeros((B, H, Np, d))
+    lse = np.zeros((B, H, Np))
+    for b in range(B):
+        for h in range(H):
+            Q = np.asarray(q[b, h, :N], np.float64)
+            K = np.asarray(k[b, h, :N], np.float64)
+            V = np.asarray(v[b, h, :N], np.float64)
+            S = scale * (Q @ K.T)
+            m = S.max(axis=1, keepdims=True)
+            P = np.exp(S - m)
+            D = P.sum(axis=1, keepdims=True)
+            O[b, h, :N] = (P @ V) / D
+            lse[b, h, :N] = (m + np.log(D))[:, 0]
+    return O, lse
+
+
+def _tokens(blocks, N: int, blk: int) -> np.ndarray:
+    blocks = np.asarray(blocks, np.int64)
+    t = (blocks[:, None] * blk + np.arange(blk)[None, :]).ravel()
+    return t[t < N]
+
+
+def skim_weights(L: np.ndarray) -> np.ndarray:
+    """Quantised weights p~ for one skim tile, given L = s * l~ * log2(e).
+
+    L: [rows, keys] (one key block).  Returns p~ in absolute units (as the
+    weights 2^L they stand for), each row scaled by its own power-of-two
+    reference c_t = ceil(max L_t).
+    """
+    c = np.ceil(L.max(axis=1, keepdims=True))
+    return np.exp2(c - 8.0) * e4m3.round_to_e4m3(np.exp2(8.0 + L - c))
+
+
+def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
+               exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK):
+    """Compensated rule for the valid rows Qa [r, d] of query block a, one head.
+
+    k, v: [N_pad, d]; kbar, vbar: exact fp64 means [nb, d]; kcount [nb];
+    exact / skim: key block index lists; kmom [nb, d, d] for comp == 1;
+    fp8: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp, vexp [nb]) for skim.
+    Returns (o [r, d], lse [r]).
+    """
+    Qa = np.asarray(Qa, np.float64)
+    nb = kbar.shape[0]
+    exact = np.asarray(sorted(exact), np.int64)
+    skim = np.asarray(sorted(skim), np.int64)
+    U = np.setdiff1d(np.arange(nb), np.concatenate([exact, skim]))
+
+    # ordinary softmax terms: exact keys, then centroid pseudo-keys
+    te = _tokens(exact, N, blk)
+    logits = [scale * (Qa @ np.asarray(k[te], np.float64).T)]
+    values = [np.asarray(v[te], np.float64)]
+    if comp >= 0 and U.size:
+        cl = scale * (Qa @ kbar[U].T) + np.log(kcount[U].astype(np.float64))[None, :]
+        logits.append(cl)
+        values.append(vbar[U])
+
+    skim_terms = []
+    if skim.size:
+        qa = e4m3.decode(fp8["q8"][a * blk:a * blk + Qa.shape[0]])
+        for j in skim:
+            tj = _tokens([j], N, blk)
+            l = (qa @ e4m3.decode(fp8["k8"][tj]).T) * 2.0 ** (int(fp8["qexp"][a]) + int(fp8["kexp"][j]))
+            vt = e4m3.decode(fp8["v8"][tj]) * 2.0 ** int(fp8["vexp"][j])
+            skim_terms.append((scale * l, vt))
+
+    m = np.max(np.concatenate([x for x in logits] + [t[0] for t in skim_terms], axis=1), axis=1)
+    D = np.zeros(Qa.shape[0])
+    Nt = np.zeros_like(Qa)
+    for lg, val in zip(logits, values):
+        P = np.exp(lg - m[:, None])
+        D += P.sum(axis=1)
+        Nt += P @ val
+    for lg, vt in skim_terms:
+        D += np.exp(lg - m[:, None]).sum(axis=1)
+        L = lg * LOG2E
+        pq = skim_weights(L) * np.exp2(-m * LOG2E)[:, None]
+        Nt += pq @ vt
+    if comp == 1 and U.size:
+        alpha = np.exp(scale * (Qa @ kbar[U].T) - m[:, None])        # [r, |U|]
+        QH = np.matmul(Qa[None], kmom[U])                             # [|U|, r, d]: q^T H_j
+        Nt += scale * np.einsum("ru,uro->ro", alpha, QH)
+    return Nt / D[:, None], m + np.log(D)
+
+
+def sparse_attention(q, k, v, N: int, scale: float, comp: int, pooled: dict,
+                     exact_idx, exact_cnt, skim_idx=None, skim_cnt=None, blk: int = BLK):
+    """The rule on every query block of every (b, h); fp64 (O, lse), pad rows 0.
+
+    `pooled` is oracle.pooling.pool(...) output (kbar64, vbar64, kcount and,
+    when needed, kmom and the fp8 copies).
+    """
+    B, H, Np, d = q.shape
+    nb = Np // blk
+    O = np.zeros((B, H, Np, d))
+    lse = np.zeros((B, H, Np))
+    for b in range(B):
+        for h in range(H):
+            fp8 = None
+            if skim_idx is not None:
+                fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
+            kmom = pooled["kmom"][b, h] if comp == 1 else None
+            for a in range(nb):
+                r0, r1 = a * blk, min(N, (a + 1) * blk)
+                if r1 <= r0:
+                    continue
+                ex = exact_idx[b, h, a, :exact_cnt[b, h, a]]
+                sk = () if skim_idx is None else skim_idx[b, h, a, :skim_cnt[b, h, a]]
+                o, l = rule_block(q[b, h, r0:r1], k[b, h], v[b, h], N, scale, comp,
+                                  pooled["kbar64"][b, h], pooled["vbar64"][b, h], pooled["kcount"],
+                                  ex, sk, kmom, fp8, a, blk)
+                O[b, h, r0:r1] = o
+                lse[b, h, r0:r1] = l
+    return O, lse

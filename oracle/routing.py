@@ -1,0 +1,146 @@
+"""Block routing: which key blocks each query block computes exactly.
+
+All selections are returned as ascending index lists padded with -1 plus a
+count per query block.  Orderings are total: ties on the score go to the lower
+block index.
+"""
+
+import numpy as np
+
+
+def block_scores(qbar: np.ndarray, kbar: np.ndarray) -> np.ndarray:
+    """s(a, j) = sum_i qbar[a, i] * kbar[j, i] in fp64, accumulated in i order.
+
+    qbar, kbar: fp32 [..., nq, d] and [..., nk, d].  Each fp32 x fp32 product
+    is exact in fp64, so a fused or an unfused multiply-add gives the same
+    bits; the sum runs over i = 0 .. d-1 in order from +0.0.
+    Pages: pooled block scores drive PISA's top-k selection (section 2,
+    "Routage Sensible a la Covariance") and SVG-EAR's critique of score
+    routing (section 1).
+    """
+    q = np.asarray(qbar, np.float32).astype(np.float64)
+    k = np.asarray(kbar, np.float32).astype(np.float64)
+    acc = np.zeros(q.shape[:-1] + (k.shape[-2],), np.float64)
+    for i in range(q.shape[-1]):
+        acc = acc + q[..., :, None, i] * k[..., None, :, i]
+    return acc
+
+
+def _select_first(keys: np.ndarray, count: int) -> np.ndarray:
+    """Indices of the first `count` entries in the order (-key, index), ascending."""
+    order = np.lexsort((np.arange(keys.shape[0]), -keys))
+    return np.sort(order[:count])
+
+
+def _pack(lists, cap: int):
+    idx = np.full((len(lists), cap), -1, np.int32)
+    cnt = np.zeros(len(lists), np.int32)
+    for a, sel in enumerate(lists):
+        idx[a, :len(sel)] = sel
+        cnt[a] = len(sel)
+    return idx, cnt
+
+
+def route_topk(qbar: np.ndarray, kbar: np.ndarray, k: int):
+    """Top-k key blocks per query block on pooled scores.
+
+    qbar, kbar fp32 [B,H,nb,d] -> (idx int32 [B,H,nb,k], cnt int32 [B,H,nb]).
+    PISA selects the critical set S_i per query block by top-k on block
+    scores (section 2, "Algorithme Central" / "Routage Sensible a la
+    Covariance"); ties go to the lower index.
+    """
+    B, H, nq, _ = qbar.shape
+    nk = kbar.shape[2]
+    kk = min(k, nk)
+    idx = np.full((B, H, nq, kk), -1, np.int32)
+    cnt = np.full((B, H, nq), kk, np.int32)
+    for b in range(B):
+        for h in range(H):
+            s = block_scores(qbar[b, h], kbar[b, h])
+            for a in range(nq):
+                idx[b, h, a] = _select_first(s[a], kk)
+    return idx, cnt
+
+
+def lvsa_anchor_set(nb: int, anchors: int, phase: int, step: int) -> np.ndarray:
+    """Rotating global anchor key blocks G_s at denoising step s.
+
+    LVSA ("LVSA: Training-Free Sparse Attention for Long Video Diffusion",
+    section 2, "Mecanisme Central"): the global set shifts by s mod T_per at
+    each step, so over T_per steps every position is an anchor exactly once.
+    Here the grid is `anchors` key blocks at stride P = nb // anchors with
+    offset (phase + s) mod P.  No anchors when `anchors` is 0; `anchors`
+    may not exceed nb.
+    """
+    if anchors == 0:
+        return np.zeros(0, np.int64)
+    assert anchors <= nb
+    P = nb // anchors
+    off = (phase + step) % P
+    return off + P * np.arange(anchors)
+
+
+def route_lvsa(frame_lo: np.ndarray, frame_hi: np.ndarray, window: int,
+               anchors: int, phase: int, step: int):
+    """LVSA block mask A(t) = G_s  U  W(t) on 64-token blocks.
+
+    Query block a attends to key block j when their latent-frame ranges come
+    within `window` frames of each other ([lo_j, hi_j] meets
+    [lo_a - w, hi_a + w]), or when j is one of the step's anchors.  Page:
+    LVSA section 2, "Mecanisme Central" (A(t) = G U W(t)).
+    Returns (idx int32 [nb, cap], cnt int32 [nb]) with cap = the row maximum.
+    """
+    lo = np.asarray(frame_lo, np.int64)
+    hi = np.asarray(frame_hi, np.int64)
+    nb = lo.shape[0]
+    anc = np.zeros(nb, bool)
+    anc[lvsa_anchor_set(nb, anchors, phase, step)] = True
+    lists = []
+    for a in range(nb):
+        near = (lo <= hi[a] + window) & (hi >= lo[a] - window)
+        lists.append(np.nonzero(near | anc)[0])
+    cap = max(len(x) for x in lists)
+    return _pack(lists, cap)
+
+
+def route_triage(qbar: np.ndarray, kbar: np.ndarray, klam: np.ndarray, kcount: np.ndarray,
+                 scale: float, n_keep: int, n_refine: int):
+    """Triage tiers per (query block, key block) tile: refine / skim / skip.
+
+    Page: "Triage: Skip, Skim, or Refine Attention Tiles in Video Diffusion
+    Transformers" ("Un routage fonde sur l'erreur estimee"): from block
+    statistics the router estimates each tile's weight and the error of
+    omitting it, and spends more compute where the estimated error drop
+    justifies it.  Reading used here, in log space with fp64 keys:
+      e_skip(a, j) = fl(fl(scale * s(a, j)) + lambda_j)   omission error
+      w(a, j)      = fl(fl(scale * s(a, j)) + ln n_j)     tile weight
+    The first n_keep blocks in the order (-e_skip, j) are not skipped; of
+    those, the first n_refine in the order (-w, j) are refined (exact bf16)
+    and the rest skimmed (fp8).  Everything else is skipped and compensated.
+    Returns (ref_idx, ref_cnt, skim_idx, skim_cnt) with caps n_refine and
+    n_keep - n_refine.
+    """
+    B, H, nq, _ = qbar.shape
+    nk = kbar.shape[2]
+    n_keep = min(n_keep, nk)
+    n_refine = min(n_refine, n_keep)
+    sc = np.float64(np.float32(scale))
+    logn = np.log(np.asarray(kcount, np.float64))
+    ref_idx = np.full((B, H, nq, n_refine), -1, np.int32)
+    skim_idx = np.full((B, H, nq, n_keep - n_refine), -1, np.int32)
+    for b in range(B):
+        for h in range(H):
+            s = block_scores(qbar[b, h], kbar[b, h])
+            ss = sc * s
+            eskip = ss + np.asarray(klam[b, h], np.float32).astype(np.float64)[None, :]
+            w = ss + logn[None, :]
+            for a in range(nq):
+                keep = _select_first(eskip[a], n_keep)
+                ref = keep[_select_first(w[a, keep], n_refine)]
+                ref = np.sort(ref)
+                skim = np.setdiff1d(keep, ref)
+                ref_idx[b, h, a] = ref
+                skim_idx[b, h, a] = skim
+    ref_cnt = np.full((B, H, nq), n_refine, np.int32)
+    skim_cnt = np.full((B, H, nq), n_keep - n_refine, np.int32)
+    return ref_idx, ref_cnt, skim_idx, skim_cnt

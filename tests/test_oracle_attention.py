@@ -1,0 +1,264 @@
+"""Pins for the attention oracle: library SDPA, reductions to dense attention,
+invariants of softmax weights, Taylor convergence orders, an independent
+per-token form of the first-order term, exact fp8 skim cases, brute force."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, pooling, routing, e4m3
+
+
+def rand_qkv(seed, H=2, N=150, d=8, scale=0.6):
+    rng = np.random.default_rng(seed)
+    Np = 64 * ((N + 63) // 64)
+    out = []
+    for _ in range(3):
+        x = np.zeros((1, H, Np, d))
+        x[:, :, :N] = rng.standard_normal((1, H, N, d)) * scale
+        out.append(x)
+    return out
+
+
+def random_lists(rng, B, H, nb, k):
+    idx = np.zeros((B, H, nb, k), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for a in range(nb):
+                idx[b, h, a] = np.sort(rng.choice(nb, k, replace=False))
+    return idx, np.full((B, H, nb), k, np.int32)
+
+
+def test_dense_matches_torch_sdpa():
+    q, k, v = rand_qkv(0, N=150)
+    O, lse = attention.dense_attention(q, k, v, 150, 0.7)
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q[:, :, :150]), torch.from_numpy(k[:, :, :150]),
+        torch.from_numpy(v[:, :, :150]), scale=0.7)
+    np.testing.assert_allclose(O[:, :, :150], ref.numpy(), atol=1e-12)
+    S = 0.7 * np.einsum("bhti,bhni->bhtn", q[:, :, :150], k[:, :, :150])
+    np.testing.assert_allclose(lse[:, :, :150], np.log(np.exp(S).sum(-1)), atol=1e-12)
+    assert np.all(O[:, :, 150:] == 0)
+
+
+@pytest.mark.parametrize("comp", [-1, 0, 1])
+def test_all_blocks_exact_is_dense(comp):
+    q, k, v = rand_qkv(1, N=170)
+    nb = 3
+    idx = np.tile(np.arange(nb, dtype=np.int32), (1, 2, nb, 1))
+    cnt = np.full((1, 2, nb), nb, np.int32)
+    pooled = pooling.pool(q, k, v, 170, moments=True)
+    O, lse = attention.sparse_attention(q, k, v, 170, 1.0, comp, pooled, idx, cnt)
+    Od, lsed = attention.dense_attention(q, k, v, 170, 1.0)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+@pytest.mark.parametrize("comp", [0, 1])
+def test_block_size_one_is_dense_for_any_selection(comp):
+    # with one token per block the centroid is the token itself
+    q, k, v = rand_qkv(2, N=40, d=5)
+    q, k, v = (x[:, :, :40] for x in (q, k, v))
+    rng = np.random.default_rng(2)
+    idx, cnt = random_lists(rng, 1, 2, 40, 7)
+    pooled = pooling.pool(q, k, v, 40, blk=1, moments=True)
+    O, lse = attention.sparse_attention(q, k, v, 40, 0.9, comp, pooled, idx, cnt, blk=1)
+    Od, lsed = attention.dense_attention(q, k, v, 40, 0.9)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+@pytest.mark.parametrize("comp", [-1, 0, 1])
+def test_constant_values_give_constant_output(comp):
+    q, k, v = rand_qkv(3, N=200)
+    v[:, :, :200] = np.linspace(-1, 1, 8)[None, None, None, :]
+    rng = np.random.default_rng(3)
+    idx, cnt = random_lists(rng, 1, 2, 4, 2)
+    pooled = pooling.pool(q, k, v, 200, moments=True)
+    O, _ = attention.sparse_attention(q, k, v, 200, 1.0, comp, pooled, idx, cnt)
+    np.testing.assert_allclose(O[:, :, :200], v[:, :, :200], atol=1e-13)
+
+
+def test_identical_keys_in_blocks_make_order0_exact():
+    q, k, v = rand_qkv(4, N=192)
+    k = np.repeat(k[:, :, ::64], 64, axis=2)
+    rng = np.random.default_rng(4)
+    idx, cnt = random_lists(rng, 1, 2, 3, 1)
+    pooled = pooling.pool(q, k, v, 192)
+    O, _ = attention.sparse_attention(q, k, v, 192, 1.0, 0, pooled, idx, cnt)
+    Od, _ = attention.dense_attention(q, k, v, 192, 1.0)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+
+
+def test_taylor_orders_converge_at_their_rates():
+    q, k, v = rand_qkv(5, N=192, d=6)
+    base = np.repeat(k[:, :, ::64], 64, axis=2)
+    dev = k - base
+    rng = np.random.default_rng(5)
+    idx, cnt = random_lists(rng, 1, 2, 3, 1)
+    errs = {0: [], 1: []}
+    for eps in (0.2, 0.1, 0.05):
+        ke = base + eps * dev
+        Od, _ = attention.dense_attention(q, ke, v, 192, 1.0)
+        pooled = pooling.pool(q, ke, v, 192, moments=True)
+        for comp in (0, 1):
+            O, _ = attention.sparse_attention(q, ke, v, 192, 1.0, comp, pooled, idx, cnt)
+            errs[comp].append(np.abs(O - Od).max())
+    r0 = errs[0][0] / errs[0][1], errs[0][1] / errs[0][2]
+    r1 = errs[1][0] / errs[1][1], errs[1][1] / errs[1][2]
+    assert all(1.7 < r < 2.3 for r in r0), r0      # O(eps)
+    assert all(3.4 < r < 4.6 for r in r1), r1      # O(eps^2)
+
+
+def test_order0_is_sdpa_over_augmented_keys():
+    # exact keys plus one pseudo-key per skipped block with bias ln n_j
+    q, k, v = rand_qkv(6, H=1, N=230)
+    N, nb = 230, 4
+    pooled = pooling.pool(q, k, v, N)
+    rng = np.random.default_rng(6)
+    idx, cnt = random_lists(rng, 1, 1, nb, 2)
+    O, _ = attention.sparse_attention(q, k, v, N, 0.8, 0, pooled, idx, cnt)
+    for a in range(nb):
+        ex = idx[0, 0, a]
+        U = [j for j in range(nb) if j not in ex]
+        toks = [t for j in ex for t in range(64 * j, min(N, 64 * j + 64))]
+        keys = np.concatenate([k[0, 0, toks], pooled["kbar64"][0, 0, U]])
+        vals = np.concatenate([v[0, 0, toks], pooled["vbar64"][0, 0, U]])
+        bias = np.concatenate([np.zeros(len(toks)), np.log(pooled["kcount"][U].astype(float))])
+        rows = slice(64 * a, min(N, 64 * a + 64))
+        Q = torch.from_numpy(q[0, 0, rows])[None, None]
+        ref = torch.nn.functional.scaled_dot_product_attention(
+            Q, torch.from_numpy(keys)[None, None], torch.from_numpy(vals)[None, None],
+            attn_mask=torch.from_numpy(bias)[None, None, None, :].expand(1, 1, Q.shape[2], -1), scale=0.8)
+        np.testing.assert_allclose(O[0, 0, rows], ref[0, 0].numpy(), atol=1e-12)
+
+
+def test_order1_equals_per_token_linearised_exponential():
+    # PISA's block Taylor term written per token, without H_j, n_j or v_bar:
+    # e^{s q.k_n} ~ e^{s q.kbar_j} (1 + s q.(k_n - kbar_j)) for n in block j
+    q, k, v = rand_qkv(7, H=1, N=180, d=6)
+    N, nb, s = 180, 3, 0.9
+    pooled = pooling.pool(q, k, v, N, moments=True)
+    rng = np.random.default_rng(7)
+    idx, cnt = random_lists(rng, 1, 1, nb, 1)
+    O, _ = attention.sparse_attention(q, k, v, N, s, 1, pooled, idx, cnt)
+    for a in range(nb):
+        rows = slice(64 * a, min(N, 64 * a + 64))
+        Q = q[0, 0, rows]
+        num = np.zeros_like(Q)
+        den = np.zeros(Q.shape[0])
+        for j in range(nb):
+            toks = slice(64 * j, min(N, 64 * j + 64))
+            K, V = k[0, 0, toks], v[0, 0, toks]
+            if j in idx[0, 0, a]:
+                w = np.exp(s * Q @ K.T)
+            else:
+                kb = K.mean(axis=0)
+                w = np.exp(s * Q @ kb)[:, None] * (1.0 + s * (Q @ (K - kb).T))
+            num += w @ V
+            den += w.sum(axis=1)
+        np.testing.assert_allclose(O[0, 0, rows], num / den[:, None], atol=1e-12)
+
+
+def brute_rule(q, k, v, N, blk, s, comp, exact):
+    """Scalar loops over the rule, straight from its definition."""
+    nb = (N + blk - 1) // blk
+    d = q.shape[1]
+    out = np.zeros((N, d))
+    for t in range(N):
+        a = t // blk
+        D, num = 0.0, [0.0] * d
+        for j in range(nb):
+            toks = [n for n in range(j * blk, min(N, j * blk + blk))]
+            if j in exact[a]:
+                for n in toks:
+                    w = math.exp(s * sum(q[t, i] * k[n, i] for i in range(d)))
+                    D += w
+                    for o in range(d):
+                        num[o] += w * v[n, o]
+            elif comp >= 0:
+                kb = [sum(k[n, i] for n in toks) / len(toks) for i in range(d)]
+                vb = [sum(v[n, o] for n in toks) / len(toks) for o in range(d)]
+                al = math.exp(s * sum(q[t, i] * kb[i] for i in range(d)))
+                D += len(toks) * al
+                for o in range(d):
+                    num[o] += len(toks) * al * vb[o]
+                    if comp == 1:
+                        num[o] += al * s * sum(q[t, i] * (k[n, i] - kb[i]) * v[n, o]
+                                               for n in toks for i in range(d))
+        for o in range(d):
+            out[t, o] = num[o] / D
+    return out
+
+
+@pytest.mark.parametrize("comp,blk", [(-1, 3), (0, 4), (1, 2), (1, 4)])
+def test_brute_force_tiny(comp, blk):
+    rng = np.random.default_rng(10 + blk)
+    N, d = 14, 3
+    nb = (N + blk - 1) // blk
+    Np = nb * blk
+    q, k, v = (np.zeros((1, 1, Np, d)) for _ in range(3))
+    for x in (q, k, v):
+        x[0, 0, :N] = rng.standard_normal((N, d))
+    idx, cnt = random_lists(rng, 1, 1, nb, 2)
+    pooled = pooling.pool(q, k, v, N, blk=blk, moments=True)
+    O, _ = attention.sparse_attention(q, k, v, N, 0.8, comp, pooled, idx, cnt, blk=blk)
+    ref = brute_rule(q[0, 0], k[0, 0], v[0, 0], N, blk, 0.8, comp, [list(r) for r in idx[0, 0]])
+    np.testing.assert_allclose(O[0, 0, :N], ref, atol=1e-12)
+
+
+def test_skim_is_exact_when_everything_is_representable():
+    # Integer q, k, v are exact in e4m3 after the block scaling, and with
+    # s = ln 2 every weight is a power of two that e4m3 holds exactly, so the
+    # fp8 tier must reproduce dense attention: this pins the bookkeeping of
+    # the scales 2^{e_q+e_k}, 2^{e_v} and the per-row 2^{c-8}.
+    rng = np.random.default_rng(12)
+    N, d, nb = 128, 4, 2
+    q = np.zeros((1, 1, N, d)); k = np.zeros_like(q); v = np.zeros_like(q)
+    q[0, 0] = rng.integers(-1, 2, (N, d))
+    k[0, 0] = rng.integers(-1, 2, (N, d))
+    v[0, 0] = rng.integers(-3, 4, (N, d))
+    q[0, 0, ::64, 0] = 4; k[0, 0, ::64, 0] = 2; v[0, 0, ::64, 0] = 4   # pin amax per block
+    pooled = pooling.pool(q, k, v, N, fp8=True)
+    s = math.log(2.0)
+    exact = np.full((1, 1, nb, 0), -1, np.int32)
+    skim = np.tile(np.arange(nb, dtype=np.int32), (1, 1, nb, 1))
+    O, lse = attention.sparse_attention(q, k, v, N, s, -1, pooled, exact, np.zeros((1, 1, nb), np.int32),
+                                        skim, np.full((1, 1, nb), nb, np.int32))
+    Od, lsed = attention.dense_attention(q, k, v, N, s)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+def test_skim_error_is_bounded_by_e4m3_precision():
+    q, k, v = rand_qkv(13, H=1, N=192, d=16, scale=0.8)
+    pooled = pooling.pool(q, k, v, 192, fp8=True)
+    nb = 3
+    exact = np.zeros((1, 1, nb, 1), np.int32)
+    skim = np.tile(np.array([1, 2], np.int32), (1, 1, nb, 1))
+    O, _ = attention.sparse_attention(q, k, v, 192, 1.0, -1, pooled, exact, np.ones((1, 1, nb), np.int32),
+                                      skim, np.full((1, 1, nb), 2, np.int32))
+    Od, _ = attention.dense_attention(q, k, v, 192, 1.0)
+    # e4m3 keeps 3 mantissa bits (relative half-ulp 2^-4), so logits carry
+    # errors of a few percent of |q||k|: fp8-level, neither zero nor garbage
+    err = np.abs(O - Od)[0, 0, :192]
+    assert 1e-3 < err.mean() < 5e-2, err.mean()
+    assert err.max() < 0.5
+
+
+def test_quality_compensation_beats_dropping():
+    # report-only page claim (centroids recover context that dropping loses);
+    # asserted loosely on smooth synthetic fields
+    from workloads import get_workload, make_qkv
+    wl = get_workload(2, small=True)
+    q, k, v, _ = make_qkv(wl)
+    pooled = pooling.pool(q, k, v, wl.N)
+    idx, cnt = routing.route_topk(pooled["qbar"], pooled["kbar"], wl.topk)
+    Od, _ = attention.dense_attention(q, k, v, wl.N, 1.0)
+    rel = {}
+    for comp in (-1, 0):
+        O, _ = attention.sparse_attention(q, k, v, wl.N, 1.0, comp, pooled, idx, cnt)
+        rel[comp] = np.linalg.norm(O - Od) / np.linalg.norm(Od)
+    assert rel[0] < rel[-1]

@@ -1,0 +1,143 @@
+"""Pins for the routing oracle: exact integer scores, exhaustive top-k,
+LVSA rotation and window invariants, Triage tier structure."""
+
+import itertools
+
+import numpy as np
+import pytest
+
+from oracle import routing
+from workloads import get_workload, tile_major_coords, block_frame_ranges
+
+
+def int_feats(rng, shape, lo=-3, hi=4):
+    return rng.integers(lo, hi, shape).astype(np.float32)
+
+
+def test_scores_exact_on_integers():
+    rng = np.random.default_rng(0)
+    q, k = int_feats(rng, (2, 3, 7, 5)), int_feats(rng, (2, 3, 9, 5))
+    s = routing.block_scores(q, k)
+    ref = np.einsum("bhai,bhji->bhaj", q.astype(np.int64), k.astype(np.int64))
+    assert np.array_equal(s, ref.astype(np.float64))
+
+
+def test_scores_fold_in_dimension_order():
+    q = np.array([[1.0, 1.0, 1.0, 1.0]], np.float32)
+    k = np.array([[2.0 ** 60, 1.0, 1.0, -(2.0 ** 60)]], np.float32)
+    assert routing.block_scores(q, k)[0, 0] == 0.0
+
+
+def brute_topk(scores, k):
+    """Among all k-subsets, the max-sum one; ties -> lexicographically smallest."""
+    best, best_sum = None, None
+    for sub in itertools.combinations(range(len(scores)), k):
+        s = sum(int(scores[j]) for j in sub)
+        if best_sum is None or s > best_sum:
+            best, best_sum = sub, s
+    return list(best)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_topk_exhaustive(seed):
+    rng = np.random.default_rng(seed)
+    nb = 9
+    q, kb = int_feats(rng, (1, 1, nb, 3), -2, 3), int_feats(rng, (1, 1, nb, 3), -2, 3)
+    s = routing.block_scores(q, kb)[0, 0]
+    for k in (1, 3, 5, 9):
+        idx, cnt = routing.route_topk(q, kb, k)
+        for a in range(nb):
+            assert list(idx[0, 0, a]) == brute_topk(s[a], k)
+            assert cnt[0, 0, a] == k
+
+
+def test_topk_monotone_and_ties_low_index():
+    rng = np.random.default_rng(9)
+    q = np.ones((1, 1, 1, 1), np.float32)
+    kb = np.array([3, 1, 3, 2, 3, 0], np.float32).reshape(1, 1, 6, 1)
+    idx, _ = routing.route_topk(q, kb, 2)
+    assert list(idx[0, 0, 0]) == [0, 2]
+    for _ in range(20):
+        kb = rng.standard_normal((1, 1, 20, 4)).astype(np.float32)
+        q = rng.standard_normal((1, 1, 3, 4)).astype(np.float32)
+        idx, _ = routing.route_topk(q, kb, 5)
+        j = int(idx[0, 0, 0, 2])
+        kb2 = kb.copy()
+        kb2[0, 0, j] *= 2.0 if float(q[0, 0, 0] @ kb[0, 0, j]) > 0 else 0.5
+        idx2, _ = routing.route_topk(q, kb2, 5)
+        assert j in idx2[0, 0, 0]
+
+
+def test_lvsa_anchor_rotation_covers_each_block_once():
+    nb, anchors, phase = 1975, 8, 117
+    P = nb // anchors
+    seen = np.zeros(nb, int)
+    for s in range(P):
+        seen[routing.lvsa_anchor_set(nb, anchors, phase, s)] += 1
+    assert np.all(seen[:anchors * P] == 1)
+    assert np.all(seen[anchors * P:] == 0)
+
+
+def test_lvsa_window_symmetric_and_contains_self():
+    wl = get_workload(4, small=True)
+    lo, hi = block_frame_ranges(tile_major_coords(wl.T, wl.Y, wl.X))
+    idx, cnt = routing.route_lvsa(lo, hi, wl.window, 0, 0, 0)     # window only
+    nb = wl.nb
+    M = np.zeros((nb, nb), bool)
+    for a in range(nb):
+        M[a, idx[a, :cnt[a]]] = True
+        assert M[a, a]
+        assert np.all(np.diff(idx[a, :cnt[a]]) > 0)
+        assert np.all(idx[a, cnt[a]:] == -1)
+    assert np.array_equal(M, M.T)
+
+
+def test_lvsa_window_closed_form_on_aligned_blocks():
+    # 8 frames of 8x8: every block is one 4x4x4 tile inside a 4-frame group.
+    lo, hi = block_frame_ranges(tile_major_coords(12, 8, 8))
+    assert np.all(hi - lo == 3)
+    idx, cnt = routing.route_lvsa(lo, hi, 2, 0, 0, 0)
+    group = lo // 4
+    for a in range(len(lo)):
+        ref = np.nonzero(np.abs(group - group[a]) <= 1)[0]
+        assert list(idx[a, :cnt[a]]) == list(ref)
+
+
+def test_lvsa_anchors_added_to_every_row():
+    wl = get_workload(4, small=True)
+    lo, hi = block_frame_ranges(tile_major_coords(wl.T, wl.Y, wl.X))
+    anc = routing.lvsa_anchor_set(wl.nb, wl.anchors, 1, 2)
+    idx, cnt = routing.route_lvsa(lo, hi, wl.window, wl.anchors, 1, 2)
+    for a in range(wl.nb):
+        assert set(anc) <= set(idx[a, :cnt[a]])
+
+
+def test_triage_tiers_partition_and_counts():
+    rng = np.random.default_rng(4)
+    nb = 40
+    q, kb = rng.standard_normal((1, 2, nb, 8)).astype(np.float32), rng.standard_normal((1, 2, nb, 8)).astype(np.float32)
+    lam = rng.standard_normal((1, 2, nb)).astype(np.float32)
+    n = np.full(nb, 64, np.int32)
+    n[-1] = 17
+    ri, rc, si, sc = routing.route_triage(q, kb, lam, n, 1.0, 16, 6)
+    assert np.all(rc == 6) and np.all(sc == 10)
+    for b, h, a in itertools.product(range(1), range(2), range(nb)):
+        r, s = set(ri[b, h, a]), set(si[b, h, a])
+        assert not (r & s) and len(r) == 6 and len(s) == 10
+        eskip = routing.block_scores(q, kb)[b, h, a] + lam[b, h].astype(np.float64)
+        keep = np.lexsort((np.arange(nb), -eskip))[:16]
+        assert r | s == set(keep.tolist())
+
+
+def test_triage_equal_spreads_give_nested_topk():
+    rng = np.random.default_rng(5)
+    nb = 30
+    q, kb = rng.standard_normal((1, 1, nb, 8)).astype(np.float32), rng.standard_normal((1, 1, nb, 8)).astype(np.float32)
+    lam = np.full((1, 1, nb), 0.25, np.float32)
+    n = np.full(nb, 64, np.int32)
+    ri, _, si, _ = routing.route_triage(q, kb, lam, n, 1.0, 12, 5)
+    top12, _ = routing.route_topk(q, kb, 12)
+    top5, _ = routing.route_topk(q, kb, 5)
+    for a in range(nb):
+        assert list(ri[0, 0, a]) == list(top5[0, 0, a])
+        assert sorted(set(ri[0, 0, a]) | set(si[0, 0, a])) == list(top12[0, 0, a])
