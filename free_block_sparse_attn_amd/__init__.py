@@ -1,0 +1,174 @@
+"""Compensated block-sparse attention for video diffusion transformers on MI355X.
+
+Python face of libsparse_attn.so.  The three calls mirror the C ABI
+(include/sparse_attn.h) and take torch tensors that already live on the GPU;
+outputs are allocated here with torch (plumbing) and filled by the HIP
+kernels on the current stream:
+
+    pooled = sparse_attn_pool(q, k, v, N, moments=..., spreads=..., fp8=...)
+    idx, cnt, idx2, cnt2 = sparse_attn_route(pooled, N, mode=..., ...)
+    out, lse = sparse_attn_fwd(q, k, v, N, scale, comp, pooled, idx, cnt, idx2, cnt2)
+"""
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER0,
+                   SA_COMP_ORDER1_BLOCK, SA_ROUTE_TOPK, SA_ROUTE_LVSA, SA_ROUTE_TRIAGE)
+
+__all__ = [
+    "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
+    "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
+    "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE",
+]
+
+BLK = 64
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _shape(q, N):
+    B, H, Np, d = q.shape
+    return _lib.Shape(B, H, N, Np, d)
+
+
+def _dtype(t):
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    if t.dtype == torch.float32:
+        return SA_F32
+    raise SparseAttnError(1, f"unsupported tensor dtype {t.dtype}")
+
+
+def _contig(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise SparseAttnError(1, "tensors must be contiguous CUDA tensors")
+
+
+def abi_version() -> int:
+    return _lib.load().sparse_attn_abi_version()
+
+
+def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, out=None) -> dict:
+    """Block means (fp32), counts and the optional moments / spreads / e4m3 copies.
+
+    `out` may pass a dict returned by an earlier call to reuse its buffers.
+    """
+    lib = _lib.load()
+    _contig(q, k, v)
+    B, H, Np, d = q.shape
+    nb = Np // BLK
+    dev = q.device
+    if out is not None:
+        g = out.get
+        _lib.check(lib.sparse_attn_pool(
+            ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
+            _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+            _stream(q)))
+        return out
+    out = {
+        "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+        "kbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+        "vbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+        "kcount": torch.empty(nb, dtype=torch.int32, device=dev),
+    }
+    if moments:
+        out["kmom"] = torch.empty(B, H, nb, d, d, dtype=torch.bfloat16, device=dev)
+    if spreads:
+        out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
+    if fp8:
+        for n in ("q8", "k8", "v8"):
+            out[n] = torch.empty(B, H, Np, d, dtype=torch.uint8, device=dev)
+        out["exp8"] = torch.empty(B, H, nb, 3, dtype=torch.int8, device=dev)
+    g = out.get
+    _lib.check(lib.sparse_attn_pool(
+        ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
+        _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+        _stream(q)))
+    return out
+
+
+def sparse_attn_lvsa_capacity(frame_lo, frame_hi, window: int, anchors: int) -> int:
+    """Row capacity that holds every LVSA row (host int32 arrays)."""
+    import numpy as np
+    lo = np.ascontiguousarray(frame_lo, np.int32)
+    hi = np.ascontiguousarray(frame_hi, np.int32)
+    return _lib.load().sparse_attn_lvsa_capacity(lo.ctypes.data_as(ctypes.c_void_p),
+                                                 hi.ctypes.data_as(ctypes.c_void_p),
+                                                 lo.shape[0], window, anchors)
+
+
+def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int = 0,
+                      frame_lo=None, frame_hi=None, window: int = 0, anchors: int = 0,
+                      anchor_phase: int = 0, step: int = 0, cap: int = 0,
+                      n_keep: int = 0, n_refine: int = 0, scale: float = 1.0,
+                      out=None):
+    """Key-block lists per query block: (idx, cnt, idx2, cnt2); idx2/cnt2 only for Triage.
+
+    `out` may pass preallocated (idx, cnt, idx2, cnt2) tensors.
+    """
+    lib = _lib.load()
+    qbar, kbar = pooled["qbar"], pooled["kbar"]
+    B, H, nb, d = qbar.shape
+    dev = qbar.device
+    shape = _lib.Shape(B, H, N, nb * BLK, d)
+    spec = _lib.RouteSpec(mode, topk, None, None, window, anchors, anchor_phase, step,
+                          n_keep, n_refine, scale)
+    cap2 = 0
+    if mode == SA_ROUTE_TOPK:
+        cap = cap or topk
+    elif mode == SA_ROUTE_LVSA:
+        _contig(frame_lo, frame_hi)
+        spec.frame_lo = frame_lo.data_ptr()
+        spec.frame_hi = frame_hi.data_ptr()
+        if not cap:
+            raise SparseAttnError(1, "LVSA routing needs cap (see sparse_attn_lvsa_capacity)")
+    elif mode == SA_ROUTE_TRIAGE:
+        cap = n_refine
+        cap2 = n_keep - n_refine
+    if out is None:
+        idx = torch.empty(B, H, nb, max(cap, 1), dtype=torch.int32, device=dev)
+        cnt = torch.empty(B, H, nb, dtype=torch.int32, device=dev)
+        idx2 = cnt2 = None
+        if mode == SA_ROUTE_TRIAGE:
+            idx2 = torch.empty(B, H, nb, max(cap2, 1), dtype=torch.int32, device=dev)
+            cnt2 = torch.empty(B, H, nb, dtype=torch.int32, device=dev)
+    else:
+        idx, cnt, idx2, cnt2 = out
+    _lib.check(lib.sparse_attn_route(
+        ctypes.byref(shape), ctypes.byref(spec), _ptr(qbar), _ptr(kbar), _ptr(pooled.get("kcount")),
+        _ptr(pooled.get("klam")), _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2, _stream(qbar)))
+    return idx, cnt, idx2, cnt2
+
+
+def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx, cnt,
+                    idx2=None, cnt2=None, want_lse=True, out=None, lse=None):
+    """Compensated block-sparse attention forward; returns (out, lse)."""
+    lib = _lib.load()
+    _contig(q, k, v, idx, cnt, idx2, cnt2)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        B, H, Np, _ = q.shape
+        lse = torch.empty(B, H, Np, dtype=torch.float32, device=q.device)
+    g = pooled.get
+    cap = idx.shape[-1] if idx is not None else 0
+    cap2 = idx2.shape[-1] if idx2 is not None else 0
+    _lib.check(lib.sparse_attn_fwd(
+        ctypes.byref(_shape(q, N)), _dtype(q), comp, scale, _ptr(q), _ptr(k), _ptr(v),
+        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("kcount")), _ptr(g("kmom")),
+        _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+        _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
+        _ptr(out), _ptr(lse), _stream(q)))
+    return out, lse

@@ -1,0 +1,210 @@
+// C ABI of the compensated block-sparse attention library: argument
+// validation on the host, then asynchronous launches on the caller's stream.
+#include "../../include/sparse_attn.h"
+#include "launch.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sa_status fail(sa_status st, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sa_status ok() {
+    g_last_error.clear();
+    return SA_OK;
+}
+
+bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define NEED(ptr)                                                                          \
+    do {                                                                                   \
+        if ((ptr) == nullptr) return fail(SA_ERR_INVALID_ARG, "%s must not be NULL", #ptr); \
+        if (!aligned(ptr)) return fail(SA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #ptr); \
+    } while (0)
+#define MAYBE(ptr)                                                                         \
+    do {                                                                                   \
+        if ((ptr) != nullptr && !aligned(ptr))                                             \
+            return fail(SA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #ptr);           \
+    } while (0)
+
+constexpr int MAX_BLOCKS = 4096;   // routing keeps one row of keys in LDS; kept-block bitmask size
+
+// Checks the shape; sets `empty` when there is nothing to compute.
+sa_status check_shape(const sa_shape* s, bool& empty) {
+    if (s == nullptr) return fail(SA_ERR_INVALID_ARG, "shape must not be NULL");
+    if (s->B < 0 || s->H < 0 || s->N < 0 || s->N_pad < 0)
+        return fail(SA_ERR_INVALID_ARG, "negative size in shape (B=%d H=%d N=%d N_pad=%d)", s->B, s->H, s->N, s->N_pad);
+    if (s->d != 64 && s->d != 128) return fail(SA_ERR_INVALID_ARG, "d must be 64 or 128, got %d", s->d);
+    const int64_t want = 64 * ((static_cast<int64_t>(s->N) + 63) / 64);
+    if (s->N_pad != want)
+        return fail(SA_ERR_INVALID_ARG, "N_pad must be 64*ceil(N/64) = %lld, got %d", static_cast<long long>(want), s->N_pad);
+    empty = (s->B == 0 || s->H == 0 || s->N == 0);
+    return SA_OK;
+}
+
+sa_status hip_result(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(SA_ERR_HIP, "%s launch failed: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sparse_attn_status_string(sa_status status) {
+    switch (status) {
+        case SA_OK: return "ok";
+        case SA_ERR_INVALID_ARG: return "invalid argument";
+        case SA_ERR_UNSUPPORTED: return "unsupported";
+        case SA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }
+
+int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
+
+sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
+                           float* qbar, float* kbar, float* vbar, int32_t* kcount, void* kmom, float* klam,
+                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, hipStream_t stream) {
+    bool empty = false;
+    if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
+    if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (empty) return ok();
+    NEED(q); NEED(k); NEED(v); NEED(qbar); NEED(kbar); NEED(vbar); NEED(kcount);
+    MAYBE(kmom); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
+    const int fp8 = (q8 != nullptr) + (k8 != nullptr) + (v8 != nullptr) + (exp8 != nullptr);
+    if (fp8 != 0 && fp8 != 4) return fail(SA_ERR_INVALID_ARG, "q8, k8, v8 and exp8 must be given together");
+    const bool bf16_128 = dtype == SA_BF16 && shape->d == 128;
+    if (kmom && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "kmom needs bf16 inputs with d == 128");
+    if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
+    if (empty) return ok();
+    sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
+                   kmom, klam, q8, k8, v8, exp8};
+    return hip_result(sa::launch_pool(a, dtype == SA_BF16, stream), "pool");
+}
+
+int32_t sparse_attn_lvsa_capacity(const int32_t* lo, const int32_t* hi, int32_t nb, int32_t window, int32_t anchors) {
+    if (lo == nullptr || hi == nullptr || nb <= 0) return 0;
+    // window blocks of the widest row plus every anchor (an upper bound over all steps)
+    int32_t best = 0;
+    for (int a = 0; a < nb; ++a) {
+        int32_t c = 0;
+        for (int j = 0; j < nb; ++j)
+            if (lo[j] <= hi[a] + window && hi[j] >= lo[a] - window) ++c;
+        best = c > best ? c : best;
+    }
+    best += anchors > 0 ? anchors : 0;
+    return best > nb ? nb : best;
+}
+
+sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, const float* qbar, const float* kbar,
+                            const int32_t* kcount, const float* klam, int32_t* idx, int32_t* cnt, int32_t cap,
+                            int32_t* idx2, int32_t* cnt2, int32_t cap2, hipStream_t stream) {
+    bool empty = false;
+    if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
+    if (spec == nullptr) return fail(SA_ERR_INVALID_ARG, "spec must not be NULL");
+    const int nb = shape->N_pad / 64;
+    if (nb > MAX_BLOCKS) return fail(SA_ERR_UNSUPPORTED, "at most %d blocks per sequence, got %d", MAX_BLOCKS, nb);
+    if (empty) return ok();
+    sa::RouteArgs a{};
+    a.B = shape->B; a.H = shape->H; a.nb = nb; a.d = shape->d; a.mode = spec->mode;
+    a.qbar = qbar; a.kbar = kbar; a.kcount = kcount; a.klam = klam;
+    a.idx = idx; a.cnt = cnt; a.cap = cap; a.idx2 = idx2; a.cnt2 = cnt2; a.cap2 = cap2;
+    switch (spec->mode) {
+        case SA_ROUTE_TOPK:
+            NEED(qbar); NEED(kbar); NEED(idx); NEED(cnt);
+            if (!empty && (spec->topk < 1 || spec->topk > nb))
+                return fail(SA_ERR_INVALID_ARG, "topk must be in [1, nb=%d], got %d", nb, spec->topk);
+            if (cap < spec->topk) return fail(SA_ERR_INVALID_ARG, "cap %d < topk %d", cap, spec->topk);
+            a.topk = spec->topk;
+            break;
+        case SA_ROUTE_LVSA:
+            NEED(spec->frame_lo); NEED(spec->frame_hi); NEED(idx); NEED(cnt);
+            if (spec->window < 0 || spec->anchor_phase < 0 || spec->step < 0)
+                return fail(SA_ERR_INVALID_ARG, "window, anchor_phase and step must be >= 0");
+            if (spec->anchors < 0 || (!empty && spec->anchors > nb))
+                return fail(SA_ERR_INVALID_ARG, "anchors must be in [0, nb=%d], got %d", nb, spec->anchors);
+            if (cap < 1) return fail(SA_ERR_INVALID_ARG, "cap must be >= 1");
+            a.frame_lo = spec->frame_lo; a.frame_hi = spec->frame_hi; a.window = spec->window;
+            a.anchors = spec->anchors; a.anchor_phase = spec->anchor_phase; a.step = spec->step;
+            break;
+        case SA_ROUTE_TRIAGE:
+            NEED(qbar); NEED(kbar); NEED(kcount); NEED(klam); NEED(cnt);
+            if (!empty && (spec->n_keep < 1 || spec->n_keep > nb))
+                return fail(SA_ERR_INVALID_ARG, "n_keep must be in [1, nb=%d], got %d", nb, spec->n_keep);
+            if (spec->n_refine < 0 || spec->n_refine > spec->n_keep)
+                return fail(SA_ERR_INVALID_ARG, "n_refine must be in [0, n_keep], got %d", spec->n_refine);
+            if (cap < spec->n_refine) return fail(SA_ERR_INVALID_ARG, "cap %d < n_refine %d", cap, spec->n_refine);
+            if (cap > 0) NEED(idx); else MAYBE(idx);
+            if (cap2 < spec->n_keep - spec->n_refine)
+                return fail(SA_ERR_INVALID_ARG, "cap2 %d < n_keep - n_refine %d", cap2, spec->n_keep - spec->n_refine);
+            NEED(cnt2);
+            if (cap2 > 0) NEED(idx2); else MAYBE(idx2);
+            if (!std::isfinite(spec->scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+            a.n_keep = spec->n_keep; a.n_refine = spec->n_refine; a.scale = spec->scale;
+            break;
+        default:
+            return fail(SA_ERR_INVALID_ARG, "unknown route mode %d", spec->mode);
+    }
+    if (empty) return ok();
+    return hip_result(sa::launch_route(a, stream), "route");
+}
+
+sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale, const void* q,
+                          const void* k, const void* v, const float* kbar, const float* vbar, const int32_t* kcount,
+                          const void* kmom, const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                          const int8_t* exp8, const int32_t* idx, const int32_t* cnt, int32_t cap,
+                          const int32_t* idx2, const int32_t* cnt2, int32_t cap2, void* out, float* lse,
+                          hipStream_t stream) {
+    bool empty = false;
+    if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
+    if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
+    if (comp < SA_COMP_DROP || comp > SA_COMP_ORDER1_BLOCK)
+        return fail(SA_ERR_INVALID_ARG, "unknown compensation order %d", static_cast<int>(comp));
+    if (!std::isfinite(scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+    const int nb = shape->N_pad / 64;
+    if (nb > MAX_BLOCKS) return fail(SA_ERR_UNSUPPORTED, "at most %d blocks per sequence, got %d", MAX_BLOCKS, nb);
+    if (empty) return ok();
+    NEED(q); NEED(k); NEED(v); NEED(out); MAYBE(lse);
+    if (cap < 0 || cap2 < 0) return fail(SA_ERR_INVALID_ARG, "cap and cap2 must be >= 0");
+    if (cap > 0) { NEED(idx); NEED(cnt); }
+    const bool skim = idx2 != nullptr && cap2 > 0;
+    if (skim) { NEED(cnt2); }
+    if (comp >= SA_COMP_ORDER0) { NEED(kbar); NEED(vbar); NEED(kcount); }
+    if (comp == SA_COMP_ORDER1_BLOCK) { NEED(kmom); }
+    if (dtype == SA_F32) {
+        if (shape->d != 64) return fail(SA_ERR_UNSUPPORTED, "fp32 forward supports d == 64 only");
+        if (comp == SA_COMP_ORDER1_BLOCK) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no first-order term");
+        if (skim) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no fp8 skim tier");
+    } else {
+        if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "bf16 forward supports d == 128 only");
+        if (skim) {
+            NEED(q8); NEED(k8); NEED(v8); NEED(exp8);
+            return fail(SA_ERR_UNSUPPORTED, "the fp8 skim tier is not available in this build");
+        }
+    }
+    if (comp == SA_COMP_DROP && cap == 0 && !skim)
+        return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");
+    if (empty) return ok();
+    sa::FwdArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, static_cast<int>(comp), scale, q, k, v,
+                  kbar, vbar, kcount, kmom, q8, k8, v8, exp8, idx, cnt, cap, idx2, cnt2, cap2, out, lse};
+    if (dtype == SA_F32) return hip_result(sa::launch_fwd_f32(a, stream), "fwd_f32");
+    return hip_result(sa::launch_fwd_bf16(a, stream), "fwd_bf16");
+}
+
+}  // extern "C"

@@ -1,0 +1,515 @@
+// bf16 compensated block-sparse attention forward for gfx950 (d = 128).
+//
+// What it computes (per query t of query block a, one softmax):
+//   exact key blocks E          e^{s q.k_n} (v_n)                    bf16 MFMA
+//   every other key block j     n_j e^{s q.k_bar_j} (v_bar_j)         order 0
+//                               + e^{s q.k_bar_j} s q^T H_j (N only)  order 1
+// PISA ("PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
+// Transformers", section 2, "Algorithme Central" and "Implementation
+// Materielle": exact phase on selected blocks, then a scan of the block
+// aggregates, then the first-order correction, all inside one
+// FlashAttention-style online softmax); SVG-EAR's centroid compensation
+// ("SVG-EAR ...", section 2A).
+//
+// Work split.  One wave owns a whole 64-row query block, so a 64-key tile is
+// 2 x 2 blocks of 32x32 and every K/V byte loaded feeds 64 query rows.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows loaded straight from
+//                 global memory into VGPRs one tile ahead, B = Q^T held in
+//                 VGPRs for the whole kernel.  Each lane ends up owning one
+//                 query row per 32-row block, so the row max / row sum need a
+//                 single exchange with the other half of the wave.
+//   O^T += V^T P^T  B = P^T straight from S's accumulators (rounded to bf16),
+//                 A = V^T read from a row-major LDS copy of V with
+//                 ds_read_b64_tr_b16 (4 consecutive keys of one d per read).
+//                 V tiles reach LDS by global_load_lds_dwordx4 (no VGPRs),
+//                 double buffered one tile ahead, with a 16-byte XOR swizzle.
+// The P^T operand's key order follows S's accumulator layout: within each
+// 16-key MFMA step, slot s holds key s with bits 2 and 3 swapped; the V^T
+// reads use the same order.  Centroid pseudo-keys go through the same MFMA
+// path as 64-wide tiles (means split into bf16 high + low parts so the fp32
+// means keep ~16 bits), with bias log2(n_j) and -inf at the exact blocks.
+// The running max is updated lazily (only when a row's tile max exceeds it
+// by more than 8 in log2 units), which keeps the accumulator rescale off the
+// common path.  The softmax denominator sums the same bf16-rounded P that
+// the MFMA consumes, so rounding of P cancels in o = N / D.
+//
+// Workgroup = one wave; consecutive query blocks of one head are mapped to
+// the same XCD so their overlapping K/V blocks are shared through its L2.
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+
+namespace {
+
+#ifndef SA_K_PREFETCH
+#define SA_K_PREFETCH 0            // K tiles: 1 = loaded one tile ahead into VGPRs
+#endif
+
+constexpr int D = 128;
+constexpr int ROWB = D * 2;                // bytes per bf16 row
+constexpr int TILEB = BLK * ROWB;          // bytes per 64-key bf16 tile (16 KiB)
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+constexpr float TAU = 8.0f;                // lazy rescale threshold (log2 units)
+
+struct Lds {
+    uint8_t v[2][TILEB];                   // V tiles, row-major, swizzled 16-byte chunks
+    uint32_t kept[128];                    // bitmask of blocks not compensated (nb <= 4096)
+};
+struct LdsOrder1 {
+    Lds base;
+    float w[BLK * (BLK + 1)];              // order-1 weights [centroid][row]
+};
+
+// physical 16-byte chunk of logical chunk c (0..15) in LDS row `row`
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row & 7) << 1); }
+
+__device__ __forceinline__ int xcd_remap(int bid, int grid) {
+    const int xcd = bid & 7, slot = bid >> 3;
+    const int per = grid >> 3, extra = grid & 7;
+    return xcd * per + min(xcd, extra) + slot;
+}
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// s_waitcnt with vmcnt <= n (expcnt and lgkmcnt left open), gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | (((N >> 4) & 3) << 14));
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((ext_vector_type(8))) short i16x8;
+
+// 16 x global_load_lds_dwordx4: the whole 64x128 bf16 V tile into one LDS
+// buffer.  Instruction m fills LDS rows 4m .. 4m+3; lane l lands at row
+// 4m + l/16, physical chunk l%16, so it fetches the logical chunk that the
+// swizzle maps there.
+__device__ __forceinline__ void dma_v_tile(const uint16_t* vrow0, uint8_t* buf) {
+    const int l = lane_id();
+    const int rsub = l >> 4, p = l & 15;
+#pragma unroll
+    for (int m = 0; m < 16; ++m) {
+        const int row = 4 * m + rsub;
+        const int c = swz(row, p);                 // swz is an involution
+        const uint16_t* src = vrow0 + row * D + 8 * c;
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+                                         (lds_void*)(buf + m * 1024), 16, 0, 0);
+    }
+}
+
+// Zero rows nvalid..63 of an LDS tile (pad keys of the ragged tail block).
+__device__ __forceinline__ void zero_tail_rows(uint8_t* buf, int nvalid) {
+    const int l = lane_id();
+    for (int x = nvalid * 16 + l; x < BLK * 16; x += 64) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(buf + x * 16) = z;
+    }
+}
+
+// Write 64 fp32 mean rows (centroid values) as bf16 rows into an LDS tile:
+// the high parts (LO = false) or the residuals x - bf16(x) (LO = true).
+template <bool LO>
+__device__ __forceinline__ void stage_means(const float* vrow0, int nvalid, uint8_t* buf) {
+    const int l = lane_id();
+    const int rsub = l >> 4, c = l & 15;
+#pragma unroll 4
+    for (int m = 0; m < 16; ++m) {
+        const int row = 4 * m + rsub;
+        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        if (row < nvalid) {
+            const float4 x0 = *reinterpret_cast<const float4*>(vrow0 + row * D + 8 * c);
+            const float4 x1 = *reinterpret_cast<const float4*>(vrow0 + row * D + 8 * c + 4);
+            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+        }
+        if (LO) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t) x[t] -= bf16_to_f32(f32_to_bf16(x[t]));
+        }
+        u32x4 w;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
+        *reinterpret_cast<u32x4*>(buf + row * ROWB + 16 * swz(row, c)) = w;
+    }
+}
+
+struct State {
+    f32x16 o[4][2];        // O^T[d-block][row-block]
+    float m[2];            // running reference max (log2 units, an integer) per row block
+    float l[2];            // partial row sums of the bf16-rounded P (normalises O)
+    float le[2];           // partial row sums of the unrounded weights (for lse)
+};
+
+// Lazy max update: when a row's tile max exceeds the reference by more than
+// TAU, move the reference up to ceil(tile max) and rescale that row's
+// accumulators.  The reference stays an integer so that powers of two
+// relative to it are exact.
+__device__ __forceinline__ void rescale_if_needed(State& st, int rb, float mx) {
+    const bool need = mx > st.m[rb] + TAU;
+    if (__ballot(need)) {
+        const float mnew = need ? ceilf(mx) : st.m[rb];
+        const float alpha = exp2f(st.m[rb] - mnew);
+        st.l[rb] *= alpha;
+        st.le[rb] *= alpha;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) st.o[db][rb][r] *= alpha;
+        st.m[rb] = mnew;
+    }
+}
+
+// Online-softmax update of one 64-key tile whose logits (already in log2
+// units with bias and masking applied) are in s[kb][rb]; returns P^T as the
+// bf16 B operands of the O^T update, pb[2 kb + q2][rb].
+__device__ __forceinline__ void softmax_tile(State& st, f32x16 s[2][2], bf16x8 pb[4][2]) {
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][rb][r]);
+        mx = fmaxf(mx, swap_halves(mx));
+        rescale_if_needed(st, rb, mx);
+        const float mref = st.m[rb];
+        float ls = 0.f, le = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                bf16x8 p;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float sv = s[kb][rb][8 * q2 + e];
+                    const float x = (sv == -INFINITY) ? 0.f : exp2f(sv - mref);
+                    p[e] = static_cast<__bf16>(x);
+                    ls += static_cast<float>(p[e]);
+                    le += x;
+                }
+                pb[2 * kb + q2][rb] = p;
+            }
+        }
+        st.l[rb] += ls;
+        st.le[rb] += le;
+    }
+}
+
+// O^T += V^T P^T for one tile whose V rows sit in LDS buffer `buf`.
+// ds_read_b64_tr_b16: within each 16-lane group, output lane i receives
+// element i%4 of the 8-byte pieces addressed by lanes i/4 + 4e (e = 0..3).
+// Supplying lane r addresses row key0 + r/4 at d0 + 4(r%4), so output lane
+// i gets keys key0 .. key0+3 of column d0 + i.
+__device__ __forceinline__ void pv_tile(State& st, const uint8_t* buf, const bf16x8 pb[4][2]) {
+    const int l = lane_id();
+    const int h = l >> 5, g2 = (l >> 4) & 1, r = l & 15;
+    const int rsub = r >> 2, csub = r & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+        const int chunk = 4 * db + 2 * g2 + (csub >> 1);
+        const int half = (csub & 1) * 8;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int rowA = 16 * kk + 4 * h + rsub;          // keys 16kk + 4h + e
+            const int rowB = rowA + 8;                        // keys 16kk + 8 + 4h + e
+            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(const_cast<uint8_t*>(buf) + rowA * ROWB + 16 * swz(rowA, chunk) + half));
+            const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (lds_i16x4*)(const_cast<uint8_t*>(buf) + rowB * ROWB + 16 * swz(rowB, chunk) + half));
+            const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+            const bf16x8 a8 = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk][rb], st.o[db][rb], 0, 0, 0);
+        }
+    }
+}
+
+// K tile as MFMA A operands: ka[kb][ks] = K[32kb + l32][16ks + 8h .. +7]
+__device__ __forceinline__ void load_k_tile(const uint16_t* krow0, bf16x8 ka[2][8]) {
+    const int l = lane_id(), h = l >> 5, l32 = l & 31;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+            ka[kb][ks] = *reinterpret_cast<const bf16x8*>(krow0 + (32 * kb + l32) * D + 16 * ks + 8 * h);
+}
+
+__device__ __forceinline__ void s_tile(const bf16x8 ka[2][8], const bf16x8 qb[2][8], f32x16 s[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qb[rb][ks], s[kb][rb], 0, 0, 0);
+}
+
+template <int COMP>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
+    Lds& lds = *reinterpret_cast<Lds*>(smem_raw);
+    float* wbuf = (COMP == 1) ? reinterpret_cast<LdsOrder1*>(smem_raw)->w : nullptr;
+
+    const int nq = a.N_pad / BLK, nb = nq;
+    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int qa = lin % nq;
+    const size_t bh = lin / nq;
+    const int l = lane_id(), h = l >> 5, l32 = l & 31;
+    const size_t head = bh * a.N_pad * D;
+    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + head;
+    const uint16_t* K = static_cast<const uint16_t*>(a.k) + head;
+    const uint16_t* V = static_cast<const uint16_t*>(a.v) + head;
+    const float c2 = a.scale * LOG2E;
+
+    const size_t rowid = bh * nq + qa;
+    const int cntE = a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0;
+    const int32_t* listE = a.idx + rowid * a.cap;
+
+    // first exact tile in flight before anything else
+    bf16x8 ka[2][8];
+    if (cntE > 0) {
+        const int j0 = listE[0];
+#if SA_K_PREFETCH
+        load_k_tile(K + static_cast<size_t>(j0) * BLK * D, ka);
+#endif
+        dma_v_tile(V + static_cast<size_t>(j0) * BLK * D, lds.v[0]);
+    }
+
+    // Q^T as B operands: qb[rb][ks] = Q[row 32rb + l32][16ks + 8h .. +7]
+    bf16x8 qb[2][8];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = qa * BLK + 32 * rb + l32;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            bf16x8 z = {};
+            if (row < a.N) z = *reinterpret_cast<const bf16x8*>(Q + static_cast<size_t>(row) * D + 16 * ks + 8 * h);
+            qb[rb][ks] = z;
+        }
+    }
+
+    // blocks that are not compensated
+    for (int x = l; x < 128; x += 64) lds.kept[x] = 0u;
+    wave_lds_sync();
+    if (COMP >= 0) {
+        for (int e = l; e < cntE; e += 64) {
+            const int j = listE[e];
+            atomicOr(&lds.kept[j >> 5], 1u << (j & 31));
+        }
+        wave_lds_sync();
+    }
+
+    State st;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) st.o[db][rb] = f32x16{};
+    st.m[0] = st.m[1] = -INFINITY;
+    st.l[0] = st.l[1] = 0.f;
+    st.le[0] = st.le[1] = 0.f;
+
+    // ---- phase 1: exact key blocks, one tile of K (VGPRs) and V (LDS) ahead ----
+    for (int e = 0; e < cntE; ++e) {
+        const int j = listE[e];
+        const int nj = min(BLK, a.N - BLK * j);
+        f32x16 s[2][2];
+#if !SA_K_PREFETCH
+        load_k_tile(K + static_cast<size_t>(j) * BLK * D, ka);
+#endif
+        s_tile(ka, qb, s);
+        const bool more = e + 1 < cntE;
+        if (more) {
+            const int jn = listE[e + 1];
+#if SA_K_PREFETCH
+            load_k_tile(K + static_cast<size_t>(jn) * BLK * D, ka);
+#endif
+            dma_v_tile(V + static_cast<size_t>(jn) * BLK * D, lds.v[(e + 1) & 1]);
+        }
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    s[kb][rb][r] = (key < nj) ? s[kb][rb][r] * c2 : -INFINITY;
+                }
+        bf16x8 pb[4][2];
+        softmax_tile(st, s, pb);
+        // this tile's V has landed once only the next tile's loads may be outstanding
+        if (more) wait_vmcnt<SA_K_PREFETCH ? 32 : 16>(); else wait_vmcnt<0>();
+        uint8_t* vb = lds.v[e & 1];
+        if (nj < BLK) zero_tail_rows(vb, nj);
+        wave_lds_sync();
+        pv_tile(st, vb, pb);
+        wave_lds_sync();
+    }
+
+    // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
+    if (COMP >= 0) {
+        const float* KB = a.kbar + bh * nb * D;
+        const float* VB = a.vbar + bh * nb * D;
+        uint8_t* vb = lds.v[0];
+        for (int c0 = 0; c0 < nb; c0 += BLK) {
+            const int nc = min(BLK, nb - c0);
+            f32x16 s[2][2];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+                const int cj = min(c0 + 32 * kb + l32, nb - 1);
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const float4 x0 = *reinterpret_cast<const float4*>(KB + static_cast<size_t>(cj) * D + 16 * ks + 8 * h);
+                    const float4 x1 = *reinterpret_cast<const float4*>(KB + static_cast<size_t>(cj) * D + 16 * ks + 8 * h + 4);
+                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    u32x4 whi, wlo;
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        whi[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
+                        const float r0 = x[2 * t] - bf16_to_f32(static_cast<uint16_t>(whi[t] & 0xFFFFu));
+                        const float r1 = x[2 * t + 1] - bf16_to_f32(static_cast<uint16_t>(whi[t] >> 16));
+                        wlo[t] = pack_bf16x2(r0, r1);
+                    }
+                    const bf16x8 khi = __builtin_bit_cast(bf16x8, whi), klo = __builtin_bit_cast(bf16x8, wlo);
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb[rb][ks], s[kb][rb], 0, 0, 0);
+                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb[rb][ks], s[kb][rb], 0, 0, 0);
+                    }
+                }
+            }
+            float bias[2][16];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int jj = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    float bv = -INFINITY;
+                    if (jj < nb && !((lds.kept[jj >> 5] >> (jj & 31)) & 1u))
+                        bv = __log2f(static_cast<float>(min(BLK, a.N - BLK * jj)));
+                    bias[kb][r] = bv;
+                }
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) s[kb][rb][r] = s[kb][rb][r] * c2 + bias[kb][r];
+            bf16x8 pb[4][2];
+            softmax_tile(st, s, pb);
+            if (COMP == 1) {
+                // order-1 weights w = scale * e^{L - m} / n_j (L without the count bias)
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            const int cc = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                            const float x = (bias[kb][r] == -INFINITY) ? 0.f
+                                : exp2f(s[kb][rb][r] - bias[kb][r] - st.m[rb]) * a.scale;
+                            wbuf[cc * (BLK + 1) + 32 * rb + l32] = x;
+                        }
+            }
+            stage_means<false>(VB + static_cast<size_t>(c0) * D, nc, vb);
+            wave_lds_sync();
+            pv_tile(st, vb, pb);
+            wave_lds_sync();
+            stage_means<true>(VB + static_cast<size_t>(c0) * D, nc, vb);
+            wave_lds_sync();
+            pv_tile(st, vb, pb);
+            wave_lds_sync();
+            if (COMP == 1) {
+                // O^T += w (.) (H_j^T Q^T) for every compensated block of this tile
+                const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom);
+                for (int cc = 0; cc < nc; ++cc) {
+                    const int jj = c0 + cc;
+                    if ((lds.kept[jj >> 5] >> (jj & 31)) & 1u) continue;
+                    const uint16_t* Hj = MOM + (bh * nb + jj) * static_cast<size_t>(D) * D;
+                    const float w0 = wbuf[cc * (BLK + 1) + l32];
+                    const float w1 = wbuf[cc * (BLK + 1) + 32 + l32];
+#pragma unroll
+                    for (int db = 0; db < 4; ++db) {
+                        bf16x8 ha[8];
+#pragma unroll
+                        for (int ks = 0; ks < 8; ++ks)
+                            ha[ks] = *reinterpret_cast<const bf16x8*>(Hj + (32 * db + l32) * D + 16 * ks + 8 * h);
+                        f32x16 t0 = {}, t1 = {};
+#pragma unroll
+                        for (int ks = 0; ks < 8; ++ks) {
+                            t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qb[0][ks], t0, 0, 0, 0);
+                            t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qb[1][ks], t1, 0, 0, 0);
+                        }
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) {
+                            st.o[db][0][r] = fmaf(w0, t0[r], st.o[db][0][r]);
+                            st.o[db][1][r] = fmaf(w1, t1[r], st.o[db][1][r]);
+                        }
+                    }
+                }
+                wave_lds_sync();
+            }
+        }
+    }
+
+    // ---- normalise and write O (bf16) and lse ----
+    uint16_t* O = static_cast<uint16_t*>(a.out) + head;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float lt = st.l[rb] + swap_halves(st.l[rb]);
+        const int row = qa * BLK + 32 * rb + l32;
+        const bool valid = row < a.N;
+        const float inv = valid ? 1.0f / lt : 0.f;
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4) {
+                const int dd = 32 * db + 8 * q4 + 4 * h;
+                uint2 w;
+                w.x = pack_bf16x2(st.o[db][rb][4 * q4 + 0] * inv, st.o[db][rb][4 * q4 + 1] * inv);
+                w.y = pack_bf16x2(st.o[db][rb][4 * q4 + 2] * inv, st.o[db][rb][4 * q4 + 3] * inv);
+                *reinterpret_cast<uint2*>(O + static_cast<size_t>(row) * D + dd) = w;
+            }
+        }
+        const float le = st.le[rb] + swap_halves(st.le[rb]);
+        if (a.lse && h == 0) a.lse[bh * a.N_pad + row] = valid ? (st.m[rb] + __log2f(le)) * LN2 : 0.f;
+    }
+}
+
+template <int COMP>
+hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
+    const size_t lds = (COMP == 1) ? sizeof(LdsOrder1) : sizeof(Lds);
+    const int nq = a.N_pad / BLK;
+    dim3 grid(nq * a.H * a.B);
+    hipLaunchKernelGGL((fwd_bf16_kernel<COMP>), grid, dim3(64), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
+    switch (a.comp) {
+        case -1: return launch_t<-1>(a, s);
+        case 0: return launch_t<0>(a, s);
+        default: return launch_t<1>(a, s);
+    }
+}
+
+}  // namespace sa

@@ -1,0 +1,78 @@
+// Internal kernel argument blocks and launchers (host side of each .hip file).
+// The public C ABI in include/sparse_attn.h validates arguments and calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace sa {
+
+struct PoolArgs {
+    int B, H, N, N_pad, d;
+    const void* q;
+    const void* k;
+    const void* v;
+    float* qbar;
+    float* kbar;
+    float* vbar;
+    int32_t* kcount;
+    void* kmom;       // bf16 [B,H,nb,d,d] value-major, or null
+    float* klam;      // [B,H,nb] or null
+    uint8_t* q8;      // e4m3 copies or null (all or none)
+    uint8_t* k8;
+    uint8_t* v8;
+    int8_t* exp8;     // [B,H,nb,3]
+};
+hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s);
+
+struct RouteArgs {
+    int B, H, nb, d;
+    int mode;
+    int topk;
+    const int32_t* frame_lo;
+    const int32_t* frame_hi;
+    int window, anchors, anchor_phase, step;
+    int n_keep, n_refine;
+    float scale;
+    const float* qbar;
+    const float* kbar;
+    const int32_t* kcount;
+    const float* klam;
+    int32_t* idx;
+    int32_t* cnt;
+    int cap;
+    int32_t* idx2;
+    int32_t* cnt2;
+    int cap2;
+};
+hipError_t launch_route(const RouteArgs& a, hipStream_t s);
+
+struct FwdArgs {
+    int B, H, N, N_pad, d;
+    int comp;                 // -1, 0, 1
+    float scale;
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* kbar;
+    const float* vbar;
+    const int32_t* kcount;
+    const void* kmom;
+    const uint8_t* q8;
+    const uint8_t* k8;
+    const uint8_t* v8;
+    const int8_t* exp8;
+    const int32_t* idx;
+    const int32_t* cnt;
+    int cap;
+    const int32_t* idx2;
+    const int32_t* cnt2;
+    int cap2;
+    void* out;
+    float* lse;
+};
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+
+}  // namespace sa

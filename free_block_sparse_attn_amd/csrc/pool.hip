@@ -1,0 +1,318 @@
+// Block pooling: means (routing features), key counts and the optional
+// per-block statistics the forward pass and the routers read.
+//
+// Page basis: PISA ("PISA: Piecewise Sparse Attention Is Wiser for Efficient
+// Diffusion Transformers", section 2, "Implementation Materielle") precomputes
+// block centroids, value sums and per-block first-order matrices before the
+// attention pass; SVG-EAR (section 2A) approximates skipped blocks by their
+// means; Triage's router works from block statistics.
+//
+// One workgroup (4 waves) per (b, h, block).  The kernel is HBM-bound: every
+// token row is read once with 16-byte coalesced loads and parked in LDS in a
+// column-major (transposed) layout, so that per-column sums, the moment MFMAs
+// and the spreads all read contiguous LDS runs.
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+
+namespace {
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+    static constexpr int PER16 = 4;
+    static __device__ __forceinline__ float get(const u32x4& r, int e) { return __uint_as_float(r[e]); }
+    static __device__ __forceinline__ float raw(const u32x4& r, int e) { return __uint_as_float(r[e]); }
+    static __device__ __forceinline__ float val(float x) { return x; }
+};
+template <> struct Elem<uint16_t> {
+    static constexpr int PER16 = 8;
+    static __device__ __forceinline__ float get(const u32x4& r, int e) {
+        uint32_t w = r[e >> 1];
+        return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+    }
+    static __device__ __forceinline__ uint16_t raw(const u32x4& r, int e) {
+        return static_cast<uint16_t>((e & 1) ? (r[e >> 1] >> 16) : (r[e >> 1] & 0xFFFFu));
+    }
+    static __device__ __forceinline__ float val(uint16_t x) { return bf16_to_f32(x); }
+};
+
+constexpr int THREADS = 256;
+constexpr int TPITCH = BLK + 8;     // transposed row pitch in elements (16-byte multiple)
+
+template <typename T, int D>
+constexpr size_t pool_lds() { return 3 * D * TPITCH * sizeof(T) + (3 * D + 64) * sizeof(float); }
+
+// Block exponent of the e4m3 copies: smallest e with amax * 2^-e <= 448.
+// amax = f * 2^k, f in [0.5, 1): 448 * 2^(k-9) = 0.875 * 2^k.
+__device__ __forceinline__ int e4m3_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int k;
+    float f = frexpf(amax, &k);
+    return (f <= 0.875f) ? k - 9 : k - 8;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
+    using E = Elem<T>;
+    constexpr int PER16 = E::PER16;
+    constexpr int CPR = D / PER16;                 // 16-byte chunks per row
+    constexpr int CHUNKS = BLK * CPR;              // chunks per tensor tile
+    constexpr int PT = CHUNKS / THREADS;           // chunks per thread per tensor
+    static_assert(CHUNKS % THREADS == 0, "tile must split evenly");
+
+    // Transposed staging in the input dtype: xt[tensor][col][token]
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    T* xt = reinterpret_cast<T*>(smem);                                          // 3 * D * TPITCH
+    float* means = reinterpret_cast<float*>(smem + 3 * D * TPITCH * sizeof(T));  // 3 * D
+    float* red = means + 3 * D;                    // 64 scratch floats for reductions
+
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int nb = a.N_pad / BLK;
+    const int n = min(BLK, a.N - BLK * j);
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
+
+    const T* src[3] = {static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v)};
+
+    // Phase 1: coalesced 16-byte row loads (pad rows read as zero).
+    u32x4 reg[3][PT];
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+#pragma unroll
+        for (int c = 0; c < PT; ++c) {
+            const int chunk = tid + THREADS * c;
+            const int row = chunk / CPR;
+            const int col0 = (chunk % CPR) * PER16;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (row < n)
+                z = *reinterpret_cast<const u32x4*>(src[t] + tok0 + static_cast<size_t>(row) * D + col0);
+            reg[t][c] = z;
+        }
+    }
+    // transposed staging
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+#pragma unroll
+        for (int c = 0; c < PT; ++c) {
+            const int chunk = tid + THREADS * c;
+            const int row = chunk / CPR;
+            const int col0 = (chunk % CPR) * PER16;
+#pragma unroll
+            for (int e = 0; e < PER16; ++e)
+                xt[(t * D + col0 + e) * TPITCH + row] = E::raw(reg[t][c], e);
+        }
+    }
+    __syncthreads();
+
+    // Phase 2: per-column fp64 sums in token order, mean = RN32(sum / n).
+    for (int task = tid; task < 3 * D; task += THREADS) {
+        const T* col = xt + task * TPITCH;
+        double acc = 0.0;
+        for (int r = 0; r < n; ++r) acc = acc + static_cast<double>(E::val(col[r]));
+        const float m = static_cast<float>(acc / static_cast<double>(n));
+        means[task] = m;
+        const int t = task / D, i = task % D;
+        float* dst = (t == 0) ? a.qbar : (t == 1) ? a.kbar : a.vbar;
+        dst[(bh * nb + j) * D + i] = m;
+    }
+    if (b == 0 && h == 0 && tid == 0) a.kcount[j] = n;
+    __syncthreads();
+
+    // Phase 3 (optional): spreads lambda = ln(r_k r_v), fp64.
+    if (a.klam) {
+        double part[2] = {0.0, 0.0};
+        for (int task = tid; task < 2 * D; task += THREADS) {
+            const int t = 1 + task / D;            // K then V
+            const T* col = xt + (t * D + task % D) * TPITCH;
+            const double mu = static_cast<double>(means[t * D + task % D]);
+            double s = 0.0;
+            for (int r = 0; r < n; ++r) {
+                const double dv = static_cast<double>(E::val(col[r])) - mu;
+                s = fma(dv, dv, s);
+            }
+            part[task / D] += s;
+        }
+        // wave reduction then across the 4 waves
+        for (int p = 0; p < 2; ++p) {
+            double v = part[p];
+            for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
+            part[p] = v;
+        }
+        double* dred = reinterpret_cast<double*>(red);
+        if ((tid & 63) == 0) {
+            dred[(tid >> 6) * 2 + 0] = part[0];
+            dred[(tid >> 6) * 2 + 1] = part[1];
+        }
+        __syncthreads();
+        if (tid == 0) {
+            double rk = 0.0, rv = 0.0;
+            for (int w = 0; w < THREADS / 64; ++w) { rk += dred[2 * w]; rv += dred[2 * w + 1]; }
+            a.klam[bh * nb + j] = static_cast<float>(0.5 * log(rk) + 0.5 * log(rv));
+        }
+        __syncthreads();
+    }
+
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        // Phase 4 (optional): value-major moment kmom[o][i] = sum_n v_n[o] (k_n[i] - kbar[i])
+        // via bf16 MFMA 32x32x16; centred keys are split hi + lo so the
+        // product keeps ~16 mantissa bits.
+        if (a.kmom) {
+            const int w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+            const int icol = 32 * w + l32;                 // this wave's i block
+            const float kb = means[D + icol];
+            f32x16 acc[4];
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int t0 = 16 * ks + 8 * hl;
+                bf16x8 bhi, blo;
+                const T* kc = xt + (D + icol) * TPITCH + t0;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float x = (t0 + e < n) ? E::val(kc[e]) - kb : 0.0f;
+                    const __bf16 hi = static_cast<__bf16>(x);
+                    bhi[e] = hi;
+                    blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+                }
+#pragma unroll
+                for (int ob = 0; ob < 4; ++ob) {
+                    const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (2 * D + 32 * ob + l32) * TPITCH + t0);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[ob], 0, 0, 0);
+                    acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
+                }
+            }
+            uint16_t* mom = static_cast<uint16_t*>(a.kmom) + (bh * nb + j) * static_cast<size_t>(D) * D;
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) {
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int o = 32 * ob + 8 * (r >> 2) + 4 * hl + (r & 3);
+                    mom[o * D + icol] = f32_to_bf16(acc[ob][r]);
+                }
+            }
+        }
+
+        // Phase 5 (optional): per-block power-of-two scaled e4m3 copies.
+        if (a.q8) {
+            uint8_t* dst8[3] = {a.q8, a.k8, a.v8};
+            float amax[3] = {0.f, 0.f, 0.f};
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+#pragma unroll
+                for (int c = 0; c < PT; ++c)
+#pragma unroll
+                    for (int e = 0; e < PER16; ++e) amax[t] = fmaxf(amax[t], fabsf(E::get(reg[t][c], e)));
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                for (int off = 32; off > 0; off >>= 1) amax[t] = fmaxf(amax[t], __shfl_xor(amax[t], off));
+            if ((tid & 63) == 0)
+                for (int t = 0; t < 3; ++t) red[(tid >> 6) * 3 + t] = amax[t];
+            __syncthreads();
+            int ex[3];
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+                float m = 0.f;
+                for (int w = 0; w < THREADS / 64; ++w) m = fmaxf(m, red[w * 3 + t]);
+                ex[t] = e4m3_block_exponent(m);
+            }
+            if (tid < 3) a.exp8[(bh * nb + j) * 3 + tid] = static_cast<int8_t>(ex[tid]);
+#pragma unroll
+            for (int t = 0; t < 3; ++t) {
+#pragma unroll
+                for (int c = 0; c < PT; ++c) {
+                    const int chunk = tid + THREADS * c;
+                    const int row = chunk / CPR;
+                    const int col0 = (chunk % CPR) * PER16;
+                    uint32_t w0 = 0, w1 = 0;
+                    w0 = pack_fp8x2<false>(ldexpf(E::get(reg[t][c], 0), -ex[t]), ldexpf(E::get(reg[t][c], 1), -ex[t]), w0);
+                    w0 = pack_fp8x2<true>(ldexpf(E::get(reg[t][c], 2), -ex[t]), ldexpf(E::get(reg[t][c], 3), -ex[t]), w0);
+                    w1 = pack_fp8x2<false>(ldexpf(E::get(reg[t][c], 4), -ex[t]), ldexpf(E::get(reg[t][c], 5), -ex[t]), w1);
+                    w1 = pack_fp8x2<true>(ldexpf(E::get(reg[t][c], 6), -ex[t]), ldexpf(E::get(reg[t][c], 7), -ex[t]), w1);
+                    if (row >= n) { w0 = 0; w1 = 0; }
+                    uint2 out = {w0, w1};
+                    *reinterpret_cast<uint2*>(dst8[t] + tok0 + static_cast<size_t>(row) * D + col0) = out;
+                }
+            }
+        }
+    }
+}
+
+// Means-only pooling (no optional statistics): each lane owns one 16-byte
+// column chunk of one block of one tensor and folds the block's rows into fp64
+// accumulators in token order (the same contract as above).  No LDS, small
+// register footprint, many waves in flight: this is the HBM-streaming form.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
+    using E = Elem<T>;
+    constexpr int PER16 = E::PER16;
+    constexpr int CPR = D / PER16;                 // chunks per row
+    constexpr int BPW = 64 / CPR;                  // blocks per wave
+    constexpr int UNROLL = 8;
+    const int tensor = blockIdx.y;
+    const size_t bh = blockIdx.z;
+    const int nb = a.N_pad / BLK;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int j = (blockIdx.x * 4 + wave) * BPW + lane / CPR;
+    if (j >= nb) return;
+    const int col0 = (lane % CPR) * PER16;
+    const int n = min(BLK, a.N - BLK * j);
+    const T* src = static_cast<const T*>(tensor == 0 ? a.q : tensor == 1 ? a.k : a.v) +
+                   (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D + col0;
+    double acc[PER16];
+#pragma unroll
+    for (int e = 0; e < PER16; ++e) acc[e] = 0.0;
+    for (int r0 = 0; r0 < n; r0 += UNROLL) {
+        u32x4 x[UNROLL];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (r0 + u < n) z = *reinterpret_cast<const u32x4*>(src + static_cast<size_t>(r0 + u) * D);
+            x[u] = z;
+        }
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+            if (r0 + u < n) {
+#pragma unroll
+                for (int e = 0; e < PER16; ++e) acc[e] = acc[e] + static_cast<double>(E::get(x[u], e));
+            }
+        }
+    }
+    float* dst = (tensor == 0 ? a.qbar : tensor == 1 ? a.kbar : a.vbar) + (bh * nb + j) * D + col0;
+#pragma unroll
+    for (int e = 0; e < PER16; e += 4) {
+        float4 m;
+        m.x = static_cast<float>(acc[e] / static_cast<double>(n));
+        m.y = static_cast<float>(acc[e + 1] / static_cast<double>(n));
+        m.z = static_cast<float>(acc[e + 2] / static_cast<double>(n));
+        m.w = static_cast<float>(acc[e + 3] / static_cast<double>(n));
+        *reinterpret_cast<float4*>(dst + e) = m;
+    }
+    if (tensor == 0 && bh == 0 && (lane % CPR) == 0) a.kcount[j] = n;
+}
+
+template <typename T, int D>
+hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
+    if (!a.kmom && !a.klam && !a.q8) {
+        constexpr int BPW = 64 / (D / Elem<T>::PER16);
+        const int nb = a.N_pad / BLK;
+        dim3 grid((nb + 4 * BPW - 1) / (4 * BPW), 3, a.B * a.H);
+        hipLaunchKernelGGL((pool_means_kernel<T, D>), grid, dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
+    const size_t lds = pool_lds<T, D>();
+    dim3 grid(a.N_pad / BLK, a.H, a.B);
+    hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
+    if (bf16) return a.d == 128 ? launch_pool_t<uint16_t, 128>(a, s) : launch_pool_t<uint16_t, 64>(a, s);
+    return a.d == 128 ? launch_pool_t<float, 128>(a, s) : launch_pool_t<float, 64>(a, s);
+}
+
+}  // namespace sa

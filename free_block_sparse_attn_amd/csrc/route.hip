@@ -1,0 +1,300 @@
+// Block routing kernels: pooled-score top-k, Triage tiers, LVSA mask.
+//
+// Scores follow one arithmetic contract so the selection is reproducible bit
+// for bit: s(a, j) = sum_i qbar[a,i] * kbar[j,i] with fp64 fused multiply-adds
+// in i order (the fp32 x fp32 products are exact in fp64, so the fusion does
+// not change a bit).  A selection takes the first k elements of the total
+// order (-key, j): keys are mapped to order-preserving 64-bit integers and a
+// wave runs an 8-pass MSB radix select (256-bin LDS histogram per pass) to find
+// the k-th key; ties at that key go to the lowest block indices.  Lists are
+// written ascending by ballot compaction.
+//
+// Page basis: PISA's top-k critical set per query block ("PISA: Piecewise
+// Sparse Attention Is Wiser for Efficient Diffusion Transformers", section 2,
+// "Algorithme Central"); Triage's router choosing skip / skim / refine from
+// block statistics ("Triage: Skip, Skim, or Refine Attention Tiles in Video
+// Diffusion Transformers", "Un routage fonde sur l'erreur estimee"); LVSA's
+// A(t) = G_s U W(t) ("LVSA: Training-Free Sparse Attention for Long Video
+// Diffusion", section 2, "Mecanisme Central").
+#include "common.h"
+#include "launch.h"
+
+namespace sa {
+
+namespace {
+
+constexpr int THREADS = 256;
+constexpr int WAVES = THREADS / 64;
+
+__device__ __forceinline__ uint64_t order_key(double s) {
+    if (s == 0.0) s = 0.0;                                  // -0 sorts as +0
+    const uint64_t b = static_cast<uint64_t>(__double_as_longlong(s));
+    return (b >> 63) ? ~b : (b | (1ull << 63));
+}
+
+__device__ __forceinline__ void wave_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+struct Threshold {
+    uint64_t key;     // the k-th key in the order (-key, j)
+    int need;         // how many elements equal to `key` are taken (lowest j first)
+};
+
+// k-th largest key among candidates (key != 0 when `cand_nonzero`), k >= 1,
+// k <= number of candidates.  One wave; `hist` is 256 words of wave-private LDS.
+__device__ Threshold radix_select(const uint64_t* keys, int nb, int k, uint32_t* hist, bool cand_nonzero) {
+    const int lane = lane_id();
+    uint64_t prefix = 0, pmask = 0;
+    int kk = k;
+    for (int shift = 56; shift >= 0; shift -= 8) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
+        wave_sync();
+        for (int j = lane; j < nb; j += 64) {
+            const uint64_t key = keys[j];
+            const bool cand = !cand_nonzero || key != 0ull;
+            if (cand && (key & pmask) == prefix)
+                atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
+        }
+        wave_sync();
+        uint32_t c[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
+        const uint32_t own = c[0] + c[1] + c[2] + c[3];
+        uint32_t suf = own;                                  // sum over lanes >= lane
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const uint32_t y = __shfl_down(suf, off);
+            if (lane + off < 64) suf += y;
+        }
+        const uint32_t above = suf - own;                    // digits > 4*lane+3
+        // the lane whose digit range contains the k-th key
+        const bool mine = above < static_cast<uint32_t>(kk) && static_cast<uint32_t>(kk) <= suf;
+        int digit = 0;
+        uint32_t gt = 0;
+        if (mine) {
+            uint32_t run = above;
+            for (int q = 3; q >= 0; --q) {
+                if (run + c[q] >= static_cast<uint32_t>(kk)) { digit = 4 * lane + q; gt = run; break; }
+                run += c[q];
+            }
+        }
+        const uint64_t who = __ballot(mine);
+        const int src = __ffsll(static_cast<long long>(who)) - 1;
+        digit = __shfl(digit, src);
+        gt = __shfl(gt, src);
+        kk -= static_cast<int>(gt);
+        prefix |= static_cast<uint64_t>(digit) << shift;
+        pmask |= 0xFFull << shift;
+        wave_sync();
+    }
+    return Threshold{prefix, kk};
+}
+
+// Writes the selected indices ascending into out[0..cap), -1 after, returns the count.
+// `excl` (optional): a second threshold whose selected elements are excluded.
+__device__ int compact_selection(const uint64_t* keys, int nb, Threshold t, bool cand_nonzero,
+                                 int32_t* out, int cap, bool none) {
+    const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int base = 0, eqseen = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        const uint64_t key = (j < nb) ? keys[j] : 0ull;
+        const bool cand = (j < nb) && (!cand_nonzero || key != 0ull) && !none;
+        const bool gt = cand && key > t.key;
+        const bool eq = cand && key == t.key;
+        const uint64_t eqm = __ballot(eq);
+        const int eqrank = eqseen + __popcll(eqm & lt);
+        const bool sel = gt || (eq && eqrank < t.need);
+        const uint64_t selm = __ballot(sel);
+        const int pos = base + __popcll(selm & lt);
+        if (sel && pos < cap) out[pos] = j;
+        base += __popcll(selm);
+        eqseen += __popcll(eqm);
+    }
+    for (int p = base + lane; p < cap; p += 64) out[p] = -1;
+    return base;
+}
+
+// fp64 scores of R query blocks against all key blocks, row-major in LDS as keys.
+template <int R>
+__device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, uint64_t* keyE,
+                           uint64_t* keyW, int nbp) {
+    const int d = a.d, nb = a.nb, tid = threadIdx.x;
+    for (int x = tid; x < R * d; x += THREADS) {
+        const int r = x / d, i = x % d;
+        const int row = row0 + r;
+        qs[x] = (row < nb) ? static_cast<double>(a.qbar[(bh * nb + row) * d + i]) : 0.0;
+    }
+    __syncthreads();
+    const bool triage = a.mode == 2;
+    const double sc = static_cast<double>(a.scale);
+    for (int j = tid; j < nb; j += THREADS) {
+        double acc[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r] = 0.0;
+        const float4* kr = reinterpret_cast<const float4*>(a.kbar + (bh * nb + j) * d);
+        for (int i4 = 0; i4 < d / 4; ++i4) {
+            const float4 kv = kr[i4];
+            const double kd[4] = {static_cast<double>(kv.x), static_cast<double>(kv.y),
+                                  static_cast<double>(kv.z), static_cast<double>(kv.w)};
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * d + 4 * i4 + u], kd[u], acc[r]);
+            }
+        }
+        if (!triage) {
+#pragma unroll
+            for (int r = 0; r < R; ++r) keyE[r * nbp + j] = order_key(acc[r]);
+        } else {
+            const double lam = static_cast<double>(a.klam[bh * nb + j]);
+            const double lgn = log(static_cast<double>(a.kcount[j]));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const double ss = __dmul_rn(sc, acc[r]);
+                keyE[r * nbp + j] = order_key(__dadd_rn(ss, lam));
+                keyW[r * nbp + j] = order_key(__dadd_rn(ss, lgn));
+            }
+        }
+    }
+    __syncthreads();
+}
+
+template <int R>
+__global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+    const int nbp = (a.nb + 63) & ~63;
+    const bool triage = a.mode == 2;
+    double* qs = reinterpret_cast<double*>(smem);                            // R * d
+    uint64_t* keyE = reinterpret_cast<uint64_t*>(qs + R * a.d);              // R * nbp
+    uint64_t* keyW = keyE + R * nbp;                                         // R * nbp (triage)
+    uint32_t* hist = reinterpret_cast<uint32_t*>(keyW + (triage ? R * nbp : 0));  // WAVES * 256
+
+    const int row0 = blockIdx.x * R;
+    const size_t bh = static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y;
+    score_rows<R>(a, bh, row0, qs, keyE, keyW, nbp);
+
+    const int w = threadIdx.x >> 6;
+    uint32_t* myhist = hist + 256 * w;
+    for (int r = w; r < R; r += WAVES) {
+        const int row = row0 + r;
+        if (row >= a.nb) break;
+        const size_t rowid = bh * a.nb + row;
+        uint64_t* kE = keyE + r * nbp;
+        if (!triage) {
+            const Threshold t = radix_select(kE, a.nb, a.topk, myhist, false);
+            const int c = compact_selection(kE, a.nb, t, false, a.idx + rowid * a.cap, a.cap, false);
+            if (lane_id() == 0) a.cnt[rowid] = c;
+        } else {
+            uint64_t* kW = keyW + r * nbp;
+            // kept = first n_keep by e_skip; blank the w-keys of the others
+            const Threshold tk = radix_select(kE, a.nb, a.n_keep, myhist, false);
+            {
+                const int lane = lane_id();
+                const uint64_t lt = (1ull << lane) - 1ull;
+                int eqseen = 0;
+                for (int j0 = 0; j0 < a.nb; j0 += 64) {
+                    const int j = j0 + lane;
+                    const uint64_t key = (j < a.nb) ? kE[j] : 0ull;
+                    const bool eq = (j < a.nb) && key == tk.key;
+                    const uint64_t eqm = __ballot(eq);
+                    const int eqrank = eqseen + __popcll(eqm & lt);
+                    const bool kept = (j < a.nb) && (key > tk.key || (eq && eqrank < tk.need));
+                    if (j < a.nb && !kept) kW[j] = 0ull;
+                    eqseen += __popcll(eqm);
+                }
+                wave_sync();
+            }
+            // refine = first n_refine of the kept blocks by w
+            const bool none = a.n_refine == 0;
+            Threshold tr{~0ull, 0};
+            if (!none) tr = radix_select(kW, a.nb, a.n_refine, myhist, true);
+            const int c1 = compact_selection(kW, a.nb, tr, true, a.idx + rowid * a.cap, a.cap, none);
+            // skim = kept and not refine: blank the refine keys, take every remaining candidate
+            {
+                const int lane = lane_id();
+                const uint64_t lt = (1ull << lane) - 1ull;
+                int eqseen = 0;
+                for (int j0 = 0; j0 < a.nb; j0 += 64) {
+                    const int j = j0 + lane;
+                    const uint64_t key = (j < a.nb) ? kW[j] : 0ull;
+                    const bool cand = (j < a.nb) && key != 0ull && !none;
+                    const bool eq = cand && key == tr.key;
+                    const uint64_t eqm = __ballot(eq);
+                    const int eqrank = eqseen + __popcll(eqm & lt);
+                    const bool ref = cand && (key > tr.key || (eq && eqrank < tr.need));
+                    if (ref) kW[j] = 0ull;
+                    eqseen += __popcll(eqm);
+                }
+                wave_sync();
+            }
+            const Threshold all{1ull, 0};             // every candidate has key > 1
+            const int c2 = compact_selection(kW, a.nb, all, true, a.idx2 + rowid * a.cap2, a.cap2, false);
+            if (lane_id() == 0) { a.cnt[rowid] = c1; a.cnt2[rowid] = c2; }
+        }
+        wave_sync();
+    }
+}
+
+// LVSA: one wave per (b, h, query block); pure integer work.
+__global__ __launch_bounds__(64) void route_lvsa_kernel(RouteArgs a) {
+    const int row = blockIdx.x;
+    const size_t rowid = (static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y) * a.nb + row;
+    const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int lo = a.frame_lo[row] - a.window, hi = a.frame_hi[row] + a.window;
+    const int P = a.anchors > 0 ? a.nb / a.anchors : 0;
+    const int off = P > 0 ? (a.anchor_phase + a.step) % P : 0;
+    int32_t* out = a.idx + rowid * a.cap;
+    int base = 0;
+    for (int j0 = 0; j0 < a.nb; j0 += 64) {
+        const int j = j0 + lane;
+        bool sel = false;
+        if (j < a.nb) {
+            sel = a.frame_lo[j] <= hi && a.frame_hi[j] >= lo;
+            if (P > 0 && j >= off && (j - off) % P == 0 && (j - off) / P < a.anchors) sel = true;
+        }
+        const uint64_t m = __ballot(sel);
+        const int pos = base + __popcll(m & lt);
+        if (sel && pos < a.cap) out[pos] = j;
+        base += __popcll(m);
+    }
+    for (int p = base + lane; p < a.cap; p += 64) out[p] = -1;
+    if (lane == 0) a.cnt[rowid] = base;
+}
+
+template <int R>
+hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
+    const int nbp = (a.nb + 63) & ~63;
+    const size_t lds = R * a.d * sizeof(double) + (a.mode == 2 ? 2 : 1) * R * nbp * sizeof(uint64_t) +
+                       WAVES * 256 * sizeof(uint32_t);
+    dim3 grid((a.nb + R - 1) / R, a.H, a.B);
+    hipLaunchKernelGGL((route_scored_kernel<R>), grid, dim3(THREADS), lds, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+    if (a.mode == 1) {
+        dim3 grid(a.nb, a.H, a.B);
+        hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64), 0, s, a);
+        return hipGetLastError();
+    }
+    // rows per workgroup: as many as fit a 64 KiB key budget, at most 16
+    const int nbp = (a.nb + 63) & ~63;
+    const size_t per_row = (a.mode == 2 ? 2 : 1) * nbp * sizeof(uint64_t);
+    const size_t budget = 64 * 1024;
+    if (per_row * 16 <= budget) return launch_scored<16>(a, s);
+    if (per_row * 8 <= budget) return launch_scored<8>(a, s);
+    if (per_row * 4 <= budget) return launch_scored<4>(a, s);
+    if (per_row * 2 <= budget) return launch_scored<2>(a, s);
+    return launch_scored<1>(a, s);
+}
+
+}  // namespace sa

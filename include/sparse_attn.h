@@ -1,0 +1,226 @@
+/*
+ * sparse_attn.h - C ABI of the MI355X (gfx950) compensated block-sparse
+ * attention library: pool -> route -> fused forward.
+ *
+ * The method.  Self-attention over a video token sequence is cut into
+ * 64-token blocks.  For every query block only some key blocks are computed
+ * exactly; every other key block is not dropped but compensated inside the
+ * same softmax normalisation:
+ *   - zeroth order: the block's n_j keys and values are replaced by their
+ *     means, i.e. a pseudo-logit q.k_bar_j + ln n_j with value v_bar_j
+ *     (page "SVG-EAR: Parameter-Free Linear Compensation for Sparse Video
+ *     Generation via Error-aware Routing", section 2A; page "PISA: Piecewise
+ *     Sparse Attention Is Wiser for Efficient Diffusion Transformers",
+ *     section 2 "Algorithme Central", zeroth-order block term
+ *     alpha_{t,j} * sum_n v_{j,n} with alpha_{t,j} = exp(q_t k_bar_j));
+ *   - first order (optional): PISA's block Taylor term
+ *     exp(q.k_bar_j) * (q^T H_j) with the per-block moment
+ *     H_j = sum_n (k_n - k_bar_j) v_n^T (PISA section 2, per-block
+ *     first-order matrices);
+ *   - a low-precision tier (optional): key blocks computed from fp8 e4m3
+ *     copies (page "Triage: Skip, Skim, or Refine Attention Tiles in Video
+ *     Diffusion Transformers", the skim tier of its per-tile choice).
+ * Routing chooses the exact blocks by top-k on pooled block scores (PISA),
+ * by LVSA's local window plus rotating global anchors (page "LVSA:
+ * Training-Free Sparse Attention for Long Video Diffusion", section 2
+ * "Mecanisme Central"), or by Triage's three tiers.
+ *
+ * Conventions shared by every call
+ *   - Tensors are dense, contiguous, row-major device buffers owned by the
+ *     caller; the library never allocates, frees or retains them and keeps
+ *     no state between calls.
+ *   - Token tensors are [B, H, N_pad, d] with N_pad = 64 * ceil(N / 64);
+ *     tokens N .. N_pad-1 are padding: they are never read into a result
+ *     and their contents may be anything.  nb = N_pad / 64 blocks; block j
+ *     holds n_j = min(64, N - 64 j) valid tokens.
+ *   - Every argument is validated on the host before any HIP call.  On a
+ *     validation error nothing is launched and no output is touched.
+ *   - Work is enqueued asynchronously on `stream` (0 = the null stream).
+ *     Launch failures return SA_ERR_HIP; faults inside kernels surface at
+ *     the caller's next synchronisation, as for any HIP library.
+ *   - Every device pointer must be 16-byte aligned.
+ *   - B == 0, H == 0 or N == 0 is a valid empty problem: nothing is
+ *     launched and SA_OK is returned.
+ *   - Calls are thread-safe; the last-error text is thread-local.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPARSE_ATTN_ABI_VERSION 1
+#define SPARSE_ATTN_BLOCK 64
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_INVALID_ARG = 1,   /* a null, misaligned, negative or inconsistent argument */
+    SA_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    SA_ERR_HIP = 3            /* a HIP launch failed; see sparse_attn_last_error() */
+} sa_status;
+
+typedef enum {
+    SA_F32 = 0,               /* fp32 token tensors */
+    SA_BF16 = 1               /* bf16 token tensors (the MFMA path) */
+} sa_dtype;
+
+typedef enum {
+    SA_COMP_DROP = -1,        /* unselected blocks contribute nothing */
+    SA_COMP_ORDER0 = 0,       /* centroid term n_j exp(q.k_bar_j) v_bar_j */
+    SA_COMP_ORDER1_BLOCK = 1  /* centroid term + per-block Taylor term with H_j */
+} sa_comp;
+
+typedef enum {
+    SA_ROUTE_TOPK = 0,
+    SA_ROUTE_LVSA = 1,
+    SA_ROUTE_TRIAGE = 2
+} sa_route_mode;
+
+/* Problem shape.  d must be 64 or 128. */
+typedef struct {
+    int32_t B, H, N, N_pad, d;
+} sa_shape;
+
+/*
+ * sparse_attn_pool - per-block statistics (the precompute step of PISA's
+ * fused pipeline, section 2 "Implementation Materielle": centroids, value
+ * sums and first-order matrices are computed before the attention pass).
+ *
+ * Inputs  q, k, v        dtype [B,H,N_pad,d]
+ * Outputs (required)
+ *   qbar, kbar, vbar     fp32 [B,H,nb,d]  block means over valid tokens.
+ *                        Contract: fp64 sum of the valid tokens in increasing
+ *                        token order from +0.0, fp64 division by n_j, then
+ *                        round-to-nearest-even to fp32.  These are the
+ *                        routing features; they are bit-reproducible.
+ *   kcount               int32 [nb]       n_j (same for every b, h).
+ * Outputs (optional, NULL to skip)
+ *   kmom                 bf16 [B,H,nb,d,d]  moment of block j stored
+ *                        value-major: kmom[..., o, i] =
+ *                        sum_n (k_n[i] - k_bar_j[i]) v_n[o]   (H_j transposed).
+ *                        bf16 inputs only.
+ *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
+ *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
+ *                        omission-error statistic); -inf for 1-token blocks.
+ *   q8, k8, v8, exp8     fp8 e4m3 (OCP) copies uint8 [B,H,N_pad,d] with one
+ *                        power-of-two scale per block and tensor:
+ *                        x8 = e4m3_rne(x * 2^-e), e = smallest integer with
+ *                        amax_block * 2^-e <= 448; exp8 int8 [B,H,nb,3] holds
+ *                        e for (q, k, v).  Pad rows are written as 0.  All
+ *                        four pointers or none.  bf16 inputs only.
+ */
+sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
+                           const void* q, const void* k, const void* v,
+                           float* qbar, float* kbar, float* vbar, int32_t* kcount,
+                           void* kmom, float* klam,
+                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
+                           hipStream_t stream);
+
+/* Routing request.  Unused fields are ignored by the other modes. */
+typedef struct {
+    int32_t mode;                 /* sa_route_mode */
+    /* SA_ROUTE_TOPK: keep `topk` (1..nb) key blocks per query block. */
+    int32_t topk;
+    /* SA_ROUTE_LVSA: device int32 [nb] first/last latent frame of each block. */
+    const int32_t* frame_lo;
+    const int32_t* frame_hi;
+    int32_t window;               /* +- frames around the query block's frames */
+    int32_t anchors;              /* rotating anchor key blocks (0..nb) */
+    int32_t anchor_phase;         /* seeded offset o >= 0 */
+    int32_t step;                 /* denoising step s >= 0 */
+    /* SA_ROUTE_TRIAGE: tiers per query block. */
+    int32_t n_keep;               /* refine + skim blocks (1..nb) */
+    int32_t n_refine;             /* refine blocks (0..n_keep) */
+    float scale;                  /* softmax scale used in the router's keys */
+} sa_route_spec;
+
+/*
+ * sparse_attn_route - choose the key blocks of every query block.
+ *
+ * Scores (TOPK, TRIAGE): s(a, j) = sum_i qbar[a,i] * kbar[j,i], fp64,
+ * accumulated in i = 0..d-1 order (products of fp32 values are exact in
+ * fp64).  Selections use the total order (-key, j): ties go to the lower
+ * block index.  Lists are written ascending, padded with -1 up to `cap`.
+ *
+ *   TOPK   idx/cnt = the topk best blocks by s (PISA's top-k critical set);
+ *          cap >= topk.  idx2/cnt2 unused (may be NULL).
+ *   LVSA   idx/cnt = {j : [lo_j, hi_j] meets [lo_a - window, hi_a + window]}
+ *          U {((phase + step) mod P) + i P : i < anchors}, P = nb / anchors.
+ *          A row longer than cap is truncated to its first cap blocks while
+ *          cnt holds the full length; sparse_attn_lvsa_capacity() gives the
+ *          cap that avoids truncation.
+ *   TRIAGE e_skip = fl(fl(scale s) + lambda_j), w = fl(fl(scale s) + ln n_j)
+ *          (fp64).  The first n_keep blocks by (-e_skip, j) are kept; of
+ *          those the first n_refine by (-w, j) go to idx/cnt (refine, exact
+ *          bf16, cap >= n_refine) and the rest to idx2/cnt2 (skim, fp8,
+ *          cap2 >= n_keep - n_refine).  Needs klam and kcount.
+ *
+ * qbar, kbar  fp32 [B,H,nb,d] (sparse_attn_pool outputs)
+ * kcount      int32 [nb]      (TRIAGE)   klam fp32 [B,H,nb] (TRIAGE)
+ * idx         int32 [B,H,nb,cap]   cnt int32 [B,H,nb]
+ * idx2        int32 [B,H,nb,cap2]  cnt2 int32 [B,H,nb]  (TRIAGE)
+ */
+sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec,
+                            const float* qbar, const float* kbar,
+                            const int32_t* kcount, const float* klam,
+                            int32_t* idx, int32_t* cnt, int32_t cap,
+                            int32_t* idx2, int32_t* cnt2, int32_t cap2,
+                            hipStream_t stream);
+
+/* Host helper: the longest LVSA row for host copies of the frame ranges. */
+int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* frame_hi_host,
+                                  int32_t nb, int32_t window, int32_t anchors);
+
+/*
+ * sparse_attn_fwd - fused compensated block-sparse attention forward.
+ *
+ * For query t in block a with exact list E (idx), skim list M (idx2) and
+ * the remaining blocks U, computes o_t = N_t / D_t in one online softmax
+ * (PISA section 2: the approximations enter numerator and denominator of a
+ * single normalisation):
+ *   exact   sum_{j in E} sum_n e^{scale q.k_n} (v_n)              bf16 MFMA
+ *   skim    sum_{j in M} e4m3 logits and e4m3 P V via fp8 MFMA with block
+ *           scales; P is quantised per row and tile against a power of two
+ *           2^ceil(max L); D takes the unquantised weights
+ *   order0  sum_{j in U} n_j e^{scale q.k_bar_j} (v_bar_j)         comp >= 0
+ *   order1  sum_{j in U} e^{scale q.k_bar_j} scale q^T H_j  (N only)  comp == 1
+ *
+ * q, k, v    dtype [B,H,N_pad,d]        kbar, vbar fp32 [B,H,nb,d]
+ * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d,d] (comp == 1)
+ * q8, k8, v8, exp8                      from sparse_attn_pool (skim only)
+ * idx, cnt, cap     exact lists (ascending, entries in [0, nb))
+ * idx2, cnt2, cap2  skim lists, or NULL / 0 when there is no skim tier
+ * out        dtype [B,H,N_pad,d]: fp32 accumulation rounded to the output
+ *            dtype (RNE); pad rows are written as 0.
+ * lse        fp32 [B,H,N_pad] natural-log normaliser ln D_t, or NULL;
+ *            pad rows are written as 0.
+ * A row's count is clamped to its cap.  Every row must hold at least one
+ * exact or skim block when comp == SA_COMP_DROP.
+ * Supported: SA_F32 with d in {64, 128} (no skim); SA_BF16 with d == 128.
+ */
+sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale,
+                          const void* q, const void* k, const void* v,
+                          const float* kbar, const float* vbar, const int32_t* kcount,
+                          const void* kmom,
+                          const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                          const int8_t* exp8,
+                          const int32_t* idx, const int32_t* cnt, int32_t cap,
+                          const int32_t* idx2, const int32_t* cnt2, int32_t cap2,
+                          void* out, float* lse, hipStream_t stream);
+
+/* Static text for a status code. */
+const char* sparse_attn_status_string(sa_status status);
+/* Detail of the calling thread's last failure ("" if none). */
+const char* sparse_attn_last_error(void);
+/* SPARSE_ATTN_ABI_VERSION of the loaded library. */
+int32_t sparse_attn_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

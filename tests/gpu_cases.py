@@ -1,0 +1,86 @@
+"""Shared helpers of the GPU parity tests: seeded inputs on the device, the
+oracle on the same values, and the comparison bars."""
+
+import numpy as np
+import torch
+
+from oracle import attention, pooling, routing
+from workloads import make_qkv, block_frame_ranges, lvsa_anchor_phase
+
+BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs
+F32_TOL = 1e-4       # max |out - oracle| for fp32 outputs
+LSE_TOL = {"bf16": 2e-3, "f32": 1e-5}
+
+
+def to_device(wl, q, k, v):
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    return [torch.from_numpy(x).to(dt).cuda() for x in (q, k, v)]
+
+
+def inputs(wl, heads=None):
+    """numpy fp32 (exact input values) and device tensors of a workload."""
+    q, k, v, coords = make_qkv(wl, heads=heads)
+    return (q, k, v), to_device(wl, q, k, v), coords
+
+
+SKIM_BUILT = False      # the fp8 skim tier of the forward pass
+
+
+def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
+    """pool -> route -> fwd through the C ABI; returns dict of numpy results."""
+    import free_block_sparse_attn_amd as fbsa
+    q, k, v = dev_qkv
+    N = wl.N
+    pooled = fbsa.sparse_attn_pool(q, k, v, N, moments=wl.comp == 1,
+                                   spreads=wl.rule == "triage", fp8=wl.rule == "triage")
+    idx2 = cnt2 = None
+    if wl.rule == "topk":
+        idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk)
+    elif wl.rule == "lvsa":
+        lo, hi = block_frame_ranges(coords)
+        cap = fbsa.sparse_attn_lvsa_capacity(lo, hi, wl.window, wl.anchors)
+        idx, cnt, _, _ = fbsa.sparse_attn_route(
+            pooled, N, fbsa.SA_ROUTE_LVSA, frame_lo=torch.from_numpy(lo).cuda(),
+            frame_hi=torch.from_numpy(hi).cuda(), window=wl.window, anchors=wl.anchors,
+            anchor_phase=lvsa_anchor_phase(wl.wid, wl.anchor_period), step=step, cap=cap)
+    else:
+        idx, cnt, idx2, cnt2 = fbsa.sparse_attn_route(
+            pooled, N, fbsa.SA_ROUTE_TRIAGE, n_keep=wl.n_keep, n_refine=wl.n_refine, scale=scale)
+    run_fwd = wl.rule != "triage" or SKIM_BUILT
+    if run_fwd:
+        out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2)
+    torch.cuda.synchronize()
+    res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
+    res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
+    if idx2 is not None:
+        res["idx2"], res["cnt2"] = idx2.cpu().numpy(), cnt2.cpu().numpy()
+    if run_fwd:
+        res["out"] = out.float().cpu().numpy()
+        res["lse"] = lse.cpu().numpy()
+    return res
+
+
+def oracle_pool(wl, q, k, v):
+    return pooling.pool(q, k, v, wl.N, moments=wl.comp == 1, spreads=wl.rule == "triage",
+                        fp8=wl.rule == "triage")
+
+
+def lists_of(idx, cnt, b, h, a):
+    return idx[b, h, a, :cnt[b, h, a]]
+
+
+def oracle_rows(wl, q, k, v, pooled, res, rows, scale=1.0):
+    """Oracle (o, lse) of the sampled (b, h, a) query blocks, with the GPU's lists."""
+    out = {}
+    for (b, h, a) in rows:
+        r0, r1 = 64 * a, min(wl.N, 64 * a + 64)
+        ex = lists_of(res["idx"], res["cnt"], b, h, a) if res["idx"].shape[-1] else []
+        sk = lists_of(res["idx2"], res["cnt2"], b, h, a) if "idx2" in res else ()
+        fp8 = None
+        if len(sk):
+            fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
+        kmom = pooled["kmom"][b, h] if wl.comp == 1 else None
+        out[(b, h, a)] = attention.rule_block(
+            q[b, h, r0:r1], k[b, h], v[b, h], wl.N, scale, wl.comp, pooled["kbar64"][b, h],
+            pooled["vbar64"][b, h], pooled["kcount"], ex, sk, kmom, fp8, a)
+    return out

