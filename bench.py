@@ -50,8 +50,11 @@ def kernel_traffic():
         return None
 
 
+CPU_HEADS = 6
+
+
 def cpu_baseline(wl, q, k, v):
-    """fp64 oracle on one head of the layer (pool, route, compensated rule)."""
+    """fp64 oracle on CPU_HEADS heads of the layer (pool, route, compensated rule)."""
     import numpy as np
     from oracle import pooling, routing, attention
     try:
@@ -59,7 +62,7 @@ def cpu_baseline(wl, q, k, v):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
-    qh, kh, vh = (x[:, :1] for x in (q, k, v))
+    qh, kh, vh = (x[:, :CPU_HEADS] for x in (q, k, v))
     t0 = time.perf_counter()
     po = pooling.pool(qh, kh, vh, wl.N)
     idx, cnt = routing.route_topk(po["qbar"], po["kbar"], wl.topk)
@@ -67,8 +70,8 @@ def cpu_baseline(wl, q, k, v):
     dt = time.perf_counter() - t0
     kept = float(cnt.sum()) * 4 * 64 * 64 * wl.d
     return {"value": kept / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 of {wl.H} heads (all {wl.nb} query blocks): pool + top-k route + "
-                      f"compensated rule, fp64 numpy, {dt:.1f} s"}
+            "sample": f"{CPU_HEADS} of {wl.H} heads (all {wl.nb} query blocks each): pool + top-k "
+                      f"route + compensated rule, fp64 numpy, {dt:.1f} s"}
 
 
 def main():

@@ -87,8 +87,9 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, o
     if spreads:
         out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
     if fp8:
-        for n in ("q8", "k8", "v8"):
+        for n in ("q8", "k8"):
             out[n] = torch.empty(B, H, Np, d, dtype=torch.uint8, device=dev)
+        out["v8"] = torch.empty(B, H, nb, d, BLK, dtype=torch.uint8, device=dev)   # block-transposed
         out["exp8"] = torch.empty(B, H, nb, 3, dtype=torch.int8, device=dev)
     g = out.get
     _lib.check(lib.sparse_attn_pool(

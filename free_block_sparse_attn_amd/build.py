@@ -19,7 +19,7 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 
-def build(verbose: bool = False, lib_path: str = LIB, defines=()) -> str:
+def build(verbose: bool = False, lib_path: str = LIB, defines=(), extra_flags=()) -> str:
     """Compile every source to an object, link libsparse_attn.so; returns its path."""
     build_dir = os.path.join(os.path.dirname(os.path.abspath(lib_path)), "_build")
     os.makedirs(build_dir, exist_ok=True)
@@ -28,7 +28,7 @@ def build(verbose: bool = False, lib_path: str = LIB, defines=()) -> str:
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + FLAGS + [f"-D{x}" for x in defines] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + FLAGS + list(extra_flags) + [f"-D{x}" for x in defines] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     for src, cmd, p in procs:

@@ -193,10 +193,7 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
         if (skim) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no fp8 skim tier");
     } else {
         if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "bf16 forward supports d == 128 only");
-        if (skim) {
-            NEED(q8); NEED(k8); NEED(v8); NEED(exp8);
-            return fail(SA_ERR_UNSUPPORTED, "the fp8 skim tier is not available in this build");
-        }
+        if (skim) { NEED(q8); NEED(k8); NEED(v8); NEED(exp8); }
     }
     if (comp == SA_COMP_DROP && cap == 0 && !skim)
         return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");

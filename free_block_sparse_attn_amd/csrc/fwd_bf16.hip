@@ -258,7 +258,114 @@ __device__ __forceinline__ void s_tile(const bf16x8 ka[2][8], const bf16x8 qb[2]
                 s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qb[rb][ks], s[kb][rb], 0, 0, 0);
 }
 
-template <int COMP>
+// fp8 e4m3 skim tiles with per-block power-of-two scales (E8M0 operand
+// scales of v_mfma_scale_f32_32x32x64_f8f6f4):
+//   S^T = (K~ 2^{e_k}) (Q~ 2^{e_q})^T; L = scale log2(e) S (pad keys -inf)
+//   per row: c = ceil(max_tile L); codes p~ = e4m3(2^{8 + L - c})
+//   O^T += (V~^T 2^{e_v}) (p~^T 2^{c - 8 - m}) with the per-row B scale;
+//   the denominators take the unquantised 2^{L - m}.
+// Q~ and K~ are row-major; V~ is stored block-transposed [d][64] in the key
+// order of P's accumulator layout, so both fp8 PV operands are contiguous
+// 32-byte loads and no LDS is needed.
+__device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t bh, int qa,
+                                        const int32_t* listM, int cntM, float c2) {
+    const int nb = a.N_pad / BLK;
+    const int l = lane_id(), h = l >> 5, l32 = l & 31;
+    const size_t head = bh * a.N_pad * D;
+    const uint8_t* Q8 = a.q8 + head;
+    const uint8_t* K8 = a.k8 + head;
+    const uint8_t* V8 = a.v8 + head;
+    const int8_t* EX = a.exp8 + bh * nb * 3;
+    i32x8 qb8[2][2];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const int row = qa * BLK + 32 * rb + l32;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            i32x8 z = {};
+            if (row < a.N) z = *reinterpret_cast<const i32x8*>(Q8 + static_cast<size_t>(row) * D + 64 * ks + 32 * h);
+            qb8[rb][ks] = z;
+        }
+    }
+    const int sq = static_cast<int>(EX[qa * 3 + 0]) + 127;
+    for (int e = 0; e < cntM; ++e) {
+        const int j = listM[e];
+        const int nj = min(BLK, a.N - BLK * j);
+        const int sk = static_cast<int>(EX[j * 3 + 1]) + 127;
+        const int sv = static_cast<int>(EX[j * 3 + 2]) + 127;
+        const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * D;
+        i32x8 ka[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
+        const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * D;
+        i32x8 va[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
+        f32x16 s[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+                    s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
+        i32x8 pb[2];
+        int sb[2];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float mx = -INFINITY;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                    const float x = (key < nj) ? s[kb][rb][r] * c2 : -INFINITY;
+                    s[kb][rb][r] = x;
+                    mx = fmaxf(mx, x);
+                }
+            mx = fmaxf(mx, swap_halves(mx));
+            rescale_if_needed(st, rb, mx);
+            const float mref = st.m[rb];
+            const float ct = (mx == -INFINITY) ? mref : ceilf(mx);
+            const float mult = ldexpf(1.0f, 8 + static_cast<int>(mref - ct));
+            float le = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const float sv2 = s[kb][rb][4 * w + u];
+                        const float x = (sv2 == -INFINITY) ? 0.f : exp2f(sv2 - mref);
+                        le += x;
+                        y[u] = x * mult;
+                    }
+                    const uint32_t lo = pack_fp8x2<false>(y[0], y[1], 0u);
+                    pb[rb][4 * kb + w] = static_cast<int>(pack_fp8x2<true>(y[2], y[3], lo));
+                }
+            st.l[rb] += le;
+            st.le[rb] += le;
+            sb[rb] = min(max(static_cast<int>(ct - mref) - 8 + 127, 0), 254);
+        }
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    va[db], pb[rb], st.o[db][rb], 0, 0, 0, sv, 0, sb[rb]);
+    }
+}
+
+template <int COMP, bool SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
     extern __shared__ __attribute__((aligned(16))) char smem_raw[];
     Lds& lds = *reinterpret_cast<Lds*>(smem_raw);
@@ -305,9 +412,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // blocks that are not compensated
     for (int x = l; x < 128; x += 64) lds.kept[x] = 0u;
     wave_lds_sync();
+    const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
+    const int32_t* listM = SKIM ? a.idx2 + rowid * a.cap2 : nullptr;
     if (COMP >= 0) {
         for (int e = l; e < cntE; e += 64) {
             const int j = listE[e];
+            atomicOr(&lds.kept[j >> 5], 1u << (j & 31));
+        }
+        for (int e = l; e < cntM; e += 64) {
+            const int j = listM[e];
             atomicOr(&lds.kept[j >> 5], 1u << (j & 31));
         }
         wave_lds_sync();
@@ -358,6 +471,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         pv_tile(st, vb, pb);
         wave_lds_sync();
     }
+
+    // ---- phase 1b: fp8 skim blocks (Triage's low-precision tier) ----
+    if constexpr (SKIM) skim_tiles(a, st, bh, qa, listM, cntM, c2);
 
     // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
     if (COMP >= 0) {
@@ -493,23 +609,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
 }
 
-template <int COMP>
+template <int COMP, bool SKIM>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const size_t lds = (COMP == 1) ? sizeof(LdsOrder1) : sizeof(Lds);
     const int nq = a.N_pad / BLK;
     dim3 grid(nq * a.H * a.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<COMP>), grid, dim3(64), lds, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64), lds, s, a);
     return hipGetLastError();
+}
+
+template <bool SKIM>
+hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
+    switch (a.comp) {
+        case -1: return launch_t<-1, SKIM>(a, s);
+        case 0: return launch_t<0, SKIM>(a, s);
+        default: return launch_t<1, SKIM>(a, s);
+    }
 }
 
 }  // namespace
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
-    switch (a.comp) {
-        case -1: return launch_t<-1>(a, s);
-        case 0: return launch_t<0>(a, s);
-        default: return launch_t<1>(a, s);
-    }
+    const bool skim = a.idx2 != nullptr && a.cap2 > 0;
+    return skim ? launch_c<true>(a, s) : launch_c<false>(a, s);
 }
 
 }  // namespace sa

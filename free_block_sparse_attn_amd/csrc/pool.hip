@@ -219,8 +219,9 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                 ex[t] = e4m3_block_exponent(m);
             }
             if (tid < 3) a.exp8[(bh * nb + j) * 3 + tid] = static_cast<int8_t>(ex[tid]);
+            // Q and K copies stay row-major
 #pragma unroll
-            for (int t = 0; t < 3; ++t) {
+            for (int t = 0; t < 2; ++t) {
 #pragma unroll
                 for (int c = 0; c < PT; ++c) {
                     const int chunk = tid + THREADS * c;
@@ -235,6 +236,29 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                     uint2 out = {w0, w1};
                     *reinterpret_cast<uint2*>(dst8[t] + tok0 + static_cast<size_t>(row) * D + col0) = out;
                 }
+            }
+            // V copy block-transposed, [d][64 positions]; position p holds key
+            // 32((p%32)/16) + 8((p%16)/4) + 4(p/32) + p%4, the key order of the
+            // fp8 P operand in the forward pass.  Pad keys get code 0.
+            {
+                const int dcol = tid >> 1, p0 = 32 * (tid & 1);
+                const T* col = xt + (2 * D + dcol) * TPITCH;
+                uint32_t w[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) {
+                    float x[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int p = p0 + 4 * q + u;
+                        const int key = 32 * ((p & 31) >> 4) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3);
+                        x[u] = (key < n) ? ldexpf(E::val(col[key]), -ex[2]) : 0.0f;
+                    }
+                    uint32_t v = pack_fp8x2<false>(x[0], x[1], 0u);
+                    w[q] = pack_fp8x2<true>(x[2], x[3], v);
+                }
+                uint8_t* dstv = a.v8 + ((bh * nb + j) * static_cast<size_t>(D) + dcol) * BLK + p0;
+                *reinterpret_cast<u32x4*>(dstv) = u32x4{w[0], w[1], w[2], w[3]};
+                *reinterpret_cast<u32x4*>(dstv + 16) = u32x4{w[4], w[5], w[6], w[7]};
             }
         }
     }

@@ -106,11 +106,16 @@ typedef struct {
  *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
  *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
  *                        omission-error statistic); -inf for 1-token blocks.
- *   q8, k8, v8, exp8     fp8 e4m3 (OCP) copies uint8 [B,H,N_pad,d] with one
- *                        power-of-two scale per block and tensor:
- *                        x8 = e4m3_rne(x * 2^-e), e = smallest integer with
- *                        amax_block * 2^-e <= 448; exp8 int8 [B,H,nb,3] holds
- *                        e for (q, k, v).  Pad rows are written as 0.  All
+ *   q8, k8, v8, exp8     fp8 e4m3 (OCP) copies with one power-of-two scale
+ *                        per block and tensor: x8 = e4m3_rne(x * 2^-e), e =
+ *                        smallest integer with amax_block * 2^-e <= 448;
+ *                        exp8 int8 [B,H,nb,3] holds e for (q, k, v).
+ *                        q8, k8: uint8 [B,H,N_pad,d] row-major.
+ *                        v8: uint8 [B,H,nb,d,64] block-transposed: entry
+ *                        (j, i, p) is value dimension i of key 64 j + kappa(p),
+ *                        kappa(p) = 32((p%32)/16) + 8((p%16)/4) + 4(p/32) + p%4
+ *                        (the key order of the forward pass's fp8 P operand).
+ *                        Pad keys are written as 0.  All
  *                        four pointers or none.  bf16 inputs only.
  */
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,

@@ -23,7 +23,7 @@ def inputs(wl, heads=None):
     return (q, k, v), to_device(wl, q, k, v), coords
 
 
-SKIM_BUILT = False      # the fp8 skim tier of the forward pass
+SKIM_BUILT = True       # the fp8 skim tier of the forward pass
 
 
 def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
@@ -51,6 +51,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
         out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2)
     torch.cuda.synchronize()
     res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
+    if "v8" in res:
+        res["v8"] = v8_row_major(res["v8"], wl.N_pad)
     res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
     if idx2 is not None:
         res["idx2"], res["cnt2"] = idx2.cpu().numpy(), cnt2.cpu().numpy()
@@ -58,6 +60,20 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
         res["out"] = out.float().cpu().numpy()
         res["lse"] = lse.cpu().numpy()
     return res
+
+
+def kappa(p):
+    """Key held at position p of a block-transposed fp8 V block."""
+    return 32 * ((p % 32) // 16) + 8 * ((p % 16) // 4) + 4 * (p // 32) + p % 4
+
+
+def v8_row_major(v8t, n_pad):
+    """[B,H,nb,d,64] block-transposed codes -> [B,H,N_pad,d] row-major codes."""
+    B, H, nb, d, _ = v8t.shape
+    out = np.empty((B, H, nb, 64, d), v8t.dtype)
+    p = np.arange(64)
+    out[:, :, :, kappa(p), :] = np.swapaxes(v8t, -1, -2)
+    return out.reshape(B, H, n_pad, d)
 
 
 def oracle_pool(wl, q, k, v):
