@@ -1,7 +1,8 @@
 """Build the gfx950 HIP library libsparse_attn.so in-tree with hipcc.
 
 Every source under csrc/ is compiled for gfx950 only.  Packed fp32 vector
-instructions are disabled (-packed-fp32-ops) for all device code.
+instructions are disabled (-packed-fp32-ops) for all device code, and MFMA
+instructions use the VGPR form for their accumulators.
 """
 
 import os
@@ -16,6 +17,9 @@ SOURCES = ["api.cpp", "pool.hip", "route.hip", "fwd_f32.hip", "fwd_bf16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         # MFMA accumulators in VGPRs: the forward kernel's register budget
+         # then fits without scratch (AGPRs hold the spare operands)
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1",
          "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function"]
 
 

@@ -42,25 +42,12 @@ namespace sa {
 
 namespace {
 
-#ifndef SA_K_PREFETCH
-#define SA_K_PREFETCH 0            // K tiles: 1 = loaded one tile ahead into VGPRs
-#endif
-
 constexpr int D = 128;
 constexpr int ROWB = D * 2;                // bytes per bf16 row
 constexpr int TILEB = BLK * ROWB;          // bytes per 64-key bf16 tile (16 KiB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
-constexpr float TAU = 8.0f;                // lazy rescale threshold (log2 units)
-
-struct Lds {
-    uint8_t v[2][TILEB];                   // V tiles, row-major, swizzled 16-byte chunks
-    uint32_t kept[128];                    // bitmask of blocks not compensated (nb <= 4096)
-};
-struct LdsOrder1 {
-    Lds base;
-    float w[BLK * (BLK + 1)];              // order-1 weights [centroid][row]
-};
+constexpr float M_INIT = -1.0e30f;         // "no reference yet" (finite: 2^(-inf - M_INIT) = 0)
 
 // physical 16-byte chunk of logical chunk c (0..15) in LDS row `row`
 __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row & 7) << 1); }
@@ -92,18 +79,22 @@ typedef __attribute__((ext_vector_type(8))) short i16x8;
 // 16 x global_load_lds_dwordx4: the whole 64x128 bf16 V tile into one LDS
 // buffer.  Instruction m fills LDS rows 4m .. 4m+3; lane l lands at row
 // 4m + l/16, physical chunk l%16, so it fetches the logical chunk that the
-// swizzle maps there.
-__device__ __forceinline__ void dma_v_tile(const uint16_t* vrow0, uint8_t* buf) {
+// swizzle maps there.  The swizzle depends on row & 7, i.e. on m & 1, so two
+// lane offsets cover all 16 instructions.
+__device__ __forceinline__ void dma_offsets(uint32_t off[2]) {
     const int l = lane_id();
     const int rsub = l >> 4, p = l & 15;
 #pragma unroll
-    for (int m = 0; m < 16; ++m) {
-        const int row = 4 * m + rsub;
-        const int c = swz(row, p);                 // swz is an involution
-        const uint16_t* src = vrow0 + row * D + 8 * c;
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src),
+    for (int par = 0; par < 2; ++par)
+        off[par] = rsub * ROWB + 16 * swz(4 * par + rsub, p);   // swz is an involution
+}
+
+__device__ __forceinline__ void dma_v_tile(const uint16_t* vrow0, uint8_t* buf, const uint32_t off[2]) {
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(vrow0);
+#pragma unroll
+    for (int m = 0; m < 16; ++m)
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + m * 4 * ROWB + off[m & 1]),
                                          (lds_void*)(buf + m * 1024), 16, 0, 0);
-    }
 }
 
 // Zero rows nvalid..63 of an LDS tile (pad keys of the ragged tail block).
@@ -149,15 +140,14 @@ struct State {
     float le[2];           // partial row sums of the unrounded weights (for lse)
 };
 
-// Lazy max update: when a row's tile max exceeds the reference by more than
-// TAU, move the reference up to ceil(tile max) and rescale that row's
-// accumulators.  The reference stays an integer so that powers of two
-// relative to it are exact.
-__device__ __forceinline__ void rescale_if_needed(State& st, int rb, float mx) {
-    const bool need = mx > st.m[rb] + TAU;
+// Lazy max: the reference of a row (log2 units, an integer so that powers of
+// two relative to it are exact) moves up to ceil(tile max) only when a tile
+// max exceeds it by more than 8; then the row's accumulators are rescaled.
+__device__ __forceinline__ void rescale_lazy(State& st, int rb, float mx) {
+    const bool need = st.m[rb] == M_INIT ? mx > -INFINITY : mx > st.m[rb] + 8.0f;
     if (__ballot(need)) {
         const float mnew = need ? ceilf(mx) : st.m[rb];
-        const float alpha = exp2f(st.m[rb] - mnew);
+        const float alpha = __builtin_amdgcn_exp2f(st.m[rb] - mnew);
         st.l[rb] *= alpha;
         st.le[rb] *= alpha;
 #pragma unroll
@@ -168,35 +158,56 @@ __device__ __forceinline__ void rescale_if_needed(State& st, int rb, float mx) {
     }
 }
 
-// Online-softmax update of one 64-key tile whose logits (already in log2
-// units with bias and masking applied) are in s[kb][rb]; returns P^T as the
-// bf16 B operands of the O^T update, pb[2 kb + q2][rb].
-__device__ __forceinline__ void softmax_tile(State& st, f32x16 s[2][2], bf16x8 pb[4][2]) {
+__device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc) {
+    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+}
+
+// Online-softmax update of one 64-key tile of raw logits s[kb][rb] (before
+// the log2(e) * scale factor c2; scale > 0).  bias (optional) adds a per-key
+// log2 term; -inf marks keys that do not take part.  Returns P^T as the bf16
+// B operands of the O^T update, pb[2 kb + q2][rb].  P = 2^(c2 s + bias - m)
+// comes from one FMA and one v_exp_f32; the row sum for O's normalisation
+// adds the bf16-rounded P pairs with v_dot2_f32_bf16, the lse sum the
+// unrounded values.
+template <bool BIAS>
+__device__ __forceinline__ void softmax_tile(State& st, f32x16 s[2][2], bf16x8 pb[4][2], float c2,
+                                             const float bias[2][16]) {
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][rb][r]);
+            for (int r = 0; r < 16; ++r) {
+                const float v = BIAS ? fmaf(s[kb][rb][r], c2, bias[kb][r]) : s[kb][rb][r];
+                if (BIAS) s[kb][rb][r] = v;
+                mx = fmaxf(mx, v);
+            }
         mx = fmaxf(mx, swap_halves(mx));
-        rescale_if_needed(st, rb, mx);
-        const float mref = st.m[rb];
+        rescale_lazy(st, rb, BIAS ? mx : mx * c2);
+    }
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+        const float negm = -st.m[rb];
         float ls = 0.f, le = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int q2 = 0; q2 < 2; ++q2) {
-                bf16x8 p;
+                u32x4 w;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float sv = s[kb][rb][8 * q2 + e];
-                    const float x = (sv == -INFINITY) ? 0.f : exp2f(sv - mref);
-                    p[e] = static_cast<__bf16>(x);
-                    ls += static_cast<float>(p[e]);
-                    le += x;
+                for (int e = 0; e < 8; e += 2) {
+                    const float a0 = s[kb][rb][8 * q2 + e], a1 = s[kb][rb][8 * q2 + e + 1];
+                    const float x0 = __builtin_amdgcn_exp2f(BIAS ? a0 + negm : fmaf(a0, c2, negm));
+                    const float x1 = __builtin_amdgcn_exp2f(BIAS ? a1 + negm : fmaf(a1, c2, negm));
+                    const uint32_t pr = pack_bf16x2(x0, x1);
+                    w[e >> 1] = pr;
+                    ls = sum_bf16_pair(pr, ls);
+                    le += x0;
+                    le += x1;
                 }
-                pb[2 * kb + q2][rb] = p;
+                pb[2 * kb + q2][rb] = __builtin_bit_cast(bf16x8, w);
             }
         }
         st.l[rb] += ls;
@@ -204,58 +215,51 @@ __device__ __forceinline__ void softmax_tile(State& st, f32x16 s[2][2], bf16x8 p
     }
 }
 
-// O^T += V^T P^T for one tile whose V rows sit in LDS buffer `buf`.
-// ds_read_b64_tr_b16: within each 16-lane group, output lane i receives
-// element i%4 of the 8-byte pieces addressed by lanes i/4 + 4e (e = 0..3).
-// Supplying lane r addresses row key0 + r/4 at d0 + 4(r%4), so output lane
-// i gets keys key0 .. key0+3 of column d0 + i.
-__device__ __forceinline__ void pv_tile(State& st, const uint8_t* buf, const bf16x8 pb[4][2]) {
+// Lane offsets (bytes within a V tile buffer) of the transposed reads, one per
+// 32-wide d block.  ds_read_b64_tr_b16: within each 16-lane group, output
+// lane i receives element i%4 of the 8-byte pieces addressed by lanes i/4 + 4e
+// (e = 0..3).  Supplying lane r addresses row key0 + r/4 at d0 + 4(r%4), so
+// output lane i gets keys key0 .. key0+3 of column d0 + i.  The row swizzle
+// depends only on row & 7 = (4h + r/4) & 7, the same for every k-step.
+__device__ __forceinline__ void pv_offsets(uint32_t off[4]) {
     const int l = lane_id();
     const int h = l >> 5, g2 = (l >> 4) & 1, r = l & 15;
     const int rsub = r >> 2, csub = r & 3;
+    const int row0 = 4 * h + rsub;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const int chunk = 4 * db + 2 * g2 + (csub >> 1);
-        const int half = (csub & 1) * 8;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const int rowA = 16 * kk + 4 * h + rsub;          // keys 16kk + 4h + e
-            const int rowB = rowA + 8;                        // keys 16kk + 8 + 4h + e
-            const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(const_cast<uint8_t*>(buf) + rowA * ROWB + 16 * swz(rowA, chunk) + half));
-            const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (lds_i16x4*)(const_cast<uint8_t*>(buf) + rowB * ROWB + 16 * swz(rowB, chunk) + half));
-            const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-            const bf16x8 a8 = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a8, pb[kk][rb], st.o[db][rb], 0, 0, 0);
-        }
+        off[db] = row0 * ROWB + 16 * swz(row0, chunk) + (csub & 1) * 8;
     }
 }
 
-// K tile as MFMA A operands: ka[kb][ks] = K[32kb + l32][16ks + 8h .. +7]
-__device__ __forceinline__ void load_k_tile(const uint16_t* krow0, bf16x8 ka[2][8]) {
-    const int l = lane_id(), h = l >> 5, l32 = l & 31;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-            ka[kb][ks] = *reinterpret_cast<const bf16x8*>(krow0 + (32 * kb + l32) * D + 16 * ks + 8 * h);
+__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* base) {
+    // keys 16kk + 4h + e (slots 0..3) and 16kk + 8 + 4h + e (slots 4..7)
+    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
+    const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * ROWB));
+    const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
+    return __builtin_bit_cast(bf16x8, v8);
 }
 
-__device__ __forceinline__ void s_tile(const bf16x8 ka[2][8], const bf16x8 qb[2][8], f32x16 s[2][2]) {
+// O^T += V^T P^T for one tile whose V rows sit in LDS buffer `buf`; the
+// transposed reads of the next (d block, k-step) are issued before the
+// MFMAs of the current one.
+__device__ __forceinline__ void pv_tile(State& st, const uint8_t* buf, const uint32_t off[4],
+                                        const bf16x8 pb[4][2]) {
+    bf16x8 cur = tr_read_pair(buf + off[0]), nxt;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int t = 0; t < 16; ++t) {
+        const int db = t >> 2, kk = t & 3;
+        if (t < 15) {
+            const int db1 = (t + 1) >> 2, kk1 = (t + 1) & 3;
+            nxt = tr_read_pair(buf + off[db1] + kk1 * 16 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[kb][ks], qb[rb][ks], s[kb][rb], 0, 0, 0);
+        for (int rb = 0; rb < 2; ++rb)
+            st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pb[kk][rb], st.o[db][rb], 0, 0, 0);
+        cur = nxt;
+    }
 }
 
 // fp8 e4m3 skim tiles with per-block power-of-two scales (E8M0 operand
@@ -319,9 +323,10 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                         ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
         i32x8 pb[2];
         int sb[2];
+        float mx[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            float mx = -INFINITY;
+            float m0 = -INFINITY;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -329,12 +334,15 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                     const float x = (key < nj) ? s[kb][rb][r] * c2 : -INFINITY;
                     s[kb][rb][r] = x;
-                    mx = fmaxf(mx, x);
+                    m0 = fmaxf(m0, x);
                 }
-            mx = fmaxf(mx, swap_halves(mx));
-            rescale_if_needed(st, rb, mx);
+            mx[rb] = fmaxf(m0, swap_halves(m0));
+            rescale_lazy(st, rb, mx[rb]);
+        }
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
             const float mref = st.m[rb];
-            const float ct = (mx == -INFINITY) ? mref : ceilf(mx);
+            const float ct = (mx[rb] == -INFINITY) ? mref : ceilf(mx[rb]);
             const float mult = ldexpf(1.0f, 8 + static_cast<int>(mref - ct));
             float le = 0.f;
 #pragma unroll
@@ -344,8 +352,7 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     float y[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float sv2 = s[kb][rb][4 * w + u];
-                        const float x = (sv2 == -INFINITY) ? 0.f : exp2f(sv2 - mref);
+                        const float x = __builtin_amdgcn_exp2f(s[kb][rb][4 * w + u] - mref);
                         le += x;
                         y[u] = x * mult;
                     }
@@ -365,11 +372,49 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
     }
 }
 
+// K tile A operands come from the row-major, swizzled LDS copy of K:
+// ka(kb, ks) = K[32kb + l32][16ks + 8h .. +7].  Lane offsets for ks = 0..7
+// (kb = 1 adds 32 rows); the swizzle depends on row & 7 = l32 & 7.
+__device__ __forceinline__ void k_offsets(uint32_t off[8]) {
+    const int l = lane_id(), h = l >> 5, l32 = l & 31;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) off[ks] = l32 * ROWB + 16 * swz(l32, 2 * ks + h);
+}
+
+__device__ __forceinline__ void s_tile_lds(const uint8_t* kbuf, const uint32_t koff[8], const bf16x8 qb[2][8],
+                                           f32x16 s[2][2]) {
+    const f32x16 zero = {};
+    // two k-steps of LDS reads in flight ahead of the MFMAs that use them
+    bf16x8 cur[2], nxt[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) cur[kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff[0] + kb * 32 * ROWB);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        if (ks < 7) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+                nxt[kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks + 1] + kb * 32 * ROWB);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[kb], qb[rb][ks], ks ? s[kb][rb] : zero, 0, 0, 0);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) cur[kb] = nxt[kb];
+    }
+}
+
 template <int COMP, bool SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
-    extern __shared__ __attribute__((aligned(16))) char smem_raw[];
-    Lds& lds = *reinterpret_cast<Lds*>(smem_raw);
-    float* wbuf = (COMP == 1) ? reinterpret_cast<LdsOrder1*>(smem_raw)->w : nullptr;
+    // separate LDS objects so that the K and V copies are known not to alias
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf[TILEB];     // K tile (row-major, swizzled)
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf[TILEB];     // V tile (row-major, swizzled)
+    __shared__ uint32_t kept_mask[128];                              // blocks not compensated (nb <= 4096)
+    __shared__ float wbuf_s[COMP == 1 ? BLK * (BLK + 1) : 1];        // order-1 weights [centroid][row]
+    float* wbuf = wbuf_s;
+    struct { uint32_t* kept; } lds = {kept_mask};
 
     const int nq = a.N_pad / BLK, nb = nq;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -385,15 +430,19 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const size_t rowid = bh * nq + qa;
     const int cntE = a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0;
     const int32_t* listE = a.idx + rowid * a.cap;
+    const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
+    const int32_t* listM = SKIM ? a.idx2 + rowid * a.cap2 : nullptr;
+
+    uint32_t dmaoff[2], troff[4], koff[8];
+    dma_offsets(dmaoff);
+    pv_offsets(troff);
+    k_offsets(koff);
 
     // first exact tile in flight before anything else
-    bf16x8 ka[2][8];
     if (cntE > 0) {
         const int j0 = listE[0];
-#if SA_K_PREFETCH
-        load_k_tile(K + static_cast<size_t>(j0) * BLK * D, ka);
-#endif
-        dma_v_tile(V + static_cast<size_t>(j0) * BLK * D, lds.v[0]);
+        dma_v_tile(K + static_cast<size_t>(j0) * BLK * D, kbuf, dmaoff);
+        dma_v_tile(V + static_cast<size_t>(j0) * BLK * D, vbuf, dmaoff);
     }
 
     // Q^T as B operands: qb[rb][ks] = Q[row 32rb + l32][16ks + 8h .. +7]
@@ -409,11 +458,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         }
     }
 
-    // blocks that are not compensated
+    // blocks that are not compensated (exact and skim lists)
     for (int x = l; x < 128; x += 64) lds.kept[x] = 0u;
     wave_lds_sync();
-    const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
-    const int32_t* listM = SKIM ? a.idx2 + rowid * a.cap2 : nullptr;
     if (COMP >= 0) {
         for (int e = l; e < cntE; e += 64) {
             const int j = listE[e];
@@ -431,46 +478,48 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) st.o[db][rb] = f32x16{};
-    st.m[0] = st.m[1] = -INFINITY;
+    st.m[0] = st.m[1] = M_INIT;
     st.l[0] = st.l[1] = 0.f;
     st.le[0] = st.le[1] = 0.f;
 
-    // ---- phase 1: exact key blocks, one tile of K (VGPRs) and V (LDS) ahead ----
+    // ---- phase 1: exact key blocks ----
+    // K and V each have one LDS buffer; each is refilled for the next tile as
+    // soon as this tile is done reading it, so the K copy overlaps softmax and
+    // PV, and the V copy overlaps the next S and softmax.
     for (int e = 0; e < cntE; ++e) {
         const int j = listE[e];
         const int nj = min(BLK, a.N - BLK * j);
-        f32x16 s[2][2];
-#if !SA_K_PREFETCH
-        load_k_tile(K + static_cast<size_t>(j) * BLK * D, ka);
-#endif
-        s_tile(ka, qb, s);
         const bool more = e + 1 < cntE;
-        if (more) {
-            const int jn = listE[e + 1];
-#if SA_K_PREFETCH
-            load_k_tile(K + static_cast<size_t>(jn) * BLK * D, ka);
-#endif
-            dma_v_tile(V + static_cast<size_t>(jn) * BLK * D, lds.v[(e + 1) & 1]);
+        const int jn = more ? listE[e + 1] : j;
+        // K of this tile: only this tile's V copy may still be in flight
+        wait_vmcnt<16>();
+        wave_lds_sync();
+        f32x16 s[2][2];
+        s_tile_lds(kbuf, koff, qb, s);
+        wave_lds_sync();                                   // every lane's K reads have returned
+        if (more) dma_v_tile(K + static_cast<size_t>(jn) * BLK * D, kbuf, dmaoff);
+        if (nj < BLK) {                                    // ragged tail block only
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+                        if (key >= nj) s[kb][rb][r] = -INFINITY;
+                    }
         }
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    s[kb][rb][r] = (key < nj) ? s[kb][rb][r] * c2 : -INFINITY;
-                }
         bf16x8 pb[4][2];
-        softmax_tile(st, s, pb);
-        // this tile's V has landed once only the next tile's loads may be outstanding
-        if (more) wait_vmcnt<SA_K_PREFETCH ? 32 : 16>(); else wait_vmcnt<0>();
-        uint8_t* vb = lds.v[e & 1];
-        if (nj < BLK) zero_tail_rows(vb, nj);
+        softmax_tile<false>(st, s, pb, c2, nullptr);
+        // V of this tile: only the next tile's K copy may still be in flight
+        if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+        if (nj < BLK) zero_tail_rows(vbuf, nj);
         wave_lds_sync();
-        pv_tile(st, vb, pb);
-        wave_lds_sync();
+        pv_tile(st, vbuf, troff, pb);
+        wave_lds_sync();                                   // every lane's V reads have returned
+        if (more) dma_v_tile(V + static_cast<size_t>(jn) * BLK * D, vbuf, dmaoff);
     }
+    wait_vmcnt<0>();
 
     // ---- phase 1b: fp8 skim blocks (Triage's low-precision tier) ----
     if constexpr (SKIM) skim_tiles(a, st, bh, qa, listM, cntM, c2);
@@ -479,14 +528,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if (COMP >= 0) {
         const float* KB = a.kbar + bh * nb * D;
         const float* VB = a.vbar + bh * nb * D;
-        uint8_t* vb = lds.v[0];
         for (int c0 = 0; c0 < nb; c0 += BLK) {
             const int nc = min(BLK, nb - c0);
             f32x16 s[2][2];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
+            const f32x16 zero = {};
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb) {
                 const int cj = min(c0 + 32 * kb + l32, nb - 1);
@@ -506,7 +551,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                     const bf16x8 khi = __builtin_bit_cast(bf16x8, whi), klo = __builtin_bit_cast(bf16x8, wlo);
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
-                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb[rb][ks], s[kb][rb], 0, 0, 0);
+                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb[rb][ks], ks ? s[kb][rb] : zero, 0, 0, 0);
                         s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb[rb][ks], s[kb][rb], 0, 0, 0);
                     }
                 }
@@ -522,16 +567,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                         bv = __log2f(static_cast<float>(min(BLK, a.N - BLK * jj)));
                     bias[kb][r] = bv;
                 }
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) s[kb][rb][r] = s[kb][rb][r] * c2 + bias[kb][r];
             bf16x8 pb[4][2];
-            softmax_tile(st, s, pb);
+            softmax_tile<true>(st, s, pb, c2, bias);
             if (COMP == 1) {
-                // order-1 weights w = scale * e^{L - m} / n_j (L without the count bias)
+                // order-1 weights w = scale * 2^{L - m} / n_j (L without the count bias)
 #pragma unroll
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -540,44 +579,52 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                         for (int r = 0; r < 16; ++r) {
                             const int cc = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
                             const float x = (bias[kb][r] == -INFINITY) ? 0.f
-                                : exp2f(s[kb][rb][r] - bias[kb][r] - st.m[rb]) * a.scale;
+                                : __builtin_amdgcn_exp2f(s[kb][rb][r] - bias[kb][r] - st.m[rb]) * a.scale;
                             wbuf[cc * (BLK + 1) + 32 * rb + l32] = x;
                         }
             }
-            stage_means<false>(VB + static_cast<size_t>(c0) * D, nc, vb);
+            stage_means<false>(VB + static_cast<size_t>(c0) * D, nc, vbuf);
             wave_lds_sync();
-            pv_tile(st, vb, pb);
+            pv_tile(st, vbuf, troff, pb);
             wave_lds_sync();
-            stage_means<true>(VB + static_cast<size_t>(c0) * D, nc, vb);
+            stage_means<true>(VB + static_cast<size_t>(c0) * D, nc, vbuf);
             wave_lds_sync();
-            pv_tile(st, vb, pb);
+            pv_tile(st, vbuf, troff, pb);
             wave_lds_sync();
             if (COMP == 1) {
-                // O^T += w (.) (H_j^T Q^T) for every compensated block of this tile
+                // O^T += H_j^T (Q^T diag(w_j)) for every compensated block of this tile:
+                // the per-row weight scales the B operand, so the MFMA accumulates
+                // straight into O.
                 const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom);
                 for (int cc = 0; cc < nc; ++cc) {
                     const int jj = c0 + cc;
                     if ((lds.kept[jj >> 5] >> (jj & 31)) & 1u) continue;
                     const uint16_t* Hj = MOM + (bh * nb + jj) * static_cast<size_t>(D) * D;
-                    const float w0 = wbuf[cc * (BLK + 1) + l32];
-                    const float w1 = wbuf[cc * (BLK + 1) + 32 + l32];
+                    const float w[2] = {wbuf[cc * (BLK + 1) + l32], wbuf[cc * (BLK + 1) + 32 + l32]};
+                    bf16x8 qs[2][8];
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                        for (int ks = 0; ks < 8; ++ks) {
+                            const u32x4 qw = __builtin_bit_cast(u32x4, qb[rb][ks]);
+                            u32x4 o;
+#pragma unroll
+                            for (int t = 0; t < 4; ++t)
+                                o[t] = pack_bf16x2(__uint_as_float(qw[t] << 16) * w[rb],
+                                                   __uint_as_float(qw[t] & 0xFFFF0000u) * w[rb]);
+                            qs[rb][ks] = __builtin_bit_cast(bf16x8, o);
+                        }
 #pragma unroll
                     for (int db = 0; db < 4; ++db) {
                         bf16x8 ha[8];
 #pragma unroll
                         for (int ks = 0; ks < 8; ++ks)
                             ha[ks] = *reinterpret_cast<const bf16x8*>(Hj + (32 * db + l32) * D + 16 * ks + 8 * h);
-                        f32x16 t0 = {}, t1 = {};
 #pragma unroll
-                        for (int ks = 0; ks < 8; ++ks) {
-                            t0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qb[0][ks], t0, 0, 0, 0);
-                            t1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qb[1][ks], t1, 0, 0, 0);
-                        }
+                        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            st.o[db][0][r] = fmaf(w0, t0[r], st.o[db][0][r]);
-                            st.o[db][1][r] = fmaf(w1, t1[r], st.o[db][1][r]);
-                        }
+                            for (int rb = 0; rb < 2; ++rb)
+                                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qs[rb][ks], st.o[db][rb], 0, 0, 0);
                     }
                 }
                 wave_lds_sync();
@@ -590,6 +637,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const float lt = st.l[rb] + swap_halves(st.l[rb]);
+        const float le = st.le[rb] + swap_halves(st.le[rb]);
         const int row = qa * BLK + 32 * rb + l32;
         const bool valid = row < a.N;
         const float inv = valid ? 1.0f / lt : 0.f;
@@ -604,17 +652,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 *reinterpret_cast<uint2*>(O + static_cast<size_t>(row) * D + dd) = w;
             }
         }
-        const float le = st.le[rb] + swap_halves(st.le[rb]);
         if (a.lse && h == 0) a.lse[bh * a.N_pad + row] = valid ? (st.m[rb] + __log2f(le)) * LN2 : 0.f;
     }
 }
 
 template <int COMP, bool SKIM>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    const size_t lds = (COMP == 1) ? sizeof(LdsOrder1) : sizeof(Lds);
     const int nq = a.N_pad / BLK;
     dim3 grid(nq * a.H * a.B);
-    hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64), lds, s, a);
+    hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }
 
