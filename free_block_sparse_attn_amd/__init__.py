@@ -58,8 +58,10 @@ def abi_version() -> int:
     return _lib.load().sparse_attn_abi_version()
 
 
-def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, out=None) -> dict:
-    """Block means (fp32), counts and the optional moments / spreads / e4m3 copies.
+def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None, out=None) -> dict:
+    """Block means (fp32), counts and the optional centroid planes / moments /
+    spreads / e4m3 copies.  The bf16 centroid planes (what the bf16 forward
+    reads) are produced by default for bf16 inputs with d == 128.
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
     """
@@ -73,8 +75,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, o
         _lib.check(lib.sparse_attn_pool(
             ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
             _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-            _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
-            _stream(q)))
+            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")),
+            _ptr(g("exp8")), _stream(q)))
         return out
     out = {
         "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
@@ -82,6 +84,11 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, o
         "vbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
         "kcount": torch.empty(nb, dtype=torch.int32, device=dev),
     }
+    if cent is None:
+        cent = q.dtype == torch.bfloat16 and d == 128
+    if cent:
+        nbc = BLK * ((nb + BLK - 1) // BLK)
+        out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.bfloat16, device=dev)
     if moments:
         out["kmom"] = torch.empty(B, H, nb, d, d, dtype=torch.bfloat16, device=dev)
     if spreads:
@@ -95,8 +102,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, o
     _lib.check(lib.sparse_attn_pool(
         ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-        _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
-        _stream(q)))
+        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")),
+        _ptr(g("exp8")), _stream(q)))
     return out
 
 
@@ -168,7 +175,7 @@ def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx,
     cap2 = idx2.shape[-1] if idx2 is not None else 0
     _lib.check(lib.sparse_attn_fwd(
         ctypes.byref(_shape(q, N)), _dtype(q), comp, scale, _ptr(q), _ptr(k), _ptr(v),
-        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("kcount")), _ptr(g("kmom")),
+        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("kcount")), _ptr(g("kmom")),
         _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
         _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
         _ptr(out), _ptr(lse), _stream(q)))

@@ -58,12 +58,12 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.sparse_attn_pool.argtypes = [ctypes.POINTER(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, vp, vp, vp, vp]
+                                     vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_pool.restype = i32
     lib.sparse_attn_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(RouteSpec), vp, vp, vp, vp,
                                       vp, vp, i32, vp, vp, i32, vp]
     lib.sparse_attn_route.restype = i32
-    lib.sparse_attn_fwd.argtypes = [ctypes.POINTER(Shape), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp,
+    lib.sparse_attn_fwd.argtypes = [ctypes.POINTER(Shape), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
                                     vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
     lib.sparse_attn_fwd.restype = i32
     lib.sparse_attn_lvsa_capacity.argtypes = [vp, vp, i32, i32, i32]

@@ -32,9 +32,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
     return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
 }
 
-// Lane l reads lane l ^ 32 (the other half of the wave).
-__device__ __forceinline__ float swap_halves(float x) {
-    return __shfl_xor(x, 32);
+// Lanes l and l ^ 32 combined (v_permlane32_swap, no LDS round trip): with
+// both operands = x the swap returns (own, other) in the low half of the wave
+// and (other, own) in the high half, so a symmetric combination of the two
+// results is the same on both lanes.
+__device__ __forceinline__ float pair_max(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return fmaxf(__builtin_bit_cast(float, static_cast<uint32_t>(r[0])),
+                 __builtin_bit_cast(float, static_cast<uint32_t>(r[1])));
+}
+
+__device__ __forceinline__ float pair_sum(float x) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __builtin_bit_cast(float, static_cast<uint32_t>(r[0])) +
+           __builtin_bit_cast(float, static_cast<uint32_t>(r[1]));
 }
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }

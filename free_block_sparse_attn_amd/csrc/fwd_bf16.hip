@@ -11,27 +11,45 @@
 // FlashAttention-style online softmax); SVG-EAR's centroid compensation
 // ("SVG-EAR ...", section 2A).
 //
-// Work split.  One wave owns a whole 64-row query block, so a 64-key tile is
-// 2 x 2 blocks of 32x32 and every K/V byte loaded feeds 64 query rows.
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows loaded straight from
-//                 global memory into VGPRs one tile ahead, B = Q^T held in
-//                 VGPRs for the whole kernel.  Each lane ends up owning one
-//                 query row per 32-row block, so the row max / row sum need a
-//                 single exchange with the other half of the wave.
+// Work split.  One wave owns a whole 64-row query block, so every K/V byte
+// brought into LDS feeds 64 query rows.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16; A = K rows from LDS
+//                 (ds_read_b128), B = Q^T held in VGPRs for the whole kernel.
+//                 A lane owns one query row per 32-row block; its 16
+//                 accumulator entries are 16 of the 32 keys of a half tile,
+//                 the other 16 sit in lane l ^ 32.
 //   O^T += V^T P^T  B = P^T straight from S's accumulators (rounded to bf16),
-//                 A = V^T read from a row-major LDS copy of V with
+//                 A = V^T read from the row-major LDS copy of V with
 //                 ds_read_b64_tr_b16 (4 consecutive keys of one d per read).
-//                 V tiles reach LDS by global_load_lds_dwordx4 (no VGPRs),
-//                 double buffered one tile ahead, with a 16-byte XOR swizzle.
 // The P^T operand's key order follows S's accumulator layout: within each
 // 16-key MFMA step, slot s holds key s with bits 2 and 3 swapped; the V^T
-// reads use the same order.  Centroid pseudo-keys go through the same MFMA
-// path as 64-wide tiles (means split into bf16 high + low parts so the fp32
-// means keep ~16 bits), with bias log2(n_j) and -inf at the exact blocks.
-// The running max is updated lazily (only when a row's tile max exceeds it
-// by more than 8 in log2 units), which keeps the accumulator rescale off the
-// common path.  The softmax denominator sums the same bf16-rounded P that
-// the MFMA consumes, so rounding of P cancels in o = N / D.
+// reads use the same order.
+//
+// Exact tiles run as a software pipeline over half tiles (32 keys).  Each
+// tile is four MFMA regions of 16 MFMAs,
+//   A: S(keys 0-31, tile i)      C: S(keys 32-63, tile i)
+//   B: PV(keys 32-63, tile i-1)  D: PV(keys 0-31, tile i),
+// run in the order A B C D, and the exponentials of one row block of a half
+// (48 VALU instructions) are interleaved between the MFMAs of each region, so
+// the VALU work of the softmax runs under the matrix core.  K and V halves
+// have LDS buffers of their own, filled by buffer_load ... lds (no VGPRs, no
+// VALU address arithmetic) as soon as the region that reads them is done;
+// each copy has three regions to land.
+//
+// Softmax reference.  P = 2^(c2 s - m) with a per-row reference m that only
+// moves when a half tile's weights overflow a bound (sum of one lane's 16
+// weights > 2^40; the first tile always does, from m = -1e30).  Then m
+// becomes the ceiling of the row max over that half and the accumulators are
+// rescaled; otherwise no row max is computed at all.  Any m keeps the bf16
+// weights and the fp32 sums exact to rounding as long as nothing overflows,
+// which the bound guarantees.  The denominator sums the same bf16-rounded P
+// that the MFMA consumes, so the rounding of P cancels in o = N / D; lse is
+// m + log2 of that sum (within 2^-8, the bf16 unit roundoff, relative of the
+// unrounded sum).
+//
+// Centroid pseudo-keys go through the same MFMA path as 64-wide tiles (means
+// split into bf16 high + low parts so the fp32 means keep ~16 bits), with
+// bias log2(n_j) and -inf at the exact blocks, and a lazily updated max.
 //
 // Workgroup = one wave; consecutive query blocks of one head are mapped to
 // the same XCD so their overlapping K/V blocks are shared through its L2.
@@ -45,12 +63,18 @@ namespace {
 constexpr int D = 128;
 constexpr int ROWB = D * 2;                // bytes per bf16 row
 constexpr int TILEB = BLK * ROWB;          // bytes per 64-key bf16 tile (16 KiB)
+constexpr int HALFB = TILEB / 2;           // 32 rows (8 KiB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float M_INIT = -1.0e30f;         // "no reference yet" (finite: 2^(-inf - M_INIT) = 0)
+constexpr float OVF = 1099511627776.0f;    // 2^40: per-lane half-tile weight sum that moves m
+constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9)
 
-// physical 16-byte chunk of logical chunk c (0..15) in LDS row `row`
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row & 7) << 1); }
+// Physical 16-byte chunk of logical chunk c (0..15) in LDS row `row`.  The
+// XOR key is a bijection of row & 15, so 16 consecutive rows reading the same
+// logical chunk (K reads) hit 16 different chunks, and rows 0-3 (or 8-11)
+// reading 4 consecutive chunks (V^T transposed reads) hit 16 different chunks.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (((row & 3) << 2) | ((row >> 2) & 3)); }
 
 __device__ __forceinline__ int xcd_remap(int bid, int grid) {
     const int xcd = bid & 7, slot = bid >> 3;
@@ -75,86 +99,64 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((ext_vector_type(8))) short i16x8;
+typedef __attribute__((address_space(4))) const int32_t const_i32;   // read through the scalar cache
 
-// 16 x global_load_lds_dwordx4: the whole 64x128 bf16 V tile into one LDS
-// buffer.  Instruction m fills LDS rows 4m .. 4m+3; lane l lands at row
-// 4m + l/16, physical chunk l%16, so it fetches the logical chunk that the
-// swizzle maps there.  The swizzle depends on row & 7, i.e. on m & 1, so two
-// lane offsets cover all 16 instructions.
-__device__ __forceinline__ void dma_offsets(uint32_t off[2]) {
+// ---- LDS copies of K and V half tiles ----
+
+// 8 x buffer_load_dwordx4 ... lds: rows 32hk .. 32hk+31 of one 64-row tile
+// into a half buffer.  Instruction m fills half-buffer rows 4m .. 4m+3; lane l
+// lands at row 4m + l/16, physical chunk l%16, so it fetches the logical
+// chunk that the swizzle maps there.  row & 15 = 4(m & 3) + l/16, so four lane
+// offsets cover the eight instructions; the tile offset is a scalar.
+__device__ __forceinline__ void dma_offsets(uint32_t off[4]) {
     const int l = lane_id();
     const int rsub = l >> 4, p = l & 15;
 #pragma unroll
-    for (int par = 0; par < 2; ++par)
-        off[par] = rsub * ROWB + 16 * swz(4 * par + rsub, p);   // swz is an involution
+    for (int par = 0; par < 4; ++par)
+        off[par] = rsub * ROWB + 16 * swz(4 * par + rsub, p);   // swz is an involution per row
 }
 
-__device__ __forceinline__ void dma_v_tile(const uint16_t* vrow0, uint8_t* buf, const uint32_t off[2]) {
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(vrow0);
+__device__ __forceinline__ void dma_half(__amdgpu_buffer_rsrc_t rs, uint8_t* buf, uint32_t src,
+                                         const uint32_t off[4]) {
 #pragma unroll
-    for (int m = 0; m < 16; ++m)
-        __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + m * 4 * ROWB + off[m & 1]),
-                                         (lds_void*)(buf + m * 1024), 16, 0, 0);
+    for (int m = 0; m < 8; ++m)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + m * 1024), 16, off[m & 3],
+                                                 src + m * 1024, 0, 0);
 }
 
-// Zero rows nvalid..63 of an LDS tile (pad keys of the ragged tail block).
-__device__ __forceinline__ void zero_tail_rows(uint8_t* buf, int nvalid) {
+// Zero half-buffer rows r0 .. 31 (pad keys of the ragged tail block).
+__device__ __forceinline__ void zero_rows(uint8_t* buf, int r0) {
     const int l = lane_id();
-    for (int x = nvalid * 16 + l; x < BLK * 16; x += 64) {
+    for (int x = r0 * 16 + l; x < 32 * 16; x += 64) {
         const u32x4 z = {0u, 0u, 0u, 0u};
         *reinterpret_cast<u32x4*>(buf + x * 16) = z;
     }
 }
 
-// Write 64 fp32 mean rows (centroid values) as bf16 rows into an LDS tile:
-// the high parts (LO = false) or the residuals x - bf16(x) (LO = true).
-template <bool LO>
-__device__ __forceinline__ void stage_means(const float* vrow0, int nvalid, uint8_t* buf) {
-    const int l = lane_id();
-    const int rsub = l >> 4, c = l & 15;
-#pragma unroll 4
-    for (int m = 0; m < 16; ++m) {
-        const int row = 4 * m + rsub;
-        float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        if (row < nvalid) {
-            const float4 x0 = *reinterpret_cast<const float4*>(vrow0 + row * D + 8 * c);
-            const float4 x1 = *reinterpret_cast<const float4*>(vrow0 + row * D + 8 * c + 4);
-            x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-            x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-        }
-        if (LO) {
-#pragma unroll
-            for (int t = 0; t < 8; ++t) x[t] -= bf16_to_f32(f32_to_bf16(x[t]));
-        }
-        u32x4 w;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) w[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
-        *reinterpret_cast<u32x4*>(buf + row * ROWB + 16 * swz(row, c)) = w;
-    }
-}
+// ---- online softmax state ----
 
 struct State {
     f32x16 o[4][2];        // O^T[d-block][row-block]
-    float m[2];            // running reference max (log2 units, an integer) per row block
-    float l[2];            // partial row sums of the bf16-rounded P (normalises O)
-    float le[2];           // partial row sums of the unrounded weights (for lse)
+    float m[2];            // reference (log2 units, an integer) per row block
+    float l[2];            // this lane's partial row sums of the bf16-rounded P
 };
 
-// Lazy max: the reference of a row (log2 units, an integer so that powers of
-// two relative to it are exact) moves up to ceil(tile max) only when a tile
-// max exceeds it by more than 8; then the row's accumulators are rescaled.
+__device__ __forceinline__ void rescale_row(State& st, int rb, float mnew) {
+    const float alpha = __builtin_amdgcn_exp2f(st.m[rb] - mnew);
+    st.l[rb] *= alpha;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st.o[db][rb][r] *= alpha;
+    st.m[rb] = mnew;
+}
+
+// Lazy max for the centroid and skim tiles: the reference moves up to
+// ceil(tile max) only when a tile max exceeds it by more than 8 (log2 units).
 __device__ __forceinline__ void rescale_lazy(State& st, int rb, float mx) {
     const bool need = st.m[rb] == M_INIT ? mx > -INFINITY : mx > st.m[rb] + 8.0f;
     if (__ballot(need)) {
-        const float mnew = need ? ceilf(mx) : st.m[rb];
-        const float alpha = __builtin_amdgcn_exp2f(st.m[rb] - mnew);
-        st.l[rb] *= alpha;
-        st.le[rb] *= alpha;
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) st.o[db][rb][r] *= alpha;
-        st.m[rb] = mnew;
+        if (need) rescale_row(st, rb, ceilf(mx));
     }
 }
 
@@ -163,102 +165,167 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
 }
 
-// Online-softmax update of one 64-key tile of raw logits s[kb][rb] (before
-// the log2(e) * scale factor c2; scale > 0).  bias (optional) adds a per-key
-// log2 term; -inf marks keys that do not take part.  Returns P^T as the bf16
-// B operands of the O^T update, pb[2 kb + q2][rb].  P = 2^(c2 s + bias - m)
-// comes from one FMA and one v_exp_f32; the row sum for O's normalisation
-// adds the bf16-rounded P pairs with v_dot2_f32_bf16, the lse sum the
-// unrounded values.
-template <bool BIAS>
-__device__ __forceinline__ void softmax_tile(State& st, f32x16 s[2][2], bf16x8 pb[4][2], float c2,
-                                             const float bias[2][16]) {
+// P = 2^(c2 s - m) for the 16 logits a lane holds in one row block of a
+// 32-key half, as the two bf16 B operands of that half's PV k-steps
+// (p0: accumulator entries 0-7, p1: 8-15), and the sum of the rounded values.
+// 16 FMA + 16 v_exp_f32 + 8 v_cvt_pk_bf16_f32 + 8 v_dot2 = 48 VALU.
+__device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+    const float negm = -m;
+    float acc = 0.f;
+    u32x4 w0, w1;
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const float v = BIAS ? fmaf(s[kb][rb][r], c2, bias[kb][r]) : s[kb][rb][r];
-                if (BIAS) s[kb][rb][r] = v;
-                mx = fmaxf(mx, v);
-            }
-        mx = fmaxf(mx, swap_halves(mx));
-        rescale_lazy(st, rb, BIAS ? mx : mx * c2);
+    for (int e = 0; e < 8; e += 2) {
+        const uint32_t pr = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[e], c2, negm)),
+                                        __builtin_amdgcn_exp2f(fmaf(s[e + 1], c2, negm)));
+        w0[e >> 1] = pr;
+        acc = sum_bf16_pair(pr, acc);
     }
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        const float negm = -st.m[rb];
-        float ls = 0.f, le = 0.f;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int q2 = 0; q2 < 2; ++q2) {
-                u32x4 w;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float a0 = s[kb][rb][8 * q2 + e], a1 = s[kb][rb][8 * q2 + e + 1];
-                    const float x0 = __builtin_amdgcn_exp2f(BIAS ? a0 + negm : fmaf(a0, c2, negm));
-                    const float x1 = __builtin_amdgcn_exp2f(BIAS ? a1 + negm : fmaf(a1, c2, negm));
-                    const uint32_t pr = pack_bf16x2(x0, x1);
-                    w[e >> 1] = pr;
-                    ls = sum_bf16_pair(pr, ls);
-                    le += x0;
-                    le += x1;
-                }
-                pb[2 * kb + q2][rb] = __builtin_bit_cast(bf16x8, w);
-            }
-        }
-        st.l[rb] += ls;
-        st.le[rb] += le;
+    for (int e = 0; e < 8; e += 2) {
+        const uint32_t pr = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[8 + e], c2, negm)),
+                                        __builtin_amdgcn_exp2f(fmaf(s[8 + e + 1], c2, negm)));
+        w1[e >> 1] = pr;
+        acc = sum_bf16_pair(pr, acc);
     }
+    p0 = __builtin_bit_cast(bf16x8, w0);
+    p1 = __builtin_bit_cast(bf16x8, w1);
+    ls = acc;
 }
 
-// Lane offsets (bytes within a V tile buffer) of the transposed reads, one per
-// 32-wide d block.  ds_read_b64_tr_b16: within each 16-lane group, output
-// lane i receives element i%4 of the 8-byte pieces addressed by lanes i/4 + 4e
-// (e = 0..3).  Supplying lane r addresses row key0 + r/4 at d0 + 4(r%4), so
-// output lane i gets keys key0 .. key0+3 of column d0 + i.  The row swizzle
-// depends only on row & 7 = (4h + r/4) & 7, the same for every k-step.
-__device__ __forceinline__ void pv_offsets(uint32_t off[4]) {
+// After both row blocks of a half have their weights: if any lane's sum
+// overflowed the bound (first tile, or a large logit), move the reference of
+// the affected rows to the ceiling of their max over this half, rescale, and
+// redo the weights.  Then fold the half's sums into the row sums.
+__device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float c2, bf16x8 pb[2][2], float ls[2]) {
+    if (__builtin_expect(__ballot(ls[0] > OVF || ls[1] > OVF) != 0, 0)) {
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+            float mx = s[rb][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
+            mx = pair_max(mx) * c2;
+            const bool need = pair_max(ls[rb]) > OVF;
+            if (need) rescale_row(st, rb, ceilf(mx));
+            exp_rb(s[rb], st.m[rb], c2, pb[0][rb], pb[1][rb], ls[rb]);
+        }
+    }
+    st.l[0] += ls[0];
+    st.l[1] += ls[1];
+}
+
+// Keys at or beyond nvalid (ragged tail block) drop out: logit -inf.
+__device__ __forceinline__ void mask_half(f32x16 s[2], int key0, int nvalid) {
+    const int h = lane_id() >> 5;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+            if (key0 + 8 * (r >> 2) + 4 * h + (r & 3) >= nvalid) s[rb][r] = -INFINITY;
+}
+
+// ---- LDS operand offsets ----
+
+// K A operands: ka(ks) = K[half row l32][16ks + 8h .. +7] of a half buffer.
+__device__ __forceinline__ void k_offsets(uint32_t off[8]) {
+    const int l = lane_id(), h = l >> 5, l32 = l & 31;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) off[ks] = l32 * ROWB + 16 * swz(l32, 2 * ks + h);
+}
+
+// V^T A operands through ds_read_b64_tr_b16: within each 16-lane group,
+// output lane i receives element i%4 of the 8-byte pieces addressed by lanes
+// i/4 + 4e (e = 0..3).  Supplying lane r addresses row key0 + r/4 at
+// d0 + 4(r%4), so output lane i gets keys key0 .. key0+3 of column d0 + i.
+// One operand = rows 4h + r/4 (offset oa) and rows 8 + 4h + r/4 (offset ob)
+// of a 16-key step; the next k-step adds 16 rows, which keeps row & 15.
+__device__ __forceinline__ void pv_offsets(uint32_t oa[4], uint32_t ob[4]) {
     const int l = lane_id();
     const int h = l >> 5, g2 = (l >> 4) & 1, r = l & 15;
     const int rsub = r >> 2, csub = r & 3;
-    const int row0 = 4 * h + rsub;
+    const int row0 = 4 * h + rsub, row1 = row0 + 8;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
         const int chunk = 4 * db + 2 * g2 + (csub >> 1);
-        off[db] = row0 * ROWB + 16 * swz(row0, chunk) + (csub & 1) * 8;
+        oa[db] = row0 * ROWB + 16 * swz(row0, chunk) + (csub & 1) * 8;
+        ob[db] = row1 * ROWB + 16 * swz(row1, chunk) + (csub & 1) * 8;
     }
 }
 
-__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* base) {
+__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* pa, const uint8_t* pb) {
     // keys 16kk + 4h + e (slots 0..3) and 16kk + 8 + 4h + e (slots 4..7)
-    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base));
-    const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + 8 * ROWB));
+    const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa));
+    const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb));
     const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
     return __builtin_bit_cast(bf16x8, v8);
 }
 
-// O^T += V^T P^T for one tile whose V rows sit in LDS buffer `buf`; the
-// transposed reads of the next (d block, k-step) are issued before the
-// MFMAs of the current one.
-__device__ __forceinline__ void pv_tile(State& st, const uint8_t* buf, const uint32_t off[4],
-                                        const bf16x8 pb[4][2]) {
-    bf16x8 cur = tr_read_pair(buf + off[0]), nxt;
+// ---- the four MFMA regions of the exact-tile pipeline ----
+//
+// Each region issues 16 MFMAs; after each MFMA come three VALU instructions
+// of the weights of one row block of the other pending half (48 in all), and
+// the LDS reads run two steps ahead.  IGroupLP sched_group_barriers lay out
+// that pattern; sched_barrier(0) on both sides keeps each region a
+// scheduling unit of its own.
+
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+
+template <int READS_PER_STEP>
+__device__ __forceinline__ void region_schedule() {
+    __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * READS_PER_STEP, 0);
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-        const int db = t >> 2, kk = t & 3;
-        if (t < 15) {
-            const int db1 = (t + 1) >> 2, kk1 = (t + 1) & 3;
-            nxt = tr_read_pair(buf + off[db1] + kk1 * 16 * ROWB);
-        }
-        __builtin_amdgcn_sched_barrier(0);
+    for (int t = 0; t < 8; ++t) {
+        if (t < 6) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, READS_PER_STEP, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// S^T of one half tile (K rows of half buffer kb_, both row blocks) while
+// the weights of one row block (logits xs) of the other pending half are
+// computed.
+__device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff[8], const bf16x8 qb[2][8],
+                                         f32x16 s[2], const f32x16& xs, float m, float c2, bf16x8& p0,
+                                         bf16x8& p1, float& ls) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 ka[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) ka[ks] = *reinterpret_cast<const bf16x8*>(kb_ + koff[ks]);
+    const f32x16 zero = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
-            st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, pb[kk][rb], st.o[db][rb], 0, 0, 0);
-        cur = nxt;
+            s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
+    exp_rb(xs, m, c2, p0, p1, ls);
+    region_schedule<1>();
+}
+
+// O^T += V^T P^T over one half tile (V rows in half buffer vb_, P^T operands
+// pb[q2][rb]), with (EXP) the weights of one row block of the next half.
+template <bool EXP>
+__device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const uint32_t oa[4], const uint32_t ob[4],
+                                          const bf16x8 pb[2][2], const f32x16& xs, float m, float c2, bf16x8& p0,
+                                          bf16x8& p1, float& ls) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 va[2][4];
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+            va[q2][db] = tr_read_pair(vb_ + oa[db] + q2 * 16 * ROWB, vb_ + ob[db] + q2 * 16 * ROWB);
+#pragma unroll
+    for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb)
+                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q2][db], pb[q2][rb], st.o[db][rb], 0, 0, 0);
+    if (EXP) {
+        exp_rb(xs, m, c2, p0, p1, ls);
+        region_schedule<2>();
     }
 }
 
@@ -336,7 +403,7 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     s[kb][rb][r] = x;
                     m0 = fmaxf(m0, x);
                 }
-            mx[rb] = fmaxf(m0, swap_halves(m0));
+            mx[rb] = pair_max(m0);
             rescale_lazy(st, rb, mx[rb]);
         }
 #pragma unroll
@@ -360,7 +427,6 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     pb[rb][4 * kb + w] = static_cast<int>(pack_fp8x2<true>(y[2], y[3], lo));
                 }
             st.l[rb] += le;
-            st.le[rb] += le;
             sb[rb] = min(max(static_cast<int>(ct - mref) - 8 + 127, 0), 254);
         }
 #pragma unroll
@@ -372,49 +438,17 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
     }
 }
 
-// K tile A operands come from the row-major, swizzled LDS copy of K:
-// ka(kb, ks) = K[32kb + l32][16ks + 8h .. +7].  Lane offsets for ks = 0..7
-// (kb = 1 adds 32 rows); the swizzle depends on row & 7 = l32 & 7.
-__device__ __forceinline__ void k_offsets(uint32_t off[8]) {
-    const int l = lane_id(), h = l >> 5, l32 = l & 31;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) off[ks] = l32 * ROWB + 16 * swz(l32, 2 * ks + h);
-}
-
-__device__ __forceinline__ void s_tile_lds(const uint8_t* kbuf, const uint32_t koff[8], const bf16x8 qb[2][8],
-                                           f32x16 s[2][2]) {
-    const f32x16 zero = {};
-    // two k-steps of LDS reads in flight ahead of the MFMAs that use them
-    bf16x8 cur[2], nxt[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) cur[kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff[0] + kb * 32 * ROWB);
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-        if (ks < 7) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-                nxt[kb] = *reinterpret_cast<const bf16x8*>(kbuf + koff[ks + 1] + kb * 32 * ROWB);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur[kb], qb[rb][ks], ks ? s[kb][rb] : zero, 0, 0, 0);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) cur[kb] = nxt[kb];
-    }
-}
-
 template <int COMP, bool SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
-    // separate LDS objects so that the K and V copies are known not to alias
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf[TILEB];     // K tile (row-major, swizzled)
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf[TILEB];     // V tile (row-major, swizzled)
+    // separate LDS objects per half tile, so that each copy is known not to
+    // alias the reads of the other three
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf0[HALFB];    // K rows 0-31 (row-major, swizzled)
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf1[HALFB];    // K rows 32-63
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf0[HALFB];    // V rows 0-31
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf1[HALFB];    // V rows 32-63
     __shared__ uint32_t kept_mask[128];                              // blocks not compensated (nb <= 4096)
     __shared__ float wbuf_s[COMP == 1 ? BLK * (BLK + 1) : 1];        // order-1 weights [centroid][row]
     float* wbuf = wbuf_s;
-    struct { uint32_t* kept; } lds = {kept_mask};
 
     const int nq = a.N_pad / BLK, nb = nq;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -430,20 +464,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const size_t rowid = bh * nq + qa;
     const int cntE = a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0;
     const int32_t* listE = a.idx + rowid * a.cap;
+    const const_i32* lstE = (const const_i32*)listE;
     const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
     const int32_t* listM = SKIM ? a.idx2 + rowid * a.cap2 : nullptr;
 
-    uint32_t dmaoff[2], troff[4], koff[8];
+    uint32_t dmaoff[4], oa[4], ob[4], koff[8];
     dma_offsets(dmaoff);
-    pv_offsets(troff);
+    pv_offsets(oa, ob);
     k_offsets(koff);
-
-    // first exact tile in flight before anything else
-    if (cntE > 0) {
-        const int j0 = listE[0];
-        dma_v_tile(K + static_cast<size_t>(j0) * BLK * D, kbuf, dmaoff);
-        dma_v_tile(V + static_cast<size_t>(j0) * BLK * D, vbuf, dmaoff);
-    }
 
     // Q^T as B operands: qb[rb][ks] = Q[row 32rb + l32][16ks + 8h .. +7]
     bf16x8 qb[2][8];
@@ -454,21 +482,43 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int ks = 0; ks < 8; ++ks) {
             bf16x8 z = {};
             if (row < a.N) z = *reinterpret_cast<const bf16x8*>(Q + static_cast<size_t>(row) * D + 16 * ks + 8 * h);
-            qb[rb][ks] = z;
+            // Q^T only ever feeds MFMA B operands, which read AGPRs directly:
+            // keep it there and leave the VGPRs to the accumulators and weights.
+            u32x4 zu = __builtin_bit_cast(u32x4, z);
+            asm volatile("" : "+a"(zu));
+            qb[rb][ks] = __builtin_bit_cast(bf16x8, zu);
         }
     }
 
+    // K and V of this head as raw buffers (tile offsets are scalars)
+    const int slab = a.N_pad * ROWB;
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), 0, slab, RSRC_WORD3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V), 0, slab, RSRC_WORD3);
+
+    // First copies, in the order the steady state expects them:
+    // K(0, lo), V(0, hi) (in place of the previous tile's V, read with P = 0),
+    // K(0, hi), V(0, lo).
+    int j = 0;
+    if (cntE > 0) {
+        j = lstE[0];
+        const uint32_t t0 = static_cast<uint32_t>(j) * TILEB;
+        dma_half(rk, kbuf0, t0, dmaoff);
+        dma_half(rv, vbuf1, t0 + HALFB, dmaoff);
+        dma_half(rk, kbuf1, t0 + HALFB, dmaoff);
+        dma_half(rv, vbuf0, t0, dmaoff);
+    }
+
     // blocks that are not compensated (exact and skim lists)
-    for (int x = l; x < 128; x += 64) lds.kept[x] = 0u;
+    for (int x = l; x < 128; x += 64) kept_mask[x] = 0u;
     wave_lds_sync();
     if (COMP >= 0) {
         for (int e = l; e < cntE; e += 64) {
-            const int j = listE[e];
-            atomicOr(&lds.kept[j >> 5], 1u << (j & 31));
+            const int jj = listE[e];
+            atomicOr(&kept_mask[jj >> 5], 1u << (jj & 31));
         }
         for (int e = l; e < cntM; e += 64) {
-            const int j = listM[e];
-            atomicOr(&lds.kept[j >> 5], 1u << (j & 31));
+            const int jj = listM[e];
+            atomicOr(&kept_mask[jj >> 5], 1u << (jj & 31));
         }
         wave_lds_sync();
     }
@@ -480,125 +530,183 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int rb = 0; rb < 2; ++rb) st.o[db][rb] = f32x16{};
     st.m[0] = st.m[1] = M_INIT;
     st.l[0] = st.l[1] = 0.f;
-    st.le[0] = st.le[1] = 0.f;
 
-    // ---- phase 1: exact key blocks ----
-    // K and V each have one LDS buffer; each is refilled for the next tile as
-    // soon as this tile is done reading it, so the K copy overlaps softmax and
-    // PV, and the V copy overlaps the next S and softmax.
-    for (int e = 0; e < cntE; ++e) {
-        const int j = listE[e];
-        const int nj = min(BLK, a.N - BLK * j);
-        const bool more = e + 1 < cntE;
-        const int jn = more ? listE[e + 1] : j;
-        // K of this tile: only this tile's V copy may still be in flight
-        wait_vmcnt<16>();
-        wave_lds_sync();
-        f32x16 s[2][2];
-        s_tile_lds(kbuf, koff, qb, s);
-        wave_lds_sync();                                   // every lane's K reads have returned
-        if (more) dma_v_tile(K + static_cast<size_t>(jn) * BLK * D, kbuf, dmaoff);
-        if (nj < BLK) {                                    // ragged tail block only
+    // ---- phase 1: exact key blocks, pipelined over half tiles ----
+    // Copies in flight: each region waits for the copy it reads, issued three
+    // regions earlier; 24 dwordx4 loads (three half tiles) were issued after it.
+    if (cntE > 0) {
+        f32x16 s0[2], s1[2];                 // logits of the low / high key half
+        bf16x8 pb0[2][2], pb1[2][2];         // their bf16 weights [q2][rb]
+        float ls0[2], ls1[2];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+        for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                        if (key >= nj) s[kb][rb][r] = -INFINITY;
-                    }
+            for (int r = 0; r < 16; ++r) s1[rb][r] = -INFINITY;
+            pb1[0][rb] = bf16x8{};
+            pb1[1][rb] = bf16x8{};
+            ls1[rb] = 0.f;
         }
-        bf16x8 pb[4][2];
-        softmax_tile<false>(st, s, pb, c2, nullptr);
-        // V of this tile: only the next tile's K copy may still be in flight
-        if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
-        if (nj < BLK) zero_tail_rows(vbuf, nj);
+        int nj = min(BLK, a.N - BLK * j);
+        int nj_prev = nj;
+        for (int i = 0; i < cntE; ++i) {
+            const int jn = i + 1 < cntE ? lstE[i + 1] : j;    // the last tile copies itself again (never read)
+            const uint32_t tj = static_cast<uint32_t>(j) * TILEB, tn = static_cast<uint32_t>(jn) * TILEB;
+
+            // A: S(lo, i) | weights of (hi, i-1), row block 1
+            wait_vmcnt<24>();
+            wave_lds_sync();
+            region_s(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
+            wave_lds_sync();
+            dma_half(rk, kbuf0, tn, dmaoff);
+            settle_half(st, s1, c2, pb1, ls1);
+            if (nj < 32) mask_half(s0, 0, nj);
+
+            // B: PV(hi, i-1) | weights of (lo, i), row block 0
+            wait_vmcnt<24>();
+            if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
+            wave_lds_sync();
+            region_pv<true>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0]);
+            wave_lds_sync();
+            dma_half(rv, vbuf1, tj + HALFB, dmaoff);
+
+            // C: S(hi, i) | weights of (lo, i), row block 1
+            wait_vmcnt<24>();
+            wave_lds_sync();
+            region_s(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1]);
+            wave_lds_sync();
+            dma_half(rk, kbuf1, tn + HALFB, dmaoff);
+            settle_half(st, s0, c2, pb0, ls0);
+            if (nj < BLK) mask_half(s1, 32, nj);
+
+            // D: PV(lo, i) | weights of (hi, i), row block 0
+            wait_vmcnt<24>();
+            if (nj < 32) zero_rows(vbuf0, nj);
+            wave_lds_sync();
+            region_pv<true>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0]);
+            wave_lds_sync();
+            dma_half(rv, vbuf0, tn, dmaoff);
+
+            nj_prev = nj;
+            j = jn;
+            nj = min(BLK, a.N - BLK * j);
+        }
+        // drain: weights of (hi, last), row block 1, then PV(hi, last)
+        exp_rb(s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
+        settle_half(st, s1, c2, pb1, ls1);
+        wait_vmcnt<0>();
+        if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
         wave_lds_sync();
-        pv_tile(st, vbuf, troff, pb);
-        wave_lds_sync();                                   // every lane's V reads have returned
-        if (more) dma_v_tile(V + static_cast<size_t>(jn) * BLK * D, vbuf, dmaoff);
+        {
+            float unused_l;
+            bf16x8 unused0, unused1;
+            region_pv<false>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l);
+        }
+        wave_lds_sync();
     }
-    wait_vmcnt<0>();
 
     // ---- phase 1b: fp8 skim blocks (Triage's low-precision tier) ----
     if constexpr (SKIM) skim_tiles(a, st, bh, qa, listM, cntM, c2);
 
     // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
+    // Units of 32 centroids.  The centroid planes (bf16 high and low parts of
+    // the fp32 means, from the pooling pass) are copied into the four half
+    // buffers: K hi -> kbuf0, K lo -> kbuf1, V hi -> vbuf0, V lo -> vbuf1; the
+    // next unit's K planes load during this unit's softmax and PV, its V
+    // planes during the next S.
     if (COMP >= 0) {
-        const float* KB = a.kbar + bh * nb * D;
-        const float* VB = a.vbar + bh * nb * D;
-        for (int c0 = 0; c0 < nb; c0 += BLK) {
-            const int nc = min(BLK, nb - c0);
-            f32x16 s[2][2];
-            const f32x16 zero = {};
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-                const int cj = min(c0 + 32 * kb + l32, nb - 1);
+        const int nbc = BLK * ((nb + BLK - 1) / BLK);
+        const int nu = (nb + 31) / 32;
+        const uint16_t* C = static_cast<const uint16_t*>(a.cent) + bh * 4 * static_cast<size_t>(nbc) * D;
+        const __amdgpu_buffer_rsrc_t rc =
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(C), 0, 4 * nbc * ROWB, RSRC_WORD3);
+        const uint32_t plane = static_cast<uint32_t>(nbc) * ROWB;
+        const int nlast = a.N - BLK * (nb - 1);
+        const float blast = __log2f(static_cast<float>(nlast));   // log2 n_j of the last block
+        dma_half(rc, kbuf0, 0, dmaoff);
+        dma_half(rc, kbuf1, plane, dmaoff);
+        dma_half(rc, vbuf0, 2 * plane, dmaoff);
+        dma_half(rc, vbuf1, 3 * plane, dmaoff);
+        for (int u = 0; u < nu; ++u) {
+            const bool more = u + 1 < nu;
+            const uint32_t un = static_cast<uint32_t>(more ? u + 1 : u) * HALFB;
+            // K planes of unit u: only its V planes were issued after them
+            wait_vmcnt<16>();
+            wave_lds_sync();
+            f32x16 s[2];
+            {
+                bf16x8 khi[8], klo[8];
 #pragma unroll
                 for (int ks = 0; ks < 8; ++ks) {
-                    const float4 x0 = *reinterpret_cast<const float4*>(KB + static_cast<size_t>(cj) * D + 16 * ks + 8 * h);
-                    const float4 x1 = *reinterpret_cast<const float4*>(KB + static_cast<size_t>(cj) * D + 16 * ks + 8 * h + 4);
-                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                    u32x4 whi, wlo;
+                    khi[ks] = *reinterpret_cast<const bf16x8*>(kbuf0 + koff[ks]);
+                    klo[ks] = *reinterpret_cast<const bf16x8*>(kbuf1 + koff[ks]);
+                }
+                const f32x16 zero = {};
 #pragma unroll
-                    for (int t = 0; t < 4; ++t) {
-                        whi[t] = pack_bf16x2(x[2 * t], x[2 * t + 1]);
-                        const float r0 = x[2 * t] - bf16_to_f32(static_cast<uint16_t>(whi[t] & 0xFFFFu));
-                        const float r1 = x[2 * t + 1] - bf16_to_f32(static_cast<uint16_t>(whi[t] >> 16));
-                        wlo[t] = pack_bf16x2(r0, r1);
-                    }
-                    const bf16x8 khi = __builtin_bit_cast(bf16x8, whi), klo = __builtin_bit_cast(bf16x8, wlo);
+                for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb) {
-                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi, qb[rb][ks], ks ? s[kb][rb] : zero, 0, 0, 0);
-                        s[kb][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo, qb[rb][ks], s[kb][rb], 0, 0, 0);
+                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
+                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[ks], qb[rb][ks], s[rb], 0, 0, 0);
                     }
-                }
             }
-            float bias[2][16];
+            wave_lds_sync();
+            if (more) {
+                dma_half(rc, kbuf0, un, dmaoff);
+                dma_half(rc, kbuf1, plane + un, dmaoff);
+            }
+            // logits in log2 units with the count bias; -inf at exact / skim / pad centroids
+            const uint32_t keptw = kept_mask[u];
+            float bias[16];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int r = 0; r < 16; ++r) {
+                const int cc = 8 * (r >> 2) + 4 * h + (r & 3);
+                const int jj = 32 * u + cc;
+                const bool comp = jj < nb && !((keptw >> cc) & 1u);
+                bias[r] = !comp ? -INFINITY : (jj == nb - 1 ? blast : 6.0f);   // log2 64 = 6
+            }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int jj = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    float bv = -INFINITY;
-                    if (jj < nb && !((lds.kept[jj >> 5] >> (jj & 31)) & 1u))
-                        bv = __log2f(static_cast<float>(min(BLK, a.N - BLK * jj)));
-                    bias[kb][r] = bv;
-                }
-            bf16x8 pb[4][2];
-            softmax_tile<true>(st, s, pb, c2, bias);
+            for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) s[rb][r] = fmaf(s[rb][r], c2, bias[r]);
+            bf16x8 pb[2][2];
+            float ls[2];
+#pragma unroll
+            for (int rb = 0; rb < 2; ++rb) exp_rb(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
+            settle_half(st, s, 1.0f, pb, ls);
             if (COMP == 1) {
                 // order-1 weights w = scale * 2^{L - m} / n_j (L without the count bias)
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
+                for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                    for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                        for (int r = 0; r < 16; ++r) {
-                            const int cc = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                            const float x = (bias[kb][r] == -INFINITY) ? 0.f
-                                : __builtin_amdgcn_exp2f(s[kb][rb][r] - bias[kb][r] - st.m[rb]) * a.scale;
-                            wbuf[cc * (BLK + 1) + 32 * rb + l32] = x;
-                        }
+                    for (int r = 0; r < 16; ++r) {
+                        const int cc = 8 * (r >> 2) + 4 * h + (r & 3);
+                        const float x = (bias[r] == -INFINITY) ? 0.f
+                            : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]) * a.scale;
+                        wbuf[cc * (BLK + 1) + 32 * rb + l32] = x;
+                    }
             }
-            stage_means<false>(VB + static_cast<size_t>(c0) * D, nc, vbuf);
+            // V planes of unit u: only the next unit's K planes may still be in flight
+            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
             wave_lds_sync();
-            pv_tile(st, vbuf, troff, pb);
+            {
+                float unused_l;
+                bf16x8 unused0, unused1;
+                region_pv<false>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l);
+                region_pv<false>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l);
+            }
             wave_lds_sync();
-            stage_means<true>(VB + static_cast<size_t>(c0) * D, nc, vbuf);
-            wave_lds_sync();
-            pv_tile(st, vbuf, troff, pb);
-            wave_lds_sync();
+            if (more) {
+                dma_half(rc, vbuf0, 2 * plane + un, dmaoff);
+                dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
+            }
             if (COMP == 1) {
-                // O^T += H_j^T (Q^T diag(w_j)) for every compensated block of this tile:
+                // O^T += H_j^T (Q^T diag(w_j)) for every compensated block of this unit:
                 // the per-row weight scales the B operand, so the MFMA accumulates
                 // straight into O.
                 const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom);
-                for (int cc = 0; cc < nc; ++cc) {
-                    const int jj = c0 + cc;
-                    if ((lds.kept[jj >> 5] >> (jj & 31)) & 1u) continue;
+                for (int cc = 0; cc < 32; ++cc) {
+                    const int jj = 32 * u + cc;
+                    if (jj >= nb || ((keptw >> cc) & 1u)) continue;
                     const uint16_t* Hj = MOM + (bh * nb + jj) * static_cast<size_t>(D) * D;
                     const float w[2] = {wbuf[cc * (BLK + 1) + l32], wbuf[cc * (BLK + 1) + 32 + l32]};
                     bf16x8 qs[2][8];
@@ -630,14 +738,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 wave_lds_sync();
             }
         }
+        wait_vmcnt<0>();
     }
 
     // ---- normalise and write O (bf16) and lse ----
     uint16_t* O = static_cast<uint16_t*>(a.out) + head;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        const float lt = st.l[rb] + swap_halves(st.l[rb]);
-        const float le = st.le[rb] + swap_halves(st.le[rb]);
+        const float lt = pair_sum(st.l[rb]);
         const int row = qa * BLK + 32 * rb + l32;
         const bool valid = row < a.N;
         const float inv = valid ? 1.0f / lt : 0.f;
@@ -652,7 +760,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 *reinterpret_cast<uint2*>(O + static_cast<size_t>(row) * D + dd) = w;
             }
         }
-        if (a.lse && h == 0) a.lse[bh * a.N_pad + row] = valid ? (st.m[rb] + __log2f(le)) * LN2 : 0.f;
+        if (a.lse && h == 0) a.lse[bh * a.N_pad + row] = valid ? (st.m[rb] + __log2f(lt)) * LN2 : 0.f;
     }
 }
 

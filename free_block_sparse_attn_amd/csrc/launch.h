@@ -17,6 +17,7 @@ struct PoolArgs {
     float* kbar;
     float* vbar;
     int32_t* kcount;
+    void* cent;       // bf16 [B,H,4,nbc,d] centroid planes, or null
     void* kmom;       // bf16 [B,H,nb,d,d] value-major, or null
     float* klam;      // [B,H,nb] or null
     uint8_t* q8;      // e4m3 copies or null (all or none)
@@ -57,6 +58,7 @@ struct FwdArgs {
     const void* v;
     const float* kbar;
     const float* vbar;
+    const void* cent;         // bf16 centroid planes (bf16 path)
     const int32_t* kcount;
     const void* kmom;
     const uint8_t* q8;

@@ -38,6 +38,17 @@ template <> struct Elem<uint16_t> {
 };
 
 constexpr int THREADS = 256;
+
+// Centroid planes of one (b, h): plane p row j at cent + ((bh * 4 + p) * nbc + j) * D.
+__device__ __forceinline__ uint16_t* cent_row(void* cent, size_t bh, int plane, int nbc, int j, int D) {
+    return static_cast<uint16_t*>(cent) + ((bh * 4 + plane) * nbc + static_cast<size_t>(j)) * D;
+}
+
+// bf16 high part and residual of an fp32 mean (m - hi is exact in fp32).
+__device__ __forceinline__ void split_hi_lo(float m, uint16_t& hi, uint16_t& lo) {
+    hi = f32_to_bf16(m);
+    lo = f32_to_bf16(m - bf16_to_f32(hi));
+}
 constexpr int TPITCH = BLK + 8;     // transposed row pitch in elements (16-byte multiple)
 
 template <typename T, int D>
@@ -70,8 +81,14 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
     const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int nb = a.N_pad / BLK;
-    const int n = min(BLK, a.N - BLK * j);
+    const int nbc = BLK * ((nb + BLK - 1) / BLK);
     const size_t bh = static_cast<size_t>(b) * a.H + h;
+    if (j >= nb) {
+        // centroid pad rows (only launched when cent is requested)
+        for (int x = tid; x < 4 * D; x += THREADS) cent_row(a.cent, bh, x / D, nbc, j, D)[x % D] = 0;
+        return;
+    }
+    const int n = min(BLK, a.N - BLK * j);
     const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
 
     const T* src[3] = {static_cast<const T*>(a.q), static_cast<const T*>(a.k), static_cast<const T*>(a.v)};
@@ -116,6 +133,12 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
         const int t = task / D, i = task % D;
         float* dst = (t == 0) ? a.qbar : (t == 1) ? a.kbar : a.vbar;
         dst[(bh * nb + j) * D + i] = m;
+        if (a.cent && t > 0) {
+            uint16_t hi, lo;
+            split_hi_lo(m, hi, lo);
+            cent_row(a.cent, bh, 2 * (t - 1), nbc, j, D)[i] = hi;
+            cent_row(a.cent, bh, 2 * (t - 1) + 1, nbc, j, D)[i] = lo;
+        }
     }
     if (b == 0 && h == 0 && tid == 0) a.kcount[j] = n;
     __syncthreads();
@@ -280,8 +303,19 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
     const int nb = a.N_pad / BLK;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int j = (blockIdx.x * 4 + wave) * BPW + lane / CPR;
-    if (j >= nb) return;
     const int col0 = (lane % CPR) * PER16;
+    const int nbc = BLK * ((nb + BLK - 1) / BLK);
+    if (j >= nb) {
+        // centroid pad rows (the grid covers nbc blocks when cent is requested)
+        if constexpr (sizeof(T) == 2 && D == 128) {
+            if (a.cent && tensor > 0 && j < nbc) {
+                const u32x4 z = {0u, 0u, 0u, 0u};
+                *reinterpret_cast<u32x4*>(cent_row(a.cent, bh, 2 * (tensor - 1), nbc, j, D) + col0) = z;
+                *reinterpret_cast<u32x4*>(cent_row(a.cent, bh, 2 * (tensor - 1) + 1, nbc, j, D) + col0) = z;
+            }
+        }
+        return;
+    }
     const int n = min(BLK, a.N - BLK * j);
     const T* src = static_cast<const T*>(tensor == 0 ? a.q : tensor == 1 ? a.k : a.v) +
                    (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D + col0;
@@ -305,14 +339,28 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
         }
     }
     float* dst = (tensor == 0 ? a.qbar : tensor == 1 ? a.kbar : a.vbar) + (bh * nb + j) * D + col0;
+    float mv[PER16];
+#pragma unroll
+    for (int e = 0; e < PER16; ++e) mv[e] = static_cast<float>(acc[e] / static_cast<double>(n));
 #pragma unroll
     for (int e = 0; e < PER16; e += 4) {
-        float4 m;
-        m.x = static_cast<float>(acc[e] / static_cast<double>(n));
-        m.y = static_cast<float>(acc[e + 1] / static_cast<double>(n));
-        m.z = static_cast<float>(acc[e + 2] / static_cast<double>(n));
-        m.w = static_cast<float>(acc[e + 3] / static_cast<double>(n));
+        const float4 m = {mv[e], mv[e + 1], mv[e + 2], mv[e + 3]};
         *reinterpret_cast<float4*>(dst + e) = m;
+    }
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (a.cent && tensor > 0) {
+            u32x4 whi, wlo;
+#pragma unroll
+            for (int e = 0; e < PER16; e += 2) {
+                uint16_t h0, l0, h1, l1;
+                split_hi_lo(mv[e], h0, l0);
+                split_hi_lo(mv[e + 1], h1, l1);
+                whi[e >> 1] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+                wlo[e >> 1] = static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+            }
+            *reinterpret_cast<u32x4*>(cent_row(a.cent, bh, 2 * (tensor - 1), nbc, j, D) + col0) = whi;
+            *reinterpret_cast<u32x4*>(cent_row(a.cent, bh, 2 * (tensor - 1) + 1, nbc, j, D) + col0) = wlo;
+        }
     }
     if (tensor == 0 && bh == 0 && (lane % CPR) == 0) a.kcount[j] = n;
 }
@@ -322,12 +370,14 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
     if (!a.kmom && !a.klam && !a.q8) {
         constexpr int BPW = 64 / (D / Elem<T>::PER16);
         const int nb = a.N_pad / BLK;
-        dim3 grid((nb + 4 * BPW - 1) / (4 * BPW), 3, a.B * a.H);
+        const int rows = a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb;   // centroid pad rows too
+        dim3 grid((rows + 4 * BPW - 1) / (4 * BPW), 3, a.B * a.H);
         hipLaunchKernelGGL((pool_means_kernel<T, D>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
     const size_t lds = pool_lds<T, D>();
-    dim3 grid(a.N_pad / BLK, a.H, a.B);
+    const int nb = a.N_pad / BLK;
+    dim3 grid(a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb, a.H, a.B);
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 1
+#define SPARSE_ATTN_ABI_VERSION 2
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -99,6 +99,14 @@ typedef struct {
  *                        routing features; they are bit-reproducible.
  *   kcount               int32 [nb]       n_j (same for every b, h).
  * Outputs (optional, NULL to skip)
+ *   cent                 bf16 [B,H,4,nbc,d], nbc = 64 * ceil(nb / 64): the
+ *                        centroids in the form the bf16 forward pass reads.
+ *                        With m the fp32 mean above, hi = bf16_rne(m) and
+ *                        lo = bf16_rne(m - hi) (the difference is exact in
+ *                        fp32), so hi + lo carries m to about 16 bits:
+ *                        plane 0 hi(k_bar), 1 lo(k_bar), 2 hi(v_bar),
+ *                        3 lo(v_bar); rows nb .. nbc-1 are 0.  bf16 inputs
+ *                        with d == 128 only.
  *   kmom                 bf16 [B,H,nb,d,d]  moment of block j stored
  *                        value-major: kmom[..., o, i] =
  *                        sum_n (k_n[i] - k_bar_j[i]) v_n[o]   (H_j transposed).
@@ -121,7 +129,7 @@ typedef struct {
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount,
-                           void* kmom, float* klam,
+                           void* cent, void* kmom, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
                            hipStream_t stream);
 
@@ -194,7 +202,12 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *   order0  sum_{j in U} n_j e^{scale q.k_bar_j} (v_bar_j)         comp >= 0
  *   order1  sum_{j in U} e^{scale q.k_bar_j} scale q^T H_j  (N only)  comp == 1
  *
- * q, k, v    dtype [B,H,N_pad,d]        kbar, vbar fp32 [B,H,nb,d]
+ * scale      softmax scale, finite and > 0
+ * q, k, v    dtype [B,H,N_pad,d]
+ * kbar, vbar fp32 [B,H,nb,d] centroids (SA_F32 with comp >= 0; unused by
+ *            SA_BF16, may be NULL there)
+ * cent       bf16 [B,H,4,nbc,d] centroid planes from sparse_attn_pool
+ *            (SA_BF16 with comp >= 0; unused by SA_F32)
  * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d,d] (comp == 1)
  * q8, k8, v8, exp8                      from sparse_attn_pool (skim only)
  * idx, cnt, cap     exact lists (ascending, entries in [0, nb))
@@ -205,12 +218,13 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *            pad rows are written as 0.
  * A row's count is clamped to its cap.  Every row must hold at least one
  * exact or skim block when comp == SA_COMP_DROP.
- * Supported: SA_F32 with d in {64, 128} (no skim); SA_BF16 with d == 128.
+ * Supported: SA_F32 with d == 64 (comp <= 0, no skim); SA_BF16 with
+ * d == 128.
  */
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale,
                           const void* q, const void* k, const void* v,
-                          const float* kbar, const float* vbar, const int32_t* kcount,
-                          const void* kmom,
+                          const float* kbar, const float* vbar, const void* cent,
+                          const int32_t* kcount, const void* kmom,
                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                           const int8_t* exp8,
                           const int32_t* idx, const int32_t* cnt, int32_t cap,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 1
+    assert lib.sparse_attn_abi_version() == 2
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -46,11 +46,12 @@ MIS = ctypes.c_void_p(4097)
 
 
 def pool(lib, sh, dtype=1, **kw):
-    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, kmom=None, klam=None,
+    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, klam=None,
              q8=None, k8=None, v8=None, exp8=None)
     a.update(kw)
     return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
-                                a["kcount"], a["kmom"], a["klam"], a["q8"], a["k8"], a["v8"], a["exp8"], None)
+                                a["kcount"], a["cent"], a["kmom"], a["klam"], a["q8"], a["k8"], a["v8"],
+                                a["exp8"], None)
 
 
 def test_pool_rejects_bad_arguments(lib):
@@ -61,10 +62,13 @@ def test_pool_rejects_bad_arguments(lib):
     assert pool(lib, shape(), dtype=7) == 1
     assert pool(lib, shape(), q=None) == 1
     assert pool(lib, shape(), kbar=MIS) == 1
+    assert b"kbar" in lib.sparse_attn_last_error()
     assert pool(lib, shape(), q8=P) == 1                     # fp8 copies: all four or none
     assert pool(lib, shape(), dtype=0, kmom=P) == 2          # moments need bf16, d=128
     assert pool(lib, shape(d=64), kmom=P) == 2
-    assert b"kbar" in lib.sparse_attn_last_error() or True
+    assert pool(lib, shape(), dtype=0, cent=P) == 2          # centroid planes need bf16, d=128
+    assert pool(lib, shape(d=64), cent=P) == 2
+    assert pool(lib, shape(), cent=MIS) == 1
     assert pool(lib, shape(B=0)) == 0                        # empty problem: nothing launched
     assert pool(lib, shape(N=0, N_pad=0)) == 0
 
@@ -95,11 +99,11 @@ def test_route_rejects_bad_arguments(lib):
 
 
 def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
-    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, kcount=P, kmom=None, q8=None, k8=None, v8=None, exp8=None,
-             idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
+    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, kcount=P, kmom=None, q8=None, k8=None, v8=None,
+             exp8=None, idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
     a.update(kw)
     return lib.sparse_attn_fwd(sh, dtype, comp, scale, a["q"], a["k"], a["v"], a["kbar"], a["vbar"],
-                               a["kcount"], a["kmom"], a["q8"], a["k8"], a["v8"], a["exp8"], a["idx"],
+                               a["cent"], a["kcount"], a["kmom"], a["q8"], a["k8"], a["v8"], a["exp8"], a["idx"],
                                a["cnt"], a["cap"], a["idx2"], a["cnt2"], a["cap2"], a["out"], a["lse"], None)
 
 
@@ -108,7 +112,10 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, shape(), comp=1) == 1                     # order 1 without kmom
     assert fwd(lib, shape(), scale=float("inf")) == 1
     assert fwd(lib, shape(), out=None) == 1
-    assert fwd(lib, shape(), kbar=None) == 1                  # order 0 needs the means
+    assert fwd(lib, shape(), cent=None) == 1                  # bf16 order 0 needs the centroid planes
+    assert fwd(lib, shape(d=64), dtype=0, kbar=None) == 1     # fp32 order 0 needs the means
+    assert fwd(lib, shape(), scale=0.0) == 1                  # scale must be > 0
+    assert fwd(lib, shape(), scale=-1.0) == 1
     assert fwd(lib, shape(), cap=-1) == 1
     assert fwd(lib, shape(), comp=-1, cap=0, idx=None, cnt=None) == 1   # nothing to attend to
     assert fwd(lib, shape(d=64)) == 2                         # bf16 needs d = 128

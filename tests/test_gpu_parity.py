@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 1
+    assert fbsa.abi_version() == 2
 
 
 def medium(wid):
@@ -34,6 +34,17 @@ def check_pool(wl, pooled_o, res):
     assert np.array_equal(res["kcount"], pooled_o["kcount"])
     for n in ("qbar", "kbar", "vbar"):
         assert np.array_equal(res[n], pooled_o[n]), n          # bit-exact contract
+    if "cent" in res:
+        # bf16 high part and residual of the fp32 means; rows nb .. nbc-1 zero
+        from workloads.fields import round_to_bf16
+        nb = pooled_o["kbar"].shape[2]
+        for p, n in ((0, "kbar"), (2, "vbar")):
+            m = pooled_o[n].astype(np.float32)
+            hi = round_to_bf16(m)
+            lo = round_to_bf16((m - hi).astype(np.float32))
+            assert np.array_equal(res["cent"][:, :, p, :nb], hi), n
+            assert np.array_equal(res["cent"][:, :, p + 1, :nb], lo), n
+        assert not np.any(res["cent"][:, :, :, nb:]), "centroid pad rows"
     if "kmom" in res:
         ref = np.swapaxes(pooled_o["kmom"], -1, -2)               # value-major layout
         err = np.abs(res["kmom"].astype(np.float64) - ref)
