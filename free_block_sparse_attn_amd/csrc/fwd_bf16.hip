@@ -262,33 +262,43 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* pa, const uint8_t*
 // ---- the four MFMA regions of the exact-tile pipeline ----
 //
 // Each region issues 16 MFMAs; after each MFMA come three VALU instructions
-// of the weights of one row block of the other pending half (48 in all), and
-// the LDS reads run two steps ahead.  IGroupLP sched_group_barriers lay out
-// that pattern; sched_barrier(0) on both sides keeps each region a
-// scheduling unit of its own.
+// of the weights of one row block of the other pending half (48 in all), the
+// LDS reads run two steps ahead, and the eight buffer_load ... lds of one
+// half-tile copy (into the buffer the previous region finished reading) sit
+// between the MFMAs of the first half of the region.  IGroupLP
+// sched_group_barriers lay out that pattern; sched_barrier(0) on both sides
+// keeps each region a scheduling unit of its own.
 
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_DS_READ = 0x100;
+constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-template <int READS_PER_STEP>
+template <int READS_PER_STEP, bool EXP, bool COPY>
 __device__ __forceinline__ void region_schedule() {
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * READS_PER_STEP, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         if (t < 6) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, READS_PER_STEP, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        if (EXP) __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        if (COPY) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        if (EXP) __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// One half-tile copy issued inside a region.
+struct Copy {
+    __amdgpu_buffer_rsrc_t rs;
+    uint8_t* dst;
+    uint32_t src;
+};
+
 // S^T of one half tile (K rows of half buffer kb_, both row blocks) while
 // the weights of one row block (logits xs) of the other pending half are
-// computed.
+// computed and the copy cp is issued.
 __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff[8], const bf16x8 qb[2][8],
                                          f32x16 s[2], const f32x16& xs, float m, float c2, bf16x8& p0,
-                                         bf16x8& p1, float& ls) {
+                                         bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 ka[8];
 #pragma unroll
@@ -300,15 +310,17 @@ __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff
         for (int rb = 0; rb < 2; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
     exp_rb(xs, m, c2, p0, p1, ls);
-    region_schedule<1>();
+    dma_half(cp.rs, cp.dst, cp.src, dmaoff);
+    region_schedule<1, true, true>();
 }
 
 // O^T += V^T P^T over one half tile (V rows in half buffer vb_, P^T operands
-// pb[q2][rb]), with (EXP) the weights of one row block of the next half.
-template <bool EXP>
+// pb[q2][rb]), with (EXP) the weights of one row block of the next half and
+// (COPY) one half-tile copy.
+template <bool EXP, bool COPY>
 __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const uint32_t oa[4], const uint32_t ob[4],
                                           const bf16x8 pb[2][2], const f32x16& xs, float m, float c2, bf16x8& p0,
-                                          bf16x8& p1, float& ls) {
+                                          bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 va[2][4];
 #pragma unroll
@@ -323,10 +335,9 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
                 st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q2][db], pb[q2][rb], st.o[db][rb], 0, 0, 0);
-    if (EXP) {
-        exp_rb(xs, m, c2, p0, p1, ls);
-        region_schedule<2>();
-    }
+    if (EXP) exp_rb(xs, m, c2, p0, p1, ls);
+    if (COPY) dma_half(cp.rs, cp.dst, cp.src, dmaoff);
+    if (EXP || COPY) region_schedule<2, EXP, COPY>();
 }
 
 // fp8 e4m3 skim tiles with per-block power-of-two scales (E8M0 operand
@@ -495,9 +506,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(K), 0, slab, RSRC_WORD3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(V), 0, slab, RSRC_WORD3);
 
-    // First copies, in the order the steady state expects them:
-    // K(0, lo), V(0, hi) (in place of the previous tile's V, read with P = 0),
-    // K(0, hi), V(0, lo).
+    // First copies, in the order the steady state expects them: K(0, lo),
+    // V(0, hi) (in place of the previous tile's V, read with P = 0), K(0, hi);
+    // region A of the first tile issues V(0, lo).
     int j = 0;
     if (cntE > 0) {
         j = lstE[0];
@@ -505,7 +516,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         dma_half(rk, kbuf0, t0, dmaoff);
         dma_half(rv, vbuf1, t0 + HALFB, dmaoff);
         dma_half(rk, kbuf1, t0 + HALFB, dmaoff);
-        dma_half(rv, vbuf0, t0, dmaoff);
     }
 
     // blocks that are not compensated (exact and skim lists)
@@ -532,8 +542,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     st.l[0] = st.l[1] = 0.f;
 
     // ---- phase 1: exact key blocks, pipelined over half tiles ----
-    // Copies in flight: each region waits for the copy it reads, issued three
-    // regions earlier; 24 dwordx4 loads (three half tiles) were issued after it.
+    // Each region refills the buffer the previous region read:
+    //   A(i): V(i, lo) -> vbuf0      B(i): K(i+1, lo) -> kbuf0
+    //   C(i): V(i, hi) -> vbuf1      D(i): K(i+1, hi) -> kbuf1
+    // so every copy has two regions to land, and when a region starts two
+    // half-tile copies (16 dwordx4 loads) were issued after the one it reads.
     if (cntE > 0) {
         f32x16 s0[2], s1[2];                 // logits of the low / high key half
         bf16x8 pb0[2][2], pb1[2][2];         // their bf16 weights [q2][rb]
@@ -552,39 +565,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             const int jn = i + 1 < cntE ? lstE[i + 1] : j;    // the last tile copies itself again (never read)
             const uint32_t tj = static_cast<uint32_t>(j) * TILEB, tn = static_cast<uint32_t>(jn) * TILEB;
 
-            // A: S(lo, i) | weights of (hi, i-1), row block 1
-            wait_vmcnt<24>();
+            // A: S(lo, i) | weights of (hi, i-1), row block 1 | copy V(i, lo)
+            wait_vmcnt<16>();
             wave_lds_sync();
-            region_s(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
-            wave_lds_sync();
-            dma_half(rk, kbuf0, tn, dmaoff);
+            region_s(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1],
+                     Copy{rv, vbuf0, tj}, dmaoff);
             settle_half(st, s1, c2, pb1, ls1);
             if (nj < 32) mask_half(s0, 0, nj);
 
-            // B: PV(hi, i-1) | weights of (lo, i), row block 0
-            wait_vmcnt<24>();
+            // B: PV(hi, i-1) | weights of (lo, i), row block 0 | copy K(i+1, lo)
+            wait_vmcnt<16>();
             if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
             wave_lds_sync();
-            region_pv<true>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0]);
-            wave_lds_sync();
-            dma_half(rv, vbuf1, tj + HALFB, dmaoff);
+            region_pv<true, true>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0],
+                                  Copy{rk, kbuf0, tn}, dmaoff);
 
-            // C: S(hi, i) | weights of (lo, i), row block 1
-            wait_vmcnt<24>();
+            // C: S(hi, i) | weights of (lo, i), row block 1 | copy V(i, hi)
+            wait_vmcnt<16>();
             wave_lds_sync();
-            region_s(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1]);
-            wave_lds_sync();
-            dma_half(rk, kbuf1, tn + HALFB, dmaoff);
+            region_s(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1],
+                     Copy{rv, vbuf1, tj + HALFB}, dmaoff);
             settle_half(st, s0, c2, pb0, ls0);
             if (nj < BLK) mask_half(s1, 32, nj);
 
-            // D: PV(lo, i) | weights of (hi, i), row block 0
-            wait_vmcnt<24>();
+            // D: PV(lo, i) | weights of (hi, i), row block 0 | copy K(i+1, hi)
+            wait_vmcnt<16>();
             if (nj < 32) zero_rows(vbuf0, nj);
             wave_lds_sync();
-            region_pv<true>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0]);
-            wave_lds_sync();
-            dma_half(rv, vbuf0, tn, dmaoff);
+            region_pv<true, true>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0],
+                                  Copy{rk, kbuf1, tn + HALFB}, dmaoff);
 
             nj_prev = nj;
             j = jn;
@@ -599,7 +608,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         {
             float unused_l;
             bf16x8 unused0, unused1;
-            region_pv<false>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l);
+            region_pv<false, false>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l,
+                                    Copy{rv, vbuf1, 0}, dmaoff);
         }
         wave_lds_sync();
     }
@@ -691,8 +701,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             {
                 float unused_l;
                 bf16x8 unused0, unused1;
-                region_pv<false>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l);
-                region_pv<false>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l);
+                region_pv<false, false>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
+                                        Copy{rc, vbuf0, 0}, dmaoff);
+                region_pv<false, false>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
+                                        Copy{rc, vbuf1, 0}, dmaoff);
             }
             wave_lds_sync();
             if (more) {
