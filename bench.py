@@ -80,6 +80,8 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a 1 GiB device-to-device copy (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
@@ -169,7 +171,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, q, k, v)
-    print(json.dumps(line))
+    print(json.dumps(line), flush=True)
+    if args.copy_calibration:
+        x = torch.ones(1 << 29, dtype=torch.int16, device=dev)       # 1 GiB
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
