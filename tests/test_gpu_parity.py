@@ -143,7 +143,8 @@ def test_parity_full_size_sampled(wid):
         rsub = {n: (x[:, heads] if n not in ("kcount",) else x) for n, x in res.items()}
         check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount")})
         if wl.rule == "triage":
-            check_pool(wl, pooled_o, {n: rsub[n] for n in ("klam", "q8", "exp8", "kcount", "qbar", "kbar", "vbar")})
+            check_pool(wl, pooled_o, {n: rsub[n] for n in ("klam", "q8", "k8", "v8", "exp8", "kcount",
+                                                           "qbar", "kbar", "vbar")})
         check_route(wl, pooled_o, rsub, coords, step)
         rows = [(0, hi, int(a)) for hi in range(len(heads)) for a in rng.choice(wl.nb, 3, replace=False)]
         rows.append((0, 0, wl.nb - 1))                                  # ragged tail block
