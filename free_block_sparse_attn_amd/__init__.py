@@ -90,7 +90,7 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
         nbc = BLK * ((nb + BLK - 1) // BLK)
         out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.bfloat16, device=dev)
     if moments:
-        out["kmom"] = torch.empty(B, H, nb, d, d, dtype=torch.bfloat16, device=dev)
+        out["kmom"] = torch.empty(B, H, nb, d * d, dtype=torch.bfloat16, device=dev)   # MFMA operand order
     if spreads:
         out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
     if fp8:

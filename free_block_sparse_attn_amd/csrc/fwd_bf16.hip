@@ -458,8 +458,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     __shared__ __attribute__((aligned(16))) uint8_t vbuf0[HALFB];    // V rows 0-31
     __shared__ __attribute__((aligned(16))) uint8_t vbuf1[HALFB];    // V rows 32-63
     __shared__ uint32_t kept_mask[128];                              // blocks not compensated (nb <= 4096)
-    __shared__ float wbuf_s[COMP == 1 ? BLK * (BLK + 1) : 1];        // order-1 weights [centroid][row]
-    float* wbuf = wbuf_s;
+    // order-1 weights of 16 centroids, fp32 [centroid][row] (4 KiB: the LDS
+    // footprint stays within four workgroups per CU)
+    __shared__ float wbuf[COMP == 1 ? 16 * BLK : 1];
 
     const int nq = a.N_pad / BLK, nb = nq;
     const int lin = xcd_remap(blockIdx.x, gridDim.x);
@@ -683,18 +684,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) exp_rb(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
             settle_half(st, s, 1.0f, pb, ls);
-            if (COMP == 1) {
-                // order-1 weights w = scale * 2^{L - m} / n_j (L without the count bias)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int cc = 8 * (r >> 2) + 4 * h + (r & 3);
-                        const float x = (bias[r] == -INFINITY) ? 0.f
-                            : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]) * a.scale;
-                        wbuf[cc * (BLK + 1) + 32 * rb + l32] = x;
-                    }
-            }
             // V planes of unit u: only the next unit's K planes may still be in flight
             if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
             wave_lds_sync();
@@ -712,42 +701,72 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
             }
             if (COMP == 1) {
-                // O^T += H_j^T (Q^T diag(w_j)) for every compensated block of this unit:
-                // the per-row weight scales the B operand, so the MFMA accumulates
-                // straight into O.
-                const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom);
-                for (int cc = 0; cc < 32; ++cc) {
-                    const int jj = 32 * u + cc;
-                    if (jj >= nb || ((keptw >> cc) & 1u)) continue;
-                    const uint16_t* Hj = MOM + (bh * nb + jj) * static_cast<size_t>(D) * D;
-                    const float w[2] = {wbuf[cc * (BLK + 1) + l32], wbuf[cc * (BLK + 1) + 32 + l32]};
-                    bf16x8 qs[2][8];
+                // O^T[., row] += w_j[row] T, T = H_j^T Q^T (fp32, 16 MFMAs per
+                // 32-wide d block), for every compensated block j of this unit,
+                // with w_j = scale 2^{L - m} / n_j (L without the count bias).
+                // Two batches of 16 centroids (their weights staged in LDS); the A
+                // operands (H_j^T in MFMA operand order) load two d blocks ahead.
+                const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom) + bh * nb * static_cast<size_t>(D) * D;
+                // H_j^T in MFMA operand order: (d block, i step) operands are 1 KiB runs
+                auto load_step = [&](int jj, int db, bf16x8 op[8]) __attribute__((always_inline)) {
+                    const uint16_t* Hop = MOM + static_cast<size_t>(jj) * D * D + (db * 8 * 64 + l) * 8;
+#pragma unroll
+                    for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const bf16x8*>(Hop + ks * 64 * 8);
+                };
+#pragma unroll
+                for (int hb = 0; hb < 2; ++hb) {
+                    // accumulator entries r = 8 hb .. 8 hb + 7 hold centroids 16 hb .. 16 hb + 15
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                        for (int ks = 0; ks < 8; ++ks) {
-                            const u32x4 qw = __builtin_bit_cast(u32x4, qb[rb][ks]);
-                            u32x4 o;
-#pragma unroll
-                            for (int t = 0; t < 4; ++t)
-                                o[t] = pack_bf16x2(__uint_as_float(qw[t] << 16) * w[rb],
-                                                   __uint_as_float(qw[t] & 0xFFFF0000u) * w[rb]);
-                            qs[rb][ks] = __builtin_bit_cast(bf16x8, o);
+                        for (int r = 8 * hb; r < 8 * hb + 8; ++r) {
+                            const int cc = 8 * (r >> 2) + 4 * h + (r & 3) - 16 * hb;
+                            const float x = (bias[r] == -INFINITY) ? 0.f
+                                : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]) * a.scale;
+                            wbuf[cc * BLK + 32 * rb + l32] = x;
                         }
+                    wave_lds_sync();
+                    uint32_t pend = 0;                    // compensated blocks of this batch
 #pragma unroll
-                    for (int db = 0; db < 4; ++db) {
-                        bf16x8 ha[8];
-#pragma unroll
-                        for (int ks = 0; ks < 8; ++ks)
-                            ha[ks] = *reinterpret_cast<const bf16x8*>(Hj + (32 * db + l32) * D + 16 * ks + 8 * h);
-#pragma unroll
-                        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                            for (int rb = 0; rb < 2; ++rb)
-                                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ha[ks], qs[rb][ks], st.o[db][rb], 0, 0, 0);
+                    for (int c = 0; c < 16; ++c) {
+                        const int cc = 16 * hb + c;
+                        if (32 * u + cc < nb && !((keptw >> cc) & 1u)) pend |= 1u << c;
                     }
+                    if (pend) {
+                        // steps (block, d block) in order; each step's eight A
+                        // operands load two steps (32 MFMAs) ahead into one of two
+                        // operand sets
+                        int c = __builtin_ctz(pend);
+                        pend &= pend - 1;
+                        bf16x8 buf[2][8];
+                        load_step(32 * u + 16 * hb + c, 0, buf[0]);
+                        load_step(32 * u + 16 * hb + c, 1, buf[1]);
+                        for (;;) {
+                            const float w0 = wbuf[c * BLK + l32], w1 = wbuf[c * BLK + 32 + l32];
+                            const int nc = pend ? __builtin_ctz(pend) : -1;
+#pragma unroll
+                            for (int db = 0; db < 4; ++db) {
+                                f32x16 t[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+                                for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+                                    for (int rb = 0; rb < 2; ++rb)
+                                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[db & 1][ks], qb[rb][ks], t[rb], 0, 0, 0);
+                                if (db < 2) load_step(32 * u + 16 * hb + c, db + 2, buf[db & 1]);
+                                else if (nc >= 0) load_step(32 * u + 16 * hb + nc, db - 2, buf[db & 1]);
+#pragma unroll
+                                for (int r = 0; r < 16; ++r) {
+                                    st.o[db][0][r] = fmaf(t[0][r], w0, st.o[db][0][r]);
+                                    st.o[db][1][r] = fmaf(t[1][r], w1, st.o[db][1][r]);
+                                }
+                            }
+                            if (nc < 0) break;
+                            c = nc;
+                            pend &= pend - 1;
+                        }
+                    }
+                    wave_lds_sync();
                 }
-                wave_lds_sync();
             }
         }
         wait_vmcnt<0>();

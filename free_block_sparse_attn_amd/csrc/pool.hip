@@ -207,13 +207,17 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                     acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
                 }
             }
+            // MFMA A-operand order of the forward pass: element (o, i) of H_j^T
+            // at ((o/32 * 8 + i/16) * 64 + o%32 + 32 (i/8 % 2)) * 8 + i%8, so each
+            // (32-row d block, 16-wide i step) operand is 1 KiB contiguous
             uint16_t* mom = static_cast<uint16_t*>(a.kmom) + (bh * nb + j) * static_cast<size_t>(D) * D;
+            const int ks = icol >> 4, hi8 = (icol >> 3) & 1, e8 = icol & 7;
 #pragma unroll
             for (int ob = 0; ob < 4; ++ob) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const int o = 32 * ob + 8 * (r >> 2) + 4 * hl + (r & 3);
-                    mom[o * D + icol] = f32_to_bf16(acc[ob][r]);
+                    const int o32 = 8 * (r >> 2) + 4 * hl + (r & 3);
+                    mom[((ob * 8 + ks) * 64 + o32 + 32 * hi8) * 8 + e8] = f32_to_bf16(acc[ob][r]);
                 }
             }
         }

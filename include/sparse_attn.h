@@ -107,10 +107,12 @@ typedef struct {
  *                        plane 0 hi(k_bar), 1 lo(k_bar), 2 hi(v_bar),
  *                        3 lo(v_bar); rows nb .. nbc-1 are 0.  bf16 inputs
  *                        with d == 128 only.
- *   kmom                 bf16 [B,H,nb,d,d]  moment of block j stored
- *                        value-major: kmom[..., o, i] =
- *                        sum_n (k_n[i] - k_bar_j[i]) v_n[o]   (H_j transposed).
- *                        bf16 inputs only.
+ *   kmom                 bf16 [B,H,nb,d*d]  moment of block j,
+ *                        G[o][i] = sum_n (k_n[i] - k_bar_j[i]) v_n[o]
+ *                        (H_j transposed), stored in the forward pass's MFMA
+ *                        operand order: G[o][i] at element
+ *                        ((o/32 * 8 + i/16) * 64 + o%32 + 32 * ((i/8) % 2)) * 8
+ *                        + i%8 of the block.  bf16 inputs with d == 128 only.
  *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
  *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
  *                        omission-error statistic); -inf for 1-token blocks.
@@ -208,7 +210,7 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *            SA_BF16, may be NULL there)
  * cent       bf16 [B,H,4,nbc,d] centroid planes from sparse_attn_pool
  *            (SA_BF16 with comp >= 0; unused by SA_F32)
- * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d,d] (comp == 1)
+ * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d*d] (comp == 1)
  * q8, k8, v8, exp8                      from sparse_attn_pool (skim only)
  * idx, cnt, cap     exact lists (ascending, entries in [0, nb))
  * idx2, cnt2, cap2  skim lists, or NULL / 0 when there is no skim tier

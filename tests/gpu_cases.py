@@ -57,6 +57,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
     if "v8" in res:
         res["v8"] = v8_row_major(res["v8"], wl.N_pad)
+    if "kmom" in res:
+        res["kmom"] = kmom_value_major(res["kmom"])
     res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
     if idx2 is not None:
         res["idx2"], res["cnt2"] = idx2.cpu().numpy(), cnt2.cpu().numpy()
@@ -78,6 +80,16 @@ def v8_row_major(v8t, n_pad):
     p = np.arange(64)
     out[:, :, :, kappa(p), :] = np.swapaxes(v8t, -1, -2)
     return out.reshape(B, H, n_pad, d)
+
+
+def kmom_value_major(x):
+    """[B,H,nb,d*d] moments in MFMA operand order -> [B,H,nb,d,d] value-major G[o][i]:
+    element ((o/32*8 + i/16)*64 + o%32 + 32*((i/8)%2))*8 + i%8 holds G[o][i]."""
+    B, H, nb, dd = x.shape
+    d = int(round(dd ** 0.5))
+    y = x.reshape(B, H, nb, d // 32, d // 16, 2, 32, 8)        # [db][ks][h][o32][e]
+    y = y.transpose(0, 1, 2, 3, 6, 4, 5, 7)                    # [db][o32][ks][h][e]
+    return y.reshape(B, H, nb, d, d)
 
 
 def oracle_pool(wl, q, k, v):
