@@ -348,7 +348,9 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
 //   the denominators take the unquantised 2^{L - m}.
 // Q~ and K~ are row-major; V~ is stored block-transposed [d][64] in the key
 // order of P's accumulator layout, so both fp8 PV operands are contiguous
-// 32-byte loads and no LDS is needed.
+// 32-byte loads and no LDS is needed.  The next tile's list entry and block
+// exponents come through the scalar cache, and its K~ / V~ operands load
+// while this tile computes.
 __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t bh, int qa,
                                         const int32_t* listM, int cntM, float c2) {
     const int nb = a.N_pad / BLK;
@@ -357,7 +359,9 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
     const uint8_t* Q8 = a.q8 + head;
     const uint8_t* K8 = a.k8 + head;
     const uint8_t* V8 = a.v8 + head;
-    const int8_t* EX = a.exp8 + bh * nb * 3;
+    typedef __attribute__((address_space(4))) const int8_t const_i8;
+    const const_i8* EX = (const const_i8*)(a.exp8 + bh * nb * 3);
+    const const_i32* LM = (const const_i32*)listM;
     i32x8 qb8[2][2];
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
@@ -370,22 +374,38 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
         }
     }
     const int sq = static_cast<int>(EX[qa * 3 + 0]) + 127;
-    for (int e = 0; e < cntM; ++e) {
-        const int j = listM[e];
-        const int nj = min(BLK, a.N - BLK * j);
-        const int sk = static_cast<int>(EX[j * 3 + 1]) + 127;
-        const int sv = static_cast<int>(EX[j * 3 + 2]) + 127;
+    auto load_tile = [&](int j, i32x8 ka[2][2], i32x8 va[4]) __attribute__((always_inline)) {
         const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * D;
-        i32x8 ka[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
                 ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
         const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * D;
-        i32x8 va[4];
 #pragma unroll
         for (int db = 0; db < 4; ++db) va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
+    };
+    if (cntM <= 0) return;
+    i32x8 nka[2][2], nva[4];
+    int jn = LM[0];
+    load_tile(jn, nka, nva);
+    int skn = static_cast<int>(EX[jn * 3 + 1]) + 127, svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
+    for (int e = 0; e < cntM; ++e) {
+        const int j = jn, sk = skn, sv = svn;
+        i32x8 ka[2][2], va[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) ka[kb][ks] = nka[kb][ks];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va[db] = nva[db];
+        if (e + 1 < cntM) {
+            jn = LM[e + 1];
+            load_tile(jn, nka, nva);
+            skn = static_cast<int>(EX[jn * 3 + 1]) + 127;
+            svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
+        }
+        const int nj = min(BLK, a.N - BLK * j);
         f32x16 s[2][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -399,30 +419,33 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                 for (int rb = 0; rb < 2; ++rb)
                     s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
+        // raw logits; pad keys of the ragged tail block -inf (c2 > 0 commutes with max)
+        if (nj < BLK) {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) mask_half(s[kb], 32 * kb, nj);
+        }
         i32x8 pb[2];
         int sb[2];
         float mx[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
-            float m0 = -INFINITY;
+            float m0 = s[0][rb][0];
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-                    const float x = (key < nj) ? s[kb][rb][r] * c2 : -INFINITY;
-                    s[kb][rb][r] = x;
-                    m0 = fmaxf(m0, x);
-                }
-            mx[rb] = pair_max(m0);
+                for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, s[kb][rb][r]);
+            mx[rb] = pair_max(m0) * c2;
             rescale_lazy(st, rb, mx[rb]);
         }
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
+            // y = 2^{8 + L - c} is the pre-quantisation code value; the
+            // unquantised weight 2^{L - m} = y 2^{c - 8 - m}, so the denominator
+            // takes 2^{c - 8 - m} times the sum of the y.
             const float mref = st.m[rb];
             const float ct = (mx[rb] == -INFINITY) ? mref : ceilf(mx[rb]);
-            const float mult = ldexpf(1.0f, 8 + static_cast<int>(mref - ct));
-            float le = 0.f;
+            const float off = 8.0f - ct;
+            float ysum = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -430,14 +453,13 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     float y[4];
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
-                        const float x = __builtin_amdgcn_exp2f(s[kb][rb][4 * w + u] - mref);
-                        le += x;
-                        y[u] = x * mult;
+                        y[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][rb][4 * w + u], c2, off));
+                        ysum += y[u];
                     }
                     const uint32_t lo = pack_fp8x2<false>(y[0], y[1], 0u);
                     pb[rb][4 * kb + w] = static_cast<int>(pack_fp8x2<true>(y[2], y[3], lo));
                 }
-            st.l[rb] += le;
+            st.l[rb] = fmaf(ysum, ldexpf(1.0f, static_cast<int>(ct - mref) - 8), st.l[rb]);
             sb[rb] = min(max(static_cast<int>(ct - mref) - 8 + 127, 0), 254);
         }
 #pragma unroll
