@@ -12,6 +12,7 @@ query t of query block a,
         + sum_{j in M} sum_n p~_tn v~_n 2^{e_v(j)}
         + [c >= 0] sum_{j in U} n_j e^{s q.k_bar_j} v_bar_j
         + [c == 1] sum_{j in U} e^{s q.k_bar_j} s (q^T H_j)
+        + [c == 2] s (sum_{j in U} e^{s q.k_bar_j}) (q^T H_bar)
 
 with s the softmax scale, E the exactly computed key blocks, M the fp8 skim
 blocks (Triage's low-precision tier), U every other block, n_j the block's
@@ -20,7 +21,9 @@ valid key count, k_bar_j / v_bar_j its exact means and H_j = sum_n
 block's value sum (alpha_{t,j} = exp(q_t k_bar_j^T)), which equals SVG-EAR's
 centroid replacement ("SVG-EAR ...", section 2A) of all n_j keys and values
 by their means.  The first-order term is PISA's with the per-block matrix
-H_j in place of the global mean H_bar; its denominator share is zero because
+H_j in place of the global mean H_bar; c == 2 is PISA's own hybrid-order
+form, with H_bar = mean_j H_j over all blocks of the head shared by every
+skipped block.  Either first-order term has no denominator share because
 sum_n (k_n - k_bar_j) = 0 for the exact mean.  Every approximation sits
 inside the one normalisation D_t, as PISA's "Coherence de Normalisation"
 asks.
@@ -83,11 +86,12 @@ def skim_weights(L: np.ndarray) -> np.ndarray:
 
 
 def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
-               exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK):
+               exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK, hbar=None):
     """Compensated rule for the valid rows Qa [r, d] of query block a, one head.
 
     k, v: [N_pad, d]; kbar, vbar: exact fp64 means [nb, d]; kcount [nb];
     exact / skim: key block index lists; kmom [nb, d, d] for comp == 1;
+    hbar [d, d] (the head's mean first-order matrix) for comp == 2;
     fp8: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp, vexp [nb]) for skim.
     Returns (o [r, d], lse [r]).
     """
@@ -127,6 +131,9 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
         L = lg * LOG2E
         pq = skim_weights(L) * np.exp2(-m * LOG2E)[:, None]
         Nt += pq @ vt
+    if comp == 2 and U.size:
+        alpha = np.exp(scale * (Qa @ kbar[U].T) - m[:, None])        # [r, |U|]
+        Nt += scale * alpha.sum(axis=1)[:, None] * (Qa @ hbar)
     if comp == 1 and U.size:
         alpha = np.exp(scale * (Qa @ kbar[U].T) - m[:, None])        # [r, |U|]
         QH = np.matmul(Qa[None], kmom[U])                             # [|U|, r, d]: q^T H_j
@@ -151,6 +158,7 @@ def sparse_attention(q, k, v, N: int, scale: float, comp: int, pooled: dict,
             if skim_idx is not None:
                 fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
             kmom = pooled["kmom"][b, h] if comp == 1 else None
+            hbar = pooled["hbar"][b, h] if comp == 2 else None
             for a in range(nb):
                 r0, r1 = a * blk, min(N, (a + 1) * blk)
                 if r1 <= r0:
@@ -159,7 +167,7 @@ def sparse_attention(q, k, v, N: int, scale: float, comp: int, pooled: dict,
                 sk = () if skim_idx is None else skim_idx[b, h, a, :skim_cnt[b, h, a]]
                 o, l = rule_block(q[b, h, r0:r1], k[b, h], v[b, h], N, scale, comp,
                                   pooled["kbar64"][b, h], pooled["vbar64"][b, h], pooled["kcount"],
-                                  ex, sk, kmom, fp8, a, blk)
+                                  ex, sk, kmom, fp8, a, blk, hbar)
                 O[b, h, r0:r1] = o
                 lse[b, h, r0:r1] = l
     return O, lse

@@ -69,6 +69,15 @@ def block_moments(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.nd
     return np.einsum("bhjni,bhjno->bhjio", kc, vb * valid[None, None, :, :, None])
 
 
+def global_moment(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.ndarray:
+    """PISA's global first-order statistic H_bar, fp64 [B,H,d,d]: the mean of
+    the per-block first-order matrices H_j over all nb blocks of the head
+    (PISA, section 2, "Algorithme Central", global first-order correction;
+    precomputed before the attention pass per "Implementation Materielle").
+    """
+    return block_moments(k, v, N, blk).mean(axis=2)
+
+
 def block_spreads(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.ndarray:
     """lambda_j = ln(r_k * r_v) with r_x^2 = sum_n ||x_n - x_bar_j||^2, as fp32 [B,H,nb].
 
@@ -110,7 +119,7 @@ def e4m3_blocks(x: np.ndarray, N: int, blk: int = BLK):
     return codes.reshape(B, H, nb * blk, d), e
 
 
-def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False):
+def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hbar=False):
     """Everything the router and the fused forward read, in one dict."""
     qbar, qbar64, n = block_means(q, N, blk)
     kbar, kbar64, _ = block_means(k, N, blk)
@@ -119,6 +128,8 @@ def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False):
                qbar64=qbar64, kbar64=kbar64, vbar64=vbar64)
     if moments:
         out["kmom"] = block_moments(k, v, N, blk)
+    if hbar:
+        out["hbar"] = global_moment(k, v, N, blk)
     if spreads:
         out["klam"] = block_spreads(k, v, N, blk)
     if fp8:

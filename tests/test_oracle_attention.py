@@ -43,13 +43,13 @@ def test_dense_matches_torch_sdpa():
     assert np.all(O[:, :, 150:] == 0)
 
 
-@pytest.mark.parametrize("comp", [-1, 0, 1])
+@pytest.mark.parametrize("comp", [-1, 0, 1, 2])
 def test_all_blocks_exact_is_dense(comp):
     q, k, v = rand_qkv(1, N=170)
     nb = 3
     idx = np.tile(np.arange(nb, dtype=np.int32), (1, 2, nb, 1))
     cnt = np.full((1, 2, nb), nb, np.int32)
-    pooled = pooling.pool(q, k, v, 170, moments=True)
+    pooled = pooling.pool(q, k, v, 170, moments=True, hbar=True)
     O, lse = attention.sparse_attention(q, k, v, 170, 1.0, comp, pooled, idx, cnt)
     Od, lsed = attention.dense_attention(q, k, v, 170, 1.0)
     np.testing.assert_allclose(O, Od, atol=1e-13)
@@ -70,13 +70,13 @@ def test_block_size_one_is_dense_for_any_selection(comp):
     np.testing.assert_allclose(lse, lsed, atol=1e-12)
 
 
-@pytest.mark.parametrize("comp", [-1, 0, 1])
+@pytest.mark.parametrize("comp", [-1, 0, 1, 2])
 def test_constant_values_give_constant_output(comp):
     q, k, v = rand_qkv(3, N=200)
     v[:, :, :200] = np.linspace(-1, 1, 8)[None, None, None, :]
     rng = np.random.default_rng(3)
     idx, cnt = random_lists(rng, 1, 2, 4, 2)
-    pooled = pooling.pool(q, k, v, 200, moments=True)
+    pooled = pooling.pool(q, k, v, 200, moments=True, hbar=True)
     O, _ = attention.sparse_attention(q, k, v, 200, 1.0, comp, pooled, idx, cnt)
     np.testing.assert_allclose(O[:, :, :200], v[:, :, :200], atol=1e-13)
 
@@ -167,9 +167,17 @@ def brute_rule(q, k, v, N, blk, s, comp, exact):
     nb = (N + blk - 1) // blk
     d = q.shape[1]
     out = np.zeros((N, d))
+    hb = [[0.0] * d for _ in range(d)]          # mean over all blocks of H_j
+    for j in range(nb):
+        toks = [n for n in range(j * blk, min(N, j * blk + blk))]
+        kb = [sum(k[n, i] for n in toks) / len(toks) for i in range(d)]
+        for i in range(d):
+            for o in range(d):
+                hb[i][o] += sum((k[n, i] - kb[i]) * v[n, o] for n in toks) / nb
     for t in range(N):
         a = t // blk
         D, num = 0.0, [0.0] * d
+        asum = 0.0
         for j in range(nb):
             toks = [n for n in range(j * blk, min(N, j * blk + blk))]
             if j in exact[a]:
@@ -182,18 +190,22 @@ def brute_rule(q, k, v, N, blk, s, comp, exact):
                 kb = [sum(k[n, i] for n in toks) / len(toks) for i in range(d)]
                 vb = [sum(v[n, o] for n in toks) / len(toks) for o in range(d)]
                 al = math.exp(s * sum(q[t, i] * kb[i] for i in range(d)))
+                asum += al
                 D += len(toks) * al
                 for o in range(d):
                     num[o] += len(toks) * al * vb[o]
                     if comp == 1:
                         num[o] += al * s * sum(q[t, i] * (k[n, i] - kb[i]) * v[n, o]
                                                for n in toks for i in range(d))
+        if comp == 2:
+            for o in range(d):
+                num[o] += s * asum * sum(q[t, i] * hb[i][o] for i in range(d))
         for o in range(d):
             out[t, o] = num[o] / D
     return out
 
 
-@pytest.mark.parametrize("comp,blk", [(-1, 3), (0, 4), (1, 2), (1, 4)])
+@pytest.mark.parametrize("comp,blk", [(-1, 3), (0, 4), (1, 2), (1, 4), (2, 3), (2, 4)])
 def test_brute_force_tiny(comp, blk):
     rng = np.random.default_rng(10 + blk)
     N, d = 14, 3
@@ -203,7 +215,7 @@ def test_brute_force_tiny(comp, blk):
     for x in (q, k, v):
         x[0, 0, :N] = rng.standard_normal((N, d))
     idx, cnt = random_lists(rng, 1, 1, nb, 2)
-    pooled = pooling.pool(q, k, v, N, blk=blk, moments=True)
+    pooled = pooling.pool(q, k, v, N, blk=blk, moments=True, hbar=True)
     O, _ = attention.sparse_attention(q, k, v, N, 0.8, comp, pooled, idx, cnt, blk=blk)
     ref = brute_rule(q[0, 0], k[0, 0], v[0, 0], N, blk, 0.8, comp, [list(r) for r in idx[0, 0]])
     np.testing.assert_allclose(O[0, 0, :N], ref, atol=1e-12)
@@ -262,3 +274,39 @@ def test_quality_compensation_beats_dropping():
         O, _ = attention.sparse_attention(q, k, v, wl.N, 1.0, comp, pooled, idx, cnt)
         rel[comp] = np.linalg.norm(O - Od) / np.linalg.norm(Od)
     assert rel[0] < rel[-1]
+
+
+def test_global_moment_closed_form():
+    # H_bar = (1/nb) (sum_n k_n v_n^T - sum_j n_j kbar_j vbar_j^T) over valid tokens
+    q, k, v = rand_qkv(20, N=170, d=5)
+    N, nb = 170, 3
+    hb = pooling.global_moment(k, v, N)
+    for h in range(2):
+        K, V = k[0, h, :N], v[0, h, :N]
+        ref = K.T @ V
+        for j in range(nb):
+            toks = slice(64 * j, min(N, 64 * j + 64))
+            nj = min(N, 64 * j + 64) - 64 * j
+            ref -= nj * np.outer(K[toks].mean(axis=0), V[toks].mean(axis=0))
+        np.testing.assert_allclose(hb[0, h], ref / nb, atol=1e-12)
+
+
+def test_global_first_order_equals_block_when_all_moments_agree():
+    # blocks that are shifted copies of one block (same values) share one H_j,
+    # so the global mean equals every H_j and the two first-order forms agree
+    rng = np.random.default_rng(21)
+    d, nb = 6, 4
+    k0, v0 = rng.standard_normal((64, d)) * 0.4, rng.standard_normal((64, d))
+    k = np.concatenate([k0 + 0.3 * rng.standard_normal(d) for _ in range(nb)])[None, None]
+    v = np.concatenate([v0] * nb)[None, None]
+    q = rng.standard_normal((1, 1, 64 * nb, d)) * 0.5
+    N = 64 * nb
+    pooled = pooling.pool(q, k, v, N, moments=True, hbar=True)
+    np.testing.assert_allclose(pooled["kmom"][0, 0, 2], pooled["hbar"][0, 0], atol=1e-12)
+    idx, cnt = random_lists(rng, 1, 1, nb, 1)
+    O1, l1 = attention.sparse_attention(q, k, v, N, 0.9, 1, pooled, idx, cnt)
+    O2, l2 = attention.sparse_attention(q, k, v, N, 0.9, 2, pooled, idx, cnt)
+    np.testing.assert_allclose(O2, O1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+    O0, _ = attention.sparse_attention(q, k, v, N, 0.9, 0, pooled, idx, cnt)
+    assert np.abs(O2 - O0).max() > 1e-3                       # the term is not trivially zero
