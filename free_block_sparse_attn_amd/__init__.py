@@ -16,11 +16,13 @@ import torch
 
 from . import _lib
 from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER0,
-                   SA_COMP_ORDER1_BLOCK, SA_ROUTE_TOPK, SA_ROUTE_LVSA, SA_ROUTE_TRIAGE)
+                   SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL, SA_ROUTE_TOPK, SA_ROUTE_LVSA,
+                   SA_ROUTE_TRIAGE)
 
 __all__ = [
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
+    "SA_COMP_ORDER1_GLOBAL",
     "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE",
 ]
 
@@ -58,9 +60,10 @@ def abi_version() -> int:
     return _lib.load().sparse_attn_abi_version()
 
 
-def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None, out=None) -> dict:
+def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None,
+                     global_moment=False, out=None) -> dict:
     """Block means (fp32), counts and the optional centroid planes / moments /
-    spreads / e4m3 copies.  The bf16 centroid planes (what the bf16 forward
+    mean moment H_bar (with its 64-partial scratch) / spreads / e4m3 copies.  The bf16 centroid planes (what the bf16 forward
     reads) are produced by default for bf16 inputs with d == 128.
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
@@ -75,8 +78,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
         _lib.check(lib.sparse_attn_pool(
             ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
             _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")),
-            _ptr(g("exp8")), _stream(q)))
+            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("klam")),
+            _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
         return out
     out = {
         "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
@@ -91,6 +94,9 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
         out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.bfloat16, device=dev)
     if moments:
         out["kmom"] = torch.empty(B, H, nb, d * d, dtype=torch.bfloat16, device=dev)   # MFMA operand order
+    if global_moment:
+        out["hbar"] = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)          # value-major
+        out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
     if spreads:
         out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
     if fp8:
@@ -102,8 +108,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
     _lib.check(lib.sparse_attn_pool(
         ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")),
-        _ptr(g("exp8")), _stream(q)))
+        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("klam")),
+        _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
     return out
 
 
@@ -175,7 +181,7 @@ def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx,
     cap2 = idx2.shape[-1] if idx2 is not None else 0
     _lib.check(lib.sparse_attn_fwd(
         ctypes.byref(_shape(q, N)), _dtype(q), comp, scale, _ptr(q), _ptr(k), _ptr(v),
-        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("kcount")), _ptr(g("kmom")),
+        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("kcount")), _ptr(g("kmom")), _ptr(g("hbar")),
         _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
         _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
         _ptr(out), _ptr(lse), _stream(q)))

@@ -80,22 +80,24 @@ int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* kmom,
-                           float* klam,
+                           float* hbar, float* hbar_ws, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (empty) return ok();
     NEED(q); NEED(k); NEED(v); NEED(qbar); NEED(kbar); NEED(vbar); NEED(kcount);
-    MAYBE(cent); MAYBE(kmom); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
+    MAYBE(cent); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
     const int fp8 = (q8 != nullptr) + (k8 != nullptr) + (v8 != nullptr) + (exp8 != nullptr);
     if (fp8 != 0 && fp8 != 4) return fail(SA_ERR_INVALID_ARG, "q8, k8, v8 and exp8 must be given together");
     const bool bf16_128 = dtype == SA_BF16 && shape->d == 128;
     if (cent && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "cent needs bf16 inputs with d == 128");
     if (kmom && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "kmom needs bf16 inputs with d == 128");
+    if ((hbar != nullptr) != (hbar_ws != nullptr)) return fail(SA_ERR_INVALID_ARG, "hbar and hbar_ws go together");
+    if (hbar && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "hbar needs bf16 inputs with d == 128");
     if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
     sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
-                   cent, kmom, klam, q8, k8, v8, exp8};
+                   cent, kmom, hbar, hbar_ws, klam, q8, k8, v8, exp8};
     return hip_result(sa::launch_pool(a, dtype == SA_BF16, stream), "pool");
 }
 
@@ -168,14 +170,15 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
 
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale, const void* q,
                           const void* k, const void* v, const float* kbar, const float* vbar, const void* cent,
-                          const int32_t* kcount, const void* kmom, const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
+                          const int32_t* kcount, const void* kmom, const float* hbar, const uint8_t* q8,
+                          const uint8_t* k8, const uint8_t* v8,
                           const int8_t* exp8, const int32_t* idx, const int32_t* cnt, int32_t cap,
                           const int32_t* idx2, const int32_t* cnt2, int32_t cap2, void* out, float* lse,
                           hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
-    if (comp < SA_COMP_DROP || comp > SA_COMP_ORDER1_BLOCK)
+    if (comp < SA_COMP_DROP || comp > SA_COMP_ORDER1_GLOBAL)
         return fail(SA_ERR_INVALID_ARG, "unknown compensation order %d", static_cast<int>(comp));
     if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(SA_ERR_INVALID_ARG, "scale must be finite and > 0");
     const int nb = shape->N_pad / 64;
@@ -188,10 +191,11 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
     if (skim) { NEED(cnt2); }
     if (comp >= SA_COMP_ORDER0) { NEED(kcount); }
     if (comp == SA_COMP_ORDER1_BLOCK) { NEED(kmom); }
+    if (comp == SA_COMP_ORDER1_GLOBAL) { NEED(hbar); }
     if (dtype == SA_F32) {
         if (comp >= SA_COMP_ORDER0) { NEED(kbar); NEED(vbar); }
         if (shape->d != 64) return fail(SA_ERR_UNSUPPORTED, "fp32 forward supports d == 64 only");
-        if (comp == SA_COMP_ORDER1_BLOCK) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no first-order term");
+        if (comp >= SA_COMP_ORDER1_BLOCK) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no first-order term");
         if (skim) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no fp8 skim tier");
     } else {
         if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "bf16 forward supports d == 128 only");
@@ -201,7 +205,8 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
     if (comp == SA_COMP_DROP && cap == 0 && !skim)
         return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");
     sa::FwdArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, static_cast<int>(comp), scale, q, k, v,
-                  kbar, vbar, cent, kcount, kmom, q8, k8, v8, exp8, idx, cnt, cap, idx2, cnt2, cap2, out, lse};
+                  kbar, vbar, cent, kcount, kmom, hbar, q8, k8, v8, exp8, idx, cnt, cap, idx2, cnt2, cap2,
+                  out, lse};
     if (dtype == SA_F32) return hip_result(sa::launch_fwd_f32(a, stream), "fwd_f32");
     return hip_result(sa::launch_fwd_bf16(a, stream), "fwd_bf16");
 }

@@ -4,6 +4,7 @@
 //   exact key blocks E          e^{s q.k_n} (v_n)                    bf16 MFMA
 //   every other key block j     n_j e^{s q.k_bar_j} (v_bar_j)         order 0
 //                               + e^{s q.k_bar_j} s q^T H_j (N only)  order 1
+//   all skipped blocks together  s (sum_j e^{s q.k_bar_j}) q^T H_bar     global order 1
 // PISA ("PISA: Piecewise Sparse Attention Is Wiser for Efficient Diffusion
 // Transformers", section 2, "Algorithme Central" and "Implementation
 // Materielle": exact phase on selected blocks, then a scan of the block
@@ -139,11 +140,13 @@ struct State {
     f32x16 o[4][2];        // O^T[d-block][row-block]
     float m[2];            // reference (log2 units, an integer) per row block
     float l[2];            // this lane's partial row sums of the bf16-rounded P
+    float a1[2];           // global first order: partial sums of e^{s q.k_bar_j} 2^{-m} over skipped j
 };
 
 __device__ __forceinline__ void rescale_row(State& st, int rb, float mnew) {
     const float alpha = __builtin_amdgcn_exp2f(st.m[rb] - mnew);
     st.l[rb] *= alpha;
+    st.a1[rb] *= alpha;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -563,6 +566,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int rb = 0; rb < 2; ++rb) st.o[db][rb] = f32x16{};
     st.m[0] = st.m[1] = M_INIT;
     st.l[0] = st.l[1] = 0.f;
+    st.a1[0] = st.a1[1] = 0.f;
 
     // ---- phase 1: exact key blocks, pipelined over half tiles ----
     // Each region refills the buffer the previous region read:
@@ -706,6 +710,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb) exp_rb(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
             settle_half(st, s, 1.0f, pb, ls);
+            if (COMP == 2) {
+                // PISA's global first-order weight: sum over skipped blocks of
+                // alpha_{t,j} = e^{s q.k_bar_j}, relative to the reference m
+#pragma unroll
+                for (int rb = 0; rb < 2; ++rb) {
+                    float acc = 0.f;
+#pragma unroll
+                    for (int r = 0; r < 16; ++r)
+                        if (bias[r] != -INFINITY) acc += __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]);
+                    st.a1[rb] += acc;
+                }
+            }
             // V planes of unit u: only the next unit's K planes may still be in flight
             if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
             wave_lds_sync();
@@ -792,6 +808,42 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             }
         }
         wait_vmcnt<0>();
+        if (COMP == 2) {
+            // O^T[., row] += s A_row (H_bar^T Q^T)[., row], A_row = sum_j alpha_{t,j}:
+            // one d x d product per query block (H_bar split into bf16 high +
+            // low parts, fp32 accumulation)
+            const float* HB = a.hbar + bh * static_cast<size_t>(D) * D;    // value-major G[o][i]
+            const float w0 = a.scale * pair_sum(st.a1[0]), w1 = a.scale * pair_sum(st.a1[1]);
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                f32x16 t[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+                for (int ks = 0; ks < 8; ++ks) {
+                    const float* g = HB + (32 * db + l32) * D + 16 * ks + 8 * h;
+                    const float4 x0 = *reinterpret_cast<const float4*>(g);
+                    const float4 x1 = *reinterpret_cast<const float4*>(g + 4);
+                    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                    u32x4 whi, wlo;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        whi[e] = pack_bf16x2(x[2 * e], x[2 * e + 1]);
+                        wlo[e] = pack_bf16x2(x[2 * e] - bf16_to_f32(static_cast<uint16_t>(whi[e] & 0xFFFFu)),
+                                             x[2 * e + 1] - bf16_to_f32(static_cast<uint16_t>(whi[e] >> 16)));
+                    }
+                    const bf16x8 ghi = __builtin_bit_cast(bf16x8, whi), glo = __builtin_bit_cast(bf16x8, wlo);
+#pragma unroll
+                    for (int rb = 0; rb < 2; ++rb) {
+                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ghi, qb[rb][ks], t[rb], 0, 0, 0);
+                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(glo, qb[rb][ks], t[rb], 0, 0, 0);
+                    }
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    st.o[db][0][r] = fmaf(t[0][r], w0, st.o[db][0][r]);
+                    st.o[db][1][r] = fmaf(t[1][r], w1, st.o[db][1][r]);
+                }
+            }
+        }
     }
 
     // ---- normalise and write O (bf16) and lse ----
@@ -830,7 +882,8 @@ hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
     switch (a.comp) {
         case -1: return launch_t<-1, SKIM>(a, s);
         case 0: return launch_t<0, SKIM>(a, s);
-        default: return launch_t<1, SKIM>(a, s);
+        case 1: return launch_t<1, SKIM>(a, s);
+        default: return launch_t<2, SKIM>(a, s);
     }
 }
 

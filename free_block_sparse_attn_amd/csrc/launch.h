@@ -18,7 +18,9 @@ struct PoolArgs {
     float* vbar;
     int32_t* kcount;
     void* cent;       // bf16 [B,H,4,nbc,d] centroid planes, or null
-    void* kmom;       // bf16 [B,H,nb,d,d] value-major, or null
+    void* kmom;       // bf16 [B,H,nb,d*d] in MFMA operand order, or null
+    float* hbar;      // fp32 [B,H,d,d] value-major mean moment, or null
+    float* hbar_ws;   // fp32 [B,H,64,d,d] partial sums (with hbar)
     float* klam;      // [B,H,nb] or null
     uint8_t* q8;      // e4m3 copies or null (all or none)
     uint8_t* k8;
@@ -61,6 +63,7 @@ struct FwdArgs {
     const void* cent;         // bf16 centroid planes (bf16 path)
     const int32_t* kcount;
     const void* kmom;
+    const float* hbar;        // fp32 [B,H,d,d] value-major (comp 2)
     const uint8_t* q8;
     const uint8_t* k8;
     const uint8_t* v8;

@@ -369,6 +369,101 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
     if (tensor == 0 && bh == 0 && (lane % CPR) == 0) a.kcount[j] = n;
 }
 
+// PISA's global first-order statistic H_bar = (1/nb) sum_j H_j (section 2,
+// "Algorithme Central").  Pass 1: workgroup (c, bh) accumulates the centred
+// moments of blocks j = c, c + 64, ... in fp32 MFMA (the same staging and
+// hi + lo split of the centred keys as the per-block moments above) and
+// writes its partial G[o][i] = sum_j sum_n v_n[o] (k_n[i] - kbar_j[i]).
+// Pass 2 adds the 64 partials of a head in a fixed order (fp64) and divides
+// by nb, so H_bar is bit-reproducible.
+constexpr int HBAR_PARTS = 64;
+
+__global__ __launch_bounds__(THREADS) void hbar_partial_kernel(PoolArgs a) {
+    constexpr int D = 128;
+    using E = Elem<uint16_t>;
+    constexpr int CPR = D / 8;
+    constexpr int PT = BLK * CPR / THREADS;
+    __shared__ __attribute__((aligned(16))) uint16_t xt[2 * D * TPITCH];   // K^T, V^T of one block
+    __shared__ float kb_s[D];
+    const int c = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int nb = a.N_pad / BLK;
+    const int icol = 32 * w + l32;
+    f32x16 acc[4];
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x16{};
+    const uint16_t* src[2] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v)};
+    for (int j = c; j < nb; j += HBAR_PARTS) {
+        const int n = min(BLK, a.N - BLK * j);
+        const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
+        u32x4 reg[2][PT];
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < PT; ++q) {
+                const int chunk = tid + THREADS * q;
+                const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
+                u32x4 z = {0u, 0u, 0u, 0u};
+                if (row < n) z = *reinterpret_cast<const u32x4*>(src[t] + tok0 + static_cast<size_t>(row) * D + col0);
+                reg[t][q] = z;
+            }
+        const float kbj = tid < D ? a.kbar[(bh * nb + j) * D + tid] : 0.0f;
+        __syncthreads();                          // every wave is done with the previous block
+        if (tid < D) kb_s[tid] = kbj;
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+            for (int q = 0; q < PT; ++q) {
+                const int chunk = tid + THREADS * q;
+                const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) xt[(t * D + col0 + e) * TPITCH + row] = E::raw(reg[t][q], e);
+            }
+        __syncthreads();
+        const float kb = kb_s[icol];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int t0 = 16 * ks + 8 * hl;
+            bf16x8 bhi, blo;
+            const uint16_t* kc = xt + icol * TPITCH + t0;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float x = (t0 + e < n) ? E::val(kc[e]) - kb : 0.0f;
+                const __bf16 hi = static_cast<__bf16>(x);
+                bhi[e] = hi;
+                blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+            }
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob) {
+                const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (D + 32 * ob + l32) * TPITCH + t0);
+                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[ob], 0, 0, 0);
+                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
+            }
+        }
+    }
+    float* part = a.hbar_ws + (bh * HBAR_PARTS + c) * static_cast<size_t>(D) * D;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int o = 32 * ob + 8 * (r >> 2) + 4 * hl + (r & 3);
+            part[o * D + icol] = acc[ob][r];
+        }
+}
+
+__global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
+    constexpr int D = 128;
+    const size_t bh = blockIdx.x;
+    const int nb = a.N_pad / BLK;
+    const float* part = a.hbar_ws + bh * HBAR_PARTS * static_cast<size_t>(D) * D;
+    for (int e = threadIdx.x; e < D * D; e += THREADS) {
+        double sum = 0.0;
+        for (int c = 0; c < HBAR_PARTS; ++c) sum += static_cast<double>(part[static_cast<size_t>(c) * D * D + e]);
+        a.hbar[bh * D * D + e] = static_cast<float>(sum / static_cast<double>(nb));
+    }
+}
+
 template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
     if (!a.kmom && !a.klam && !a.q8) {
@@ -389,8 +484,15 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
-    if (bf16) return a.d == 128 ? launch_pool_t<uint16_t, 128>(a, s) : launch_pool_t<uint16_t, 64>(a, s);
-    return a.d == 128 ? launch_pool_t<float, 128>(a, s) : launch_pool_t<float, 64>(a, s);
+    hipError_t e;
+    if (bf16) e = a.d == 128 ? launch_pool_t<uint16_t, 128>(a, s) : launch_pool_t<uint16_t, 64>(a, s);
+    else e = a.d == 128 ? launch_pool_t<float, 128>(a, s) : launch_pool_t<float, 64>(a, s);
+    if (e != hipSuccess || !a.hbar) return e;
+    // after the means (the centring uses kbar)
+    hipLaunchKernelGGL(hbar_partial_kernel, dim3(HBAR_PARTS, a.B * a.H), dim3(THREADS), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(hbar_reduce_kernel, dim3(a.B * a.H), dim3(THREADS), 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace sa

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 2
+#define SPARSE_ATTN_ABI_VERSION 3
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -71,7 +71,8 @@ typedef enum {
 typedef enum {
     SA_COMP_DROP = -1,        /* unselected blocks contribute nothing */
     SA_COMP_ORDER0 = 0,       /* centroid term n_j exp(q.k_bar_j) v_bar_j */
-    SA_COMP_ORDER1_BLOCK = 1  /* centroid term + per-block Taylor term with H_j */
+    SA_COMP_ORDER1_BLOCK = 1, /* centroid term + per-block Taylor term with H_j */
+    SA_COMP_ORDER1_GLOBAL = 2 /* centroid term + PISA's global Taylor term with H_bar */
 } sa_comp;
 
 typedef enum {
@@ -113,6 +114,15 @@ typedef struct {
  *                        operand order: G[o][i] at element
  *                        ((o/32 * 8 + i/16) * 64 + o%32 + 32 * ((i/8) % 2)) * 8
  *                        + i%8 of the block.  bf16 inputs with d == 128 only.
+ *   hbar                 fp32 [B,H,d,d]  PISA's global first-order statistic
+ *                        H_bar = (1/nb) sum_j H_j over all blocks of the head
+ *                        (section 2, "Algorithme Central": the mean of the
+ *                        per-block first-order matrices), stored value-major
+ *                        like kmom's G: hbar[..., o, i] = H_bar[i][o].  Needs
+ *                        hbar_ws, fp32 [B,H,64,d,d] caller-owned scratch
+ *                        (64 partial sums per head, summed in a fixed order,
+ *                        so the result is bit-reproducible).  bf16 inputs with
+ *                        d == 128 only.
  *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
  *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
  *                        omission-error statistic); -inf for 1-token blocks.
@@ -131,7 +141,7 @@ typedef struct {
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount,
-                           void* cent, void* kmom, float* klam,
+                           void* cent, void* kmom, float* hbar, float* hbar_ws, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
                            hipStream_t stream);
 
@@ -203,6 +213,9 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *           2^ceil(max L); D takes the unquantised weights
  *   order0  sum_{j in U} n_j e^{scale q.k_bar_j} (v_bar_j)         comp >= 0
  *   order1  sum_{j in U} e^{scale q.k_bar_j} scale q^T H_j  (N only)  comp == 1
+ *   global  scale (sum_{j in U} e^{scale q.k_bar_j}) q^T H_bar (N only) comp == 2
+ *           (PISA section 2, "Algorithme Central": the hybrid-order form,
+ *           one d x d statistic for every skipped block)
  *
  * scale      softmax scale, finite and > 0
  * q, k, v    dtype [B,H,N_pad,d]
@@ -211,6 +224,7 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  * cent       bf16 [B,H,4,nbc,d] centroid planes from sparse_attn_pool
  *            (SA_BF16 with comp >= 0; unused by SA_F32)
  * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d*d] (comp == 1)
+ * hbar       fp32 [B,H,d,d] from sparse_attn_pool (comp == 2, SA_BF16)
  * q8, k8, v8, exp8                      from sparse_attn_pool (skim only)
  * idx, cnt, cap     exact lists (ascending, entries in [0, nb))
  * idx2, cnt2, cap2  skim lists, or NULL / 0 when there is no skim tier
@@ -221,12 +235,12 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  * A row's count is clamped to its cap.  Every row must hold at least one
  * exact or skim block when comp == SA_COMP_DROP.
  * Supported: SA_F32 with d == 64 (comp <= 0, no skim); SA_BF16 with
- * d == 128.
+ * d == 128 (every comp).
  */
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale,
                           const void* q, const void* k, const void* v,
                           const float* kbar, const float* vbar, const void* cent,
-                          const int32_t* kcount, const void* kmom,
+                          const int32_t* kcount, const void* kmom, const float* hbar,
                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                           const int8_t* exp8,
                           const int32_t* idx, const int32_t* cnt, int32_t cap,

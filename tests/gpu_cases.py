@@ -35,7 +35,7 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     import free_block_sparse_attn_amd as fbsa
     q, k, v = dev_qkv
     N = wl.N
-    pooled = fbsa.sparse_attn_pool(q, k, v, N, moments=wl.comp == 1,
+    pooled = fbsa.sparse_attn_pool(q, k, v, N, moments=wl.comp == 1, global_moment=wl.comp == 2,
                                    spreads=wl.rule == "triage", fp8=wl.rule == "triage")
     idx2 = cnt2 = None
     if wl.rule == "topk":
@@ -94,7 +94,7 @@ def kmom_value_major(x):
 
 def oracle_pool(wl, q, k, v):
     return pooling.pool(q, k, v, wl.N, moments=wl.comp == 1, spreads=wl.rule == "triage",
-                        fp8=wl.rule == "triage")
+                        fp8=wl.rule == "triage", hbar=wl.comp == 2)
 
 
 def lists_of(idx, cnt, b, h, a):
@@ -112,7 +112,8 @@ def oracle_rows(wl, q, k, v, pooled, res, rows, scale=1.0):
         if len(sk):
             fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
         kmom = pooled["kmom"][b, h] if wl.comp == 1 else None
+        hbar = pooled["hbar"][b, h] if wl.comp == 2 else None
         out[(b, h, a)] = attention.rule_block(
             q[b, h, r0:r1], k[b, h], v[b, h], wl.N, scale, wl.comp, pooled["kbar64"][b, h],
-            pooled["vbar64"][b, h], pooled["kcount"], ex, sk, kmom, fp8, a)
+            pooled["vbar64"][b, h], pooled["kcount"], ex, sk, kmom, fp8, a, hbar=hbar)
     return out

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 2
+    assert lib.sparse_attn_abi_version() == 3
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -46,12 +46,12 @@ MIS = ctypes.c_void_p(4097)
 
 
 def pool(lib, sh, dtype=1, **kw):
-    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, klam=None,
-             q8=None, k8=None, v8=None, exp8=None)
+    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, hbar=None, hbar_ws=None,
+             klam=None, q8=None, k8=None, v8=None, exp8=None)
     a.update(kw)
     return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
-                                a["kcount"], a["cent"], a["kmom"], a["klam"], a["q8"], a["k8"], a["v8"],
-                                a["exp8"], None)
+                                a["kcount"], a["cent"], a["kmom"], a["hbar"], a["hbar_ws"], a["klam"], a["q8"],
+                                a["k8"], a["v8"], a["exp8"], None)
 
 
 def test_pool_rejects_bad_arguments(lib):
@@ -69,6 +69,9 @@ def test_pool_rejects_bad_arguments(lib):
     assert pool(lib, shape(), dtype=0, cent=P) == 2          # centroid planes need bf16, d=128
     assert pool(lib, shape(d=64), cent=P) == 2
     assert pool(lib, shape(), cent=MIS) == 1
+    assert pool(lib, shape(), hbar=P) == 1                   # the mean moment needs its scratch
+    assert pool(lib, shape(), hbar_ws=P) == 1
+    assert pool(lib, shape(), dtype=0, hbar=P, hbar_ws=P) == 2
     assert pool(lib, shape(B=0)) == 0                        # empty problem: nothing launched
     assert pool(lib, shape(N=0, N_pad=0)) == 0
 
@@ -99,17 +102,20 @@ def test_route_rejects_bad_arguments(lib):
 
 
 def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
-    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, kcount=P, kmom=None, q8=None, k8=None, v8=None,
+    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, kcount=P, kmom=None, hbar=None, q8=None, k8=None, v8=None,
              exp8=None, idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
     a.update(kw)
     return lib.sparse_attn_fwd(sh, dtype, comp, scale, a["q"], a["k"], a["v"], a["kbar"], a["vbar"],
-                               a["cent"], a["kcount"], a["kmom"], a["q8"], a["k8"], a["v8"], a["exp8"], a["idx"],
+                               a["cent"], a["kcount"], a["kmom"], a["hbar"], a["q8"], a["k8"], a["v8"], a["exp8"],
+                               a["idx"],
                                a["cnt"], a["cap"], a["idx2"], a["cnt2"], a["cap2"], a["out"], a["lse"], None)
 
 
 def test_fwd_rejects_bad_arguments(lib):
-    assert fwd(lib, shape(), comp=5) == 1
     assert fwd(lib, shape(), comp=1) == 1                     # order 1 without kmom
+    assert fwd(lib, shape(), comp=2) == 1                     # global order 1 without hbar
+    assert fwd(lib, shape(), comp=3) == 1
+    assert fwd(lib, shape(d=64), dtype=0, comp=2, hbar=P) == 2   # fp32 path has no first-order term
     assert fwd(lib, shape(), scale=float("inf")) == 1
     assert fwd(lib, shape(), out=None) == 1
     assert fwd(lib, shape(), cent=None) == 1                  # bf16 order 0 needs the centroid planes

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 2
+    assert fbsa.abi_version() == 3
 
 
 def medium(wid):
@@ -45,6 +45,11 @@ def check_pool(wl, pooled_o, res):
             assert np.array_equal(res["cent"][:, :, p, :nb], hi), n
             assert np.array_equal(res["cent"][:, :, p + 1, :nb], lo), n
         assert not np.any(res["cent"][:, :, :, nb:]), "centroid pad rows"
+    if "hbar" in res and "hbar" in pooled_o:
+        # value-major mean moment; fp32 MFMA sums of bf16 products against fp64
+        ref = np.swapaxes(pooled_o["hbar"], -1, -2)
+        err = np.abs(res["hbar"].astype(np.float64) - ref)
+        assert err.max() <= 1e-4 * np.abs(ref).max(), err.max()
     if "kmom" in res:
         ref = np.swapaxes(pooled_o["kmom"], -1, -2)               # value-major layout
         err = np.abs(res["kmom"].astype(np.float64) - ref)
@@ -202,3 +207,41 @@ def test_topk_all_blocks_matches_dense():
     Od, lsed = attention.dense_attention(q, k, v, wl.N, 1.0)
     assert np.abs(out.float().cpu().numpy() - Od).max() <= gc.BF16_TOL
     assert np.abs(lse.cpu().numpy()[:, :, :wl.N] - lsed[:, :, :wl.N]).max() <= gc.LSE_TOL["bf16"]
+
+
+@pytest.mark.parametrize("size", ["small", "medium"])
+def test_parity_global_first_order(size):
+    """PISA's global first-order term (comp 2) on the HunyuanVideo-like rule."""
+    from workloads.configs import GLOBAL_ORDER1, GLOBAL_ORDER1_SMALL
+    from dataclasses import replace
+    wl = GLOBAL_ORDER1_SMALL if size == "small" else replace(medium(3), comp=2)
+    print(f"\n[case] {wl.name} size={size} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+def test_parity_global_first_order_full_size_sampled():
+    from workloads.configs import GLOBAL_ORDER1
+    wl = GLOBAL_ORDER1
+    print(f"\n[case] full {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    rng = np.random.default_rng(7)
+    heads = sorted(rng.choice(wl.H, 2, replace=False).tolist())
+    res = gc.run_gpu(wl, dev, coords)
+    qs, ks, vs = (x[:, heads] for x in (q, k, v))
+    pooled_o = pooling.pool(qs, ks, vs, wl.N, hbar=True)
+    rsub = {n: (x[:, heads] if n not in ("kcount",) else x) for n, x in res.items()}
+    check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount", "hbar")})
+    check_route(wl, pooled_o, rsub, coords)
+    rows = [(0, hi, int(a)) for hi in range(len(heads)) for a in rng.choice(wl.nb, 3, replace=False)]
+    rows.append((0, 0, wl.nb - 1))
+    ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
+    worst = check_out(wl, rsub, ref, rows)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)

@@ -26,7 +26,8 @@ class Workload:
     X: int
     dtype: str          # "f32" or "bf16"
     rule: str           # "topk", "lvsa" or "triage"
-    comp: int           # compensation order of skipped blocks: -1 drop, 0 centroid, 1 block Taylor
+    comp: int           # compensation order of skipped blocks: -1 drop, 0 centroid, 1 block Taylor,
+                        # 2 global Taylor (one mean moment per head)
     keep_pct: int = 0           # top-k: percent of key blocks kept per query block
     window: int = 0             # LVSA: +- latent frames around the query block's frames
     anchors: int = 0            # LVSA: number of rotating anchor key blocks
@@ -86,6 +87,12 @@ SMALL = {
     4: WORKLOADS[4].small(21, 8, 9),      # 1512 tokens -> 24 blocks, tail 40
     5: WORKLOADS[5].small(6, 12, 15),     # 1080 tokens -> 17 blocks, tail 56
 }
+
+
+# The HunyuanVideo-like layer with PISA's global first-order term (same seeds
+# and shapes as workload 3, so the two first-order forms see the same inputs).
+GLOBAL_ORDER1 = replace(WORKLOADS[3], name="hunyuan720p-global", comp=2)
+GLOBAL_ORDER1_SMALL = replace(SMALL[3], name="hunyuan720p-global-small", comp=2)
 
 
 def get_workload(wid: int, small: bool = False) -> Workload:
