@@ -119,10 +119,13 @@ __device__ __forceinline__ void dma_offsets(uint32_t off[4]) {
 
 __device__ __forceinline__ void dma_half(__amdgpu_buffer_rsrc_t rs, uint8_t* buf, uint32_t src,
                                          const uint32_t off[4]) {
+    // the low 32 bits of a generic pointer into LDS are the LDS address (no
+    // null-pointer select per instruction, as a generic -> LDS cast would emit)
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(buf + m * 1024), 16, off[m & 3],
-                                                 src + m * 1024, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(static_cast<uintptr_t>(lds + m * 1024)),
+                                                 16, off[m & 3], src + m * 1024, 0, 0);
 }
 
 // Zero half-buffer rows r0 .. 31 (pad keys of the ragged tail block).

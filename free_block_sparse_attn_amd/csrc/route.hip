@@ -45,11 +45,38 @@ struct Threshold {
 
 // k-th largest key among candidates (key != 0 when `cand_nonzero`), k >= 1,
 // k <= number of candidates.  One wave; `hist` is 256 words of wave-private LDS.
+__device__ __forceinline__ uint64_t wave_and64(uint64_t x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x &= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(x), off));
+    return x;
+}
+__device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) x |= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(x), off));
+    return x;
+}
+
 __device__ Threshold radix_select(const uint64_t* keys, int nb, int k, uint32_t* hist, bool cand_nonzero) {
     const int lane = lane_id();
+    // Leading bytes shared by every candidate are fixed without a pass (their
+    // histogram would put every key in one bin: a 64-way LDS atomic conflict).
+    uint64_t kand = ~0ull, kor = 0ull;
+    for (int j = lane; j < nb; j += 64) {
+        const uint64_t key = keys[j];
+        if (!cand_nonzero || key != 0ull) { kand &= key; kor |= key; }
+    }
+    kand = wave_and64(kand);
+    kor = wave_or64(kor);
+    const uint64_t diff = kand ^ kor;            // bits that differ between candidates
+    int start = 56;
     uint64_t prefix = 0, pmask = 0;
+    while (start > 0 && ((diff >> start) & 0xFFull) == 0ull) {
+        pmask |= 0xFFull << start;
+        prefix |= kand & (0xFFull << start);
+        start -= 8;
+    }
     int kk = k;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int shift = start; shift >= 0; shift -= 8) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
         wave_sync();
@@ -241,31 +268,51 @@ __global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
     }
 }
 
-// LVSA: one wave per (b, h, query block); pure integer work.
-__global__ __launch_bounds__(64) void route_lvsa_kernel(RouteArgs a) {
-    const int row = blockIdx.x;
-    const size_t rowid = (static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y) * a.nb + row;
-    const int lane = lane_id();
+// LVSA: the mask depends only on the frame ranges, the anchors and the step,
+// so every (b, h) gets the same lists.  One wave per query block scans the
+// key blocks from LDS copies of the frame ranges and an anchor bitmap and
+// writes its list for every (b, h).  Pure integer work.
+constexpr int LVSA_ROWS = 4;      // query blocks per workgroup (one per wave)
+
+__global__ __launch_bounds__(64 * LVSA_ROWS) void route_lvsa_kernel(RouteArgs a) {
+    __shared__ int32_t flo[4096], fhi[4096];
+    __shared__ uint32_t anchor_bits[128];
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const int nb = a.nb;
+    for (int j = tid; j < nb; j += 64 * LVSA_ROWS) {
+        flo[j] = a.frame_lo[j];
+        fhi[j] = a.frame_hi[j];
+    }
+    for (int x = tid; x < 128; x += 64 * LVSA_ROWS) anchor_bits[x] = 0u;
+    __syncthreads();
+    const int P = a.anchors > 0 ? nb / a.anchors : 0;
+    if (P > 0) {
+        for (int i = tid; i < a.anchors; i += 64 * LVSA_ROWS) {
+            const int j = (a.anchor_phase + a.step) % P + i * P;    // < anchors * P <= nb
+            atomicOr(&anchor_bits[j >> 5], 1u << (j & 31));
+        }
+    }
+    __syncthreads();
+    const int row = blockIdx.x * LVSA_ROWS + w;
+    if (row >= nb) return;
     const uint64_t lt = (1ull << lane) - 1ull;
-    const int lo = a.frame_lo[row] - a.window, hi = a.frame_hi[row] + a.window;
-    const int P = a.anchors > 0 ? a.nb / a.anchors : 0;
-    const int off = P > 0 ? (a.anchor_phase + a.step) % P : 0;
-    int32_t* out = a.idx + rowid * a.cap;
+    const int lo = flo[row] - a.window, hi = fhi[row] + a.window;
+    const int BH = a.B * a.H;
     int base = 0;
-    for (int j0 = 0; j0 < a.nb; j0 += 64) {
+    for (int j0 = 0; j0 < nb; j0 += 64) {
         const int j = j0 + lane;
         bool sel = false;
-        if (j < a.nb) {
-            sel = a.frame_lo[j] <= hi && a.frame_hi[j] >= lo;
-            if (P > 0 && j >= off && (j - off) % P == 0 && (j - off) / P < a.anchors) sel = true;
-        }
+        if (j < nb) sel = (flo[j] <= hi && fhi[j] >= lo) || ((anchor_bits[j >> 5] >> (j & 31)) & 1u);
         const uint64_t m = __ballot(sel);
         const int pos = base + __popcll(m & lt);
-        if (sel && pos < a.cap) out[pos] = j;
+        if (sel && pos < a.cap)
+            for (int bh = 0; bh < BH; ++bh) a.idx[(static_cast<size_t>(bh) * nb + row) * a.cap + pos] = j;
         base += __popcll(m);
     }
-    for (int p = base + lane; p < a.cap; p += 64) out[p] = -1;
-    if (lane == 0) a.cnt[rowid] = base;
+    for (int p = base + lane; p < a.cap; p += 64)
+        for (int bh = 0; bh < BH; ++bh) a.idx[(static_cast<size_t>(bh) * nb + row) * a.cap + p] = -1;
+    if (lane == 0)
+        for (int bh = 0; bh < BH; ++bh) a.cnt[static_cast<size_t>(bh) * nb + row] = base;
 }
 
 template <int R>
@@ -282,8 +329,8 @@ hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     if (a.mode == 1) {
-        dim3 grid(a.nb, a.H, a.B);
-        hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64), 0, s, a);
+        dim3 grid((a.nb + LVSA_ROWS - 1) / LVSA_ROWS);
+        hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64 * LVSA_ROWS), 0, s, a);
         return hipGetLastError();
     }
     // rows per workgroup: as many as fit a 64 KiB key budget, at most 16
