@@ -78,6 +78,23 @@ def global_moment(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.nd
     return block_moments(k, v, N, blk).mean(axis=2)
 
 
+def covariance_norms(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.ndarray:
+    """ln M_j with M_j = ||H_j - H_bar||_2, the largest singular value of the
+    block's deviation from the head's mean moment, fp64 [B,H,nb].
+
+    PISA's covariance-aware top-k ("PISA ...", section 2, "Routage Sensible a
+    la Covariance") weighs each block by this norm: a block whose moment is
+    far from H_bar is badly served by the global first-order term.  The
+    spectral norm is taken from the singular values (numpy's matrix 2-norm);
+    a block whose moment equals H_bar gets ln 0 = -inf.
+    """
+    H = block_moments(k, v, N, blk)
+    D = H - H.mean(axis=2)[:, :, None]
+    M = np.linalg.norm(D, ord=2, axis=(3, 4))
+    with np.errstate(divide="ignore"):
+        return np.log(M)
+
+
 def block_spreads(k: np.ndarray, v: np.ndarray, N: int, blk: int = BLK) -> np.ndarray:
     """lambda_j = ln(r_k * r_v) with r_x^2 = sum_n ||x_n - x_bar_j||^2, as fp32 [B,H,nb].
 
@@ -119,7 +136,7 @@ def e4m3_blocks(x: np.ndarray, N: int, blk: int = BLK):
     return codes.reshape(B, H, nb * blk, d), e
 
 
-def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hbar=False):
+def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hbar=False, cov=False):
     """Everything the router and the fused forward read, in one dict."""
     qbar, qbar64, n = block_means(q, N, blk)
     kbar, kbar64, _ = block_means(k, N, blk)
@@ -130,6 +147,8 @@ def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hb
         out["kmom"] = block_moments(k, v, N, blk)
     if hbar:
         out["hbar"] = global_moment(k, v, N, blk)
+    if cov:
+        out["kcov"] = covariance_norms(k, v, N, blk)
     if spreads:
         out["klam"] = block_spreads(k, v, N, blk)
     if fp8:

@@ -62,6 +62,36 @@ def route_topk(qbar: np.ndarray, kbar: np.ndarray, k: int):
     return idx, cnt
 
 
+def route_topk_cov(qbar: np.ndarray, kbar: np.ndarray, kcov: np.ndarray, scale: float, k: int):
+    """PISA's covariance-aware top-k ("PISA ...", section 2, "Routage Sensible
+    a la Covariance"): the selection key combines the block's attention score
+    with the norm M_j = ||H_j - H_bar||_2 of its deviation from the global
+    first-order statistic.
+
+    Reading used: after the global term, block j's remaining first-order
+    error at query t is alpha_{t,j} q_t (H_j - H_bar), at most
+    exp(scale q_t.k_bar_j) |q_t| M_j; at the pooled query the row factor |q|
+    is common to all j, so blocks are ranked by its log
+      key(a, j) = fl(fl(scale * s(a, j)) + ln M_j)      (fp64, ln M_j from fp32)
+    High-score blocks and strongly heterogeneous blocks both rank high.  The
+    first k in the order (-key, j) are computed exactly.
+    kcov: fp32 [B,H,nb] = ln M_j.  Returns (idx int32 [B,H,nb,k], cnt).
+    """
+    B, H, nq, _ = qbar.shape
+    nk = kbar.shape[2]
+    kk = min(k, nk)
+    sc = np.float64(np.float32(scale))
+    idx = np.full((B, H, nq, kk), -1, np.int32)
+    cnt = np.full((B, H, nq), kk, np.int32)
+    for b in range(B):
+        for h in range(H):
+            key = sc * block_scores(qbar[b, h], kbar[b, h]) + \
+                np.asarray(kcov[b, h], np.float32).astype(np.float64)[None, :]
+            for a in range(nq):
+                idx[b, h, a] = _select_first(key[a], kk)
+    return idx, cnt
+
+
 def lvsa_anchor_set(nb: int, anchors: int, phase: int, step: int) -> np.ndarray:
     """Rotating global anchor key blocks G_s at denoising step s.
 

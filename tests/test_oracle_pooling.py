@@ -87,6 +87,67 @@ def test_moments_brute_force():
                 assert abs(H[0, 0, j, i, o] - ref) < 1e-9
 
 
+def test_covariance_norm_rank_one_closed_form():
+    # block 0: keys move along one direction u, so H_0 = u w^T with
+    # w = sum_n (c_n - c_mean) v_n; block 1: constant keys, H_1 = 0.
+    # H_bar = H_0 / 2, so both deviations have norm |u| |w| / 2.
+    rng = np.random.default_rng(61)
+    d, blk = 5, 8
+    u = rng.integers(-3, 4, d).astype(np.float64)
+    c = rng.integers(-4, 5, blk).astype(np.float64)
+    k = np.zeros((1, 1, 2 * blk, d), np.float32)
+    k[0, 0, :blk] = 1.0 + c[:, None] * u[None, :]
+    k[0, 0, blk:] = rng.integers(-2, 3, d)
+    v = rng.integers(-3, 4, (1, 1, 2 * blk, d)).astype(np.float32)
+    cm = sum(c) / blk
+    w = [sum((c[n] - cm) * float(v[0, 0, n, o]) for n in range(blk)) for o in range(d)]
+    ref = math.sqrt(sum(x * x for x in u)) * math.sqrt(sum(x * x for x in w)) / 2
+    lnm = pooling.covariance_norms(k, v, 2 * blk, blk)
+    np.testing.assert_allclose(np.exp(lnm[0, 0]), [ref, ref], rtol=1e-12)
+
+
+def test_covariance_norm_diagonal_closed_form():
+    # each block holds, per dimension i, a token pair k = base +- a e_i,
+    # v = c +- b e_i: the keys average to base and H_j = diag(2 a b), so
+    # M_j = max_i |2 a_ji b_ji - mean_j(2 a_ji b_ji)|.
+    rng = np.random.default_rng(62)
+    d, nb = 4, 3
+    blk = 2 * d
+    a = rng.integers(1, 5, (nb, d)).astype(np.float64)
+    b = rng.integers(-4, 5, (nb, d)).astype(np.float64)
+    k = np.zeros((1, 1, nb * blk, d), np.float32)
+    v = np.zeros((1, 1, nb * blk, d), np.float32)
+    for j in range(nb):
+        base = rng.integers(-3, 4, d)
+        for i in range(d):
+            cvec = rng.integers(-3, 4, d)
+            for s, t in ((1, 2 * i), (-1, 2 * i + 1)):
+                k[0, 0, j * blk + t] = base
+                k[0, 0, j * blk + t, i] += s * a[j, i]
+                v[0, 0, j * blk + t] = cvec
+                v[0, 0, j * blk + t, i] += s * b[j, i]
+    h = 2 * a * b
+    ref = [max(abs(h[j, i] - sum(h[:, i]) / nb) for i in range(d)) for j in range(nb)]
+    lnm = pooling.covariance_norms(k, v, nb * blk, blk)
+    np.testing.assert_allclose(np.exp(lnm[0, 0]), ref, rtol=1e-12)
+
+
+def test_covariance_norm_invariances():
+    k, v = rand_inputs(63, N=200, d=6), rand_inputs(64, N=200, d=6)
+    base = pooling.covariance_norms(k, v, 200)
+    # a constant shift of one block's keys leaves its centred moment unchanged
+    k2 = k.copy()
+    k2[:, :, 64:128] += np.float32(0.5)
+    np.testing.assert_allclose(pooling.covariance_norms(k2, v, 200), base, rtol=1e-9)
+    # scaling V by c scales every M_j by |c|
+    np.testing.assert_allclose(pooling.covariance_norms(k, np.float32(-2.0) * v, 200), base + math.log(2.0),
+                               rtol=1e-9)
+    # identical blocks (a power-of-two count, so the mean is exact): M_j = 0
+    blockv = v[:, :, :64]
+    same = np.concatenate([k[:, :, :64]] * 4, axis=2), np.concatenate([blockv] * 4, axis=2)
+    assert np.all(np.isneginf(pooling.covariance_norms(*same, 256)))
+
+
 def test_spreads_variance_identity():
     k, v = rand_inputs(31, N=130), rand_inputs(32, N=130)
     lam = pooling.block_spreads(k, v, 130)

@@ -68,6 +68,43 @@ def test_topk_monotone_and_ties_low_index():
         assert j in idx2[0, 0, 0]
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_topk_cov_exhaustive(seed):
+    # integer scores and integer log-norms: every key is an exact integer
+    rng = np.random.default_rng(100 + seed)
+    nb = 9
+    q, kb = int_feats(rng, (1, 1, nb, 3), -2, 3), int_feats(rng, (1, 1, nb, 3), -2, 3)
+    kcov = rng.integers(-3, 4, (1, 1, nb)).astype(np.float32)
+    s = routing.block_scores(q, kb)[0, 0]
+    for scale in (1.0, 2.0):
+        for k in (1, 4, 9):
+            idx, cnt = routing.route_topk_cov(q, kb, kcov, scale, k)
+            for a in range(nb):
+                key = [scale * s[a, j] + float(kcov[0, 0, j]) for j in range(nb)]
+                assert list(idx[0, 0, a]) == brute_topk(key, k)
+                assert cnt[0, 0, a] == k
+
+
+def test_topk_cov_equal_norms_is_topk():
+    rng = np.random.default_rng(110)
+    q = rng.standard_normal((2, 2, 12, 8)).astype(np.float32)
+    kb = rng.standard_normal((2, 2, 12, 8)).astype(np.float32)
+    kcov = np.full((2, 2, 12), 1.25, np.float32)
+    a, _ = routing.route_topk_cov(q, kb, kcov, 1.0, 5)
+    b, _ = routing.route_topk(q, kb, 5)
+    assert np.array_equal(a, b)
+
+
+def test_topk_cov_zero_queries_rank_by_norm():
+    # all scores 0: the key is ln M_j alone; -inf (M_j = 0) blocks come last
+    kcov = np.array([0.5, -np.inf, 2.0, 0.5, -1.0, -np.inf, 3.0], np.float32).reshape(1, 1, 7)
+    q = np.zeros((1, 1, 2, 3), np.float32)
+    kb = np.ones((1, 1, 7, 3), np.float32)
+    for k, want in ((3, [0, 2, 6]), (5, [0, 2, 3, 4, 6]), (6, [0, 1, 2, 3, 4, 6])):
+        idx, _ = routing.route_topk_cov(q, kb, kcov, 1.0, k)
+        assert list(idx[0, 0, 0]) == want and list(idx[0, 0, 1]) == want
+
+
 def test_lvsa_anchor_rotation_covers_each_block_once():
     nb, anchors, phase = 1975, 8, 117
     P = nb // anchors
