@@ -17,13 +17,13 @@ import torch
 from . import _lib
 from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER0,
                    SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL, SA_ROUTE_TOPK, SA_ROUTE_LVSA,
-                   SA_ROUTE_TRIAGE)
+                   SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV)
 
 __all__ = [
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
-    "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE",
+    "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE", "SA_ROUTE_TOPK_COV",
 ]
 
 BLK = 64
@@ -61,10 +61,12 @@ def abi_version() -> int:
 
 
 def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None,
-                     global_moment=False, out=None) -> dict:
+                     global_moment=False, cov=False, out=None) -> dict:
     """Block means (fp32), counts and the optional centroid planes / moments /
-    mean moment H_bar (with its 64-partial scratch) / spreads / e4m3 copies.  The bf16 centroid planes (what the bf16 forward
-    reads) are produced by default for bf16 inputs with d == 128.
+    mean moment H_bar (with its 64-partial scratch) / covariance log-norms
+    ln ||H_j - H_bar||_2 (`cov`, implies `global_moment`) / spreads / e4m3
+    copies.  The bf16 centroid planes (what the bf16 forward reads) are
+    produced by default for bf16 inputs with d == 128.
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
     """
@@ -78,8 +80,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
         _lib.check(lib.sparse_attn_pool(
             ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
             _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("klam")),
-            _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
+            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
+            _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
         return out
     out = {
         "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
@@ -94,9 +96,11 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
         out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.bfloat16, device=dev)
     if moments:
         out["kmom"] = torch.empty(B, H, nb, d * d, dtype=torch.bfloat16, device=dev)   # MFMA operand order
-    if global_moment:
+    if global_moment or cov:
         out["hbar"] = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)          # value-major
         out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
+    if cov:
+        out["kcov"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
     if spreads:
         out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
     if fp8:
@@ -108,8 +112,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
     _lib.check(lib.sparse_attn_pool(
         ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("klam")),
-        _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
+        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
+        _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
     return out
 
 
@@ -130,6 +134,9 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
                       out=None):
     """Key-block lists per query block: (idx, cnt, idx2, cnt2); idx2/cnt2 only for Triage.
 
+    TOPK_COV reads pooled["kcov"] (sparse_attn_pool(..., cov=True)), Triage
+    pooled["klam"] (spreads=True); both use `scale` in their keys.
+
     `out` may pass preallocated (idx, cnt, idx2, cnt2) tensors.
     """
     lib = _lib.load()
@@ -140,7 +147,8 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
     spec = _lib.RouteSpec(mode, topk, None, None, window, anchors, anchor_phase, step,
                           n_keep, n_refine, scale)
     cap2 = 0
-    if mode == SA_ROUTE_TOPK:
+    kterm = pooled.get("kcov") if mode == SA_ROUTE_TOPK_COV else pooled.get("klam")
+    if mode in (SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV):
         cap = cap or topk
     elif mode == SA_ROUTE_LVSA:
         _contig(frame_lo, frame_hi)
@@ -162,7 +170,7 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
         idx, cnt, idx2, cnt2 = out
     _lib.check(lib.sparse_attn_route(
         ctypes.byref(shape), ctypes.byref(spec), _ptr(qbar), _ptr(kbar), _ptr(pooled.get("kcount")),
-        _ptr(pooled.get("klam")), _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2, _stream(qbar)))
+        _ptr(kterm), _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2, _stream(qbar)))
     return idx, cnt, idx2, cnt2
 
 

@@ -80,14 +80,14 @@ int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* kmom,
-                           float* hbar, float* hbar_ws, float* klam,
+                           float* hbar, float* hbar_ws, float* kcov, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (empty) return ok();
     NEED(q); NEED(k); NEED(v); NEED(qbar); NEED(kbar); NEED(vbar); NEED(kcount);
-    MAYBE(cent); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
+    MAYBE(cent); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(kcov); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
     const int fp8 = (q8 != nullptr) + (k8 != nullptr) + (v8 != nullptr) + (exp8 != nullptr);
     if (fp8 != 0 && fp8 != 4) return fail(SA_ERR_INVALID_ARG, "q8, k8, v8 and exp8 must be given together");
     const bool bf16_128 = dtype == SA_BF16 && shape->d == 128;
@@ -95,9 +95,10 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q,
     if (kmom && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "kmom needs bf16 inputs with d == 128");
     if ((hbar != nullptr) != (hbar_ws != nullptr)) return fail(SA_ERR_INVALID_ARG, "hbar and hbar_ws go together");
     if (hbar && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "hbar needs bf16 inputs with d == 128");
+    if (kcov && !hbar) return fail(SA_ERR_INVALID_ARG, "kcov needs hbar (M_j is taken against H_bar)");
     if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
     sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
-                   cent, kmom, hbar, hbar_ws, klam, q8, k8, v8, exp8};
+                   cent, kmom, hbar, hbar_ws, kcov, klam, q8, k8, v8, exp8};
     return hip_result(sa::launch_pool(a, dtype == SA_BF16, stream), "pool");
 }
 
@@ -116,7 +117,7 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* lo, const int32_t* hi, int32_t 
 }
 
 sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, const float* qbar, const float* kbar,
-                            const int32_t* kcount, const float* klam, int32_t* idx, int32_t* cnt, int32_t cap,
+                            const int32_t* kcount, const float* kterm, int32_t* idx, int32_t* cnt, int32_t cap,
                             int32_t* idx2, int32_t* cnt2, int32_t cap2, hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
@@ -126,7 +127,7 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
     if (empty) return ok();
     sa::RouteArgs a{};
     a.B = shape->B; a.H = shape->H; a.nb = nb; a.d = shape->d; a.mode = spec->mode;
-    a.qbar = qbar; a.kbar = kbar; a.kcount = kcount; a.klam = klam;
+    a.qbar = qbar; a.kbar = kbar; a.kcount = kcount; a.klam = kterm;
     a.idx = idx; a.cnt = cnt; a.cap = cap; a.idx2 = idx2; a.cnt2 = cnt2; a.cap2 = cap2;
     switch (spec->mode) {
         case SA_ROUTE_TOPK:
@@ -135,6 +136,14 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
                 return fail(SA_ERR_INVALID_ARG, "topk must be in [1, nb=%d], got %d", nb, spec->topk);
             if (cap < spec->topk) return fail(SA_ERR_INVALID_ARG, "cap %d < topk %d", cap, spec->topk);
             a.topk = spec->topk;
+            break;
+        case SA_ROUTE_TOPK_COV:
+            NEED(qbar); NEED(kbar); NEED(kterm); NEED(idx); NEED(cnt);
+            if (!empty && (spec->topk < 1 || spec->topk > nb))
+                return fail(SA_ERR_INVALID_ARG, "topk must be in [1, nb=%d], got %d", nb, spec->topk);
+            if (cap < spec->topk) return fail(SA_ERR_INVALID_ARG, "cap %d < topk %d", cap, spec->topk);
+            if (!std::isfinite(spec->scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+            a.topk = spec->topk; a.scale = spec->scale;
             break;
         case SA_ROUTE_LVSA:
             NEED(spec->frame_lo); NEED(spec->frame_hi); NEED(idx); NEED(cnt);
@@ -147,7 +156,7 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
             a.anchors = spec->anchors; a.anchor_phase = spec->anchor_phase; a.step = spec->step;
             break;
         case SA_ROUTE_TRIAGE:
-            NEED(qbar); NEED(kbar); NEED(kcount); NEED(klam); NEED(cnt);
+            NEED(qbar); NEED(kbar); NEED(kcount); NEED(kterm); NEED(cnt);
             if (!empty && (spec->n_keep < 1 || spec->n_keep > nb))
                 return fail(SA_ERR_INVALID_ARG, "n_keep must be in [1, nb=%d], got %d", nb, spec->n_keep);
             if (spec->n_refine < 0 || spec->n_refine > spec->n_keep)

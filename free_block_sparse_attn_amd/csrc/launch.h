@@ -21,6 +21,7 @@ struct PoolArgs {
     void* kmom;       // bf16 [B,H,nb,d*d] in MFMA operand order, or null
     float* hbar;      // fp32 [B,H,d,d] value-major mean moment, or null
     float* hbar_ws;   // fp32 [B,H,64,d,d] partial sums (with hbar)
+    float* kcov;      // fp32 [B,H,nb] ln ||H_j - H_bar||_2 (with hbar), or null
     float* klam;      // [B,H,nb] or null
     uint8_t* q8;      // e4m3 copies or null (all or none)
     uint8_t* k8;
@@ -41,7 +42,7 @@ struct RouteArgs {
     const float* qbar;
     const float* kbar;
     const int32_t* kcount;
-    const float* klam;
+    const float* klam;        // per-block log term: lambda_j (Triage) or ln M_j (covariance top-k)
     int32_t* idx;
     int32_t* cnt;
     int cap;

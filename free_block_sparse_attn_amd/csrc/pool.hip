@@ -378,70 +378,83 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
 // by nb, so H_bar is bit-reproducible.
 constexpr int HBAR_PARTS = 64;
 
-__global__ __launch_bounds__(THREADS) void hbar_partial_kernel(PoolArgs a) {
+// Adds block j's centred moment G[o][i] = sum_n v_n[o] (k_n[i] - kbar_j[i])
+// to the workgroup's fp32 MFMA accumulators: wave w, lane l holds column
+// i = 32 w + l % 32 and rows o = 32 ob + 8 (r / 4) + 4 ((l / 32) % 2) + r % 4 of
+// acc[ob][r].  The centred keys are split into bf16 hi + lo parts, so the
+// products carry about 16 bits of each key deviation (fp32 accumulation).
+// xt: 2 * D * TPITCH bf16 of LDS, kb_s: D floats of LDS.
+__device__ __forceinline__ void add_block_moment(const PoolArgs& a, size_t bh, int j, uint16_t* xt, float* kb_s,
+                                                 f32x16 (&acc)[4]) {
     constexpr int D = 128;
     using E = Elem<uint16_t>;
     constexpr int CPR = D / 8;
     constexpr int PT = BLK * CPR / THREADS;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int nb = a.N_pad / BLK;
+    const int icol = 32 * w + l32;
+    const uint16_t* src[2] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v)};
+    const int n = min(BLK, a.N - BLK * j);
+    const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
+    u32x4 reg[2][PT];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+            const int chunk = tid + THREADS * q;
+            const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (row < n) z = *reinterpret_cast<const u32x4*>(src[t] + tok0 + static_cast<size_t>(row) * D + col0);
+            reg[t][q] = z;
+        }
+    const float kbj = tid < D ? a.kbar[(bh * nb + j) * D + tid] : 0.0f;
+    __syncthreads();                          // every wave is done with the previous staging
+    if (tid < D) kb_s[tid] = kbj;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int q = 0; q < PT; ++q) {
+            const int chunk = tid + THREADS * q;
+            const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xt[(t * D + col0 + e) * TPITCH + row] = E::raw(reg[t][q], e);
+        }
+    __syncthreads();
+    const float kb = kb_s[icol];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int t0 = 16 * ks + 8 * hl;
+        bf16x8 bhi, blo;
+        const uint16_t* kc = xt + icol * TPITCH + t0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float x = (t0 + e < n) ? E::val(kc[e]) - kb : 0.0f;
+            const __bf16 hi = static_cast<__bf16>(x);
+            bhi[e] = hi;
+            blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+        }
+#pragma unroll
+        for (int ob = 0; ob < 4; ++ob) {
+            const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (D + 32 * ob + l32) * TPITCH + t0);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[ob], 0, 0, 0);
+            acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
+        }
+    }
+}
+
+__global__ __launch_bounds__(THREADS) void hbar_partial_kernel(PoolArgs a) {
+    constexpr int D = 128;
     __shared__ __attribute__((aligned(16))) uint16_t xt[2 * D * TPITCH];   // K^T, V^T of one block
     __shared__ float kb_s[D];
     const int c = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int l = threadIdx.x & 63, hl = l >> 5;
+    const int icol = 32 * (threadIdx.x >> 6) + (l & 31);
     const int nb = a.N_pad / BLK;
-    const int icol = 32 * w + l32;
     f32x16 acc[4];
 #pragma unroll
     for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x16{};
-    const uint16_t* src[2] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v)};
-    for (int j = c; j < nb; j += HBAR_PARTS) {
-        const int n = min(BLK, a.N - BLK * j);
-        const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
-        u32x4 reg[2][PT];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < PT; ++q) {
-                const int chunk = tid + THREADS * q;
-                const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
-                u32x4 z = {0u, 0u, 0u, 0u};
-                if (row < n) z = *reinterpret_cast<const u32x4*>(src[t] + tok0 + static_cast<size_t>(row) * D + col0);
-                reg[t][q] = z;
-            }
-        const float kbj = tid < D ? a.kbar[(bh * nb + j) * D + tid] : 0.0f;
-        __syncthreads();                          // every wave is done with the previous block
-        if (tid < D) kb_s[tid] = kbj;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-            for (int q = 0; q < PT; ++q) {
-                const int chunk = tid + THREADS * q;
-                const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) xt[(t * D + col0 + e) * TPITCH + row] = E::raw(reg[t][q], e);
-            }
-        __syncthreads();
-        const float kb = kb_s[icol];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int t0 = 16 * ks + 8 * hl;
-            bf16x8 bhi, blo;
-            const uint16_t* kc = xt + icol * TPITCH + t0;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float x = (t0 + e < n) ? E::val(kc[e]) - kb : 0.0f;
-                const __bf16 hi = static_cast<__bf16>(x);
-                bhi[e] = hi;
-                blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
-            }
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob) {
-                const bf16x8 av = *reinterpret_cast<const bf16x8*>(xt + (D + 32 * ob + l32) * TPITCH + t0);
-                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[ob], 0, 0, 0);
-                acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
-            }
-        }
-    }
+    for (int j = c; j < nb; j += HBAR_PARTS) add_block_moment(a, bh, j, xt, kb_s, acc);
     float* part = a.hbar_ws + (bh * HBAR_PARTS + c) * static_cast<size_t>(D) * D;
 #pragma unroll
     for (int ob = 0; ob < 4; ++ob)
@@ -461,6 +474,186 @@ __global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
         double sum = 0.0;
         for (int c = 0; c < HBAR_PARTS; ++c) sum += static_cast<double>(part[static_cast<size_t>(c) * D * D + e]);
         a.hbar[bh * D * D + e] = static_cast<float>(sum / static_cast<double>(nb));
+    }
+}
+
+// PISA's covariance-aware routing statistic ("PISA ...", section 2, "Routage
+// Sensible a la Covariance"): M_j = ||H_j - H_bar||_2, written as ln M_j.
+// One workgroup per (block, head): the block's moment is rebuilt in MFMA
+// accumulators (never stored), H_bar subtracted, and the deviation parked in
+// LDS as fp32 value-major Dm[o][i], from which each thread keeps an 8 x 8 tile
+// in registers.  M_j^2 is the largest eigenvalue of A = Dm^T Dm, found by
+// COV_STEPS steps of the Lanczos recurrence on A (two tile products per step,
+// partial sums combined across tiles in a fixed order through LDS, so the
+// result is deterministic) and then the largest eigenvalue of the Lanczos
+// tridiagonal by 64-point multisection with Sturm counts.  Lanczos converges
+// with the square root of the relative gap, so blocks whose two top singular
+// values are within a few percent (where plain power iteration stalls) still
+// come out to fp32 accuracy.  The Ritz value never exceeds M_j^2 beyond
+// rounding.
+constexpr int COV_STEPS = 32;
+
+__device__ __forceinline__ float block_sum128(float x, float* red) {
+    // sum over threads 0..127 (waves 0 and 1); every thread of the workgroup gets it
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+    if ((threadIdx.x & 63) == 0 && threadIdx.x < 128) red[threadIdx.x >> 6] = x;
+    __syncthreads();
+    return red[0] + red[1];
+}
+
+// Eigenvalues of the symmetric tridiagonal (diagonal al, off-diagonal be) below x.
+__device__ __forceinline__ int sturm_below(const float* al, const float* be, int n, float x) {
+    int c = 0;
+    float d = 1.0f;
+    for (int k = 0; k < n; ++k) {
+        d = al[k] - x - (k > 0 ? be[k - 1] * be[k - 1] / d : 0.0f);
+        if (fabsf(d) < 1e-30f) d = -1e-30f;
+        c += d < 0.0f;
+    }
+    return c;
+}
+
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void cov_norm_kernel(PoolArgs a) {
+    constexpr int D = 128;
+    // the block staging, then half of Dm at a time (rows 64 hf .. 64 hf + 63)
+    __shared__ __attribute__((aligned(16))) uint16_t stage[2 * D * TPITCH];
+    __shared__ float part[16 * D];
+    __shared__ float yv_s[D], wv_s[D];
+    __shared__ float kb_s[D];
+    __shared__ float al[COV_STEPS], be[COV_STEPS];
+    __shared__ float red[4];
+    float* dmh = reinterpret_cast<float*>(stage);
+    static_assert(64 * D * sizeof(float) <= sizeof(stage), "half of Dm fits the staging buffer");
+    const int j = blockIdx.x;
+    const size_t bh = blockIdx.y;
+    const int tid = threadIdx.x, l = tid & 63, hl = l >> 5;
+    const int icol = 32 * (tid >> 6) + (l & 31);
+    const int nb = a.N_pad / BLK;
+    f32x16 acc[4];
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x16{};
+    add_block_moment(a, bh, j, stage, kb_s, acc);
+    const float* hb = a.hbar + bh * D * D;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[ob][r] -= hb[(32 * ob + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + icol];
+    // thread tile: rows o = 8 tr + u, columns i = 8 tc + v, moved over in two row halves
+    const int tr = tid >> 4, tc = tid & 15;
+    float t[8][8];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+        __syncthreads();                      // the staging / previous half is consumed
+#pragma unroll
+        for (int ob = 2 * hf; ob < 2 * hf + 2; ++ob)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                dmh[(32 * (ob - 2 * hf) + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + icol] = acc[ob][r];
+        __syncthreads();
+        if ((tr >> 3) == hf) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const float* row = dmh + (8 * (tr & 7) + u) * D + 8 * tc;
+                const f32x4 lo = *reinterpret_cast<const f32x4*>(row);
+                const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 4);
+#pragma unroll
+                for (int v = 0; v < 4; ++v) { t[u][v] = lo[v]; t[u][v + 4] = hi[v]; }
+            }
+        }
+    }
+    // Lanczos start q_1 = x / |x|, x_i = 1 + frac(0.618034 i); q_0 = 0.  Thread
+    // i < 128 keeps q_i and q_prev_i; the new q reaches every tile through wv_s.
+    float n0 = 0.0f;
+    for (int i = 0; i < D; ++i) {
+        const float fi = static_cast<float>(i) * 0.618034f;
+        const float xi = 1.0f + (fi - floorf(fi));
+        n0 += xi * xi;
+    }
+    const float inv0 = rsqrtf(n0);
+    float qi = 0.0f, qpi = 0.0f;
+    if (tid < D) {
+        const float fi = static_cast<float>(tid) * 0.618034f;
+        qi = (1.0f + (fi - floorf(fi))) * inv0;
+    }
+    float x[8];
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+        const float fi = static_cast<float>(8 * tc + v) * 0.618034f;
+        x[v] = (1.0f + (fi - floorf(fi))) * inv0;
+    }
+    int steps = 0;
+    float beta = 0.0f;
+    for (int k = 0; k < COV_STEPS; ++k) {
+        // y = Dm q: partial sums over this tile's columns, summed over the 16 column tiles
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            float p = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) p = fmaf(t[u][v], x[v], p);
+            part[tc * D + 8 * tr + u] = p;
+        }
+        __syncthreads();
+        float y = 0.0f;
+        if (tid < D) {
+#pragma unroll
+            for (int c = 0; c < 16; ++c) y += part[c * D + tid];
+            yv_s[tid] = y;
+        }
+        const float alpha = block_sum128(tid < D ? y * y : 0.0f, red);   // q^T A q = |Dm q|^2
+        // w = Dm^T y - alpha q - beta q_prev: partial sums over this tile's rows
+        float yy[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) yy[u] = yv_s[8 * tr + u];
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+            float p = 0.0f;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) p = fmaf(t[u][v], yy[u], p);
+            part[tr * D + 8 * tc + v] = p;
+        }
+        __syncthreads();
+        float w = 0.0f;
+        if (tid < D) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) w += part[r * D + tid];
+            w = w - alpha * qi - beta * qpi;
+            wv_s[tid] = w;
+        }
+        beta = sqrtf(block_sum128(tid < D ? w * w : 0.0f, red + 2));
+        if (tid == 0) { al[k] = alpha; be[k] = beta; }
+        steps = k + 1;
+        if (!(beta > alpha * 0x1p-20f)) break;    // invariant subspace (or A = 0): T is exact
+        const float ib = 1.0f / beta;
+        qpi = qi;
+        qi = w * ib;
+#pragma unroll
+        for (int v = 0; v < 8; ++v) x[v] = wv_s[8 * tc + v] * ib;
+    }
+    __syncthreads();
+    if (tid < 64) {
+        // largest eigenvalue of T: Gershgorin bracket, then five rounds of
+        // 64-point multisection (lane p tests lo + (p + 1) (hi - lo) / 64)
+        float lo = 0.0f, hi = 0.0f;
+        for (int k = 0; k < steps; ++k) {
+            const float off = (k > 0 ? fabsf(be[k - 1]) : 0.0f) + (k + 1 < steps ? fabsf(be[k]) : 0.0f);
+            lo = fmaxf(lo, al[k]);
+            hi = fmaxf(hi, al[k] + off);
+        }
+        hi = hi * (1.0f + 0x1p-20f) + 1e-30f;
+        for (int rnd = 0; rnd < 5; ++rnd) {
+            const float pt = lo + (hi - lo) * (static_cast<float>(l + 1) * (1.0f / 64.0f));
+            const uint64_t all = __ballot(sturm_below(al, be, steps, pt) == steps);
+            const int m = all ? __builtin_ctzll(all) : 63;
+            const float nhi = __shfl(pt, m);
+            const float nlo = m > 0 ? __shfl(pt, m - 1) : lo;
+            lo = nlo;
+            hi = nhi;
+        }
+        if (tid == 0) {
+            const bool zero = al[0] == 0.0f && steps == 1;
+            a.kcov[bh * nb + j] = zero ? -INFINITY : 0.5f * logf(hi);
+        }
     }
 }
 
@@ -492,6 +685,8 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
     hipLaunchKernelGGL(hbar_partial_kernel, dim3(HBAR_PARTS, a.B * a.H), dim3(THREADS), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(hbar_reduce_kernel, dim3(a.B * a.H), dim3(THREADS), 0, s, a);
+    if ((e = hipGetLastError()) != hipSuccess || !a.kcov) return e;
+    hipLaunchKernelGGL(cov_norm_kernel, dim3(a.N_pad / BLK, a.B * a.H), dim3(THREADS), 0, s, a);
     return hipGetLastError();
 }
 

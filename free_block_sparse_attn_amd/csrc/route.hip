@@ -158,7 +158,7 @@ __device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, 
         qs[x] = (row < nb) ? static_cast<double>(a.qbar[(bh * nb + row) * d + i]) : 0.0;
     }
     __syncthreads();
-    const bool triage = a.mode == 2;
+    const bool triage = a.mode == 2, cov = a.mode == 3;
     const double sc = static_cast<double>(a.scale);
     for (int j = tid; j < nb; j += THREADS) {
         double acc[R];
@@ -175,7 +175,11 @@ __device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, 
                 for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * d + 4 * i4 + u], kd[u], acc[r]);
             }
         }
-        if (!triage) {
+        if (cov) {
+            const double lm = static_cast<double>(a.klam[bh * nb + j]);
+#pragma unroll
+            for (int r = 0; r < R; ++r) keyE[r * nbp + j] = order_key(__dadd_rn(__dmul_rn(sc, acc[r]), lm));
+        } else if (!triage) {
 #pragma unroll
             for (int r = 0; r < R; ++r) keyE[r * nbp + j] = order_key(acc[r]);
         } else {

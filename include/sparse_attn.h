@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 3
+#define SPARSE_ATTN_ABI_VERSION 4
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -78,7 +78,8 @@ typedef enum {
 typedef enum {
     SA_ROUTE_TOPK = 0,
     SA_ROUTE_LVSA = 1,
-    SA_ROUTE_TRIAGE = 2
+    SA_ROUTE_TRIAGE = 2,
+    SA_ROUTE_TOPK_COV = 3
 } sa_route_mode;
 
 /* Problem shape.  d must be 64 or 128. */
@@ -123,6 +124,16 @@ typedef struct {
  *                        (64 partial sums per head, summed in a fixed order,
  *                        so the result is bit-reproducible).  bf16 inputs with
  *                        d == 128 only.
+ *   kcov                 fp32 [B,H,nb]  ln M_j, M_j = ||H_j - H_bar||_2 (the
+ *                        largest singular value of the block's deviation from
+ *                        the mean moment): the statistic of PISA's
+ *                        covariance-aware top-k (section 2, "Routage Sensible
+ *                        a la Covariance").  H_j is rebuilt in fp32 (never
+ *                        stored); M_j comes from power iteration on
+ *                        (H_j - H_bar)^T (H_j - H_bar), stopped when the
+ *                        estimate moves by < 2^-22 relative (4..64 steps); it
+ *                        approaches M_j from below.  -inf when M_j = 0.  Needs
+ *                        hbar (and hbar_ws).
  *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
  *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
  *                        omission-error statistic); -inf for 1-token blocks.
@@ -141,14 +152,15 @@ typedef struct {
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount,
-                           void* cent, void* kmom, float* hbar, float* hbar_ws, float* klam,
+                           void* cent, void* kmom, float* hbar, float* hbar_ws, float* kcov, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
                            hipStream_t stream);
 
 /* Routing request.  Unused fields are ignored by the other modes. */
 typedef struct {
     int32_t mode;                 /* sa_route_mode */
-    /* SA_ROUTE_TOPK: keep `topk` (1..nb) key blocks per query block. */
+    /* SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV: keep `topk` (1..nb) key blocks per
+       query block. */
     int32_t topk;
     /* SA_ROUTE_LVSA: device int32 [nb] first/last latent frame of each block. */
     const int32_t* frame_lo;
@@ -160,19 +172,26 @@ typedef struct {
     /* SA_ROUTE_TRIAGE: tiers per query block. */
     int32_t n_keep;               /* refine + skim blocks (1..nb) */
     int32_t n_refine;             /* refine blocks (0..n_keep) */
-    float scale;                  /* softmax scale used in the router's keys */
+    float scale;                  /* softmax scale in the keys (TRIAGE, TOPK_COV) */
 } sa_route_spec;
 
 /*
  * sparse_attn_route - choose the key blocks of every query block.
  *
- * Scores (TOPK, TRIAGE): s(a, j) = sum_i qbar[a,i] * kbar[j,i], fp64,
+ * Scores (TOPK, TOPK_COV, TRIAGE): s(a, j) = sum_i qbar[a,i] * kbar[j,i], fp64,
  * accumulated in i = 0..d-1 order (products of fp32 values are exact in
  * fp64).  Selections use the total order (-key, j): ties go to the lower
  * block index.  Lists are written ascending, padded with -1 up to `cap`.
  *
  *   TOPK   idx/cnt = the topk best blocks by s (PISA's top-k critical set);
  *          cap >= topk.  idx2/cnt2 unused (may be NULL).
+ *   TOPK_COV  PISA's covariance-aware top-k (section 2, "Routage Sensible
+ *          a la Covariance"): key = fl(fl(scale s) + kterm_j) (fp64) with
+ *          kterm = ln M_j (sparse_attn_pool's kcov); the first topk blocks
+ *          by (-key, j).  The key is the log of the bound
+ *          exp(scale q.k_bar_j) |q| M_j on the first-order error a skipped
+ *          block leaves after the global H_bar term, up to the row's |q|.
+ *          cap >= topk.  Needs kterm.
  *   LVSA   idx/cnt = {j : [lo_j, hi_j] meets [lo_a - window, hi_a + window]}
  *          U {((phase + step) mod P) + i P : i < anchors}, P = nb / anchors.
  *          A row longer than cap is truncated to its first cap blocks while
@@ -182,16 +201,18 @@ typedef struct {
  *          (fp64).  The first n_keep blocks by (-e_skip, j) are kept; of
  *          those the first n_refine by (-w, j) go to idx/cnt (refine, exact
  *          bf16, cap >= n_refine) and the rest to idx2/cnt2 (skim, fp8,
- *          cap2 >= n_keep - n_refine).  Needs klam and kcount.
+ *          cap2 >= n_keep - n_refine).  Needs kterm = lambda_j
+ *          (sparse_attn_pool's klam) and kcount.
  *
  * qbar, kbar  fp32 [B,H,nb,d] (sparse_attn_pool outputs)
- * kcount      int32 [nb]      (TRIAGE)   klam fp32 [B,H,nb] (TRIAGE)
+ * kcount      int32 [nb]      (TRIAGE)
+ * kterm       fp32 [B,H,nb]   per-block log term (TRIAGE: lambda_j; TOPK_COV: ln M_j)
  * idx         int32 [B,H,nb,cap]   cnt int32 [B,H,nb]
  * idx2        int32 [B,H,nb,cap2]  cnt2 int32 [B,H,nb]  (TRIAGE)
  */
 sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec,
                             const float* qbar, const float* kbar,
-                            const int32_t* kcount, const float* klam,
+                            const int32_t* kcount, const float* kterm,
                             int32_t* idx, int32_t* cnt, int32_t cap,
                             int32_t* idx2, int32_t* cnt2, int32_t cap2,
                             hipStream_t stream);

@@ -36,10 +36,13 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     q, k, v = dev_qkv
     N = wl.N
     pooled = fbsa.sparse_attn_pool(q, k, v, N, moments=wl.comp == 1, global_moment=wl.comp == 2,
-                                   spreads=wl.rule == "triage", fp8=wl.rule == "triage")
+                                   cov=wl.rule == "topk_cov", spreads=wl.rule == "triage",
+                                   fp8=wl.rule == "triage")
     idx2 = cnt2 = None
     if wl.rule == "topk":
         idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk)
+    elif wl.rule == "topk_cov":
+        idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK_COV, topk=wl.topk, scale=scale)
     elif wl.rule == "lvsa":
         lo, hi = block_frame_ranges(coords)
         cap = fbsa.sparse_attn_lvsa_capacity(lo, hi, wl.window, wl.anchors)
@@ -94,7 +97,7 @@ def kmom_value_major(x):
 
 def oracle_pool(wl, q, k, v):
     return pooling.pool(q, k, v, wl.N, moments=wl.comp == 1, spreads=wl.rule == "triage",
-                        fp8=wl.rule == "triage", hbar=wl.comp == 2)
+                        fp8=wl.rule == "triage", hbar=wl.comp == 2, cov=wl.rule == "topk_cov")
 
 
 def lists_of(idx, cnt, b, h, a):

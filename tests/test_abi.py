@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 3
+    assert lib.sparse_attn_abi_version() == 4
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -47,10 +47,10 @@ MIS = ctypes.c_void_p(4097)
 
 def pool(lib, sh, dtype=1, **kw):
     a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, hbar=None, hbar_ws=None,
-             klam=None, q8=None, k8=None, v8=None, exp8=None)
+             kcov=None, klam=None, q8=None, k8=None, v8=None, exp8=None)
     a.update(kw)
     return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
-                                a["kcount"], a["cent"], a["kmom"], a["hbar"], a["hbar_ws"], a["klam"], a["q8"],
+                                a["kcount"], a["cent"], a["kmom"], a["hbar"], a["hbar_ws"], a["kcov"], a["klam"], a["q8"],
                                 a["k8"], a["v8"], a["exp8"], None)
 
 
@@ -72,6 +72,9 @@ def test_pool_rejects_bad_arguments(lib):
     assert pool(lib, shape(), hbar=P) == 1                   # the mean moment needs its scratch
     assert pool(lib, shape(), hbar_ws=P) == 1
     assert pool(lib, shape(), dtype=0, hbar=P, hbar_ws=P) == 2
+    assert pool(lib, shape(), kcov=P) == 1                   # M_j is taken against H_bar
+    assert b"hbar" in lib.sparse_attn_last_error()
+    assert pool(lib, shape(), dtype=0, kcov=P, hbar=P, hbar_ws=P) == 2
     assert pool(lib, shape(B=0)) == 0                        # empty problem: nothing launched
     assert pool(lib, shape(N=0, N_pad=0)) == 0
 
@@ -97,6 +100,12 @@ def test_route_rejects_bad_arguments(lib):
     assert route(lib, shape(), sp, klam=P, kcount=P, cap=1, cap2=0, cnt2=P) == 1   # cap2 too small
     sp = S(2, 0, None, None, 0, 0, 0, 0, 2, 3, 1.0)
     assert route(lib, shape(), sp, klam=P, kcount=P, cnt2=P, idx2=P, cap2=2) == 1  # n_refine > n_keep
+    sp = S(3, 1, None, None, 0, 0, 0, 0, 0, 0, 1.0)
+    assert route(lib, shape(), sp) == 1                       # covariance top-k without ln M_j
+    assert b"kterm" in lib.sparse_attn_last_error()
+    assert route(lib, shape(), S(3, 0, None, None, 0, 0, 0, 0, 0, 0, 1.0), klam=P) == 1   # topk 0
+    assert route(lib, shape(), S(3, 2, None, None, 0, 0, 0, 0, 0, 0, 1.0), klam=P, cap=1) == 1  # cap < topk
+    assert route(lib, shape(), S(3, 1, None, None, 0, 0, 0, 0, 0, 0, float("inf")), klam=P) == 1
     big = shape(N=64 * 5000, N_pad=64 * 5000, H=1)
     assert route(lib, big, S(0, 4)) == 2                      # beyond the block limit
 

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 3
+    assert fbsa.abi_version() == 4
 
 
 def medium(wid):
@@ -54,6 +54,15 @@ def check_pool(wl, pooled_o, res):
         ref = np.swapaxes(pooled_o["kmom"], -1, -2)               # value-major layout
         err = np.abs(res["kmom"].astype(np.float64) - ref)
         assert np.all(err <= 2.0 ** -8 * np.abs(ref) + 1e-4 * np.abs(ref).max()), err.max()
+    if "kcov" in res and "kcov" in pooled_o:
+        # ln M_j: the block moment rebuilt in fp32 MFMA sums, H_bar subtracted,
+        # power iteration in fp32 (a lower bound that stops at < 2^-22
+        # relative change) against the fp64 singular value
+        ref = pooled_o["kcov"]
+        assert np.array_equal(np.isneginf(res["kcov"]), np.isneginf(ref))
+        fin = np.isfinite(ref)
+        err = np.abs(res["kcov"][fin].astype(np.float64) - ref[fin])
+        assert err.max() <= 1e-3, err.max()
     if "klam" in res:
         np.testing.assert_allclose(res["klam"], pooled_o["klam"], rtol=1e-5, atol=1e-5)
     if "q8" in res:
@@ -69,6 +78,11 @@ def check_route(wl, pooled_o, res, coords, step=0):
             idx, cnt = routing.route_topk(feats["qbar"], feats["kbar"], wl.topk)
             assert np.array_equal(res["idx"], idx)
             assert np.array_equal(res["cnt"], cnt)
+        elif wl.rule == "topk_cov":
+            idx, cnt = routing.route_topk_cov(feats["qbar"], feats["kbar"], feats["kcov"], 1.0, wl.topk)
+            assert np.array_equal(res["idx"], idx)
+            assert np.array_equal(res["cnt"], cnt)
+            break          # ln M_j is not bit-reproducible: stage-wise only
         elif wl.rule == "lvsa":
             lo, hi = block_frame_ranges(coords)
             idx, cnt = routing.route_lvsa(lo, hi, wl.window, wl.anchors,
@@ -209,12 +223,17 @@ def test_topk_all_blocks_matches_dense():
     assert np.abs(lse.cpu().numpy()[:, :, :wl.N] - lsed[:, :, :wl.N]).max() <= gc.LSE_TOL["bf16"]
 
 
+@pytest.mark.parametrize("rule", ["topk", "topk_cov"])
 @pytest.mark.parametrize("size", ["small", "medium"])
-def test_parity_global_first_order(size):
-    """PISA's global first-order term (comp 2) on the HunyuanVideo-like rule."""
-    from workloads.configs import GLOBAL_ORDER1, GLOBAL_ORDER1_SMALL
+def test_parity_global_first_order(size, rule):
+    """PISA's global first-order term (comp 2) on the HunyuanVideo-like layer,
+    routed by plain or covariance-aware top-k."""
+    from workloads.configs import GLOBAL_ORDER1_SMALL, GLOBAL_COV_SMALL
     from dataclasses import replace
-    wl = GLOBAL_ORDER1_SMALL if size == "small" else replace(medium(3), comp=2)
+    if size == "small":
+        wl = GLOBAL_ORDER1_SMALL if rule == "topk" else GLOBAL_COV_SMALL
+    else:
+        wl = replace(medium(3), comp=2, rule=rule)
     print(f"\n[case] {wl.name} size={size} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
     (q, k, v), dev, coords = gc.inputs(wl)
     pooled_o = gc.oracle_pool(wl, q, k, v)
@@ -227,18 +246,19 @@ def test_parity_global_first_order(size):
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
-def test_parity_global_first_order_full_size_sampled():
-    from workloads.configs import GLOBAL_ORDER1
-    wl = GLOBAL_ORDER1
+@pytest.mark.parametrize("rule", ["topk", "topk_cov"])
+def test_parity_global_first_order_full_size_sampled(rule):
+    from workloads.configs import GLOBAL_ORDER1, GLOBAL_COV
+    wl = GLOBAL_ORDER1 if rule == "topk" else GLOBAL_COV
     print(f"\n[case] full {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
     (q, k, v), dev, coords = gc.inputs(wl)
     rng = np.random.default_rng(7)
     heads = sorted(rng.choice(wl.H, 2, replace=False).tolist())
     res = gc.run_gpu(wl, dev, coords)
     qs, ks, vs = (x[:, heads] for x in (q, k, v))
-    pooled_o = pooling.pool(qs, ks, vs, wl.N, hbar=True)
+    pooled_o = pooling.pool(qs, ks, vs, wl.N, hbar=True, cov=rule == "topk_cov")
     rsub = {n: (x[:, heads] if n not in ("kcount",) else x) for n, x in res.items()}
-    check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount", "hbar")})
+    check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount", "hbar", "kcov") if n in rsub})
     check_route(wl, pooled_o, rsub, coords)
     rows = [(0, hi, int(a)) for hi in range(len(heads)) for a in rng.choice(wl.nb, 3, replace=False)]
     rows.append((0, 0, wl.nb - 1))

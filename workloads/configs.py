@@ -25,7 +25,7 @@ class Workload:
     Y: int
     X: int
     dtype: str          # "f32" or "bf16"
-    rule: str           # "topk", "lvsa" or "triage"
+    rule: str           # "topk", "topk_cov", "lvsa" or "triage"
     comp: int           # compensation order of skipped blocks: -1 drop, 0 centroid, 1 block Taylor,
                         # 2 global Taylor (one mean moment per head)
     keep_pct: int = 0           # top-k: percent of key blocks kept per query block
@@ -93,6 +93,10 @@ SMALL = {
 # and shapes as workload 3, so the two first-order forms see the same inputs).
 GLOBAL_ORDER1 = replace(WORKLOADS[3], name="hunyuan720p-global", comp=2)
 GLOBAL_ORDER1_SMALL = replace(SMALL[3], name="hunyuan720p-global-small", comp=2)
+# ... routed by PISA's covariance-aware top-k (attention score and the norm of
+# each block's moment deviation from H_bar) at the same 10% budget.
+GLOBAL_COV = replace(GLOBAL_ORDER1, name="hunyuan720p-global-cov", rule="topk_cov")
+GLOBAL_COV_SMALL = replace(GLOBAL_ORDER1_SMALL, name="hunyuan720p-global-cov-small", rule="topk_cov")
 
 
 def get_workload(wid: int, small: bool = False) -> Workload:
