@@ -17,13 +17,14 @@ import torch
 from . import _lib
 from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER0,
                    SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL, SA_ROUTE_TOPK, SA_ROUTE_LVSA,
-                   SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV)
+                   SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR)
 
 __all__ = [
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
     "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE", "SA_ROUTE_TOPK_COV",
+    "SA_ROUTE_ERROR",
 ]
 
 BLK = 64
@@ -131,11 +132,13 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
                       frame_lo=None, frame_hi=None, window: int = 0, anchors: int = 0,
                       anchor_phase: int = 0, step: int = 0, cap: int = 0,
                       n_keep: int = 0, n_refine: int = 0, scale: float = 1.0,
-                      out=None):
+                      keys=None, ekey=None, out=None):
     """Key-block lists per query block: (idx, cnt, idx2, cnt2); idx2/cnt2 only for Triage.
 
     TOPK_COV reads pooled["kcov"] (sparse_attn_pool(..., cov=True)), Triage
-    pooled["klam"] (spreads=True); both use `scale` in their keys.
+    pooled["klam"] (spreads=True); ERROR reads the bf16 token `keys` and
+    fills the fp32 [B,H,nb,nb] workspace `ekey` (allocated here when None;
+    ekey[b,h,j,a] = L(a, j)).  All three use `scale` in their keys.
 
     `out` may pass preallocated (idx, cnt, idx2, cnt2) tensors.
     """
@@ -148,8 +151,15 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
                           n_keep, n_refine, scale)
     cap2 = 0
     kterm = pooled.get("kcov") if mode == SA_ROUTE_TOPK_COV else pooled.get("klam")
-    if mode in (SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV):
+    if mode in (SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR):
         cap = cap or topk
+    if mode == SA_ROUTE_ERROR:
+        _contig(keys)
+        if ekey is None:
+            ekey = torch.empty(B, H, nb, nb, dtype=torch.float32, device=dev)
+        _contig(ekey)
+        spec.keys = keys.data_ptr()
+        spec.ekey = ekey.data_ptr()
     elif mode == SA_ROUTE_LVSA:
         _contig(frame_lo, frame_hi)
         spec.frame_lo = frame_lo.data_ptr()

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("SPARSE_ATTN_LIB", os.path.join(HERE, "libsparse_attn.
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
 SA_F32, SA_BF16 = 0, 1
 SA_COMP_DROP, SA_COMP_ORDER0, SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL = -1, 0, 1, 2
-SA_ROUTE_TOPK, SA_ROUTE_LVSA, SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV = 0, 1, 2, 3
+SA_ROUTE_TOPK, SA_ROUTE_LVSA, SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR = 0, 1, 2, 3, 4
 
 EXPORTED = (
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
@@ -34,7 +34,7 @@ class RouteSpec(ctypes.Structure):
                 ("window", ctypes.c_int32), ("anchors", ctypes.c_int32),
                 ("anchor_phase", ctypes.c_int32), ("step", ctypes.c_int32),
                 ("n_keep", ctypes.c_int32), ("n_refine", ctypes.c_int32),
-                ("scale", ctypes.c_float)]
+                ("scale", ctypes.c_float), ("keys", ctypes.c_void_p), ("ekey", ctypes.c_void_p)]
 
 
 class SparseAttnError(RuntimeError):

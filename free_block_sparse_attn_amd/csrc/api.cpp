@@ -126,7 +126,7 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
     if (nb > MAX_BLOCKS) return fail(SA_ERR_UNSUPPORTED, "at most %d blocks per sequence, got %d", MAX_BLOCKS, nb);
     if (empty) return ok();
     sa::RouteArgs a{};
-    a.B = shape->B; a.H = shape->H; a.nb = nb; a.d = shape->d; a.mode = spec->mode;
+    a.B = shape->B; a.H = shape->H; a.nb = nb; a.d = shape->d; a.N = shape->N; a.mode = spec->mode;
     a.qbar = qbar; a.kbar = kbar; a.kcount = kcount; a.klam = kterm;
     a.idx = idx; a.cnt = cnt; a.cap = cap; a.idx2 = idx2; a.cnt2 = cnt2; a.cap2 = cap2;
     switch (spec->mode) {
@@ -144,6 +144,15 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
             if (cap < spec->topk) return fail(SA_ERR_INVALID_ARG, "cap %d < topk %d", cap, spec->topk);
             if (!std::isfinite(spec->scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
             a.topk = spec->topk; a.scale = spec->scale;
+            break;
+        case SA_ROUTE_ERROR:
+            NEED(qbar); NEED(kbar); NEED(kcount); NEED(idx); NEED(cnt); NEED(spec->keys); NEED(spec->ekey);
+            if (!empty && (spec->topk < 1 || spec->topk > nb))
+                return fail(SA_ERR_INVALID_ARG, "topk must be in [1, nb=%d], got %d", nb, spec->topk);
+            if (cap < spec->topk) return fail(SA_ERR_INVALID_ARG, "cap %d < topk %d", cap, spec->topk);
+            if (!std::isfinite(spec->scale)) return fail(SA_ERR_INVALID_ARG, "scale must be finite");
+            if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "error-aware routing supports d == 128 only");
+            a.topk = spec->topk; a.scale = spec->scale; a.keys = spec->keys; a.ekey = spec->ekey;
             break;
         case SA_ROUTE_LVSA:
             NEED(spec->frame_lo); NEED(spec->frame_hi); NEED(idx); NEED(cnt);

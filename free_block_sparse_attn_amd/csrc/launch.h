@@ -32,6 +32,7 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s);
 
 struct RouteArgs {
     int B, H, nb, d;
+    int N;                    // valid tokens (error-aware mode)
     int mode;
     int topk;
     const int32_t* frame_lo;
@@ -43,6 +44,8 @@ struct RouteArgs {
     const float* kbar;
     const int32_t* kcount;
     const float* klam;        // per-block log term: lambda_j (Triage) or ln M_j (covariance top-k)
+    const void* keys;         // bf16 [B,H,N_pad,d] token keys (error-aware mode)
+    float* ekey;              // fp32 [B,H,nb(key),nb(query)] error logs (error-aware mode)
     int32_t* idx;
     int32_t* cnt;
     int cap;

@@ -158,7 +158,7 @@ __device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, 
         qs[x] = (row < nb) ? static_cast<double>(a.qbar[(bh * nb + row) * d + i]) : 0.0;
     }
     __syncthreads();
-    const bool triage = a.mode == 2, cov = a.mode == 3;
+    const bool triage = a.mode == 2, cov = a.mode == 3, err = a.mode == 4;
     const double sc = static_cast<double>(a.scale);
     for (int j = tid; j < nb; j += THREADS) {
         double acc[R];
@@ -175,7 +175,16 @@ __device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, 
                 for (int r = 0; r < R; ++r) acc[r] = fma(qs[r * d + 4 * i4 + u], kd[u], acc[r]);
             }
         }
-        if (cov) {
+        if (err) {
+            // ln(E / n_j) = 2 scale s + L - ln n_j; the R error logs of key block j are contiguous
+            const float* el = a.ekey + (bh * nb + j) * static_cast<size_t>(nb) + row0;
+            const double lgn = log(static_cast<double>(a.kcount[j]));
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const double L = (row0 + r < nb) ? static_cast<double>(el[r]) : 0.0;
+                keyE[r * nbp + j] = order_key(__dadd_rn(__dadd_rn(2.0 * __dmul_rn(sc, acc[r]), L), -lgn));
+            }
+        } else if (cov) {
             const double lm = static_cast<double>(a.klam[bh * nb + j]);
 #pragma unroll
             for (int r = 0; r < R; ++r) keyE[r * nbp + j] = order_key(__dadd_rn(__dmul_rn(sc, acc[r]), lm));
@@ -319,6 +328,170 @@ __global__ __launch_bounds__(64 * LVSA_ROWS) void route_lvsa_kernel(RouteArgs a)
         for (int bh = 0; bh < BH; ++bh) a.cnt[static_cast<size_t>(bh) * nb + row] = base;
 }
 
+// SVG-EAR error estimate ("SVG-EAR: Parameter-Free Linear Compensation for
+// Sparse Video Generation via Error-aware Routing", section 2B): for every
+// query-block centroid a (the proxy of its queries) and key block j,
+//   L(a, j) = ln sum_n expm1(delta_n)^2,  delta_n = scale qbar_a . (k_n - kbar_j),
+// the log of the squared error of the proxy's attention weights when the
+// block's keys are replaced by their centroid, without the factor e^{2c}
+// (c = scale qbar_a . kbar_j) that the selection adds from the fp64 score.
+// Streaming: a workgroup holds 64 centroids and walks ERR_CHUNK key blocks;
+// the logits never leave the chip.  Each key block is centred in fp32 and
+// staged in LDS as bf16 high + low parts, the centroids sit in registers as
+// high + low MFMA operands, and delta = (kc_hi + kc_lo) . (q_hi + q_lo) less
+// the lo.lo term (three MFMA passes, about 16 bits per factor).  Wave w takes
+// key half w / 2 and centroid half w % 2 of the 64 x 64 tile.  Sums use a
+// per-lane max shift, sum expm1(delta)^2 = e^{2m} sum (expm1(delta) e^{-m})^2,
+// so no term overflows.
+constexpr int ERR_CHUNK = 64;          // key blocks per workgroup
+constexpr int ERR_PITCH = 128 + 8;     // staged key row pitch (bf16), 16-byte multiple
+
+__device__ __forceinline__ void lse2_combine(float& m, float& s, float mo, float so) {
+    // (m, s) represents e^{2m} s
+    const float mn = fmaxf(m, mo);
+    s = s * __expf(2.0f * (m - mn)) + so * __expf(2.0f * (mo - mn));
+    m = mn;
+}
+
+__global__ __launch_bounds__(THREADS) void route_err_kernel(RouteArgs a) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) uint16_t khi[BLK * ERR_PITCH], klo[BLK * ERR_PITCH];
+    __shared__ float xch[2][2][2][32];    // [parity][centroid half][m, s][lane]
+    const int nb = a.nb;
+    const int nct = (nb + BLK - 1) / BLK;
+    const int ct = blockIdx.x % nct, ch = blockIdx.x / nct;
+    const size_t bh = static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int kw = w >> 1, cw = w & 1;
+    const int j0 = ch * ERR_CHUNK, j1 = min(nb, j0 + ERR_CHUNK);
+    const float sc = a.scale;
+    // centroid operands: B[k = d][n = centroid], lane holds d = 16 ks + 8 hl .. + 7 of centroid l32
+    bf16x8 qh[8], ql[8];
+    {
+        const int c = BLK * ct + 32 * cw + l32;
+        const float* qr = a.qbar + (bh * nb + min(c, nb - 1)) * D;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const f32x4 x0 = *reinterpret_cast<const f32x4*>(qr + 16 * ks + 8 * hl);
+            const f32x4 x1 = *reinterpret_cast<const f32x4*>(qr + 16 * ks + 8 * hl + 4);
+            const float x[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float v = c < nb ? x[e] : 0.0f;
+                const __bf16 h = static_cast<__bf16>(v);
+                qh[ks][e] = h;
+                ql[ks][e] = static_cast<__bf16>(v - static_cast<float>(h));
+            }
+        }
+    }
+    // staging: chunk p of thread t covers key row (t + 256 p) / 16, columns 8 ((t + 256 p) % 16) .. + 7
+    const uint16_t* K = static_cast<const uint16_t*>(a.keys) + bh * static_cast<size_t>(nb) * BLK * D;
+    u32x4 kreg[4];
+    auto load_block = [&](int j) __attribute__((always_inline)) {
+        const int n = min(BLK, a.N - BLK * j);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int chunk = tid + THREADS * p, row = chunk >> 4, col0 = (chunk & 15) * 8;
+            u32x4 z = {0u, 0u, 0u, 0u};
+            if (row < n) z = *reinterpret_cast<const u32x4*>(K + (static_cast<size_t>(j) * BLK + row) * D + col0);
+            kreg[p] = z;
+        }
+    };
+    auto stage_block = [&](int j) __attribute__((always_inline)) {
+        const int n = min(BLK, a.N - BLK * j);
+        const float* kb = a.kbar + (bh * nb + j) * D;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int chunk = tid + THREADS * p, row = chunk >> 4, col0 = (chunk & 15) * 8;
+            const f32x4 m0 = *reinterpret_cast<const f32x4*>(kb + col0);
+            const f32x4 m1 = *reinterpret_cast<const f32x4*>(kb + col0 + 4);
+            const float mb[8] = {m0[0], m0[1], m0[2], m0[3], m1[0], m1[1], m1[2], m1[3]};
+            u32x4 hi, lo;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+                float c[2];
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const int e = 2 * e2 + t;
+                    const uint32_t wd = kreg[p][e2];
+                    const float kv = __uint_as_float(t ? (wd & 0xFFFF0000u) : (wd << 16));
+                    c[t] = row < n ? kv - mb[e] : 0.0f;           // pad keys contribute delta = 0
+                }
+                hi[e2] = pack_bf16x2(c[0], c[1]);
+                lo[e2] = pack_bf16x2(c[0] - bf16_to_f32(static_cast<uint16_t>(hi[e2] & 0xFFFFu)),
+                                     c[1] - bf16_to_f32(static_cast<uint16_t>(hi[e2] >> 16)));
+            }
+            *reinterpret_cast<u32x4*>(khi + row * ERR_PITCH + col0) = hi;
+            *reinterpret_cast<u32x4*>(klo + row * ERR_PITCH + col0) = lo;
+        }
+    };
+    float pm = 0.0f, ps = 0.0f;             // wave kw = 0: this lane's (m, s) of the previous block
+    auto finish = [&](int j, int par) __attribute__((always_inline)) {
+        // wave kw = 0, lanes 0..31: combine with the other key half, write L(a, j)
+        if (kw == 0 && hl == 0) {
+            float m = pm, s = ps;
+            lse2_combine(m, s, xch[par][cw][0][l32], xch[par][cw][1][l32]);
+            const int c = BLK * ct + 32 * cw + l32;
+            if (c < nb) a.ekey[(bh * nb + j) * static_cast<size_t>(nb) + c] = s > 0.0f ? 2.0f * m + __logf(s) : -INFINITY;
+        }
+    };
+    if (j0 < j1) load_block(j0);
+    for (int j = j0; j < j1; ++j) {
+        __syncthreads();                      // the previous block's operands are read; xch of j - 1 visible
+        if (j > j0) finish(j - 1, (j - 1) & 1);
+        stage_block(j);
+        if (j + 1 < j1) load_block(j + 1);
+        __syncthreads();
+        f32x16 acc = f32x16{};
+        const uint16_t* ah = khi + (32 * kw + l32) * ERR_PITCH + 8 * hl;
+        const uint16_t* al = klo + (32 * kw + l32) * ERR_PITCH + 8 * hl;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const bf16x8 xh = *reinterpret_cast<const bf16x8*>(ah + 16 * ks);
+            const bf16x8 xl = *reinterpret_cast<const bf16x8*>(al + 16 * ks);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, qh[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xh, ql[ks], acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(xl, qh[ks], acc, 0, 0, 0);
+        }
+        // this lane: 16 keys of the half for centroid l32
+        float dl[16];
+        float m = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            dl[r] = sc * acc[r];
+            m = fmaxf(m, dl[r]);
+        }
+        // t = expm1(delta) e^{-m}: expm1 keeps small deviations exact when m
+        // is small; for m > 1 the form e^{delta - m} - e^{-m} cannot overflow
+        const float em = __expf(-m);
+        const bool big = m > 1.0f;
+        float s = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const float t = big ? __expf(dl[r] - m) - em : expm1f(dl[r]) * em;
+            s = fmaf(t, t, s);
+        }
+        // the other 16 keys of the half sit in lane l ^ 32
+        {
+            const auto pmv = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+            const auto psv = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+            const float mo = __uint_as_float(hl ? static_cast<uint32_t>(pmv[0]) : static_cast<uint32_t>(pmv[1]));
+            const float so = __uint_as_float(hl ? static_cast<uint32_t>(psv[0]) : static_cast<uint32_t>(psv[1]));
+            lse2_combine(m, s, mo, so);
+        }
+        if (kw == 1 && hl == 0) {
+            xch[j & 1][cw][0][l32] = m;
+            xch[j & 1][cw][1][l32] = s;
+        }
+        pm = m;
+        ps = s;
+    }
+    if (j0 < j1) {
+        __syncthreads();
+        finish(j1 - 1, (j1 - 1) & 1);
+    }
+}
+
 template <int R>
 hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
     const int nbp = (a.nb + 63) & ~63;
@@ -332,6 +505,11 @@ hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
+    if (a.mode == 4) {
+        const int nct = (a.nb + BLK - 1) / BLK, nch = (a.nb + ERR_CHUNK - 1) / ERR_CHUNK;
+        hipLaunchKernelGGL(route_err_kernel, dim3(nct * nch, a.H, a.B), dim3(THREADS), 0, s, a);
+        if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    }
     if (a.mode == 1) {
         dim3 grid((a.nb + LVSA_ROWS - 1) / LVSA_ROWS);
         hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64 * LVSA_ROWS), 0, s, a);

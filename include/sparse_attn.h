@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 4
+#define SPARSE_ATTN_ABI_VERSION 5
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -79,7 +79,8 @@ typedef enum {
     SA_ROUTE_TOPK = 0,
     SA_ROUTE_LVSA = 1,
     SA_ROUTE_TRIAGE = 2,
-    SA_ROUTE_TOPK_COV = 3
+    SA_ROUTE_TOPK_COV = 3,
+    SA_ROUTE_ERROR = 4
 } sa_route_mode;
 
 /* Problem shape.  d must be 64 or 128. */
@@ -159,8 +160,8 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
 /* Routing request.  Unused fields are ignored by the other modes. */
 typedef struct {
     int32_t mode;                 /* sa_route_mode */
-    /* SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV: keep `topk` (1..nb) key blocks per
-       query block. */
+    /* SA_ROUTE_TOPK, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR: keep `topk` (1..nb)
+       key blocks per query block. */
     int32_t topk;
     /* SA_ROUTE_LVSA: device int32 [nb] first/last latent frame of each block. */
     const int32_t* frame_lo;
@@ -172,13 +173,17 @@ typedef struct {
     /* SA_ROUTE_TRIAGE: tiers per query block. */
     int32_t n_keep;               /* refine + skim blocks (1..nb) */
     int32_t n_refine;             /* refine blocks (0..n_keep) */
-    float scale;                  /* softmax scale in the keys (TRIAGE, TOPK_COV) */
+    float scale;                  /* softmax scale in the keys (TRIAGE, TOPK_COV, ERROR) */
+    /* SA_ROUTE_ERROR */
+    const void* keys;             /* device bf16 [B,H,N_pad,d] token keys (d == 128) */
+    float* ekey;                  /* device fp32 [B,H,nb,nb] caller workspace; on return
+                                     ekey[b,h,j,a] = L(a, j) (key block j, query block a) */
 } sa_route_spec;
 
 /*
  * sparse_attn_route - choose the key blocks of every query block.
  *
- * Scores (TOPK, TOPK_COV, TRIAGE): s(a, j) = sum_i qbar[a,i] * kbar[j,i], fp64,
+ * Scores (TOPK, TOPK_COV, TRIAGE, ERROR): s(a, j) = sum_i qbar[a,i] * kbar[j,i], fp64,
  * accumulated in i = 0..d-1 order (products of fp32 values are exact in
  * fp64).  Selections use the total order (-key, j): ties go to the lower
  * block index.  Lists are written ascending, padded with -1 up to `cap`.
@@ -192,6 +197,19 @@ typedef struct {
  *          exp(scale q.k_bar_j) |q| M_j on the first-order error a skipped
  *          block leaves after the global H_bar term, up to the row's |q|.
  *          cap >= topk.  Needs kterm.
+ *   ERROR  SVG-EAR error-aware routing ("SVG-EAR: Parameter-Free Linear
+ *          Compensation for Sparse Video Generation via Error-aware Routing",
+ *          section 2B).  With the query-block centroid qbar_a as the proxy
+ *          of its queries, E(a, j) = sum_n (e^{scale qbar_a.k_n} -
+ *          e^{scale qbar_a.kbar_j})^2 is the squared error of its attention
+ *          weights when block j's keys are replaced by their centroid.  A
+ *          streaming pass over all keys writes L(a, j) = ln sum_n
+ *          expm1(scale qbar_a.(k_n - kbar_j))^2 to ekey (fp32; the product
+ *          is formed from bf16 high + low parts of both factors, three MFMA
+ *          passes, fp32 sums); then key = fl(fl(2 fl(scale s) + L) - ln n_j)
+ *          = ln(E / n_j) (fp64) and the first topk blocks by (-key, j) are
+ *          kept: the greedy error-to-cost choice with one tile per block.
+ *          cap >= topk.  Needs kcount, spec->keys, spec->ekey; d == 128.
  *   LVSA   idx/cnt = {j : [lo_j, hi_j] meets [lo_a - window, hi_a + window]}
  *          U {((phase + step) mod P) + i P : i < anchors}, P = nb / anchors.
  *          A row longer than cap is truncated to its first cap blocks while
@@ -205,7 +223,7 @@ typedef struct {
  *          (sparse_attn_pool's klam) and kcount.
  *
  * qbar, kbar  fp32 [B,H,nb,d] (sparse_attn_pool outputs)
- * kcount      int32 [nb]      (TRIAGE)
+ * kcount      int32 [nb]      (TRIAGE, ERROR)
  * kterm       fp32 [B,H,nb]   per-block log term (TRIAGE: lambda_j; TOPK_COV: ln M_j)
  * idx         int32 [B,H,nb,cap]   cnt int32 [B,H,nb]
  * idx2        int32 [B,H,nb,cap2]  cnt2 int32 [B,H,nb]  (TRIAGE)

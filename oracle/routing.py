@@ -92,6 +92,66 @@ def route_topk_cov(qbar: np.ndarray, kbar: np.ndarray, kcov: np.ndarray, scale: 
     return idx, cnt
 
 
+def error_logs(qbar: np.ndarray, k: np.ndarray, kbar: np.ndarray, N: int, scale: float,
+               blk: int = 64) -> np.ndarray:
+    """SVG-EAR's per-block approximation error ("SVG-EAR ...", section 2B,
+    error estimation with query centroids as proxies), as a log.
+
+    For query-block centroid q_a and key block j (valid keys k_n, centroid
+    k_bar_j), the proxy query's attention weights to the block are
+    e^{x_n}, x_n = scale q_a.k_n; replacing the keys by their centroid gives
+    e^{c} to each, c = scale q_a.k_bar_j.  The squared error of the weights is
+      E(a, j) = sum_n (e^{x_n} - e^{c})^2 = e^{2c} sum_n expm1(delta_n)^2,
+      delta_n = scale q_a.(k_n - k_bar_j).
+    Returns L(a, j) = ln sum_n expm1(delta_n)^2 (the factor e^{2c} is added by
+    the router, from the pooled score), fp64 [B,H,nq,nb]; -inf where every
+    delta is 0 (e.g. one-token blocks).  qbar, kbar: the pooled fp32 means;
+    k: the input token keys [B,H,N_pad,d].
+    """
+    B, H, nq, d = qbar.shape
+    nb = kbar.shape[2]
+    sc = np.float64(np.float32(scale))
+    out = np.empty((B, H, nq, nb), np.float64)
+    for b in range(B):
+        for h in range(H):
+            qa = np.asarray(qbar[b, h], np.float32).astype(np.float64)
+            for j in range(nb):
+                n = min(blk, N - blk * j)
+                kc = np.asarray(k[b, h, blk * j: blk * j + n], np.float64) - \
+                    np.asarray(kbar[b, h, j], np.float32).astype(np.float64)[None, :]
+                delta = sc * (qa @ kc.T)                                  # [nq, n]
+                with np.errstate(divide="ignore"):
+                    out[b, h, :, j] = np.log(np.sum(np.expm1(delta) ** 2, axis=1))
+    return out
+
+
+def route_error(qbar: np.ndarray, kbar: np.ndarray, kcount: np.ndarray, elog: np.ndarray,
+                scale: float, k: int):
+    """SVG-EAR error-aware routing ("SVG-EAR ...", section 2B): under the
+    block budget, greedily take the blocks with the largest error-to-cost
+    ratio E(a, j) / n_j (error normalised by the block's size).  With every
+    block costing one tile, the greedy choice is the first k in the order
+    (-key, j) of
+      key(a, j) = fl(fl(2 fl(scale s(a, j)) + L(a, j)) - ln n_j)     (fp64)
+    = ln(E / n_j), where L = error_logs(...) (given as fp32, the router's input).
+    elog: [B,H,nq,nb].  Returns (idx int32 [B,H,nq,k], cnt).
+    """
+    B, H, nq, _ = qbar.shape
+    nk = kbar.shape[2]
+    kk = min(k, nk)
+    sc = np.float64(np.float32(scale))
+    logn = np.log(np.asarray(kcount, np.float64))
+    idx = np.full((B, H, nq, kk), -1, np.int32)
+    cnt = np.full((B, H, nq), kk, np.int32)
+    for b in range(B):
+        for h in range(H):
+            ss = sc * block_scores(qbar[b, h], kbar[b, h])
+            key = (2.0 * ss + np.asarray(elog[b, h], np.float32).astype(np.float64)) - logn[None, :]
+            for a in range(nq):
+                idx[b, h, a] = _select_first(key[a], kk)
+    return idx, cnt
+
+
 def lvsa_anchor_set(nb: int, anchors: int, phase: int, step: int) -> np.ndarray:
     """Rotating global anchor key blocks G_s at denoising step s.
 

@@ -43,6 +43,12 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
         idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk)
     elif wl.rule == "topk_cov":
         idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK_COV, topk=wl.topk, scale=scale)
+    elif wl.rule == "error":
+        B, H = q.shape[:2]
+        ekey = torch.empty(B, H, wl.nb, wl.nb, dtype=torch.float32, device=q.device)
+        idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_ERROR, topk=wl.topk, scale=scale,
+                                                keys=k, ekey=ekey)
+        pooled = dict(pooled, ekey=ekey)
     elif wl.rule == "lvsa":
         lo, hi = block_frame_ranges(coords)
         cap = fbsa.sparse_attn_lvsa_capacity(lo, hi, wl.window, wl.anchors)

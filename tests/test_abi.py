@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 4
+    assert lib.sparse_attn_abi_version() == 5
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -106,6 +106,16 @@ def test_route_rejects_bad_arguments(lib):
     assert route(lib, shape(), S(3, 0, None, None, 0, 0, 0, 0, 0, 0, 1.0), klam=P) == 1   # topk 0
     assert route(lib, shape(), S(3, 2, None, None, 0, 0, 0, 0, 0, 0, 1.0), klam=P, cap=1) == 1  # cap < topk
     assert route(lib, shape(), S(3, 1, None, None, 0, 0, 0, 0, 0, 0, float("inf")), klam=P) == 1
+    sp = S(4, 1, None, None, 0, 0, 0, 0, 0, 0, 1.0, None, P)
+    assert route(lib, shape(), sp, kcount=P) == 1              # error-aware routing without keys
+    assert b"keys" in lib.sparse_attn_last_error()
+    sp = S(4, 1, None, None, 0, 0, 0, 0, 0, 0, 1.0, P, None)
+    assert route(lib, shape(), sp, kcount=P) == 1              # ... without its workspace
+    sp = S(4, 1, None, None, 0, 0, 0, 0, 0, 0, 1.0, P, P)
+    assert route(lib, shape(), sp) == 1                        # ... without kcount
+    assert route(lib, shape(d=64), sp, kcount=P) == 2          # d == 128 only
+    sp = S(4, 3, None, None, 0, 0, 0, 0, 0, 0, 1.0, P, P)
+    assert route(lib, shape(), sp, kcount=P) == 1              # topk > nb
     big = shape(N=64 * 5000, N_pad=64 * 5000, H=1)
     assert route(lib, big, S(0, 4)) == 2                      # beyond the block limit
 

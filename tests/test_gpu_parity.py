@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 4
+    assert fbsa.abi_version() == 5
 
 
 def medium(wid):
@@ -78,6 +78,14 @@ def check_route(wl, pooled_o, res, coords, step=0):
             idx, cnt = routing.route_topk(feats["qbar"], feats["kbar"], wl.topk)
             assert np.array_equal(res["idx"], idx)
             assert np.array_equal(res["cnt"], cnt)
+        elif wl.rule == "error":
+            # GPU error logs L(a, j) (stored key-block-major) against the fp64
+            # definition; selection bit-exact on the GPU's logs
+            elog = np.swapaxes(res["ekey"], -1, -2)
+            idx, cnt = routing.route_error(res["qbar"], res["kbar"], res["kcount"], elog, 1.0, wl.topk)
+            assert np.array_equal(res["idx"], idx)
+            assert np.array_equal(res["cnt"], cnt)
+            break          # the logs are not bit-reproducible: stage-wise only
         elif wl.rule == "topk_cov":
             idx, cnt = routing.route_topk_cov(feats["qbar"], feats["kbar"], feats["kcov"], 1.0, wl.topk)
             assert np.array_equal(res["idx"], idx)
@@ -102,6 +110,21 @@ def check_route(wl, pooled_o, res, coords, step=0):
             assert np.array_equal(res["idx2"], si)
             assert np.array_equal(res["cnt2"], sc)
             break          # klam is not bit-reproducible: stage-wise only
+
+
+ELOG_TOL = 1e-3   # |L_gpu - L| : three bf16 hi/lo MFMA passes (~16 bits per factor), fp32 sums
+
+
+def check_error_logs(wl, res, elog, k, rows=None):
+    """L(a, j) of the query blocks `rows` (all when None) against the oracle's fp64 value."""
+    sel = np.arange(wl.nb) if rows is None else np.asarray(rows)
+    ref = routing.error_logs(res["qbar"][:, :, sel], k, res["kbar"], wl.N, 1.0)
+    got = elog[:, :, sel]
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref)
+    err = np.abs(got[fin].astype(np.float64) - ref[fin])
+    assert err.max() <= ELOG_TOL, err.max()
+    return err.max()
 
 
 def check_out(wl, res, ref, rows):
@@ -265,3 +288,43 @@ def test_parity_global_first_order_full_size_sampled(rule):
     ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
     worst = check_out(wl, rsub, ref, rows)
     print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("size", ["small", "medium"])
+def test_parity_error_routed(size):
+    """SVG-EAR error-aware routing on the Wan-like layer, centroid compensation."""
+    from dataclasses import replace
+    from workloads.configs import ERROR_ROUTED_SMALL
+    wl = ERROR_ROUTED_SMALL if size == "small" else replace(medium(2), rule="error")
+    print(f"\n[case] {wl.name} size={size} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords)
+    lerr = check_error_logs(wl, res, np.swapaxes(res["ekey"], -1, -2), k)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    print(f"[ok] max|dL|={lerr:.2e} max|err|={worst:.3e}", flush=True)
+
+
+def test_parity_error_routed_full_size_sampled():
+    from workloads.configs import ERROR_ROUTED
+    wl = ERROR_ROUTED
+    print(f"\n[case] full {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    rng = np.random.default_rng(8)
+    heads = sorted(rng.choice(wl.H, 2, replace=False).tolist())
+    res = gc.run_gpu(wl, dev, coords)
+    qs, ks, vs = (x[:, heads] for x in (q, k, v))
+    pooled_o = pooling.pool(qs, ks, vs, wl.N)
+    rsub = {n: (x[:, heads] if n not in ("kcount",) else x) for n, x in res.items()}
+    check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount")})
+    check_route(wl, pooled_o, rsub, coords)
+    sample = sorted(rng.choice(wl.nb, 6, replace=False).tolist()) + [wl.nb - 1]
+    lerr = check_error_logs(wl, rsub, np.swapaxes(rsub["ekey"], -1, -2), ks, rows=sample)
+    rows = [(0, hi, int(a)) for hi in range(len(heads)) for a in sample[:3]] + [(0, 0, wl.nb - 1)]
+    ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
+    worst = check_out(wl, rsub, ref, rows)
+    print(f"[ok] max|dL|={lerr:.2e} max|err|={worst:.3e}", flush=True)

@@ -2,6 +2,7 @@
 LVSA rotation and window invariants, Triage tier structure."""
 
 import itertools
+import math
 
 import numpy as np
 import pytest
@@ -103,6 +104,84 @@ def test_topk_cov_zero_queries_rank_by_norm():
     for k, want in ((3, [0, 2, 6]), (5, [0, 2, 3, 4, 6]), (6, [0, 1, 2, 3, 4, 6])):
         idx, _ = routing.route_topk_cov(q, kb, kcov, 1.0, k)
         assert list(idx[0, 0, 0]) == want and list(idx[0, 0, 1]) == want
+
+
+def brute_error(q, kb_tokens, kbar_j, scale):
+    """E = sum_n (exp(scale q.k_n) - exp(scale q.kbar_j))^2 straight from the definition."""
+    c = math.exp(scale * sum(float(a) * float(b) for a, b in zip(q, kbar_j)))
+    return sum((math.exp(scale * sum(float(a) * float(b) for a, b in zip(q, kn))) - c) ** 2 for kn in kb_tokens)
+
+
+def test_error_logs_brute_force():
+    rng = np.random.default_rng(120)
+    blk, d, N = 4, 3, 11                      # blocks of 4, 4, 3 tokens
+    k = rng.standard_normal((1, 2, 12, d)).astype(np.float32)
+    q = rng.standard_normal((1, 2, 3, d)).astype(np.float32)
+    kbar = np.stack([k[:, :, 4 * j:min(N, 4 * j + 4)].mean(axis=2) for j in range(3)], axis=2).astype(np.float32)
+    for scale in (1.0, 0.7):
+        L = routing.error_logs(q, k, kbar, N, scale, blk)
+        for h in range(2):
+            for a in range(3):
+                for j in range(3):
+                    toks = k[0, h, 4 * j:min(N, 4 * j + 4)]
+                    E = brute_error(q[0, h, a], toks, kbar[0, h, j], float(np.float32(scale)))
+                    c = float(np.float32(scale)) * sum(float(x) * float(y) for x, y in zip(q[0, h, a], kbar[0, h, j]))
+                    assert abs(L[0, h, a, j] + 2 * c - math.log(E)) < 1e-9
+
+
+def test_error_logs_two_token_closed_form():
+    # keys kbar +- u: delta = +-t with t = q.u, and
+    # expm1(t)^2 + expm1(-t)^2 = 2 cosh(2t) - 4 cosh(t) + 2
+    q = np.array([[[[0.5, -1.0, 2.0]]]], np.float32)
+    u = np.array([0.25, 0.5, -0.125], np.float32)
+    base = np.array([1.0, 2.0, -1.0], np.float32)
+    k = np.stack([base + u, base - u])[None, None].astype(np.float32)
+    L = routing.error_logs(q, k, base[None, None, None, :], 2, 1.0, 2)
+    t = float(q[0, 0, 0] @ u)
+    assert abs(L[0, 0, 0, 0] - math.log(2 * math.cosh(2 * t) - 4 * math.cosh(t) + 2)) < 1e-12
+
+
+def test_error_logs_degenerate_blocks_are_minus_inf():
+    rng = np.random.default_rng(121)
+    k = rng.standard_normal((1, 1, 8, 4)).astype(np.float32)
+    k[0, 0, 4:8] = k[0, 0, 4]                 # block 1: four identical keys
+    N = 8
+    kbar = np.stack([k[:, :, 0:4].mean(axis=2), k[:, :, 4:5].mean(axis=2)], axis=2).astype(np.float32)
+    q = rng.standard_normal((1, 1, 2, 4)).astype(np.float32)
+    L = routing.error_logs(q, k, kbar, N, 1.0, 4)
+    assert np.all(np.isfinite(L[..., 0])) and np.all(np.isneginf(L[..., 1]))
+    # a one-token tail block
+    L1 = routing.error_logs(q, k[:, :, :5], kbar, 5, 1.0, 4)
+    assert np.all(np.isneginf(L1[..., 1]))
+
+
+def test_route_error_follows_the_error_to_size_ratio():
+    # brute-force E / n_j from the definition, then the first k by (-ratio, j)
+    rng = np.random.default_rng(122)
+    blk, d, N, nb = 4, 3, 22, 6                # last block holds 2 tokens
+    for trial in range(4):
+        k = rng.standard_normal((1, 1, nb * blk, d)).astype(np.float32)
+        q = rng.standard_normal((1, 1, nb, d)).astype(np.float32)
+        n = np.array([min(blk, N - blk * j) for j in range(nb)], np.int32)
+        kbar = np.stack([k[:, :, blk * j:blk * j + n[j]].mean(axis=2) for j in range(nb)], axis=2).astype(np.float32)
+        L = routing.error_logs(q, k, kbar, N, 1.0, blk)
+        for kk in (1, 3, 5):
+            idx, cnt = routing.route_error(q, kbar, n, L.astype(np.float32), 1.0, kk)
+            for a in range(nb):
+                ratio = [brute_error(q[0, 0, a], k[0, 0, blk * j:blk * j + n[j]], kbar[0, 0, j], 1.0) / n[j]
+                         for j in range(nb)]
+                want = sorted(sorted(range(nb), key=lambda j: (-ratio[j], j))[:kk])
+                assert list(idx[0, 0, a]) == want and cnt[0, 0, a] == kk
+
+
+def test_route_error_equal_logs_is_topk():
+    rng = np.random.default_rng(123)
+    q = rng.standard_normal((1, 2, 10, 8)).astype(np.float32)
+    kb = rng.standard_normal((1, 2, 10, 8)).astype(np.float32)
+    L = np.full((1, 2, 10, 10), -3.5, np.float32)
+    a, _ = routing.route_error(q, kb, np.full(10, 64, np.int32), L, 1.0, 4)
+    b, _ = routing.route_topk(q, kb, 4)
+    assert np.array_equal(a, b)
 
 
 def test_lvsa_anchor_rotation_covers_each_block_once():

@@ -25,7 +25,7 @@ class Workload:
     Y: int
     X: int
     dtype: str          # "f32" or "bf16"
-    rule: str           # "topk", "topk_cov", "lvsa" or "triage"
+    rule: str           # "topk", "topk_cov", "error", "lvsa" or "triage"
     comp: int           # compensation order of skipped blocks: -1 drop, 0 centroid, 1 block Taylor,
                         # 2 global Taylor (one mean moment per head)
     keep_pct: int = 0           # top-k: percent of key blocks kept per query block
@@ -97,6 +97,11 @@ GLOBAL_ORDER1_SMALL = replace(SMALL[3], name="hunyuan720p-global-small", comp=2)
 # each block's moment deviation from H_bar) at the same 10% budget.
 GLOBAL_COV = replace(GLOBAL_ORDER1, name="hunyuan720p-global-cov", rule="topk_cov")
 GLOBAL_COV_SMALL = replace(GLOBAL_ORDER1_SMALL, name="hunyuan720p-global-cov-small", rule="topk_cov")
+
+# The Wan-1.3B-like layer routed by SVG-EAR's error-aware rule at the same
+# 20% block budget, centroid compensation of the rest.
+ERROR_ROUTED = replace(WORKLOADS[2], name="wan13b-ear", rule="error")
+ERROR_ROUTED_SMALL = replace(SMALL[2], name="wan13b-ear-small", rule="error")
 
 
 def get_workload(wid: int, small: bool = False) -> Workload:
