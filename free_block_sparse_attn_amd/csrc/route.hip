@@ -5,8 +5,8 @@
 // in i order (the fp32 x fp32 products are exact in fp64, so the fusion does
 // not change a bit).  A selection takes the first k elements of the total
 // order (-key, j): keys are mapped to order-preserving 64-bit integers and a
-// wave runs an 8-pass MSB radix select (256-bin LDS histogram per pass) to find
-// the k-th key; ties at that key go to the lowest block indices.  Lists are
+// wave finds the k-th key bit by bit with ballots over keys held in registers;
+// ties at that key go to the lowest block indices.  Lists are
 // written ascending by ballot compaction.
 //
 // Page basis: PISA's top-k critical set per query block ("PISA: Piecewise
@@ -43,8 +43,6 @@ struct Threshold {
     int need;         // how many elements equal to `key` are taken (lowest j first)
 };
 
-// k-th largest key among candidates (key != 0 when `cand_nonzero`), k >= 1,
-// k <= number of candidates.  One wave; `hist` is 256 words of wave-private LDS.
 __device__ __forceinline__ uint64_t wave_and64(uint64_t x) {
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) x &= static_cast<uint64_t>(__shfl_xor(static_cast<long long>(x), off));
@@ -56,10 +54,48 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
     return x;
 }
 
-__device__ Threshold radix_select(const uint64_t* keys, int nb, int k, uint32_t* hist, bool cand_nonzero) {
+// k-th largest key among candidates (key != 0 when `cand_nonzero`), k >= 1,
+// k <= number of candidates.  One wave; lane l holds keys l + 64 t (t < KPL)
+// in registers.  The threshold is found bit by bit from the highest bit in
+// which the candidates differ: bit b is set when at least k keys are >= the
+// threshold with it set (one 64-bit compare and one ballot per key and bit,
+// no LDS traffic).  Real keys are never 0 (order_key of a non-NaN value), so
+// 0 marks missing entries.
+template <int KPL>
+__device__ Threshold threshold_select(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
     const int lane = lane_id();
-    // Leading bytes shared by every candidate are fixed without a pass (their
-    // histogram would put every key in one bin: a 64-way LDS atomic conflict).
+    uint64_t kr[KPL];
+    uint64_t kand = ~0ull, kor = 0ull;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) {
+        const int j = lane + 64 * t;
+        uint64_t key = j < nb ? keys[j] : 0ull;
+        if (!cand_nonzero && j < nb) { kand &= key; kor |= key; }
+        if (cand_nonzero && key != 0ull) { kand &= key; kor |= key; }
+        kr[t] = key;
+    }
+    kand = wave_and64(kand);
+    kor = wave_or64(kor);
+    const uint64_t diff = kand ^ kor;                 // bits in which candidates differ
+    const int top = diff ? 63 - __builtin_clzll(diff) : -1;
+    // the bits above `top` are common to every candidate; lower bits start at 0
+    uint64_t T = top < 0 ? kand : (top == 63 ? 0ull : (kand & ~((2ull << top) - 1ull)));
+    for (int b = top; b >= 0; --b) {
+        const uint64_t cand = T | (1ull << b);
+        int c = 0;
+#pragma unroll
+        for (int t = 0; t < KPL; ++t) c += __popcll(__ballot(kr[t] >= cand));
+        if (c >= k) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) gt += __popcll(__ballot(kr[t] > T));
+    return Threshold{T, k - gt};
+}
+
+// The same search for long rows, reading the keys from LDS at every bit.
+__device__ Threshold threshold_select_lds(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
+    const int lane = lane_id();
     uint64_t kand = ~0ull, kor = 0ull;
     for (int j = lane; j < nb; j += 64) {
         const uint64_t key = keys[j];
@@ -67,58 +103,34 @@ __device__ Threshold radix_select(const uint64_t* keys, int nb, int k, uint32_t*
     }
     kand = wave_and64(kand);
     kor = wave_or64(kor);
-    const uint64_t diff = kand ^ kor;            // bits that differ between candidates
-    int start = 56;
-    uint64_t prefix = 0, pmask = 0;
-    while (start > 0 && ((diff >> start) & 0xFFull) == 0ull) {
-        pmask |= 0xFFull << start;
-        prefix |= kand & (0xFFull << start);
-        start -= 8;
+    const uint64_t diff = kand ^ kor;
+    const int top = diff ? 63 - __builtin_clzll(diff) : -1;
+    uint64_t T = top < 0 ? kand : (top == 63 ? 0ull : (kand & ~((2ull << top) - 1ull)));
+    for (int b = top; b >= 0; --b) {
+        const uint64_t cand = T | (1ull << b);
+        int c = 0;
+        for (int j0 = 0; j0 < nb; j0 += 64) {
+            const int j = j0 + lane;
+            c += __popcll(__ballot(j < nb && keys[j] >= cand));
+        }
+        if (c >= k) T = cand;
     }
-    int kk = k;
-    for (int shift = start; shift >= 0; shift -= 8) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) hist[4 * lane + q] = 0u;
-        wave_sync();
-        for (int j = lane; j < nb; j += 64) {
-            const uint64_t key = keys[j];
-            const bool cand = !cand_nonzero || key != 0ull;
-            if (cand && (key & pmask) == prefix)
-                atomicAdd(&hist[(key >> shift) & 0xFFu], 1u);
-        }
-        wave_sync();
-        uint32_t c[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) c[q] = hist[4 * lane + q];
-        const uint32_t own = c[0] + c[1] + c[2] + c[3];
-        uint32_t suf = own;                                  // sum over lanes >= lane
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t y = __shfl_down(suf, off);
-            if (lane + off < 64) suf += y;
-        }
-        const uint32_t above = suf - own;                    // digits > 4*lane+3
-        // the lane whose digit range contains the k-th key
-        const bool mine = above < static_cast<uint32_t>(kk) && static_cast<uint32_t>(kk) <= suf;
-        int digit = 0;
-        uint32_t gt = 0;
-        if (mine) {
-            uint32_t run = above;
-            for (int q = 3; q >= 0; --q) {
-                if (run + c[q] >= static_cast<uint32_t>(kk)) { digit = 4 * lane + q; gt = run; break; }
-                run += c[q];
-            }
-        }
-        const uint64_t who = __ballot(mine);
-        const int src = __ffsll(static_cast<long long>(who)) - 1;
-        digit = __shfl(digit, src);
-        gt = __shfl(gt, src);
-        kk -= static_cast<int>(gt);
-        prefix |= static_cast<uint64_t>(digit) << shift;
-        pmask |= 0xFFull << shift;
-        wave_sync();
+    int gt = 0;
+    for (int j0 = 0; j0 < nb; j0 += 64) {
+        const int j = j0 + lane;
+        gt += __popcll(__ballot(j < nb && keys[j] > T));
     }
-    return Threshold{prefix, kk};
+    return Threshold{T, k - gt};
+}
+
+__device__ __forceinline__ Threshold select_kth(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
+    const int kpl = (nb + 63) / 64;
+    if (kpl <= 2) return threshold_select<2>(keys, nb, k, cand_nonzero);
+    if (kpl <= 4) return threshold_select<4>(keys, nb, k, cand_nonzero);
+    if (kpl <= 8) return threshold_select<8>(keys, nb, k, cand_nonzero);
+    if (kpl <= 16) return threshold_select<16>(keys, nb, k, cand_nonzero);
+    if (kpl <= 32) return threshold_select<32>(keys, nb, k, cand_nonzero);
+    return threshold_select_lds(keys, nb, k, cand_nonzero);
 }
 
 // Writes the selected indices ascending into out[0..cap), -1 after, returns the count.
@@ -213,27 +225,25 @@ __global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
     double* qs = reinterpret_cast<double*>(smem);                            // R * d
     uint64_t* keyE = reinterpret_cast<uint64_t*>(qs + R * a.d);              // R * nbp
     uint64_t* keyW = keyE + R * nbp;                                         // R * nbp (triage)
-    uint32_t* hist = reinterpret_cast<uint32_t*>(keyW + (triage ? R * nbp : 0));  // WAVES * 256
 
     const int row0 = blockIdx.x * R;
     const size_t bh = static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y;
     score_rows<R>(a, bh, row0, qs, keyE, keyW, nbp);
 
     const int w = threadIdx.x >> 6;
-    uint32_t* myhist = hist + 256 * w;
     for (int r = w; r < R; r += WAVES) {
         const int row = row0 + r;
         if (row >= a.nb) break;
         const size_t rowid = bh * a.nb + row;
         uint64_t* kE = keyE + r * nbp;
         if (!triage) {
-            const Threshold t = radix_select(kE, a.nb, a.topk, myhist, false);
+            const Threshold t = select_kth(kE, a.nb, a.topk, false);
             const int c = compact_selection(kE, a.nb, t, false, a.idx + rowid * a.cap, a.cap, false);
             if (lane_id() == 0) a.cnt[rowid] = c;
         } else {
             uint64_t* kW = keyW + r * nbp;
             // kept = first n_keep by e_skip; blank the w-keys of the others
-            const Threshold tk = radix_select(kE, a.nb, a.n_keep, myhist, false);
+            const Threshold tk = select_kth(kE, a.nb, a.n_keep, false);
             {
                 const int lane = lane_id();
                 const uint64_t lt = (1ull << lane) - 1ull;
@@ -253,7 +263,7 @@ __global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
             // refine = first n_refine of the kept blocks by w
             const bool none = a.n_refine == 0;
             Threshold tr{~0ull, 0};
-            if (!none) tr = radix_select(kW, a.nb, a.n_refine, myhist, true);
+            if (!none) tr = select_kth(kW, a.nb, a.n_refine, true);
             const int c1 = compact_selection(kW, a.nb, tr, true, a.idx + rowid * a.cap, a.cap, none);
             // skim = kept and not refine: blank the refine keys, take every remaining candidate
             {
@@ -495,8 +505,7 @@ __global__ __launch_bounds__(THREADS) void route_err_kernel(RouteArgs a) {
 template <int R>
 hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
     const int nbp = (a.nb + 63) & ~63;
-    const size_t lds = R * a.d * sizeof(double) + (a.mode == 2 ? 2 : 1) * R * nbp * sizeof(uint64_t) +
-                       WAVES * 256 * sizeof(uint32_t);
+    const size_t lds = R * a.d * sizeof(double) + (a.mode == 2 ? 2 : 1) * R * nbp * sizeof(uint64_t);
     dim3 grid((a.nb + R - 1) / R, a.H, a.B);
     hipLaunchKernelGGL((route_scored_kernel<R>), grid, dim3(THREADS), lds, s, a);
     return hipGetLastError();
