@@ -28,19 +28,22 @@ sum_n (k_n - k_bar_j) = 0 for the exact mean.  Every approximation sits
 inside the one normalisation D_t, as PISA's "Coherence de Normalisation"
 asks.
 
-Skim tile (a, j) emulation (the fp8 reading of Triage's fast tier):
-q~, k~, v~ are the per-block scaled e4m3 copies with exponents e_q(a),
-e_k(j), e_v(j); l~_tn = (q~_t . k~_n) 2^{e_q(a) + e_k(j)}; with
-L_tn = s l~_tn log2(e) and c_t = ceil(max_n L_tn) for the tile,
-p~_tn = 2^{c_t - 8} e4m3(2^{8 + L_tn - c_t}).  The denominator takes the
-unquantised weights.
+Skim tile (a, j) emulation (Triage's fast tier), in one of two formats:
+  e4m3   q~, k~, v~ are the per-block scaled e4m3 copies with exponents
+         e_q(a), e_k(j), e_v(j): l~_tn = (q~_t . k~_n) 2^{e_q(a) + e_k(j)}
+  mxfp4  the page's 4 bits: q~, k~ carry one E8M0 scale per token and 32
+         dimensions, v~ one per block and dimension; l~ = q~ . k~ and v~ are
+         the dequantised values (exact in fp64)
+With L_tn = s l~_tn log2(e) and c_t = ceil(max_n L_tn) for the tile,
+p~_tn = 2^{c_t - 8} e4m3(2^{8 + L_tn - c_t}) in both formats (the weights
+stay 8-bit).  The denominator takes the unquantised weights.
 """
 
 import math
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mxfp4
 
 BLK = 64
 LOG2E = 1.0 / math.log(2.0)
@@ -92,7 +95,8 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
     k, v: [N_pad, d]; kbar, vbar: exact fp64 means [nb, d]; kcount [nb];
     exact / skim: key block index lists; kmom [nb, d, d] for comp == 1;
     hbar [d, d] (the head's mean first-order matrix) for comp == 2;
-    fp8: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp, vexp [nb]) for skim.
+    fp8: the skim tier's copies: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp,
+    vexp [nb]) for e4m3, or dict(q4, qs4, k4, ks4, v4, vs4) for mxfp4.
     Returns (o [r, d], lse [r]).
     """
     Qa = np.asarray(Qa, np.float64)
@@ -111,7 +115,15 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
         values.append(vbar[U])
 
     skim_terms = []
-    if skim.size:
+    if skim.size and "q4" in fp8:
+        rows = slice(a * blk, a * blk + Qa.shape[0])
+        qa = mxfp4.dequantize_blocks(fp8["q4"][rows], fp8["qs4"][rows])
+        for j in skim:
+            tj = _tokens([j], N, blk)
+            l = qa @ mxfp4.dequantize_blocks(fp8["k4"][tj], fp8["ks4"][tj]).T
+            vt = mxfp4.decode(fp8["v4"][tj]) * np.exp2(np.asarray(fp8["vs4"][j], np.float64))[None, :]
+            skim_terms.append((scale * l, vt))
+    elif skim.size:
         qa = e4m3.decode(fp8["q8"][a * blk:a * blk + Qa.shape[0]])
         for j in skim:
             tj = _tokens([j], N, blk)
@@ -142,11 +154,12 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
 
 
 def sparse_attention(q, k, v, N: int, scale: float, comp: int, pooled: dict,
-                     exact_idx, exact_cnt, skim_idx=None, skim_cnt=None, blk: int = BLK):
+                     exact_idx, exact_cnt, skim_idx=None, skim_cnt=None, blk: int = BLK,
+                     lowp: str = "e4m3"):
     """The rule on every query block of every (b, h); fp64 (O, lse), pad rows 0.
 
     `pooled` is oracle.pooling.pool(...) output (kbar64, vbar64, kcount and,
-    when needed, kmom and the fp8 copies).
+    when needed, kmom and the skim copies: fp8 for lowp "e4m3", fp4 for "mxfp4").
     """
     B, H, Np, d = q.shape
     nb = Np // blk
@@ -156,7 +169,9 @@ def sparse_attention(q, k, v, N: int, scale: float, comp: int, pooled: dict,
         for h in range(H):
             fp8 = None
             if skim_idx is not None:
-                fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
+                names = ("q4", "qs4", "k4", "ks4", "v4", "vs4") if lowp == "mxfp4" else \
+                    ("q8", "k8", "v8", "qexp", "kexp", "vexp")
+                fp8 = {n: pooled[n][b, h] for n in names}
             kmom = pooled["kmom"][b, h] if comp == 1 else None
             hbar = pooled["hbar"][b, h] if comp == 2 else None
             for a in range(nb):

@@ -16,7 +16,7 @@ is the fp64 quotient sum / n_j, then rounded to fp32.
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, mxfp4
 
 BLK = 64
 
@@ -136,7 +136,34 @@ def e4m3_blocks(x: np.ndarray, N: int, blk: int = BLK):
     return codes.reshape(B, H, nb * blk, d), e
 
 
-def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hbar=False, cov=False):
+def mxfp4_copies(q, k, v, N: int, blk: int = BLK) -> dict:
+    """MXFP4 copies for the 4-bit skim tier (Triage's fast tier in the page's
+    own 4 bits).  Q and K: one E8M0 scale per token and 32 consecutive
+    dimensions (the reduction axis of Q K^T); V: one scale per key block and
+    dimension over the block's valid keys (the reduction axis of P V is the
+    key).  Codes are one per element (0..15); pad tokens are code 0 with
+    exponent 0.  Returns q4, qs4 [B,H,N_pad,d/32], k4, ks4, v4 [B,H,N_pad,d],
+    vs4 [B,H,nb,d].
+    """
+    out = {}
+    for name, x in (("q", q), ("k", k)):
+        xx = np.array(x, np.float64)
+        xx[:, :, N:] = 0.0
+        c, e = mxfp4.quantize_blocks(xx, axis=-1, block=32)
+        out[name + "4"], out[name + "s4"] = c, e
+    vb = _blocked(np.array(v, np.float64), blk)
+    nb = vb.shape[2]
+    valid = ((np.arange(nb)[:, None] * blk + np.arange(blk)[None, :]) < N)
+    vb = np.where(valid[None, None, :, :, None], vb, 0.0)
+    e = mxfp4.block_exponent(np.abs(vb).max(axis=3))                     # [B,H,nb,d]
+    codes = mxfp4.encode(vb * np.exp2(-e.astype(np.float64))[:, :, :, None, :])
+    out["v4"] = codes.reshape(np.shape(v))
+    out["vs4"] = e
+    return out
+
+
+def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hbar=False, cov=False,
+         fp4=False):
     """Everything the router and the fused forward read, in one dict."""
     qbar, qbar64, n = block_means(q, N, blk)
     kbar, kbar64, _ = block_means(k, N, blk)
@@ -151,6 +178,8 @@ def pool(q, k, v, N, blk: int = BLK, moments=False, spreads=False, fp8=False, hb
         out["kcov"] = covariance_norms(k, v, N, blk)
     if spreads:
         out["klam"] = block_spreads(k, v, N, blk)
+    if fp4:
+        out.update(mxfp4_copies(q, k, v, N, blk))
     if fp8:
         for name, x in (("q", q), ("k", k), ("v", v)):
             c, e = e4m3_blocks(x, N, blk)

@@ -260,6 +260,63 @@ def test_skim_error_is_bounded_by_e4m3_precision():
     assert err.max() < 0.5
 
 
+def test_mxfp4_skim_is_exact_when_everything_is_representable():
+    # integers of magnitude <= 3 sit on the E2M1 grid for every block scale
+    # the rule can pick, and with s = ln 2 every weight is a power of two, so
+    # the 4-bit tier must reproduce dense attention: this pins the per-group
+    # scales of Q and K, the per-column scales of V and the P bookkeeping
+    rng = np.random.default_rng(14)
+    N, d, nb = 128, 32, 2
+    q = np.zeros((1, 1, N, d)); k = np.zeros_like(q); v = np.zeros_like(q)
+    q[0, 0] = rng.integers(-1, 2, (N, d)) * (rng.random((N, d)) < 0.2)
+    k[0, 0] = rng.integers(-1, 2, (N, d)) * (rng.random((N, d)) < 0.2)
+    v[0, 0] = rng.integers(-3, 4, (N, d))
+    v[0, 0, :, :4] = rng.integers(-1, 2, (N, 4))       # columns with a smaller scale
+    q[0, 0, :, 5] = 2; k[0, 0, :, 7] = 3               # mixed group maxima
+    pooled = pooling.pool(q, k, v, N, fp4=True)
+    assert len(set(pooled["vs4"].ravel().tolist())) > 1
+    s = math.log(2.0)
+    exact = np.full((1, 1, nb, 0), -1, np.int32)
+    skim = np.tile(np.arange(nb, dtype=np.int32), (1, 1, nb, 1))
+    O, lse = attention.sparse_attention(q, k, v, N, s, -1, pooled, exact, np.zeros((1, 1, nb), np.int32),
+                                        skim, np.full((1, 1, nb), nb, np.int32), lowp="mxfp4")
+    Od, lsed = attention.dense_attention(q, k, v, N, s)
+    np.testing.assert_allclose(O, Od, atol=1e-13)
+    np.testing.assert_allclose(lse, lsed, atol=1e-12)
+
+
+def test_mxfp4_skim_error_is_4bit_level():
+    q, k, v = rand_qkv(15, H=1, N=192, d=32, scale=0.8)
+    pooled = pooling.pool(q, k, v, 192, fp4=True, fp8=True)
+    nb = 3
+    exact = np.zeros((1, 1, nb, 1), np.int32)
+    skim = np.tile(np.array([1, 2], np.int32), (1, 1, nb, 1))
+    args = (q, k, v, 192, 1.0, -1, pooled, exact, np.ones((1, 1, nb), np.int32), skim,
+            np.full((1, 1, nb), 2, np.int32))
+    O4, _ = attention.sparse_attention(*args, lowp="mxfp4")
+    O8, _ = attention.sparse_attention(*args, lowp="e4m3")
+    Od, _ = attention.dense_attention(q, k, v, 192, 1.0)
+    e4 = np.abs(O4 - Od)[0, 0, :192].mean()
+    e8 = np.abs(O8 - Od)[0, 0, :192].mean()
+    # E2M1 keeps one mantissa bit: coarser than e4m3, still far from garbage
+    assert e8 < e4 < 0.2, (e4, e8)
+
+
+def test_mxfp4_copies_quantise_the_right_groups():
+    q, k, v = rand_qkv(16, H=2, N=150, d=64, scale=1.0)
+    p = pooling.pool(q, k, v, 150, fp4=True)
+    from oracle import mxfp4
+    # Q / K: per token and 32 dimensions
+    c, e = mxfp4.quantize_blocks(np.asarray(k[0, 1, 70], np.float64), axis=-1, block=32)
+    assert np.array_equal(p["k4"][0, 1, 70], c) and np.array_equal(p["ks4"][0, 1, 70], e)
+    # V: per block and dimension, over the valid keys only (block 2 holds 22)
+    col = np.asarray(v[0, 0, 128:150, 9], np.float64)
+    ee = int(mxfp4.block_exponent(np.abs(col).max()))
+    assert p["vs4"][0, 0, 2, 9] == ee
+    assert np.array_equal(p["v4"][0, 0, 128:150, 9], mxfp4.encode(col * 2.0 ** -ee))
+    assert not np.any(p["v4"][0, 0, 150:]) and not np.any(p["q4"][0, 0, 150:])
+
+
 def test_quality_compensation_beats_dropping():
     # report-only page claim (centroids recover context that dropping loses);
     # asserted loosely on smooth synthetic fields
