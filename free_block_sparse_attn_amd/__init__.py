@@ -17,14 +17,14 @@ import torch
 from . import _lib
 from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER0,
                    SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL, SA_ROUTE_TOPK, SA_ROUTE_LVSA,
-                   SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR)
+                   SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR, SA_SKIM_E4M3, SA_SKIM_MXFP4)
 
 __all__ = [
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
     "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE", "SA_ROUTE_TOPK_COV",
-    "SA_ROUTE_ERROR",
+    "SA_ROUTE_ERROR", "SA_SKIM_E4M3", "SA_SKIM_MXFP4",
 ]
 
 BLK = 64
@@ -62,11 +62,11 @@ def abi_version() -> int:
 
 
 def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None,
-                     global_moment=False, cov=False, out=None) -> dict:
+                     global_moment=False, cov=False, fp4=False, out=None) -> dict:
     """Block means (fp32), counts and the optional centroid planes / moments /
     mean moment H_bar (with its 64-partial scratch) / covariance log-norms
     ln ||H_j - H_bar||_2 (`cov`, implies `global_moment`) / spreads / e4m3
-    copies.  The bf16 centroid planes (what the bf16 forward reads) are
+    copies / MXFP4 copies (`fp4`).  The bf16 centroid planes (what the bf16 forward reads) are
     produced by default for bf16 inputs with d == 128.
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
@@ -82,7 +82,8 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
             ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
             _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
             _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
-            _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
+            _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+            *_fp4_ptrs(out), _stream(q)))
         return out
     out = {
         "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
@@ -109,13 +110,25 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
             out[n] = torch.empty(B, H, Np, d, dtype=torch.uint8, device=dev)
         out["v8"] = torch.empty(B, H, nb, d, BLK, dtype=torch.uint8, device=dev)   # block-transposed
         out["exp8"] = torch.empty(B, H, nb, 3, dtype=torch.int8, device=dev)
+    if fp4:
+        for n in ("q4", "k4"):
+            out[n] = torch.empty(B, H, Np, d // 2, dtype=torch.uint8, device=dev)
+        for n in ("qs4", "ks4"):
+            out[n] = torch.empty(B, H, Np, d // 32, dtype=torch.uint8, device=dev)
+        out["v4"] = torch.empty(B, H, nb, d, BLK // 2, dtype=torch.uint8, device=dev)   # block-transposed
+        out["vs4"] = torch.empty(B, H, nb, d, dtype=torch.uint8, device=dev)
     g = out.get
     _lib.check(lib.sparse_attn_pool(
         ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
         _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
         _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
-        _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), _stream(q)))
+        _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+        *_fp4_ptrs(out), _stream(q)))
     return out
+
+
+def _fp4_ptrs(pooled):
+    return [_ptr(pooled.get(n)) for n in ("q4", "k4", "v4", "qs4", "ks4", "vs4")]
 
 
 def sparse_attn_lvsa_capacity(frame_lo, frame_hi, window: int, anchors: int) -> int:
@@ -185,8 +198,11 @@ def sparse_attn_route(pooled: dict, N: int, mode: int = SA_ROUTE_TOPK, topk: int
 
 
 def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx, cnt,
-                    idx2=None, cnt2=None, want_lse=True, out=None, lse=None):
-    """Compensated block-sparse attention forward; returns (out, lse)."""
+                    idx2=None, cnt2=None, want_lse=True, out=None, lse=None, skim_fmt=SA_SKIM_E4M3):
+    """Compensated block-sparse attention forward; returns (out, lse).
+
+    The skim tier (idx2 / cnt2) reads the e4m3 copies (skim_fmt SA_SKIM_E4M3)
+    or the MXFP4 copies (SA_SKIM_MXFP4) from `pooled`."""
     lib = _lib.load()
     _contig(q, k, v, idx, cnt, idx2, cnt2)
     if out is None:
@@ -200,7 +216,7 @@ def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx,
     _lib.check(lib.sparse_attn_fwd(
         ctypes.byref(_shape(q, N)), _dtype(q), comp, scale, _ptr(q), _ptr(k), _ptr(v),
         _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("kcount")), _ptr(g("kmom")), _ptr(g("hbar")),
-        _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+        _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), skim_fmt, *_fp4_ptrs(pooled),
         _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
         _ptr(out), _ptr(lse), _stream(q)))
     return out, lse

@@ -16,6 +16,7 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_HIP = 0, 1, 2, 3
 SA_F32, SA_BF16 = 0, 1
 SA_COMP_DROP, SA_COMP_ORDER0, SA_COMP_ORDER1_BLOCK, SA_COMP_ORDER1_GLOBAL = -1, 0, 1, 2
 SA_ROUTE_TOPK, SA_ROUTE_LVSA, SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR = 0, 1, 2, 3, 4
+SA_SKIM_E4M3, SA_SKIM_MXFP4 = 0, 1
 
 EXPORTED = (
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
@@ -58,13 +59,14 @@ def load(path: str = LIB_PATH):
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     lib.sparse_attn_pool.argtypes = [ctypes.POINTER(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, vp, vp, vp, vp, vp, vp, vp, vp]
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
     lib.sparse_attn_pool.restype = i32
     lib.sparse_attn_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(RouteSpec), vp, vp, vp, vp,
                                       vp, vp, i32, vp, vp, i32, vp]
     lib.sparse_attn_route.restype = i32
     lib.sparse_attn_fwd.argtypes = [ctypes.POINTER(Shape), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    vp, vp, vp, vp, vp, vp, vp, i32, vp, vp, i32, vp, vp, vp]
+                                    vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
+                                    vp, vp, i32, vp, vp, i32, vp, vp, vp]
     lib.sparse_attn_fwd.restype = i32
     lib.sparse_attn_lvsa_capacity.argtypes = [vp, vp, i32, i32, i32]
     lib.sparse_attn_lvsa_capacity.restype = i32

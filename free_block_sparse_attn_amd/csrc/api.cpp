@@ -81,13 +81,18 @@ int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* kmom,
                            float* hbar, float* hbar_ws, float* kcov, float* klam,
-                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, hipStream_t stream) {
+                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
+                           uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (empty) return ok();
     NEED(q); NEED(k); NEED(v); NEED(qbar); NEED(kbar); NEED(vbar); NEED(kcount);
     MAYBE(cent); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(kcov); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
+    MAYBE(q4); MAYBE(k4); MAYBE(v4); MAYBE(qs4); MAYBE(ks4); MAYBE(vs4);
+    const int fp4 = (q4 != nullptr) + (k4 != nullptr) + (v4 != nullptr) + (qs4 != nullptr) + (ks4 != nullptr) +
+                    (vs4 != nullptr);
+    if (fp4 != 0 && fp4 != 6) return fail(SA_ERR_INVALID_ARG, "q4, k4, v4, qs4, ks4 and vs4 must be given together");
     const int fp8 = (q8 != nullptr) + (k8 != nullptr) + (v8 != nullptr) + (exp8 != nullptr);
     if (fp8 != 0 && fp8 != 4) return fail(SA_ERR_INVALID_ARG, "q8, k8, v8 and exp8 must be given together");
     const bool bf16_128 = dtype == SA_BF16 && shape->d == 128;
@@ -97,8 +102,9 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q,
     if (hbar && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "hbar needs bf16 inputs with d == 128");
     if (kcov && !hbar) return fail(SA_ERR_INVALID_ARG, "kcov needs hbar (M_j is taken against H_bar)");
     if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
+    if (fp4 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "MXFP4 copies need bf16 inputs with d == 128");
     sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
-                   cent, kmom, hbar, hbar_ws, kcov, klam, q8, k8, v8, exp8};
+                   cent, kmom, hbar, hbar_ws, kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4};
     return hip_result(sa::launch_pool(a, dtype == SA_BF16, stream), "pool");
 }
 
@@ -190,7 +196,9 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
                           const void* k, const void* v, const float* kbar, const float* vbar, const void* cent,
                           const int32_t* kcount, const void* kmom, const float* hbar, const uint8_t* q8,
                           const uint8_t* k8, const uint8_t* v8,
-                          const int8_t* exp8, const int32_t* idx, const int32_t* cnt, int32_t cap,
+                          const int8_t* exp8, sa_skim_format skim_fmt, const uint8_t* q4, const uint8_t* k4,
+                          const uint8_t* v4, const uint8_t* qs4, const uint8_t* ks4, const uint8_t* vs4,
+                          const int32_t* idx, const int32_t* cnt, int32_t cap,
                           const int32_t* idx2, const int32_t* cnt2, int32_t cap2, void* out, float* lse,
                           hipStream_t stream) {
     bool empty = false;
@@ -218,13 +226,16 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
     } else {
         if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "bf16 forward supports d == 128 only");
         if (comp >= SA_COMP_ORDER0) { NEED(cent); }
-        if (skim) { NEED(q8); NEED(k8); NEED(v8); NEED(exp8); }
+        if (skim && skim_fmt == SA_SKIM_E4M3) { NEED(q8); NEED(k8); NEED(v8); NEED(exp8); }
+        if (skim && skim_fmt == SA_SKIM_MXFP4) { NEED(q4); NEED(k4); NEED(v4); NEED(qs4); NEED(ks4); NEED(vs4); }
     }
+    if (skim_fmt != SA_SKIM_E4M3 && skim_fmt != SA_SKIM_MXFP4)
+        return fail(SA_ERR_INVALID_ARG, "unknown skim format %d", static_cast<int>(skim_fmt));
     if (comp == SA_COMP_DROP && cap == 0 && !skim)
         return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");
     sa::FwdArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, static_cast<int>(comp), scale, q, k, v,
-                  kbar, vbar, cent, kcount, kmom, hbar, q8, k8, v8, exp8, idx, cnt, cap, idx2, cnt2, cap2,
-                  out, lse};
+                  kbar, vbar, cent, kcount, kmom, hbar, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4,
+                  static_cast<int>(skim_fmt), idx, cnt, cap, idx2, cnt2, cap2, out, lse};
     if (dtype == SA_F32) return hip_result(sa::launch_fwd_f32(a, stream), "fwd_f32");
     return hip_result(sa::launch_fwd_bf16(a, stream), "fwd_bf16");
 }

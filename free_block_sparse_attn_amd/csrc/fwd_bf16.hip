@@ -357,57 +357,111 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
 // 32-byte loads and no LDS is needed.  The next tile's list entry and block
 // exponents come through the scalar cache, and its K~ / V~ operands load
 // while this tile computes.
+// FMT 1: e4m3 copies with one power-of-two scale per block and tensor.
+// FMT 2: MXFP4 copies; each lane's 32 reduction values of an operand carry
+// their own E8M0 scale (Q, K: per token and 32 dimensions; V: per block and
+// dimension), passed to the block-scaled MFMA per lane.  P stays e4m3.  Q and
+// K are packed alike, so the order in which the matrix core reads a lane's
+// fp4 values does not matter for Q K^T; for V (fp4) against P (e4m3) it does.
+template <int FMT>
 __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t bh, int qa,
                                         const int32_t* listM, int cntM, float c2) {
+    constexpr bool F4 = FMT == 2;
+    constexpr int QB = F4 ? D / 2 : D;             // bytes per token row of the Q / K copies
     const int nb = a.N_pad / BLK;
     const int l = lane_id(), h = l >> 5, l32 = l & 31;
     const size_t head = bh * a.N_pad * D;
-    const uint8_t* Q8 = a.q8 + head;
-    const uint8_t* K8 = a.k8 + head;
-    const uint8_t* V8 = a.v8 + head;
+    const size_t headb = bh * a.N_pad * QB;
+    const uint8_t* Q8 = (F4 ? a.q4 : a.q8) + headb;
+    const uint8_t* K8 = (F4 ? a.k4 : a.k8) + headb;
+    const uint8_t* V8 = (F4 ? a.v4 : a.v8) + headb;
+    typedef __attribute__((address_space(4))) const uint8_t const_u8;
+    const uint8_t* QS = F4 ? a.qs4 + bh * a.N_pad * (D / 32) : nullptr;
+    const uint8_t* KS = F4 ? a.ks4 + bh * a.N_pad * (D / 32) : nullptr;
+    const uint8_t* VS = F4 ? a.vs4 + bh * static_cast<size_t>(nb) * D : nullptr;
     typedef __attribute__((address_space(4))) const int8_t const_i8;
     const const_i8* EX = (const const_i8*)(a.exp8 + bh * nb * 3);
     const const_i32* LM = (const const_i32*)listM;
     i32x8 qb8[2][2];
+    int qsc[2][2];                                  // MXFP4: E8M0 scale of each B operand
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const int row = qa * BLK + 32 * rb + l32;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             i32x8 z = {};
-            if (row < a.N) z = *reinterpret_cast<const i32x8*>(Q8 + static_cast<size_t>(row) * D + 64 * ks + 32 * h);
+            if constexpr (F4) {
+                // 32 four-bit codes in the low four dwords
+                const u32x4 w = *reinterpret_cast<const u32x4*>(Q8 + static_cast<size_t>(row) * QB + 32 * ks + 16 * h);
+                z[0] = w[0]; z[1] = w[1]; z[2] = w[2]; z[3] = w[3];
+                qsc[rb][ks] = QS[static_cast<size_t>(row) * (D / 32) + 2 * ks + h];
+            } else {
+                if (row < a.N) z = *reinterpret_cast<const i32x8*>(Q8 + static_cast<size_t>(row) * D + 64 * ks + 32 * h);
+                qsc[rb][ks] = 0;
+            }
             qb8[rb][ks] = z;
         }
     }
     const int sq = static_cast<int>(EX[qa * 3 + 0]) + 127;
-    auto load_tile = [&](int j, i32x8 ka[2][2], i32x8 va[4]) __attribute__((always_inline)) {
-        const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * D;
+    auto load_tile = [&](int j, i32x8 ka[2][2], i32x8 va[4], int ksc[2][2], int vsc[4]) __attribute__((always_inline)) {
+        const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * QB;
+        const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * QB;
+        if constexpr (F4) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks)
-                ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
-        const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * D;
+                for (int ks = 0; ks < 2; ++ks) {
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(Kj + (32 * kb + l32) * QB + 32 * ks + 16 * h);
+                    ka[kb][ks] = i32x8{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                                       static_cast<int>(w[3]), 0, 0, 0, 0};
+                    ksc[kb][ks] = KS[(static_cast<size_t>(j) * BLK + 32 * kb + l32) * (D / 32) + 2 * ks + h];
+                }
+            // An fp4 operand lane of half h holds reduction indices
+            // 32 (p / 16) + 16 h + p % 16 for its nibbles p (the fp8 P operand:
+            // 32 h + p), so V^T takes positions 16h .. 16h+15 and 32+16h .. 32+16h+15.
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
+            for (int db = 0; db < 4; ++db) {
+                const uint8_t* vr = Vj + (32 * db + l32) * (BLK / 2);
+                const uint2 w0 = *reinterpret_cast<const uint2*>(vr + 8 * h);
+                const uint2 w1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * h);
+                va[db] = i32x8{static_cast<int>(w0.x), static_cast<int>(w0.y), static_cast<int>(w1.x),
+                               static_cast<int>(w1.y), 0, 0, 0, 0};
+                vsc[db] = VS[static_cast<size_t>(j) * D + 32 * db + l32];
+            }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) {
+                    ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
+                    ksc[kb][ks] = 0;
+                }
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
+                vsc[db] = 0;
+            }
+        }
     };
     if (cntM <= 0) return;
     i32x8 nka[2][2], nva[4];
+    int nksc[2][2], nvsc[4];
     int jn = LM[0];
-    load_tile(jn, nka, nva);
+    load_tile(jn, nka, nva, nksc, nvsc);
     int skn = static_cast<int>(EX[jn * 3 + 1]) + 127, svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
     for (int e = 0; e < cntM; ++e) {
         const int j = jn, sk = skn, sv = svn;
         i32x8 ka[2][2], va[4];
+        int ksc[2][2], vsc[4];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) ka[kb][ks] = nka[kb][ks];
+            for (int ks = 0; ks < 2; ++ks) { ka[kb][ks] = nka[kb][ks]; ksc[kb][ks] = nksc[kb][ks]; }
 #pragma unroll
-        for (int db = 0; db < 4; ++db) va[db] = nva[db];
+        for (int db = 0; db < 4; ++db) { va[db] = nva[db]; vsc[db] = nvsc[db]; }
         if (e + 1 < cntM) {
             jn = LM[e + 1];
-            load_tile(jn, nka, nva);
+            load_tile(jn, nka, nva, nksc, nvsc);
             skn = static_cast<int>(EX[jn * 3 + 1]) + 127;
             svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
         }
@@ -422,9 +476,14 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int rb = 0; rb < 2; ++rb)
-                    s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
+                for (int rb = 0; rb < 2; ++rb) {
+                    if constexpr (F4)
+                        s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            ka[kb][ks], qb8[rb][ks], s[kb][rb], 4, 4, 0, ksc[kb][ks], 0, qsc[rb][ks]);
+                    else
+                        s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
+                }
         // raw logits; pad keys of the ragged tail block -inf (c2 > 0 commutes with max)
         if (nj < BLK) {
 #pragma unroll
@@ -471,13 +530,18 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-                st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                    va[db], pb[rb], st.o[db][rb], 0, 0, 0, sv, 0, sb[rb]);
+            for (int rb = 0; rb < 2; ++rb) {
+                if constexpr (F4)
+                    st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        va[db], pb[rb], st.o[db][rb], 4, 0, 0, vsc[db], 0, sb[rb]);
+                else
+                    st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        va[db], pb[rb], st.o[db][rb], 0, 0, 0, sv, 0, sb[rb]);
+            }
     }
 }
 
-template <int COMP, bool SKIM>
+template <int COMP, int SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
     // separate LDS objects per half tile, so that each copy is known not to
     // alias the reads of the other three
@@ -645,7 +709,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
 
     // ---- phase 1b: fp8 skim blocks (Triage's low-precision tier) ----
-    if constexpr (SKIM) skim_tiles(a, st, bh, qa, listM, cntM, c2);
+    if constexpr (SKIM > 0) skim_tiles<SKIM>(a, st, bh, qa, listM, cntM, c2);
 
     // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
     // Units of 32 centroids.  The centroid planes (bf16 high and low parts of
@@ -872,7 +936,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
 }
 
-template <int COMP, bool SKIM>
+template <int COMP, int SKIM>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nq = a.N_pad / BLK;
     dim3 grid(nq * a.H * a.B);
@@ -880,7 +944,7 @@ hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <bool SKIM>
+template <int SKIM>
 hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
     switch (a.comp) {
         case -1: return launch_t<-1, SKIM>(a, s);
@@ -894,7 +958,8 @@ hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
     const bool skim = a.idx2 != nullptr && a.cap2 > 0;
-    return skim ? launch_c<true>(a, s) : launch_c<false>(a, s);
+    if (!skim) return launch_c<0>(a, s);
+    return a.skim_fmt == 1 ? launch_c<2>(a, s) : launch_c<1>(a, s);
 }
 
 }  // namespace sa

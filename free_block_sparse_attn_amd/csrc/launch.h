@@ -27,6 +27,12 @@ struct PoolArgs {
     uint8_t* k8;
     uint8_t* v8;
     int8_t* exp8;     // [B,H,nb,3]
+    uint8_t* q4;      // MXFP4 copies or null (all six or none): packed E2M1 codes
+    uint8_t* k4;
+    uint8_t* v4;
+    uint8_t* qs4;     // E8M0 scales: [B,H,N_pad,d/32] for q4 / k4, [B,H,nb,d] for v4
+    uint8_t* ks4;
+    uint8_t* vs4;
 };
 hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s);
 
@@ -72,6 +78,13 @@ struct FwdArgs {
     const uint8_t* k8;
     const uint8_t* v8;
     const int8_t* exp8;
+    const uint8_t* q4;        // MXFP4 skim copies (skim_fmt 1)
+    const uint8_t* k4;
+    const uint8_t* v4;
+    const uint8_t* qs4;
+    const uint8_t* ks4;
+    const uint8_t* vs4;
+    int skim_fmt;             // 0 e4m3, 1 MXFP4
     const int32_t* idx;
     const int32_t* cnt;
     int cap;

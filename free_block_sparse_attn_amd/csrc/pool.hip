@@ -54,6 +54,25 @@ constexpr int TPITCH = BLK + 8;     // transposed row pitch in elements (16-byte
 template <typename T, int D>
 constexpr size_t pool_lds() { return 3 * D * TPITCH * sizeof(T) + (3 * D + 64) * sizeof(float); }
 
+// MXFP4 block exponent: smallest e with amax * 2^-e <= 6 (amax = f 2^k,
+// f in [0.5, 1): 6 = 0.75 * 2^3), kept within the E8M0 range.
+__device__ __forceinline__ int fp4_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int k;
+    const float f = frexpf(amax, &k);
+    return max((f <= 0.75f) ? k - 3 : k - 2, -127);
+}
+
+// E2M1 code of y (|y| <= 6 by the scale rule), nearest with ties to the even
+// code: the decision points 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 alternate
+// between rounding down and up at the tie.  Magnitude 0 is +0.
+__device__ __forceinline__ uint32_t e2m1_code(float y) {
+    const float a = fabsf(y);
+    const uint32_t m = (a > 0.25f) + (a >= 0.75f) + (a > 1.25f) + (a >= 1.75f) + (a > 2.5f) + (a >= 3.5f) +
+                       (a > 5.0f);
+    return m | ((y < 0.0f && m != 0u) ? 8u : 0u);
+}
+
 // Block exponent of the e4m3 copies: smallest e with amax * 2^-e <= 448.
 // amax = f * 2^k, f in [0.5, 1): 448 * 2^(k-9) = 0.875 * 2^k.
 __device__ __forceinline__ int e4m3_block_exponent(float amax) {
@@ -286,6 +305,62 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                 uint8_t* dstv = a.v8 + ((bh * nb + j) * static_cast<size_t>(D) + dcol) * BLK + p0;
                 *reinterpret_cast<u32x4*>(dstv) = u32x4{w[0], w[1], w[2], w[3]};
                 *reinterpret_cast<u32x4*>(dstv + 16) = u32x4{w[4], w[5], w[6], w[7]};
+            }
+        }
+
+        // Phase 6 (optional): MXFP4 copies for the 4-bit skim tier.  Q and K:
+        // one E8M0 scale per token and 32 dimensions (the four threads of a
+        // 32-wide group combine their maxima); codes packed two per byte,
+        // element 2i in the low nibble.  V: block-transposed like v8 (two
+        // positions per byte) with one scale per block and dimension.
+        if (a.q4) {
+            uint8_t* dst4[2] = {a.q4, a.k4};
+            uint8_t* sc4[2] = {a.qs4, a.ks4};
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                for (int c = 0; c < PT; ++c) {
+                    const int chunk = tid + THREADS * c;
+                    const int row = chunk / CPR;
+                    const int col0 = (chunk % CPR) * PER16;
+                    float x[8];
+                    float am = 0.0f;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        x[e] = row < n ? E::get(reg[t][c], e) : 0.0f;
+                        am = fmaxf(am, fabsf(x[e]));
+                    }
+                    am = fmaxf(am, __shfl_xor(am, 1));
+                    am = fmaxf(am, __shfl_xor(am, 2));
+                    const int ex = fp4_block_exponent(am);
+                    uint32_t w = 0u;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) w |= e2m1_code(ldexpf(x[e], -ex)) << (4 * e);
+                    const size_t tok = bh * a.N_pad + static_cast<size_t>(j) * BLK + row;
+                    *reinterpret_cast<uint32_t*>(dst4[t] + tok * (D / 2) + col0 / 2) = w;
+                    if ((tid & 3) == 0) sc4[t][tok * (D / 32) + col0 / 32] = static_cast<uint8_t>(ex + 127);
+                }
+            }
+            {
+                const int dcol = tid >> 1, p0 = 32 * (tid & 1);
+                const T* col = xt + (2 * D + dcol) * TPITCH;
+                float x[32];
+                float am = 0.0f;
+#pragma unroll
+                for (int q = 0; q < 32; ++q) {
+                    const int p = p0 + q;
+                    const int key = 32 * ((p & 31) >> 4) + 8 * ((p & 15) >> 2) + 4 * (p >> 5) + (p & 3);
+                    x[q] = (key < n) ? E::val(col[key]) : 0.0f;
+                    am = fmaxf(am, fabsf(x[q]));
+                }
+                am = fmaxf(am, __shfl_xor(am, 1));            // the other 32 positions of the column
+                const int ex = fp4_block_exponent(am);
+                uint32_t w[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int q = 0; q < 32; ++q) w[q >> 3] |= e2m1_code(ldexpf(x[q], -ex)) << (4 * (q & 7));
+                const size_t cj = (bh * nb + j) * static_cast<size_t>(D) + dcol;
+                *reinterpret_cast<u32x4*>(a.v4 + cj * (BLK / 2) + p0 / 2) = u32x4{w[0], w[1], w[2], w[3]};
+                if ((tid & 1) == 0) a.vs4[cj] = static_cast<uint8_t>(ex + 127);
             }
         }
     }
@@ -659,7 +734,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 
 template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
-    if (!a.kmom && !a.klam && !a.q8) {
+    if (!a.kmom && !a.klam && !a.q8 && !a.q4) {
         constexpr int BPW = 64 / (D / Elem<T>::PER16);
         const int nb = a.N_pad / BLK;
         const int rows = a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb;   // centroid pad rows too

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 5
+#define SPARSE_ATTN_ABI_VERSION 6
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -82,6 +82,11 @@ typedef enum {
     SA_ROUTE_TOPK_COV = 3,
     SA_ROUTE_ERROR = 4
 } sa_route_mode;
+
+typedef enum {
+    SA_SKIM_E4M3 = 0,         /* skim tier in fp8 e4m3, one scale per block and tensor */
+    SA_SKIM_MXFP4 = 1         /* skim tier in MXFP4 (fp4 E2M1, E8M0 scales per 32 values) */
+} sa_skim_format;
 
 /* Problem shape.  d must be 64 or 128. */
 typedef struct {
@@ -149,12 +154,31 @@ typedef struct {
  *                        (the key order of the forward pass's fp8 P operand).
  *                        Pad keys are written as 0.  All
  *                        four pointers or none.  bf16 inputs only.
+ *   q4, k4, v4, qs4, ks4, vs4  MXFP4 copies for the 4-bit skim tier (Triage's
+ *                        fast tier in the page's own 4 bits, "Triage: Skip,
+ *                        Skim, or Refine Attention Tiles in Video Diffusion
+ *                        Transformers").  Elements are OCP E2M1 codes (nearest,
+ *                        ties to the even code, magnitude 0 as +0) of x 2^-e,
+ *                        e the smallest integer with amax 2^-e <= 6 over the
+ *                        scale's group (at least -127); scales are E8M0 bytes
+ *                        e + 127.  Two codes per byte, the even element in
+ *                        the low nibble.
+ *                        q4, k4: uint8 [B,H,N_pad,d/2] row-major; qs4, ks4:
+ *                        uint8 [B,H,N_pad,d/32], one scale per token and 32
+ *                        dimensions (the reduction axis of Q K^T).
+ *                        v4: uint8 [B,H,nb,d,32] block-transposed in the
+ *                        position order of v8 (kappa above); vs4: uint8
+ *                        [B,H,nb,d], one scale per block and dimension over
+ *                        the block's valid keys (the reduction axis of P V).
+ *                        Pad tokens are code 0 with scale byte 127.  All six
+ *                        pointers or none.  bf16 inputs with d == 128 only.
  */
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount,
                            void* cent, void* kmom, float* hbar, float* hbar_ws, float* kcov, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
+                           uint8_t* q4, uint8_t* k4, uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4,
                            hipStream_t stream);
 
 /* Routing request.  Unused fields are ignored by the other modes. */
@@ -247,9 +271,12 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  * (PISA section 2: the approximations enter numerator and denominator of a
  * single normalisation):
  *   exact   sum_{j in E} sum_n e^{scale q.k_n} (v_n)              bf16 MFMA
- *   skim    sum_{j in M} e4m3 logits and e4m3 P V via fp8 MFMA with block
- *           scales; P is quantised per row and tile against a power of two
- *           2^ceil(max L); D takes the unquantised weights
+ *   skim    sum_{j in M} low-precision logits and P V via the block-scaled
+ *           MFMA: skim_fmt SA_SKIM_E4M3 takes the e4m3 copies (one scale per
+ *           block and tensor), SA_SKIM_MXFP4 the MXFP4 copies (per-lane E8M0
+ *           scales of 32 values); P is e4m3 in both, quantised per row and
+ *           tile against a power of two 2^ceil(max L); D takes the
+ *           unquantised weights
  *   order0  sum_{j in U} n_j e^{scale q.k_bar_j} (v_bar_j)         comp >= 0
  *   order1  sum_{j in U} e^{scale q.k_bar_j} scale q^T H_j  (N only)  comp == 1
  *   global  scale (sum_{j in U} e^{scale q.k_bar_j}) q^T H_bar (N only) comp == 2
@@ -264,7 +291,9 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *            (SA_BF16 with comp >= 0; unused by SA_F32)
  * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d*d] (comp == 1)
  * hbar       fp32 [B,H,d,d] from sparse_attn_pool (comp == 2, SA_BF16)
- * q8, k8, v8, exp8                      from sparse_attn_pool (skim only)
+ * q8, k8, v8, exp8                      from sparse_attn_pool (skim, SA_SKIM_E4M3)
+ * skim_fmt   sa_skim_format of the skim tier
+ * q4, k4, v4, qs4, ks4, vs4             from sparse_attn_pool (skim, SA_SKIM_MXFP4)
  * idx, cnt, cap     exact lists (ascending, entries in [0, nb))
  * idx2, cnt2, cap2  skim lists, or NULL / 0 when there is no skim tier
  * out        dtype [B,H,N_pad,d]: fp32 accumulation rounded to the output
@@ -281,7 +310,9 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
                           const float* kbar, const float* vbar, const void* cent,
                           const int32_t* kcount, const void* kmom, const float* hbar,
                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
-                          const int8_t* exp8,
+                          const int8_t* exp8, sa_skim_format skim_fmt,
+                          const uint8_t* q4, const uint8_t* k4, const uint8_t* v4,
+                          const uint8_t* qs4, const uint8_t* ks4, const uint8_t* vs4,
                           const int32_t* idx, const int32_t* cnt, int32_t cap,
                           const int32_t* idx2, const int32_t* cnt2, int32_t cap2,
                           void* out, float* lse, hipStream_t stream);

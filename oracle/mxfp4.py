@@ -46,14 +46,15 @@ def encode(x: np.ndarray) -> np.ndarray:
 
 
 def block_exponent(amax: np.ndarray) -> np.ndarray:
-    """Smallest integer e with amax * 2^-e <= 6 (0 where amax == 0).
+    """Smallest integer e with amax * 2^-e <= 6 (0 where amax == 0), but at
+    least -127, the smallest E8M0 scale.
 
     With amax = f * 2^k, f in [0.5, 1): 6 = 0.75 * 2^3, so e = k - 3 when
     f <= 0.75 and k - 2 otherwise.
     """
     amax = np.asarray(amax, dtype=np.float64)
     f, k = np.frexp(amax)
-    e = np.where(f <= 0.75, k - 3, k - 2)
+    e = np.maximum(np.where(f <= 0.75, k - 3, k - 2), -127)
     return np.where(amax > 0, e, 0).astype(np.int64)
 
 

@@ -37,7 +37,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     N = wl.N
     pooled = fbsa.sparse_attn_pool(q, k, v, N, moments=wl.comp == 1, global_moment=wl.comp == 2,
                                    cov=wl.rule == "topk_cov", spreads=wl.rule == "triage",
-                                   fp8=wl.rule == "triage")
+                                   fp8=wl.rule == "triage" and wl.skim_fmt == "e4m3",
+                                   fp4=wl.rule == "triage" and wl.skim_fmt == "mxfp4")
     idx2 = cnt2 = None
     if wl.rule == "topk":
         idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk)
@@ -61,11 +62,18 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
             pooled, N, fbsa.SA_ROUTE_TRIAGE, n_keep=wl.n_keep, n_refine=wl.n_refine, scale=scale)
     run_fwd = wl.rule != "triage" or SKIM_BUILT
     if run_fwd:
-        out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2)
+        out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2,
+                                        skim_fmt=fbsa.SA_SKIM_MXFP4 if wl.skim_fmt == "mxfp4" else fbsa.SA_SKIM_E4M3)
     torch.cuda.synchronize()
     res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
     if "v8" in res:
         res["v8"] = v8_row_major(res["v8"], wl.N_pad)
+    if "q4" in res:
+        for n in ("q4", "k4"):
+            res[n] = unpack_nibbles(res[n])
+        for n in ("qs4", "ks4", "vs4"):
+            res[n] = res[n].astype(np.int64) - 127
+        res["v4"] = v8_row_major(unpack_nibbles(res["v4"]), wl.N_pad)
     if "kmom" in res:
         res["kmom"] = kmom_value_major(res["kmom"])
     res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
@@ -91,6 +99,12 @@ def v8_row_major(v8t, n_pad):
     return out.reshape(B, H, n_pad, d)
 
 
+def unpack_nibbles(x):
+    """uint8 [..., n] with two 4-bit codes per byte (even element low) -> [..., 2n]."""
+    lo, hi = x & 0xF, x >> 4
+    return np.stack([lo, hi], axis=-1).reshape(x.shape[:-1] + (2 * x.shape[-1],))
+
+
 def kmom_value_major(x):
     """[B,H,nb,d*d] moments in MFMA operand order -> [B,H,nb,d,d] value-major G[o][i]:
     element ((o/32*8 + i/16)*64 + o%32 + 32*((i/8)%2))*8 + i%8 holds G[o][i]."""
@@ -103,7 +117,8 @@ def kmom_value_major(x):
 
 def oracle_pool(wl, q, k, v):
     return pooling.pool(q, k, v, wl.N, moments=wl.comp == 1, spreads=wl.rule == "triage",
-                        fp8=wl.rule == "triage", hbar=wl.comp == 2, cov=wl.rule == "topk_cov")
+                        fp8=wl.rule == "triage" and wl.skim_fmt == "e4m3", hbar=wl.comp == 2,
+                        cov=wl.rule == "topk_cov", fp4=wl.rule == "triage" and wl.skim_fmt == "mxfp4")
 
 
 def lists_of(idx, cnt, b, h, a):
@@ -119,7 +134,9 @@ def oracle_rows(wl, q, k, v, pooled, res, rows, scale=1.0):
         sk = lists_of(res["idx2"], res["cnt2"], b, h, a) if "idx2" in res else ()
         fp8 = None
         if len(sk):
-            fp8 = {n: pooled[n][b, h] for n in ("q8", "k8", "v8", "qexp", "kexp", "vexp")}
+            names = ("q4", "qs4", "k4", "ks4", "v4", "vs4") if wl.skim_fmt == "mxfp4" else \
+                ("q8", "k8", "v8", "qexp", "kexp", "vexp")
+            fp8 = {n: pooled[n][b, h] for n in names}
         kmom = pooled["kmom"][b, h] if wl.comp == 1 else None
         hbar = pooled["hbar"][b, h] if wl.comp == 2 else None
         out[(b, h, a)] = attention.rule_block(

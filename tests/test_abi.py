@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 5
+    assert lib.sparse_attn_abi_version() == 6
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -47,11 +47,13 @@ MIS = ctypes.c_void_p(4097)
 
 def pool(lib, sh, dtype=1, **kw):
     a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, hbar=None, hbar_ws=None,
-             kcov=None, klam=None, q8=None, k8=None, v8=None, exp8=None)
+             kcov=None, klam=None, q8=None, k8=None, v8=None, exp8=None, q4=None, k4=None, v4=None, qs4=None,
+             ks4=None, vs4=None)
     a.update(kw)
     return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
                                 a["kcount"], a["cent"], a["kmom"], a["hbar"], a["hbar_ws"], a["kcov"], a["klam"], a["q8"],
-                                a["k8"], a["v8"], a["exp8"], None)
+                                a["k8"], a["v8"], a["exp8"], a["q4"], a["k4"], a["v4"], a["qs4"], a["ks4"],
+                                a["vs4"], None)
 
 
 def test_pool_rejects_bad_arguments(lib):
@@ -75,6 +77,9 @@ def test_pool_rejects_bad_arguments(lib):
     assert pool(lib, shape(), kcov=P) == 1                   # M_j is taken against H_bar
     assert b"hbar" in lib.sparse_attn_last_error()
     assert pool(lib, shape(), dtype=0, kcov=P, hbar=P, hbar_ws=P) == 2
+    assert pool(lib, shape(), q4=P, k4=P) == 1               # MXFP4 copies: all six or none
+    assert b"q4" in lib.sparse_attn_last_error()
+    assert pool(lib, shape(d=64), q4=P, k4=P, v4=P, qs4=P, ks4=P, vs4=P) == 2   # bf16, d = 128 only
     assert pool(lib, shape(B=0)) == 0                        # empty problem: nothing launched
     assert pool(lib, shape(N=0, N_pad=0)) == 0
 
@@ -122,10 +127,12 @@ def test_route_rejects_bad_arguments(lib):
 
 def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
     a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, kcount=P, kmom=None, hbar=None, q8=None, k8=None, v8=None,
-             exp8=None, idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
+             exp8=None, skim_fmt=0, q4=None, k4=None, v4=None, qs4=None, ks4=None, vs4=None,
+             idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
     a.update(kw)
     return lib.sparse_attn_fwd(sh, dtype, comp, scale, a["q"], a["k"], a["v"], a["kbar"], a["vbar"],
                                a["cent"], a["kcount"], a["kmom"], a["hbar"], a["q8"], a["k8"], a["v8"], a["exp8"],
+                               a["skim_fmt"], a["q4"], a["k4"], a["v4"], a["qs4"], a["ks4"], a["vs4"],
                                a["idx"],
                                a["cnt"], a["cap"], a["idx2"], a["cnt2"], a["cap2"], a["out"], a["lse"], None)
 
@@ -146,6 +153,11 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, shape(d=64)) == 2                         # bf16 needs d = 128
     assert fwd(lib, shape(), dtype=0) == 2                    # fp32 needs d = 64
     assert fwd(lib, shape(d=64), dtype=0, comp=1, kmom=P) == 2
+    assert fwd(lib, shape(), skim_fmt=2) == 1                 # unknown skim format
+    sk = dict(idx2=P, cnt2=P, cap2=2)
+    assert fwd(lib, shape(), **sk) == 1                       # e4m3 skim without its copies
+    assert fwd(lib, shape(), skim_fmt=1, q8=P, k8=P, v8=P, exp8=P, **sk) == 1   # MXFP4 skim needs q4 ...
+    assert b"q4" in lib.sparse_attn_last_error()
     assert fwd(lib, shape(B=0)) == 0
 
 

@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 5
+    assert fbsa.abi_version() == 6
 
 
 def medium(wid):
@@ -65,6 +65,10 @@ def check_pool(wl, pooled_o, res):
         assert err.max() <= 1e-3, err.max()
     if "klam" in res:
         np.testing.assert_allclose(res["klam"], pooled_o["klam"], rtol=1e-5, atol=1e-5)
+    if "q4" in res and "q4" in pooled_o:
+        # MXFP4 codes and scale exponents: bit-exact
+        for n in ("q4", "qs4", "k4", "ks4", "v4", "vs4"):
+            assert np.array_equal(res[n], pooled_o[n]), n
     if "q8" in res:
         for i, n in enumerate(("q", "k", "v")):
             assert np.array_equal(res[n + "8"], pooled_o[n + "8"]), n
@@ -328,3 +332,42 @@ def test_parity_error_routed_full_size_sampled():
     ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
     worst = check_out(wl, rsub, ref, rows)
     print(f"[ok] max|dL|={lerr:.2e} max|err|={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("size", ["small", "medium"])
+def test_parity_triage_mxfp4(size):
+    """Triage with the skim tier in MXFP4 (the page's 4 bits)."""
+    from dataclasses import replace
+    from workloads.configs import TRIAGE_FP4_SMALL
+    wl = TRIAGE_FP4_SMALL if size == "small" else replace(medium(5), skim_fmt="mxfp4")
+    print(f"\n[case] {wl.name} size={size} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+def test_parity_triage_mxfp4_full_size_sampled():
+    from workloads.configs import TRIAGE_FP4
+    wl = TRIAGE_FP4
+    print(f"\n[case] full {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    rng = np.random.default_rng(9)
+    heads = sorted(rng.choice(wl.H, 2, replace=False).tolist())
+    res = gc.run_gpu(wl, dev, coords)
+    qs, ks, vs = (x[:, heads] for x in (q, k, v))
+    pooled_o = pooling.pool(qs, ks, vs, wl.N, spreads=True, fp4=True)
+    rsub = {n: (x[:, heads] if n not in ("kcount",) else x) for n, x in res.items()}
+    check_pool(wl, pooled_o, {n: rsub[n] for n in ("qbar", "kbar", "vbar", "kcount", "q4", "qs4", "k4", "ks4",
+                                                  "v4", "vs4")})
+    check_route(wl, pooled_o, rsub, coords)
+    rows = [(0, hi, int(a)) for hi in range(len(heads)) for a in rng.choice(wl.nb, 3, replace=False)]
+    rows.append((0, 0, wl.nb - 1))
+    ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
+    worst = check_out(wl, rsub, ref, rows)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)

@@ -52,6 +52,7 @@ def test_block_exponent_is_smallest_fitting_power():
         assert amax * 2.0 ** -e <= 6.0
         assert amax * 2.0 ** -(e - 1) > 6.0
     assert int(mxfp4.block_exponent(np.array(0.0))) == 0
+    assert int(mxfp4.block_exponent(np.array(2.0 ** -140))) == -127      # E8M0 floor
 
 
 def test_quantize_blocks_bound_and_round_trip():

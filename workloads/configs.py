@@ -33,7 +33,8 @@ class Workload:
     anchors: int = 0            # LVSA: number of rotating anchor key blocks
     steps: int = 1              # LVSA: denoising steps (anchor rotation index s)
     refine_pct: int = 0         # Triage: percent of tiles computed exactly in bf16
-    skim_pct: int = 0           # Triage: percent of tiles computed in fp8 e4m3
+    skim_pct: int = 0           # Triage: percent of tiles computed in low precision
+    skim_fmt: str = "e4m3"      # Triage: skim tier format, "e4m3" or "mxfp4"
 
     @property
     def N(self) -> int:
@@ -102,6 +103,11 @@ GLOBAL_COV_SMALL = replace(GLOBAL_ORDER1_SMALL, name="hunyuan720p-global-cov-sma
 # 20% block budget, centroid compensation of the rest.
 ERROR_ROUTED = replace(WORKLOADS[2], name="wan13b-ear", rule="error")
 ERROR_ROUTED_SMALL = replace(SMALL[2], name="wan13b-ear-small", rule="error")
+
+
+# The Triage layer with its skim tier in the page's own 4 bits (MXFP4).
+TRIAGE_FP4 = replace(WORKLOADS[5], name="triage-mxfp4", skim_fmt="mxfp4")
+TRIAGE_FP4_SMALL = replace(SMALL[5], name="triage-mxfp4-small", skim_fmt="mxfp4")
 
 
 def get_workload(wid: int, small: bool = False) -> Workload:
