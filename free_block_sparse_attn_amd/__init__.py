@@ -21,6 +21,7 @@ from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER
 
 __all__ = [
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
+    "sparse_attn_residual",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
     "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE", "SA_ROUTE_TOPK_COV",
@@ -220,3 +221,33 @@ def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx,
         _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
         _ptr(out), _ptr(lse), _stream(q)))
     return out, lse
+
+
+def sparse_attn_residual(q, k, v, out, N: int, scale: float, phase: int = 0, ridge: float = 1e-3,
+                         rank: int = 8, workspace=None) -> dict:
+    """SparsePR probe-fitted residual correction of `out` (bf16, in place).
+
+    Returns views into the workspace: "xp" / "od" (sparse / dense output at
+    the probes, fp32 [B,H,Mp,d]), "W" [B,H,d,d] and "c" [B,H,d].
+    """
+    lib = _lib.load()
+    _contig(q, k, v, out)
+    B, H, Np, d = q.shape
+    shape = _shape(q, N)
+    nbytes = lib.sparse_attn_residual_workspace(ctypes.byref(shape))
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    _contig(workspace)
+    _lib.check(lib.sparse_attn_residual(
+        ctypes.byref(shape), _dtype(q), scale, _ptr(q), _ptr(k), _ptr(v), _ptr(out), phase, ridge, rank,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q)))
+    nb = Np // BLK
+    mp = BLK * ((nb + BLK - 1) // BLK)
+    bh = B * H
+    off = bh * 8 * (3 * d * d + 2 * d) * 8 + bh * 3 * d * d * 8
+    f32 = workspace[off:].view(torch.float32)
+    xp = f32[:bh * mp * d].view(B, H, mp, d)
+    od = f32[bh * mp * d:2 * bh * mp * d].view(B, H, mp, d)
+    wc = f32[2 * bh * mp * d:2 * bh * mp * d + bh * (d * d + d)].view(B, H, d * d + d)
+    return {"xp": xp, "od": od, "W": wc[:, :, :d * d].view(B, H, d, d), "c": wc[:, :, d * d:],
+            "workspace": workspace}

@@ -21,6 +21,7 @@ SA_SKIM_E4M3, SA_SKIM_MXFP4 = 0, 1
 EXPORTED = (
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_abi_version",
+    "sparse_attn_residual", "sparse_attn_residual_workspace",
 )
 
 
@@ -74,6 +75,11 @@ def load(path: str = LIB_PATH):
     lib.sparse_attn_status_string.restype = ctypes.c_char_p
     lib.sparse_attn_last_error.argtypes = []
     lib.sparse_attn_last_error.restype = ctypes.c_char_p
+    lib.sparse_attn_residual_workspace.argtypes = [ctypes.POINTER(Shape)]
+    lib.sparse_attn_residual_workspace.restype = ctypes.c_size_t
+    lib.sparse_attn_residual.argtypes = [ctypes.POINTER(Shape), i32, f32, vp, vp, vp, vp, i32, f32, i32, vp,
+                                         ctypes.c_size_t, vp]
+    lib.sparse_attn_residual.restype = i32
     lib.sparse_attn_abi_version.argtypes = []
     lib.sparse_attn_abi_version.restype = i32
     _lib = lib

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "pool.hip", "route.hip", "fwd_f32.hip", "fwd_bf16.hip"]
+SOURCES = ["api.cpp", "pool.hip", "route.hip", "fwd_f32.hip", "fwd_bf16.hip", "residual.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

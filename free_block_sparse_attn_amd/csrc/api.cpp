@@ -192,6 +192,38 @@ sa_status sparse_attn_route(const sa_shape* shape, const sa_route_spec* spec, co
     return hip_result(sa::launch_route(a, stream), "route");
 }
 
+size_t sparse_attn_residual_workspace(const sa_shape* shape) {
+    if (shape == nullptr || shape->B < 0 || shape->H < 0 || shape->N_pad < 0) return 0;
+    return sa::residual_workspace_bytes(shape->B, shape->H, shape->N_pad);
+}
+
+sa_status sparse_attn_residual(const sa_shape* shape, sa_dtype dtype, float scale, const void* q, const void* k,
+                               const void* v, void* out, int32_t phase, float ridge, int32_t rank, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+    bool empty = false;
+    if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
+    if (dtype != SA_BF16) return fail(SA_ERR_UNSUPPORTED, "the residual pass takes bf16 tensors");
+    if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "the residual pass supports d == 128 only");
+    const int nb = shape->N_pad / 64;
+    if (nb > MAX_BLOCKS) return fail(SA_ERR_UNSUPPORTED, "at most %d blocks per sequence, got %d", MAX_BLOCKS, nb);
+    if (!std::isfinite(scale) || !(scale > 0.0f)) return fail(SA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!std::isfinite(ridge) || ridge < 0.0f) return fail(SA_ERR_INVALID_ARG, "ridge must be finite and >= 0");
+    if (rank < 1 || rank > 8) return fail(SA_ERR_INVALID_ARG, "rank must be in [1, 8], got %d", rank);
+    if (phase < 0) return fail(SA_ERR_INVALID_ARG, "phase must be >= 0");
+    if (empty) return ok();
+    NEED(q); NEED(k); NEED(v); NEED(out); NEED(workspace);
+    const size_t need = sa::residual_workspace_bytes(shape->B, shape->H, shape->N_pad);
+    if (workspace_bytes < need)
+        return fail(SA_ERR_INVALID_ARG, "workspace of %zu bytes, need %zu", workspace_bytes, need);
+    sa::ResidualArgs r{};
+    r.B = shape->B; r.H = shape->H; r.N = shape->N; r.N_pad = shape->N_pad;
+    r.Mp = 64 * ((nb + 63) / 64);
+    r.phase = phase; r.rank = rank; r.scale = scale; r.ridge = ridge;
+    r.q = q; r.k = k; r.v = v; r.out = out;
+    sa::residual_carve(r, workspace);
+    return hip_result(sa::launch_residual(r, stream), "residual");
+}
+
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale, const void* q,
                           const void* k, const void* v, const float* kbar, const float* vbar, const void* cent,
                           const int32_t* kcount, const void* kmom, const float* hbar, const uint8_t* q8,
@@ -235,7 +267,8 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
         return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");
     sa::FwdArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, static_cast<int>(comp), scale, q, k, v,
                   kbar, vbar, cent, kcount, kmom, hbar, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4,
-                  static_cast<int>(skim_fmt), idx, cnt, cap, idx2, cnt2, cap2, out, lse};
+                  static_cast<int>(skim_fmt), idx, cnt, cap, idx2, cnt2, cap2, out, lse,
+                  shape->N, shape->N_pad, 0, 0};
     if (dtype == SA_F32) return hip_result(sa::launch_fwd_f32(a, stream), "fwd_f32");
     return hip_result(sa::launch_fwd_bf16(a, stream), "fwd_bf16");
 }

@@ -554,19 +554,25 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // footprint stays within four workgroups per CU)
     __shared__ float wbuf[COMP == 1 ? 16 * BLK : 1];
 
-    const int nq = a.N_pad / BLK, nb = nq;
-    const int lin = xcd_remap(blockIdx.x, gridDim.x);
+    const int nq = a.Nq_pad / BLK, nb = a.N_pad / BLK;
+    const int lin0 = xcd_remap(blockIdx.x, gridDim.x);
+    const int per_chunk = nq * a.H * a.B;
+    const int chunk = a.dense ? lin0 / per_chunk : 0;   // dense mode: key chunk of this wave
+    const int lin = lin0 - chunk * per_chunk;
     const int qa = lin % nq;
     const size_t bh = lin / nq;
+    const int jlo = a.dense ? static_cast<int>(static_cast<long long>(chunk) * nb / a.dense) : 0;
+    const int jhi = a.dense ? static_cast<int>(static_cast<long long>(chunk + 1) * nb / a.dense) : nb;
     const int l = lane_id(), h = l >> 5, l32 = l & 31;
     const size_t head = bh * a.N_pad * D;
-    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + head;
+    const size_t headq = bh * a.Nq_pad * D;
+    const uint16_t* Q = static_cast<const uint16_t*>(a.q) + headq;
     const uint16_t* K = static_cast<const uint16_t*>(a.k) + head;
     const uint16_t* V = static_cast<const uint16_t*>(a.v) + head;
     const float c2 = a.scale * LOG2E;
 
     const size_t rowid = bh * nq + qa;
-    const int cntE = a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0;
+    const int cntE = a.dense ? jhi - jlo : (a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0);
     const int32_t* listE = a.idx + rowid * a.cap;
     const const_i32* lstE = (const const_i32*)listE;
     const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
@@ -585,7 +591,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             bf16x8 z = {};
-            if (row < a.N) z = *reinterpret_cast<const bf16x8*>(Q + static_cast<size_t>(row) * D + 16 * ks + 8 * h);
+            if (row < a.Nq) z = *reinterpret_cast<const bf16x8*>(Q + static_cast<size_t>(row) * D + 16 * ks + 8 * h);
             // Q^T only ever feeds MFMA B operands, which read AGPRs directly:
             // keep it there and leave the VGPRs to the accumulators and weights.
             u32x4 zu = __builtin_bit_cast(u32x4, z);
@@ -604,7 +610,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // region A of the first tile issues V(0, lo).
     int j = 0;
     if (cntE > 0) {
-        j = lstE[0];
+        j = a.dense ? jlo : lstE[0];
         const uint32_t t0 = static_cast<uint32_t>(j) * TILEB;
         dma_half(rk, kbuf0, t0, dmaoff);
         dma_half(rv, vbuf1, t0 + HALFB, dmaoff);
@@ -656,7 +662,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         int nj = min(BLK, a.N - BLK * j);
         int nj_prev = nj;
         for (int i = 0; i < cntE; ++i) {
-            const int jn = i + 1 < cntE ? lstE[i + 1] : j;    // the last tile copies itself again (never read)
+            const int jn = i + 1 < cntE ? (a.dense ? jlo + i + 1 : lstE[i + 1]) : j;   // the last tile copies itself again (never read)
             const uint32_t tj = static_cast<uint32_t>(j) * TILEB, tn = static_cast<uint32_t>(jn) * TILEB;
 
             // A: S(lo, i) | weights of (hi, i-1), row block 1 | copy V(i, lo)
@@ -914,32 +920,40 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     }
 
     // ---- normalise and write O (bf16) and lse ----
-    uint16_t* O = static_cast<uint16_t*>(a.out) + head;
+    const size_t cofs = static_cast<size_t>(chunk) * per_chunk * BLK;   // B H Nq_pad rows per chunk
+    uint16_t* O = static_cast<uint16_t*>(a.out) + headq + cofs * D;
+    float* OF = static_cast<float*>(a.out) + headq + cofs * D;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
         const float lt = pair_sum(st.l[rb]);
         const int row = qa * BLK + 32 * rb + l32;
-        const bool valid = row < a.N;
+        const bool valid = row < a.Nq;
         const float inv = valid ? 1.0f / lt : 0.f;
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
 #pragma unroll
             for (int q4 = 0; q4 < 4; ++q4) {
                 const int dd = 32 * db + 8 * q4 + 4 * h;
+                if (a.out_f32) {
+                    const f32x4 w = {st.o[db][rb][4 * q4 + 0] * inv, st.o[db][rb][4 * q4 + 1] * inv,
+                                     st.o[db][rb][4 * q4 + 2] * inv, st.o[db][rb][4 * q4 + 3] * inv};
+                    *reinterpret_cast<f32x4*>(OF + static_cast<size_t>(row) * D + dd) = w;
+                    continue;
+                }
                 uint2 w;
                 w.x = pack_bf16x2(st.o[db][rb][4 * q4 + 0] * inv, st.o[db][rb][4 * q4 + 1] * inv);
                 w.y = pack_bf16x2(st.o[db][rb][4 * q4 + 2] * inv, st.o[db][rb][4 * q4 + 3] * inv);
                 *reinterpret_cast<uint2*>(O + static_cast<size_t>(row) * D + dd) = w;
             }
         }
-        if (a.lse && h == 0) a.lse[bh * a.N_pad + row] = valid ? (st.m[rb] + __log2f(lt)) * LN2 : 0.f;
+        if (a.lse && h == 0) a.lse[cofs + bh * a.Nq_pad + row] = valid ? (st.m[rb] + __log2f(lt)) * LN2 : 0.f;
     }
 }
 
 template <int COMP, int SKIM>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
-    const int nq = a.N_pad / BLK;
-    dim3 grid(nq * a.H * a.B);
+    const int nq = a.Nq_pad / BLK;
+    dim3 grid(nq * a.H * a.B * (a.dense > 0 ? a.dense : 1));
     hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64), 0, s, a);
     return hipGetLastError();
 }

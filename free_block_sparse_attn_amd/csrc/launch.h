@@ -93,8 +93,40 @@ struct FwdArgs {
     int cap2;
     void* out;
     float* lse;
+    // query rows: Nq valid of Nq_pad (= N, N_pad for attention over the same
+    // sequence); dense > 0: every key block is exact (no lists), split into
+    // `dense` consecutive chunks of key blocks, chunk c writing its own
+    // normalised O and lse at out / lse + c * B H Nq_pad (d) elements;
+    // out_f32: write O in fp32 (bf16 path)
+    int Nq, Nq_pad;
+    int dense;
+    int out_f32;
 };
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s);
+
+struct ResidualArgs {
+    int B, H, N, N_pad;
+    int Mp;                   // probe rows padded to a multiple of 64 (one probe per query block)
+    int phase, rank;
+    float scale, ridge;
+    const void* q;            // bf16 [B,H,N_pad,128]
+    const void* k;
+    const void* v;
+    void* out;                // bf16 [B,H,N_pad,128], corrected in place
+    // carved from the caller's workspace (residual_carve)
+    int kchunks;              // key chunks of the dense probe pass
+    float* odp;               // [kchunks,B,H,Mp,d] dense output per key chunk
+    float* lsep;              // [kchunks,B,H,Mp] its natural-log normaliser
+    double* part;             // [B,H,8,3*d*d + 2*d] Gram partial sums
+    double* mat;              // [B,H,3,d,d] X^T X, X^T R (then B), R^T R
+    float* xp;                // [B,H,Mp,d] sparse output at the probes
+    float* od;                // [B,H,Mp,d] dense output at the probes
+    float* wc;                // [B,H,d*d + d] W, c
+    uint16_t* qp;             // [B,H,Mp,d] gathered probe queries
+};
+size_t residual_workspace_bytes(int B, int H, int N_pad);
+void residual_carve(ResidualArgs& r, void* ws);
+hipError_t launch_residual(const ResidualArgs& r, hipStream_t s);
 
 }  // namespace sa

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 6
+#define SPARSE_ATTN_ABI_VERSION 7
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -316,6 +316,44 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
                           const int32_t* idx, const int32_t* cnt, int32_t cap,
                           const int32_t* idx2, const int32_t* cnt2, int32_t cap2,
                           void* out, float* lse, hipStream_t stream);
+
+/*
+ * sparse_attn_residual - SparsePR's probe-fitted residual reconstruction
+ * ("Partition the Support, Reconstruct the Residual: ...", section 2B), a
+ * post-pass that corrects the output of sparse_attn_fwd in place.
+ *
+ * One probe row per query block a, row 64 a + ((phase + 37 a) mod n_a), is
+ * computed by dense attention (every key block exact, fp32).  With X the
+ * sparse outputs and R = O_dense - X at the probes, the residual is fitted as
+ * R ~ b + X B by ridge regression on the centred probes (lambda = ridge *
+ * tr(Xc^T Xc) / d, intercept not penalised; fp64 normal equations solved by
+ * Cholesky) and restricted to the span of the top `rank` right singular
+ * vectors of R (simultaneous iteration on R^T R, 8 columns, 16 steps of
+ * Cholesky QR, the first `rank` columns): W = B P, c = b P.  Every valid row then gets
+ * o + c + o W, each probe row its dense output (RNE to bf16); pad rows 0.
+ *
+ * dtype      SA_BF16; d == 128
+ * scale      the softmax scale of the forward call, finite and > 0
+ * q, k, v    bf16 [B,H,N_pad,d]
+ * out        bf16 [B,H,N_pad,d]: the sparse output on entry, corrected on return
+ * phase      >= 0, picks the probe rows; ridge finite >= 0; rank in [1, 8]
+ * workspace  device memory of at least sparse_attn_residual_workspace()
+ *            bytes, 16-byte aligned, laid out as (Mp = 64 ceil(nb / 64)):
+ *              fp64 [B,H,8,3 d d + 2 d]  Gram partial sums
+ *              fp64 [B,H,3,d,d]          X^T X, then B; X^T R; R^T R
+ *              fp32 [B,H,Mp,d]           X (sparse output at the probes)
+ *              fp32 [B,H,Mp,d]           dense output at the probes
+ *              fp32 [B,H,d d + d]        W (row-major, o W), then c
+ *              fp32 [K,B,H,Mp,d], fp32 [K,B,H,Mp]  the dense probe output and
+ *                                        lse per chunk of key blocks,
+ *                                        K = min(8, nb)
+ *              bf16 [B,H,Mp,d]           gathered probe queries
+ */
+size_t sparse_attn_residual_workspace(const sa_shape* shape);
+sa_status sparse_attn_residual(const sa_shape* shape, sa_dtype dtype, float scale,
+                               const void* q, const void* k, const void* v, void* out,
+                               int32_t phase, float ridge, int32_t rank,
+                               void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* sparse_attn_status_string(sa_status status);

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 6
+    assert lib.sparse_attn_abi_version() == 7
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -159,6 +159,27 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, shape(), skim_fmt=1, q8=P, k8=P, v8=P, exp8=P, **sk) == 1   # MXFP4 skim needs q4 ...
     assert b"q4" in lib.sparse_attn_last_error()
     assert fwd(lib, shape(B=0)) == 0
+
+
+def test_residual_rejects_bad_arguments(lib):
+    from free_block_sparse_attn_amd import _lib
+    sh = shape()
+    need = lib.sparse_attn_residual_workspace(sh)
+    assert need > 0
+    def res(dtype=1, scale=1.0, phase=0, ridge=1e-3, rank=8, ws=P, nbytes=None, **kw):
+        a = dict(q=P, k=P, v=P, out=P)
+        a.update(kw)
+        return lib.sparse_attn_residual(sh, dtype, scale, a["q"], a["k"], a["v"], a["out"], phase, ridge, rank,
+                                        ws, need if nbytes is None else nbytes, None)
+    assert res(dtype=0) == 2                                  # bf16 only
+    assert res(rank=0) == 1 and res(rank=9) == 1
+    assert res(ridge=-1.0) == 1 and res(ridge=float("nan")) == 1
+    assert res(phase=-1) == 1
+    assert res(scale=0.0) == 1
+    assert res(nbytes=need - 1) == 1                          # workspace too small
+    assert b"workspace" in lib.sparse_attn_last_error()
+    assert res(out=None) == 1
+    assert lib.sparse_attn_residual(shape(d=64), 1, 1.0, P, P, P, P, 0, 1e-3, 8, P, 1 << 30, None) == 2
 
 
 def test_status_strings(lib):

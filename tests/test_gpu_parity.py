@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 6
+    assert fbsa.abi_version() == 7
 
 
 def medium(wid):
@@ -370,4 +370,71 @@ def test_parity_triage_mxfp4_full_size_sampled():
     rows.append((0, 0, wl.nb - 1))
     ref = gc.oracle_rows(wl, qs, ks, vs, pooled_o, rsub, rows)
     worst = check_out(wl, rsub, ref, rows)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+RES_PHASE, RES_RIDGE, RES_RANK = 3, 1e-3, 8
+
+
+def run_residual(wl, dev, coords):
+    """GPU sparse forward, then the probe-fitted residual pass on its output."""
+    import free_block_sparse_attn_amd as fbsa
+    res = gc.run_gpu(wl, dev, coords)
+    q, k, v = dev
+    out = torch.from_numpy(res["out"]).to(torch.bfloat16).cuda()
+    r = fbsa.sparse_attn_residual(q, k, v, out, wl.N, 1.0, RES_PHASE, RES_RIDGE, RES_RANK)
+    torch.cuda.synchronize()
+    fit = {n: r[n].cpu().numpy() for n in ("xp", "od", "W", "c")}
+    return res, out.float().cpu().numpy(), fit
+
+
+def check_residual(wl, q, k, v, res, corr, fit, heads_rows):
+    """Dense probe rows, the fit on the GPU's probe data, and the corrected rows."""
+    from oracle import residual
+    nb = wl.nb
+    rows = residual.probe_rows(wl.N, nb, RES_PHASE)
+    worst = 0.0
+    for (b, h), check_rows in heads_rows.items():
+        od = residual.probe_dense(q[b, h], k[b, h], v[b, h], wl.N, 1.0, rows)
+        assert np.abs(fit["od"][b, h, :nb] - od).max() <= gc.BF16_TOL
+        assert np.array_equal(fit["xp"][b, h, :nb], res["out"][b, h, rows])
+        # stage-wise: the oracle's fit on the GPU's probe outputs
+        X = fit["xp"][b, h, :nb].astype(np.float64)
+        W, c = residual.fit_residual(X, fit["od"][b, h, :nb] - X, RES_RIDGE, RES_RANK)
+        scale = max(np.abs(W).max(), np.abs(c).max(), 1e-12)
+        assert np.abs(fit["W"][b, h] - W).max() <= 1e-3 * scale, np.abs(fit["W"][b, h] - W).max()
+        assert np.abs(fit["c"][b, h] - c).max() <= 1e-3 * scale
+        # end to end: o + c + o W on the GPU's sparse output, dense rows at the probes
+        O = res["out"][b, h].astype(np.float64)
+        ref = O + c + O @ W
+        ref[rows] = od
+        ref[wl.N:] = 0.0
+        err = np.abs(corr[b, h, check_rows] - ref[check_rows]).max()
+        worst = max(worst, err)
+        assert err <= gc.BF16_TOL, (b, h, err)
+    return worst
+
+
+@pytest.mark.parametrize("size", ["small", "medium"])
+def test_parity_probe_residual(size):
+    """SparsePR's probe-fitted residual on the Wan-like layer's sparse output."""
+    wl = get_workload(2, small=True) if size == "small" else medium(2)
+    print(f"\n[case] residual {wl.name} size={size} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    res, corr, fit = run_residual(wl, dev, coords)
+    heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
+    worst = check_residual(wl, q, k, v, res, corr, fit, heads)
+    assert np.all(corr[:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+def test_parity_probe_residual_full_size_sampled():
+    wl = WORKLOADS[2]
+    print(f"\n[case] residual full {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    res, corr, fit = run_residual(wl, dev, coords)
+    rng = np.random.default_rng(10)
+    heads = sorted(rng.choice(wl.H, 2, replace=False).tolist())
+    sample = {(0, h): np.sort(rng.choice(wl.N, 512, replace=False)) for h in heads}
+    worst = check_residual(wl, q, k, v, res, corr, fit, sample)
     print(f"[ok] max|err|={worst:.3e}", flush=True)
