@@ -85,7 +85,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: --gpus {args.gpus} is not supported "
-              "(the path shards by head with no exchange; see the design notes)", file=sys.stderr)
+              "(one GPU runs the whole layer; heads are independent, so more GPUs would split them with no exchange)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
