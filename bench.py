@@ -105,38 +105,36 @@ def main():
     out, lse = fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0], route_out[1])
     torch.cuda.synchronize()
 
-    def step():
-        fbsa.sparse_attn_pool(dq, dk, dv, N, out=pooled)
-        fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk, out=route_out)
-        fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0], route_out[1],
-                             out=out, lse=lse)
+    # HIP events bracket each kernel of every timed step on the current
+    # stream, which is the stream the binding launches on
+    names = ("pool", "route", "fwd")
+    evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)] for n in names}
+
+    def step(i=None):
+        def run(name, fn):
+            if i is None:
+                fn()
+                return
+            s, e = evs[name][i]
+            s.record()
+            fn()
+            e.record()
+        run("pool", lambda: fbsa.sparse_attn_pool(dq, dk, dv, N, out=pooled))
+        run("route", lambda: fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk, out=route_out))
+        run("fwd", lambda: fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0], route_out[1],
+                                                out=out, lse=lse))
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        step(i)
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # per-kernel mean launch times with HIP events on the launch stream
-    def timed(fn, reps):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        fn()
-        s.record()
-        for _ in range(reps):
-            fn()
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / reps
-
-    reps = max(args.steps, 5)
-    ms_pool = timed(lambda: fbsa.sparse_attn_pool(dq, dk, dv, N, out=pooled), reps)
-    ms_route = timed(lambda: fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk,
-                                                    out=route_out), reps)
-    ms_fwd = timed(lambda: fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0],
-                                                route_out[1], out=out, lse=lse), reps)
+    # mean launch duration of each kernel over the timed steps
+    ms_pool, ms_route, ms_fwd = (sum(s.elapsed_time(e) for s, e in evs[n]) / args.steps for n in names)
 
     cnt = route_out[1].cpu().numpy()
     kept_flop = float(cnt.sum()) * 4 * 64 * 64 * wl.d

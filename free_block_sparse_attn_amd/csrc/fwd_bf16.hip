@@ -31,11 +31,11 @@
 //   A: S(keys 0-31, tile i)      C: S(keys 32-63, tile i)
 //   B: PV(keys 32-63, tile i-1)  D: PV(keys 0-31, tile i),
 // run in the order A B C D, and the exponentials of one row block of a half
-// (48 VALU instructions) are interleaved between the MFMAs of each region, so
+// (48-56 VALU instructions) are interleaved between the MFMAs of each region, so
 // the VALU work of the softmax runs under the matrix core.  K and V halves
 // have LDS buffers of their own, filled by buffer_load ... lds (no VGPRs, no
 // VALU address arithmetic) as soon as the region that reads them is done;
-// each copy has three regions to land.
+// each copy has the rest of its region and the next two to land.
 //
 // Softmax reference.  P = 2^(c2 s - m) with a per-row reference m that only
 // moves when a half tile's weights overflow a bound (sum of one lane's 16
@@ -43,10 +43,16 @@
 // becomes the ceiling of the row max over that half and the accumulators are
 // rescaled; otherwise no row max is computed at all.  Any m keeps the bf16
 // weights and the fp32 sums exact to rounding as long as nothing overflows,
-// which the bound guarantees.  The denominator sums the same bf16-rounded P
-// that the MFMA consumes, so the rounding of P cancels in o = N / D; lse is
-// m + log2 of that sum (within 2^-8, the bf16 unit roundoff, relative of the
-// unrounded sum).
+// which the bound guarantees.  The denominator is the fp32 sum of the
+// unrounded weights and lse is m + log2 of it (exact to fp32 rounding); the
+// MFMA consumes P rounded to bf16, so o = N / D scales the exact convex
+// combination by sum(bf16(p)) / sum(p), within 2^-8 (the bf16 unit roundoff)
+// of 1.  The first-order Taylor forms (per-block H_j, global H_bar) instead
+// sum the bf16-rounded pairs with v_dot2_f32_bf16, which cancels that rounding
+// in o (lse then within 2^-8 relative of the unrounded sum): their H terms
+// leave less of the bf16 error budget.  Only there, because on gfx950 each
+// v_dot2 holds up the next MFMA issue (8 per 16 MFMAs cost ~60 cycles), while
+// FMA, v_exp_f32 and v_cvt_pk_bf16_f32 run under the MFMAs almost for free.
 //
 // Centroid pseudo-keys go through the same MFMA path as 64-wide tiles (means
 // split into bf16 high + low parts so the fp32 means keep ~16 bits), with
@@ -117,15 +123,28 @@ __device__ __forceinline__ void dma_offsets(uint32_t off[4]) {
         off[par] = rsub * ROWB + 16 * swz(4 * par + rsub, p);   // swz is an involution per row
 }
 
+// Instruction M: the immediate offset (M % 4) KiB applies to both the global
+// and the LDS address, so M0 (the LDS base) and the scalar source offset
+// change once per 4 KiB instead of once per instruction.
+template <int M>
+__device__ __forceinline__ void dma_one(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t src, const uint32_t off[4]) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(static_cast<uintptr_t>(lds + (M >> 2) * 4096)),
+                                             16, off[M & 3], src + (M >> 2) * 4096, (M & 3) * 1024, 0);
+}
+
 __device__ __forceinline__ void dma_half(__amdgpu_buffer_rsrc_t rs, uint8_t* buf, uint32_t src,
                                          const uint32_t off[4]) {
     // the low 32 bits of a generic pointer into LDS are the LDS address (no
     // null-pointer select per instruction, as a generic -> LDS cast would emit)
     const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(buf));
-#pragma unroll
-    for (int m = 0; m < 8; ++m)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(static_cast<uintptr_t>(lds + m * 1024)),
-                                                 16, off[m & 3], src + m * 1024, 0, 0);
+    dma_one<0>(rs, lds, src, off);
+    dma_one<1>(rs, lds, src, off);
+    dma_one<2>(rs, lds, src, off);
+    dma_one<3>(rs, lds, src, off);
+    dma_one<4>(rs, lds, src, off);
+    dma_one<5>(rs, lds, src, off);
+    dma_one<6>(rs, lds, src, off);
+    dma_one<7>(rs, lds, src, off);
 }
 
 // Zero half-buffer rows r0 .. 31 (pad keys of the ragged tail block).
@@ -166,6 +185,7 @@ __device__ __forceinline__ void rescale_lazy(State& st, int rb, float mx) {
     }
 }
 
+// Sum of a bf16 pair in fp32 (v_dot2 with ones).
 __device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc) {
     const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
@@ -173,25 +193,29 @@ __device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc) {
 
 // P = 2^(c2 s - m) for the 16 logits a lane holds in one row block of a
 // 32-key half, as the two bf16 B operands of that half's PV k-steps
-// (p0: accumulator entries 0-7, p1: 8-15), and the sum of the rounded values.
-// 16 FMA + 16 v_exp_f32 + 8 v_cvt_pk_bf16_f32 + 8 v_dot2 = 48 VALU.
+// (p0: accumulator entries 0-7, p1: 8-15), and the sum of the weights: of
+// the bf16-rounded ones (RS) or of the fp32 ones.
+// 16 FMA + 16 v_exp_f32 + 8 v_cvt_pk_bf16_f32 + 8 v_dot2 (RS) or 16 v_add.
+template <bool RS>
 __device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
     const float negm = -m;
     float acc = 0.f;
     u32x4 w0, w1;
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-        const uint32_t pr = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[e], c2, negm)),
-                                        __builtin_amdgcn_exp2f(fmaf(s[e + 1], c2, negm)));
-        w0[e >> 1] = pr;
-        acc = sum_bf16_pair(pr, acc);
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[e], c2, negm));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], c2, negm));
+        w0[e >> 1] = pack_bf16x2(x0, x1);
+        if constexpr (RS) acc = sum_bf16_pair(w0[e >> 1], acc);
+        else acc += x0 + x1;
     }
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
-        const uint32_t pr = pack_bf16x2(__builtin_amdgcn_exp2f(fmaf(s[8 + e], c2, negm)),
-                                        __builtin_amdgcn_exp2f(fmaf(s[8 + e + 1], c2, negm)));
-        w1[e >> 1] = pr;
-        acc = sum_bf16_pair(pr, acc);
+        const float x0 = __builtin_amdgcn_exp2f(fmaf(s[8 + e], c2, negm));
+        const float x1 = __builtin_amdgcn_exp2f(fmaf(s[8 + e + 1], c2, negm));
+        w1[e >> 1] = pack_bf16x2(x0, x1);
+        if constexpr (RS) acc = sum_bf16_pair(w1[e >> 1], acc);
+        else acc += x0 + x1;
     }
     p0 = __builtin_bit_cast(bf16x8, w0);
     p1 = __builtin_bit_cast(bf16x8, w1);
@@ -202,6 +226,7 @@ __device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x
 // overflowed the bound (first tile, or a large logit), move the reference of
 // the affected rows to the ceiling of their max over this half, rescale, and
 // redo the weights.  Then fold the half's sums into the row sums.
+template <bool RS>
 __device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float c2, bf16x8 pb[2][2], float ls[2]) {
     if (__builtin_expect(__ballot(ls[0] > OVF || ls[1] > OVF) != 0, 0)) {
 #pragma unroll
@@ -212,7 +237,7 @@ __device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float 
             mx = pair_max(mx) * c2;
             const bool need = pair_max(ls[rb]) > OVF;
             if (need) rescale_row(st, rb, ceilf(mx));
-            exp_rb(s[rb], st.m[rb], c2, pb[0][rb], pb[1][rb], ls[rb]);
+            exp_rb<RS>(s[rb], st.m[rb], c2, pb[0][rb], pb[1][rb], ls[rb]);
         }
     }
     st.l[0] += ls[0];
@@ -267,27 +292,36 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* pa, const uint8_t*
 
 // ---- the four MFMA regions of the exact-tile pipeline ----
 //
-// Each region issues 16 MFMAs; after each MFMA come three VALU instructions
-// of the weights of one row block of the other pending half (48 in all), the
+// Each region issues 16 MFMAs; after each MFMA come up to four VALU instructions
+// of the weights of one row block of the other pending half (48-56 in all), the
 // LDS reads run two steps ahead, and the eight buffer_load ... lds of one
-// half-tile copy (into the buffer the previous region finished reading) sit
-// between the MFMAs of the first half of the region.  IGroupLP
-// sched_group_barriers lay out that pattern; sched_barrier(0) on both sides
-// keeps each region a scheduling unit of its own.
+// half-tile copy (into the buffer the previous region finished reading) get
+// one slot per MFMA pair (the M0 chain still lets the scheduler bunch most of
+// them near the end of the region).  IGroupLP sched_group_barriers lay out
+// that pattern; sched_barrier(0) on both sides keeps each region a
+// scheduling unit of its own.
 
-constexpr int SG_VALU = 0x002, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
+// group masks; transcendental VALU (v_exp_f32) has its own bit (0x400) and is
+// not covered by the VALU bit
+constexpr int SG_VALU = 0x002, SG_TRANS = 0x400, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-template <int READS_PER_STEP, bool EXP, bool COPY>
+// With the fp32 weight sum (RS false) the exponentials join the VALU groups,
+// four instructions after each MFMA.  With the v_dot2 sum the groups take
+// three plain VALU instructions and the scheduler places the exponentials,
+// which measured faster with the dot2 stalls.
+template <int READS_PER_STEP, bool EXP, bool COPY, bool RS>
 __device__ __forceinline__ void region_schedule() {
+    constexpr int VM = RS ? SG_VALU : (SG_VALU | SG_TRANS);
+    constexpr int VN = RS ? 3 : 4;
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * READS_PER_STEP, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
         if (t < 6) __builtin_amdgcn_sched_group_barrier(SG_DS_READ, READS_PER_STEP, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        if (EXP) __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        if (EXP) __builtin_amdgcn_sched_group_barrier(VM, VN, 0);
         if (COPY) __builtin_amdgcn_sched_group_barrier(SG_VMEM_READ, 1, 0);
         __builtin_amdgcn_sched_group_barrier(SG_MFMA, 1, 0);
-        if (EXP) __builtin_amdgcn_sched_group_barrier(SG_VALU, 3, 0);
+        if (EXP) __builtin_amdgcn_sched_group_barrier(VM, VN, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -302,6 +336,7 @@ struct Copy {
 // S^T of one half tile (K rows of half buffer kb_, both row blocks) while
 // the weights of one row block (logits xs) of the other pending half are
 // computed and the copy cp is issued.
+template <bool RS>
 __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff[8], const bf16x8 qb[2][8],
                                          f32x16 s[2], const f32x16& xs, float m, float c2, bf16x8& p0,
                                          bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
@@ -315,15 +350,15 @@ __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
-    exp_rb(xs, m, c2, p0, p1, ls);
+    exp_rb<RS>(xs, m, c2, p0, p1, ls);
     dma_half(cp.rs, cp.dst, cp.src, dmaoff);
-    region_schedule<1, true, true>();
+    region_schedule<1, true, true, RS>();
 }
 
 // O^T += V^T P^T over one half tile (V rows in half buffer vb_, P^T operands
 // pb[q2][rb]), with (EXP) the weights of one row block of the next half and
 // (COPY) one half-tile copy.
-template <bool EXP, bool COPY>
+template <bool EXP, bool COPY, bool RS>
 __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const uint32_t oa[4], const uint32_t ob[4],
                                           const bf16x8 pb[2][2], const f32x16& xs, float m, float c2, bf16x8& p0,
                                           bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
@@ -341,9 +376,9 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
                 st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q2][db], pb[q2][rb], st.o[db][rb], 0, 0, 0);
-    if (EXP) exp_rb(xs, m, c2, p0, p1, ls);
+    if (EXP) exp_rb<RS>(xs, m, c2, p0, p1, ls);
     if (COPY) dma_half(cp.rs, cp.dst, cp.src, dmaoff);
-    if (EXP || COPY) region_schedule<2, EXP, COPY>();
+    if (EXP || COPY) region_schedule<2, EXP, COPY, RS>();
 }
 
 // fp8 e4m3 skim tiles with per-block power-of-two scales (E8M0 operand
@@ -543,6 +578,10 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
 
 template <int COMP, int SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
+    // the first-order Taylor forms normalise with the sum of the bf16-rounded
+    // weights (their H terms already spend most of the bf16 error budget);
+    // order 0 and drop with the fp32 sum
+    constexpr bool RS = COMP >= 1;
     // separate LDS objects per half tile, so that each copy is known not to
     // alias the reads of the other three
     __shared__ __attribute__((aligned(16))) uint8_t kbuf0[HALFB];    // K rows 0-31 (row-major, swizzled)
@@ -668,31 +707,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             // A: S(lo, i) | weights of (hi, i-1), row block 1 | copy V(i, lo)
             wait_vmcnt<16>();
             wave_lds_sync();
-            region_s(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1],
+            region_s<RS>(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1],
                      Copy{rv, vbuf0, tj}, dmaoff);
-            settle_half(st, s1, c2, pb1, ls1);
+            settle_half<RS>(st, s1, c2, pb1, ls1);
             if (nj < 32) mask_half(s0, 0, nj);
 
             // B: PV(hi, i-1) | weights of (lo, i), row block 0 | copy K(i+1, lo)
             wait_vmcnt<16>();
             if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
             wave_lds_sync();
-            region_pv<true, true>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0],
+            region_pv<true, true, RS>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0],
                                   Copy{rk, kbuf0, tn}, dmaoff);
 
             // C: S(hi, i) | weights of (lo, i), row block 1 | copy V(i, hi)
             wait_vmcnt<16>();
             wave_lds_sync();
-            region_s(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1],
+            region_s<RS>(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1],
                      Copy{rv, vbuf1, tj + HALFB}, dmaoff);
-            settle_half(st, s0, c2, pb0, ls0);
+            settle_half<RS>(st, s0, c2, pb0, ls0);
             if (nj < BLK) mask_half(s1, 32, nj);
 
             // D: PV(lo, i) | weights of (hi, i), row block 0 | copy K(i+1, hi)
             wait_vmcnt<16>();
             if (nj < 32) zero_rows(vbuf0, nj);
             wave_lds_sync();
-            region_pv<true, true>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0],
+            region_pv<true, true, RS>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0],
                                   Copy{rk, kbuf1, tn + HALFB}, dmaoff);
 
             nj_prev = nj;
@@ -700,15 +739,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             nj = min(BLK, a.N - BLK * j);
         }
         // drain: weights of (hi, last), row block 1, then PV(hi, last)
-        exp_rb(s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
-        settle_half(st, s1, c2, pb1, ls1);
+        exp_rb<RS>(s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
+        settle_half<RS>(st, s1, c2, pb1, ls1);
         wait_vmcnt<0>();
         if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
         wave_lds_sync();
         {
             float unused_l;
             bf16x8 unused0, unused1;
-            region_pv<false, false>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l,
+            region_pv<false, false, RS>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l,
                                     Copy{rv, vbuf1, 0}, dmaoff);
         }
         wave_lds_sync();
@@ -781,8 +820,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             bf16x8 pb[2][2];
             float ls[2];
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) exp_rb(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
-            settle_half(st, s, 1.0f, pb, ls);
+            for (int rb = 0; rb < 2; ++rb) exp_rb<RS>(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
+            settle_half<RS>(st, s, 1.0f, pb, ls);
             if (COMP == 2) {
                 // PISA's global first-order weight: sum over skipped blocks of
                 // alpha_{t,j} = e^{s q.k_bar_j}, relative to the reference m
@@ -801,9 +840,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             {
                 float unused_l;
                 bf16x8 unused0, unused1;
-                region_pv<false, false>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
+                region_pv<false, false, RS>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
                                         Copy{rc, vbuf0, 0}, dmaoff);
-                region_pv<false, false>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
+                region_pv<false, false, RS>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
                                         Copy{rc, vbuf1, 0}, dmaoff);
             }
             wave_lds_sync();

@@ -9,10 +9,12 @@ from workloads import make_qkv, block_frame_ranges, lvsa_anchor_phase
 
 BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs
 F32_TOL = 1e-4       # max |out - oracle| for fp32 outputs
-# lse: the bf16 path's denominator is the sum of the bf16-rounded weights the
-# matrix core multiplies, each within 2^-8 (bf16 unit roundoff) relative of the
-# exact weight, so |d lse| <= -ln(1 - 2^-8) = 3.92e-3; plus fp32 logit error
-# (centroid means carried as bf16 high + low parts, MFMA accumulation): 4.5e-3.
+# lse: the bf16 path's first-order Taylor forms normalise with the sum of the
+# bf16-rounded weights the matrix core multiplies, each within 2^-8 (bf16 unit
+# roundoff) relative of the exact weight, so |d lse| <= -ln(1 - 2^-8) = 3.92e-3;
+# plus fp32 logit error (centroid means carried as bf16 high + low parts, MFMA
+# accumulation): 4.5e-3.  The other forms sum the fp32 weights and land far
+# inside this bar (~1e-5).
 LSE_TOL = {"bf16": 4.5e-3, "f32": 1e-5}
 
 
