@@ -15,7 +15,8 @@
 // Work split.  One wave owns a whole 64-row query block, so every K/V byte
 // brought into LDS feeds 64 query rows.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16; A = K rows from LDS
-//                 (ds_read_b128), B = Q^T held in VGPRs for the whole kernel.
+//                 (ds_read_b128), B = Q^T held in AGPRs through the exact
+//                 and centroid phases (the skim tiles, last, reuse them).
 //                 A lane owns one query row per 32-row block; its 16
 //                 accumulator entries are 16 of the 32 keys of a half tile,
 //                 the other 16 sit in lane l ^ 32.
@@ -479,27 +480,9 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
         }
     };
     if (cntM <= 0) return;
-    i32x8 nka[2][2], nva[4];
-    int nksc[2][2], nvsc[4];
-    int jn = LM[0];
-    load_tile(jn, nka, nva, nksc, nvsc);
-    int skn = static_cast<int>(EX[jn * 3 + 1]) + 127, svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
-    for (int e = 0; e < cntM; ++e) {
-        const int j = jn, sk = skn, sv = svn;
-        i32x8 ka[2][2], va[4];
-        int ksc[2][2], vsc[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int ks = 0; ks < 2; ++ks) { ka[kb][ks] = nka[kb][ks]; ksc[kb][ks] = nksc[kb][ks]; }
-#pragma unroll
-        for (int db = 0; db < 4; ++db) { va[db] = nva[db]; vsc[db] = nvsc[db]; }
-        if (e + 1 < cntM) {
-            jn = LM[e + 1];
-            load_tile(jn, nka, nva, nksc, nvsc);
-            skn = static_cast<int>(EX[jn * 3 + 1]) + 127;
-            svn = static_cast<int>(EX[jn * 3 + 2]) + 127;
-        }
+    // One skim tile: S^T = K Q^T on the scaled MFMA, quantised weights, O^T += V^T P^T.
+    auto tile = [&](int j, int sk, int sv, const i32x8 ka[2][2], const i32x8 va[4], const int ksc[2][2],
+                    const int vsc[4]) __attribute__((always_inline)) {
         const int nj = min(BLK, a.N - BLK * j);
         f32x16 s[2][2];
 #pragma unroll
@@ -573,6 +556,37 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
                     st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         va[db], pb[rb], st.o[db][rb], 0, 0, 0, sv, 0, sb[rb]);
             }
+    };
+    // Three register slots: each tile's loads are issued two tiles ahead of
+    // its use (one ahead left the loads' latency exposed).  Loads past the end
+    // of the list repeat the last tile (never used), so the load sequence is
+    // straight-line and its waits stay counted.
+    struct Slot {
+        i32x8 ka[2][2], va[4];
+        int ksc[2][2], vsc[4];
+        int j, sk, sv;
+    };
+    // (the exponent bytes are vector loads: issued before the tile's own loads,
+    // so that waiting for them leaves the tile loads in flight)
+    auto fill = [&](Slot& sl, int e) __attribute__((always_inline)) {
+        sl.j = LM[min(e, cntM - 1)];
+        sl.sk = static_cast<int>(EX[sl.j * 3 + 1]) + 127;
+        sl.sv = static_cast<int>(EX[sl.j * 3 + 2]) + 127;
+        load_tile(sl.j, sl.ka, sl.va, sl.ksc, sl.vsc);
+    };
+    auto run = [&](const Slot& sl) __attribute__((always_inline)) {
+        tile(sl.j, sl.sk, sl.sv, sl.ka, sl.va, sl.ksc, sl.vsc);
+    };
+    Slot s0, s1, s2;
+    fill(s0, 0);
+    fill(s1, 1);
+    for (int e = 0; e < cntM; e += 3) {
+        fill(s2, e + 2);
+        run(s0);
+        fill(s0, e + 3);
+        if (e + 1 < cntM) run(s1);
+        fill(s1, e + 4);
+        if (e + 2 < cntM) run(s2);
     }
 }
 
@@ -753,8 +767,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         wave_lds_sync();
     }
 
-    // ---- phase 1b: fp8 skim blocks (Triage's low-precision tier) ----
-    if constexpr (SKIM > 0) skim_tiles<SKIM>(a, st, bh, qa, listM, cntM, c2);
 
     // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
     // Units of 32 centroids.  The centroid planes (bf16 high and low parts of
@@ -957,6 +969,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             }
         }
     }
+
+    // ---- phase 3: skim blocks (Triage's low-precision tier) ----
+    // after the centroids, so that the bf16 Q^T operands are dead and their
+    // registers hold the skim tiles in flight
+    if constexpr (SKIM > 0) skim_tiles<SKIM>(a, st, bh, qa, listM, cntM, c2);
 
     // ---- normalise and write O (bf16) and lse ----
     const size_t cofs = static_cast<size_t>(chunk) * per_chunk * BLK;   // B H Nq_pad rows per chunk
