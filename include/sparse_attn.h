@@ -282,6 +282,11 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *   global  scale (sum_{j in U} e^{scale q.k_bar_j}) q^T H_bar (N only) comp == 2
  *           (PISA section 2, "Algorithme Central": the hybrid-order form,
  *           one d x d statistic for every skipped block)
+ * Precision (SA_BF16): the exact and centroid weights enter the MFMA rounded
+ * to bf16; D sums them in fp32 unrounded for comp <= 0 (lse exact to fp32
+ * rounding, o within 2^-8 relative scaling of the convex combination) and
+ * rounded for comp >= 1 (their rounding cancels in o; lse within 2^-8
+ * relative of the unrounded sum).
  *
  * scale      softmax scale, finite and > 0
  * q, k, v    dtype [B,H,N_pad,d]
