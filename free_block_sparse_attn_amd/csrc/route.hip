@@ -524,15 +524,23 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64 * LVSA_ROWS), 0, s, a);
         return hipGetLastError();
     }
-    // rows per workgroup: as many as fit a 64 KiB key budget, at most 16
+    // rows per workgroup: as many as fit a 64 KiB key budget, at most 16, then
+    // halved while the grid has fewer than 1024 workgroups (four per CU), so
+    // that the waves' global k_bar loads overlap (Wan-size layer: 16 rows per
+    // workgroup took 101 us, 4 rows 80 us)
     const int nbp = (a.nb + 63) & ~63;
     const size_t per_row = (a.mode == 2 ? 2 : 1) * nbp * sizeof(uint64_t);
     const size_t budget = 64 * 1024;
-    if (per_row * 16 <= budget) return launch_scored<16>(a, s);
-    if (per_row * 8 <= budget) return launch_scored<8>(a, s);
-    if (per_row * 4 <= budget) return launch_scored<4>(a, s);
-    if (per_row * 2 <= budget) return launch_scored<2>(a, s);
-    return launch_scored<1>(a, s);
+    int R = 16;
+    while (R > 1 && per_row * R > budget) R >>= 1;
+    while (R > 1 && static_cast<long long>((a.nb + R - 1) / R) * a.H * a.B < 1024) R >>= 1;
+    switch (R) {
+        case 16: return launch_scored<16>(a, s);
+        case 8: return launch_scored<8>(a, s);
+        case 4: return launch_scored<4>(a, s);
+        case 2: return launch_scored<2>(a, s);
+        default: return launch_scored<1>(a, s);
+    }
 }
 
 }  // namespace sa
