@@ -59,7 +59,9 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
 // in registers.  The threshold is found bit by bit from the highest bit in
 // which the candidates differ: bit b is set when at least k keys are >= the
 // threshold with it set (one 64-bit compare and one ballot per key and bit,
-// no LDS traffic).  Real keys are never 0 (order_key of a non-NaN value), so
+// no LDS traffic).  The search ends at the first bit where exactly k keys
+// are >= the candidate; it returns {candidate - 1, 0} then, which selects
+// the same keys.  Real keys are never 0 (order_key of a non-NaN value), so
 // 0 marks missing entries.
 template <int KPL>
 __device__ Threshold threshold_select(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
@@ -85,7 +87,10 @@ __device__ Threshold threshold_select(const uint64_t* keys, int nb, int k, bool 
         int c = 0;
 #pragma unroll
         for (int t = 0; t < KPL; ++t) c += __popcll(__ballot(kr[t] >= cand));
-        if (c >= k) T = cand;
+        // exactly k keys at or above cand: they are the selection (the k-th
+        // and (k+1)-th keys first differ in bit b), whatever the lower bits
+        if (c == k) return Threshold{cand - 1ull, 0};
+        if (c > k) T = cand;
     }
     int gt = 0;
 #pragma unroll
@@ -113,7 +118,8 @@ __device__ Threshold threshold_select_lds(const uint64_t* keys, int nb, int k, b
             const int j = j0 + lane;
             c += __popcll(__ballot(j < nb && keys[j] >= cand));
         }
-        if (c >= k) T = cand;
+        if (c == k) return Threshold{cand - 1ull, 0};   // as in threshold_select
+        if (c > k) T = cand;
     }
     int gt = 0;
     for (int j0 = 0; j0 < nb; j0 += 64) {
