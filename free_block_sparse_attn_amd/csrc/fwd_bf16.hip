@@ -382,6 +382,110 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
     if (EXP || COPY) region_schedule<2, EXP, COPY, RS>();
 }
 
+// ---- centroid units: the two row blocks staggered ----
+//
+// A unit of 32 centroids is four regions of 16 MFMAs: S of row block 0, S of
+// row block 1 with the bias and weights of row block 0 between its MFMAs, PV
+// of row block 0 (over the V high and low planes) with the bias and weights
+// of row block 1, and PV of row block 1.  Each region reads its own operands
+// from LDS (no operand registers live across regions).
+
+// The weights computed inside a region must stay there: an empty volatile
+// asm that takes them as inputs at the region's end keeps LLVM from sinking
+// their computation into the code after it, out of reach of the schedule.
+__device__ __forceinline__ void pin_weights(const bf16x8& p0, const bf16x8& p1, float ls) {
+    asm volatile("" ::"v"(__builtin_bit_cast(u32x4, p0)), "v"(__builtin_bit_cast(u32x4, p1)), "v"(ls));
+}
+
+// One row block's overflow check (as settle_half, for row block RB only).
+template <bool RS, int RB>
+__device__ __forceinline__ void settle_row(State& st, const f32x16& s, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+    if (__builtin_expect(__ballot(ls > OVF) != 0, 0)) {
+        float mx = s[0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
+        mx = pair_max(mx);
+        if (pair_max(ls) > OVF) rescale_row(st, RB, ceilf(mx));
+        exp_rb<RS>(s, st.m[RB], 1.0f, p0, p1, ls);
+    }
+    st.l[RB] += ls;
+}
+
+// S^T of one row block over the unit's K high and low planes; with EXP, the
+// other row block's logits xs get their bias and weights; without, the bias
+// of the unit is set from cmh (this lane's compensated-centroid bits shifted
+// down by 4h: accumulator entry r, centroid 8(r/4) + 4h + r%4, is bit
+// 8(r/4) + r%4): log2 64 = 6 where set, -inf elsewhere.
+template <bool RS, bool EXP>
+__device__ __forceinline__ void region_cs_rb(const uint8_t* khb, const uint8_t* klb, const uint32_t koff[8],
+                                             const bf16x8 qbr[8], f32x16& s, f32x16& xs, float bias[16],
+                                             uint32_t cmh, float m, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 khi[8], klo[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        khi[ks] = *reinterpret_cast<const bf16x8*>(khb + koff[ks]);
+        klo[ks] = *reinterpret_cast<const bf16x8*>(klb + koff[ks]);
+    }
+    const f32x16 zero = {};
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[ks], qbr[ks], ks ? s : zero, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[ks], qbr[ks], s, 0, 0, 0);
+    }
+    if (EXP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[r] = fmaf(xs[r], c2, bias[r]);
+        exp_rb<RS>(xs, m, 1.0f, p0, p1, ls);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) bias[r] = ((cmh >> (8 * (r >> 2) + (r & 3))) & 1u) ? 6.0f : -INFINITY;
+    }
+    region_schedule<2, true, false, RS>();    // 16 K reads, two per MFMA pair
+    if (EXP) {
+        pin_weights(p0, p1, ls);
+    } else {
+        asm volatile("" ::"v"(bias[0]), "v"(bias[1]), "v"(bias[2]), "v"(bias[3]), "v"(bias[4]), "v"(bias[5]),
+                     "v"(bias[6]), "v"(bias[7]));
+        asm volatile("" ::"v"(bias[8]), "v"(bias[9]), "v"(bias[10]), "v"(bias[11]), "v"(bias[12]),
+                     "v"(bias[13]), "v"(bias[14]), "v"(bias[15]));
+    }
+}
+
+// O^T += V^T P^T of row block RB over the unit's V high and low planes (P^T
+// in pw[q2]); with EXP, the other row block's logits xs get bias and weights.
+template <bool RS, bool EXP, int RB>
+__device__ __forceinline__ void region_cpv_rb(State& st, const uint8_t* vhb, const uint8_t* vlb, const uint32_t oa[4],
+                                              const uint32_t ob[4], const bf16x8& pw0, const bf16x8& pw1,
+                                              f32x16& xs, const float bias[16], float m, float c2, bf16x8& p0,
+                                              bf16x8& p1, float& ls) {
+    __builtin_amdgcn_sched_barrier(0);
+    bf16x8 va[2][2][4];
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+                const uint8_t* vb_ = pl ? vlb : vhb;
+                va[pl][q2][db] = tr_read_pair(vb_ + oa[db] + q2 * 16 * ROWB, vb_ + ob[db] + q2 * 16 * ROWB);
+            }
+#pragma unroll
+    for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+                st.o[db][RB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[pl][q2][db], q2 ? pw1 : pw0, st.o[db][RB], 0, 0, 0);
+    if (EXP) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[r] = fmaf(xs[r], c2, bias[r]);
+        exp_rb<RS>(xs, m, 1.0f, p0, p1, ls);
+    }
+    region_schedule<4, EXP, false, RS>();     // 32 V^T reads, four per MFMA pair
+    if (EXP) pin_weights(p0, p1, ls);
+}
+
 // fp8 e4m3 skim tiles with per-block power-of-two scales (E8M0 operand
 // scales of v_mfma_scale_f32_32x32x64_f8f6f4):
 //   S^T = (K~ 2^{e_k}) (Q~ 2^{e_q})^T; L = scale log2(e) S (pad keys -inf)
@@ -790,50 +894,55 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int u = 0; u < nu; ++u) {
             const bool more = u + 1 < nu;
             const uint32_t un = static_cast<uint32_t>(more ? u + 1 : u) * HALFB;
+            // logits in log2 units with the count bias; -inf at exact / skim / pad
+            // centroids: bit c of cm marks centroid 32 u + c as compensated
+            const uint32_t valid = 32 * u + 32 <= nb ? 0xFFFFFFFFu : ((1u << (nb - 32 * u)) - 1u);
+            const uint32_t keptw = kept_mask[u];
+            const uint32_t cmh = (~keptw & valid) >> (4 * h);
+            float bias[16];
             // K planes of unit u: only its V planes were issued after them
             wait_vmcnt<16>();
             wave_lds_sync();
             f32x16 s[2];
+            bf16x8 pb[2][2];
+            float ls[2];
             {
-                bf16x8 khi[8], klo[8];
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks) {
-                    khi[ks] = *reinterpret_cast<const bf16x8*>(kbuf0 + koff[ks]);
-                    klo[ks] = *reinterpret_cast<const bf16x8*>(kbuf1 + koff[ks]);
-                }
-                const f32x16 zero = {};
-#pragma unroll
-                for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-                    for (int rb = 0; rb < 2; ++rb) {
-                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
-                        s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[ks], qb[rb][ks], s[rb], 0, 0, 0);
-                    }
+                float unused_l;
+                bf16x8 unused0, unused1;
+                region_cs_rb<RS, false>(kbuf0, kbuf1, koff, qb[0], s[0], s[1], bias, cmh, 0.f, c2, unused0,
+                                        unused1, unused_l);
             }
+            if (u == nu - 1 && nlast < BLK) {
+                // the last block's centroid takes log2 of its own count
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (8 * (r >> 2) + 4 * h + (r & 3) == ((nb - 1) & 31) && bias[r] != -INFINITY) bias[r] = blast;
+            }
+            region_cs_rb<RS, true>(kbuf0, kbuf1, koff, qb[1], s[1], s[0], bias, 0u, st.m[0], c2, pb[0][0],
+                                   pb[1][0], ls[0]);
             wave_lds_sync();
             if (more) {
                 dma_half(rc, kbuf0, un, dmaoff);
                 dma_half(rc, kbuf1, plane + un, dmaoff);
             }
-            // logits in log2 units with the count bias; -inf at exact / skim / pad centroids
-            const uint32_t keptw = kept_mask[u];
-            float bias[16];
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-                const int cc = 8 * (r >> 2) + 4 * h + (r & 3);
-                const int jj = 32 * u + cc;
-                const bool comp = jj < nb && !((keptw >> cc) & 1u);
-                bias[r] = !comp ? -INFINITY : (jj == nb - 1 ? blast : 6.0f);   // log2 64 = 6
+            settle_row<RS, 0>(st, s[0], 1.0f, pb[0][0], pb[1][0], ls[0]);
+            // V planes of unit u: only the next unit's K planes may still be in flight
+            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+            wave_lds_sync();
+            region_cpv_rb<RS, true, 0>(st, vbuf0, vbuf1, oa, ob, pb[0][0], pb[1][0], s[1], bias, st.m[1], c2,
+                                       pb[0][1], pb[1][1], ls[1]);
+            settle_row<RS, 1>(st, s[1], 1.0f, pb[0][1], pb[1][1], ls[1]);
+            {
+                float unused_l;
+                bf16x8 unused0, unused1;
+                region_cpv_rb<RS, false, 1>(st, vbuf0, vbuf1, oa, ob, pb[0][1], pb[1][1], s[0], bias, 0.f, c2,
+                                            unused0, unused1, unused_l);
             }
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) s[rb][r] = fmaf(s[rb][r], c2, bias[r]);
-            bf16x8 pb[2][2];
-            float ls[2];
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) exp_rb<RS>(s[rb], st.m[rb], 1.0f, pb[0][rb], pb[1][rb], ls[rb]);
-            settle_half<RS>(st, s, 1.0f, pb, ls);
+            wave_lds_sync();
+            if (more) {
+                dma_half(rc, vbuf0, 2 * plane + un, dmaoff);
+                dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
+            }
             if (COMP == 2) {
                 // PISA's global first-order weight: sum over skipped blocks of
                 // alpha_{t,j} = e^{s q.k_bar_j}, relative to the reference m
@@ -845,22 +954,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                         if (bias[r] != -INFINITY) acc += __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]);
                     st.a1[rb] += acc;
                 }
-            }
-            // V planes of unit u: only the next unit's K planes may still be in flight
-            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
-            wave_lds_sync();
-            {
-                float unused_l;
-                bf16x8 unused0, unused1;
-                region_pv<false, false, RS>(st, vbuf0, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
-                                        Copy{rc, vbuf0, 0}, dmaoff);
-                region_pv<false, false, RS>(st, vbuf1, oa, ob, pb, s[0], 0.f, 1.0f, unused0, unused1, unused_l,
-                                        Copy{rc, vbuf1, 0}, dmaoff);
-            }
-            wave_lds_sync();
-            if (more) {
-                dma_half(rc, vbuf0, 2 * plane + un, dmaoff);
-                dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
             }
             if (COMP == 1) {
                 // O^T[., row] += w_j[row] T, T = H_j^T Q^T (fp32, 16 MFMAs per
