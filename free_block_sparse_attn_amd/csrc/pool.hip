@@ -568,15 +568,6 @@ __global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
 // rounding.
 constexpr int COV_STEPS = 32;
 
-__device__ __forceinline__ float block_sum128(float x, float* red) {
-    // sum over threads 0..127 (waves 0 and 1); every thread of the workgroup gets it
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-    if ((threadIdx.x & 63) == 0 && threadIdx.x < 128) red[threadIdx.x >> 6] = x;
-    __syncthreads();
-    return red[0] + red[1];
-}
-
 // Eigenvalues of the symmetric tridiagonal (diagonal al, off-diagonal be) below x.
 __device__ __forceinline__ int sturm_below(const float* al, const float* be, int n, float x) {
     int c = 0;
@@ -593,11 +584,12 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     constexpr int D = 128;
     // the block staging, then half of Dm at a time (rows 64 hf .. 64 hf + 63)
     __shared__ __attribute__((aligned(16))) uint16_t stage[2 * D * TPITCH];
-    __shared__ float part[16 * D];
+    constexpr int PP = D + 4;                 // padded partial-sum rows: the 16 column tiles' writes hit distinct banks
+    __shared__ float part[16 * PP];
     __shared__ float yv_s[D], wv_s[D];
+    __shared__ float red2[2][2];              // per-step wave partials of |y|^2 and |w|^2
     __shared__ float kb_s[D];
     __shared__ float al[COV_STEPS], be[COV_STEPS];
-    __shared__ float red[4];
     float* dmh = reinterpret_cast<float*>(stage);
     static_assert(64 * D * sizeof(float) <= sizeof(stage), "half of Dm fits the staging buffer");
     const int j = blockIdx.x;
@@ -659,6 +651,9 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
     int steps = 0;
     float beta = 0.0f;
+    // Four barriers per step (column sums, y to every tile, row sums, w to
+    // every tile); the squared norms ride on the second and fourth as wave
+    // partials.
     for (int k = 0; k < COV_STEPS; ++k) {
         // y = Dm q: partial sums over this tile's columns, summed over the 16 column tiles
 #pragma unroll
@@ -666,16 +661,21 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             float p = 0.0f;
 #pragma unroll
             for (int v = 0; v < 8; ++v) p = fmaf(t[u][v], x[v], p);
-            part[tc * D + 8 * tr + u] = p;
+            part[tc * PP + 8 * tr + u] = p;
         }
         __syncthreads();
         float y = 0.0f;
         if (tid < D) {
 #pragma unroll
-            for (int c = 0; c < 16; ++c) y += part[c * D + tid];
+            for (int c = 0; c < 16; ++c) y += part[c * PP + tid];
             yv_s[tid] = y;
+            float y2 = y * y;                 // alpha = q^T A q = |Dm q|^2: wave partials
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) y2 += __shfl_xor(y2, off);
+            if ((tid & 63) == 0) red2[0][tid >> 6] = y2;
         }
-        const float alpha = block_sum128(tid < D ? y * y : 0.0f, red);   // q^T A q = |Dm q|^2
+        __syncthreads();
+        const float alpha = red2[0][0] + red2[0][1];
         // w = Dm^T y - alpha q - beta q_prev: partial sums over this tile's rows
         float yy[8];
 #pragma unroll
@@ -685,17 +685,22 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             float p = 0.0f;
 #pragma unroll
             for (int u = 0; u < 8; ++u) p = fmaf(t[u][v], yy[u], p);
-            part[tr * D + 8 * tc + v] = p;
+            part[tr * PP + 8 * tc + v] = p;
         }
         __syncthreads();
         float w = 0.0f;
         if (tid < D) {
 #pragma unroll
-            for (int r = 0; r < 16; ++r) w += part[r * D + tid];
+            for (int r = 0; r < 16; ++r) w += part[r * PP + tid];
             w = w - alpha * qi - beta * qpi;
             wv_s[tid] = w;
+            float w2 = w * w;
+#pragma unroll
+            for (int off = 32; off >= 1; off >>= 1) w2 += __shfl_xor(w2, off);
+            if ((tid & 63) == 0) red2[1][tid >> 6] = w2;
         }
-        beta = sqrtf(block_sum128(tid < D ? w * w : 0.0f, red + 2));
+        __syncthreads();
+        beta = sqrtf(red2[1][0] + red2[1][1]);
         if (tid == 0) { al[k] = alpha; be[k] = beta; }
         steps = k + 1;
         if (!(beta > alpha * 0x1p-20f)) break;    // invariant subspace (or A = 0): T is exact
