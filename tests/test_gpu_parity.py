@@ -245,6 +245,29 @@ def test_empty_and_single_token():
         assert torch.all(out[:, :, 1:] == 0)
 
 
+def test_topk_ties_at_the_cut():
+    """Top-k with whole groups of equal scores straddling the k-th place: key
+    blocks repeat five token patterns, so every row's 48 scores take five
+    values about ten times each.  For every k the GPU lists must equal the
+    oracle's (first k in the order (-score, j): the lower index wins a tie)."""
+    import free_block_sparse_attn_amd as fbsa
+    rng = np.random.default_rng(7)
+    B, H, nb, d = 1, 2, 48, 128
+    N = 64 * nb
+    base = rng.standard_normal((5, 64, d)).astype(np.float32)
+    k_np = np.stack([base[j % 5] for j in range(nb)], axis=0).reshape(1, 1, N, d).repeat(H, axis=1)
+    q_np = rng.standard_normal((B, H, N, d)).astype(np.float32)
+    to = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    q, k = to(q_np), to(k_np)
+    pooled = fbsa.sparse_attn_pool(q, k, k, N)
+    qbar, kbar = pooled["qbar"].cpu().numpy(), pooled["kbar"].cpu().numpy()
+    for kk in (1, 9, 10, 11, 13, 19, 20, 21, 29, 38, 40, 47, 48):
+        idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=kk)
+        ri, rc = routing.route_topk(qbar, kbar, kk)
+        assert np.array_equal(cnt.cpu().numpy(), rc), kk
+        assert np.array_equal(idx.cpu().numpy()[..., :kk], ri), kk
+
+
 def test_topk_all_blocks_matches_dense():
     wl = get_workload(2, small=True)
     (q, k, v), dev, coords = gc.inputs(wl)
