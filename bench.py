@@ -7,6 +7,10 @@ blocks, seeded Fourier-plus-noise Q/K/V, top-k keeping 20% of key blocks per
 query block (103 of 512) with centroid (zeroth-order) compensation of the rest.
 
 One step = pool -> route -> fused forward on inputs already resident in HBM.
+--layer runs one of the pages' other workloads instead (Hunyuan-size layers
+with first-order compensation, covariance-aware or error-aware routing, the
+SparsePR residual pass, LVSA, Triage with an fp8 or MXFP4 skim tier) with the
+same step structure and JSON line (no CPU baseline, no traffic figure).
 The JSON line reports:
   value          kept-tile work of the layer / step time (TFLOP/s), where a
                  kept tile is 4*64*64*d flop (two 64x64xd products)
@@ -74,11 +78,46 @@ def cpu_baseline(wl, q, k, v):
                       f"route + compensated rule, fp64 numpy, {dt:.1f} s"}
 
 
+LAYERS = {
+    # name: (workload key, description)
+    "wan13b": ("wan13b", "wan13b-480p-layer: B=1 H=12 d=128 T*Y*X=21*30*52 (N=32760), "
+                         "64-token 4x4x4 tile-major blocks, top-k 20% (k=103/512), centroid compensation"),
+    "wan13b-error": ("wan13b-ear", "wan13b-480p-layer, SVG-EAR error-aware routing (k=103/512), "
+                                   "centroid compensation"),
+    "wan13b-residual": ("wan13b", "wan13b-480p-layer as the default, then the SparsePR probe-fitted "
+                                  "residual pass (rank 8)"),
+    "hunyuan-order1": ("hunyuan720p", "hunyuan720p-layer: B=1 H=24 d=128 T*Y*X=33*45*80 (N=118800), "
+                                      "top-k 10% (k=186/1857), per-block first-order (H_j) compensation"),
+    "hunyuan-global": ("hunyuan720p-global", "hunyuan720p-layer, top-k 10%, PISA global first-order "
+                                             "(H_bar) compensation"),
+    "hunyuan-global-cov": ("hunyuan720p-global-cov", "hunyuan720p-layer, covariance-aware top-k 10%, "
+                                                     "global first-order compensation"),
+    "lvsa": ("lvsa-long", "lvsa-long-layer: B=1 H=12 d=128 T*Y*X=81*30*52 (N=126360), +-2-frame window "
+                          "+ 8 rotating anchors (step 0), centroid compensation"),
+    "triage-e4m3": ("triage", "hunyuan720p-size layer, Triage tiers (refine 15% / skim 25%), fp8 e4m3 "
+                              "skim tier, centroid compensation of skipped blocks"),
+    "triage-mxfp4": ("triage-mxfp4", "as triage-e4m3 with the skim tier in MXFP4"),
+}
+
+
+def layer_workload(name):
+    from workloads import WORKLOADS
+    from workloads.configs import GLOBAL_ORDER1, GLOBAL_COV, ERROR_ROUTED, TRIAGE_FP4
+    key = LAYERS[name][0]
+    table = {"wan13b": WORKLOADS[2], "hunyuan720p": WORKLOADS[3], "lvsa-long": WORKLOADS[4],
+             "triage": WORKLOADS[5], "hunyuan720p-global": GLOBAL_ORDER1,
+             "hunyuan720p-global-cov": GLOBAL_COV, "wan13b-ear": ERROR_ROUTED, "triage-mxfp4": TRIAGE_FP4}
+    return table[key]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--layer", default="wan13b", choices=sorted(LAYERS),
+                    help="layer to run (default: the Wan-1.3B-like layer the headline metric is quoted on; "
+                         "the others are the pages' other workloads, for profiling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a 1 GiB device-to-device copy (reference for HBM byte counters)")
@@ -91,23 +130,48 @@ def main():
     import numpy as np
     import torch
     import free_block_sparse_attn_amd as fbsa
-    from workloads import WORKLOADS, make_qkv
+    from workloads import make_qkv, block_frame_ranges, lvsa_anchor_phase
 
-    wl = WORKLOADS[2]
+    wl = layer_workload(args.layer)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    q, k, v, _ = make_qkv(wl)
+    q, k, v, coords = make_qkv(wl)
     dq, dk, dv = (torch.from_numpy(x).to(torch.bfloat16).to(dev) for x in (q, k, v))
     N = wl.N
+    f4 = wl.skim_fmt == "mxfp4"
+    triage = wl.rule == "triage"
+    pool_kw = dict(moments=wl.comp == 1, global_moment=wl.comp == 2, cov=wl.rule == "topk_cov",
+                   spreads=triage, fp8=triage and not f4, fp4=triage and f4)
+    skim_fmt = fbsa.SA_SKIM_MXFP4 if f4 else fbsa.SA_SKIM_E4M3
+    scale = 1.0
 
-    pooled = fbsa.sparse_attn_pool(dq, dk, dv, N)
-    route_out = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk)
-    out, lse = fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0], route_out[1])
+    pooled = fbsa.sparse_attn_pool(dq, dk, dv, N, **pool_kw)
+    route_kw = {}
+    if wl.rule == "topk":
+        route_kw = dict(mode=fbsa.SA_ROUTE_TOPK, topk=wl.topk)
+    elif wl.rule == "topk_cov":
+        route_kw = dict(mode=fbsa.SA_ROUTE_TOPK_COV, topk=wl.topk, scale=scale)
+    elif wl.rule == "error":
+        ekey = torch.empty(wl.B, wl.H, wl.nb, wl.nb, dtype=torch.float32, device=dev)
+        route_kw = dict(mode=fbsa.SA_ROUTE_ERROR, topk=wl.topk, scale=scale, keys=dk, ekey=ekey)
+    elif wl.rule == "lvsa":
+        lo, hi = block_frame_ranges(coords)
+        cap = fbsa.sparse_attn_lvsa_capacity(lo, hi, wl.window, wl.anchors)
+        route_kw = dict(mode=fbsa.SA_ROUTE_LVSA, frame_lo=torch.from_numpy(lo).to(dev),
+                        frame_hi=torch.from_numpy(hi).to(dev), window=wl.window, anchors=wl.anchors,
+                        anchor_phase=lvsa_anchor_phase(wl.wid, wl.anchor_period), step=0, cap=cap)
+    else:
+        route_kw = dict(mode=fbsa.SA_ROUTE_TRIAGE, n_keep=wl.n_keep, n_refine=wl.n_refine, scale=scale)
+    mode = route_kw.pop("mode")
+    route_out = fbsa.sparse_attn_route(pooled, N, mode, **route_kw)
+    out, lse = fbsa.sparse_attn_fwd(dq, dk, dv, N, scale, wl.comp, pooled, *route_out, skim_fmt=skim_fmt)
+    residual = args.layer == "wan13b-residual"
+    ws = fbsa.sparse_attn_residual(dq, dk, dv, out, N, scale)["workspace"] if residual else None
     torch.cuda.synchronize()
 
     # HIP events bracket each kernel of every timed step on the current
     # stream, which is the stream the binding launches on
-    names = ("pool", "route", "fwd")
+    names = ("pool", "route", "fwd") + (("residual",) if residual else ())
     evs = {n: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)] for n in names}
 
@@ -121,9 +185,11 @@ def main():
             fn()
             e.record()
         run("pool", lambda: fbsa.sparse_attn_pool(dq, dk, dv, N, out=pooled))
-        run("route", lambda: fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=wl.topk, out=route_out))
-        run("fwd", lambda: fbsa.sparse_attn_fwd(dq, dk, dv, N, 1.0, wl.comp, pooled, route_out[0], route_out[1],
-                                                out=out, lse=lse))
+        run("route", lambda: fbsa.sparse_attn_route(pooled, N, mode, out=route_out, **route_kw))
+        run("fwd", lambda: fbsa.sparse_attn_fwd(dq, dk, dv, N, scale, wl.comp, pooled, *route_out,
+                                                out=out, lse=lse, skim_fmt=skim_fmt))
+        if residual:
+            run("residual", lambda: fbsa.sparse_attn_residual(dq, dk, dv, out, N, scale, workspace=ws))
 
     for _ in range(args.warmup):
         step()
@@ -134,11 +200,11 @@ def main():
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
     # mean launch duration of each kernel over the timed steps
-    ms_pool, ms_route, ms_fwd = (sum(s.elapsed_time(e) for s, e in evs[n]) / args.steps for n in names)
+    ms = {n: sum(s.elapsed_time(e) for s, e in evs[n]) / args.steps for n in names}
 
     cnt = route_out[1].cpu().numpy()
     kept_flop = float(cnt.sum()) * 4 * 64 * 64 * wl.d
-    fwd_tflops = kept_flop / (ms_fwd * 1e-3) / 1e12
+    fwd_tflops = kept_flop / (ms["fwd"] * 1e-3) / 1e12
     pool_bytes = 3 * dq.numel() * 2 + 3 * pooled["qbar"].numel() * 4
     route_flop = 2.0 * wl.B * wl.H * wl.nb * wl.nb * wl.d
     line = {
@@ -154,20 +220,20 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded Fourier-plus-noise video tokens)",
-        "config": {"workload": "wan13b-480p-layer: B=1 H=12 d=128 T*Y*X=21*30*52 (N=32760), "
-                               "64-token 4x4x4 tile-major blocks, top-k 20% (k=103/512), "
-                               "centroid compensation",
+        "config": {"workload": LAYERS[args.layer][1],
                    "global_batch": wl.B, "seq_len": wl.N, "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(fwd_tflops, 2), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(fwd_tflops / MFMA_BF16_PEAK_TFLOPS, 4),
-                     "traffic": kernel_traffic()},
-        "kernels_ms": {"pool": round(ms_pool, 4), "route": round(ms_route, 4), "fwd": round(ms_fwd, 4)},
-        "pool_GBps": round(pool_bytes / (ms_pool * 1e-3) / 1e9, 1),
-        "pool_hbm_frac": round(pool_bytes / (ms_pool * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "route_fp64_frac": round(route_flop / (ms_route * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4),
+                     "traffic": kernel_traffic() if args.layer == "wan13b" else None},
+        "kernels_ms": {n: round(t, 4) for n, t in ms.items()},
+        "pool_GBps": round(pool_bytes / (ms["pool"] * 1e-3) / 1e9, 1),
+        "pool_hbm_frac": round(pool_bytes / (ms["pool"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "route_fp64_frac": round(route_flop / (ms["route"] * 1e-3) / 1e12 / FP64_PEAK_TFLOPS, 4),
         "kept_tiles": int(cnt.sum()),
     }
-    if not args.no_cpu_baseline:
+    if triage:
+        line["skim_tiles"] = int(route_out[3].cpu().numpy().sum())
+    if args.layer == "wan13b" and not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, q, k, v)
     print(json.dumps(line), flush=True)
     if args.copy_calibration:
