@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "sparse_attn.h")
 
 def declared_functions():
     text = open(HEADER).read()
-    return sorted(set(re.findall(r"^\s*(?:sa_status|int32_t|const char\*)\s+(sparse_attn_\w+)\s*\(", text, re.M)))
+    return sorted(set(re.findall(r"^\s*(?:sa_status|int32_t|size_t|const char\*)\s+(sparse_attn_\w+)\s*\(", text, re.M)))
 
 
 @pytest.fixture(scope="module")
@@ -24,8 +24,21 @@ def lib():
 
 def test_header_declares_the_three_calls():
     names = declared_functions()
-    for n in ("sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd"):
+    for n in ("sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_residual",
+              "sparse_attn_residual_workspace"):
         assert n in names
+
+
+def test_missing_library_raises():
+    """No fallback: with the library absent, the first call raises."""
+    import subprocess
+    import sys
+    env = dict(os.environ, SPARSE_ATTN_LIB=os.path.join(ROOT, "_no_such_dir", "libsparse_attn.so"))
+    code = ("import free_block_sparse_attn_amd as f\n"
+            "try:\n    f.abi_version()\nexcept RuntimeError as e:\n    print('raised:', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert "raised:" in r.stdout and "missing" in r.stdout, r.stdout
 
 
 def test_library_exports_every_declared_symbol(lib):
