@@ -124,6 +124,7 @@ struct ResidualArgs {
     float* od;                // [B,H,Mp,d] dense output at the probes
     float* wc;                // [B,H,d*d + d] W, c
     uint16_t* qp;             // [B,H,Mp,d] gathered probe queries
+    float* zv;                // [B,H,2,d,8] the factors Z and V_r of W = Z V_r^T
 };
 size_t residual_workspace_bytes(int B, int H, int N_pad);
 void residual_carve(ResidualArgs& r, void* ws);

@@ -15,14 +15,16 @@
 //                            combine_kernel merges the chunks by their lse
 //   3. gram_kernel           fp64 partial sums of X^T X, X^T R, R^T R and the
 //                            column sums over slices of the probes
-//   4. fit_kernel            one workgroup per head: fixed-order reduction,
-//                            centring, ridge, the top-r subspace V_r of R^T R
-//                            (simultaneous iteration with Cholesky QR), then
-//                            W = B P = G^{-1} (C V_r) V_r^T by a
-//                            Cholesky solve with r right-hand sides (fp64,
-//                            packed in LDS) and c = b P = rm P - xm W (fp32 out)
-//   5. apply_kernel          o_t <- o_t + c + o_t W on every valid row, the
-//                            dense output on probe rows (bf16, in place)
+//   4. reduce_kernel         the partial sums in a fixed order, centred
+//      fit_kernel            one workgroup per head: ridge, the top-r
+//                            subspace V_r of R^T R (simultaneous iteration
+//                            with Cholesky QR), Z = (G + lambda I)^{-1} C V_r
+//                            by an LDL^T elimination that carries the r
+//                            right-hand sides, then W = Z V_r^T,
+//                            c = (rm V_r - xm Z) V_r^T and the fp32 factors
+//   5. apply_kernel          o_t <- o_t + c + (o_t Z) V_r^T on every valid
+//                            row, the dense output on probe rows (bf16, in
+//                            place)
 #include "common.h"
 #include "launch.h"
 
@@ -133,280 +135,493 @@ __global__ __launch_bounds__(THREADS) void gram_kernel(ResidualArgs r) {
     if (m == 1) P[3 * D * D + tid] = colsum;      // x sums then r sums
 }
 
-// One thread: Cholesky of the KSUB x KSUB SPD matrix A (row-major) into its
-// lower triangle, in registers.
-__device__ void chol_small(double* A) {
-    double a[KSUB][KSUB];
-#pragma unroll
-    for (int i = 0; i < KSUB; ++i)
-#pragma unroll
-        for (int j = 0; j < KSUB; ++j) a[i][j] = A[i * KSUB + j];
-#pragma unroll
-    for (int k = 0; k < KSUB; ++k) {
-        double d = a[k][k];
-#pragma unroll
-        for (int t = 0; t < k; ++t) d -= a[k][t] * a[k][t];
-        d = sqrt(fmax(d, 1e-300));
-        a[k][k] = d;
-#pragma unroll
-        for (int i = k + 1; i < KSUB; ++i) {
-            double v = a[i][k];
-#pragma unroll
-            for (int t = 0; t < k; ++t) v -= a[i][t] * a[k][t];
-            a[i][k] = v / d;
-        }
+// ---- 4a. reduce the Gram partial sums in a fixed order and centre ----
+// Workgroup (chunk, head): 4 entries per thread of the three d x d matrices;
+// the column sums give the probe means xm, rm.
+constexpr int RED_PER_WG = 4 * THREADS;
+constexpr size_t PSTRIDE = 3 * D * D + 2 * D;   // doubles per slice of the partial sums
+static_assert(3 * D * D % RED_PER_WG == 0 && THREADS == 2 * D, "reduce tiling");
+
+__global__ __launch_bounds__(THREADS) void reduce_kernel(ResidualArgs r) {
+    __shared__ double xm[D], rm[D];
+    const size_t bh = blockIdx.y;
+    const int tid = threadIdx.x;
+    const double M = static_cast<double>(r.N_pad / BLK);
+    const double* P = r.part + bh * NSPLIT * PSTRIDE;
+    {
+        double v = 0.0;
+        for (int s = 0; s < NSPLIT; ++s) v += P[s * PSTRIDE + 3 * D * D + tid];
+        if (tid < D) xm[tid] = v / M;
+        else rm[tid - D] = v / M;
     }
+    __syncthreads();
+    double* G = r.mat + bh * 3 * D * D;
 #pragma unroll
-    for (int i = 0; i < KSUB; ++i)
+    for (int u = 0; u < 4; ++u) {
+        const int e = blockIdx.x * RED_PER_WG + u * THREADS + tid;
+        double v = 0.0;
 #pragma unroll
-        for (int j = 0; j <= i; ++j) A[i * KSUB + j] = a[i][j];
+        for (int s = 0; s < NSPLIT; ++s) v += P[s * PSTRIDE + e];
+        const int m = e / (D * D), i = (e / D) % D, j = e % D;
+        if (m == 0) v -= M * xm[i] * xm[j];
+        else if (m == 1) v -= M * xm[i] * rm[j];
+        G[e] = v;
+    }
 }
 
-// ---- 4. fit: one workgroup per head ----
-// With V_r the top right singular vectors of R, W = B P = G^{-1} (C V_r) V_r^T
-// and c = b P = rm P - xm W, so only `rank` right-hand sides are solved.
+// ---- 4b. fit: one workgroup per head ----
+typedef __attribute__((ext_vector_type(2))) double f64x2;
+
 __device__ __forceinline__ double wave_sum(double x) {
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
     return x;
 }
 
-__global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
-    constexpr int LP = D * (D + 1) / 2;            // packed lower triangle, row i at i (i + 1) / 2
-    __shared__ double Lp[LP];
-    __shared__ double Qs[D * KSUB], Ys[D * KSUB];  // subspace blocks; later V_r, C V_r / solutions
-    __shared__ double xm[D], rm[D];
-    __shared__ double small[KSUB * KSUB];
-    __shared__ double red[THREADS / 64];
-    const size_t bh = blockIdx.x;
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int nb = r.N_pad / BLK;
-    const double M = static_cast<double>(nb);
-    double* G = r.mat + bh * 3 * D * D;           // X^T X, then centred
-    double* C = G + D * D;                        // X^T R, then centred
-    double* S = C + D * D;                        // R^T R
-    // reduce the partial sums in a fixed order
-    const double* P = r.part + bh * NSPLIT * (3 * D * D + 2 * D);
-    for (int e = tid; e < 3 * D * D + 2 * D; e += THREADS) {
-        double v = 0.0;
-        for (int s = 0; s < NSPLIT; ++s) v += P[static_cast<size_t>(s) * (3 * D * D + 2 * D) + e];
-        if (e < 3 * D * D) G[e] = v;
-        else if (e < 3 * D * D + D) xm[e - 3 * D * D] = v / M;
-        else rm[e - 3 * D * D - D] = v / M;
-    }
-    __syncthreads();
-    double tr = 0.0;
-    for (int e = tid; e < D * D; e += THREADS) {
-        const int i = e / D, j = e % D;
-        G[e] -= M * xm[i] * xm[j];
-        C[e] -= M * xm[i] * rm[j];
-        if (i == j) tr += G[e];
-    }
-    tr = wave_sum(tr);
-    if (lane == 0) red[wv] = tr;
-    __syncthreads();
-    const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
+// 1/x and 1/sqrt(x) for normal x > 0: the hardware estimate and two Newton steps
+__device__ __forceinline__ double rcp64(double x) {
+    double y = __builtin_amdgcn_rcp(x);
+    y = fma(y, fma(-x, y, 1.0), y);
+    y = fma(y, fma(-x, y, 1.0), y);
+    return y;
+}
+__device__ __forceinline__ double rsq64(double x) {
+    double y = __builtin_amdgcn_rsq(x);
+    const double h = 0.5 * x;
+    y = y * fma(-h * y, y, 1.5);
+    y = y * fma(-h * y, y, 1.5);
+    return y;
+}
 
-    // ---- top-rank subspace of S = R^T R: simultaneous iteration on KSUB
-    // columns; after Cholesky QR the first j columns span the leading
-    // j-dimensional invariant subspace in the limit, so the first `rank`
-    // columns are taken as V_r.  S sits in LDS as fp32 (the space the
-    // Cholesky factor takes afterwards). ----
-    float* Sf = reinterpret_cast<float*>(Lp);
-    static_assert(sizeof(Lp) >= D * D * sizeof(float), "S fits the factor's space");
-    for (int e = tid; e < D * D; e += THREADS) Sf[e] = static_cast<float>(S[e]);
-    double* Q = Qs;
-    double* Y = Ys;
-    double* Gs = small;
-    for (int e = tid; e < D * KSUB; e += THREADS) {
-        const int i = e / KSUB, c = e % KSUB;
-        Q[e] = static_cast<double>(((i * 7 + c * 13 + 3) % 17) - 8) + (i == c ? 16.0 : 0.0);
-    }
-    __syncthreads();
-    auto cholqr = [&](int reps) __attribute__((always_inline)) {     // Q <- Q L^{-T}
-        for (int rep = 0; rep < reps; ++rep) {
-            {
-                // Gram entry tid / 4 over rows 32 (tid % 4) .. + 31, four lanes combined
-                const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = 32 * (tid & 3);
-                double v = 0.0;
-                for (int i = i0; i < i0 + 32; ++i) v += Q[i * KSUB + a] * Q[i * KSUB + b];
-                v += __shfl_xor(v, 1);
-                v += __shfl_xor(v, 2);
-                if ((tid & 3) == 0) Gs[g] = v;
-            }
-            __syncthreads();
-            if (tid == 0) chol_small(Gs);
-            __syncthreads();
-            if (tid < D) {
-                double row[KSUB];
+__device__ __forceinline__ double readlane64(double v, int lane) {
+    const unsigned long long b = static_cast<unsigned long long>(__double_as_longlong(v));
+    const unsigned lo = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b & 0xFFFFFFFFull), lane));
+    const unsigned hi = static_cast<unsigned>(__builtin_amdgcn_readlane(static_cast<int>(b >> 32), lane));
+    return __longlong_as_double(static_cast<long long>((static_cast<unsigned long long>(hi) << 32) | lo));
+}
+
+// From the KSUB x KSUB Gram matrix (row-major), the inverse Mi = L^{-1} of
+// its Cholesky factor (lower triangle of Mi).  Every thread computes it.
+__device__ __forceinline__ void chol_inv8(const double* Gs, double (&Mi)[KSUB][KSUB]) {
+    double L[KSUB][KSUB], rs[KSUB];
 #pragma unroll
-                for (int c = 0; c < KSUB; ++c) {
-                    double v = Q[tid * KSUB + c];
+    for (int i = 0; i < KSUB; ++i)
 #pragma unroll
-                    for (int t = 0; t < c; ++t) v -= row[t] * Gs[c * KSUB + t];
-                    row[c] = v / Gs[c * KSUB + c];
-                }
+        for (int j = 0; j <= i; ++j) L[i][j] = Gs[i * KSUB + j];
 #pragma unroll
-                for (int c = 0; c < KSUB; ++c) Q[tid * KSUB + c] = row[c];
-            }
-            __syncthreads();
+    for (int k = 0; k < KSUB; ++k) {
+        double d = L[k][k];
+#pragma unroll
+        for (int t = 0; t < k; ++t) d = fma(-L[k][t], L[k][t], d);
+        rs[k] = rsq64(fmax(d, 1e-300));                   // 1 / L_kk
+#pragma unroll
+        for (int i = k + 1; i < KSUB; ++i) {
+            double v = L[i][k];
+#pragma unroll
+            for (int t = 0; t < k; ++t) v = fma(-L[i][t], L[k][t], v);
+            L[i][k] = v * rs[k];
         }
-    };
-    static_assert(KSUB * KSUB * 4 == THREADS, "one Gram entry per four threads");
-    cholqr(2);
-    for (int it = 0; it < SUB_ITERS; ++it) {
-        for (int e = tid; e < D * KSUB; e += THREADS) {      // Y = S Q
-            const int i = e / KSUB, c = e % KSUB;
-            const float* srow = Sf + i * D;
+    }
+#pragma unroll
+    for (int i = 0; i < KSUB; ++i) {
+        Mi[i][i] = rs[i];
+#pragma unroll
+        for (int j = 0; j < i; ++j) {
             double v = 0.0;
-            for (int l = 0; l < D; ++l) v += static_cast<double>(srow[l]) * Q[l * KSUB + c];
-            Y[e] = v;
+#pragma unroll
+            for (int t = j; t < i; ++t) v = fma(L[i][t], Mi[t][j], v);
+            Mi[i][j] = -v * rs[i];
         }
-        __syncthreads();
-        for (int e = tid; e < D * KSUB; e += THREADS) Q[e] = Y[e];
-        __syncthreads();
-        cholqr(it + 1 < SUB_ITERS ? 1 : 2);
-    }
-    const int rk = r.rank;
-    // V_r = the first rank columns of Q, into Y (stride KSUB)
-    for (int e = tid; e < D * KSUB; e += THREADS) Y[e] = (e % KSUB) < rk ? Q[e] : 0.0;
-    __syncthreads();
-    // T = C V_r into Q (the right-hand sides)
-    for (int e = tid; e < D * KSUB; e += THREADS) {
-        const int i = e / KSUB, c = e % KSUB;
-        double v = 0.0;
-        if (c < rk)
-            for (int l = 0; l < D; ++l) v += C[i * D + l] * Y[l * KSUB + c];
-        Q[e] = v;
-    }
-    __syncthreads();
-
-    // ---- Cholesky of G + lambda I, packed lower triangle in LDS ----
-    for (int e = tid; e < D * D; e += THREADS) {
-        const int i = e / D, j = e % D;
-        if (j <= i) Lp[i * (i + 1) / 2 + j] = G[e] + (i == j ? lam : 0.0);
-    }
-    __syncthreads();
-    for (int k = 0; k < D; ++k) {
-        const int kk = k * (k + 1) / 2 + k;
-        if (tid == 0) Lp[kk] = sqrt(fmax(Lp[kk], 1e-300));
-        __syncthreads();
-        const double inv = 1.0 / Lp[kk];
-        for (int i = k + 1 + tid; i < D; i += THREADS) Lp[i * (i + 1) / 2 + k] *= inv;
-        __syncthreads();
-        // trailing update: a thread pair per row i > k, alternate columns j <= i
-        const int i = k + 1 + (tid >> 1);
-        if (i < D) {
-            const int ri = i * (i + 1) / 2;
-            const double lik = Lp[ri + k];
-            for (int j = k + 1 + (tid & 1); j <= i; j += 2) Lp[ri + j] -= lik * Lp[j * (j + 1) / 2 + k];
-        }
-        __syncthreads();
-    }
-    // ---- solve (G + lambda I) Z = T for the rank columns: wave w takes columns
-    // w, w + 4, ...; each row's dot product is spread over the 64 lanes ----
-    for (int c = wv; c < rk; c += THREADS / 64) {
-        for (int i = 0; i < D; ++i) {                        // forward: L y = t (in place in Q)
-            const double* li = Lp + i * (i + 1) / 2;
-            double part = 0.0;
-            for (int t = lane; t < i; t += 64) part += li[t] * Q[t * KSUB + c];
-            part = wave_sum(part);
-            if (lane == 0) Q[i * KSUB + c] = (Q[i * KSUB + c] - part) / li[i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-        for (int i = D - 1; i >= 0; --i) {                   // backward: L^T z = y
-            double part = 0.0;
-            for (int t = i + 1 + lane; t < D; t += 64) part += Lp[t * (t + 1) / 2 + i] * Q[t * KSUB + c];
-            part = wave_sum(part);
-            if (lane == 0) Q[i * KSUB + c] = (Q[i * KSUB + c] - part) / Lp[i * (i + 1) / 2 + i];
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        }
-    }
-    __syncthreads();
-    // W = Z V_r^T (fp32 out); c = rm P - xm W
-    float* Wo = r.wc + bh * (D * D + D);
-    for (int e = tid; e < D * D; e += THREADS) {
-        const int i = e / D, j = e % D;
-        double v = 0.0;
-        for (int c = 0; c < rk; ++c) v += Q[i * KSUB + c] * Y[j * KSUB + c];
-        Wo[e] = static_cast<float>(v);
-        G[e] = v;                                          // W kept in fp64 for c
-    }
-    __syncthreads();
-    if (tid < D) {
-        double rp = 0.0;
-        for (int c = 0; c < rk; ++c) {
-            double t = 0.0;
-            for (int l = 0; l < D; ++l) t += rm[l] * Y[l * KSUB + c];
-            rp += t * Y[tid * KSUB + c];
-        }
-        double xw = 0.0;
-        for (int i = 0; i < D; ++i) xw += xm[i] * G[i * D + tid];
-        Wo[D * D + tid] = static_cast<float>(rp - xw);
     }
 }
 
-// ---- 5. apply: 64 rows per workgroup, W in LDS; thread = 4 rows x 8 columns ----
-constexpr int APPLY_ROWS = 64;
-__global__ __launch_bounds__(THREADS) void apply_kernel(ResidualArgs r) {
-    __shared__ __attribute__((aligned(16))) float w_s[D * D];
-    __shared__ __attribute__((aligned(16))) float xt_s[D * APPLY_ROWS];    // transposed: [i][row]
-    __shared__ float c_s[D];
-    const size_t bh = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int row0 = blockIdx.x * APPLY_ROWS;
-    const float* Wg = r.wc + bh * (D * D + D);
-    for (int e = 4 * tid; e < D * D; e += 4 * THREADS)
-        *reinterpret_cast<f32x4*>(w_s + e) = *reinterpret_cast<const f32x4*>(Wg + e);
-    if (tid < D) c_s[tid] = Wg[D * D + tid];
-    uint16_t* O = static_cast<uint16_t*>(r.out) + bh * r.N_pad * D;
-    for (int e = tid; e < APPLY_ROWS * D / 8; e += THREADS) {
-        const int rr = e / (D / 8), c0 = (e % (D / 8)) * 8;
-        const u32x4 v = *reinterpret_cast<const u32x4*>(O + static_cast<size_t>(row0 + rr) * D + c0);
+// Columns 16 KB .. 16 KB + 15 of the right-looking LDL^T elimination.
+// Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b and, in
+// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Column k arrives in
+// col[k % 2]; its owners (q == (k + 1) % 16) publish column k + 1 into the
+// other buffer after updating it.  Entries of rows <= k or columns <= k are
+// left alone (their multipliers are zero); blocks left of column block KB are
+// finished and skipped.
+template <int KB>
+__device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (*col)[D + KSUB], int p, int q) {
+#pragma unroll 1
+    for (int kk = 0; kk < 16; ++kk) {
+        const int k = 16 * KB + kk;
+        const double* ck = col[k & 1];
+        const double rinv = rcp64(fmax(ck[k], 1e-300));
+        double x[9], u[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            xt_s[(c0 + 2 * u) * APPLY_ROWS + rr] = bf16_to_f32(static_cast<uint16_t>(v[u] & 0xFFFFu));
-            xt_s[(c0 + 2 * u + 1) * APPLY_ROWS + rr] = bf16_to_f32(static_cast<uint16_t>(v[u] >> 16));
+        for (int a = KB; a < 8; ++a) x[a] = 16 * a + p > k ? ck[16 * a + p] : 0.0;
+        x[8] = p < KSUB ? ck[D + p] : 0.0;
+#pragma unroll
+        for (int b = KB; b < 8; ++b) u[b] = 16 * b + q > k ? ck[16 * b + q] * rinv : 0.0;
+#pragma unroll
+        for (int b = KB; b < 8; ++b)
+#pragma unroll
+            for (int a = b; a < 9; ++a) A[a][b] = fma(-x[a], u[b], A[a][b]);
+        if (k + 1 < D && q == ((k + 1) & 15)) {
+            double* cn = col[(k + 1) & 1];
+            constexpr int NB = KB < 7 ? KB + 1 : KB;
+            if (kk < 15) {
+#pragma unroll
+                for (int a = KB; a < 8; ++a) cn[16 * a + p] = A[a][KB];
+                if (p < KSUB) cn[D + p] = A[8][KB];
+            } else {
+#pragma unroll
+                for (int a = NB; a < 8; ++a) cn[16 * a + p] = A[a][NB];
+                if (p < KSUB) cn[D + p] = A[8][NB];
+            }
+        }
+        __syncthreads();
+    }
+}
+
+// With V_r the top right singular vectors of R, W = B P = Z V_r^T with
+// Z = (G + lambda I)^{-1} (C V_r), and c = b P = (rm V_r - xm Z) V_r^T, so
+// only `rank` right-hand sides are solved.  Stages:
+//   * simultaneous iteration on S = R^T R (fp32 copy in LDS, fp64 products),
+//     KSUB columns, Cholesky QR after every product;
+//   * T = C V_r;
+//   * LDL^T of G + lambda I by right-looking elimination in registers, thread
+//     (p, q) of a 16 x 16 grid holding the entries (16 a + p, 16 b + q), with
+//     T^T appended as KSUB extra rows so that the eliminated rows are L^{-1} T;
+//     one barrier per column, the column published through LDS;
+//   * back substitution with the unit upper factor, a wave per two columns,
+//     the pivot row's values read across lanes;
+//   * W, c, and the factors Z, V_r (fp32) for the apply pass.
+__global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
+    constexpr int SP = D + 4;                               // fp32 row stride of S in LDS
+    constexpr int LPK = D * (D + 1) / 2;                    // packed lower triangle, row i at i (i + 1) / 2
+    constexpr int POOL = (D * SP / 2 > LPK) ? D * SP / 2 : LPK;
+    __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32), later the factor
+    __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB], B2[D * KSUB];
+    __shared__ double col[2][D + KSUB];
+    __shared__ double xm[D], rm[D];
+    __shared__ double Gs[KSUB * KSUB];
+    __shared__ double red[THREADS / 64], s8[KSUB];
+    const size_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int rk = r.rank;
+    const double M = static_cast<double>(r.N_pad / BLK);
+    const double* P = r.part + bh * NSPLIT * PSTRIDE;
+    const double* G = r.mat + bh * 3 * D * D;              // centred X^T X
+    const double* C = G + D * D;                           // centred X^T R
+    const double* S = C + D * D;                           // R^T R
+    {
+        double v = 0.0;
+        for (int s = 0; s < NSPLIT; ++s) v += P[s * PSTRIDE + 3 * D * D + tid];
+        if (tid < D) xm[tid] = v / M;
+        else rm[tid - D] = v / M;
+    }
+    {
+        double tr = tid < D ? G[tid * (D + 1)] : 0.0;
+        tr = wave_sum(tr);
+        if (lane == 0) red[wv] = tr;
+    }
+    float* Sf = reinterpret_cast<float*>(pool);
+    for (int e = tid; e < D * D; e += THREADS) Sf[(e / D) * SP + e % D] = static_cast<float>(S[e]);
+    for (int e = tid; e < D * KSUB; e += THREADS) {
+        const int i = e / KSUB, c = e % KSUB;
+        B0[e] = static_cast<double>(((i * 7 + c * 13 + 3) % 17) - 8) + (i == c ? 16.0 : 0.0);
+    }
+    __syncthreads();
+    const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
+
+    // ---- top-rank subspace of S ----
+    const int ri = tid >> 1, rc = 4 * (tid & 1);           // row, first of four columns
+    auto cholqr = [&](const double* Yin, double* Qout) __attribute__((always_inline)) {
+        {   // Gram entry tid / 4 over rows 32 (tid % 4) .. + 31, four lanes combined
+            const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = 32 * (tid & 3);
+            double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+#pragma unroll
+            for (int i = i0; i < i0 + 32; i += 4) {
+                v0 = fma(Yin[i * KSUB + a], Yin[i * KSUB + b], v0);
+                v1 = fma(Yin[(i + 1) * KSUB + a], Yin[(i + 1) * KSUB + b], v1);
+                v2 = fma(Yin[(i + 2) * KSUB + a], Yin[(i + 2) * KSUB + b], v2);
+                v3 = fma(Yin[(i + 3) * KSUB + a], Yin[(i + 3) * KSUB + b], v3);
+            }
+            double v = (v0 + v1) + (v2 + v3);
+            v += __shfl_xor(v, 1);
+            v += __shfl_xor(v, 2);
+            if ((tid & 3) == 0) Gs[g] = v;
+        }
+        __syncthreads();
+        double Mi[KSUB][KSUB];
+        chol_inv8(Gs, Mi);
+        double y[KSUB];
+#pragma unroll
+        for (int t = 0; t < KSUB; t += 2) {
+            const f64x2 w = *reinterpret_cast<const f64x2*>(Yin + ri * KSUB + t);
+            y[t] = w[0];
+            y[t + 1] = w[1];
+        }
+#pragma unroll
+        for (int cc = 0; cc < 4; ++cc) {                     // q_c = sum_{t <= c} Mi[c][t] y_t
+            double v = 0.0;
+#pragma unroll
+            for (int c = 0; c < KSUB; ++c)
+                if (c == rc + cc) {
+#pragma unroll
+                    for (int t = 0; t <= c; ++t) v = fma(Mi[c][t], y[t], v);
+                }
+            Qout[ri * KSUB + rc + cc] = v;
+        }
+        __syncthreads();
+    };
+    auto product = [&](const double* Q, double* Y) __attribute__((always_inline)) {   // Y = S Q
+        const float* srow = Sf + ri * SP;
+        double y0 = 0.0, y1 = 0.0, y2 = 0.0, y3 = 0.0;
+#pragma unroll 2
+        for (int m = 0; m < D; m += 4) {
+            const f32x4 s4 = *reinterpret_cast<const f32x4*>(srow + m);
+#pragma unroll
+            for (int mm = 0; mm < 4; ++mm) {
+                const double sv = static_cast<double>(s4[mm]);
+                const f64x2 qa = *reinterpret_cast<const f64x2*>(Q + (m + mm) * KSUB + rc);
+                const f64x2 qb = *reinterpret_cast<const f64x2*>(Q + (m + mm) * KSUB + rc + 2);
+                y0 = fma(sv, qa[0], y0);
+                y1 = fma(sv, qa[1], y1);
+                y2 = fma(sv, qb[0], y2);
+                y3 = fma(sv, qb[1], y3);
+            }
+        }
+        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc) = f64x2{y0, y1};
+        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc + 2) = f64x2{y2, y3};
+        __syncthreads();
+    };
+    cholqr(B0, B1);
+    cholqr(B1, B0);
+    for (int it = 0; it < SUB_ITERS; ++it) {
+        product(B0, B1);
+        cholqr(B1, B0);
+    }
+    cholqr(B0, B1);                                        // V: the first rank columns of B1
+    double* V = B1;
+    for (int e = tid; e < D * KSUB; e += THREADS)
+        if (e % KSUB >= rk) V[e] = 0.0;
+    __syncthreads();
+
+    // ---- T = C V_r into B2 ----
+    {
+        const double* crow = C + ri * D;
+        double t0 = 0.0, t1 = 0.0, t2 = 0.0, t3 = 0.0;
+#pragma unroll 4
+        for (int l = 0; l < D; l += 2) {
+            const f64x2 cv = *reinterpret_cast<const f64x2*>(crow + l);
+#pragma unroll
+            for (int ll = 0; ll < 2; ++ll) {
+                const f64x2 va = *reinterpret_cast<const f64x2*>(V + (l + ll) * KSUB + rc);
+                const f64x2 vb = *reinterpret_cast<const f64x2*>(V + (l + ll) * KSUB + rc + 2);
+                t0 = fma(cv[ll], va[0], t0);
+                t1 = fma(cv[ll], va[1], t1);
+                t2 = fma(cv[ll], vb[0], t2);
+                t3 = fma(cv[ll], vb[1], t3);
+            }
+        }
+        *reinterpret_cast<f64x2*>(B2 + ri * KSUB + rc) = f64x2{t0, t1};
+        *reinterpret_cast<f64x2*>(B2 + ri * KSUB + rc + 2) = f64x2{t2, t3};
+    }
+    __syncthreads();
+
+    // ---- LDL^T of G + lambda I with T^T as rows D .. D + KSUB - 1 ----
+    double* Lp = pool;
+    {
+        const int p = tid >> 4, q = tid & 15;
+        double A[9][8];                                    // a >= b used; a = 8: row D + p
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const int i = 16 * a + p, j = 16 * b + q;
+                A[a][b] = i >= j ? G[i * D + j] + (i == j ? lam : 0.0) : 0.0;
+            }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) A[8][b] = p < KSUB ? B2[(16 * b + q) * KSUB + p] : 0.0;
+        if (q == 0) {
+#pragma unroll
+            for (int a = 0; a < 8; ++a) col[0][16 * a + p] = A[a][0];
+            if (p < KSUB) col[0][D + p] = A[8][0];
+        }
+        __syncthreads();
+        ldl_columns<0>(A, col, p, q);
+        ldl_columns<1>(A, col, p, q);
+        ldl_columns<2>(A, col, p, q);
+        ldl_columns<3>(A, col, p, q);
+        ldl_columns<4>(A, col, p, q);
+        ldl_columns<5>(A, col, p, q);
+        ldl_columns<6>(A, col, p, q);
+        ldl_columns<7>(A, col, p, q);
+        // the factor (stored column k = L_.k D_kk) and the eliminated rows y = L^{-1} T
+#pragma unroll
+        for (int a = 0; a < 8; ++a)
+#pragma unroll
+            for (int b = 0; b <= a; ++b) {
+                const int i = 16 * a + p, j = 16 * b + q;
+                if (i >= j) Lp[i * (i + 1) / 2 + j] = A[a][b];
+            }
+        if (p < KSUB) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) B0[(16 * b + q) * KSUB + p] = A[8][b];
         }
     }
     __syncthreads();
-    const int rg = tid >> 4, c0 = 8 * (tid & 15);              // rows 4 rg .. 4 rg + 3
-    float acc[4][8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 8; ++u) acc[q][u] = xt_s[(c0 + u) * APPLY_ROWS + 4 * rg + q] + c_s[c0 + u];
-#pragma unroll 4
-    for (int i = 0; i < D; ++i) {
-        const f32x4 x4 = *reinterpret_cast<const f32x4*>(xt_s + i * APPLY_ROWS + 4 * rg);
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(w_s + i * D + c0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(w_s + i * D + c0 + 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                acc[q][u] = fmaf(x4[q], w0[u], acc[q][u]);
-                acc[q][u + 4] = fmaf(x4[q], w1[u], acc[q][u + 4]);
+
+    // ---- back substitution L^T Z = D^{-1} y: wave w solves columns 2w, 2w + 1 ----
+    {
+        const int c0 = 2 * wv, j0 = 2 * lane;              // lane: rows j0, j0 + 1
+        if (c0 < rk) {
+            double u00 = B0[j0 * KSUB + c0], u01 = B0[j0 * KSUB + c0 + 1];
+            double u10 = B0[(j0 + 1) * KSUB + c0], u11 = B0[(j0 + 1) * KSUB + c0 + 1];
+            const double rd0 = rcp64(fmax(Lp[j0 * (j0 + 1) / 2 + j0], 1e-300));
+            const double rd1 = rcp64(fmax(Lp[(j0 + 1) * (j0 + 2) / 2 + j0 + 1], 1e-300));
+#pragma unroll 2
+            for (int i = D - 1; i >= 0; --i) {
+                const int o = i >> 1;
+                const bool odd = i & 1;
+                const double rdi = readlane64(odd ? rd1 : rd0, o);
+                const double z0 = readlane64(odd ? u10 : u00, o) * rdi;
+                const double z1 = readlane64(odd ? u11 : u01, o) * rdi;
+                const double* li = Lp + i * (i + 1) / 2;
+                const double l0 = j0 < i ? li[j0] : 0.0;
+                const double l1 = j0 + 1 < i ? li[j0 + 1] : 0.0;
+                u00 = fma(-l0, z0, u00);
+                u01 = fma(-l0, z1, u01);
+                u10 = fma(-l1, z0, u10);
+                u11 = fma(-l1, z1, u11);
             }
+            *reinterpret_cast<f64x2*>(B2 + j0 * KSUB + c0) = f64x2{u00 * rd0, u01 * rd0};
+            *reinterpret_cast<f64x2*>(B2 + (j0 + 1) * KSUB + c0) = f64x2{u10 * rd1, u11 * rd1};
         }
     }
+    __syncthreads();
+
+    // ---- outputs: Z (B2) and V_r (B1), W = Z V_r^T, c = (rm V_r - xm Z) V_r^T ----
+    const double* Z = B2;
+    float* zvo = r.zv + bh * 2 * D * KSUB;
+    for (int e = tid; e < D * KSUB; e += THREADS) {
+        zvo[e] = static_cast<float>(Z[e]);
+        zvo[D * KSUB + e] = static_cast<float>(V[e]);
+    }
+    float* Wo = r.wc + bh * (D * D + D);
+    {
+        double zr[KSUB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int row = row0 + 4 * rg + q;
-        const int a = row / BLK;
-        if (row < r.N && row == probe_row(a, r.N, r.phase)) {
-            const float* od = r.od + (bh * r.Mp + a) * D + c0;
+        for (int t = 0; t < KSUB; ++t) zr[t] = Z[ri * KSUB + t];
+        const int j0 = 64 * (tid & 1);
+#pragma unroll 2
+        for (int j = j0; j < j0 + 64; j += 4) {
+            f32x4 w;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) acc[q][u] = od[u];
+            for (int jj = 0; jj < 4; ++jj) {
+                double v = 0.0;
+#pragma unroll
+                for (int t = 0; t < KSUB; ++t) v = fma(zr[t], V[(j + jj) * KSUB + t], v);
+                w[jj] = static_cast<float>(v);
+            }
+            *reinterpret_cast<f32x4*>(Wo + ri * D + j) = w;
         }
-        u32x4 w;
+    }
+    {
+        const int t = tid >> 5, part = tid & 31;
+        double v = 0.0;
+        for (int l = part; l < D; l += 32) v += rm[l] * V[l * KSUB + t] - xm[l] * Z[l * KSUB + t];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = row < r.N ? pack_bf16x2(acc[q][2 * u], acc[q][2 * u + 1]) : 0u;
-        *reinterpret_cast<u32x4*>(O + static_cast<size_t>(row) * D + c0) = w;
+        for (int off = 16; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+        if (part == 0) s8[t] = v;
+    }
+    __syncthreads();
+    if (tid < D) {
+        double v = 0.0;
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) v = fma(s8[t], V[tid * KSUB + t], v);
+        Wo[D * D + tid] = static_cast<float>(v);
+    }
+}
+
+// ---- 5. apply: o <- o + c + (o Z) V_r^T; a row per 16 lanes, 8 columns per lane ----
+constexpr int APPLY_ROWS = 256;                     // rows per workgroup
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+// sum over the 16 lanes of a DPP row: quad swaps, then the half-row and row mirrors
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f32<0xB1>(x);
+    x += dpp_f32<0x4E>(x);
+    x += dpp_f32<0x141>(x);
+    x += dpp_f32<0x140>(x);
+    return x;
+}
+
+__global__ __launch_bounds__(THREADS) void apply_kernel(ResidualArgs r) {
+    constexpr int RU = 4;                           // rows in flight per lane group
+    const size_t bh = blockIdx.y;
+    const int tid = threadIdx.x, c0 = 8 * (tid & 15), g = tid >> 4;
+    const float* zv = r.zv + bh * 2 * D * KSUB;
+    const float* cg = r.wc + bh * (D * D + D) + D * D;
+    float z[8][KSUB], vr[8][KSUB], cc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+#pragma unroll
+        for (int h = 0; h < KSUB; h += 4) {
+            const f32x4 a = *reinterpret_cast<const f32x4*>(zv + (c0 + u) * KSUB + h);
+            const f32x4 b = *reinterpret_cast<const f32x4*>(zv + D * KSUB + (c0 + u) * KSUB + h);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                z[u][h + e] = a[e];
+                vr[u][h + e] = b[e];
+            }
+        }
+        cc[u] = cg[c0 + u];
+    }
+    uint16_t* O = static_cast<uint16_t*>(r.out) + bh * r.N_pad * D;
+    for (int base = blockIdx.x * APPLY_ROWS; base < (blockIdx.x + 1) * APPLY_ROWS; base += RU * (THREADS / 16)) {
+        u32x4 w[RU];
+#pragma unroll
+        for (int s = 0; s < RU; ++s) {
+            const int row = base + g + s * (THREADS / 16);
+            w[s] = row < r.N_pad ? *reinterpret_cast<const u32x4*>(O + static_cast<size_t>(row) * D + c0)
+                                 : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int s = 0; s < RU; ++s) {
+            const int row = base + g + s * (THREADS / 16);
+            float o[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                o[2 * e] = bf16_to_f32(static_cast<uint16_t>(w[s][e] & 0xFFFFu));
+                o[2 * e + 1] = bf16_to_f32(static_cast<uint16_t>(w[s][e] >> 16));
+            }
+            float sv[KSUB];
+#pragma unroll
+            for (int t = 0; t < KSUB; ++t) {
+                float a = 0.0f;
+#pragma unroll
+                for (int u = 0; u < 8; ++u) a = fmaf(o[u], z[u][t], a);
+                sv[t] = row16_sum(a);
+            }
+            float res[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                float a = o[u] + cc[u];
+#pragma unroll
+                for (int t = 0; t < KSUB; ++t) a = fmaf(sv[t], vr[u][t], a);
+                res[u] = a;
+            }
+            if (row < r.N_pad) {
+                const int blk = row / BLK;
+                if (row < r.N && row == probe_row(blk, r.N, r.phase)) {
+                    const float* od = r.od + (bh * r.Mp + blk) * D + c0;
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) res[u] = od[u];
+                }
+                u32x4 pk;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pk[e] = row < r.N ? pack_bf16x2(res[2 * e], res[2 * e + 1]) : 0u;
+                *reinterpret_cast<u32x4*>(O + static_cast<size_t>(row) * D + c0) = pk;
+            }
+        }
     }
 }
 
@@ -419,7 +634,7 @@ size_t residual_workspace_bytes(int B, int H, int N_pad) {
     const size_t mp = BLK * ((N_pad / BLK + BLK - 1) / BLK);
     const size_t kc = residual_key_chunks(N_pad);
     const size_t f64 = bh * (NSPLIT * (3 * D * D + 2 * D) + 3 * D * D);
-    const size_t f32 = bh * (2 * mp * D + D * D + D) + kc * bh * mp * (D + 1);
+    const size_t f32 = bh * (2 * mp * D + D * D + D) + kc * bh * mp * (D + 1) + bh * 2 * D * KSUB;
     const size_t b16 = bh * mp * D;
     return f64 * 8 + f32 * 4 + b16 * 2;
 }
@@ -436,7 +651,8 @@ void residual_carve(ResidualArgs& r, void* ws) {
     r.kchunks = residual_key_chunks(r.N_pad);
     r.odp = reinterpret_cast<float*>(p);   p += r.kchunks * bh * mp * D * 4;
     r.lsep = reinterpret_cast<float*>(p);  p += r.kchunks * bh * mp * 4;
-    r.qp = reinterpret_cast<uint16_t*>(p);
+    r.qp = reinterpret_cast<uint16_t*>(p);  p += bh * mp * D * 2;
+    r.zv = reinterpret_cast<float*>(p);
 }
 
 hipError_t launch_residual(const ResidualArgs& r, hipStream_t s) {
@@ -457,9 +673,11 @@ hipError_t launch_residual(const ResidualArgs& r, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(gram_kernel, dim3(NSPLIT, 3, bh), dim3(THREADS), 0, s, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(reduce_kernel, dim3(3 * D * D / RED_PER_WG, bh), dim3(THREADS), 0, s, r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(fit_kernel, dim3(bh), dim3(THREADS), 0, s, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(apply_kernel, dim3(r.N_pad / APPLY_ROWS, bh), dim3(THREADS), 0, s, r);
+    hipLaunchKernelGGL(apply_kernel, dim3((r.N_pad + APPLY_ROWS - 1) / APPLY_ROWS, bh), dim3(THREADS), 0, s, r);
     return hipGetLastError();
 }
 

@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 7
+#define SPARSE_ATTN_ABI_VERSION 8
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -332,10 +332,11 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
  * sparse outputs and R = O_dense - X at the probes, the residual is fitted as
  * R ~ b + X B by ridge regression on the centred probes (lambda = ridge *
  * tr(Xc^T Xc) / d, intercept not penalised; fp64 normal equations solved by
- * Cholesky) and restricted to the span of the top `rank` right singular
- * vectors of R (simultaneous iteration on R^T R, 8 columns, 16 steps of
- * Cholesky QR, the first `rank` columns): W = B P, c = b P.  Every valid row then gets
- * o + c + o W, each probe row its dense output (RNE to bf16); pad rows 0.
+ * an LDL^T elimination) and restricted to the span of the top `rank` right
+ * singular vectors of R (simultaneous iteration on R^T R, 8 columns, 16 steps
+ * of Cholesky QR, the first `rank` columns): W = B P, c = b P.  Every valid
+ * row then gets o + c + o W, evaluated in fp32 as o + c + (o Z) V_r^T with
+ * W = Z V_r^T, each probe row its dense output (RNE to bf16); pad rows 0.
  *
  * dtype      SA_BF16; d == 128
  * scale      the softmax scale of the forward call, finite and > 0
@@ -353,6 +354,9 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
  *                                        lse per chunk of key blocks,
  *                                        K = min(8, nb)
  *              bf16 [B,H,Mp,d]           gathered probe queries
+ *              fp32 [B,H,2,d,8]          Z = (Xc^T Xc + lambda I)^{-1} Xc^T Rc V_r
+ *                                        and V_r (columns >= rank zero), the
+ *                                        factors W = Z V_r^T is applied by
  */
 size_t sparse_attn_residual_workspace(const sa_shape* shape);
 sa_status sparse_attn_residual(const sa_shape* shape, sa_dtype dtype, float scale,

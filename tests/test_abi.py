@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 7
+    assert lib.sparse_attn_abi_version() == 8
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):

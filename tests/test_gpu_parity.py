@@ -21,7 +21,7 @@ pytestmark = pytest.mark.gpu
 def gpu_present():
     assert torch.cuda.is_available(), "GPU tests need a GPU"
     import free_block_sparse_attn_amd as fbsa
-    assert fbsa.abi_version() == 7
+    assert fbsa.abi_version() == 8
 
 
 def medium(wid):
