@@ -87,51 +87,72 @@ __global__ __launch_bounds__(THREADS) void combine_kernel(ResidualArgs r) {
 }
 
 // ---- 3. Gram partial sums ----
-// Workgroup (slice s, matrix m, head): probes p = s, s + NSPLIT, ...; thread t
-// owns entries (i = t / 2, j = 64 (t % 2) .. + 63) of matrix m:
-// m = 0: sum x_i x_j, 1: sum x_i r_j, 2: sum r_i r_j (r = o_dense - x).
-// Matrix 1's workgroup (u = x, w = r) also sums the columns of x and r.
+// Workgroup (slice s, matrix m, head): probes p = s, s + NSPLIT, ... in
+// order; thread (ti, tj) of a 16 x 16 grid owns the 8 x 8 entries
+// (ti + 16 a, tj + 16 b) of matrix m: m = 0: sum x_i x_j, 1: sum x_i r_j,
+// 2: sum r_i r_j (r = o_dense - x).  Per probe a thread reads 8 + 8 values
+// for 64 products.  Matrix 1's workgroup also sums the columns of x and r.
 __global__ __launch_bounds__(THREADS) void gram_kernel(ResidualArgs r) {
-    constexpr int STAGE = 8;
+    constexpr int STAGE = 16;
+    constexpr int PER = STAGE * D / THREADS;      // staged values per thread
     __shared__ double u_s[STAGE][D], w_s[STAGE][D];
     const int s = blockIdx.x, m = blockIdx.y;
     const size_t bh = blockIdx.z;
     const int nb = r.N_pad / BLK, mp = r.Mp;
-    const int tid = threadIdx.x, i = tid >> 1, j0 = 64 * (tid & 1);
-    double acc[64];
+    const int tid = threadIdx.x, ti = tid >> 4, tj = tid & 15;
+    double acc[8][8];
 #pragma unroll
-    for (int jj = 0; jj < 64; ++jj) acc[jj] = 0.0;
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) acc[a][b] = 0.0;
     double colsum = 0.0;                          // m == 1: thread t < 128 sums x_t, t >= 128 sums r_{t-128}
     const float* X = r.xp + bh * mp * D;
     const float* O = r.od + bh * mp * D;
+    float xv[PER], ov[PER];
+    auto fetch = [&](int p0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int v = 0; v < PER; ++v) {
+            const int e = tid + v * THREADS, q = e / D, col = e % D;
+            const int p = p0 + NSPLIT * q;
+            xv[v] = p < nb ? X[static_cast<size_t>(p) * D + col] : 0.0f;
+            ov[v] = p < nb ? O[static_cast<size_t>(p) * D + col] : 0.0f;
+        }
+    };
+    fetch(s);
     for (int p0 = s; p0 < nb; p0 += NSPLIT * STAGE) {
         __syncthreads();
-        for (int e = tid; e < STAGE * D; e += THREADS) {
-            const int q = e / D, col = e % D;
-            const int p = p0 + NSPLIT * q;
-            double xv = 0.0, rv = 0.0;
-            if (p < nb) {
-                xv = static_cast<double>(X[static_cast<size_t>(p) * D + col]);
-                rv = static_cast<double>(O[static_cast<size_t>(p) * D + col]) - xv;
-            }
-            u_s[q][col] = (m == 2) ? rv : xv;
-            w_s[q][col] = (m == 0) ? xv : rv;
+#pragma unroll
+        for (int v = 0; v < PER; ++v) {
+            const int e = tid + v * THREADS, q = e / D, col = e % D;
+            const double x = static_cast<double>(xv[v]);
+            const double rr = static_cast<double>(ov[v]) - x;
+            u_s[q][col] = (m == 2) ? rr : x;
+            w_s[q][col] = (m == 0) ? x : rr;
         }
         __syncthreads();
+        if (p0 + NSPLIT * STAGE < nb) fetch(p0 + NSPLIT * STAGE);
         if (m == 1) {
 #pragma unroll
             for (int q = 0; q < STAGE; ++q) colsum += tid < D ? u_s[q][tid] : w_s[q][tid - D];
         }
-#pragma unroll 1
+#pragma unroll 2
         for (int q = 0; q < STAGE; ++q) {
-            const double ui = u_s[q][i];
+            double uu[8], ww[8];
 #pragma unroll
-            for (int jj = 0; jj < 64; ++jj) acc[jj] = fma(ui, w_s[q][j0 + jj], acc[jj]);
+            for (int a = 0; a < 8; ++a) uu[a] = u_s[q][ti + 16 * a];
+#pragma unroll
+            for (int b = 0; b < 8; ++b) ww[b] = w_s[q][tj + 16 * b];
+#pragma unroll
+            for (int a = 0; a < 8; ++a)
+#pragma unroll
+                for (int b = 0; b < 8; ++b) acc[a][b] = fma(uu[a], ww[b], acc[a][b]);
         }
     }
     double* P = r.part + ((bh * NSPLIT + s) * (3 * D * D + 2 * D));
 #pragma unroll
-    for (int jj = 0; jj < 64; ++jj) P[m * D * D + i * D + j0 + jj] = acc[jj];
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b < 8; ++b) P[m * D * D + (ti + 16 * a) * D + tj + 16 * b] = acc[a][b];
     if (m == 1) P[3 * D * D + tid] = colsum;      // x sums then r sums
 }
 
@@ -140,6 +161,7 @@ __global__ __launch_bounds__(THREADS) void gram_kernel(ResidualArgs r) {
 // the column sums give the probe means xm, rm.
 constexpr int RED_PER_WG = 4 * THREADS;
 constexpr size_t PSTRIDE = 3 * D * D + 2 * D;   // doubles per slice of the partial sums
+constexpr int ZS = D + KSUB;                    // the zero slot of a published column
 static_assert(3 * D * D % RED_PER_WG == 0 && THREADS == 2 * D, "reduce tiling");
 
 __global__ __launch_bounds__(THREADS) void reduce_kernel(ResidualArgs r) {
@@ -237,42 +259,76 @@ __device__ __forceinline__ void chol_inv8(const double* Gs, double (&Mi)[KSUB][K
 
 // Columns 16 KB .. 16 KB + 15 of the right-looking LDL^T elimination.
 // Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b and, in
-// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Column k arrives in
-// col[k % 2]; its owners (q == (k + 1) % 16) publish column k + 1 into the
-// other buffer after updating it.  Entries of rows <= k or columns <= k are
-// left alone (their multipliers are zero); blocks left of column block KB are
-// finished and skipped.
+// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Entering step k,
+// x and cu hold column k's entries of the thread's rows and columns, zero for
+// rows / columns <= k (so finished entries are left alone), and rinv the
+// reciprocal pivot; the multipliers are cu * rinv.  Step k: the owners of column k + 1
+// (q == (k + 1) % 16) apply step k to it and publish it in col[(k + 1) % 2];
+// after the barrier every thread reads column k + 1 and applies the rest of
+// step k, the reads overlapping the update.  Blocks left of column block KB
+// are finished and skipped.
 template <int KB>
-__device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (*col)[D + KSUB], int p, int q) {
-#pragma unroll 1
-    for (int kk = 0; kk < 16; ++kk) {
-        const int k = 16 * KB + kk;
-        const double* ck = col[k & 1];
-        const double rinv = rcp64(fmax(ck[k], 1e-300));
-        double x[9], u[8];
+__device__ __forceinline__ void ldl_step(int kk, double (&A)[9][8], const double (&x)[9], const double (&cu)[8],
+                                         double nrinv, double (&xn)[9], double (&cn)[8], double& nrn,
+                                         double (*col)[D + KSUB + 1], int p, int q) {
+    constexpr int NB = KB < 7 ? KB + 1 : KB;
+    const int k = 16 * KB + kk;
+    double u[8];                                           // minus the multipliers of step k
 #pragma unroll
-        for (int a = KB; a < 8; ++a) x[a] = 16 * a + p > k ? ck[16 * a + p] : 0.0;
-        x[8] = p < KSUB ? ck[D + p] : 0.0;
+    for (int b = KB; b < 8; ++b) u[b] = cu[b] * nrinv;
+    if (k + 1 < D && q == ((k + 1) & 15)) {
+        double* cw = col[(k + 1) & 1];
+        if (kk < 15) {
 #pragma unroll
-        for (int b = KB; b < 8; ++b) u[b] = 16 * b + q > k ? ck[16 * b + q] * rinv : 0.0;
+            for (int a = KB; a < 9; ++a) A[a][KB] = fma(x[a], u[KB], A[a][KB]);
 #pragma unroll
-        for (int b = KB; b < 8; ++b)
+            for (int a = KB; a < 8; ++a) cw[16 * a + p] = A[a][KB];
+            if (p < KSUB) cw[D + p] = A[8][KB];
+            u[KB] = 0.0;
+        } else {
 #pragma unroll
-            for (int a = b; a < 9; ++a) A[a][b] = fma(-x[a], u[b], A[a][b]);
-        if (k + 1 < D && q == ((k + 1) & 15)) {
-            double* cn = col[(k + 1) & 1];
-            constexpr int NB = KB < 7 ? KB + 1 : KB;
-            if (kk < 15) {
+            for (int a = NB; a < 9; ++a) A[a][NB] = fma(x[a], u[NB], A[a][NB]);
 #pragma unroll
-                for (int a = KB; a < 8; ++a) cn[16 * a + p] = A[a][KB];
-                if (p < KSUB) cn[D + p] = A[8][KB];
-            } else {
-#pragma unroll
-                for (int a = NB; a < 8; ++a) cn[16 * a + p] = A[a][NB];
-                if (p < KSUB) cn[D + p] = A[8][NB];
-            }
+            for (int a = NB; a < 8; ++a) cw[16 * a + p] = A[a][NB];
+            if (p < KSUB) cw[D + p] = A[8][NB];
+            u[NB] = 0.0;
         }
-        __syncthreads();
+    }
+    __syncthreads();
+    // column k + 1 (read past the end on the last step, then unused); the
+    // update below does not wait for these reads
+    const double* ck = col[(k + 1) & 1];
+    const double dn = ck[k + 1];
+#pragma unroll
+    for (int a = KB; a < 8; ++a) xn[a] = ck[16 * a + p > k + 1 ? 16 * a + p : ZS];
+    xn[8] = ck[p < KSUB ? D + p : ZS];
+#pragma unroll
+    for (int bb = KB; bb < 8; ++bb) cn[bb] = ck[16 * bb + q > k + 1 ? 16 * bb + q : ZS];
+#pragma unroll
+    for (int bb = KB; bb < 8; ++bb)
+#pragma unroll
+        for (int a = bb; a < 9; ++a) A[a][bb] = fma(x[a], u[bb], A[a][bb]);
+    nrn = -rcp64(fmax(dn, 1e-300));
+}
+
+// Columns 16 KB .. 16 KB + 15 of the right-looking LDL^T elimination.
+// Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b and, in
+// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Entering step k,
+// x and cu hold column k's entries of the thread's rows and columns, zero for
+// rows / columns <= k (so finished entries are left alone), and nrinv minus
+// the reciprocal pivot.  Step k: the owners of column k + 1
+// (q == (k + 1) % 16) apply step k to it and publish it in col[(k + 1) % 2];
+// after the barrier every thread reads column k + 1 and applies the rest of
+// step k, the reads overlapping the update.  Two register sets alternate
+// between the steps.  Blocks left of column block KB are finished and skipped.
+template <int KB>
+__device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (&x)[9], double (&cu)[8], double& nrinv,
+                                            double (*col)[D + KSUB + 1], int p, int q) {
+    double x2[9], c2[8], nr2;
+#pragma unroll 1
+    for (int kk = 0; kk < 16; kk += 2) {
+        ldl_step<KB>(kk, A, x, cu, nrinv, x2, c2, nr2, col, p, q);
+        ldl_step<KB>(kk + 1, A, x2, c2, nr2, x, cu, nrinv, col, p, q);
     }
 }
 
@@ -292,10 +348,11 @@ __device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (*col)[D +
 __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
     constexpr int SP = D + 4;                               // fp32 row stride of S in LDS
     constexpr int LPK = D * (D + 1) / 2;                    // packed lower triangle, row i at i (i + 1) / 2
-    constexpr int POOL = (D * SP / 2 > LPK) ? D * SP / 2 : LPK;
+    constexpr int POOL = (D * SP / 2 > LPK + 1) ? D * SP / 2 : LPK + 1;   // + the zero slot
     __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32), later the factor
     __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB], B2[D * KSUB];
-    __shared__ double col[2][D + KSUB];
+    __shared__ __attribute__((aligned(16))) double Pt[4 * D * KSUB];   // partial products, one per wave
+    __shared__ double col[2][D + KSUB + 1];                // slot D + KSUB holds 0
     __shared__ double xm[D], rm[D];
     __shared__ double Gs[KSUB * KSUB];
     __shared__ double red[THREADS / 64], s8[KSUB];
@@ -319,26 +376,38 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
         if (lane == 0) red[wv] = tr;
     }
     float* Sf = reinterpret_cast<float*>(pool);
-    for (int e = tid; e < D * D; e += THREADS) Sf[(e / D) * SP + e % D] = static_cast<float>(S[e]);
+#pragma unroll 1
+    for (int e0 = 0; e0 < D * D; e0 += 16 * 2 * THREADS) {     // 16 pairs in flight per thread
+        f64x2 v[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const f64x2*>(S + e0 + 2 * (j * THREADS + tid));
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int e = e0 + 2 * (j * THREADS + tid);
+            Sf[(e / D) * SP + e % D] = static_cast<float>(v[j][0]);
+            Sf[(e / D) * SP + e % D + 1] = static_cast<float>(v[j][1]);
+        }
+    }
     for (int e = tid; e < D * KSUB; e += THREADS) {
         const int i = e / KSUB, c = e % KSUB;
         B0[e] = static_cast<double>(((i * 7 + c * 13 + 3) % 17) - 8) + (i == c ? 16.0 : 0.0);
     }
+    if (tid < 2) col[tid][ZS] = 0.0;
     __syncthreads();
     const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
 
     // ---- top-rank subspace of S ----
     const int ri = tid >> 1, rc = 4 * (tid & 1);           // row, first of four columns
     auto cholqr = [&](const double* Yin, double* Qout) __attribute__((always_inline)) {
-        {   // Gram entry tid / 4 over rows 32 (tid % 4) .. + 31, four lanes combined
-            const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = 32 * (tid & 3);
+        {   // Gram entry tid / 4 over rows i = tid % 4 (mod 4), four lanes combined
+            const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
             double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
 #pragma unroll
-            for (int i = i0; i < i0 + 32; i += 4) {
+            for (int i = i0; i < D; i += 16) {
                 v0 = fma(Yin[i * KSUB + a], Yin[i * KSUB + b], v0);
-                v1 = fma(Yin[(i + 1) * KSUB + a], Yin[(i + 1) * KSUB + b], v1);
-                v2 = fma(Yin[(i + 2) * KSUB + a], Yin[(i + 2) * KSUB + b], v2);
-                v3 = fma(Yin[(i + 3) * KSUB + a], Yin[(i + 3) * KSUB + b], v3);
+                v1 = fma(Yin[(i + 4) * KSUB + a], Yin[(i + 4) * KSUB + b], v1);
+                v2 = fma(Yin[(i + 8) * KSUB + a], Yin[(i + 8) * KSUB + b], v2);
+                v3 = fma(Yin[(i + 12) * KSUB + a], Yin[(i + 12) * KSUB + b], v3);
             }
             double v = (v0 + v1) + (v2 + v3);
             v += __shfl_xor(v, 1);
@@ -359,34 +428,60 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
         for (int cc = 0; cc < 4; ++cc) {                     // q_c = sum_{t <= c} Mi[c][t] y_t
             double v = 0.0;
 #pragma unroll
-            for (int c = 0; c < KSUB; ++c)
-                if (c == rc + cc) {
-#pragma unroll
-                    for (int t = 0; t <= c; ++t) v = fma(Mi[c][t], y[t], v);
-                }
+            for (int t = 0; t <= 4 + cc; ++t) {             // rc is 0 or 4
+                const double m = rc ? Mi[4 + cc][t] : (t <= cc ? Mi[cc][t] : 0.0);
+                v = fma(m, y[t], v);
+            }
             Qout[ri * KSUB + rc + cc] = v;
         }
         __syncthreads();
     };
-    auto product = [&](const double* Q, double* Y) __attribute__((always_inline)) {   // Y = S Q
-        const float* srow = Sf + ri * SP;
-        double y0 = 0.0, y1 = 0.0, y2 = 0.0, y3 = 0.0;
+    // Y = S Q: wave w takes the terms m in [32 w, 32 w + 32); lane l the
+    // rows l / 2 + 32 r (r < 4) and columns rc .. rc + 3; the four partial
+    // products are summed in wave order.
+    auto product = [&](const double* Q, double* Y) __attribute__((always_inline)) {
+        const int g = lane >> 1, kc = 32 * wv;
+        double y[4][4];
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) y[rr][cc] = 0.0;
+        const float* s0 = Sf + g * SP + kc;
 #pragma unroll 2
-        for (int m = 0; m < D; m += 4) {
-            const f32x4 s4 = *reinterpret_cast<const f32x4*>(srow + m);
+        for (int m = 0; m < 32; m += 4) {
+            f32x4 sv[4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) sv[rr] = *reinterpret_cast<const f32x4*>(s0 + 32 * rr * SP + m);
 #pragma unroll
             for (int mm = 0; mm < 4; ++mm) {
-                const double sv = static_cast<double>(s4[mm]);
-                const f64x2 qa = *reinterpret_cast<const f64x2*>(Q + (m + mm) * KSUB + rc);
-                const f64x2 qb = *reinterpret_cast<const f64x2*>(Q + (m + mm) * KSUB + rc + 2);
-                y0 = fma(sv, qa[0], y0);
-                y1 = fma(sv, qa[1], y1);
-                y2 = fma(sv, qb[0], y2);
-                y3 = fma(sv, qb[1], y3);
+                const double* qr = Q + (kc + m + mm) * KSUB + rc;
+                const f64x2 qa = *reinterpret_cast<const f64x2*>(qr);
+                const f64x2 qb = *reinterpret_cast<const f64x2*>(qr + 2);
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) {
+                    const double sd = static_cast<double>(sv[rr][mm]);
+                    y[rr][0] = fma(sd, qa[0], y[rr][0]);
+                    y[rr][1] = fma(sd, qa[1], y[rr][1]);
+                    y[rr][2] = fma(sd, qb[0], y[rr][2]);
+                    y[rr][3] = fma(sd, qb[1], y[rr][3]);
+                }
             }
         }
-        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc) = f64x2{y0, y1};
-        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc + 2) = f64x2{y2, y3};
+        double* pw = Pt + wv * D * KSUB;
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+            *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc) = f64x2{y[rr][0], y[rr][1]};
+            *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc + 2) = f64x2{y[rr][2], y[rr][3]};
+        }
+        __syncthreads();
+        f64x2 o01 = {0.0, 0.0}, o23 = {0.0, 0.0};
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            o01 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc);
+            o23 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc + 2);
+        }
+        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc) = o01;
+        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc + 2) = o23;
         __syncthreads();
     };
     cholqr(B0, B1);
@@ -433,24 +528,31 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
 #pragma unroll
             for (int b = 0; b <= a; ++b) {
                 const int i = 16 * a + p, j = 16 * b + q;
-                A[a][b] = i >= j ? G[i * D + j] + (i == j ? lam : 0.0) : 0.0;
+                A[a][b] = G[i * D + j] + (i == j ? lam : 0.0);
             }
 #pragma unroll
-        for (int b = 0; b < 8; ++b) A[8][b] = p < KSUB ? B2[(16 * b + q) * KSUB + p] : 0.0;
+        for (int b = 0; b < 8; ++b) A[8][b] = B2[(16 * b + q) * KSUB + (p & (KSUB - 1))];
         if (q == 0) {
 #pragma unroll
             for (int a = 0; a < 8; ++a) col[0][16 * a + p] = A[a][0];
             if (p < KSUB) col[0][D + p] = A[8][0];
         }
         __syncthreads();
-        ldl_columns<0>(A, col, p, q);
-        ldl_columns<1>(A, col, p, q);
-        ldl_columns<2>(A, col, p, q);
-        ldl_columns<3>(A, col, p, q);
-        ldl_columns<4>(A, col, p, q);
-        ldl_columns<5>(A, col, p, q);
-        ldl_columns<6>(A, col, p, q);
-        ldl_columns<7>(A, col, p, q);
+        double x[9], cu[8], nrinv;
+        nrinv = -rcp64(fmax(col[0][0], 1e-300));
+#pragma unroll
+        for (int a = 0; a < 8; ++a) x[a] = col[0][16 * a + p > 0 ? 16 * a + p : ZS];
+        x[8] = col[0][p < KSUB ? D + p : ZS];
+#pragma unroll
+        for (int b = 0; b < 8; ++b) cu[b] = col[0][16 * b + q > 0 ? 16 * b + q : ZS];
+        ldl_columns<0>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<1>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<2>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<3>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<4>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<5>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<6>(A, x, cu, nrinv, col, p, q);
+        ldl_columns<7>(A, x, cu, nrinv, col, p, q);
         // the factor (stored column k = L_.k D_kk) and the eliminated rows y = L^{-1} T
 #pragma unroll
         for (int a = 0; a < 8; ++a)
@@ -459,6 +561,7 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
                 const int i = 16 * a + p, j = 16 * b + q;
                 if (i >= j) Lp[i * (i + 1) / 2 + j] = A[a][b];
             }
+        if (tid == 0) Lp[LPK] = 0.0;                       // zero slot for the back substitution
         if (p < KSUB) {
 #pragma unroll
             for (int b = 0; b < 8; ++b) B0[(16 * b + q) * KSUB + p] = A[8][b];
@@ -481,9 +584,8 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
                 const double rdi = readlane64(odd ? rd1 : rd0, o);
                 const double z0 = readlane64(odd ? u10 : u00, o) * rdi;
                 const double z1 = readlane64(odd ? u11 : u01, o) * rdi;
-                const double* li = Lp + i * (i + 1) / 2;
-                const double l0 = j0 < i ? li[j0] : 0.0;
-                const double l1 = j0 + 1 < i ? li[j0 + 1] : 0.0;
+                const double l0 = Lp[j0 < i ? i * (i + 1) / 2 + j0 : LPK];
+                const double l1 = Lp[j0 + 1 < i ? i * (i + 1) / 2 + j0 + 1 : LPK];
                 u00 = fma(-l0, z0, u00);
                 u01 = fma(-l0, z1, u01);
                 u10 = fma(-l1, z0, u10);
