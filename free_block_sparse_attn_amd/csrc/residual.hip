@@ -332,6 +332,58 @@ __device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (&x)[9], d
     }
 }
 
+// Eigen-decomposition of the symmetric KSUB x KSUB matrix Hs (row-major, in
+// LDS) by cyclic Jacobi on one wave: each round applies 4 disjoint plane
+// rotations (round-robin pairing of the 8 indices, 7 rounds a sweep), the 64
+// entries of H and of the eigenvector matrix Es updated one per lane.  The
+// rotation for (p, q) zeroes H[p][q] (Golub and Van Loan's symmetric 2 x 2
+// Schur decomposition).  On return Hs holds the eigenvalues on its diagonal
+// and the columns of Es the eigenvectors.
+constexpr int JACOBI_SWEEPS = 6;
+__device__ __forceinline__ void wave_sync_lds() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+__device__ __forceinline__ int rr_partner(int x, int r) {     // round r pairing of 0..7
+    if (x == 7) return r;
+    if (x == r) return 7;
+    return ((2 * r - x) % 7 + 7) % 7;
+}
+__device__ void jacobi8(double* Hs, double* Es, double* cs, int lane) {
+    const int i = lane >> 3, j = lane & 7;
+    Es[lane] = i == j ? 1.0 : 0.0;
+    wave_sync_lds();
+    for (int sweep = 0; sweep < JACOBI_SWEEPS; ++sweep) {
+        for (int r = 0; r < 7; ++r) {
+            if (lane < KSUB) {                     // lane x: the rotation of its pair, from the lower index
+                const int x = lane, y = rr_partner(x, r);
+                const int pp = min(x, y), qq = max(x, y);
+                const double hpq = Hs[pp * KSUB + qq];
+                double c = 1.0, sn = 0.0;
+                if (hpq != 0.0) {
+                    const double tau = (Hs[qq * KSUB + qq] - Hs[pp * KSUB + pp]) / (2.0 * hpq);
+                    const double t = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+                    c = 1.0 / sqrt(1.0 + t * t);
+                    sn = t * c;
+                }
+                cs[2 * x] = c;                     // J[x][x] = c, J[partner][x] = sigma_x
+                cs[2 * x + 1] = x == pp ? -sn : sn;
+            }
+            wave_sync_lds();
+            const int pi = rr_partner(i, r), pj = rr_partner(j, r);
+            const double ci = cs[2 * i], si = cs[2 * i + 1], cj = cs[2 * j], sj = cs[2 * j + 1];
+            const double h = ci * (cj * Hs[i * KSUB + j] + sj * Hs[i * KSUB + pj]) +
+                             si * (cj * Hs[pi * KSUB + j] + sj * Hs[pi * KSUB + pj]);
+            const double e = cj * Es[i * KSUB + j] + sj * Es[i * KSUB + pj];
+            wave_sync_lds();
+            Hs[lane] = h;
+            Es[lane] = e;
+            wave_sync_lds();
+        }
+    }
+}
+
 // With V_r the top right singular vectors of R, W = B P = Z V_r^T with
 // Z = (G + lambda I)^{-1} (C V_r), and c = b P = (rm V_r - xm Z) V_r^T, so
 // only `rank` right-hand sides are solved.  Stages:
@@ -354,7 +406,7 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
     __shared__ __attribute__((aligned(16))) double Pt[4 * D * KSUB];   // partial products, one per wave
     __shared__ double col[2][D + KSUB + 1];                // slot D + KSUB holds 0
     __shared__ double xm[D], rm[D];
-    __shared__ double Gs[KSUB * KSUB];
+    __shared__ double Gs[KSUB * KSUB], Es[KSUB * KSUB], jcs[2 * KSUB];
     __shared__ double red[THREADS / 64], s8[KSUB];
     const size_t bh = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -490,10 +542,57 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
         product(B0, B1);
         cholqr(B1, B0);
     }
-    cholqr(B0, B1);                                        // V: the first rank columns of B1
+    cholqr(B0, B1);                                        // Q, orthonormal, in B1
+    // ---- Rayleigh-Ritz: H = Q^T S Q, H = E diag(l) E^T; V = Q E with the
+    // columns ordered by decreasing eigenvalue, the first rank kept ----
+    product(B1, B0);                                       // B0 = S Q
+    {
+        const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
+        double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+#pragma unroll
+        for (int i = i0; i < D; i += 16) {
+            v0 = fma(B1[i * KSUB + a], B0[i * KSUB + b], v0);
+            v1 = fma(B1[(i + 4) * KSUB + a], B0[(i + 4) * KSUB + b], v1);
+            v2 = fma(B1[(i + 8) * KSUB + a], B0[(i + 8) * KSUB + b], v2);
+            v3 = fma(B1[(i + 12) * KSUB + a], B0[(i + 12) * KSUB + b], v3);
+        }
+        double v = (v0 + v1) + (v2 + v3);
+        v += __shfl_xor(v, 1);
+        v += __shfl_xor(v, 2);
+        if ((tid & 3) == 0) Gs[g] = v;
+    }
+    __syncthreads();
+    if (wv == 0) {
+        // symmetrise (the two halves come from different sums) and diagonalise
+        const int i = lane >> 3, j = lane & 7;
+        const double hs = 0.5 * (Gs[i * KSUB + j] + Gs[j * KSUB + i]);
+        wave_sync_lds();
+        Gs[lane] = hs;
+        wave_sync_lds();
+        jacobi8(Gs, Es, jcs, lane);
+    }
+    __syncthreads();
     double* V = B1;
-    for (int e = tid; e < D * KSUB; e += THREADS)
-        if (e % KSUB >= rk) V[e] = 0.0;
+    {
+        double qrow[KSUB], ev[KSUB];
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) qrow[t] = V[ri * KSUB + t];
+#pragma unroll
+        for (int t = 0; t < KSUB; ++t) ev[t] = Gs[t * (KSUB + 1)];
+        __syncthreads();
+#pragma unroll
+        for (int jc = 0; jc < KSUB; ++jc) {                 // eigenvector jc goes to column rank(jc)
+            int pos = 0;
+#pragma unroll
+            for (int t = 0; t < KSUB; ++t) pos += (ev[t] > ev[jc]) || (ev[t] == ev[jc] && t < jc);
+            if (pos >= rc && pos < rc + 4) {
+                double v = 0.0;
+#pragma unroll
+                for (int t = 0; t < KSUB; ++t) v = fma(qrow[t], Es[t * KSUB + jc], v);
+                V[ri * KSUB + pos] = pos < rk ? v : 0.0;
+            }
+        }
+    }
     __syncthreads();
 
     // ---- T = C V_r into B2 ----

@@ -334,7 +334,8 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
  * tr(Xc^T Xc) / d, intercept not penalised; fp64 normal equations solved by
  * an LDL^T elimination) and restricted to the span of the top `rank` right
  * singular vectors of R (simultaneous iteration on R^T R, 8 columns, 16 steps
- * of Cholesky QR, the first `rank` columns): W = B P, c = b P.  Every valid
+ * of Cholesky QR, then Rayleigh-Ritz on the 8-column span; the leading `rank`
+ * Ritz vectors): W = B P, c = b P.  Every valid
  * row then gets o + c + o W, evaluated in fp32 as o + c + (o Z) V_r^T with
  * W = Z V_r^T, each probe row its dense output (RNE to bf16); pad rows 0.
  *

@@ -406,23 +406,23 @@ def test_parity_triage_mxfp4_full_size_sampled():
 RES_PHASE, RES_RIDGE, RES_RANK = 3, 1e-3, 8
 
 
-def run_residual(wl, dev, coords):
+def run_residual(wl, dev, coords, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK):
     """GPU sparse forward, then the probe-fitted residual pass on its output."""
     import free_block_sparse_attn_amd as fbsa
     res = gc.run_gpu(wl, dev, coords)
     q, k, v = dev
     out = torch.from_numpy(res["out"]).to(torch.bfloat16).cuda()
-    r = fbsa.sparse_attn_residual(q, k, v, out, wl.N, 1.0, RES_PHASE, RES_RIDGE, RES_RANK)
+    r = fbsa.sparse_attn_residual(q, k, v, out, wl.N, 1.0, phase, ridge, rank)
     torch.cuda.synchronize()
     fit = {n: r[n].cpu().numpy() for n in ("xp", "od", "W", "c")}
     return res, out.float().cpu().numpy(), fit
 
 
-def check_residual(wl, q, k, v, res, corr, fit, heads_rows):
+def check_residual(wl, q, k, v, res, corr, fit, heads_rows, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK):
     """Dense probe rows, the fit on the GPU's probe data, and the corrected rows."""
     from oracle import residual
     nb = wl.nb
-    rows = residual.probe_rows(wl.N, nb, RES_PHASE)
+    rows = residual.probe_rows(wl.N, nb, phase)
     worst = 0.0
     for (b, h), check_rows in heads_rows.items():
         od = residual.probe_dense(q[b, h], k[b, h], v[b, h], wl.N, 1.0, rows)
@@ -430,7 +430,7 @@ def check_residual(wl, q, k, v, res, corr, fit, heads_rows):
         assert np.array_equal(fit["xp"][b, h, :nb], res["out"][b, h, rows])
         # stage-wise: the oracle's fit on the GPU's probe outputs
         X = fit["xp"][b, h, :nb].astype(np.float64)
-        W, c = residual.fit_residual(X, fit["od"][b, h, :nb] - X, RES_RIDGE, RES_RANK)
+        W, c = residual.fit_residual(X, fit["od"][b, h, :nb] - X, ridge, rank)
         scale = max(np.abs(W).max(), np.abs(c).max(), 1e-12)
         assert np.abs(fit["W"][b, h] - W).max() <= 1e-3 * scale, np.abs(fit["W"][b, h] - W).max()
         assert np.abs(fit["c"][b, h] - c).max() <= 1e-3 * scale
@@ -454,6 +454,20 @@ def test_parity_probe_residual(size):
     res, corr, fit = run_residual(wl, dev, coords)
     heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
     worst = check_residual(wl, q, k, v, res, corr, fit, heads)
+    assert np.all(corr[:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
+def test_parity_probe_residual_odd_rank():
+    """Rank 3 (two of the four solve waves idle, one zero right-hand side in
+    the last pair), another probe phase and a larger ridge."""
+    wl = get_workload(2, small=True)
+    phase, ridge, rank = 11, 1e-2, 3
+    print(f"\n[case] residual {wl.name} rank={rank} phase={phase} ridge={ridge} N={wl.N} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    res, corr, fit = run_residual(wl, dev, coords, phase, ridge, rank)
+    heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
+    worst = check_residual(wl, q, k, v, res, corr, fit, heads, phase, ridge, rank)
     assert np.all(corr[:, :, wl.N:] == 0)
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
