@@ -88,8 +88,30 @@ def skim_weights(L: np.ndarray) -> np.ndarray:
     return np.exp2(c - 8.0) * e4m3.round_to_e4m3(np.exp2(8.0 + L - c))
 
 
+def skim_weight_slack(L: np.ndarray, eps: float) -> np.ndarray:
+    """Largest change of each quantised weight of skim_weights(L) over the
+    decisions that an evaluation of L off by at most eps (log2 units) can take
+    differently: each weight's e4m3 code (rounding is monotone, so the codes
+    reachable from [L - eps, L + eps] are those of its ends) and the row's
+    reference c_t = ceil(max L_t) (ceil(max L_t -+ eps)).  Zero wherever every
+    such evaluation gives the same weight.  [rows, keys], absolute units.
+    """
+    base = skim_weights(L)
+    mx = L.max(axis=1, keepdims=True)
+    c = np.ceil(mx)
+    lo, hi = np.ceil(mx - eps), np.ceil(mx + eps)
+    d = np.zeros_like(base)
+    for cc in (c - 1.0, c, c + 1.0):
+        reach = (lo <= cc) & (cc <= hi)
+        for dl in (-eps, 0.0, eps):
+            alt = np.exp2(cc - 8.0) * e4m3.round_to_e4m3(np.exp2(8.0 + L + dl - cc))
+            d = np.maximum(d, np.where(reach, np.abs(alt - base), 0.0))
+    return d
+
+
 def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
-               exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK, hbar=None):
+               exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK, hbar=None,
+               slack_eps=None):
     """Compensated rule for the valid rows Qa [r, d] of query block a, one head.
 
     k, v: [N_pad, d]; kbar, vbar: exact fp64 means [nb, d]; kcount [nb];
@@ -97,7 +119,10 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
     hbar [d, d] (the head's mean first-order matrix) for comp == 2;
     fp8: the skim tier's copies: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp,
     vexp [nb]) for e4m3, or dict(q4, qs4, k4, ks4, v4, vs4) for mxfp4.
-    Returns (o [r, d], lse [r]).
+    Returns (o [r, d], lse [r]); with slack_eps, also a per-row bound [r] on
+    how far o moves when the skim logits (log2 units) are evaluated off by up
+    to slack_eps: the weights' code decisions (skim_weight_slack), their
+    continuous change, and the denominator's.
     """
     Qa = np.asarray(Qa, np.float64)
     nb = kbar.shape[0]
@@ -138,11 +163,20 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
         P = np.exp(lg - m[:, None])
         D += P.sum(axis=1)
         Nt += P @ val
+    slack = np.zeros(Qa.shape[0])
+    slack_den = np.zeros(Qa.shape[0])
     for lg, vt in skim_terms:
         D += np.exp(lg - m[:, None]).sum(axis=1)
         L = lg * LOG2E
         pq = skim_weights(L) * np.exp2(-m * LOG2E)[:, None]
         Nt += pq @ vt
+        if slack_eps is not None:
+            # code decisions, plus the continuous change of every weight (in
+            # the numerator, and through the denominator on o)
+            g = np.exp2(slack_eps) - 1.0
+            sc = np.exp2(-m * LOG2E)[:, None]
+            slack += ((skim_weight_slack(L, slack_eps) + g * skim_weights(L)) * sc) @ np.abs(vt).max(axis=1)
+            slack_den += g * np.exp(lg - m[:, None]).sum(axis=1)
     if comp == 2 and U.size:
         alpha = np.exp(scale * (Qa @ kbar[U].T) - m[:, None])        # [r, |U|]
         Nt += scale * alpha.sum(axis=1)[:, None] * (Qa @ hbar)
@@ -150,6 +184,9 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
         alpha = np.exp(scale * (Qa @ kbar[U].T) - m[:, None])        # [r, |U|]
         QH = np.matmul(Qa[None], kmom[U])                             # [|U|, r, d]: q^T H_j
         Nt += scale * np.einsum("ru,uro->ro", alpha, QH)
+    if slack_eps is not None:
+        o = Nt / D[:, None]
+        return o, m + np.log(D), (slack + slack_den * np.abs(o).max(axis=1)) / D
     return Nt / D[:, None], m + np.log(D)
 
 

@@ -7,7 +7,7 @@ import torch
 from oracle import attention, pooling, routing
 from workloads import make_qkv, block_frame_ranges, lvsa_anchor_phase
 
-BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs
+BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs, per row scaled by max(1, |o|_inf) (row_tol)
 F32_TOL = 1e-4       # max |out - oracle| for fp32 outputs
 # lse: the bf16 path's first-order Taylor forms normalise with the sum of the
 # bf16-rounded weights the matrix core multiplies, each within 2^-8 (bf16 unit
@@ -16,6 +16,24 @@ F32_TOL = 1e-4       # max |out - oracle| for fp32 outputs
 # accumulation): 4.5e-3.  The other forms sum the fp32 weights and land far
 # inside this bar (~1e-5).
 LSE_TOL = {"bf16": 4.5e-3, "f32": 1e-5}
+# The fp8 / MXFP4 skim tier's logits come out of the block-scaled MFMA, whose
+# sums differ from the exact dot products of the low-precision copies by up
+# to ~2e-4 in log2 units on these workloads (row lse off by <= 1.4e-4 where a
+# skim block dominates).  Skim rows are checked against the oracle's bound of
+# how far the output moves when those logits are off by SKIM_EPS (both e4m3
+# codes accepted for weights that close to a rounding boundary, plus the
+# continuous change; oracle.attention.rule_block slack_eps).
+SKIM_EPS = 5e-4
+
+
+def row_tol(dtype, o):
+    """Per-row output bar: fp32 absolute; bf16 max-abs 1e-2 for rows with
+    |o|_inf <= 1 and 1e-2 |o|_inf above (a bf16 value of magnitude in [2, 4)
+    is itself only resolved to 2^-6, so an absolute 1e-2 cannot be met there by
+    any bf16 result; bf16 error is relative)."""
+    if dtype != "bf16":
+        return np.full(o.shape[0], F32_TOL)
+    return BF16_TOL * np.maximum(1.0, np.abs(o).max(axis=1))
 
 
 def to_device(wl, q, k, v):
@@ -141,7 +159,9 @@ def oracle_rows(wl, q, k, v, pooled, res, rows, scale=1.0):
             fp8 = {n: pooled[n][b, h] for n in names}
         kmom = pooled["kmom"][b, h] if wl.comp == 1 else None
         hbar = pooled["hbar"][b, h] if wl.comp == 2 else None
-        out[(b, h, a)] = attention.rule_block(
+        r = attention.rule_block(
             q[b, h, r0:r1], k[b, h], v[b, h], wl.N, scale, wl.comp, pooled["kbar64"][b, h],
-            pooled["vbar64"][b, h], pooled["kcount"], ex, sk, kmom, fp8, a, hbar=hbar)
+            pooled["vbar64"][b, h], pooled["kcount"], ex, sk, kmom, fp8, a, hbar=hbar,
+            slack_eps=SKIM_EPS if len(sk) else None)
+        out[(b, h, a)] = r if len(sk) else (r[0], r[1], np.zeros(r1 - r0))
     return out

@@ -132,14 +132,16 @@ def check_error_logs(wl, res, elog, k, rows=None):
 
 
 def check_out(wl, res, ref, rows):
-    tol = gc.BF16_TOL if wl.dtype == "bf16" else gc.F32_TOL
+    """Outputs row by row against gc.row_tol (plus the oracle's skim slack), lse."""
     worst = 0.0
-    for (b, h, a), (o, l) in ref.items():
+    for (b, h, a), (o, l, slack) in ref.items():
         r0, r1 = 64 * a, min(wl.N, 64 * a + 64)
-        err = np.abs(res["out"][b, h, r0:r1] - o).max()
+        err = np.abs(res["out"][b, h, r0:r1] - o).max(axis=1)
+        bar = gc.row_tol(wl.dtype, o) + slack
         lerr = np.abs(res["lse"][b, h, r0:r1] - l).max()
-        worst = max(worst, err)
-        assert err <= tol, (b, h, a, err)
+        worst = max(worst, err.max())
+        i = int(np.argmax(err - bar))
+        assert err[i] <= bar[i], (b, h, a, i, err[i], bar[i])
         assert lerr <= gc.LSE_TOL[wl.dtype], (b, h, a, lerr)
     return worst
 
@@ -169,6 +171,30 @@ def test_parity_reduced(wid, size):
         # pad rows are written as zero
         assert np.all(res["out"][:, :, wl.N:] == 0)
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("wid", [2, 4, 5])
+def test_parity_batch_of_two(wid):
+    """B = 2: the (batch, head) indexing of pooling, routing (LVSA writes its
+    shared lists for every batch and head), the forward and, for the top-k
+    layer, the residual pass."""
+    from dataclasses import replace
+    wl = replace(get_workload(wid, small=True), B=2)
+    print(f"\n[case] {wl.name} B={wl.B} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    assert q.shape[0] == 2 and not np.array_equal(q[0], q[1])
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords, 0)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    if wid == 2:
+        res, corr, fit = run_residual(wl, dev, coords)
+        heads = {(b, h): np.arange(wl.N_pad) for b in range(wl.B) for h in range(wl.H)}
+        worst = max(worst, check_residual(wl, q, k, v, res, corr, fit, heads))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
 @pytest.mark.parametrize("wid", [2, 3, 4, 5])
@@ -439,9 +465,10 @@ def check_residual(wl, q, k, v, res, corr, fit, heads_rows, phase=RES_PHASE, rid
         ref = O + c + O @ W
         ref[rows] = od
         ref[wl.N:] = 0.0
-        err = np.abs(corr[b, h, check_rows] - ref[check_rows]).max()
-        worst = max(worst, err)
-        assert err <= gc.BF16_TOL, (b, h, err)
+        err = np.abs(corr[b, h, check_rows] - ref[check_rows]).max(axis=1)
+        bar = gc.row_tol("bf16", ref[check_rows])
+        worst = max(worst, err.max())
+        assert np.all(err <= bar), (b, h, err.max())
     return worst
 
 

@@ -367,3 +367,58 @@ def test_global_first_order_equals_block_when_all_moments_agree():
     np.testing.assert_allclose(l2, l1, atol=1e-12)
     O0, _ = attention.sparse_attention(q, k, v, N, 0.9, 0, pooled, idx, cnt)
     assert np.abs(O2 - O0).max() > 1e-3                       # the term is not trivially zero
+
+
+# ---- skim-weight decision slack (oracle.attention.skim_weight_slack) ----
+
+def test_skim_slack_zero_away_from_boundaries():
+    # y = 2^(8 + L - c) = 144 and 72 are e4m3 values; max L = log2(144) - 8 + c
+    # is far from an integer, so no evaluation within 1e-3 changes anything
+    c = 3.0
+    L = np.array([[np.log2(144.0) - 8.0 + c, np.log2(72.0) - 8.0 + c]])
+    assert np.array_equal(attention.skim_weight_slack(L, 1e-3), np.zeros_like(L))
+
+
+def test_skim_slack_is_one_code_step_at_a_midpoint():
+    # y = 136 is the midpoint of the e4m3 values 128 and 144 (ties to even:
+    # 128); within any eps > 0 the code 144 is also reachable: slack 16 * 2^(c-8)
+    c = 5.0
+    L = np.array([[np.log2(196.0) - 8.0 + c, np.log2(136.0) - 8.0 + c]])
+    d = attention.skim_weight_slack(L, 1e-6)
+    assert d[0, 1] == 16.0 * 2.0 ** (c - 8.0)
+    assert d[0, 0] == 0.0      # 196 rounds to 192, 4 below the midpoint 200
+
+
+def test_skim_slack_covers_the_row_reference():
+    # max L exactly an integer: c = ceil(max L) = max L, and max L + eps gives
+    # c + 1, halving every y = 2^(8 + L - c); the slack is the change of the
+    # weights under that reference, which is nonzero for an odd code
+    L = np.array([[4.0, 4.0 + np.log2(176.0 / 256.0)]])     # y = 256 and 176 at c = 4
+    base = attention.skim_weights(L)
+    d = attention.skim_weight_slack(L, 1e-9)
+    y_alt = e4m3.round_to_e4m3(np.exp2(8.0 + L - 5.0))       # 128 and 88
+    alt = np.exp2(5.0 - 8.0) * y_alt
+    assert np.allclose(d, np.maximum(np.abs(alt - base), 0.0))
+    assert d[0, 1] == abs(alt[0, 1] - base[0, 1])
+
+
+def test_rule_block_slack_bounds_a_perturbed_evaluation():
+    # the output of the rule with the skim logits moved by up to eps stays
+    # within the reported slack of the unperturbed output
+    rng = np.random.default_rng(5)
+    N, d = 192, 128
+    q = rng.standard_normal((N, d)) * 0.5
+    k = rng.standard_normal((N, d)) * 0.5
+    v = rng.standard_normal((N, d))
+    nb = 3
+    kbar = np.stack([k[64 * j:64 * j + 64].mean(0) for j in range(nb)])
+    vbar = np.stack([v[64 * j:64 * j + 64].mean(0) for j in range(nb)])
+    kcount = np.full(nb, 64)
+    codes = {n: e4m3.encode(x * 2.0 ** -(-3)) for n, x in (("q8", q), ("k8", k))}
+    fp8 = dict(q8=codes["q8"], k8=codes["k8"], v8=e4m3.encode(v * 8.0),
+               qexp=np.full(nb, -3), kexp=np.full(nb, -3), vexp=np.full(nb, -3))
+    o, l, slack = attention.rule_block(q[:64], k, v, N, 1.0, 0, kbar, vbar, kcount, [0], [1, 2],
+                                       None, fp8, 0, slack_eps=1e-3)
+    assert slack.shape == (64,) and np.all(slack >= 0.0)
+    o2, l2 = attention.rule_block(q[:64], k, v, N, 1.0, 0, kbar, vbar, kcount, [0], [1, 2], None, fp8, 0)
+    assert np.array_equal(o, o2) and np.array_equal(l, l2)
