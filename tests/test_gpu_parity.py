@@ -173,13 +173,23 @@ def test_parity_reduced(wid, size):
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("wid", [2, 4, 5])
-def test_parity_batch_of_two(wid):
-    """B = 2: the (batch, head) indexing of pooling, routing (LVSA writes its
-    shared lists for every batch and head), the forward and, for the top-k
-    layer, the residual pass."""
+def _batch2_workload(kind):
     from dataclasses import replace
-    wl = replace(get_workload(wid, small=True), B=2)
+    from workloads import configs as C
+    base = {"topk": C.SMALL[2], "lvsa": C.SMALL[4], "triage": C.SMALL[5], "order1": C.SMALL[3],
+            "global": C.GLOBAL_ORDER1_SMALL, "cov": C.GLOBAL_COV_SMALL, "error": C.ERROR_ROUTED_SMALL,
+            "mxfp4": C.TRIAGE_FP4_SMALL}[kind]
+    return replace(base, B=2)
+
+
+@pytest.mark.parametrize("kind", ["topk", "lvsa", "triage", "order1", "global", "cov", "error", "mxfp4"])
+def test_parity_batch_of_two(kind):
+    """B = 2: the (batch, head) indexing of pooling (moments, H-bar, covariance
+    norms, fp8 / MXFP4 copies), routing (LVSA writes its shared lists for every
+    batch and head; the error pass), the forward and, for the top-k layer, the
+    residual pass."""
+    wl = _batch2_workload(kind)
+    wid = 2 if kind == "topk" else 0
     print(f"\n[case] {wl.name} B={wl.B} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
     (q, k, v), dev, coords = gc.inputs(wl)
     assert q.shape[0] == 2 and not np.array_equal(q[0], q[1])
@@ -187,6 +197,8 @@ def test_parity_batch_of_two(wid):
     res = gc.run_gpu(wl, dev, coords)
     check_pool(wl, pooled_o, res)
     check_route(wl, pooled_o, res, coords, 0)
+    if kind == "error":
+        check_error_logs(wl, res, np.swapaxes(res["ekey"], -1, -2), k)
     ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
     worst = check_out(wl, res, ref, all_rows(wl))
     assert np.all(res["out"][:, :, wl.N:] == 0)
