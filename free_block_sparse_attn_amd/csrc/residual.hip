@@ -16,12 +16,14 @@
 //   3. gram_kernel           fp64 partial sums of X^T X, X^T R, R^T R and the
 //                            column sums over slices of the probes
 //   4. reduce_kernel         the partial sums in a fixed order, centred
-//      fit_kernel            one workgroup per head: ridge, the top-r
+//      fit_factor_kernel     two workgroups per head side by side: the top-r
 //                            subspace V_r of R^T R (simultaneous iteration
-//                            with Cholesky QR), Z = (G + lambda I)^{-1} C V_r
-//                            by an LDL^T elimination that carries the r
-//                            right-hand sides, then W = Z V_r^T,
-//                            c = (rm V_r - xm Z) V_r^T and the fp32 factors
+//                            with Cholesky QR, then Rayleigh-Ritz), and the
+//                            LDL^T factor of G + lambda I
+//      fit_solve_kernel      one workgroup per head: Z = (G + lambda I)^{-1}
+//                            C V_r by forward and back substitution, then
+//                            W = Z V_r^T, c = (rm V_r - xm Z) V_r^T and the
+//                            fp32 factors
 //   5. apply_kernel          o_t <- o_t + c + (o_t Z) V_r^T on every valid
 //                            row, the dense output on probe rows (bf16, in
 //                            place)
@@ -386,80 +388,167 @@ __device__ void jacobi8(double* Hs, double* Es, double* cs, int lane) {
 
 // With V_r the top right singular vectors of R, W = B P = Z V_r^T with
 // Z = (G + lambda I)^{-1} (C V_r), and c = b P = (rm V_r - xm Z) V_r^T, so
-// only `rank` right-hand sides are solved.  Stages:
-//   * simultaneous iteration on S = R^T R (fp32 copy in LDS, fp64 products),
-//     KSUB columns, Cholesky QR after every product;
-//   * T = C V_r;
-//   * LDL^T of G + lambda I by right-looking elimination in registers, thread
-//     (p, q) of a 16 x 16 grid holding the entries (16 a + p, 16 b + q), with
-//     T^T appended as KSUB extra rows so that the eliminated rows are L^{-1} T;
-//     one barrier per column, the column published through LDS;
-//   * back substitution with the unit upper factor, a wave per two columns,
-//     the pivot row's values read across lanes;
-//   * W, c, and the factors Z, V_r (fp32) for the apply pass.
-__global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
+// only `rank` right-hand sides are solved.  The subspace and the factor of
+// G + lambda I do not depend on each other, so they run side by side:
+//   fit_factor_kernel, workgroups (0, head) and (1, head):
+//     0: simultaneous iteration on S = R^T R (fp32 copy in LDS, fp64
+//        products), KSUB columns, Cholesky QR after every product, then
+//        Rayleigh-Ritz; V_r (fp64) into the workspace;
+//     1: LDL^T of G + lambda I by right-looking elimination in registers,
+//        thread (p, q) of a 16 x 16 grid holding the entries (16 a + p,
+//        16 b + q), one barrier per column, the column published through
+//        LDS; the packed factor (stored column k = L_.k D_kk) into the
+//        workspace.
+//   fit_solve_kernel, one workgroup per head: T = C V_r, the forward and back
+//     substitutions with the unit triangular factors (a wave per two
+//     right-hand sides, the pivot row's values read across lanes), then W, c
+//     and the factors Z, V_r (fp32) for the apply pass.
+// Both write into the Gram partial sums' space past the reduction (V_r at 0,
+// the factor after it; the column sums further on stay untouched).
+constexpr int LPK = D * (D + 1) / 2;                        // packed lower triangle, row i at i (i + 1) / 2
+static_assert(D * KSUB + LPK + 1 <= 3 * D * D, "the fit's scratch stays below the column sums");
+
+__global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
     constexpr int SP = D + 4;                               // fp32 row stride of S in LDS
-    constexpr int LPK = D * (D + 1) / 2;                    // packed lower triangle, row i at i (i + 1) / 2
-    constexpr int POOL = (D * SP / 2 > LPK + 1) ? D * SP / 2 : LPK + 1;   // + the zero slot
-    __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32), later the factor
-    __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB], B2[D * KSUB];
+    constexpr int POOL = D * SP / 2;
+    __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32)
+    __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB];
     __shared__ __attribute__((aligned(16))) double Pt[4 * D * KSUB];   // partial products, one per wave
     __shared__ double col[2][D + KSUB + 1];                // slot D + KSUB holds 0
-    __shared__ double xm[D], rm[D];
     __shared__ double Gs[KSUB * KSUB], Es[KSUB * KSUB], jcs[2 * KSUB];
-    __shared__ double red[THREADS / 64], s8[KSUB];
-    const size_t bh = blockIdx.x;
+    __shared__ double red[THREADS / 64];
+    const size_t bh = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int rk = r.rank;
-    const double M = static_cast<double>(r.N_pad / BLK);
-    const double* P = r.part + bh * NSPLIT * PSTRIDE;
     const double* G = r.mat + bh * 3 * D * D;              // centred X^T X
-    const double* C = G + D * D;                           // centred X^T R
-    const double* S = C + D * D;                           // R^T R
-    {
-        double v = 0.0;
-        for (int s = 0; s < NSPLIT; ++s) v += P[s * PSTRIDE + 3 * D * D + tid];
-        if (tid < D) xm[tid] = v / M;
-        else rm[tid - D] = v / M;
-    }
-    {
-        double tr = tid < D ? G[tid * (D + 1)] : 0.0;
-        tr = wave_sum(tr);
-        if (lane == 0) red[wv] = tr;
-    }
-    float* Sf = reinterpret_cast<float*>(pool);
+    const double* S = G + 2 * D * D;                       // R^T R
+    double* scratch = r.part + bh * NSPLIT * PSTRIDE;
+    if (blockIdx.x == 0) {
+        const int ri = tid >> 1, rc = 4 * (tid & 1);       // row, first of four columns
+        float* Sf = reinterpret_cast<float*>(pool);
 #pragma unroll 1
-    for (int e0 = 0; e0 < D * D; e0 += 16 * 2 * THREADS) {     // 16 pairs in flight per thread
-        f64x2 v[16];
+        for (int e0 = 0; e0 < D * D; e0 += 16 * 2 * THREADS) {     // 16 pairs in flight per thread
+            f64x2 v[16];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const f64x2*>(S + e0 + 2 * (j * THREADS + tid));
+            for (int j = 0; j < 16; ++j) v[j] = *reinterpret_cast<const f64x2*>(S + e0 + 2 * (j * THREADS + tid));
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int e = e0 + 2 * (j * THREADS + tid);
-            Sf[(e / D) * SP + e % D] = static_cast<float>(v[j][0]);
-            Sf[(e / D) * SP + e % D + 1] = static_cast<float>(v[j][1]);
+            for (int j = 0; j < 16; ++j) {
+                const int e = e0 + 2 * (j * THREADS + tid);
+                Sf[(e / D) * SP + e % D] = static_cast<float>(v[j][0]);
+                Sf[(e / D) * SP + e % D + 1] = static_cast<float>(v[j][1]);
+            }
         }
-    }
-    for (int e = tid; e < D * KSUB; e += THREADS) {
-        const int i = e / KSUB, c = e % KSUB;
-        B0[e] = static_cast<double>(((i * 7 + c * 13 + 3) % 17) - 8) + (i == c ? 16.0 : 0.0);
-    }
-    if (tid < 2) col[tid][ZS] = 0.0;
-    __syncthreads();
-    const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
-
-    // ---- top-rank subspace of S ----
-    const int ri = tid >> 1, rc = 4 * (tid & 1);           // row, first of four columns
-    auto cholqr = [&](const double* Yin, double* Qout) __attribute__((always_inline)) {
-        {   // Gram entry tid / 4 over rows i = tid % 4 (mod 4), four lanes combined
+        for (int e = tid; e < D * KSUB; e += THREADS) {
+            const int i = e / KSUB, c = e % KSUB;
+            B0[e] = static_cast<double>(((i * 7 + c * 13 + 3) % 17) - 8) + (i == c ? 16.0 : 0.0);
+        }
+        __syncthreads();
+        // ---- top-rank subspace of S ----
+        auto cholqr = [&](const double* Yin, double* Qout) __attribute__((always_inline)) {
+            {   // Gram entry tid / 4 over rows i = tid % 4 (mod 4), four lanes combined
+                const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
+                double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
+#pragma unroll
+                for (int i = i0; i < D; i += 16) {
+                    v0 = fma(Yin[i * KSUB + a], Yin[i * KSUB + b], v0);
+                    v1 = fma(Yin[(i + 4) * KSUB + a], Yin[(i + 4) * KSUB + b], v1);
+                    v2 = fma(Yin[(i + 8) * KSUB + a], Yin[(i + 8) * KSUB + b], v2);
+                    v3 = fma(Yin[(i + 12) * KSUB + a], Yin[(i + 12) * KSUB + b], v3);
+                }
+                double v = (v0 + v1) + (v2 + v3);
+                v += __shfl_xor(v, 1);
+                v += __shfl_xor(v, 2);
+                if ((tid & 3) == 0) Gs[g] = v;
+            }
+            __syncthreads();
+            double Mi[KSUB][KSUB];
+            chol_inv8(Gs, Mi);
+            double y[KSUB];
+#pragma unroll
+            for (int t = 0; t < KSUB; t += 2) {
+                const f64x2 w = *reinterpret_cast<const f64x2*>(Yin + ri * KSUB + t);
+                y[t] = w[0];
+                y[t + 1] = w[1];
+            }
+#pragma unroll
+            for (int cc = 0; cc < 4; ++cc) {                     // q_c = sum_{t <= c} Mi[c][t] y_t
+                double v = 0.0;
+#pragma unroll
+                for (int t = 0; t <= 4 + cc; ++t) {             // rc is 0 or 4
+                    const double m = rc ? Mi[4 + cc][t] : (t <= cc ? Mi[cc][t] : 0.0);
+                    v = fma(m, y[t], v);
+                }
+                Qout[ri * KSUB + rc + cc] = v;
+            }
+            __syncthreads();
+        };
+        // Y = S Q: wave w takes the terms m in [32 w, 32 w + 32); lane l the
+        // rows l / 2 + 32 r (r < 4) and columns rc .. rc + 3; the four partial
+        // products are summed in wave order.
+        auto product = [&](const double* Q, double* Y) __attribute__((always_inline)) {
+            const int g = lane >> 1, kc = 32 * wv;
+            double y[4][4];
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+                for (int cc = 0; cc < 4; ++cc) y[rr][cc] = 0.0;
+            const float* s0 = Sf + g * SP + kc;
+#pragma unroll 2
+            for (int m = 0; m < 32; m += 4) {
+                f32x4 sv[4];
+#pragma unroll
+                for (int rr = 0; rr < 4; ++rr) sv[rr] = *reinterpret_cast<const f32x4*>(s0 + 32 * rr * SP + m);
+#pragma unroll
+                for (int mm = 0; mm < 4; ++mm) {
+                    const double* qr = Q + (kc + m + mm) * KSUB + rc;
+                    const f64x2 qa = *reinterpret_cast<const f64x2*>(qr);
+                    const f64x2 qb = *reinterpret_cast<const f64x2*>(qr + 2);
+#pragma unroll
+                    for (int rr = 0; rr < 4; ++rr) {
+                        const double sd = static_cast<double>(sv[rr][mm]);
+                        y[rr][0] = fma(sd, qa[0], y[rr][0]);
+                        y[rr][1] = fma(sd, qa[1], y[rr][1]);
+                        y[rr][2] = fma(sd, qb[0], y[rr][2]);
+                        y[rr][3] = fma(sd, qb[1], y[rr][3]);
+                    }
+                }
+            }
+            double* pw = Pt + wv * D * KSUB;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+                *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc) = f64x2{y[rr][0], y[rr][1]};
+                *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc + 2) = f64x2{y[rr][2], y[rr][3]};
+            }
+            __syncthreads();
+            f64x2 o01 = {0.0, 0.0}, o23 = {0.0, 0.0};
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                o01 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc);
+                o23 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc + 2);
+            }
+            *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc) = o01;
+            *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc + 2) = o23;
+            __syncthreads();
+        };
+        cholqr(B0, B1);
+        cholqr(B1, B0);
+        for (int it = 0; it < SUB_ITERS; ++it) {
+            product(B0, B1);
+            cholqr(B1, B0);
+        }
+        cholqr(B0, B1);                                        // Q, orthonormal, in B1
+        // ---- Rayleigh-Ritz: H = Q^T S Q, H = E diag(l) E^T; V = Q E with the
+        // columns ordered by decreasing eigenvalue, the first rank kept ----
+        product(B1, B0);                                       // B0 = S Q
+        {
             const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
             double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
 #pragma unroll
             for (int i = i0; i < D; i += 16) {
-                v0 = fma(Yin[i * KSUB + a], Yin[i * KSUB + b], v0);
-                v1 = fma(Yin[(i + 4) * KSUB + a], Yin[(i + 4) * KSUB + b], v1);
-                v2 = fma(Yin[(i + 8) * KSUB + a], Yin[(i + 8) * KSUB + b], v2);
-                v3 = fma(Yin[(i + 12) * KSUB + a], Yin[(i + 12) * KSUB + b], v3);
+                v0 = fma(B1[i * KSUB + a], B0[i * KSUB + b], v0);
+                v1 = fma(B1[(i + 4) * KSUB + a], B0[(i + 4) * KSUB + b], v1);
+                v2 = fma(B1[(i + 8) * KSUB + a], B0[(i + 8) * KSUB + b], v2);
+                v3 = fma(B1[(i + 12) * KSUB + a], B0[(i + 12) * KSUB + b], v3);
             }
             double v = (v0 + v1) + (v2 + v3);
             v += __shfl_xor(v, 1);
@@ -467,134 +556,115 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
             if ((tid & 3) == 0) Gs[g] = v;
         }
         __syncthreads();
-        double Mi[KSUB][KSUB];
-        chol_inv8(Gs, Mi);
-        double y[KSUB];
-#pragma unroll
-        for (int t = 0; t < KSUB; t += 2) {
-            const f64x2 w = *reinterpret_cast<const f64x2*>(Yin + ri * KSUB + t);
-            y[t] = w[0];
-            y[t + 1] = w[1];
-        }
-#pragma unroll
-        for (int cc = 0; cc < 4; ++cc) {                     // q_c = sum_{t <= c} Mi[c][t] y_t
-            double v = 0.0;
-#pragma unroll
-            for (int t = 0; t <= 4 + cc; ++t) {             // rc is 0 or 4
-                const double m = rc ? Mi[4 + cc][t] : (t <= cc ? Mi[cc][t] : 0.0);
-                v = fma(m, y[t], v);
-            }
-            Qout[ri * KSUB + rc + cc] = v;
+        if (wv == 0) {
+            // symmetrise (the two halves come from different sums) and diagonalise
+            const int i = lane >> 3, j = lane & 7;
+            const double hs = 0.5 * (Gs[i * KSUB + j] + Gs[j * KSUB + i]);
+            wave_sync_lds();
+            Gs[lane] = hs;
+            wave_sync_lds();
+            jacobi8(Gs, Es, jcs, lane);
         }
         __syncthreads();
-    };
-    // Y = S Q: wave w takes the terms m in [32 w, 32 w + 32); lane l the
-    // rows l / 2 + 32 r (r < 4) and columns rc .. rc + 3; the four partial
-    // products are summed in wave order.
-    auto product = [&](const double* Q, double* Y) __attribute__((always_inline)) {
-        const int g = lane >> 1, kc = 32 * wv;
-        double y[4][4];
+        double* V = B1;
+        {
+            double qrow[KSUB], ev[KSUB];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
+            for (int t = 0; t < KSUB; ++t) qrow[t] = V[ri * KSUB + t];
 #pragma unroll
-            for (int cc = 0; cc < 4; ++cc) y[rr][cc] = 0.0;
-        const float* s0 = Sf + g * SP + kc;
-#pragma unroll 2
-        for (int m = 0; m < 32; m += 4) {
-            f32x4 sv[4];
+            for (int t = 0; t < KSUB; ++t) ev[t] = Gs[t * (KSUB + 1)];
+            __syncthreads();
 #pragma unroll
-            for (int rr = 0; rr < 4; ++rr) sv[rr] = *reinterpret_cast<const f32x4*>(s0 + 32 * rr * SP + m);
+            for (int jc = 0; jc < KSUB; ++jc) {                 // eigenvector jc goes to column rank(jc)
+                int pos = 0;
 #pragma unroll
-            for (int mm = 0; mm < 4; ++mm) {
-                const double* qr = Q + (kc + m + mm) * KSUB + rc;
-                const f64x2 qa = *reinterpret_cast<const f64x2*>(qr);
-                const f64x2 qb = *reinterpret_cast<const f64x2*>(qr + 2);
+                for (int t = 0; t < KSUB; ++t) pos += (ev[t] > ev[jc]) || (ev[t] == ev[jc] && t < jc);
+                if (pos >= rc && pos < rc + 4) {
+                    double v = 0.0;
 #pragma unroll
-                for (int rr = 0; rr < 4; ++rr) {
-                    const double sd = static_cast<double>(sv[rr][mm]);
-                    y[rr][0] = fma(sd, qa[0], y[rr][0]);
-                    y[rr][1] = fma(sd, qa[1], y[rr][1]);
-                    y[rr][2] = fma(sd, qb[0], y[rr][2]);
-                    y[rr][3] = fma(sd, qb[1], y[rr][3]);
+                    for (int t = 0; t < KSUB; ++t) v = fma(qrow[t], Es[t * KSUB + jc], v);
+                    V[ri * KSUB + pos] = pos < rk ? v : 0.0;
                 }
             }
         }
-        double* pw = Pt + wv * D * KSUB;
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-            *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc) = f64x2{y[rr][0], y[rr][1]};
-            *reinterpret_cast<f64x2*>(pw + (g + 32 * rr) * KSUB + rc + 2) = f64x2{y[rr][2], y[rr][3]};
-        }
         __syncthreads();
-        f64x2 o01 = {0.0, 0.0}, o23 = {0.0, 0.0};
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            o01 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc);
-            o23 += *reinterpret_cast<const f64x2*>(Pt + w * D * KSUB + ri * KSUB + rc + 2);
-        }
-        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc) = o01;
-        *reinterpret_cast<f64x2*>(Y + ri * KSUB + rc + 2) = o23;
-        __syncthreads();
-    };
-    cholqr(B0, B1);
-    cholqr(B1, B0);
-    for (int it = 0; it < SUB_ITERS; ++it) {
-        product(B0, B1);
-        cholqr(B1, B0);
-    }
-    cholqr(B0, B1);                                        // Q, orthonormal, in B1
-    // ---- Rayleigh-Ritz: H = Q^T S Q, H = E diag(l) E^T; V = Q E with the
-    // columns ordered by decreasing eigenvalue, the first rank kept ----
-    product(B1, B0);                                       // B0 = S Q
-    {
-        const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
-        double v0 = 0.0, v1 = 0.0, v2 = 0.0, v3 = 0.0;
-#pragma unroll
-        for (int i = i0; i < D; i += 16) {
-            v0 = fma(B1[i * KSUB + a], B0[i * KSUB + b], v0);
-            v1 = fma(B1[(i + 4) * KSUB + a], B0[(i + 4) * KSUB + b], v1);
-            v2 = fma(B1[(i + 8) * KSUB + a], B0[(i + 8) * KSUB + b], v2);
-            v3 = fma(B1[(i + 12) * KSUB + a], B0[(i + 12) * KSUB + b], v3);
-        }
-        double v = (v0 + v1) + (v2 + v3);
-        v += __shfl_xor(v, 1);
-        v += __shfl_xor(v, 2);
-        if ((tid & 3) == 0) Gs[g] = v;
-    }
-    __syncthreads();
-    if (wv == 0) {
-        // symmetrise (the two halves come from different sums) and diagonalise
-        const int i = lane >> 3, j = lane & 7;
-        const double hs = 0.5 * (Gs[i * KSUB + j] + Gs[j * KSUB + i]);
-        wave_sync_lds();
-        Gs[lane] = hs;
-        wave_sync_lds();
-        jacobi8(Gs, Es, jcs, lane);
-    }
-    __syncthreads();
-    double* V = B1;
-    {
-        double qrow[KSUB], ev[KSUB];
-#pragma unroll
-        for (int t = 0; t < KSUB; ++t) qrow[t] = V[ri * KSUB + t];
-#pragma unroll
-        for (int t = 0; t < KSUB; ++t) ev[t] = Gs[t * (KSUB + 1)];
-        __syncthreads();
-#pragma unroll
-        for (int jc = 0; jc < KSUB; ++jc) {                 // eigenvector jc goes to column rank(jc)
-            int pos = 0;
-#pragma unroll
-            for (int t = 0; t < KSUB; ++t) pos += (ev[t] > ev[jc]) || (ev[t] == ev[jc] && t < jc);
-            if (pos >= rc && pos < rc + 4) {
-                double v = 0.0;
-#pragma unroll
-                for (int t = 0; t < KSUB; ++t) v = fma(qrow[t], Es[t * KSUB + jc], v);
-                V[ri * KSUB + pos] = pos < rk ? v : 0.0;
-            }
-        }
-    }
-    __syncthreads();
 
+        for (int e = tid; e < D * KSUB; e += THREADS) scratch[e] = V[e];
+        return;
+    }
+    // ---- LDL^T of G + lambda I ----
+    {
+        double tr = tid < D ? G[tid * (D + 1)] : 0.0;
+        tr = wave_sum(tr);
+        if (lane == 0) red[wv] = tr;
+        if (tid < 2) col[tid][ZS] = 0.0;
+    }
+    __syncthreads();
+    const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
+    const int p = tid >> 4, q = tid & 15;
+    double A[9][8];                                        // a >= b used; a = 8: no appended rows here
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+            const int i = 16 * a + p, j = 16 * b + q;
+            A[a][b] = G[i * D + j] + (i == j ? lam : 0.0);
+        }
+#pragma unroll
+    for (int b = 0; b < 8; ++b) A[8][b] = 0.0;
+    if (q == 0) {
+#pragma unroll
+        for (int a = 0; a < 8; ++a) col[0][16 * a + p] = A[a][0];
+        if (p < KSUB) col[0][D + p] = 0.0;
+    }
+    __syncthreads();
+    double x[9], cu[8], nrinv;
+    nrinv = -rcp64(fmax(col[0][0], 1e-300));
+#pragma unroll
+    for (int a = 0; a < 8; ++a) x[a] = col[0][16 * a + p > 0 ? 16 * a + p : ZS];
+    x[8] = 0.0;
+#pragma unroll
+    for (int b = 0; b < 8; ++b) cu[b] = col[0][16 * b + q > 0 ? 16 * b + q : ZS];
+    ldl_columns<0>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<1>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<2>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<3>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<4>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<5>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<6>(A, x, cu, nrinv, col, p, q);
+    ldl_columns<7>(A, x, cu, nrinv, col, p, q);
+    double* F = scratch + D * KSUB;
+#pragma unroll
+    for (int a = 0; a < 8; ++a)
+#pragma unroll
+        for (int b = 0; b <= a; ++b) {
+            const int i = 16 * a + p, j = 16 * b + q;
+            if (i >= j) F[i * (i + 1) / 2 + j] = A[a][b];
+        }
+    if (tid == 0) F[LPK] = 0.0;                            // zero slot for the substitutions
+}
+
+__global__ __launch_bounds__(THREADS) void fit_solve_kernel(ResidualArgs r) {
+    __shared__ __attribute__((aligned(16))) double Lp[LPK + 1];
+    __shared__ __attribute__((aligned(16))) double B1[D * KSUB], B2[D * KSUB];
+    __shared__ double xm[D], rm[D], s8[KSUB];
+    const size_t bh = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int rk = r.rank;
+    const double M = static_cast<double>(r.N_pad / BLK);
+    const double* P = r.part + bh * NSPLIT * PSTRIDE;
+    const double* C = r.mat + bh * 3 * D * D + D * D;      // centred X^T R
+    {
+        double v = 0.0;
+        for (int s = 0; s < NSPLIT; ++s) v += P[s * PSTRIDE + 3 * D * D + tid];
+        if (tid < D) xm[tid] = v / M;
+        else rm[tid - D] = v / M;
+    }
+    for (int e = tid; e < D * KSUB; e += THREADS) B1[e] = P[e];
+    for (int e = tid; e < LPK + 1; e += THREADS) Lp[e] = P[D * KSUB + e];
+    __syncthreads();
+    const int ri = tid >> 1, rc = 4 * (tid & 1);
+    double* V = B1;
     // ---- T = C V_r into B2 ----
     {
         const double* crow = C + ri * D;
@@ -617,65 +687,32 @@ __global__ __launch_bounds__(THREADS) void fit_kernel(ResidualArgs r) {
     }
     __syncthreads();
 
-    // ---- LDL^T of G + lambda I with T^T as rows D .. D + KSUB - 1 ----
-    double* Lp = pool;
-    {
-        const int p = tid >> 4, q = tid & 15;
-        double A[9][8];                                    // a >= b used; a = 8: row D + p
-#pragma unroll
-        for (int a = 0; a < 8; ++a)
-#pragma unroll
-            for (int b = 0; b <= a; ++b) {
-                const int i = 16 * a + p, j = 16 * b + q;
-                A[a][b] = G[i * D + j] + (i == j ? lam : 0.0);
-            }
-#pragma unroll
-        for (int b = 0; b < 8; ++b) A[8][b] = B2[(16 * b + q) * KSUB + (p & (KSUB - 1))];
-        if (q == 0) {
-#pragma unroll
-            for (int a = 0; a < 8; ++a) col[0][16 * a + p] = A[a][0];
-            if (p < KSUB) col[0][D + p] = A[8][0];
-        }
-        __syncthreads();
-        double x[9], cu[8], nrinv;
-        nrinv = -rcp64(fmax(col[0][0], 1e-300));
-#pragma unroll
-        for (int a = 0; a < 8; ++a) x[a] = col[0][16 * a + p > 0 ? 16 * a + p : ZS];
-        x[8] = col[0][p < KSUB ? D + p : ZS];
-#pragma unroll
-        for (int b = 0; b < 8; ++b) cu[b] = col[0][16 * b + q > 0 ? 16 * b + q : ZS];
-        ldl_columns<0>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<1>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<2>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<3>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<4>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<5>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<6>(A, x, cu, nrinv, col, p, q);
-        ldl_columns<7>(A, x, cu, nrinv, col, p, q);
-        // the factor (stored column k = L_.k D_kk) and the eliminated rows y = L^{-1} T
-#pragma unroll
-        for (int a = 0; a < 8; ++a)
-#pragma unroll
-            for (int b = 0; b <= a; ++b) {
-                const int i = 16 * a + p, j = 16 * b + q;
-                if (i >= j) Lp[i * (i + 1) / 2 + j] = A[a][b];
-            }
-        if (tid == 0) Lp[LPK] = 0.0;                       // zero slot for the back substitution
-        if (p < KSUB) {
-#pragma unroll
-            for (int b = 0; b < 8; ++b) B0[(16 * b + q) * KSUB + p] = A[8][b];
-        }
-    }
-    __syncthreads();
 
-    // ---- back substitution L^T Z = D^{-1} y: wave w solves columns 2w, 2w + 1 ----
+    // ---- L y = T (unit lower), then L^T Z = D^{-1} y (unit upper): wave w
+    // solves columns 2w, 2w + 1, lane the rows 2 lane, 2 lane + 1 ----
     {
-        const int c0 = 2 * wv, j0 = 2 * lane;              // lane: rows j0, j0 + 1
+        const int c0 = 2 * wv, j0 = 2 * lane;
         if (c0 < rk) {
-            double u00 = B0[j0 * KSUB + c0], u01 = B0[j0 * KSUB + c0 + 1];
-            double u10 = B0[(j0 + 1) * KSUB + c0], u11 = B0[(j0 + 1) * KSUB + c0 + 1];
+            double u00 = B2[j0 * KSUB + c0], u01 = B2[j0 * KSUB + c0 + 1];
+            double u10 = B2[(j0 + 1) * KSUB + c0], u11 = B2[(j0 + 1) * KSUB + c0 + 1];
             const double rd0 = rcp64(fmax(Lp[j0 * (j0 + 1) / 2 + j0], 1e-300));
             const double rd1 = rcp64(fmax(Lp[(j0 + 1) * (j0 + 2) / 2 + j0 + 1], 1e-300));
+            // forward: y_j final at step j; rows i > j lose a_ij y_j / d_j
+#pragma unroll 2
+            for (int j = 0; j < D; ++j) {
+                const int o = j >> 1;
+                const bool odd = j & 1;
+                const double rdj = readlane64(odd ? rd1 : rd0, o);
+                const double w0 = readlane64(odd ? u10 : u00, o) * rdj;
+                const double w1 = readlane64(odd ? u11 : u01, o) * rdj;
+                const double a0 = Lp[j0 > j ? j0 * (j0 + 1) / 2 + j : LPK];
+                const double a1 = Lp[j0 + 1 > j ? (j0 + 1) * (j0 + 2) / 2 + j : LPK];
+                u00 = fma(-a0, w0, u00);
+                u01 = fma(-a0, w1, u01);
+                u10 = fma(-a1, w0, u10);
+                u11 = fma(-a1, w1, u11);
+            }
+            // back: z_i = u_i / d_i at step i; rows j < i lose a_ij z_i
 #pragma unroll 2
             for (int i = D - 1; i >= 0; --i) {
                 const int o = i >> 1;
@@ -876,7 +913,9 @@ hipError_t launch_residual(const ResidualArgs& r, hipStream_t s) {
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(reduce_kernel, dim3(3 * D * D / RED_PER_WG, bh), dim3(THREADS), 0, s, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(fit_kernel, dim3(bh), dim3(THREADS), 0, s, r);
+    hipLaunchKernelGGL(fit_factor_kernel, dim3(2, bh), dim3(THREADS), 0, s, r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(fit_solve_kernel, dim3(bh), dim3(THREADS), 0, s, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(apply_kernel, dim3((r.N_pad + APPLY_ROWS - 1) / APPLY_ROWS, bh), dim3(THREADS), 0, s, r);
     return hipGetLastError();
