@@ -163,7 +163,7 @@ __global__ __launch_bounds__(THREADS) void gram_kernel(ResidualArgs r) {
 // the column sums give the probe means xm, rm.
 constexpr int RED_PER_WG = 4 * THREADS;
 constexpr size_t PSTRIDE = 3 * D * D + 2 * D;   // doubles per slice of the partial sums
-constexpr int ZS = D + KSUB;                    // the zero slot of a published column
+constexpr int ZS = D;                           // the zero slot of a published column
 static_assert(3 * D * D % RED_PER_WG == 0 && THREADS == 2 * D, "reduce tiling");
 
 __global__ __launch_bounds__(THREADS) void reduce_kernel(ResidualArgs r) {
@@ -259,20 +259,11 @@ __device__ __forceinline__ void chol_inv8(const double* Gs, double (&Mi)[KSUB][K
     }
 }
 
-// Columns 16 KB .. 16 KB + 15 of the right-looking LDL^T elimination.
-// Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b and, in
-// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Entering step k,
-// x and cu hold column k's entries of the thread's rows and columns, zero for
-// rows / columns <= k (so finished entries are left alone), and rinv the
-// reciprocal pivot; the multipliers are cu * rinv.  Step k: the owners of column k + 1
-// (q == (k + 1) % 16) apply step k to it and publish it in col[(k + 1) % 2];
-// after the barrier every thread reads column k + 1 and applies the rest of
-// step k, the reads overlapping the update.  Blocks left of column block KB
-// are finished and skipped.
+// Step 16 KB + kk of the elimination (see ldl_columns).
 template <int KB>
-__device__ __forceinline__ void ldl_step(int kk, double (&A)[9][8], const double (&x)[9], const double (&cu)[8],
-                                         double nrinv, double (&xn)[9], double (&cn)[8], double& nrn,
-                                         double (*col)[D + KSUB + 1], int p, int q) {
+__device__ __forceinline__ void ldl_step(int kk, double (&A)[8][8], const double (&x)[8], const double (&cu)[8],
+                                         double nrinv, double (&xn)[8], double (&cn)[8], double& nrn,
+                                         double (*col)[D + 1], int p, int q) {
     constexpr int NB = KB < 7 ? KB + 1 : KB;
     const int k = 16 * KB + kk;
     double u[8];                                           // minus the multipliers of step k
@@ -282,17 +273,15 @@ __device__ __forceinline__ void ldl_step(int kk, double (&A)[9][8], const double
         double* cw = col[(k + 1) & 1];
         if (kk < 15) {
 #pragma unroll
-            for (int a = KB; a < 9; ++a) A[a][KB] = fma(x[a], u[KB], A[a][KB]);
+            for (int a = KB; a < 8; ++a) A[a][KB] = fma(x[a], u[KB], A[a][KB]);
 #pragma unroll
             for (int a = KB; a < 8; ++a) cw[16 * a + p] = A[a][KB];
-            if (p < KSUB) cw[D + p] = A[8][KB];
             u[KB] = 0.0;
         } else {
 #pragma unroll
-            for (int a = NB; a < 9; ++a) A[a][NB] = fma(x[a], u[NB], A[a][NB]);
+            for (int a = NB; a < 8; ++a) A[a][NB] = fma(x[a], u[NB], A[a][NB]);
 #pragma unroll
             for (int a = NB; a < 8; ++a) cw[16 * a + p] = A[a][NB];
-            if (p < KSUB) cw[D + p] = A[8][NB];
             u[NB] = 0.0;
         }
     }
@@ -303,30 +292,28 @@ __device__ __forceinline__ void ldl_step(int kk, double (&A)[9][8], const double
     const double dn = ck[k + 1];
 #pragma unroll
     for (int a = KB; a < 8; ++a) xn[a] = ck[16 * a + p > k + 1 ? 16 * a + p : ZS];
-    xn[8] = ck[p < KSUB ? D + p : ZS];
 #pragma unroll
     for (int bb = KB; bb < 8; ++bb) cn[bb] = ck[16 * bb + q > k + 1 ? 16 * bb + q : ZS];
 #pragma unroll
     for (int bb = KB; bb < 8; ++bb)
 #pragma unroll
-        for (int a = bb; a < 9; ++a) A[a][bb] = fma(x[a], u[bb], A[a][bb]);
+        for (int a = bb; a < 8; ++a) A[a][bb] = fma(x[a], u[bb], A[a][bb]);
     nrn = -rcp64(fmax(dn, 1e-300));
 }
 
 // Columns 16 KB .. 16 KB + 15 of the right-looking LDL^T elimination.
-// Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b and, in
-// A[8][b], entry (D + p, 16 b + q) of the appended rows.  Entering step k,
-// x and cu hold column k's entries of the thread's rows and columns, zero for
-// rows / columns <= k (so finished entries are left alone), and nrinv minus
-// the reciprocal pivot.  Step k: the owners of column k + 1
+// Thread (p, q) holds A[a][b] = entry (16 a + p, 16 b + q) for a >= b.
+// Entering step k, x and cu hold column k's entries of the thread's rows and
+// columns, zero for rows / columns <= k (so finished entries are left alone),
+// and nrinv minus the reciprocal pivot.  Step k: the owners of column k + 1
 // (q == (k + 1) % 16) apply step k to it and publish it in col[(k + 1) % 2];
 // after the barrier every thread reads column k + 1 and applies the rest of
 // step k, the reads overlapping the update.  Two register sets alternate
 // between the steps.  Blocks left of column block KB are finished and skipped.
 template <int KB>
-__device__ __forceinline__ void ldl_columns(double (&A)[9][8], double (&x)[9], double (&cu)[8], double& nrinv,
-                                            double (*col)[D + KSUB + 1], int p, int q) {
-    double x2[9], c2[8], nr2;
+__device__ __forceinline__ void ldl_columns(double (&A)[8][8], double (&x)[8], double (&cu)[8], double& nrinv,
+                                            double (*col)[D + 1], int p, int q) {
+    double x2[8], c2[8], nr2;
 #pragma unroll 1
     for (int kk = 0; kk < 16; kk += 2) {
         ldl_step<KB>(kk, A, x, cu, nrinv, x2, c2, nr2, col, p, q);
@@ -414,7 +401,7 @@ __global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
     __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32)
     __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB];
     __shared__ __attribute__((aligned(16))) double Pt[4 * D * KSUB];   // partial products, one per wave
-    __shared__ double col[2][D + KSUB + 1];                // slot D + KSUB holds 0
+    __shared__ double col[2][D + 1];                       // slot D holds 0
     __shared__ double Gs[KSUB * KSUB], Es[KSUB * KSUB], jcs[2 * KSUB];
     __shared__ double red[THREADS / 64];
     const size_t bh = blockIdx.y;
@@ -602,7 +589,7 @@ __global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
     __syncthreads();
     const double lam = static_cast<double>(r.ridge) * (red[0] + red[1] + red[2] + red[3]) / D;
     const int p = tid >> 4, q = tid & 15;
-    double A[9][8];                                        // a >= b used; a = 8: no appended rows here
+    double A[8][8];                                        // a >= b used
 #pragma unroll
     for (int a = 0; a < 8; ++a)
 #pragma unroll
@@ -610,19 +597,15 @@ __global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
             const int i = 16 * a + p, j = 16 * b + q;
             A[a][b] = G[i * D + j] + (i == j ? lam : 0.0);
         }
-#pragma unroll
-    for (int b = 0; b < 8; ++b) A[8][b] = 0.0;
     if (q == 0) {
 #pragma unroll
         for (int a = 0; a < 8; ++a) col[0][16 * a + p] = A[a][0];
-        if (p < KSUB) col[0][D + p] = 0.0;
     }
     __syncthreads();
-    double x[9], cu[8], nrinv;
+    double x[8], cu[8], nrinv;
     nrinv = -rcp64(fmax(col[0][0], 1e-300));
 #pragma unroll
     for (int a = 0; a < 8; ++a) x[a] = col[0][16 * a + p > 0 ? 16 * a + p : ZS];
-    x[8] = 0.0;
 #pragma unroll
     for (int b = 0; b < 8; ++b) cu[b] = col[0][16 * b + q > 0 ? 16 * b + q : ZS];
     ldl_columns<0>(A, x, cu, nrinv, col, p, q);
