@@ -369,7 +369,7 @@ __device__ __forceinline__ void lse2_combine(float& m, float& s, float mo, float
     m = mn;
 }
 
-__global__ __launch_bounds__(THREADS) void route_err_kernel(RouteArgs a) {
+__global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void route_err_kernel(RouteArgs a) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(16))) uint16_t khi[BLK * ERR_PITCH], klo[BLK * ERR_PITCH];
     __shared__ float xch[2][2][2][32];    // [parity][centroid half][m, s][lane]
@@ -479,12 +479,25 @@ __global__ __launch_bounds__(THREADS) void route_err_kernel(RouteArgs a) {
         }
         // t = expm1(delta) e^{-m}: expm1 keeps small deviations exact when m
         // is small; for m > 1 the form e^{delta - m} - e^{-m} cannot overflow
+        // One exponential per value (the lane's m picks the form): e^{delta - m}
+        // when m > 1; otherwise e^delta, or for |delta| < 0.5 the Taylor series
+        // of expm1 up to delta^7 (first omitted term below 2.5e-7 of the result).
         const float em = __expf(-m);
         const bool big = m > 1.0f;
+        const float shift = big ? m : 0.0f;
         float s = 0.0f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-            const float t = big ? __expf(dl[r] - m) - em : expm1f(dl[r]) * em;
+            const float x = dl[r];
+            const float e = __expf(x - shift);
+            float p = fmaf(x, 1.0f / 5040.0f, 1.0f / 720.0f);
+            p = fmaf(x, p, 1.0f / 120.0f);
+            p = fmaf(x, p, 1.0f / 24.0f);
+            p = fmaf(x, p, 1.0f / 6.0f);
+            p = fmaf(x, p, 0.5f);
+            p = fmaf(x, p, 1.0f);
+            const float em1 = fabsf(x) < 0.5f ? x * p : e - 1.0f;
+            const float t = big ? e - em : em1 * em;
             s = fmaf(t, t, s);
         }
         // the other 16 keys of the half sit in lane l ^ 32
