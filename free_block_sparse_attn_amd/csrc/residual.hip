@@ -797,7 +797,8 @@ __global__ __launch_bounds__(THREADS) void apply_kernel(ResidualArgs r) {
         cc[u] = cg[c0 + u];
     }
     uint16_t* O = static_cast<uint16_t*>(r.out) + bh * r.N_pad * D;
-    for (int base = blockIdx.x * APPLY_ROWS; base < (blockIdx.x + 1) * APPLY_ROWS; base += RU * (THREADS / 16)) {
+    const int row0 = static_cast<int>(blockIdx.x) * APPLY_ROWS;
+    for (int base = row0; base < row0 + APPLY_ROWS; base += RU * (THREADS / 16)) {
         u32x4 w[RU];
 #pragma unroll
         for (int s = 0; s < RU; ++s) {
