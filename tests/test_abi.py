@@ -213,3 +213,19 @@ def test_lvsa_capacity_bounds_every_row():
     for phase in range(wl.anchor_period):
         _, cnt = routing.route_lvsa(lo, hi, wl.window, wl.anchors, phase, 0)
         assert cnt.max() <= cap
+
+
+@pytest.mark.parametrize("B,H,N_pad", [(1, 2, 128), (2, 3, 64 * 70), (1, 12, 32768)])
+def test_residual_workspace_matches_the_documented_layout(lib, B, H, N_pad):
+    """sparse_attn_residual_workspace() is the sum of the blocks the header
+    lists (Mp = 64 ceil(nb / 64), K = min(8, nb) key chunks, d = 128)."""
+    d, bh, nb = 128, B * H, N_pad // 64
+    mp = 64 * ((nb + 63) // 64)
+    kc = min(8, nb)
+    f64 = bh * 8 * (3 * d * d + 2 * d) + bh * 3 * d * d          # Gram partial sums; X^T X, X^T R, R^T R
+    f32 = (2 * bh * mp * d                                         # X and the dense output at the probes
+           + bh * (d * d + d)                                      # W, c
+           + kc * bh * mp * d + kc * bh * mp                       # per-chunk dense output and lse
+           + bh * 2 * d * 8)                                       # Z and V_r
+    b16 = bh * mp * d                                              # gathered probe queries
+    assert lib.sparse_attn_residual_workspace(shape(B=B, H=H, N=N_pad, N_pad=N_pad)) == 8 * f64 + 4 * f32 + 2 * b16
