@@ -75,7 +75,7 @@ def check_pool(wl, pooled_o, res):
             assert np.array_equal(res["exp8"][..., i], pooled_o[n + "exp"]), n
 
 
-def check_route(wl, pooled_o, res, coords, step=0):
+def check_route(wl, pooled_o, res, coords, step=0, scale=1.0):
     """Stage-wise (the GPU's pooled features) and end-to-end (the oracle's)."""
     for feats in (res, pooled_o):
         if wl.rule == "topk":
@@ -86,12 +86,12 @@ def check_route(wl, pooled_o, res, coords, step=0):
             # GPU error logs L(a, j) (stored key-block-major) against the fp64
             # definition; selection bit-exact on the GPU's logs
             elog = np.swapaxes(res["ekey"], -1, -2)
-            idx, cnt = routing.route_error(res["qbar"], res["kbar"], res["kcount"], elog, 1.0, wl.topk)
+            idx, cnt = routing.route_error(res["qbar"], res["kbar"], res["kcount"], elog, scale, wl.topk)
             assert np.array_equal(res["idx"], idx)
             assert np.array_equal(res["cnt"], cnt)
             break          # the logs are not bit-reproducible: stage-wise only
         elif wl.rule == "topk_cov":
-            idx, cnt = routing.route_topk_cov(feats["qbar"], feats["kbar"], feats["kcov"], 1.0, wl.topk)
+            idx, cnt = routing.route_topk_cov(feats["qbar"], feats["kbar"], feats["kcov"], scale, wl.topk)
             assert np.array_equal(res["idx"], idx)
             assert np.array_equal(res["cnt"], cnt)
             break          # ln M_j is not bit-reproducible: stage-wise only
@@ -108,7 +108,7 @@ def check_route(wl, pooled_o, res, coords, step=0):
             break
         else:
             ri, rc, si, sc = routing.route_triage(feats["qbar"], feats["kbar"], feats["klam"],
-                                                  feats["kcount"], 1.0, wl.n_keep, wl.n_refine)
+                                                  feats["kcount"], scale, wl.n_keep, wl.n_refine)
             assert np.array_equal(res["idx"][..., :ri.shape[-1]], ri)
             assert np.array_equal(res["cnt"], rc)
             assert np.array_equal(res["idx2"], si)
@@ -119,10 +119,10 @@ def check_route(wl, pooled_o, res, coords, step=0):
 ELOG_TOL = 1e-3   # |L_gpu - L| : three bf16 hi/lo MFMA passes (~16 bits per factor), fp32 sums
 
 
-def check_error_logs(wl, res, elog, k, rows=None):
+def check_error_logs(wl, res, elog, k, rows=None, scale=1.0):
     """L(a, j) of the query blocks `rows` (all when None) against the oracle's fp64 value."""
     sel = np.arange(wl.nb) if rows is None else np.asarray(rows)
-    ref = routing.error_logs(res["qbar"][:, :, sel], k, res["kbar"], wl.N, 1.0)
+    ref = routing.error_logs(res["qbar"][:, :, sel], k, res["kbar"], wl.N, scale)
     got = elog[:, :, sel]
     assert np.array_equal(np.isneginf(got), np.isneginf(ref))
     fin = np.isfinite(ref)
@@ -171,6 +171,30 @@ def test_parity_reduced(wid, size):
         # pad rows are written as zero
         assert np.all(res["out"][:, :, wl.N:] == 0)
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
+
+
+@pytest.mark.parametrize("kind", ["topk", "error", "cov", "triage", "order1", "global"])
+def test_parity_softmax_scale(kind):
+    """A softmax scale other than 1 (0.37) through routing (the error pass,
+    the covariance key, Triage's tiers), every compensation form, the skim
+    tier and, for the top-k layer, the residual pass's dense probes."""
+    from dataclasses import replace
+    sc = 0.37
+    wl = replace(_batch2_workload(kind), B=1)
+    print(f"\n[case] {wl.name} scale={sc} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords, scale=sc)
+    check_route(wl, pooled_o, res, coords, 0, scale=sc)
+    if kind == "error":
+        check_error_logs(wl, res, np.swapaxes(res["ekey"], -1, -2), k, scale=sc)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl), scale=sc)
+    worst = check_out(wl, res, ref, all_rows(wl))
+    if kind == "topk":
+        res, corr, fit = run_residual(wl, dev, coords, scale=sc)
+        heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
+        worst = max(worst, check_residual(wl, q, k, v, res, corr, fit, heads, scale=sc))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
 def _batch2_workload(kind):
@@ -444,34 +468,36 @@ def test_parity_triage_mxfp4_full_size_sampled():
 RES_PHASE, RES_RIDGE, RES_RANK = 3, 1e-3, 8
 
 
-def run_residual(wl, dev, coords, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK):
+def run_residual(wl, dev, coords, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK, scale=1.0):
     """GPU sparse forward, then the probe-fitted residual pass on its output."""
     import free_block_sparse_attn_amd as fbsa
-    res = gc.run_gpu(wl, dev, coords)
+    res = gc.run_gpu(wl, dev, coords, scale=scale)
     q, k, v = dev
     out = torch.from_numpy(res["out"]).to(torch.bfloat16).cuda()
-    r = fbsa.sparse_attn_residual(q, k, v, out, wl.N, 1.0, phase, ridge, rank)
+    r = fbsa.sparse_attn_residual(q, k, v, out, wl.N, scale, phase, ridge, rank)
     torch.cuda.synchronize()
     fit = {n: r[n].cpu().numpy() for n in ("xp", "od", "W", "c")}
     return res, out.float().cpu().numpy(), fit
 
 
-def check_residual(wl, q, k, v, res, corr, fit, heads_rows, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK):
+def check_residual(wl, q, k, v, res, corr, fit, heads_rows, phase=RES_PHASE, ridge=RES_RIDGE, rank=RES_RANK,
+                   scale=1.0):
     """Dense probe rows, the fit on the GPU's probe data, and the corrected rows."""
     from oracle import residual
     nb = wl.nb
     rows = residual.probe_rows(wl.N, nb, phase)
     worst = 0.0
     for (b, h), check_rows in heads_rows.items():
-        od = residual.probe_dense(q[b, h], k[b, h], v[b, h], wl.N, 1.0, rows)
-        assert np.abs(fit["od"][b, h, :nb] - od).max() <= gc.BF16_TOL
+        od = residual.probe_dense(q[b, h], k[b, h], v[b, h], wl.N, scale, rows)
+        perr = np.abs(fit["od"][b, h, :nb] - od).max(axis=1)
+        assert perr.max() <= gc.BF16_TOL, (b, h, np.round(perr, 4))
         assert np.array_equal(fit["xp"][b, h, :nb], res["out"][b, h, rows])
         # stage-wise: the oracle's fit on the GPU's probe outputs
         X = fit["xp"][b, h, :nb].astype(np.float64)
         W, c = residual.fit_residual(X, fit["od"][b, h, :nb] - X, ridge, rank)
-        scale = max(np.abs(W).max(), np.abs(c).max(), 1e-12)
-        assert np.abs(fit["W"][b, h] - W).max() <= 1e-3 * scale, np.abs(fit["W"][b, h] - W).max()
-        assert np.abs(fit["c"][b, h] - c).max() <= 1e-3 * scale
+        wscale = max(np.abs(W).max(), np.abs(c).max(), 1e-12)
+        assert np.abs(fit["W"][b, h] - W).max() <= 1e-3 * wscale, np.abs(fit["W"][b, h] - W).max()
+        assert np.abs(fit["c"][b, h] - c).max() <= 1e-3 * wscale
         # end to end: o + c + o W on the GPU's sparse output, dense rows at the probes
         O = res["out"][b, h].astype(np.float64)
         ref = O + c + O @ W
