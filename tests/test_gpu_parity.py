@@ -197,6 +197,26 @@ def test_parity_softmax_scale(kind):
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("kind", ["topk", "lvsa", "triage", "order1", "global", "cov", "error", "mxfp4"])
+def test_parity_single_head(kind):
+    """H = 1 (and B = 1): no kernel may assume more than one head."""
+    from dataclasses import replace
+    wl = replace(_batch2_workload(kind), B=1, H=1)
+    print(f"\n[case] {wl.name} H=1 N={wl.N} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords, 0)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    if kind == "topk":
+        res, corr, fit = run_residual(wl, dev, coords)
+        worst = max(worst, check_residual(wl, q, k, v, res, corr, fit, {(0, 0): np.arange(wl.N_pad)}))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 def _batch2_workload(kind):
     from dataclasses import replace
     from workloads import configs as C
