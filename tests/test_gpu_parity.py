@@ -217,6 +217,27 @@ def test_parity_single_head(kind):
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("kind", ["topk", "triage", "error", "global", "mxfp4"])
+def test_parity_no_ragged_tail(kind):
+    """N a multiple of 64 (4 x 16 x 16 = 1024 tokens): the last block is full."""
+    from dataclasses import replace
+    wl = replace(_batch2_workload(kind), B=1, T=4, Y=16, X=16)
+    assert wl.N % 64 == 0 and wl.N == wl.N_pad
+    print(f"\n[case] {wl.name} N={wl.N} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res)
+    check_route(wl, pooled_o, res, coords, 0)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    if kind == "topk":
+        res, corr, fit = run_residual(wl, dev, coords)
+        heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
+        worst = max(worst, check_residual(wl, q, k, v, res, corr, fit, heads))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 def _batch2_workload(kind):
     from dataclasses import replace
     from workloads import configs as C
