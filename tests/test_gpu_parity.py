@@ -173,7 +173,7 @@ def test_parity_reduced(wid, size):
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
 
 
-@pytest.mark.parametrize("kind", ["topk", "error", "cov", "triage", "order1", "global"])
+@pytest.mark.parametrize("kind", ["topk", "error", "cov", "triage", "order1", "global", "lvsa", "mxfp4"])
 def test_parity_softmax_scale(kind):
     """A softmax scale other than 1 (0.37) through routing (the error pass,
     the covariance key, Triage's tiers), every compensation form, the skim
