@@ -38,7 +38,10 @@ constexpr int D = 128;
 constexpr int THREADS = 256;
 constexpr int NSPLIT = 8;                  // probe slices of the Gram partial sums
 constexpr int KSUB = 8;                    // block width of the subspace iteration (rank <= KSUB)
-constexpr int SUB_ITERS = 16;
+constexpr int SUB_MIN = 16;                // simultaneous-iteration steps: at least,
+constexpr int SUB_MAX = 32;                // at most,
+constexpr int SUB_CHECK = 4;               // and every this many a convergence check:
+constexpr double SUB_TOL = 1e-10;          // sum of squared sines between the spans
 
 __device__ __forceinline__ int probe_row(int a, int N, int phase) {
     const int n = min(BLK, N - BLK * a);
@@ -379,7 +382,8 @@ __device__ void jacobi8(double* Hs, double* Es, double* cs, int lane) {
 // G + lambda I do not depend on each other, so they run side by side:
 //   fit_factor_kernel, workgroups (0, head) and (1, head):
 //     0: simultaneous iteration on S = R^T R (fp32 copy in LDS, fp64
-//        products), KSUB columns, Cholesky QR after every product, then
+//        products), KSUB columns, Cholesky QR after every product, 16 to 32
+//        steps (until the leading rank columns' span settles), then
 //        Rayleigh-Ritz; V_r (fp64) into the workspace;
 //     1: LDL^T of G + lambda I by right-looking elimination in registers,
 //        thread (p, q) of a 16 x 16 grid holding the entries (16 a + p,
@@ -399,7 +403,7 @@ __global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
     constexpr int SP = D + 4;                               // fp32 row stride of S in LDS
     constexpr int POOL = D * SP / 2;
     __shared__ __attribute__((aligned(16))) double pool[POOL];   // S (fp32)
-    __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB];
+    __shared__ __attribute__((aligned(16))) double B0[D * KSUB], B1[D * KSUB], Qp[D * KSUB];
     __shared__ __attribute__((aligned(16))) double Pt[4 * D * KSUB];   // partial products, one per wave
     __shared__ double col[2][D + 1];                       // slot D holds 0
     __shared__ double Gs[KSUB * KSUB], Es[KSUB * KSUB], jcs[2 * KSUB];
@@ -519,9 +523,28 @@ __global__ __launch_bounds__(THREADS) void fit_factor_kernel(ResidualArgs r) {
         };
         cholqr(B0, B1);
         cholqr(B1, B0);
-        for (int it = 0; it < SUB_ITERS; ++it) {
+        for (int e = tid; e < D * KSUB; e += THREADS) Qp[e] = B0[e];
+        // Stop once the span of the leading `rank` columns moved by less than
+        // SUB_TOL (sum of squared sines of the principal angles, rank minus
+        // the squared Frobenius norm of Qp_r^T Q_r) over SUB_CHECK steps.
+        for (int it = 0; it < SUB_MAX; ++it) {
             product(B0, B1);
             cholqr(B1, B0);
+            if (it % SUB_CHECK == SUB_CHECK - 1) {
+                const int g = tid >> 2, a = g / KSUB, b = g % KSUB, i0 = tid & 3;
+                double v = 0.0;
+                for (int i = i0; i < D; i += 4) v = fma(Qp[i * KSUB + a], B0[i * KSUB + b], v);
+                v += __shfl_xor(v, 1);
+                v += __shfl_xor(v, 2);
+                double o = ((tid & 3) == 0 && a < rk && b < rk) ? v * v : 0.0;
+                o = wave_sum(o);
+                if (lane == 0) red[wv] = o;
+                __syncthreads();
+                const double moved = rk - ((red[0] + red[1]) + (red[2] + red[3]));
+                if (it + 1 >= SUB_MIN && moved < SUB_TOL) break;      // the same decision in every thread
+                for (int e = tid; e < D * KSUB; e += THREADS) Qp[e] = B0[e];
+                __syncthreads();
+            }
         }
         cholqr(B0, B1);                                        // Q, orthonormal, in B1
         // ---- Rayleigh-Ritz: H = Q^T S Q, H = E diag(l) E^T; V = Q E with the

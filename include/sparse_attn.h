@@ -333,9 +333,11 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
  * R ~ b + X B by ridge regression on the centred probes (lambda = ridge *
  * tr(Xc^T Xc) / d, intercept not penalised; fp64 normal equations solved by
  * an LDL^T elimination) and restricted to the span of the top `rank` right
- * singular vectors of R (simultaneous iteration on R^T R, 8 columns, 16 steps
- * of Cholesky QR, then Rayleigh-Ritz on the 8-column span; the leading `rank`
- * Ritz vectors): W = B P, c = b P.  Every valid
+ * singular vectors of R (simultaneous iteration on R^T R, 8 columns, Cholesky
+ * QR after each of 16 to 32 steps, stopping early once the leading `rank`
+ * columns' span moves by less than 1e-10 (squared sines) over 4 steps; then
+ * Rayleigh-Ritz on the 8-column span, the leading `rank` Ritz vectors):
+ * W = B P, c = b P.  Every valid
  * row then gets o + c + o W, evaluated in fp32 as o + c + (o Z) V_r^T with
  * W = Z V_r^T, each probe row its dense output (RNE to bf16); pad rows 0.
  *

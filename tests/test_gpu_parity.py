@@ -239,6 +239,27 @@ def test_parity_no_ragged_tail(kind):
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("kind", ["topk", "error", "order1", "global"])
+def test_parity_one_kept_block(kind):
+    """top-k = 1: capacity-1 lists, every other block compensated."""
+    from dataclasses import replace
+    wl = replace(_batch2_workload(kind), B=1, keep_pct=1)
+    assert wl.topk == 1
+    print(f"\n[case] {wl.name} topk=1 N={wl.N} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_route(wl, pooled_o, res, coords, 0)
+    assert np.all(res["cnt"] == 1)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    if kind == "topk":
+        res, corr, fit = run_residual(wl, dev, coords)
+        heads = {(0, h): np.arange(wl.N_pad) for h in range(wl.H)}
+        worst = max(worst, check_residual(wl, q, k, v, res, corr, fit, heads))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 def _batch2_workload(kind):
     from dataclasses import replace
     from workloads import configs as C
