@@ -111,7 +111,7 @@ def skim_weight_slack(L: np.ndarray, eps: float) -> np.ndarray:
 
 def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
                exact, skim=(), kmom=None, fp8=None, a: int = 0, blk: int = BLK, hbar=None,
-               slack_eps=None):
+               slack_eps=None, skim_dlog2=None):
     """Compensated rule for the valid rows Qa [r, d] of query block a, one head.
 
     k, v: [N_pad, d]; kbar, vbar: exact fp64 means [nb, d]; kcount [nb];
@@ -120,9 +120,15 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
     fp8: the skim tier's copies: dict(q8, k8, v8 codes [N_pad, d], qexp, kexp,
     vexp [nb]) for e4m3, or dict(q4, qs4, k4, ks4, v4, vs4) for mxfp4.
     Returns (o [r, d], lse [r]); with slack_eps, also a per-row bound [r] on
-    how far o moves when the skim logits (log2 units) are evaluated off by up
-    to slack_eps: the weights' code decisions (skim_weight_slack), their
-    continuous change, and the denominator's.
+    max_i |o'_i - o_i| over every evaluation o' whose skim logits (log2 units)
+    are off by at most slack_eps each: with S_N a bound on the numerator's
+    change per component (the weights' code decisions, skim_weight_slack,
+    and their continuous change, times max_i |v~_i| of each key) and S_D on
+    the denominator's, o' - o = (N' - N) / D' + o (D - D') / D', so
+    |o' - o| <= (S_N + |o|_inf S_D) / (D - S_D).
+    skim_dlog2: optional list (one per skim block, in ascending block order)
+    of [r, n_j] offsets added to that tile's logits in log2 units before
+    anything else (a perturbed evaluation, for testing the bound).
     """
     Qa = np.asarray(Qa, np.float64)
     nb = kbar.shape[0]
@@ -156,6 +162,9 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
             vt = e4m3.decode(fp8["v8"][tj]) * 2.0 ** int(fp8["vexp"][j])
             skim_terms.append((scale * l, vt))
 
+    if skim_dlog2 is not None:
+        skim_terms = [(lg + np.asarray(dl, np.float64) / LOG2E, vt)
+                      for (lg, vt), dl in zip(skim_terms, skim_dlog2)]
     m = np.max(np.concatenate([x for x in logits] + [t[0] for t in skim_terms], axis=1), axis=1)
     D = np.zeros(Qa.shape[0])
     Nt = np.zeros_like(Qa)
@@ -186,7 +195,8 @@ def rule_block(Qa, k, v, N: int, scale: float, comp: int, kbar, vbar, kcount,
         Nt += scale * np.einsum("ru,uro->ro", alpha, QH)
     if slack_eps is not None:
         o = Nt / D[:, None]
-        return o, m + np.log(D), (slack + slack_den * np.abs(o).max(axis=1)) / D
+        assert np.all(slack_den < D), "skim logit slack too large for a bound"
+        return o, m + np.log(D), (slack + slack_den * np.abs(o).max(axis=1)) / (D - slack_den)
     return Nt / D[:, None], m + np.log(D)
 
 

@@ -402,23 +402,173 @@ def test_skim_slack_covers_the_row_reference():
     assert d[0, 1] == abs(alt[0, 1] - base[0, 1])
 
 
-def test_rule_block_slack_bounds_a_perturbed_evaluation():
-    # the output of the rule with the skim logits moved by up to eps stays
-    # within the reported slack of the unperturbed output
-    rng = np.random.default_rng(5)
-    N, d = 192, 128
-    q = rng.standard_normal((N, d)) * 0.5
-    k = rng.standard_normal((N, d)) * 0.5
+# ---- skim weights pinned on hand-computed e4m3 values ----
+#
+# Reading (Triage page, its fast low-precision tier; the e4m3 format is the
+# configured one): per row and tile, c = ceil(max L) and
+# p~ = 2^(c - 8) e4m3(2^(8 + L - c)).  e4m3 grid: [2^k, 2^(k+1)) has step
+# 2^(k-3) for k >= -6 (so [128, 256) steps by 16, [256, 448] by 32), below
+# 2^-6 subnormal steps of 2^-9; 448 is the largest value (saturation).
+# Every y below sits at least 1/4 step from a rounding midpoint, so the fp64
+# evaluation of 2^(8 + L - c) (off by ~1e-16 relative) cannot change a code.
+
+def _skim_rows():
+    """(L rows, expected p~) from y = 2^(8 + L - c) values chosen by hand."""
+    cases = []
+    # c = 3 (max L = 3 + log2(240/256) = 2.907): y 240 -> 240 (the row max),
+    # 196 -> 192, 201 -> 208, 99 -> 96 ([64, 128) steps by 8), 2^-7.3 =
+    # 0.006346 = 3.25 subnormal steps -> 3 * 2^-9, 2^-11 (under half a step) -> 0
+    c = 3.0
+    y = np.array([240.0, 196.0, 201.0, 99.0, 2.0 ** -7.3, 2.0 ** -11])
+    q = np.array([240.0, 192.0, 208.0, 96.0, 3 * 2.0 ** -9, 0.0])
+    cases.append((np.log2(y) + c - 8.0, q * 2.0 ** (c - 8.0)))
+    # max L exactly an integer (4): c = 4 itself, y = 256 -> 256 (p~ = 16); a
+    # weight 15.3 binades down, y = 2^-7.3 -> 3 * 2^-9 as above; y = 16.6 ->
+    # 16 ([16, 32) steps by 2)
+    c = 4.0
+    y = np.array([256.0, 2.0 ** -7.3, 16.6])
+    q = np.array([256.0, 3 * 2.0 ** -9, 16.0])
+    L = np.log2(y) + c - 8.0
+    L[0] = 4.0
+    cases.append((L, q * 2.0 ** (c - 8.0)))
+    return cases
+
+
+def skim_weight_pin_violations(fn):
+    """Rows where fn(L) differs from the hand-computed weights (any entry)."""
+    bad = []
+    for i, (L, want) in enumerate(_skim_rows()):
+        got = fn(L[None, :])[0]
+        if not np.array_equal(got, want):
+            bad.append((i, got, want))
+    return bad
+
+
+def test_skim_weights_hand_computed():
+    assert skim_weight_pin_violations(attention.skim_weights) == []
+
+
+def test_skim_weight_pins_reject_wrong_readings():
+    # a plausible mistake in the reference, the headroom or the rounding must
+    # fail the pins above
+    def with_ref(refn, head=8.0, rnd=e4m3.round_to_e4m3):
+        def fn(L):
+            c = refn(L.max(axis=1, keepdims=True))
+            return np.exp2(c - head) * rnd(np.exp2(head + L - c))
+        return fn
+
+    def toward_zero(x):
+        # truncation onto the e4m3 grid instead of round-to-nearest
+        v = e4m3.round_to_e4m3(x)
+        return np.where(v > x, e4m3.decode(e4m3.encode(v) - 1), v)
+
+    wrong = {
+        "floor reference": with_ref(np.floor),
+        "floor + 1 reference": with_ref(lambda m: np.floor(m) + 1.0),
+        "2^7 headroom": with_ref(np.ceil, head=7.0),
+        "2^9 headroom": with_ref(np.ceil, head=9.0),
+        "truncating rounding": with_ref(np.ceil, rnd=toward_zero),
+    }
+    assert with_ref(np.ceil)(_skim_rows()[0][0][None]).tolist() == \
+        attention.skim_weights(_skim_rows()[0][0][None]).tolist()
+    for name, fn in wrong.items():
+        assert skim_weight_pin_violations(fn), name
+
+
+# ---- the skim slack bound under perturbed evaluations ----
+
+def _skim_case(seed, d=32, nb=4, spread=0.9):
+    """One head with e4m3 copies: exact block 0, skim blocks 1..nb-1, query block 0."""
+    rng = np.random.default_rng(seed)
+    N = 64 * nb
+    q = rng.standard_normal((N, d)) * spread
+    k = rng.standard_normal((N, d)) * spread
     v = rng.standard_normal((N, d))
-    nb = 3
     kbar = np.stack([k[64 * j:64 * j + 64].mean(0) for j in range(nb)])
     vbar = np.stack([v[64 * j:64 * j + 64].mean(0) for j in range(nb)])
     kcount = np.full(nb, 64)
-    codes = {n: e4m3.encode(x * 2.0 ** -(-3)) for n, x in (("q8", q), ("k8", k))}
-    fp8 = dict(q8=codes["q8"], k8=codes["k8"], v8=e4m3.encode(v * 8.0),
-               qexp=np.full(nb, -3), kexp=np.full(nb, -3), vexp=np.full(nb, -3))
-    o, l, slack = attention.rule_block(q[:64], k, v, N, 1.0, 0, kbar, vbar, kcount, [0], [1, 2],
-                                       None, fp8, 0, slack_eps=1e-3)
-    assert slack.shape == (64,) and np.all(slack >= 0.0)
-    o2, l2 = attention.rule_block(q[:64], k, v, N, 1.0, 0, kbar, vbar, kcount, [0], [1, 2], None, fp8, 0)
-    assert np.array_equal(o, o2) and np.array_equal(l, l2)
+    ex = {n: e4m3.block_exponent(np.abs(x).max()) for n, x in (("q", q), ("k", k), ("v", v))}
+    fp8 = dict(q8=e4m3.encode(q * 2.0 ** -ex["q"]), k8=e4m3.encode(k * 2.0 ** -ex["k"]),
+               v8=e4m3.encode(v * 2.0 ** -ex["v"]), qexp=np.full(nb, ex["q"]),
+               kexp=np.full(nb, ex["k"]), vexp=np.full(nb, ex["v"]))
+    skim = list(range(1, nb))
+    # the skim tiles' logits in log2 units (to place adversarial shifts)
+    qd = e4m3.decode(fp8["q8"][:64]) * 2.0 ** ex["q"]
+    L = [(qd @ (e4m3.decode(fp8["k8"][64 * j:64 * j + 64]) * 2.0 ** ex["k"]).T) * attention.LOG2E
+         for j in skim]
+    args = (q[:64], k, v, N, 1.0, 0, kbar, vbar, kcount, [0], skim, None, fp8, 0)
+    return args, L
+
+
+def _bound_violations(args, base_shift, shifts, eps):
+    o, _, slack = attention.rule_block(*args, slack_eps=eps, skim_dlog2=base_shift)
+    worst = 0.0
+    bad = 0
+    for sh in shifts:
+        assert all(np.abs(x).max() <= eps for x in sh)
+        o2, _ = attention.rule_block(*args, skim_dlog2=[b + x for b, x in zip(base_shift, sh)])
+        dev = np.abs(o2 - o).max(axis=1)
+        worst = max(worst, (dev / slack).max())
+        bad += int(np.sum(dev > slack))
+    return bad, worst
+
+
+def test_skim_slack_bounds_random_perturbations():
+    eps = 5e-4
+    rng = np.random.default_rng(11)
+    worst = 0.0
+    for seed in range(12):
+        args, L = _skim_case(seed)
+        zero = [np.zeros_like(x) for x in L]
+        shifts = [[rng.uniform(-eps, eps, x.shape) for x in L] for _ in range(6)]
+        shifts += [[np.full(x.shape, s * eps) for x in L] for s in (-1.0, 1.0)]
+        shifts += [[eps * rng.choice([-1.0, 1.0], x.shape) for x in L] for _ in range(4)]
+        bad, w = _bound_violations(args, zero, shifts, eps)
+        assert bad == 0, (seed, w)
+        worst = max(worst, w)
+    assert worst > 0.0
+
+
+def _adversarial_base(L, eps):
+    """Base shifts that put weights on e4m3 rounding midpoints and each row's
+    tile maximum just below an integer, so that +-eps flips codes and the
+    row reference c."""
+    base = []
+    for Lt in L:
+        c = np.ceil(Lt.max(axis=1, keepdims=True))
+        y = np.exp2(8.0 + Lt - c)
+        # midpoint between the grid values around y (normal range: 8 steps per binade)
+        k = np.floor(np.log2(np.maximum(y, 2.0 ** -6)))
+        step = np.exp2(k - 3.0)
+        mid = (np.floor(y / step) + 0.5) * step
+        sh = np.where((y > 2.0 ** -6) & (y < 440.0), np.log2(mid) - np.log2(y), 0.0)
+        # the row maximum to an integer minus eps / 4 (so c is decided by eps)
+        am = Lt.argmax(axis=1)
+        r = np.arange(Lt.shape[0])
+        sh[r, am] = (np.ceil(Lt[r, am]) - eps / 4) - Lt[r, am]
+        base.append(sh)
+    return base
+
+
+def test_skim_slack_bounds_code_and_reference_flips():
+    eps = 5e-4
+    rng = np.random.default_rng(12)
+    for seed in range(6):
+        args, L = _skim_case(100 + seed)
+        base = _adversarial_base(L, eps)
+        shifts = [[np.full(x.shape, s * eps) for x in L] for s in (-1.0, -0.5, 0.5, 1.0)]
+        shifts += [[eps * rng.choice([-1.0, 1.0], x.shape) for x in L] for _ in range(4)]
+        bad, _ = _bound_violations(args, base, shifts, eps)
+        assert bad == 0, seed
+
+
+def test_skim_slack_without_code_decisions_is_caught(monkeypatch):
+    # the flip test above has teeth: a bound that leaves out the code
+    # decisions (continuous change only) fails on it
+    eps = 5e-4
+    monkeypatch.setattr(attention, "skim_weight_slack", lambda L, e: np.zeros_like(L))
+    args, L = _skim_case(100)
+    base = _adversarial_base(L, eps)
+    shifts = [[np.full(x.shape, s * eps) for x in L] for s in (-1.0, 1.0)]
+    bad, worst = _bound_violations(args, base, shifts, eps)
+    assert bad > 0 and worst > 1.0
