@@ -20,8 +20,8 @@ from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER
                    SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR, SA_SKIM_E4M3, SA_SKIM_MXFP4)
 
 __all__ = [
-    "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
-    "sparse_attn_residual",
+    "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd",
+    "sparse_attn_lvsa_capacity", "sparse_attn_residual",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
     "SA_ROUTE_TOPK", "SA_ROUTE_LVSA", "SA_ROUTE_TRIAGE", "SA_ROUTE_TOPK_COV",
@@ -67,64 +67,63 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
     """Block means (fp32), counts and the optional centroid planes / moments /
     mean moment H_bar (with its 64-partial scratch) / covariance log-norms
     ln ||H_j - H_bar||_2 (`cov`, implies `global_moment`) / spreads / e4m3
-    copies / MXFP4 copies (`fp4`).  The bf16 centroid planes (what the bf16 forward reads) are
-    produced by default for bf16 inputs with d == 128.
+    copies / MXFP4 copies (`fp4`).  What the bf16 forward reads - the fp16
+    centroid planes and the fp16 copy of V - is produced by default for bf16
+    inputs with d == 128.
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
     """
+    return _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out)
+
+
+def _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out):
     lib = _lib.load()
     _contig(q, k, v)
     B, H, Np, d = q.shape
     nb = Np // BLK
     dev = q.device
-    if out is not None:
-        g = out.get
-        _lib.check(lib.sparse_attn_pool(
-            ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
-            _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-            _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
-            _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
-            *_fp4_ptrs(out), _stream(q)))
-        return out
-    out = {
-        "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
-        "kbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
-        "vbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
-        "kcount": torch.empty(nb, dtype=torch.int32, device=dev),
-    }
-    if cent is None:
-        cent = q.dtype == torch.bfloat16 and d == 128
-    if cent:
-        nbc = BLK * ((nb + BLK - 1) // BLK)
-        out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.bfloat16, device=dev)
-    if moments:
-        out["kmom"] = torch.empty(B, H, nb, d * d, dtype=torch.bfloat16, device=dev)   # MFMA operand order
-    if global_moment or cov:
-        out["hbar"] = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)          # value-major
-        out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
-    if cov:
-        out["kcov"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
-    if spreads:
-        out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
-    if fp8:
-        for n in ("q8", "k8"):
-            out[n] = torch.empty(B, H, Np, d, dtype=torch.uint8, device=dev)
-        out["v8"] = torch.empty(B, H, nb, d, BLK, dtype=torch.uint8, device=dev)   # block-transposed
-        out["exp8"] = torch.empty(B, H, nb, 3, dtype=torch.int8, device=dev)
-    if fp4:
-        for n in ("q4", "k4"):
-            out[n] = torch.empty(B, H, Np, d // 2, dtype=torch.uint8, device=dev)
-        for n in ("qs4", "ks4"):
-            out[n] = torch.empty(B, H, Np, d // 32, dtype=torch.uint8, device=dev)
-        out["v4"] = torch.empty(B, H, nb, d, BLK // 2, dtype=torch.uint8, device=dev)   # block-transposed
-        out["vs4"] = torch.empty(B, H, nb, d, dtype=torch.uint8, device=dev)
+    if out is None:
+        out = {
+            "qbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+            "kbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+            "vbar": torch.empty(B, H, nb, d, dtype=torch.float32, device=dev),
+            "kcount": torch.empty(nb, dtype=torch.int32, device=dev),
+        }
+        if cent is None:
+            cent = q.dtype == torch.bfloat16 and d == 128
+        if cent:
+            nbc = BLK * ((nb + BLK - 1) // BLK)
+            out["cent"] = torch.empty(B, H, 4, nbc, d, dtype=torch.float16, device=dev)
+            out["v16"] = torch.empty(B, H, Np, d, dtype=torch.float16, device=dev)
+        if moments:
+            out["kmom"] = torch.empty(B, H, nb, d * d, dtype=torch.float16, device=dev)    # MFMA operand order
+            out["kmom_exp"] = torch.empty(B, H, nb, dtype=torch.int8, device=dev)
+        if global_moment or cov:
+            out["hbar"] = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)          # value-major
+            out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
+        if cov:
+            out["kcov"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
+        if spreads:
+            out["klam"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
+        if fp8:
+            for n in ("q8", "k8"):
+                out[n] = torch.empty(B, H, Np, d, dtype=torch.uint8, device=dev)
+            out["v8"] = torch.empty(B, H, nb, d, BLK, dtype=torch.uint8, device=dev)   # block-transposed
+            out["exp8"] = torch.empty(B, H, nb, 3, dtype=torch.int8, device=dev)
+        if fp4:
+            for n in ("q4", "k4"):
+                out[n] = torch.empty(B, H, Np, d // 2, dtype=torch.uint8, device=dev)
+            for n in ("qs4", "ks4"):
+                out[n] = torch.empty(B, H, Np, d // 32, dtype=torch.uint8, device=dev)
+            out["v4"] = torch.empty(B, H, nb, d, BLK // 2, dtype=torch.uint8, device=dev)   # block-transposed
+            out["vs4"] = torch.empty(B, H, nb, d, dtype=torch.uint8, device=dev)
     g = out.get
-    _lib.check(lib.sparse_attn_pool(
-        ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
-        _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
-        _ptr(g("cent")), _ptr(g("kmom")), _ptr(g("hbar")), _ptr(g("hbar_ws")), _ptr(g("kcov")),
-        _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
-        *_fp4_ptrs(out), _stream(q)))
+    head = [ctypes.byref(_shape(q, N)), _dtype(q), _ptr(q), _ptr(k), _ptr(v),
+            _ptr(out["qbar"]), _ptr(out["kbar"]), _ptr(out["vbar"]), _ptr(out["kcount"]),
+            _ptr(g("cent")), _ptr(g("v16")), _ptr(g("kmom")), _ptr(g("kmom_exp")), _ptr(g("hbar"))]
+    tail = [_ptr(g("kcov")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
+            *_fp4_ptrs(out), _stream(q)]
+    _lib.check(lib.sparse_attn_pool(*head, _ptr(g("hbar_ws")), *tail))
     return out
 
 
@@ -216,7 +215,8 @@ def sparse_attn_fwd(q, k, v, N: int, scale: float, comp: int, pooled: dict, idx,
     cap2 = idx2.shape[-1] if idx2 is not None else 0
     _lib.check(lib.sparse_attn_fwd(
         ctypes.byref(_shape(q, N)), _dtype(q), comp, scale, _ptr(q), _ptr(k), _ptr(v),
-        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("kcount")), _ptr(g("kmom")), _ptr(g("hbar")),
+        _ptr(g("kbar")), _ptr(g("vbar")), _ptr(g("cent")), _ptr(g("v16")), _ptr(g("kcount")), _ptr(g("kmom")),
+        _ptr(g("kmom_exp")), _ptr(g("hbar")),
         _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")), skim_fmt, *_fp4_ptrs(pooled),
         _ptr(idx), _ptr(cnt), cap, _ptr(idx2), _ptr(cnt2), cap2,
         _ptr(out), _ptr(lse), _stream(q)))

@@ -59,15 +59,17 @@ def load(path: str = LIB_PATH):
                            "(python free_block_sparse_attn_amd/build.py)")
     lib = ctypes.CDLL(path)
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
-    lib.sparse_attn_pool.argtypes = [ctypes.POINTER(Shape), i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
-                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
+    # shape, dtype, q, k, v, qbar, kbar, vbar, kcount, cent, v16, kmom, kmom_exp, hbar, hbar_ws, kcov,
+    # klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream
+    lib.sparse_attn_pool.argtypes = [ctypes.POINTER(Shape), i32] + [vp] * 26
     lib.sparse_attn_pool.restype = i32
     lib.sparse_attn_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(RouteSpec), vp, vp, vp, vp,
                                       vp, vp, i32, vp, vp, i32, vp]
     lib.sparse_attn_route.restype = i32
-    lib.sparse_attn_fwd.argtypes = [ctypes.POINTER(Shape), i32, i32, f32, vp, vp, vp, vp, vp, vp, vp, vp,
-                                    vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp,
-                                    vp, vp, i32, vp, vp, i32, vp, vp, vp]
+    # shape, dtype, comp, scale, q, k, v, kbar, vbar, cent, v16, kcount, kmom, kmom_exp, hbar, q8, k8,
+    # v8, exp8, skim_fmt, q4, k4, v4, qs4, ks4, vs4, idx, cnt, cap, idx2, cnt2, cap2, out, lse, stream
+    lib.sparse_attn_fwd.argtypes = [ctypes.POINTER(Shape), i32, i32, f32] + [vp] * 15 + [i32] + [vp] * 6 + \
+                                   [vp, vp, i32, vp, vp, i32, vp, vp, vp]
     lib.sparse_attn_fwd.restype = i32
     lib.sparse_attn_lvsa_capacity.argtypes = [vp, vp, i32, i32, i32]
     lib.sparse_attn_lvsa_capacity.restype = i32

@@ -78,17 +78,22 @@ const char* sparse_attn_last_error(void) { return g_last_error.c_str(); }
 
 int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 
-sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
-                           float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* kmom,
-                           float* hbar, float* hbar_ws, float* kcov, float* klam,
-                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
-                           uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The pooling call's validation and launch.
+sa_status pool_impl(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
+                    float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* v16,
+                    void* kmom, int8_t* kmom_exp, float* hbar, float* hbar_ws, float* kcov, float* klam,
+                    uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
+                    uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
     if (empty) return ok();
     NEED(q); NEED(k); NEED(v); NEED(qbar); NEED(kbar); NEED(vbar); NEED(kcount);
-    MAYBE(cent); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(kcov); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
+    MAYBE(cent); MAYBE(v16); MAYBE(kmom); MAYBE(hbar); MAYBE(hbar_ws); MAYBE(kcov); MAYBE(klam); MAYBE(q8); MAYBE(k8); MAYBE(v8); MAYBE(exp8);
     MAYBE(q4); MAYBE(k4); MAYBE(v4); MAYBE(qs4); MAYBE(ks4); MAYBE(vs4);
     const int fp4 = (q4 != nullptr) + (k4 != nullptr) + (v4 != nullptr) + (qs4 != nullptr) + (ks4 != nullptr) +
                     (vs4 != nullptr);
@@ -97,15 +102,31 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q,
     if (fp8 != 0 && fp8 != 4) return fail(SA_ERR_INVALID_ARG, "q8, k8, v8 and exp8 must be given together");
     const bool bf16_128 = dtype == SA_BF16 && shape->d == 128;
     if (cent && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "cent needs bf16 inputs with d == 128");
+    if (v16 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "v16 needs bf16 inputs with d == 128");
     if (kmom && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "kmom needs bf16 inputs with d == 128");
+    if ((kmom != nullptr) != (kmom_exp != nullptr)) return fail(SA_ERR_INVALID_ARG, "kmom and kmom_exp go together");
     if ((hbar != nullptr) != (hbar_ws != nullptr)) return fail(SA_ERR_INVALID_ARG, "hbar and hbar_ws go together");
     if (hbar && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "hbar needs bf16 inputs with d == 128");
     if (kcov && !hbar) return fail(SA_ERR_INVALID_ARG, "kcov needs hbar (M_j is taken against H_bar)");
     if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
     if (fp4 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "MXFP4 copies need bf16 inputs with d == 128");
     sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
-                   cent, kmom, hbar, hbar_ws, kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4};
+                   cent, static_cast<uint16_t*>(v16), kmom, kmom_exp, hbar, hbar_ws, kcov, klam,
+                   q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4};
     return hip_result(sa::launch_pool(a, dtype == SA_BF16, stream), "pool");
+}
+
+}  // namespace
+
+extern "C" {
+
+sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
+                           float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* v16,
+                           void* kmom, int8_t* kmom_exp, float* hbar, float* hbar_ws, float* kcov, float* klam,
+                           uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
+                           uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
+    return pool_impl(shape, dtype, q, k, v, qbar, kbar, vbar, kcount, cent, v16, kmom, kmom_exp, hbar, hbar_ws,
+                     kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream);
 }
 
 int32_t sparse_attn_lvsa_capacity(const int32_t* lo, const int32_t* hi, int32_t nb, int32_t window, int32_t anchors) {
@@ -226,7 +247,8 @@ sa_status sparse_attn_residual(const sa_shape* shape, sa_dtype dtype, float scal
 
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale, const void* q,
                           const void* k, const void* v, const float* kbar, const float* vbar, const void* cent,
-                          const int32_t* kcount, const void* kmom, const float* hbar, const uint8_t* q8,
+                          const void* v16, const int32_t* kcount, const void* kmom, const int8_t* kmom_exp,
+                          const float* hbar, const uint8_t* q8,
                           const uint8_t* k8, const uint8_t* v8,
                           const int8_t* exp8, sa_skim_format skim_fmt, const uint8_t* q4, const uint8_t* k4,
                           const uint8_t* v4, const uint8_t* qs4, const uint8_t* ks4, const uint8_t* vs4,
@@ -242,13 +264,13 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
     const int nb = shape->N_pad / 64;
     if (nb > MAX_BLOCKS) return fail(SA_ERR_UNSUPPORTED, "at most %d blocks per sequence, got %d", MAX_BLOCKS, nb);
     if (empty) return ok();
-    NEED(q); NEED(k); NEED(v); NEED(out); MAYBE(lse); MAYBE(kbar); MAYBE(vbar); MAYBE(cent);
+    NEED(q); NEED(k); NEED(v); NEED(out); MAYBE(lse); MAYBE(kbar); MAYBE(vbar); MAYBE(cent); MAYBE(v16);
     if (cap < 0 || cap2 < 0) return fail(SA_ERR_INVALID_ARG, "cap and cap2 must be >= 0");
     if (cap > 0) { NEED(idx); NEED(cnt); }
     const bool skim = idx2 != nullptr && cap2 > 0;
     if (skim) { NEED(cnt2); }
     if (comp >= SA_COMP_ORDER0) { NEED(kcount); }
-    if (comp == SA_COMP_ORDER1_BLOCK) { NEED(kmom); }
+    if (comp == SA_COMP_ORDER1_BLOCK) { NEED(kmom); NEED(kmom_exp); }
     if (comp == SA_COMP_ORDER1_GLOBAL) { NEED(hbar); }
     if (dtype == SA_F32) {
         if (comp >= SA_COMP_ORDER0) { NEED(kbar); NEED(vbar); }
@@ -257,6 +279,7 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
         if (skim) return fail(SA_ERR_UNSUPPORTED, "fp32 forward has no fp8 skim tier");
     } else {
         if (shape->d != 128) return fail(SA_ERR_UNSUPPORTED, "bf16 forward supports d == 128 only");
+        NEED(v16);
         if (comp >= SA_COMP_ORDER0) { NEED(cent); }
         if (skim && skim_fmt == SA_SKIM_E4M3) { NEED(q8); NEED(k8); NEED(v8); NEED(exp8); }
         if (skim && skim_fmt == SA_SKIM_MXFP4) { NEED(q4); NEED(k4); NEED(v4); NEED(qs4); NEED(ks4); NEED(vs4); }
@@ -266,7 +289,7 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
     if (comp == SA_COMP_DROP && cap == 0 && !skim)
         return fail(SA_ERR_INVALID_ARG, "drop mode needs exact or skim lists");
     sa::FwdArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, static_cast<int>(comp), scale, q, k, v,
-                  kbar, vbar, cent, kcount, kmom, hbar, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4,
+                  kbar, vbar, cent, v16, kcount, kmom, kmom_exp, hbar, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4,
                   static_cast<int>(skim_fmt), idx, cnt, cap, idx2, cnt2, cap2, out, lse,
                   shape->N, shape->N_pad, 0, 0};
     if (dtype == SA_F32) return hip_result(sa::launch_fwd_f32(a, stream), "fwd_f32");

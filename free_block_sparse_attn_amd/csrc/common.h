@@ -32,6 +32,26 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float a) {
     return static_cast<uint16_t>(pack_bf16x2(a, 0.0f) & 0xFFFFu);
 }
 
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2;
+
+// Round-to-nearest-even fp32 -> fp16 pair, packed low = a, high = b
+// (v_cvt_pk_f16_f32 on gfx950); magnitudes beyond 65504 become inf.
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) {
+    f16x2 r;
+    r[0] = static_cast<_Float16>(a);
+    r[1] = static_cast<_Float16>(b);
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float a) {
+    return static_cast<uint16_t>(pack_f16x2(a, 0.0f) & 0xFFFFu);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+    return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
 // Lanes l and l ^ 32 combined (v_permlane32_swap, no LDS round trip): with
 // both operands = x the swap returns (own, other) in the low half of the wave
 // and (other, own) in the high half, so a symmetric combination of the two

@@ -16,13 +16,17 @@
 // brought into LDS feeds 64 query rows.
 //   S^T = K Q^T   v_mfma_f32_32x32x16_bf16; A = K rows from LDS
 //                 (ds_read_b128), B = Q^T held in AGPRs through the exact
-//                 and centroid phases (the skim tiles, last, reuse them).
+//                 phase (then an fp16 copy for the centroid phase; the skim
+//                 tiles, last, reuse the registers).
 //                 A lane owns one query row per 32-row block; its 16
 //                 accumulator entries are 16 of the 32 keys of a half tile,
 //                 the other 16 sit in lane l ^ 32.
-//   O^T += V^T P^T  B = P^T straight from S's accumulators (rounded to bf16),
-//                 A = V^T read from the row-major LDS copy of V with
-//                 ds_read_b64_tr_b16 (4 consecutive keys of one d per read).
+//   O^T += V^T P^T  v_mfma_f32_32x32x16_f16; B = P^T straight from S's
+//                 accumulators (rounded to fp16: 11 significant bits, where
+//                 bf16 would keep 8), A = V^T read from the row-major LDS copy
+//                 of the pooling pass's fp16 copy of V (exact for bf16 values
+//                 within fp16's range) with ds_read_b64_tr_b16 (4
+//                 consecutive keys of one d per read).
 // The P^T operand's key order follows S's accumulator layout: within each
 // 16-key MFMA step, slot s holds key s with bits 2 and 3 swapped; the V^T
 // reads use the same order.
@@ -40,24 +44,22 @@
 //
 // Softmax reference.  P = 2^(c2 s - m) with a per-row reference m that only
 // moves when a half tile's weights overflow a bound (sum of one lane's 16
-// weights > 2^40; the first tile always does, from m = -1e30).  Then m
-// becomes the ceiling of the row max over that half and the accumulators are
-// rescaled; otherwise no row max is computed at all.  Any m keeps the bf16
-// weights and the fp32 sums exact to rounding as long as nothing overflows,
-// which the bound guarantees.  The denominator is the fp32 sum of the
-// unrounded weights and lse is m + log2 of it (exact to fp32 rounding); the
-// MFMA consumes P rounded to bf16, so o = N / D scales the exact convex
-// combination by sum(bf16(p)) / sum(p), within 2^-8 (the bf16 unit roundoff)
-// of 1.  The first-order Taylor forms (per-block H_j, global H_bar) instead
-// sum the bf16-rounded pairs with v_dot2_f32_bf16, which cancels that rounding
-// in o (lse then within 2^-8 relative of the unrounded sum): their H terms
-// leave less of the bf16 error budget.  Only there, because on gfx950 each
-// v_dot2 holds up the next MFMA issue (8 per 16 MFMAs cost ~60 cycles), while
-// FMA, v_exp_f32 and v_cvt_pk_bf16_f32 run under the MFMAs almost for free.
+// weights > 2^15, so no fp16 weight exceeds 2^15; the first tile always does,
+// from m = -1e30).  Then m becomes the ceiling of the row max over that half
+// minus 6, so the largest weight lands in (2^5, 2^6], and the accumulators
+// are rescaled; otherwise no row max is computed at all.  Any such m keeps the
+// fp16 weights and the fp32 sums exact to rounding: nothing overflows, and
+// fp16's subnormal range starts 20 binades below the largest weight.  The
+// denominator is the fp32 sum of the same fp16-rounded weights the MFMA
+// consumes (v_dot2 of each packed pair against ones), so P's rounding
+// cancels in o = N / D (PISA's single normalisation: numerator and
+// denominator see the same weights) and lse is within 2^-11 relative of the
+// unrounded sum.
 //
-// Centroid pseudo-keys go through the same MFMA path as 64-wide tiles (means
-// split into bf16 high + low parts so the fp32 means keep ~16 bits), with
-// bias log2(n_j) and -inf at the exact blocks, and a lazily updated max.
+// Centroid pseudo-keys go through the same MFMA path as 64-wide tiles, in
+// fp16 on both products (means split into fp16 high + low parts, so the fp32
+// means keep ~22 bits; Q^T converted to fp16 once), with bias log2(n_j) and
+// -inf at the exact blocks, and a lazily updated max.
 //
 // Workgroup = one wave; consecutive query blocks of one head are mapped to
 // the same XCD so their overlapping K/V blocks are shared through its L2.
@@ -75,7 +77,13 @@ constexpr int HALFB = TILEB / 2;           // 32 rows (8 KiB)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 constexpr float M_INIT = -1.0e30f;         // "no reference yet" (finite: 2^(-inf - M_INIT) = 0)
-constexpr float OVF = 1099511627776.0f;    // 2^40: per-lane half-tile weight sum that moves m
+// The weights enter the MFMA in fp16 (largest finite value 65504): a new
+// reference is the ceiling of the row max minus REF_HEAD, so the largest
+// weight starts in (2^5, 2^6] (well clear of fp16's subnormal range, which
+// starts 20 binades below it), and it moves again when one lane's 16 weights
+// of a half tile sum past OVF = 2^15, so no weight ever exceeds 2^15.
+constexpr float REF_HEAD = 6.0f;
+constexpr float OVF = 32768.0f;
 constexpr uint32_t RSRC_WORD3 = 0x00020000u;  // raw buffer descriptor, 32-bit data format (gfx9)
 
 // Physical 16-byte chunk of logical chunk c (0..15) in LDS row `row`.  The
@@ -162,7 +170,7 @@ __device__ __forceinline__ void zero_rows(uint8_t* buf, int r0) {
 struct State {
     f32x16 o[4][2];        // O^T[d-block][row-block]
     float m[2];            // reference (log2 units, an integer) per row block
-    float l[2];            // this lane's partial row sums of the bf16-rounded P
+    float l[2];            // this lane's partial row sums of the fp16-rounded P
     float a1[2];           // global first order: partial sums of e^{s q.k_bar_j} 2^{-m} over skipped j
 };
 
@@ -182,23 +190,25 @@ __device__ __forceinline__ void rescale_row(State& st, int rb, float mnew) {
 __device__ __forceinline__ void rescale_lazy(State& st, int rb, float mx) {
     const bool need = st.m[rb] == M_INIT ? mx > -INFINITY : mx > st.m[rb] + 8.0f;
     if (__ballot(need)) {
-        if (need) rescale_row(st, rb, ceilf(mx));
+        if (need) rescale_row(st, rb, ceilf(mx) - REF_HEAD);
     }
 }
 
-// Sum of a bf16 pair in fp32 (v_dot2 with ones).
-__device__ __forceinline__ float sum_bf16_pair(uint32_t pair, float acc) {
-    const bf16x2 ones = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair), ones, acc, false);
+// P = 2^(c2 s - m) for the 16 logits a lane holds in one row block of a
+// 32-key half, as the two fp16 B operands of that half's PV k-steps
+// (p0: accumulator entries 0-7, p1: 8-15), and the fp32 sum of the
+// fp16-rounded weights (v_dot2 of each packed pair against ones).
+// 16 FMA + 16 v_exp_f32 + 8 v_cvt_pk_f16_f32 + 8 v_dot2.  (Converting each
+// pair's halves back to fp32 and adding them, 32 plain VALU instead of the 8
+// dot2, measured 9 % slower on the Wan layer: with 72 VALU per 16-MFMA
+// region the VALU no longer fits under the matrix core.)
+// Sum of an fp16 pair in fp32 (v_dot2 with ones).
+__device__ __forceinline__ float sum_f16_pair(uint32_t pair, float acc) {
+    const f16x2 ones = {static_cast<_Float16>(1.0f), static_cast<_Float16>(1.0f)};
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair), ones, acc, false);
 }
 
-// P = 2^(c2 s - m) for the 16 logits a lane holds in one row block of a
-// 32-key half, as the two bf16 B operands of that half's PV k-steps
-// (p0: accumulator entries 0-7, p1: 8-15), and the sum of the weights: of
-// the bf16-rounded ones (RS) or of the fp32 ones.
-// 16 FMA + 16 v_exp_f32 + 8 v_cvt_pk_bf16_f32 + 8 v_dot2 (RS) or 16 v_add.
-template <bool RS>
-__device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+__device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, f16x8& p0, f16x8& p1, float& ls) {
     const float negm = -m;
     float acc = 0.f;
     u32x4 w0, w1;
@@ -206,20 +216,18 @@ __device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x
     for (int e = 0; e < 8; e += 2) {
         const float x0 = __builtin_amdgcn_exp2f(fmaf(s[e], c2, negm));
         const float x1 = __builtin_amdgcn_exp2f(fmaf(s[e + 1], c2, negm));
-        w0[e >> 1] = pack_bf16x2(x0, x1);
-        if constexpr (RS) acc = sum_bf16_pair(w0[e >> 1], acc);
-        else acc += x0 + x1;
+        w0[e >> 1] = pack_f16x2(x0, x1);
+        acc = sum_f16_pair(w0[e >> 1], acc);
     }
 #pragma unroll
     for (int e = 0; e < 8; e += 2) {
         const float x0 = __builtin_amdgcn_exp2f(fmaf(s[8 + e], c2, negm));
         const float x1 = __builtin_amdgcn_exp2f(fmaf(s[8 + e + 1], c2, negm));
-        w1[e >> 1] = pack_bf16x2(x0, x1);
-        if constexpr (RS) acc = sum_bf16_pair(w1[e >> 1], acc);
-        else acc += x0 + x1;
+        w1[e >> 1] = pack_f16x2(x0, x1);
+        acc = sum_f16_pair(w1[e >> 1], acc);
     }
-    p0 = __builtin_bit_cast(bf16x8, w0);
-    p1 = __builtin_bit_cast(bf16x8, w1);
+    p0 = __builtin_bit_cast(f16x8, w0);
+    p1 = __builtin_bit_cast(f16x8, w1);
     ls = acc;
 }
 
@@ -227,8 +235,7 @@ __device__ __forceinline__ void exp_rb(const f32x16& s, float m, float c2, bf16x
 // overflowed the bound (first tile, or a large logit), move the reference of
 // the affected rows to the ceiling of their max over this half, rescale, and
 // redo the weights.  Then fold the half's sums into the row sums.
-template <bool RS>
-__device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float c2, bf16x8 pb[2][2], float ls[2]) {
+__device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float c2, f16x8 pb[2][2], float ls[2]) {
     if (__builtin_expect(__ballot(ls[0] > OVF || ls[1] > OVF) != 0, 0)) {
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
@@ -237,8 +244,8 @@ __device__ __forceinline__ void settle_half(State& st, const f32x16 s[2], float 
             for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[rb][r]);
             mx = pair_max(mx) * c2;
             const bool need = pair_max(ls[rb]) > OVF;
-            if (need) rescale_row(st, rb, ceilf(mx));
-            exp_rb<RS>(s[rb], st.m[rb], c2, pb[0][rb], pb[1][rb], ls[rb]);
+            if (need) rescale_row(st, rb, ceilf(mx) - REF_HEAD);
+            exp_rb(s[rb], st.m[rb], c2, pb[0][rb], pb[1][rb], ls[rb]);
         }
     }
     st.l[0] += ls[0];
@@ -283,12 +290,12 @@ __device__ __forceinline__ void pv_offsets(uint32_t oa[4], uint32_t ob[4]) {
     }
 }
 
-__device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* pa, const uint8_t* pb) {
+__device__ __forceinline__ f16x8 tr_read_pair(const uint8_t* pa, const uint8_t* pb) {
     // keys 16kk + 4h + e (slots 0..3) and 16kk + 8 + 4h + e (slots 4..7)
     const i16x4 va = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pa));
     const i16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(pb));
     const i16x8 v8 = {va[0], va[1], va[2], va[3], vb[0], vb[1], vb[2], vb[3]};
-    return __builtin_bit_cast(bf16x8, v8);
+    return __builtin_bit_cast(f16x8, v8);
 }
 
 // ---- the four MFMA regions of the exact-tile pipeline ----
@@ -306,14 +313,13 @@ __device__ __forceinline__ bf16x8 tr_read_pair(const uint8_t* pa, const uint8_t*
 // not covered by the VALU bit
 constexpr int SG_VALU = 0x002, SG_TRANS = 0x400, SG_MFMA = 0x008, SG_VMEM_READ = 0x020, SG_DS_READ = 0x100;
 
-// With the fp32 weight sum (RS false) the exponentials join the VALU groups,
-// four instructions after each MFMA.  With the v_dot2 sum the groups take
-// three plain VALU instructions and the scheduler places the exponentials,
-// which measured faster with the dot2 stalls.
-template <int READS_PER_STEP, bool EXP, bool COPY, bool RS>
+// The groups take three plain VALU instructions after each MFMA and the
+// scheduler places the exponentials, which measured faster with the v_dot2
+// stalls than giving them slots of their own.
+template <int READS_PER_STEP, bool EXP, bool COPY>
 __device__ __forceinline__ void region_schedule() {
-    constexpr int VM = RS ? SG_VALU : (SG_VALU | SG_TRANS);
-    constexpr int VN = RS ? 3 : 4;
+    constexpr int VM = SG_VALU;
+    constexpr int VN = 3;
     __builtin_amdgcn_sched_group_barrier(SG_DS_READ, 2 * READS_PER_STEP, 0);
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
@@ -337,10 +343,9 @@ struct Copy {
 // S^T of one half tile (K rows of half buffer kb_, both row blocks) while
 // the weights of one row block (logits xs) of the other pending half are
 // computed and the copy cp is issued.
-template <bool RS>
 __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff[8], const bf16x8 qb[2][8],
-                                         f32x16 s[2], const f32x16& xs, float m, float c2, bf16x8& p0,
-                                         bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
+                                         f32x16 s[2], const f32x16& xs, float m, float c2, f16x8& p0,
+                                         f16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
     __builtin_amdgcn_sched_barrier(0);
     bf16x8 ka[8];
 #pragma unroll
@@ -351,20 +356,20 @@ __device__ __forceinline__ void region_s(const uint8_t* kb_, const uint32_t koff
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
             s[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[ks], qb[rb][ks], ks ? s[rb] : zero, 0, 0, 0);
-    exp_rb<RS>(xs, m, c2, p0, p1, ls);
+    exp_rb(xs, m, c2, p0, p1, ls);
     dma_half(cp.rs, cp.dst, cp.src, dmaoff);
-    region_schedule<1, true, true, RS>();
+    region_schedule<1, true, true>();
 }
 
 // O^T += V^T P^T over one half tile (V rows in half buffer vb_, P^T operands
 // pb[q2][rb]), with (EXP) the weights of one row block of the next half and
 // (COPY) one half-tile copy.
-template <bool EXP, bool COPY, bool RS>
+template <bool EXP, bool COPY>
 __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const uint32_t oa[4], const uint32_t ob[4],
-                                          const bf16x8 pb[2][2], const f32x16& xs, float m, float c2, bf16x8& p0,
-                                          bf16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
+                                          const f16x8 pb[2][2], const f32x16& xs, float m, float c2, f16x8& p0,
+                                          f16x8& p1, float& ls, const Copy& cp, const uint32_t dmaoff[4]) {
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 va[2][4];
+    f16x8 va[2][4];
 #pragma unroll
     for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
@@ -376,10 +381,10 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
         for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int rb = 0; rb < 2; ++rb)
-                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[q2][db], pb[q2][rb], st.o[db][rb], 0, 0, 0);
-    if (EXP) exp_rb<RS>(xs, m, c2, p0, p1, ls);
+                st.o[db][rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[q2][db], pb[q2][rb], st.o[db][rb], 0, 0, 0);
+    if (EXP) exp_rb(xs, m, c2, p0, p1, ls);
     if (COPY) dma_half(cp.rs, cp.dst, cp.src, dmaoff);
-    if (EXP || COPY) region_schedule<2, EXP, COPY, RS>();
+    if (EXP || COPY) region_schedule<2, EXP, COPY>();
 }
 
 // ---- centroid units: the two row blocks staggered ----
@@ -393,20 +398,20 @@ __device__ __forceinline__ void region_pv(State& st, const uint8_t* vb_, const u
 // The weights computed inside a region must stay there: an empty volatile
 // asm that takes them as inputs at the region's end keeps LLVM from sinking
 // their computation into the code after it, out of reach of the schedule.
-__device__ __forceinline__ void pin_weights(const bf16x8& p0, const bf16x8& p1, float ls) {
+__device__ __forceinline__ void pin_weights(const f16x8& p0, const f16x8& p1, float ls) {
     asm volatile("" ::"v"(__builtin_bit_cast(u32x4, p0)), "v"(__builtin_bit_cast(u32x4, p1)), "v"(ls));
 }
 
 // One row block's overflow check (as settle_half, for row block RB only).
-template <bool RS, int RB>
-__device__ __forceinline__ void settle_row(State& st, const f32x16& s, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+template <int RB>
+__device__ __forceinline__ void settle_row(State& st, const f32x16& s, float c2, f16x8& p0, f16x8& p1, float& ls) {
     if (__builtin_expect(__ballot(ls > OVF) != 0, 0)) {
         float mx = s[0];
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[r]);
         mx = pair_max(mx);
-        if (pair_max(ls) > OVF) rescale_row(st, RB, ceilf(mx));
-        exp_rb<RS>(s, st.m[RB], 1.0f, p0, p1, ls);
+        if (pair_max(ls) > OVF) rescale_row(st, RB, ceilf(mx) - REF_HEAD);
+        exp_rb(s, st.m[RB], 1.0f, p0, p1, ls);
     }
     st.l[RB] += ls;
 }
@@ -416,32 +421,32 @@ __device__ __forceinline__ void settle_row(State& st, const f32x16& s, float c2,
 // of the unit is set from cmh (this lane's compensated-centroid bits shifted
 // down by 4h: accumulator entry r, centroid 8(r/4) + 4h + r%4, is bit
 // 8(r/4) + r%4): log2 64 = 6 where set, -inf elsewhere.
-template <bool RS, bool EXP>
+template <bool EXP>
 __device__ __forceinline__ void region_cs_rb(const uint8_t* khb, const uint8_t* klb, const uint32_t koff[8],
-                                             const bf16x8 qbr[8], f32x16& s, f32x16& xs, float bias[16],
-                                             uint32_t cmh, float m, float c2, bf16x8& p0, bf16x8& p1, float& ls) {
+                                             const f16x8 qbr[8], f32x16& s, f32x16& xs, float bias[16],
+                                             uint32_t cmh, float m, float c2, f16x8& p0, f16x8& p1, float& ls) {
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 khi[8], klo[8];
+    f16x8 khi[8], klo[8];
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        khi[ks] = *reinterpret_cast<const bf16x8*>(khb + koff[ks]);
-        klo[ks] = *reinterpret_cast<const bf16x8*>(klb + koff[ks]);
+        khi[ks] = *reinterpret_cast<const f16x8*>(khb + koff[ks]);
+        klo[ks] = *reinterpret_cast<const f16x8*>(klb + koff[ks]);
     }
     const f32x16 zero = {};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks) {
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(khi[ks], qbr[ks], ks ? s : zero, 0, 0, 0);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(klo[ks], qbr[ks], s, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(khi[ks], qbr[ks], ks ? s : zero, 0, 0, 0);
+        s = __builtin_amdgcn_mfma_f32_32x32x16_f16(klo[ks], qbr[ks], s, 0, 0, 0);
     }
     if (EXP) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) xs[r] = fmaf(xs[r], c2, bias[r]);
-        exp_rb<RS>(xs, m, 1.0f, p0, p1, ls);
+        exp_rb(xs, m, 1.0f, p0, p1, ls);
     } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) bias[r] = ((cmh >> (8 * (r >> 2) + (r & 3))) & 1u) ? 6.0f : -INFINITY;
     }
-    region_schedule<2, true, false, RS>();    // 16 K reads, two per MFMA pair
+    region_schedule<2, true, false>();    // 16 K reads, two per MFMA pair
     if (EXP) {
         pin_weights(p0, p1, ls);
     } else {
@@ -454,13 +459,13 @@ __device__ __forceinline__ void region_cs_rb(const uint8_t* khb, const uint8_t* 
 
 // O^T += V^T P^T of row block RB over the unit's V high and low planes (P^T
 // in pw[q2]); with EXP, the other row block's logits xs get bias and weights.
-template <bool RS, bool EXP, int RB>
+template <bool EXP, int RB>
 __device__ __forceinline__ void region_cpv_rb(State& st, const uint8_t* vhb, const uint8_t* vlb, const uint32_t oa[4],
-                                              const uint32_t ob[4], const bf16x8& pw0, const bf16x8& pw1,
-                                              f32x16& xs, const float bias[16], float m, float c2, bf16x8& p0,
-                                              bf16x8& p1, float& ls) {
+                                              const uint32_t ob[4], const f16x8& pw0, const f16x8& pw1,
+                                              f32x16& xs, const float bias[16], float m, float c2, f16x8& p0,
+                                              f16x8& p1, float& ls) {
     __builtin_amdgcn_sched_barrier(0);
-    bf16x8 va[2][2][4];
+    f16x8 va[2][2][4];
 #pragma unroll
     for (int pl = 0; pl < 2; ++pl)
 #pragma unroll
@@ -476,13 +481,13 @@ __device__ __forceinline__ void region_cpv_rb(State& st, const uint8_t* vhb, con
         for (int q2 = 0; q2 < 2; ++q2)
 #pragma unroll
             for (int db = 0; db < 4; ++db)
-                st.o[db][RB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[pl][q2][db], q2 ? pw1 : pw0, st.o[db][RB], 0, 0, 0);
+                st.o[db][RB] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va[pl][q2][db], q2 ? pw1 : pw0, st.o[db][RB], 0, 0, 0);
     if (EXP) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) xs[r] = fmaf(xs[r], c2, bias[r]);
-        exp_rb<RS>(xs, m, 1.0f, p0, p1, ls);
+        exp_rb(xs, m, 1.0f, p0, p1, ls);
     }
-    region_schedule<4, EXP, false, RS>();     // 32 V^T reads, four per MFMA pair
+    region_schedule<4, EXP, false>();     // 32 V^T reads, four per MFMA pair
     if (EXP) pin_weights(p0, p1, ls);
 }
 
@@ -696,10 +701,6 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
 
 template <int COMP, int SKIM>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
-    // the first-order Taylor forms normalise with the sum of the bf16-rounded
-    // weights (their H terms already spend most of the bf16 error budget);
-    // order 0 and drop with the fp32 sum
-    constexpr bool RS = COMP >= 1;
     // separate LDS objects per half tile, so that each copy is known not to
     // alias the reads of the other three
     __shared__ __attribute__((aligned(16))) uint8_t kbuf0[HALFB];    // K rows 0-31 (row-major, swizzled)
@@ -725,7 +726,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const size_t headq = bh * a.Nq_pad * D;
     const uint16_t* Q = static_cast<const uint16_t*>(a.q) + headq;
     const uint16_t* K = static_cast<const uint16_t*>(a.k) + head;
-    const uint16_t* V = static_cast<const uint16_t*>(a.v) + head;
+    const uint16_t* V = static_cast<const uint16_t*>(a.v16) + head;     // fp16 copy of V
     const float c2 = a.scale * LOG2E;
 
     const size_t rowid = bh * nq + qa;
@@ -806,14 +807,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     // half-tile copies (16 dwordx4 loads) were issued after the one it reads.
     if (cntE > 0) {
         f32x16 s0[2], s1[2];                 // logits of the low / high key half
-        bf16x8 pb0[2][2], pb1[2][2];         // their bf16 weights [q2][rb]
+        f16x8 pb0[2][2], pb1[2][2];          // their fp16 weights [q2][rb]
         float ls0[2], ls1[2];
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s1[rb][r] = -INFINITY;
-            pb1[0][rb] = bf16x8{};
-            pb1[1][rb] = bf16x8{};
+            pb1[0][rb] = f16x8{};
+            pb1[1][rb] = f16x8{};
             ls1[rb] = 0.f;
         }
         int nj = min(BLK, a.N - BLK * j);
@@ -825,31 +826,31 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             // A: S(lo, i) | weights of (hi, i-1), row block 1 | copy V(i, lo)
             wait_vmcnt<16>();
             wave_lds_sync();
-            region_s<RS>(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1],
+            region_s(kbuf0, koff, qb, s0, s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1],
                      Copy{rv, vbuf0, tj}, dmaoff);
-            settle_half<RS>(st, s1, c2, pb1, ls1);
+            settle_half(st, s1, c2, pb1, ls1);
             if (nj < 32) mask_half(s0, 0, nj);
 
             // B: PV(hi, i-1) | weights of (lo, i), row block 0 | copy K(i+1, lo)
             wait_vmcnt<16>();
             if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
             wave_lds_sync();
-            region_pv<true, true, RS>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0],
+            region_pv<true, true>(st, vbuf1, oa, ob, pb1, s0[0], st.m[0], c2, pb0[0][0], pb0[1][0], ls0[0],
                                   Copy{rk, kbuf0, tn}, dmaoff);
 
             // C: S(hi, i) | weights of (lo, i), row block 1 | copy V(i, hi)
             wait_vmcnt<16>();
             wave_lds_sync();
-            region_s<RS>(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1],
+            region_s(kbuf1, koff, qb, s1, s0[1], st.m[1], c2, pb0[0][1], pb0[1][1], ls0[1],
                      Copy{rv, vbuf1, tj + HALFB}, dmaoff);
-            settle_half<RS>(st, s0, c2, pb0, ls0);
+            settle_half(st, s0, c2, pb0, ls0);
             if (nj < BLK) mask_half(s1, 32, nj);
 
             // D: PV(lo, i) | weights of (hi, i), row block 0 | copy K(i+1, hi)
             wait_vmcnt<16>();
             if (nj < 32) zero_rows(vbuf0, nj);
             wave_lds_sync();
-            region_pv<true, true, RS>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0],
+            region_pv<true, true>(st, vbuf0, oa, ob, pb0, s1[0], st.m[0], c2, pb1[0][0], pb1[1][0], ls1[0],
                                   Copy{rk, kbuf1, tn + HALFB}, dmaoff);
 
             nj_prev = nj;
@@ -857,15 +858,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             nj = min(BLK, a.N - BLK * j);
         }
         // drain: weights of (hi, last), row block 1, then PV(hi, last)
-        exp_rb<RS>(s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
-        settle_half<RS>(st, s1, c2, pb1, ls1);
+        exp_rb(s1[1], st.m[1], c2, pb1[0][1], pb1[1][1], ls1[1]);
+        settle_half(st, s1, c2, pb1, ls1);
         wait_vmcnt<0>();
         if (nj_prev < BLK) zero_rows(vbuf1, max(nj_prev, 32) - 32);
         wave_lds_sync();
         {
             float unused_l;
-            bf16x8 unused0, unused1;
-            region_pv<false, false, RS>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l,
+            f16x8 unused0, unused1;
+            region_pv<false, false>(st, vbuf1, oa, ob, pb1, s1[0], 0.f, c2, unused0, unused1, unused_l,
                                     Copy{rv, vbuf1, 0}, dmaoff);
         }
         wave_lds_sync();
@@ -873,12 +874,27 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 
 
     // ---- phase 2 (and 3): centroid pseudo-keys of every compensated block ----
-    // Units of 32 centroids.  The centroid planes (bf16 high and low parts of
+    // Units of 32 centroids.  The centroid planes (fp16 high and low parts of
     // the fp32 means, from the pooling pass) are copied into the four half
     // buffers: K hi -> kbuf0, K lo -> kbuf1, V hi -> vbuf0, V lo -> vbuf1; the
     // next unit's K planes load during this unit's softmax and PV, its V
     // planes during the next S.
     if (COMP >= 0) {
+        // Q^T in fp16 for the centroid and first-order MFMAs (their other
+        // operands, the centroid planes and the moments, are fp16); the bf16
+        // copy stays live only for the global first-order product
+        f16x8 qh[2][8];
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                const u32x4 w = __builtin_bit_cast(u32x4, qb[rb][ks]);
+                u32x4 y;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) y[e] = pack_f16x2(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u));
+                asm volatile("" : "+a"(y));
+                qh[rb][ks] = __builtin_bit_cast(f16x8, y);
+            }
         const int nbc = BLK * ((nb + BLK - 1) / BLK);
         const int nu = (nb + 31) / 32;
         const uint16_t* C = static_cast<const uint16_t*>(a.cent) + bh * 4 * static_cast<size_t>(nbc) * D;
@@ -904,12 +920,12 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             wait_vmcnt<16>();
             wave_lds_sync();
             f32x16 s[2];
-            bf16x8 pb[2][2];
+            f16x8 pb[2][2];
             float ls[2];
             {
                 float unused_l;
-                bf16x8 unused0, unused1;
-                region_cs_rb<RS, false>(kbuf0, kbuf1, koff, qb[0], s[0], s[1], bias, cmh, 0.f, c2, unused0,
+                f16x8 unused0, unused1;
+                region_cs_rb<false>(kbuf0, kbuf1, koff, qh[0], s[0], s[1], bias, cmh, 0.f, c2, unused0,
                                         unused1, unused_l);
             }
             if (u == nu - 1 && nlast < BLK) {
@@ -918,24 +934,24 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                 for (int r = 0; r < 16; ++r)
                     if (8 * (r >> 2) + 4 * h + (r & 3) == ((nb - 1) & 31) && bias[r] != -INFINITY) bias[r] = blast;
             }
-            region_cs_rb<RS, true>(kbuf0, kbuf1, koff, qb[1], s[1], s[0], bias, 0u, st.m[0], c2, pb[0][0],
+            region_cs_rb<true>(kbuf0, kbuf1, koff, qh[1], s[1], s[0], bias, 0u, st.m[0], c2, pb[0][0],
                                    pb[1][0], ls[0]);
             wave_lds_sync();
             if (more) {
                 dma_half(rc, kbuf0, un, dmaoff);
                 dma_half(rc, kbuf1, plane + un, dmaoff);
             }
-            settle_row<RS, 0>(st, s[0], 1.0f, pb[0][0], pb[1][0], ls[0]);
+            settle_row<0>(st, s[0], 1.0f, pb[0][0], pb[1][0], ls[0]);
             // V planes of unit u: only the next unit's K planes may still be in flight
             if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
             wave_lds_sync();
-            region_cpv_rb<RS, true, 0>(st, vbuf0, vbuf1, oa, ob, pb[0][0], pb[1][0], s[1], bias, st.m[1], c2,
+            region_cpv_rb<true, 0>(st, vbuf0, vbuf1, oa, ob, pb[0][0], pb[1][0], s[1], bias, st.m[1], c2,
                                        pb[0][1], pb[1][1], ls[1]);
-            settle_row<RS, 1>(st, s[1], 1.0f, pb[0][1], pb[1][1], ls[1]);
+            settle_row<1>(st, s[1], 1.0f, pb[0][1], pb[1][1], ls[1]);
             {
                 float unused_l;
-                bf16x8 unused0, unused1;
-                region_cpv_rb<RS, false, 1>(st, vbuf0, vbuf1, oa, ob, pb[0][1], pb[1][1], s[0], bias, 0.f, c2,
+                f16x8 unused0, unused1;
+                region_cpv_rb<false, 1>(st, vbuf0, vbuf1, oa, ob, pb[0][1], pb[1][1], s[0], bias, 0.f, c2,
                                             unused0, unused1, unused_l);
             }
             wave_lds_sync();
@@ -958,16 +974,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             if (COMP == 1) {
                 // O^T[., row] += w_j[row] T, T = H_j^T Q^T (fp32, 16 MFMAs per
                 // 32-wide d block), for every compensated block j of this unit,
-                // with w_j = scale 2^{L - m} / n_j (L without the count bias).
+                // with w_j = scale 2^{L - m + e_j} / n_j (L without the count bias,
+                // e_j the exponent of the block's fp16 moment copy).
                 // Two batches of 16 centroids (their weights staged in LDS); the A
                 // operands (H_j^T in MFMA operand order) load two d blocks ahead.
                 const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom) + bh * nb * static_cast<size_t>(D) * D;
                 // H_j^T in MFMA operand order: (d block, i step) operands are 1 KiB runs
-                auto load_step = [&](int jj, int db, bf16x8 op[8]) __attribute__((always_inline)) {
+                auto load_step = [&](int jj, int db, f16x8 op[8]) __attribute__((always_inline)) {
                     const uint16_t* Hop = MOM + static_cast<size_t>(jj) * D * D + (db * 8 * 64 + l) * 8;
 #pragma unroll
-                    for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const bf16x8*>(Hop + ks * 64 * 8);
+                    for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const f16x8*>(Hop + ks * 64 * 8);
                 };
+                const int8_t* KEX = a.kmom_exp + bh * nb;   // block j's moments are stored as H_j 2^-KEX[j]
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     // accumulator entries r = 8 hb .. 8 hb + 7 hold centroids 16 hb .. 16 hb + 15
@@ -977,7 +995,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                         for (int r = 8 * hb; r < 8 * hb + 8; ++r) {
                             const int cc = 8 * (r >> 2) + 4 * h + (r & 3) - 16 * hb;
                             const float x = (bias[r] == -INFINITY) ? 0.f
-                                : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb]) * a.scale;
+                                : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb] +
+                                                         static_cast<float>(KEX[32 * u + 16 * hb + cc])) * a.scale;
                             wbuf[cc * BLK + 32 * rb + l32] = x;
                         }
                     wave_lds_sync();
@@ -993,7 +1012,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                         // operand sets
                         int c = __builtin_ctz(pend);
                         pend &= pend - 1;
-                        bf16x8 buf[2][8];
+                        f16x8 buf[2][8];
                         load_step(32 * u + 16 * hb + c, 0, buf[0]);
                         load_step(32 * u + 16 * hb + c, 1, buf[1]);
                         for (;;) {
@@ -1006,7 +1025,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                                 for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
                                     for (int rb = 0; rb < 2; ++rb)
-                                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(buf[db & 1][ks], qb[rb][ks], t[rb], 0, 0, 0);
+                                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(buf[db & 1][ks], qh[rb][ks], t[rb], 0, 0, 0);
                                 if (db < 2) load_step(32 * u + 16 * hb + c, db + 2, buf[db & 1]);
                                 else if (nc >= 0) load_step(32 * u + 16 * hb + nc, db - 2, buf[db & 1]);
 #pragma unroll

@@ -17,8 +17,10 @@ struct PoolArgs {
     float* kbar;
     float* vbar;
     int32_t* kcount;
-    void* cent;       // bf16 [B,H,4,nbc,d] centroid planes, or null
-    void* kmom;       // bf16 [B,H,nb,d*d] in MFMA operand order, or null
+    void* cent;       // fp16 [B,H,4,nbc,d] centroid planes, or null
+    uint16_t* v16;    // fp16 [B,H,N_pad,d] copy of V, or null
+    void* kmom;       // fp16 [B,H,nb,d*d] in MFMA operand order (scaled by 2^-kmom_exp), or null
+    int8_t* kmom_exp; // [B,H,nb] exponent of each kmom block (with kmom)
     float* hbar;      // fp32 [B,H,d,d] value-major mean moment, or null
     float* hbar_ws;   // fp32 [B,H,64,d,d] partial sums (with hbar)
     float* kcov;      // fp32 [B,H,nb] ln ||H_j - H_bar||_2 (with hbar), or null
@@ -70,9 +72,11 @@ struct FwdArgs {
     const void* v;
     const float* kbar;
     const float* vbar;
-    const void* cent;         // bf16 centroid planes (bf16 path)
+    const void* cent;         // fp16 centroid planes (bf16 path)
+    const void* v16;          // fp16 copy of V (bf16 path)
     const int32_t* kcount;
-    const void* kmom;
+    const void* kmom;         // fp16 moments, block j scaled by 2^-kmom_exp[j] (comp 1)
+    const int8_t* kmom_exp;
     const float* hbar;        // fp32 [B,H,d,d] value-major (comp 2)
     const uint8_t* q8;
     const uint8_t* k8;
@@ -125,6 +129,7 @@ struct ResidualArgs {
     float* wc;                // [B,H,d*d + d] W, c
     uint16_t* qp;             // [B,H,Mp,d] gathered probe queries
     float* zv;                // [B,H,2,d,8] the factors Z and V_r of W = Z V_r^T
+    uint16_t* v16;            // [B,H,N_pad,d] fp16 copy of V (dense probe pass)
 };
 size_t residual_workspace_bytes(int B, int H, int N_pad);
 void residual_carve(ResidualArgs& r, void* ws);

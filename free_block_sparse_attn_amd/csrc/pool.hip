@@ -44,10 +44,29 @@ __device__ __forceinline__ uint16_t* cent_row(void* cent, size_t bh, int plane, 
     return static_cast<uint16_t*>(cent) + ((bh * 4 + plane) * nbc + static_cast<size_t>(j)) * D;
 }
 
-// bf16 high part and residual of an fp32 mean (m - hi is exact in fp32).
+// fp16 high part and rounded residual of an fp32 mean (m - hi is exact in
+// fp32), so hi + lo carries m to about 22 bits.
 __device__ __forceinline__ void split_hi_lo(float m, uint16_t& hi, uint16_t& lo) {
-    hi = f32_to_bf16(m);
-    lo = f32_to_bf16(m - bf16_to_f32(hi));
+    hi = f32_to_f16(m);
+    lo = f32_to_f16(m - f16_to_f32(hi));
+}
+
+// fp16 copy of one 16-byte chunk of bf16 values (8 elements), RNE.
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(const u32x4& r) {
+    u32x4 w;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) w[e] = pack_f16x2(__uint_as_float(r[e] << 16), __uint_as_float(r[e] & 0xFFFF0000u));
+    return w;
+}
+
+// Exponent e of the fp16 moment copy H_j 2^-e: amax 2^-e in [2^14, 2^15)
+// (0 for an all-zero block), so the largest entry keeps 11 bits and the
+// copy never overflows.
+__device__ __forceinline__ int f16_block_exponent(float amax) {
+    if (!(amax > 0.0f)) return 0;
+    int k;
+    frexpf(amax, &k);                  // amax in [2^(k-1), 2^k)
+    return min(max(k - 15, -100), 100);
 }
 constexpr int TPITCH = BLK + 8;     // transposed row pitch in elements (16-byte multiple)
 
@@ -127,6 +146,18 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
             reg[t][c] = z;
         }
     }
+    // fp16 copy of V (bf16, d = 128); pad rows were loaded as zero
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (a.v16) {
+#pragma unroll
+            for (int c = 0; c < PT; ++c) {
+                const int chunk = tid + THREADS * c;
+                const int row = chunk / CPR;
+                const int col0 = (chunk % CPR) * PER16;
+                *reinterpret_cast<u32x4*>(a.v16 + tok0 + static_cast<size_t>(row) * D + col0) = bf16x8_to_f16x8(reg[2][c]);
+            }
+        }
+    }
     // transposed staging
 #pragma unroll
     for (int t = 0; t < 3; ++t) {
@@ -199,7 +230,8 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
     if constexpr (sizeof(T) == 2 && D == 128) {
         // Phase 4 (optional): value-major moment kmom[o][i] = sum_n v_n[o] (k_n[i] - kbar[i])
         // via bf16 MFMA 32x32x16; centred keys are split hi + lo so the
-        // product keeps ~16 mantissa bits.
+        // product keeps ~16 mantissa bits; stored in fp16 with a per-block
+        // power-of-two exponent.
         if (a.kmom) {
             const int w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
             const int icol = 32 * w + l32;                 // this wave's i block
@@ -226,6 +258,19 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                     acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
                 }
             }
+            // fp16 copy H_j 2^-e with the block's exponent e (largest entry
+            // in [2^14, 2^15)), written to kmom_exp
+            float am = 0.0f;
+#pragma unroll
+            for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[ob][r]));
+            for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+            if (l == 0) red[48 + w] = am;         // slots no other phase uses
+            __syncthreads();
+            am = fmaxf(fmaxf(red[48], red[49]), fmaxf(red[50], red[51]));
+            const int ex = f16_block_exponent(am);
+            if (tid == 0) a.kmom_exp[bh * nb + j] = static_cast<int8_t>(ex);
             // MFMA A-operand order of the forward pass: element (o, i) of H_j^T
             // at ((o/32 * 8 + i/16) * 64 + o%32 + 32 (i/8 % 2)) * 8 + i%8, so each
             // (32-row d block, 16-wide i step) operand is 1 KiB contiguous
@@ -236,7 +281,7 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int o32 = 8 * (r >> 2) + 4 * hl + (r & 3);
-                    mom[((ob * 8 + ks) * 64 + o32 + 32 * hi8) * 8 + e8] = f32_to_bf16(acc[ob][r]);
+                    mom[((ob * 8 + ks) * 64 + o32 + 32 * hi8) * 8 + e8] = f32_to_f16(ldexpf(acc[ob][r], -ex));
                 }
             }
         }
@@ -401,6 +446,11 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
     double acc[PER16];
 #pragma unroll
     for (int e = 0; e < PER16; ++e) acc[e] = 0.0;
+    // fp16 copy of V (bf16, d = 128): each lane rewrites its chunk of every row
+    uint16_t* v16 = nullptr;
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (a.v16 && tensor == 2) v16 = a.v16 + (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D + col0;
+    }
     for (int r0 = 0; r0 < n; r0 += UNROLL) {
         u32x4 x[UNROLL];
 #pragma unroll
@@ -415,6 +465,22 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
 #pragma unroll
                 for (int e = 0; e < PER16; ++e) acc[e] = acc[e] + static_cast<double>(E::get(x[u], e));
             }
+        }
+        if constexpr (sizeof(T) == 2 && D == 128) {
+            if (v16) {
+#pragma unroll
+                for (int u = 0; u < UNROLL; ++u)
+                    if (r0 + u < BLK)
+                        *reinterpret_cast<u32x4*>(v16 + static_cast<size_t>(r0 + u) * D) = bf16x8_to_f16x8(x[u]);
+            }
+        }
+    }
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        // pad rows of the copy (rows the loop above did not reach) are zero
+        if (v16) {
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            for (int r = ((n + UNROLL - 1) / UNROLL) * UNROLL; r < BLK; ++r)
+                *reinterpret_cast<u32x4*>(v16 + static_cast<size_t>(r) * D) = z;
         }
     }
     float* dst = (tensor == 0 ? a.qbar : tensor == 1 ? a.kbar : a.vbar) + (bh * nb + j) * D + col0;

@@ -70,6 +70,19 @@ __global__ __launch_bounds__(THREADS) void probe_gather_kernel(ResidualArgs r) {
     }
 }
 
+// fp16 copy of V for the dense probe pass (the forward kernel's value side
+// runs in fp16): one 16-byte chunk (8 values) per thread, RNE.
+__global__ __launch_bounds__(THREADS) void value_f16_kernel(ResidualArgs r) {
+    const size_t x = static_cast<size_t>(blockIdx.x) * THREADS + threadIdx.x;
+    const size_t total = static_cast<size_t>(r.B) * r.H * r.N_pad * (D / 8);
+    if (x >= total) return;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(r.v) + x * 8);
+    u32x4 y;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) y[e] = pack_f16x2(__uint_as_float(w[e] << 16), __uint_as_float(w[e] & 0xFFFF0000u));
+    *reinterpret_cast<u32x4*>(r.v16 + x * 8) = y;
+}
+
 // ---- 2b. merge the key chunks: O = sum_c e^{lse_c - lse_max} O_c / sum_c e^{lse_c - lse_max} ----
 __global__ __launch_bounds__(THREADS) void combine_kernel(ResidualArgs r) {
     const size_t bh = blockIdx.y;
@@ -880,7 +893,7 @@ size_t residual_workspace_bytes(int B, int H, int N_pad) {
     const size_t kc = residual_key_chunks(N_pad);
     const size_t f64 = bh * (NSPLIT * (3 * D * D + 2 * D) + 3 * D * D);
     const size_t f32 = bh * (2 * mp * D + D * D + D) + kc * bh * mp * (D + 1) + bh * 2 * D * KSUB;
-    const size_t b16 = bh * mp * D;
+    const size_t b16 = bh * mp * D + bh * static_cast<size_t>(N_pad) * D;
     return f64 * 8 + f32 * 4 + b16 * 2;
 }
 
@@ -897,7 +910,8 @@ void residual_carve(ResidualArgs& r, void* ws) {
     r.odp = reinterpret_cast<float*>(p);   p += r.kchunks * bh * mp * D * 4;
     r.lsep = reinterpret_cast<float*>(p);  p += r.kchunks * bh * mp * 4;
     r.qp = reinterpret_cast<uint16_t*>(p);  p += bh * mp * D * 2;
-    r.zv = reinterpret_cast<float*>(p);
+    r.zv = reinterpret_cast<float*>(p);    p += bh * 2 * D * KSUB * 4;
+    r.v16 = reinterpret_cast<uint16_t*>(p);
 }
 
 hipError_t launch_residual(const ResidualArgs& r, hipStream_t s) {
@@ -905,11 +919,15 @@ hipError_t launch_residual(const ResidualArgs& r, hipStream_t s) {
     hipError_t e;
     hipLaunchKernelGGL(probe_gather_kernel, dim3((r.Mp * (D / 8) + THREADS - 1) / THREADS, bh), dim3(THREADS), 0, s, r);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t chunks = static_cast<size_t>(bh) * r.N_pad * (D / 8);
+    hipLaunchKernelGGL(value_f16_kernel, dim3(static_cast<unsigned>((chunks + THREADS - 1) / THREADS)), dim3(THREADS),
+                       0, s, r);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
     // dense attention of the gathered probe queries (every key block exact, fp32 out)
     FwdArgs f{};
     f.B = r.B; f.H = r.H; f.N = r.N; f.N_pad = r.N_pad; f.d = D;
     f.comp = -1; f.scale = r.scale;
-    f.q = r.qp; f.k = r.k; f.v = r.v;
+    f.q = r.qp; f.k = r.k; f.v = r.v; f.v16 = r.v16;
     f.out = r.odp; f.lse = r.lsep;
     f.Nq = r.N_pad / BLK; f.Nq_pad = r.Mp;
     f.dense = r.kchunks; f.out_f32 = 1;

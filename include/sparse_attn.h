@@ -53,7 +53,7 @@
 extern "C" {
 #endif
 
-#define SPARSE_ATTN_ABI_VERSION 8
+#define SPARSE_ATTN_ABI_VERSION 9
 #define SPARSE_ATTN_BLOCK 64
 
 typedef enum {
@@ -107,17 +107,25 @@ typedef struct {
  *                        routing features; they are bit-reproducible.
  *   kcount               int32 [nb]       n_j (same for every b, h).
  * Outputs (optional, NULL to skip)
- *   cent                 bf16 [B,H,4,nbc,d], nbc = 64 * ceil(nb / 64): the
+ *   cent                 fp16 [B,H,4,nbc,d], nbc = 64 * ceil(nb / 64): the
  *                        centroids in the form the bf16 forward pass reads.
- *                        With m the fp32 mean above, hi = bf16_rne(m) and
- *                        lo = bf16_rne(m - hi) (the difference is exact in
- *                        fp32), so hi + lo carries m to about 16 bits:
+ *                        With m the fp32 mean above, hi = fp16_rne(m) and
+ *                        lo = fp16_rne(m - hi) (the difference is exact in
+ *                        fp32), so hi + lo carries m to about 22 bits:
  *                        plane 0 hi(k_bar), 1 lo(k_bar), 2 hi(v_bar),
  *                        3 lo(v_bar); rows nb .. nbc-1 are 0.  bf16 inputs
  *                        with d == 128 only.
- *   kmom                 bf16 [B,H,nb,d*d]  moment of block j,
- *                        G[o][i] = sum_n (k_n[i] - k_bar_j[i]) v_n[o]
- *                        (H_j transposed), stored in the forward pass's MFMA
+ *   v16                  fp16 [B,H,N_pad,d]  fp16_rne(v), the value operand of
+ *                        the bf16 forward pass (exact for bf16 values of
+ *                        magnitude 2^-14 .. 65504; below, rounded to fp16's
+ *                        subnormal step 2^-24; beyond 65504, inf).  Pad rows
+ *                        are 0.  bf16 inputs with d == 128 only.
+ *   kmom, kmom_exp       fp16 [B,H,nb,d*d] and int8 [B,H,nb], together: the
+ *                        moment of block j, G[o][i] = sum_n (k_n[i] -
+ *                        k_bar_j[i]) v_n[o] (H_j transposed), stored as
+ *                        fp16_rne(G 2^-e_j) with e_j = kmom_exp[j] chosen so
+ *                        that the largest |entry| lands in [2^14, 2^15) (0 for
+ *                        an all-zero block), in the forward pass's MFMA
  *                        operand order: G[o][i] at element
  *                        ((o/32 * 8 + i/16) * 64 + o%32 + 32 * ((i/8) % 2)) * 8
  *                        + i%8 of the block.  bf16 inputs with d == 128 only.
@@ -135,11 +143,16 @@ typedef struct {
  *                        the mean moment): the statistic of PISA's
  *                        covariance-aware top-k (section 2, "Routage Sensible
  *                        a la Covariance").  H_j is rebuilt in fp32 (never
- *                        stored); M_j comes from power iteration on
- *                        (H_j - H_bar)^T (H_j - H_bar), stopped when the
- *                        estimate moves by < 2^-22 relative (4..64 steps); it
- *                        approaches M_j from below.  -inf when M_j = 0.  Needs
- *                        hbar (and hbar_ws).
+ *                        stored); M_j^2 is the largest eigenvalue of
+ *                        A = (H_j - H_bar)^T (H_j - H_bar), taken from 32
+ *                        Lanczos steps on A (fixed start vector, partial sums
+ *                        combined in a fixed order, so deterministic) and
+ *                        64-point multisection of the Lanczos tridiagonal
+ *                        with Sturm counts; the Ritz value approaches M_j^2
+ *                        from below and lands within fp32 rounding of it even
+ *                        where the two top singular values are within a few
+ *                        percent.  -inf when M_j = 0.  Needs hbar (and
+ *                        hbar_ws).
  *   klam                 fp32 [B,H,nb]  lambda_j = ln(r_k r_v),
  *                        r_x^2 = sum_n ||x_n - x_bar_j||^2 (Triage router's
  *                        omission-error statistic); -inf for 1-token blocks.
@@ -176,7 +189,8 @@ typedef struct {
 sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            const void* q, const void* k, const void* v,
                            float* qbar, float* kbar, float* vbar, int32_t* kcount,
-                           void* cent, void* kmom, float* hbar, float* hbar_ws, float* kcov, float* klam,
+                           void* cent, void* v16, void* kmom, int8_t* kmom_exp,
+                           float* hbar, float* hbar_ws, float* kcov, float* klam,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
                            uint8_t* q4, uint8_t* k4, uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4,
                            hipStream_t stream);
@@ -282,19 +296,28 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
  *   global  scale (sum_{j in U} e^{scale q.k_bar_j}) q^T H_bar (N only) comp == 2
  *           (PISA section 2, "Algorithme Central": the hybrid-order form,
  *           one d x d statistic for every skipped block)
- * Precision (SA_BF16): the exact and centroid weights enter the MFMA rounded
- * to bf16; D sums them in fp32 unrounded for comp <= 0 (lse exact to fp32
- * rounding, o within 2^-8 relative scaling of the convex combination) and
- * rounded for comp >= 1 (their rounding cancels in o; lse within 2^-8
- * relative of the unrounded sum).
+ * Precision (SA_BF16): logits of the exact tiles come from bf16 MFMA on
+ * q and k (exact products, fp32 sums).  The exact and centroid weights enter
+ * the value products rounded to fp16 (11 significant bits) against the fp16
+ * copy of v, and D sums those same rounded weights in fp32, so their
+ * rounding cancels in o (every comp); lse = ln D is within 2^-11 relative of
+ * the sum of the unrounded weights.  The centroid logits and the first-order
+ * products run in fp16 MFMA (q converted once; centroid means as fp16 high +
+ * low parts; moments with their block exponents).  Skim weights enter D
+ * unquantised (see skim).  Domain: q, k and v within fp16's range
+ * (|x| <= 65504); beyond it the fp16 operands overflow and the rows that use
+ * them are undefined.
  *
  * scale      softmax scale, finite and > 0
  * q, k, v    dtype [B,H,N_pad,d]
  * kbar, vbar fp32 [B,H,nb,d] centroids (SA_F32 with comp >= 0; unused by
  *            SA_BF16, may be NULL there)
- * cent       bf16 [B,H,4,nbc,d] centroid planes from sparse_attn_pool
+ * cent       fp16 [B,H,4,nbc,d] centroid planes from sparse_attn_pool
  *            (SA_BF16 with comp >= 0; unused by SA_F32)
- * kcount     int32 [nb]                 kmom bf16 [B,H,nb,d*d] (comp == 1)
+ * v16        fp16 [B,H,N_pad,d] copy of v from sparse_attn_pool (SA_BF16:
+ *            the value operand of the exact tiles)
+ * kcount     int32 [nb]
+ * kmom, kmom_exp  fp16 moments and their block exponents (comp == 1)
  * hbar       fp32 [B,H,d,d] from sparse_attn_pool (comp == 2, SA_BF16)
  * q8, k8, v8, exp8                      from sparse_attn_pool (skim, SA_SKIM_E4M3)
  * skim_fmt   sa_skim_format of the skim tier
@@ -313,7 +336,8 @@ int32_t sparse_attn_lvsa_capacity(const int32_t* frame_lo_host, const int32_t* f
 sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, float scale,
                           const void* q, const void* k, const void* v,
                           const float* kbar, const float* vbar, const void* cent,
-                          const int32_t* kcount, const void* kmom, const float* hbar,
+                          const void* v16, const int32_t* kcount, const void* kmom, const int8_t* kmom_exp,
+                          const float* hbar,
                           const uint8_t* q8, const uint8_t* k8, const uint8_t* v8,
                           const int8_t* exp8, sa_skim_format skim_fmt,
                           const uint8_t* q4, const uint8_t* k4, const uint8_t* v4,
@@ -360,6 +384,8 @@ sa_status sparse_attn_fwd(const sa_shape* shape, sa_dtype dtype, sa_comp comp, f
  *              fp32 [B,H,2,d,8]          Z = (Xc^T Xc + lambda I)^{-1} Xc^T Rc V_r
  *                                        and V_r (columns >= rank zero), the
  *                                        factors W = Z V_r^T is applied by
+ *              fp16 [B,H,N_pad,d]        fp16 copy of v (the dense probes'
+ *                                        value operand)
  */
 size_t sparse_attn_residual_workspace(const sa_shape* shape);
 sa_status sparse_attn_residual(const sa_shape* shape, sa_dtype dtype, float scale,

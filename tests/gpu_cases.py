@@ -7,15 +7,15 @@ import torch
 from oracle import attention, pooling, routing
 from workloads import make_qkv, block_frame_ranges, lvsa_anchor_phase
 
-BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs, per row scaled by max(1, |o|_inf) (row_tol)
+BF16_TOL = 1e-2      # max |out - oracle| for bf16 outputs (row_tol: plus the store's half-ulp above 4)
 F32_TOL = 1e-4       # max |out - oracle| for fp32 outputs
-# lse: the bf16 path's first-order Taylor forms normalise with the sum of the
-# bf16-rounded weights the matrix core multiplies, each within 2^-8 (bf16 unit
-# roundoff) relative of the exact weight, so |d lse| <= -ln(1 - 2^-8) = 3.92e-3;
-# plus fp32 logit error (centroid means carried as bf16 high + low parts, MFMA
-# accumulation): 4.5e-3.  The other forms sum the fp32 weights and land far
-# inside this bar (~1e-5).
-LSE_TOL = {"bf16": 4.5e-3, "f32": 1e-5}
+# lse: the bf16 path normalises with the sum of the fp16-rounded weights the
+# matrix core multiplies, each within 2^-11 (fp16 unit roundoff) relative of
+# the exact weight, so |d lse| <= -ln(1 - 2^-11) = 4.9e-4; plus fp32 logit
+# error (exact tiles: fp32 MFMA sums of exact products; centroids: means as
+# fp16 high + low parts) and, on skim rows, the block-scaled MFMA's logit
+# error (<= 1.4e-4): 1e-3.
+LSE_TOL = {"bf16": 1e-3, "f32": 1e-5}
 # The fp8 / MXFP4 skim tier's logits come out of the block-scaled MFMA, whose
 # sums differ from the exact dot products of the low-precision copies by up
 # to ~2e-4 in log2 units on these workloads (row lse off by <= 1.4e-4 where a
@@ -27,13 +27,15 @@ SKIM_EPS = 5e-4
 
 
 def row_tol(dtype, o):
-    """Per-row output bar: fp32 absolute; bf16 max-abs 1e-2 for rows with
-    |o|_inf <= 1 and 1e-2 |o|_inf above (a bf16 value of magnitude in [2, 4)
-    is itself only resolved to 2^-6, so an absolute 1e-2 cannot be met there by
-    any bf16 result; bf16 error is relative)."""
+    """Per-row output bar.  fp32: 1e-4.  bf16: max-abs 1e-2 for rows with
+    |o|_inf < 4; above, 1e-2 plus the half-ulp of the bf16 store at the row's
+    largest magnitude (2^(e - 8) for |o|_inf in [2^e, 2^(e+1))), because from
+    4 up that rounding alone (>= 2^-6 = 0.0156) can exceed 1e-2."""
     if dtype != "bf16":
         return np.full(o.shape[0], F32_TOL)
-    return BF16_TOL * np.maximum(1.0, np.abs(o).max(axis=1))
+    amax = np.abs(o).max(axis=1)
+    e = np.floor(np.log2(np.maximum(amax, 4.0)))
+    return np.where(amax < 4.0, BF16_TOL, BF16_TOL + np.exp2(e - 8.0))
 
 
 def to_device(wl, q, k, v):
@@ -45,9 +47,6 @@ def inputs(wl, heads=None):
     """numpy fp32 (exact input values) and device tensors of a workload."""
     q, k, v, coords = make_qkv(wl, heads=heads)
     return (q, k, v), to_device(wl, q, k, v), coords
-
-
-SKIM_BUILT = True       # the fp8 skim tier of the forward pass
 
 
 def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
@@ -80,10 +79,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     else:
         idx, cnt, idx2, cnt2 = fbsa.sparse_attn_route(
             pooled, N, fbsa.SA_ROUTE_TRIAGE, n_keep=wl.n_keep, n_refine=wl.n_refine, scale=scale)
-    run_fwd = wl.rule != "triage" or SKIM_BUILT
-    if run_fwd:
-        out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2,
-                                        skim_fmt=fbsa.SA_SKIM_MXFP4 if wl.skim_fmt == "mxfp4" else fbsa.SA_SKIM_E4M3)
+    out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2,
+                                    skim_fmt=fbsa.SA_SKIM_MXFP4 if wl.skim_fmt == "mxfp4" else fbsa.SA_SKIM_E4M3)
     torch.cuda.synchronize()
     res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
     if "v8" in res:
@@ -99,9 +96,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
     if idx2 is not None:
         res["idx2"], res["cnt2"] = idx2.cpu().numpy(), cnt2.cpu().numpy()
-    if run_fwd:
-        res["out"] = out.float().cpu().numpy()
-        res["lse"] = lse.cpu().numpy()
+    res["out"] = out.float().cpu().numpy()
+    res["lse"] = lse.cpu().numpy()
     return res
 
 

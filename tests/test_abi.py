@@ -46,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
         assert name in _lib.EXPORTED, name
-    assert lib.sparse_attn_abi_version() == 8
+    assert lib.sparse_attn_abi_version() == 9
 
 
 def shape(B=1, H=2, N=100, N_pad=128, d=128):
@@ -59,14 +59,14 @@ MIS = ctypes.c_void_p(4097)
 
 
 def pool(lib, sh, dtype=1, **kw):
-    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, kmom=None, hbar=None, hbar_ws=None,
-             kcov=None, klam=None, q8=None, k8=None, v8=None, exp8=None, q4=None, k4=None, v4=None, qs4=None,
-             ks4=None, vs4=None)
+    a = dict(q=P, k=P, v=P, qbar=P, kbar=P, vbar=P, kcount=P, cent=None, v16=None, kmom=None, kmom_exp=None,
+             hbar=None, hbar_ws=None, kcov=None, klam=None, q8=None, k8=None, v8=None, exp8=None, q4=None, k4=None,
+             v4=None, qs4=None, ks4=None, vs4=None)
     a.update(kw)
     return lib.sparse_attn_pool(sh, dtype, a["q"], a["k"], a["v"], a["qbar"], a["kbar"], a["vbar"],
-                                a["kcount"], a["cent"], a["kmom"], a["hbar"], a["hbar_ws"], a["kcov"], a["klam"], a["q8"],
-                                a["k8"], a["v8"], a["exp8"], a["q4"], a["k4"], a["v4"], a["qs4"], a["ks4"],
-                                a["vs4"], None)
+                                a["kcount"], a["cent"], a["v16"], a["kmom"], a["kmom_exp"], a["hbar"], a["hbar_ws"],
+                                a["kcov"], a["klam"], a["q8"], a["k8"], a["v8"], a["exp8"], a["q4"], a["k4"], a["v4"],
+                                a["qs4"], a["ks4"], a["vs4"], None)
 
 
 def test_pool_rejects_bad_arguments(lib):
@@ -79,8 +79,14 @@ def test_pool_rejects_bad_arguments(lib):
     assert pool(lib, shape(), kbar=MIS) == 1
     assert b"kbar" in lib.sparse_attn_last_error()
     assert pool(lib, shape(), q8=P) == 1                     # fp8 copies: all four or none
-    assert pool(lib, shape(), dtype=0, kmom=P) == 2          # moments need bf16, d=128
-    assert pool(lib, shape(d=64), kmom=P) == 2
+    assert pool(lib, shape(), dtype=0, kmom=P, kmom_exp=P) == 2   # moments need bf16, d=128
+    assert pool(lib, shape(d=64), kmom=P, kmom_exp=P) == 2
+    assert pool(lib, shape(), kmom=P) == 1                   # moments come with their exponents
+    assert b"kmom_exp" in lib.sparse_attn_last_error()
+    assert pool(lib, shape(), kmom_exp=P) == 1
+    assert pool(lib, shape(), dtype=0, v16=P) == 2           # the fp16 copy of V needs bf16, d=128
+    assert pool(lib, shape(d=64), v16=P) == 2
+    assert pool(lib, shape(), v16=MIS) == 1
     assert pool(lib, shape(), dtype=0, cent=P) == 2          # centroid planes need bf16, d=128
     assert pool(lib, shape(d=64), cent=P) == 2
     assert pool(lib, shape(), cent=MIS) == 1
@@ -139,12 +145,13 @@ def test_route_rejects_bad_arguments(lib):
 
 
 def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
-    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, kcount=P, kmom=None, hbar=None, q8=None, k8=None, v8=None,
-             exp8=None, skim_fmt=0, q4=None, k4=None, v4=None, qs4=None, ks4=None, vs4=None,
+    a = dict(q=P, k=P, v=P, kbar=P, vbar=P, cent=P, v16=P, kcount=P, kmom=None, kmom_exp=None, hbar=None, q8=None,
+             k8=None, v8=None, exp8=None, skim_fmt=0, q4=None, k4=None, v4=None, qs4=None, ks4=None, vs4=None,
              idx=P, cnt=P, cap=2, idx2=None, cnt2=None, cap2=0, out=P, lse=None)
     a.update(kw)
     return lib.sparse_attn_fwd(sh, dtype, comp, scale, a["q"], a["k"], a["v"], a["kbar"], a["vbar"],
-                               a["cent"], a["kcount"], a["kmom"], a["hbar"], a["q8"], a["k8"], a["v8"], a["exp8"],
+                               a["cent"], a["v16"], a["kcount"], a["kmom"], a["kmom_exp"], a["hbar"], a["q8"],
+                               a["k8"], a["v8"], a["exp8"],
                                a["skim_fmt"], a["q4"], a["k4"], a["v4"], a["qs4"], a["ks4"], a["vs4"],
                                a["idx"],
                                a["cnt"], a["cap"], a["idx2"], a["cnt2"], a["cap2"], a["out"], a["lse"], None)
@@ -152,6 +159,10 @@ def fwd(lib, sh, dtype=1, comp=0, scale=1.0, **kw):
 
 def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, shape(), comp=1) == 1                     # order 1 without kmom
+    assert fwd(lib, shape(), comp=1, kmom=P) == 1             # ... or without its exponents
+    assert b"kmom_exp" in lib.sparse_attn_last_error()
+    assert fwd(lib, shape(), v16=None) == 1                   # the bf16 path reads the fp16 copy of V
+    assert b"v16" in lib.sparse_attn_last_error()
     assert fwd(lib, shape(), comp=2) == 1                     # global order 1 without hbar
     assert fwd(lib, shape(), comp=3) == 1
     assert fwd(lib, shape(d=64), dtype=0, comp=2, hbar=P) == 2   # fp32 path has no first-order term
@@ -165,7 +176,7 @@ def test_fwd_rejects_bad_arguments(lib):
     assert fwd(lib, shape(), comp=-1, cap=0, idx=None, cnt=None) == 1   # nothing to attend to
     assert fwd(lib, shape(d=64)) == 2                         # bf16 needs d = 128
     assert fwd(lib, shape(), dtype=0) == 2                    # fp32 needs d = 64
-    assert fwd(lib, shape(d=64), dtype=0, comp=1, kmom=P) == 2
+    assert fwd(lib, shape(d=64), dtype=0, comp=1, kmom=P, kmom_exp=P) == 2
     assert fwd(lib, shape(), skim_fmt=2) == 1                 # unknown skim format
     sk = dict(idx2=P, cnt2=P, cap2=2)
     assert fwd(lib, shape(), **sk) == 1                       # e4m3 skim without its copies
@@ -227,5 +238,5 @@ def test_residual_workspace_matches_the_documented_layout(lib, B, H, N_pad):
            + bh * (d * d + d)                                      # W, c
            + kc * bh * mp * d + kc * bh * mp                       # per-chunk dense output and lse
            + bh * 2 * d * 8)                                       # Z and V_r
-    b16 = bh * mp * d                                              # gathered probe queries
+    b16 = bh * mp * d + bh * N_pad * d                             # gathered probe queries; fp16 copy of V
     assert lib.sparse_attn_residual_workspace(shape(B=B, H=H, N=N_pad, N_pad=N_pad)) == 8 * f64 + 4 * f32 + 2 * b16

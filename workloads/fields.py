@@ -38,22 +38,37 @@ def make_head(workload_id: int, b: int, h: int, tensor: int, coords: np.ndarray,
     return out
 
 
-def make_qkv(wl, heads=None, batches=None):
+def _make_one(job):
+    return make_head(*job)
+
+
+def make_qkv(wl, heads=None, batches=None, workers: int = 1):
     """Q, K, V as float32 [B', H', N_pad, d] for the chosen batches and heads.
 
     `wl` is a Workload.  The values are exactly representable in the
-    workload's dtype.  Returns (q, k, v, coords).
+    workload's dtype.  `workers` > 1 generates the (tensor, batch, head) slabs
+    in that many processes (each slab has its own seed, so the values do not
+    depend on it).  Returns (q, k, v, coords).
     """
     coords = tile_major_coords(wl.T, wl.Y, wl.X)
     n_pad = padded_len(coords.shape[0])
     heads = list(range(wl.H)) if heads is None else list(heads)
     batches = list(range(wl.B)) if batches is None else list(batches)
+    jobs = [(wl.wid, b, h, tensor, coords, wl.d, n_pad, wl.dtype)
+            for tensor in range(3) for b in batches for h in heads]
+    if workers > 1 and len(jobs) > 1:
+        import multiprocessing
+        with multiprocessing.get_context("fork").Pool(min(workers, len(jobs))) as pool:
+            slabs = pool.map(_make_one, jobs, chunksize=1)
+    else:
+        slabs = [_make_one(j) for j in jobs]
     out = []
+    it = iter(slabs)
     for tensor in range(3):
         arr = np.zeros((len(batches), len(heads), n_pad, wl.d), np.float32)
-        for bi, b in enumerate(batches):
-            for hi, h in enumerate(heads):
-                arr[bi, hi] = make_head(wl.wid, b, h, tensor, coords, wl.d, n_pad, wl.dtype)
+        for bi in range(len(batches)):
+            for hi in range(len(heads)):
+                arr[bi, hi] = next(it)
         out.append(arr)
     return out[0], out[1], out[2], coords
 
