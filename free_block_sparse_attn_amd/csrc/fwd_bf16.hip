@@ -910,6 +910,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
         for (int u = 0; u < nu; ++u) {
             const bool more = u + 1 < nu;
             const uint32_t un = static_cast<uint32_t>(more ? u + 1 : u) * HALFB;
+            // first order: the exponents of this unit's 32 moment copies (lane
+            // l % 32 holds centroid 32 u + l % 32), loaded now so the load
+            // completes under the unit's S and PV regions
+            int kex = 0;
+            if (COMP == 1) kex = a.kmom_exp[bh * nb + min(32 * u + l32, nb - 1)];
             // logits in log2 units with the count bias; -inf at exact / skim / pad
             // centroids: bit c of cm marks centroid 32 u + c as compensated
             const uint32_t valid = 32 * u + 32 <= nb ? 0xFFFFFFFFu : ((1u << (nb - 32 * u)) - 1u);
@@ -985,7 +990,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
                     for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const f16x8*>(Hop + ks * 64 * 8);
                 };
-                const int8_t* KEX = a.kmom_exp + bh * nb;   // block j's moments are stored as H_j 2^-KEX[j]
 #pragma unroll
                 for (int hb = 0; hb < 2; ++hb) {
                     // accumulator entries r = 8 hb .. 8 hb + 7 hold centroids 16 hb .. 16 hb + 15
@@ -994,9 +998,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 #pragma unroll
                         for (int r = 8 * hb; r < 8 * hb + 8; ++r) {
                             const int cc = 8 * (r >> 2) + 4 * h + (r & 3) - 16 * hb;
+                            const float ej = static_cast<float>(__shfl(kex, 16 * hb + cc));   // every lane takes part
                             const float x = (bias[r] == -INFINITY) ? 0.f
-                                : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb] +
-                                                         static_cast<float>(KEX[32 * u + 16 * hb + cc])) * a.scale;
+                                : __builtin_amdgcn_exp2f(s[rb][r] - bias[r] - st.m[rb] + ej) * a.scale;
                             wbuf[cc * BLK + 32 * rb + l32] = x;
                         }
                     wave_lds_sync();
