@@ -20,7 +20,7 @@ from ._lib import (SparseAttnError, SA_F32, SA_BF16, SA_COMP_DROP, SA_COMP_ORDER
                    SA_ROUTE_TRIAGE, SA_ROUTE_TOPK_COV, SA_ROUTE_ERROR, SA_SKIM_E4M3, SA_SKIM_MXFP4)
 
 __all__ = [
-    "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd",
+    "sparse_attn_pool", "sparse_attn_pool_static", "sparse_attn_route", "sparse_attn_fwd",
     "sparse_attn_lvsa_capacity", "sparse_attn_residual",
     "abi_version", "SparseAttnError", "SA_COMP_DROP", "SA_COMP_ORDER0", "SA_COMP_ORDER1_BLOCK",
     "SA_COMP_ORDER1_GLOBAL",
@@ -73,10 +73,19 @@ def sparse_attn_pool(q, k, v, N: int, moments=False, spreads=False, fp8=False, c
 
     `out` may pass a dict returned by an earlier call to reuse its buffers.
     """
-    return _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out)
+    return _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out, static=False)
 
 
-def _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out):
+def sparse_attn_pool_static(q, k, v, N: int, moments=False, spreads=False, fp8=False, cent=None,
+                            global_moment=False, cov=False, fp4=False, out=None) -> dict:
+    """sparse_attn_pool through the allocation-free entry point: the H_bar
+    partial sums use the library's own device scratch (no hbar_ws buffer;
+    B * H <= SPARSE_ATTN_POOL_STATIC_HEADS when H_bar is requested).  With
+    `out`, nothing is allocated here either."""
+    return _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out, static=True)
+
+
+def _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out, static):
     lib = _lib.load()
     _contig(q, k, v)
     B, H, Np, d = q.shape
@@ -100,7 +109,8 @@ def _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out)
             out["kmom_exp"] = torch.empty(B, H, nb, dtype=torch.int8, device=dev)
         if global_moment or cov:
             out["hbar"] = torch.empty(B, H, d, d, dtype=torch.float32, device=dev)          # value-major
-            out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
+            if not static:
+                out["hbar_ws"] = torch.empty(B, H, 64, d, d, dtype=torch.float32, device=dev)   # scratch
         if cov:
             out["kcov"] = torch.empty(B, H, nb, dtype=torch.float32, device=dev)
         if spreads:
@@ -123,7 +133,10 @@ def _pool(q, k, v, N, moments, spreads, fp8, cent, global_moment, cov, fp4, out)
             _ptr(g("cent")), _ptr(g("v16")), _ptr(g("kmom")), _ptr(g("kmom_exp")), _ptr(g("hbar"))]
     tail = [_ptr(g("kcov")), _ptr(g("klam")), _ptr(g("q8")), _ptr(g("k8")), _ptr(g("v8")), _ptr(g("exp8")),
             *_fp4_ptrs(out), _stream(q)]
-    _lib.check(lib.sparse_attn_pool(*head, _ptr(g("hbar_ws")), *tail))
+    if static:
+        _lib.check(lib.sparse_attn_pool_static(*head, *tail))
+    else:
+        _lib.check(lib.sparse_attn_pool(*head, _ptr(g("hbar_ws")), *tail))
     return out
 
 

@@ -21,7 +21,7 @@ SA_SKIM_E4M3, SA_SKIM_MXFP4 = 0, 1
 EXPORTED = (
     "sparse_attn_pool", "sparse_attn_route", "sparse_attn_fwd", "sparse_attn_lvsa_capacity",
     "sparse_attn_status_string", "sparse_attn_last_error", "sparse_attn_abi_version",
-    "sparse_attn_residual", "sparse_attn_residual_workspace",
+    "sparse_attn_residual", "sparse_attn_residual_workspace", "sparse_attn_pool_static",
 )
 
 
@@ -63,6 +63,9 @@ def load(path: str = LIB_PATH):
     # klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream
     lib.sparse_attn_pool.argtypes = [ctypes.POINTER(Shape), i32] + [vp] * 26
     lib.sparse_attn_pool.restype = i32
+    # as sparse_attn_pool without hbar_ws
+    lib.sparse_attn_pool_static.argtypes = [ctypes.POINTER(Shape), i32] + [vp] * 25
+    lib.sparse_attn_pool_static.restype = i32
     lib.sparse_attn_route.argtypes = [ctypes.POINTER(Shape), ctypes.POINTER(RouteSpec), vp, vp, vp, vp,
                                       vp, vp, i32, vp, vp, i32, vp]
     lib.sparse_attn_route.restype = i32

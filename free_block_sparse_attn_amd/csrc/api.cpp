@@ -40,6 +40,8 @@ bool aligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0
             return fail(SA_ERR_INVALID_ARG, "%s must be 16-byte aligned", #ptr);           \
     } while (0)
 
+static_assert(sa::POOL_STATIC_HEADS == SPARSE_ATTN_POOL_STATIC_HEADS, "static scratch size and header disagree");
+
 constexpr int MAX_BLOCKS = 4096;   // routing keeps one row of keys in LDS; kept-block bitmask size
 
 // Checks the shape; sets `empty` when there is nothing to compute.
@@ -82,12 +84,13 @@ int32_t sparse_attn_abi_version(void) { return SPARSE_ATTN_ABI_VERSION; }
 
 namespace {
 
-// The pooling call's validation and launch.
+// Shared by sparse_attn_pool and sparse_attn_pool_static: the latter passes
+// static_ws, and hbar_ws is then the library-owned scratch.
 sa_status pool_impl(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k, const void* v,
                     float* qbar, float* kbar, float* vbar, int32_t* kcount, void* cent, void* v16,
                     void* kmom, int8_t* kmom_exp, float* hbar, float* hbar_ws, float* kcov, float* klam,
                     uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
-                    uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
+                    uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream, bool static_ws) {
     bool empty = false;
     if (sa_status st = check_shape(shape, empty); st != SA_OK) return st;
     if (dtype != SA_F32 && dtype != SA_BF16) return fail(SA_ERR_INVALID_ARG, "unknown dtype %d", static_cast<int>(dtype));
@@ -105,11 +108,20 @@ sa_status pool_impl(const sa_shape* shape, sa_dtype dtype, const void* q, const 
     if (v16 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "v16 needs bf16 inputs with d == 128");
     if (kmom && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "kmom needs bf16 inputs with d == 128");
     if ((kmom != nullptr) != (kmom_exp != nullptr)) return fail(SA_ERR_INVALID_ARG, "kmom and kmom_exp go together");
-    if ((hbar != nullptr) != (hbar_ws != nullptr)) return fail(SA_ERR_INVALID_ARG, "hbar and hbar_ws go together");
+    if (!static_ws && (hbar != nullptr) != (hbar_ws != nullptr))
+        return fail(SA_ERR_INVALID_ARG, "hbar and hbar_ws go together");
     if (hbar && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "hbar needs bf16 inputs with d == 128");
     if (kcov && !hbar) return fail(SA_ERR_INVALID_ARG, "kcov needs hbar (M_j is taken against H_bar)");
     if (fp8 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "fp8 copies need bf16 inputs with d == 128");
     if (fp4 && !bf16_128) return fail(SA_ERR_UNSUPPORTED, "MXFP4 copies need bf16 inputs with d == 128");
+    if (static_ws && hbar) {
+        const int64_t heads = static_cast<int64_t>(shape->B) * shape->H;
+        if (heads > sa::POOL_STATIC_HEADS)
+            return fail(SA_ERR_UNSUPPORTED, "the library-owned H_bar scratch holds B*H <= %d heads, got %lld",
+                        sa::POOL_STATIC_HEADS, static_cast<long long>(heads));
+        hbar_ws = sa::pool_static_scratch();
+        if (hbar_ws == nullptr) return fail(SA_ERR_HIP, "the library-owned scratch has no address on this device");
+    }
     sa::PoolArgs a{shape->B, shape->H, shape->N, shape->N_pad, shape->d, q, k, v, qbar, kbar, vbar, kcount,
                    cent, static_cast<uint16_t*>(v16), kmom, kmom_exp, hbar, hbar_ws, kcov, klam,
                    q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4};
@@ -126,7 +138,17 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype, const void* q,
                            uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4, uint8_t* k4,
                            uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4, hipStream_t stream) {
     return pool_impl(shape, dtype, q, k, v, qbar, kbar, vbar, kcount, cent, v16, kmom, kmom_exp, hbar, hbar_ws,
-                     kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream);
+                     kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream, false);
+}
+
+sa_status sparse_attn_pool_static(const sa_shape* shape, sa_dtype dtype, const void* q, const void* k,
+                                  const void* v, float* qbar, float* kbar, float* vbar, int32_t* kcount,
+                                  void* cent, void* v16, void* kmom, int8_t* kmom_exp, float* hbar, float* kcov,
+                                  float* klam, uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8, uint8_t* q4,
+                                  uint8_t* k4, uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4,
+                                  hipStream_t stream) {
+    return pool_impl(shape, dtype, q, k, v, qbar, kbar, vbar, kcount, cent, v16, kmom, kmom_exp, hbar, nullptr,
+                     kcov, klam, q8, k8, v8, exp8, q4, k4, v4, qs4, ks4, vs4, stream, true);
 }
 
 int32_t sparse_attn_lvsa_capacity(const int32_t* lo, const int32_t* hi, int32_t nb, int32_t window, int32_t anchors) {

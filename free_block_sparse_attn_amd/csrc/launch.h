@@ -37,6 +37,10 @@ struct PoolArgs {
     uint8_t* vs4;
 };
 hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s);
+// (b, h) pairs whose H_bar partial sums fit the library-owned scratch
+constexpr int POOL_STATIC_HEADS = 32;
+// That scratch on the current device (resolved once per device), or null.
+float* pool_static_scratch();
 
 struct RouteArgs {
     int B, H, nb, d;

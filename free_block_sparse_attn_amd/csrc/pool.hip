@@ -14,6 +14,8 @@
 #include "common.h"
 #include "launch.h"
 
+#include <mutex>
+
 namespace sa {
 
 namespace {
@@ -821,6 +823,29 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
 }
 
 }  // namespace
+
+// Library-owned scratch of the allocation-free pooling entry point: the H_bar
+// partial sums of up to POOL_STATIC_HEADS (b, h) pairs (HBAR_PARTS d x d fp32
+// partials each, 128 MiB).  Every GPU the library runs on holds its own copy
+// until the process ends; the host only ever uses the address that
+// hipGetSymbolAddress returns for the current device.
+constexpr size_t POOL_STATIC_FLOATS = static_cast<size_t>(POOL_STATIC_HEADS) * HBAR_PARTS * 128 * 128;
+static __device__ __align__(256) float scratch[POOL_STATIC_FLOATS];
+
+float* pool_static_scratch() {
+    constexpr int MAX_DEVICES = 64;
+    static std::mutex mu;
+    static float* addr[MAX_DEVICES] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (addr[dev] == nullptr) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        addr[dev] = static_cast<float*>(p);
+    }
+    return addr[dev];
+}
 
 hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
     hipError_t e;

@@ -195,6 +195,30 @@ sa_status sparse_attn_pool(const sa_shape* shape, sa_dtype dtype,
                            uint8_t* q4, uint8_t* k4, uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4,
                            hipStream_t stream);
 
+/*
+ * sparse_attn_pool_static - sparse_attn_pool for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): the same arguments and results without
+ * hbar_ws.  The H_bar partial sums go to a scratch array the library owns,
+ * SPARSE_ATTN_POOL_STATIC_HEADS * 64 * d * d fp32 (128 MiB at d = 128), one
+ * copy per GPU the library runs on, held until the process ends.  Requests
+ * with hbar and B * H > SPARSE_ATTN_POOL_STATIC_HEADS return
+ * SA_ERR_UNSUPPORTED and launch nothing.  Nothing in the scratch carries over
+ * from one call to the next (every partial a call reads it wrote first), but
+ * all calls on one GPU share it: calls that overlap in time on one GPU race
+ * and must be ordered by the caller (one stream, or events).  Calls no
+ * allocating routine.
+ */
+#define SPARSE_ATTN_POOL_STATIC_HEADS 32
+sa_status sparse_attn_pool_static(const sa_shape* shape, sa_dtype dtype,
+                                  const void* q, const void* k, const void* v,
+                                  float* qbar, float* kbar, float* vbar, int32_t* kcount,
+                                  void* cent, void* v16, void* kmom, int8_t* kmom_exp,
+                                  float* hbar, float* kcov, float* klam,
+                                  uint8_t* q8, uint8_t* k8, uint8_t* v8, int8_t* exp8,
+                                  uint8_t* q4, uint8_t* k4, uint8_t* v4, uint8_t* qs4, uint8_t* ks4, uint8_t* vs4,
+                                  hipStream_t stream);
+
 /* Routing request.  Unused fields are ignored by the other modes. */
 typedef struct {
     int32_t mode;                 /* sa_route_mode */
