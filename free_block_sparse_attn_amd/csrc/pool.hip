@@ -413,6 +413,239 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
     }
 }
 
+// Streaming pooling with the per-block statistics that need no matrix core
+// (bf16 inputs, d = 128): one wave per block, lane l owning dimensions 2l
+// and 2l + 1.  Each tensor's 64 x 256-byte block is copied into the wave's
+// own 16 KiB of LDS by sixteen buffer_load ... lds instructions (no registers
+// held while in flight), then read twice, row by row (lane l reads dword l of
+// a row: no bank conflicts): pass 1 takes the fp64 column sums of the means
+// contract in token order, the block maxima and the fp16 copy of V; pass 2,
+// once the block statistics are known, the spreads about the means, the e4m3
+// copies (block exponents) and the MXFP4 copies.
+constexpr int SW_WAVES = 2;                     // waves (blocks) per workgroup
+
+// Key position p of a block-transposed V copy holding key k (the inverse of
+// kappa(p) = 32 ((p % 32) / 16) + 8 ((p % 16) / 4) + 4 (p / 32) + p % 4).
+__device__ __forceinline__ constexpr int v8_position(int k) {
+    return 32 * ((k >> 2) & 1) + 16 * (k >> 5) + 4 * ((k >> 3) & 3) + (k & 3);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+    return x;
+}
+
+__device__ __forceinline__ double wave_sum(double x) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+}
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Raw buffer descriptor over `bytes` bytes at p (32-bit data format).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* p, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// Copy the 16 KiB block at `src` into LDS at `lds`: instruction m moves rows
+// 4m .. 4m + 3 (lane l: row 4m + l/16, bytes 16 (l % 16) .. +15).  The
+// immediate offset (m % 4) KiB applies to both addresses, so the LDS base and
+// the scalar source offset change once per 4 KiB.
+template <int M>
+__device__ __forceinline__ void block_dma_one(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(static_cast<uintptr_t>(lds + (M >> 2) * 4096)),
+                                             16, voff, (M >> 2) * 4096, (M & 3) * 1024, 0);
+}
+
+__device__ __forceinline__ void block_dma(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff) {
+    block_dma_one<0>(rs, lds, voff);
+    block_dma_one<1>(rs, lds, voff);
+    block_dma_one<2>(rs, lds, voff);
+    block_dma_one<3>(rs, lds, voff);
+    block_dma_one<4>(rs, lds, voff);
+    block_dma_one<5>(rs, lds, voff);
+    block_dma_one<6>(rs, lds, voff);
+    block_dma_one<7>(rs, lds, voff);
+    block_dma_one<8>(rs, lds, voff);
+    block_dma_one<9>(rs, lds, voff);
+    block_dma_one<10>(rs, lds, voff);
+    block_dma_one<11>(rs, lds, voff);
+    block_dma_one<12>(rs, lds, voff);
+    block_dma_one<13>(rs, lds, voff);
+    block_dma_one<14>(rs, lds, voff);
+    block_dma_one<15>(rs, lds, voff);
+}
+
+__device__ __forceinline__ void wave_lds_fence() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <bool Q8, bool Q4>
+__global__ __launch_bounds__(64 * SW_WAVES) void pool_stream_kernel(PoolArgs a) {
+    constexpr int D = 128;
+    __shared__ uint32_t stage[SW_WAVES][BLK * D / 2];
+    const int lane = threadIdx.x & 63;
+    // block index, wave-uniform (kept in scalar registers, so the buffer
+    // descriptors built from it are scalar)
+    const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int j = blockIdx.x * SW_WAVES + w;
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int nb = a.N_pad / BLK;
+    const int nbc = BLK * ((nb + BLK - 1) / BLK);
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    const int d0 = 2 * lane;
+    if (j >= nb) {
+        // centroid pad rows
+        if (a.cent && j < nbc)
+            for (int p = 0; p < 4; ++p) *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, p, nbc, j, D) + d0) = 0u;
+        return;
+    }
+    const int n = min(BLK, a.N - BLK * j);
+    const size_t row0 = bh * a.N_pad + static_cast<size_t>(j) * BLK;      // first token row of the block
+    const bool pass2 = Q8 || Q4 || a.klam;
+    constexpr uint32_t rowb = 2 * D;
+    const uint32_t* buf = stage[w];
+    const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(stage[w]));
+    const uint32_t dma_off = (lane >> 4) * rowb + 16 * (lane & 15);
+    const __amdgpu_buffer_rsrc_t v16r = span_rsrc(a.v16 + row0 * D, BLK * rowb);
+    double spread[2] = {0.0, 0.0};
+
+#pragma unroll 1
+    for (int t = 0; t < 3; ++t) {
+        const uint16_t* src = static_cast<const uint16_t*>(t == 0 ? a.q : t == 1 ? a.k : a.v) + row0 * D;
+        wave_lds_fence();                             // the previous tensor's LDS reads are done
+        block_dma(span_rsrc(src, n * rowb), lds, dma_off);
+        __builtin_amdgcn_s_waitcnt(0x0F70);           // vmcnt(0): the block is in LDS
+        if (n < BLK)                                  // ragged tail block: rows n .. 63 read as zero
+            for (int r = n; r < BLK; ++r) stage[w][r * (D / 2) + lane] = 0u;
+        wave_lds_fence();
+
+        // ---- pass 1: sums in token order, maxima, fp16 copy of V ----
+        double s0 = 0.0, s1 = 0.0;
+        float am0 = 0.0f, am1 = 0.0f;
+#pragma unroll 16
+        for (int r = 0; r < BLK; ++r) {
+            const uint32_t xr = buf[r * (D / 2) + lane];
+            const float lo = __uint_as_float(xr << 16), hi = __uint_as_float(xr & 0xFFFF0000u);
+            s0 = s0 + static_cast<double>(lo);          // pad rows add +0.0: exact
+            s1 = s1 + static_cast<double>(hi);
+            am0 = fmaxf(am0, fabsf(lo));
+            am1 = fmaxf(am1, fabsf(hi));
+            if (t == 2 && a.v16) __builtin_amdgcn_raw_buffer_store_b32(pack_f16x2(lo, hi), v16r, 4 * lane + r * rowb, 0, 0);
+        }
+        const float am = wave_max(fmaxf(am0, am1));
+        const float m0 = static_cast<float>(s0 / static_cast<double>(n));
+        const float m1 = static_cast<float>(s1 / static_cast<double>(n));
+        float* dst = (t == 0) ? a.qbar : (t == 1) ? a.kbar : a.vbar;
+        *reinterpret_cast<float2*>(dst + (bh * nb + j) * D + d0) = make_float2(m0, m1);
+        if (a.cent && t > 0) {
+            uint16_t h0, l0, h1, l1;
+            split_hi_lo(m0, h0, l0);
+            split_hi_lo(m1, h1, l1);
+            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (t - 1), nbc, j, D) + d0) =
+                static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (t - 1) + 1, nbc, j, D) + d0) =
+                static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+        }
+        if (!pass2) continue;
+
+        // ---- pass 2 ----
+        if (a.klam && t > 0) {
+            // spread about the mean, over the block's n tokens in order
+            double acc = 0.0;
+            const double mm0 = m0, mm1 = m1;
+#pragma unroll 8
+            for (int r = 0; r < n; ++r) {
+                const uint32_t xr = buf[r * (D / 2) + lane];
+                const double e0 = static_cast<double>(__uint_as_float(xr << 16)) - mm0;
+                const double e1 = static_cast<double>(__uint_as_float(xr & 0xFFFF0000u)) - mm1;
+                acc = fma(e1, e1, fma(e0, e0, acc));
+            }
+            spread[t - 1] = acc;
+        }
+        const int ex8 = e4m3_block_exponent(am);
+        if (Q8 && lane == 0) a.exp8[(bh * nb + j) * 3 + t] = static_cast<int8_t>(ex8);
+        if (t == 0 || t == 1) {
+            if (!(Q8 || Q4)) continue;
+            const __amdgpu_buffer_rsrc_t o8 = span_rsrc((t == 0 ? a.q8 : a.k8) + row0 * D, Q8 ? BLK * D : 0);
+            const __amdgpu_buffer_rsrc_t o4 = span_rsrc((t == 0 ? a.q4 : a.k4) + row0 * (D / 2), Q4 ? BLK * D / 2 : 0);
+            const __amdgpu_buffer_rsrc_t s4 = span_rsrc((t == 0 ? a.qs4 : a.ks4) + row0 * (D / 32), Q4 ? BLK * D / 32 : 0);
+#pragma unroll 16
+            for (int r = 0; r < BLK; ++r) {
+                const uint32_t xr = buf[r * (D / 2) + lane];
+                const float lo = __uint_as_float(xr << 16), hi = __uint_as_float(xr & 0xFFFF0000u);
+                if (Q8) {
+                    const uint32_t pair = pack_fp8x2<false>(ldexpf(lo, -ex8), ldexpf(hi, -ex8), 0u);
+                    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pair), o8, 2 * lane + r * D, 0, 0);
+                }
+                if (Q4) {
+                    // one scale per token and 32 dimensions: lanes 16g .. 16g + 15
+                    float gm = fmaxf(fabsf(lo), fabsf(hi));
+#pragma unroll
+                    for (int off = 1; off < 16; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+                    const int e4 = fp4_block_exponent(gm);
+                    const uint32_t code = e2m1_code(ldexpf(lo, -e4)) | (e2m1_code(ldexpf(hi, -e4)) << 4);
+                    __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), o4, lane + r * (D / 2), 0, 0);
+                    if ((lane & 15) == 0)
+                        __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(e4 + 127), s4, (lane >> 4) + r * (D / 32), 0, 0);
+                }
+            }
+        } else if (Q8 || Q4) {
+            // V copies, block-transposed in key-position order: this lane's two
+            // dimensions (64 fp8 codes, or 32 bytes of fp4 codes, each)
+            const int ev0 = fp4_block_exponent(am0), ev1 = fp4_block_exponent(am1);   // pad rows are zero
+            uint32_t v8w[2][16], v4w[2][8];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) { v8w[0][q] = 0u; v8w[1][q] = 0u; }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) { v4w[0][q] = 0u; v4w[1][q] = 0u; }
+#pragma unroll
+            for (int r = 0; r < BLK; ++r) {
+                const uint32_t xr = buf[r * (D / 2) + lane];
+                const float lo = __uint_as_float(xr << 16), hi = __uint_as_float(xr & 0xFFFF0000u);
+                const int p = v8_position(r);
+                if (Q8) {
+                    const uint32_t pair = pack_fp8x2<false>(ldexpf(lo, -ex8), ldexpf(hi, -ex8), 0u);
+                    v8w[0][p >> 2] |= (pair & 0xFFu) << (8 * (p & 3));
+                    v8w[1][p >> 2] |= ((pair >> 8) & 0xFFu) << (8 * (p & 3));
+                }
+                if (Q4) {
+                    v4w[0][p >> 3] |= e2m1_code(ldexpf(lo, -ev0)) << (4 * (p & 7));
+                    v4w[1][p >> 3] |= e2m1_code(ldexpf(hi, -ev1)) << (4 * (p & 7));
+                }
+            }
+            if (Q8) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    uint8_t* dstv = a.v8 + ((bh * nb + j) * static_cast<size_t>(D) + d0 + c) * BLK;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<u32x4*>(dstv + 16 * q) =
+                            u32x4{v8w[c][4 * q], v8w[c][4 * q + 1], v8w[c][4 * q + 2], v8w[c][4 * q + 3]};
+                }
+            }
+            if (Q4) {
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const size_t cj = (bh * nb + j) * static_cast<size_t>(D) + d0 + c;
+                    *reinterpret_cast<u32x4*>(a.v4 + cj * (BLK / 2)) = u32x4{v4w[c][0], v4w[c][1], v4w[c][2], v4w[c][3]};
+                    *reinterpret_cast<u32x4*>(a.v4 + cj * (BLK / 2) + 16) = u32x4{v4w[c][4], v4w[c][5], v4w[c][6], v4w[c][7]};
+                    a.vs4[cj] = static_cast<uint8_t>((c ? ev1 : ev0) + 127);
+                }
+            }
+        }
+    }
+    if (b == 0 && h == 0 && lane == 0) a.kcount[j] = n;
+    if (a.klam) {
+        const double rk = wave_sum(spread[0]), rv = wave_sum(spread[1]);
+        if (lane == 0) a.klam[bh * nb + j] = static_cast<float>(0.5 * log(rk) + 0.5 * log(rv));
+    }
+}
+
 // Means-only pooling (no optional statistics): each lane owns one 16-byte
 // column chunk of one block of one tensor and folds the block's rows into fp64
 // accumulators in token order (the same contract as above).  No LDS, small
@@ -807,6 +1040,20 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 
 template <typename T, int D>
 hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (!a.kmom && (a.klam || a.q8 || a.q4)) {
+            // streaming form for the statistics that need no matrix core
+            const int nb = a.N_pad / BLK;
+            const int rows = a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb;
+            dim3 grid((rows + SW_WAVES - 1) / SW_WAVES, a.H, a.B);
+            const dim3 blk(64 * SW_WAVES);
+            if (a.q8 && a.q4) hipLaunchKernelGGL((pool_stream_kernel<true, true>), grid, blk, 0, s, a);
+            else if (a.q8) hipLaunchKernelGGL((pool_stream_kernel<true, false>), grid, blk, 0, s, a);
+            else if (a.q4) hipLaunchKernelGGL((pool_stream_kernel<false, true>), grid, blk, 0, s, a);
+            else hipLaunchKernelGGL((pool_stream_kernel<false, false>), grid, blk, 0, s, a);
+            return hipGetLastError();
+        }
+    }
     if (!a.kmom && !a.klam && !a.q8 && !a.q4) {
         constexpr int BPW = 64 / (D / Elem<T>::PER16);
         const int nb = a.N_pad / BLK;
