@@ -63,15 +63,15 @@ __device__ __forceinline__ uint64_t wave_or64(uint64_t x) {
 // are >= the candidate; it returns {candidate - 1, 0} then, which selects
 // the same keys.  Real keys are never 0 (order_key of a non-NaN value), so
 // 0 marks missing entries.
-template <int KPL>
-__device__ Threshold threshold_select(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
+template <int KPL, typename KeyOf>
+__device__ Threshold threshold_select(KeyOf keys, int nb, int k, bool cand_nonzero) {
     const int lane = lane_id();
     uint64_t kr[KPL];
     uint64_t kand = ~0ull, kor = 0ull;
 #pragma unroll
     for (int t = 0; t < KPL; ++t) {
         const int j = lane + 64 * t;
-        uint64_t key = j < nb ? keys[j] : 0ull;
+        uint64_t key = j < nb ? keys(j) : 0ull;
         if (!cand_nonzero && j < nb) { kand &= key; kor |= key; }
         if (cand_nonzero && key != 0ull) { kand &= key; kor |= key; }
         kr[t] = key;
@@ -98,12 +98,13 @@ __device__ Threshold threshold_select(const uint64_t* keys, int nb, int k, bool 
     return Threshold{T, k - gt};
 }
 
-// The same search for long rows, reading the keys from LDS at every bit.
-__device__ Threshold threshold_select_lds(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
+// The same search for long rows, forming the keys again at every bit.
+template <typename KeyOf>
+__device__ Threshold threshold_select_lds(KeyOf keys, int nb, int k, bool cand_nonzero) {
     const int lane = lane_id();
     uint64_t kand = ~0ull, kor = 0ull;
     for (int j = lane; j < nb; j += 64) {
-        const uint64_t key = keys[j];
+        const uint64_t key = keys(j);
         if (!cand_nonzero || key != 0ull) { kand &= key; kor |= key; }
     }
     kand = wave_and64(kand);
@@ -116,7 +117,7 @@ __device__ Threshold threshold_select_lds(const uint64_t* keys, int nb, int k, b
         int c = 0;
         for (int j0 = 0; j0 < nb; j0 += 64) {
             const int j = j0 + lane;
-            c += __popcll(__ballot(j < nb && keys[j] >= cand));
+            c += __popcll(__ballot(j < nb && keys(j) >= cand));
         }
         if (c == k) return Threshold{cand - 1ull, 0};   // as in threshold_select
         if (c > k) T = cand;
@@ -124,12 +125,13 @@ __device__ Threshold threshold_select_lds(const uint64_t* keys, int nb, int k, b
     int gt = 0;
     for (int j0 = 0; j0 < nb; j0 += 64) {
         const int j = j0 + lane;
-        gt += __popcll(__ballot(j < nb && keys[j] > T));
+        gt += __popcll(__ballot(j < nb && keys(j) > T));
     }
     return Threshold{T, k - gt};
 }
 
-__device__ __forceinline__ Threshold select_kth(const uint64_t* keys, int nb, int k, bool cand_nonzero) {
+template <typename KeyOf>
+__device__ __forceinline__ Threshold select_kth(KeyOf keys, int nb, int k, bool cand_nonzero) {
     const int kpl = (nb + 63) / 64;
     if (kpl <= 2) return threshold_select<2>(keys, nb, k, cand_nonzero);
     if (kpl <= 4) return threshold_select<4>(keys, nb, k, cand_nonzero);
@@ -167,8 +169,7 @@ __device__ int compact_selection(const uint64_t* keys, int nb, Threshold t, bool
 
 // fp64 scores of R query blocks against all key blocks, row-major in LDS as keys.
 template <int R>
-__device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, uint64_t* keyE,
-                           uint64_t* keyW, int nbp) {
+__device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, uint64_t* keyE, int nbp) {
     const int d = a.d, nb = a.nb, tid = threadIdx.x;
     for (int x = tid; x < R * d; x += THREADS) {
         const int r = x / d, i = x % d;
@@ -210,14 +211,11 @@ __device__ void score_rows(const RouteArgs& a, size_t bh, int row0, double* qs, 
 #pragma unroll
             for (int r = 0; r < R; ++r) keyE[r * nbp + j] = order_key(acc[r]);
         } else {
-            const double lam = static_cast<double>(a.klam[bh * nb + j]);
-            const double lgn = log(static_cast<double>(a.kcount[j]));
+            // Triage: the scaled score itself; both tier keys are formed from
+            // it during the selection (one LDS array per row instead of two)
 #pragma unroll
-            for (int r = 0; r < R; ++r) {
-                const double ss = __dmul_rn(sc, acc[r]);
-                keyE[r * nbp + j] = order_key(__dadd_rn(ss, lam));
-                keyW[r * nbp + j] = order_key(__dadd_rn(ss, lgn));
-            }
+            for (int r = 0; r < R; ++r)
+                keyE[r * nbp + j] = static_cast<uint64_t>(__double_as_longlong(__dmul_rn(sc, acc[r])));
         }
     }
     __syncthreads();
@@ -230,11 +228,10 @@ __global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
     const bool triage = a.mode == 2;
     double* qs = reinterpret_cast<double*>(smem);                            // R * d
     uint64_t* keyE = reinterpret_cast<uint64_t*>(qs + R * a.d);              // R * nbp
-    uint64_t* keyW = keyE + R * nbp;                                         // R * nbp (triage)
 
     const int row0 = blockIdx.x * R;
     const size_t bh = static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y;
-    score_rows<R>(a, bh, row0, qs, keyE, keyW, nbp);
+    score_rows<R>(a, bh, row0, qs, keyE, nbp);
 
     const int w = threadIdx.x >> 6;
     for (int r = w; r < R; r += WAVES) {
@@ -242,34 +239,49 @@ __global__ __launch_bounds__(THREADS) void route_scored_kernel(RouteArgs a) {
         if (row >= a.nb) break;
         const size_t rowid = bh * a.nb + row;
         uint64_t* kE = keyE + r * nbp;
+        const auto from_lds = [kE](int j) { return kE[j]; };
         if (!triage) {
-            const Threshold t = select_kth(kE, a.nb, a.topk, false);
+            const Threshold t = select_kth(from_lds, a.nb, a.topk, false);
             const int c = compact_selection(kE, a.nb, t, false, a.idx + rowid * a.cap, a.cap, false);
             if (lane_id() == 0) a.cnt[rowid] = c;
         } else {
-            uint64_t* kW = keyW + r * nbp;
-            // kept = first n_keep by e_skip; blank the w-keys of the others
-            const Threshold tk = select_kth(kE, a.nb, a.n_keep, false);
+            // kE holds the scaled scores ss; e_skip = fl(ss + lambda_j),
+            // w = fl(ss + ln n_j) (n_j = 64 except for the last block)
+            const float* lam = a.klam + bh * a.nb;
+            const double lgn64 = log(64.0);
+            const double lgnl = log(static_cast<double>(a.kcount[a.nb - 1]));
+            const auto eskip = [kE, lam](int j) {
+                return order_key(__dadd_rn(__longlong_as_double(static_cast<long long>(kE[j])),
+                                           static_cast<double>(lam[j])));
+            };
+            // kept = first n_keep by e_skip; then kE[j] becomes the w-key of a
+            // kept block and 0 for the others
+            const Threshold tk = select_kth(eskip, a.nb, a.n_keep, false);
             {
                 const int lane = lane_id();
                 const uint64_t lt = (1ull << lane) - 1ull;
                 int eqseen = 0;
                 for (int j0 = 0; j0 < a.nb; j0 += 64) {
                     const int j = j0 + lane;
-                    const uint64_t key = (j < a.nb) ? kE[j] : 0ull;
+                    const uint64_t key = (j < a.nb) ? eskip(j) : 0ull;
                     const bool eq = (j < a.nb) && key == tk.key;
                     const uint64_t eqm = __ballot(eq);
                     const int eqrank = eqseen + __popcll(eqm & lt);
                     const bool kept = (j < a.nb) && (key > tk.key || (eq && eqrank < tk.need));
-                    if (j < a.nb && !kept) kW[j] = 0ull;
+                    if (j < a.nb) {
+                        const double ss = __longlong_as_double(static_cast<long long>(kE[j]));
+                        kE[j] = kept ? order_key(__dadd_rn(ss, j == a.nb - 1 ? lgnl : lgn64)) : 0ull;
+                    }
                     eqseen += __popcll(eqm);
                 }
                 wave_sync();
             }
+            uint64_t* kW = kE;
+            const auto wkey = [kW](int j) { return kW[j]; };
             // refine = first n_refine of the kept blocks by w
             const bool none = a.n_refine == 0;
             Threshold tr{~0ull, 0};
-            if (!none) tr = select_kth(kW, a.nb, a.n_refine, true);
+            if (!none) tr = select_kth(wkey, a.nb, a.n_refine, true);
             const int c1 = compact_selection(kW, a.nb, tr, true, a.idx + rowid * a.cap, a.cap, none);
             // skim = kept and not refine: blank the refine keys, take every remaining candidate
             {
@@ -524,7 +536,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
 template <int R>
 hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
     const int nbp = (a.nb + 63) & ~63;
-    const size_t lds = R * a.d * sizeof(double) + (a.mode == 2 ? 2 : 1) * R * nbp * sizeof(uint64_t);
+    const size_t lds = R * a.d * sizeof(double) + R * nbp * sizeof(uint64_t);
     dim3 grid((a.nb + R - 1) / R, a.H, a.B);
     hipLaunchKernelGGL((route_scored_kernel<R>), grid, dim3(THREADS), lds, s, a);
     return hipGetLastError();
@@ -548,7 +560,7 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
     // that the waves' global k_bar loads overlap (Wan-size layer: 16 rows per
     // workgroup took 101 us, 4 rows 80 us)
     const int nbp = (a.nb + 63) & ~63;
-    const size_t per_row = (a.mode == 2 ? 2 : 1) * nbp * sizeof(uint64_t);
+    const size_t per_row = nbp * sizeof(uint64_t);
     const size_t budget = 64 * 1024;
     int R = 16;
     while (R > 1 && per_row * R > budget) R >>= 1;
