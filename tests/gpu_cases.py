@@ -161,3 +161,70 @@ def oracle_rows(wl, q, k, v, pooled, res, rows, scale=1.0):
             slack_eps=SKIM_EPS if len(sk) else None)
         out[(b, h, a)] = r if len(sk) else (r[0], r[1], np.zeros(r1 - r0))
     return out
+
+
+def _rows_worker(job):
+    """One chunk of oracle rows in a spawned worker (reads the arrays that
+    oracle_rows_parallel saved; single-threaded BLAS)."""
+    path, wl, scale, chunk = job
+    import numpy as np_
+    from oracle import attention as att
+    z = np_.load(path, allow_pickle=False)
+    d = {n: z[n] for n in z.files}
+    out = []
+    for a in chunk:
+        r0, r1 = 64 * a, min(wl.N, 64 * a + 64)
+        ex = d["idx"][a, :d["cnt"][a]]
+        sk = d["idx2"][a, :d["cnt2"][a]] if "idx2" in d else ()
+        fp8 = None
+        if len(sk):
+            names = ("q4", "qs4", "k4", "ks4", "v4", "vs4") if wl.skim_fmt == "mxfp4" else \
+                ("q8", "k8", "v8", "qexp", "kexp", "vexp")
+            fp8 = {n: d[n] for n in names}
+        r = att.rule_block(d["q"][r0:r1], d["k"], d["v"], wl.N, scale, wl.comp, d["kbar64"], d["vbar64"],
+                           d["kcount"], ex, sk, d.get("kmom"), fp8, a, hbar=d.get("hbar"),
+                           slack_eps=SKIM_EPS if len(sk) else None)
+        out.append((a, r if len(sk) else (r[0], r[1], np_.zeros(r1 - r0))))
+    return out
+
+
+def oracle_rows_parallel(wl, q, k, v, pooled, res, rows, scale=1.0, workers=16):
+    """oracle_rows for the query blocks `rows` of one head (b = h = 0 of the
+    given arrays) in spawned worker processes (fresh interpreters, no GPU
+    state; one BLAS thread each).  Returns {(0, 0, a): (o, lse, slack)}."""
+    import os
+    import tempfile
+    import multiprocessing
+    from concurrent.futures import ProcessPoolExecutor
+    arrs = {"q": q[0, 0], "k": k[0, 0], "v": v[0, 0], "kbar64": pooled["kbar64"][0, 0],
+            "vbar64": pooled["vbar64"][0, 0], "kcount": pooled["kcount"],
+            "idx": res["idx"][0, 0], "cnt": res["cnt"][0, 0]}
+    if "idx2" in res:
+        arrs["idx2"], arrs["cnt2"] = res["idx2"][0, 0], res["cnt2"][0, 0]
+        names = ("q4", "qs4", "k4", "ks4", "v4", "vs4") if wl.skim_fmt == "mxfp4" else \
+            ("q8", "k8", "v8", "qexp", "kexp", "vexp")
+        for n in names:
+            arrs[n] = pooled[n][0, 0]
+    if wl.comp == 1:
+        arrs["kmom"] = pooled["kmom"][0, 0]
+    if wl.comp == 2:
+        arrs["hbar"] = pooled["hbar"][0, 0]
+    workers = max(1, min(workers, os.cpu_count() or 1))
+    chunks = [list(rows[i::workers * 4]) for i in range(workers * 4)]
+    with tempfile.TemporaryDirectory() as tmp:
+        path = os.path.join(tmp, "head.npz")
+        np.savez(path, **arrs)
+        saved = {n: os.environ.get(n) for n in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+        for n in saved:
+            os.environ[n] = "1"
+        try:
+            ctx = multiprocessing.get_context("spawn")
+            with ProcessPoolExecutor(workers, mp_context=ctx) as ex:
+                parts = list(ex.map(_rows_worker, [(path, wl, scale, c) for c in chunks if c]))
+        finally:
+            for n, val in saved.items():
+                if val is None:
+                    os.environ.pop(n, None)
+                else:
+                    os.environ[n] = val
+    return {(0, 0, a): r for part in parts for a, r in part}

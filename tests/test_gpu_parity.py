@@ -339,6 +339,36 @@ def test_parity_full_size_sampled(wid):
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+def test_parity_full_head(wid):
+    """One whole head at the full workload shape, element by element: every
+    query block of the last head (the Triage layer: every fourth, its oracle
+    costs ~1.4 s per query block), in the benchmark's launch configuration,
+    against the oracle computed in parallel worker processes on the GPU's
+    lists (routing is checked bit-exact on the same head).  Covers the long
+    LVSA rows (at step 1; the sampled test takes steps 0 and 3) and the full
+    kept-block bitmask."""
+    wl = WORKLOADS[wid]
+    step = 1 if wl.rule == "lvsa" else 0
+    print(f"\n[case] full head {wl.name} N={wl.N} H={wl.H} nb={wl.nb} step={step}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    res = gc.run_gpu(wl, dev, coords, step=step)
+    h = wl.H - 1
+    one = lambda x: x[:, h:h + 1]
+    qs, ks, vs = one(q), one(k), one(v)
+    pooled_o = gc.oracle_pool(wl, qs, ks, vs)
+    rsub = {n: (x if n == "kcount" else x[:, h:h + 1]) for n, x in res.items()}
+    check_pool(wl, pooled_o, {n: rsub[n] for n in rsub if n not in ("out", "lse", "idx", "cnt", "idx2", "cnt2")}, vs)
+    check_route(wl, pooled_o, rsub, coords, step)
+    rows = list(range(0, wl.nb, 4 if wl.rule == "triage" else 1))
+    if rows[-1] != wl.nb - 1:
+        rows.append(wl.nb - 1)                                     # the ragged tail block
+    ref = gc.oracle_rows_parallel(wl, qs, ks, vs, pooled_o, rsub, rows)
+    worst = check_out(wl, rsub, ref, rows)
+    assert np.all(rsub["out"][:, :, wl.N:] == 0)
+    print(f"[ok] {len(rows)} query blocks, max|err|={worst:.3e}", flush=True)
+
+
 def test_full_tiny_is_elementwise():
     # the tiny workload at its full size is oracle-cheap: compare everything
     test_parity_reduced(1, "small")
