@@ -94,6 +94,27 @@ __device__ __forceinline__ uint32_t e2m1_code(float y) {
     return m | ((y < 0.0f && m != 0u) ? 8u : 0u);
 }
 
+// E2M1 codes of two values (|x| <= 6) in the low byte, x0 in the low nibble,
+// by the hardware conversion (round to nearest, ties to the even code: the
+// same decisions as e2m1_code); a magnitude-0 code is made +0 (the conversion
+// keeps the sign of a negative value that rounds to zero).
+__device__ __forceinline__ uint32_t e2m1_pair(float x0, float x1) {
+    uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, x0, x1, 1.0f, 0) & 0xFFu;
+    const uint32_t z0 = (c & 0x07u) == 0u ? 0x08u : 0u;
+    const uint32_t z1 = (c & 0x70u) == 0u ? 0x80u : 0u;
+    return c & ~(z0 | z1);
+}
+
+// Maximum over each 16-lane row of the wave (DPP row rotations; every lane
+// of the row gets it).
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false)));  // row_ror:8
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false)));  // row_ror:4
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x122, 0xF, 0xF, false)));  // row_ror:2
+    x = fmaxf(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x121, 0xF, 0xF, false)));  // row_ror:1
+    return x;
+}
+
 // Block exponent of the e4m3 copies: smallest e with amax * 2^-e <= 448.
 // amax = f * 2^k, f in [0.5, 1): 448 * 2^(k-9) = 0.875 * 2^k.
 __device__ __forceinline__ int e4m3_block_exponent(float amax) {
@@ -584,11 +605,9 @@ __global__ __launch_bounds__(64 * SW_WAVES) void pool_stream_kernel(PoolArgs a) 
                 }
                 if (Q4) {
                     // one scale per token and 32 dimensions: lanes 16g .. 16g + 15
-                    float gm = fmaxf(fabsf(lo), fabsf(hi));
-#pragma unroll
-                    for (int off = 1; off < 16; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+                    const float gm = row16_max(fmaxf(fabsf(lo), fabsf(hi)));
                     const int e4 = fp4_block_exponent(gm);
-                    const uint32_t code = e2m1_code(ldexpf(lo, -e4)) | (e2m1_code(ldexpf(hi, -e4)) << 4);
+                    const uint32_t code = e2m1_pair(ldexpf(lo, -e4), ldexpf(hi, -e4));
                     __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(code), o4, lane + r * (D / 2), 0, 0);
                     if ((lane & 15) == 0)
                         __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(e4 + 127), s4, (lane >> 4) + r * (D / 32), 0, 0);
@@ -614,8 +633,9 @@ __global__ __launch_bounds__(64 * SW_WAVES) void pool_stream_kernel(PoolArgs a) 
                     v8w[1][p >> 2] |= ((pair >> 8) & 0xFFu) << (8 * (p & 3));
                 }
                 if (Q4) {
-                    v4w[0][p >> 3] |= e2m1_code(ldexpf(lo, -ev0)) << (4 * (p & 7));
-                    v4w[1][p >> 3] |= e2m1_code(ldexpf(hi, -ev1)) << (4 * (p & 7));
+                    const uint32_t c = e2m1_pair(ldexpf(lo, -ev0), ldexpf(hi, -ev1));
+                    v4w[0][p >> 3] |= (c & 0xFu) << (4 * (p & 7));
+                    v4w[1][p >> 3] |= (c >> 4) << (4 * (p & 7));
                 }
             }
             if (Q8) {
