@@ -780,30 +780,56 @@ constexpr int HBAR_PARTS = 64;
 // acc[ob][r].  The centred keys are split into bf16 hi + lo parts, so the
 // products carry about 16 bits of each key deviation (fp32 accumulation).
 // xt: 2 * D * TPITCH bf16 of LDS, kb_s: D floats of LDS.
-__device__ __forceinline__ void add_block_moment(const PoolArgs& a, size_t bh, int j, uint16_t* xt, float* kb_s,
-                                                 f32x16 (&acc)[4]) {
+// This thread's share of block j's K and V rows (zero past the block's valid
+// tokens) and of its key mean, in registers.
+struct BlockRegs {
+    static constexpr int PT = BLK * (128 / 8) / THREADS;
+    u32x4 reg[2][PT];
+    float kbj;
+    int n;                                    // valid tokens of the block
+};
+
+__device__ __forceinline__ void load_block(const PoolArgs& a, size_t bh, int j, BlockRegs& br) {
     constexpr int D = 128;
-    using E = Elem<uint16_t>;
     constexpr int CPR = D / 8;
-    constexpr int PT = BLK * CPR / THREADS;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int tid = threadIdx.x;
     const int nb = a.N_pad / BLK;
-    const int icol = 32 * w + l32;
     const uint16_t* src[2] = {static_cast<const uint16_t*>(a.k), static_cast<const uint16_t*>(a.v)};
     const int n = min(BLK, a.N - BLK * j);
     const size_t tok0 = (bh * a.N_pad + static_cast<size_t>(j) * BLK) * D;
-    u32x4 reg[2][PT];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int q = 0; q < PT; ++q) {
+        for (int q = 0; q < BlockRegs::PT; ++q) {
             const int chunk = tid + THREADS * q;
             const int row = chunk / CPR, col0 = (chunk % CPR) * 8;
             u32x4 z = {0u, 0u, 0u, 0u};
             if (row < n) z = *reinterpret_cast<const u32x4*>(src[t] + tok0 + static_cast<size_t>(row) * D + col0);
-            reg[t][q] = z;
+            br.reg[t][q] = z;
         }
-    const float kbj = tid < D ? a.kbar[(bh * nb + j) * D + tid] : 0.0f;
+    br.kbj = tid < D ? a.kbar[(bh * nb + j) * D + tid] : 0.0f;
+    br.n = n;
+}
+
+__device__ __forceinline__ void add_loaded_moment(const BlockRegs& br, uint16_t* xt, float* kb_s, f32x16 (&acc)[4]);
+
+__device__ __forceinline__ void add_block_moment(const PoolArgs& a, size_t bh, int j, uint16_t* xt, float* kb_s,
+                                                 f32x16 (&acc)[4]) {
+    BlockRegs br;
+    load_block(a, bh, j, br);
+    add_loaded_moment(br, xt, kb_s, acc);
+}
+
+__device__ __forceinline__ void add_loaded_moment(const BlockRegs& br, uint16_t* xt, float* kb_s, f32x16 (&acc)[4]) {
+    constexpr int D = 128;
+    using E = Elem<uint16_t>;
+    constexpr int CPR = D / 8;
+    constexpr int PT = BlockRegs::PT;
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int icol = 32 * w + l32;
+    const int n = br.n;
+    const float kbj = br.kbj;
+    const auto& reg = br.reg;
     __syncthreads();                          // every wave is done with the previous staging
     if (tid < D) kb_s[tid] = kbj;
 #pragma unroll
@@ -879,7 +905,7 @@ __global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
 // accumulators (never stored), H_bar subtracted, and the deviation parked in
 // LDS as fp32 value-major Dm[o][i], from which each thread keeps an 8 x 8 tile
 // in registers.  M_j^2 is the largest eigenvalue of A = Dm^T Dm, found by
-// COV_STEPS steps of the Lanczos recurrence on A (two tile products per step,
+// at most COV_STEPS steps of the Lanczos recurrence on A (two tile products per step,
 // partial sums combined across tiles in a fixed order through LDS, so the
 // result is deterministic) and then the largest eigenvalue of the Lanczos
 // tridiagonal by 64-point multisection with Sturm counts.  Lanczos converges
@@ -901,6 +927,35 @@ __device__ __forceinline__ int sturm_below(const float* al, const float* be, int
     return c;
 }
 
+// Largest eigenvalue of the Lanczos tridiagonal T_steps (wave 0; every lane
+// returns it): Gershgorin bracket, then five rounds of 64-point multisection
+// (lane p tests lo + (p + 1) (hi - lo) / 64); the upper end of the bracket.
+__device__ __forceinline__ float top_ritz(const float* al, const float* be, int steps, int l) {
+    float lo = 0.0f, hi = 0.0f;
+    for (int k = 0; k < steps; ++k) {
+        const float off = (k > 0 ? fabsf(be[k - 1]) : 0.0f) + (k + 1 < steps ? fabsf(be[k]) : 0.0f);
+        lo = fmaxf(lo, al[k]);
+        hi = fmaxf(hi, al[k] + off);
+    }
+    hi = hi * (1.0f + 0x1p-20f) + 1e-30f;
+    for (int rnd = 0; rnd < 5; ++rnd) {
+        const float pt = lo + (hi - lo) * (static_cast<float>(l + 1) * (1.0f / 64.0f));
+        const uint64_t all = __ballot(sturm_below(al, be, steps, pt) == steps);
+        const int m = all ? __builtin_ctzll(all) : 63;
+        const float nhi = __shfl(pt, m);
+        const float nlo = m > 0 ? __shfl(pt, m - 1) : lo;
+        lo = nlo;
+        hi = nhi;
+    }
+    return hi;
+}
+
+// The recurrence stops early once the top Ritz value, taken every
+// COV_CHECK steps, moved by at most 2^-15 of itself since the previous check
+// (Ritz values rise monotonically towards M_j^2, faster than geometrically
+// once they converge, so ln M_j is then within about 2^-16 of its limit).
+constexpr int COV_CHECK = 8;
+
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void cov_norm_kernel(PoolArgs a) {
     constexpr int D = 128;
     // the block staging, then half of Dm at a time (rows 64 hf .. 64 hf + 63)
@@ -911,6 +966,8 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     __shared__ float red2[2][2];              // per-step wave partials of |y|^2 and |w|^2
     __shared__ float kb_s[D];
     __shared__ float al[COV_STEPS], be[COV_STEPS];
+    __shared__ float ritz_s;
+    __shared__ int stop_s;
     float* dmh = reinterpret_cast<float*>(stage);
     static_assert(64 * D * sizeof(float) <= sizeof(stage), "half of Dm fits the staging buffer");
     const int j = blockIdx.x;
@@ -1025,6 +1082,18 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
         if (tid == 0) { al[k] = alpha; be[k] = beta; }
         steps = k + 1;
         if (!(beta > alpha * 0x1p-20f)) break;    // invariant subspace (or A = 0): T is exact
+        if (steps % COV_CHECK == 0 && steps < COV_STEPS) {
+            // converged?  (al / be of this step were written by lane 0 of wave 0)
+            if (tid < 64) {
+                const float r = top_ritz(al, be, steps, l);
+                if (tid == 0) {
+                    stop_s = steps > COV_CHECK && r - ritz_s <= r * 0x1p-15f;
+                    ritz_s = r;
+                }
+            }
+            __syncthreads();
+            if (stop_s) break;
+        }
         const float ib = 1.0f / beta;
         qpi = qi;
         qi = w * ib;
@@ -1033,24 +1102,7 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
     __syncthreads();
     if (tid < 64) {
-        // largest eigenvalue of T: Gershgorin bracket, then five rounds of
-        // 64-point multisection (lane p tests lo + (p + 1) (hi - lo) / 64)
-        float lo = 0.0f, hi = 0.0f;
-        for (int k = 0; k < steps; ++k) {
-            const float off = (k > 0 ? fabsf(be[k - 1]) : 0.0f) + (k + 1 < steps ? fabsf(be[k]) : 0.0f);
-            lo = fmaxf(lo, al[k]);
-            hi = fmaxf(hi, al[k] + off);
-        }
-        hi = hi * (1.0f + 0x1p-20f) + 1e-30f;
-        for (int rnd = 0; rnd < 5; ++rnd) {
-            const float pt = lo + (hi - lo) * (static_cast<float>(l + 1) * (1.0f / 64.0f));
-            const uint64_t all = __ballot(sturm_below(al, be, steps, pt) == steps);
-            const int m = all ? __builtin_ctzll(all) : 63;
-            const float nhi = __shfl(pt, m);
-            const float nlo = m > 0 ? __shfl(pt, m - 1) : lo;
-            lo = nlo;
-            hi = nhi;
-        }
+        const float hi = top_ritz(al, be, steps, l);
         if (tid == 0) {
             const bool zero = al[0] == 0.0f && steps == 1;
             a.kcov[bh * nb + j] = zero ? -INFINITY : 0.5f * logf(hi);

@@ -144,9 +144,11 @@ typedef struct {
  *                        covariance-aware top-k (section 2, "Routage Sensible
  *                        a la Covariance").  H_j is rebuilt in fp32 (never
  *                        stored); M_j^2 is the largest eigenvalue of
- *                        A = (H_j - H_bar)^T (H_j - H_bar), taken from 32
- *                        Lanczos steps on A (fixed start vector, partial sums
- *                        combined in a fixed order, so deterministic) and
+ *                        A = (H_j - H_bar)^T (H_j - H_bar), taken from up to
+ *                        32 Lanczos steps on A (fixed start vector, partial
+ *                        sums combined in a fixed order, so deterministic;
+ *                        the steps stop once the top Ritz value moved by at
+ *                        most 2^-15 of itself over 8 steps) and
  *                        64-point multisection of the Lanczos tridiagonal
  *                        with Sturm counts; the Ritz value approaches M_j^2
  *                        from below and lands within fp32 rounding of it even

@@ -68,7 +68,7 @@ def check_pool(wl, pooled_o, res, v=None):
         assert np.all(err <= 2.0 ** -11 * np.abs(ref) + 1e-4 * np.abs(ref).max()), err.max()
     if "kcov" in res and "kcov" in pooled_o:
         # ln M_j: the block moment rebuilt in fp32 MFMA sums, H_bar subtracted,
-        # 32 fp32 Lanczos steps and Sturm multisection of the tridiagonal (a
+        # up to 32 fp32 Lanczos steps and Sturm multisection of the tridiagonal (a
         # Ritz value, from below) against the fp64 singular value
         ref = pooled_o["kcov"]
         assert np.array_equal(np.isneginf(res["kcov"]), np.isneginf(ref))
