@@ -156,6 +156,27 @@ __device__ __forceinline__ void dma_half(__amdgpu_buffer_rsrc_t rs, uint8_t* buf
     dma_one<7>(rs, lds, src, off);
 }
 
+// 8 KiB copied as is (lane l: bytes 16 l .. 16 l + 15 of each KiB), from
+// byte src of rs into LDS at lds; the immediate offset (M % 4) KiB applies to
+// both addresses.
+template <int M>
+__device__ __forceinline__ void dma_plain_one(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t voff, uint32_t src) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, reinterpret_cast<lds_void*>(static_cast<uintptr_t>(lds + (M >> 2) * 4096)),
+                                             16, voff, src + (M >> 2) * 4096, (M & 3) * 1024, 0);
+}
+
+__device__ __forceinline__ void dma_plain_8k(__amdgpu_buffer_rsrc_t rs, uint32_t lds, uint32_t src) {
+    const uint32_t voff = 16 * lane_id();
+    dma_plain_one<0>(rs, lds, voff, src);
+    dma_plain_one<1>(rs, lds, voff, src);
+    dma_plain_one<2>(rs, lds, voff, src);
+    dma_plain_one<3>(rs, lds, voff, src);
+    dma_plain_one<4>(rs, lds, voff, src);
+    dma_plain_one<5>(rs, lds, voff, src);
+    dma_plain_one<6>(rs, lds, voff, src);
+    dma_plain_one<7>(rs, lds, voff, src);
+}
+
 // Zero half-buffer rows r0 .. 31 (pad keys of the ragged tail block).
 __device__ __forceinline__ void zero_rows(uint8_t* buf, int r0) {
     const int l = lane_id();
@@ -527,6 +548,7 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
     typedef __attribute__((address_space(4))) const int8_t const_i8;
     const const_i8* EX = (const const_i8*)(a.exp8 + bh * nb * 3);
     const const_i32* LM = (const const_i32*)listM;
+    if (cntM <= 0) return;
     i32x8 qb8[2][2];
     int qsc[2][2];                                  // MXFP4: E8M0 scale of each B operand
 #pragma unroll
@@ -588,7 +610,6 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
             }
         }
     };
-    if (cntM <= 0) return;
     // One skim tile: S^T = K Q^T on the scaled MFMA, quantised weights, O^T += V^T P^T.
     auto tile = [&](int j, int sk, int sv, const i32x8 ka[2][2], const i32x8 va[4], const int ksc[2][2],
                     const int vsc[4]) __attribute__((always_inline)) {
@@ -699,26 +720,56 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
     }
 }
 
+// Query blocks (one wave each) per workgroup: the block first-order form
+// runs four consecutive query blocks of one head together, so that they
+// share one stream of the moment copies H_j through LDS; the other forms run
+// one query block per workgroup.
+template <int COMP>
+struct FwdWaves {
+    static constexpr int value = COMP == 1 ? 4 : 1;
+};
+
 template <int COMP, int SKIM>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void fwd_bf16_kernel(FwdArgs a) {
-    // separate LDS objects per half tile, so that each copy is known not to
-    // alias the reads of the other three
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf0[HALFB];    // K rows 0-31 (row-major, swizzled)
-    __shared__ __attribute__((aligned(16))) uint8_t kbuf1[HALFB];    // K rows 32-63
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf0[HALFB];    // V rows 0-31
-    __shared__ __attribute__((aligned(16))) uint8_t vbuf1[HALFB];    // V rows 32-63
-    __shared__ uint32_t kept_mask[128];                              // blocks not compensated (nb <= 4096)
-    // order-1 weights of 16 centroids, fp32 [centroid][row] (4 KiB: the LDS
-    // footprint stays within four workgroups per CU)
-    __shared__ float wbuf[COMP == 1 ? 16 * BLK : 1];
+__global__ __launch_bounds__(64 * FwdWaves<COMP>::value) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void fwd_bf16_kernel(FwdArgs a) {
+    constexpr int NW = FwdWaves<COMP>::value;
+    // separate LDS objects per half tile (each wave has its own row of each),
+    // so that each copy is known not to alias the reads of the other three
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf0_w[NW][HALFB];    // K rows 0-31 (row-major, swizzled)
+    __shared__ __attribute__((aligned(16))) uint8_t kbuf1_w[NW][HALFB];    // K rows 32-63
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf0_w[NW][HALFB];    // V rows 0-31
+    __shared__ __attribute__((aligned(16))) uint8_t vbuf1_w[NW][HALFB];    // V rows 32-63
+    __shared__ uint32_t kept_w[NW][128];                                  // blocks not compensated (nb <= 4096)
+    // order-1 weights of 16 centroids, fp32 [centroid][row] (4 KiB per wave)
+    __shared__ float wbuf_w[NW][COMP == 1 ? 16 * BLK : 1];
+    __shared__ uint32_t pend_w[NW];                                       // order 1: each wave's pending blocks
+    const int wv = NW > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x >> 6)) : 0;
+    uint8_t* const kbuf0 = kbuf0_w[wv];
+    uint8_t* const kbuf1 = kbuf1_w[wv];
+    uint8_t* const vbuf0 = vbuf0_w[wv];
+    uint8_t* const vbuf1 = vbuf1_w[wv];
+    uint32_t* const kept_mask = kept_w[wv];
+    float* const wbuf = wbuf_w[wv];
 
     const int nq = a.Nq_pad / BLK, nb = a.N_pad / BLK;
     const int lin0 = xcd_remap(blockIdx.x, gridDim.x);
     const int per_chunk = nq * a.H * a.B;
-    const int chunk = a.dense ? lin0 / per_chunk : 0;   // dense mode: key chunk of this wave
-    const int lin = lin0 - chunk * per_chunk;
-    const int qa = lin % nq;
-    const size_t bh = lin / nq;
+    int chunk = 0, qa;
+    size_t bh;
+    if constexpr (NW > 1) {
+        // workgroup: query blocks NW g .. NW g + NW - 1 of head bh
+        const int groups = (nq + NW - 1) / NW;
+        bh = static_cast<size_t>(lin0 / groups);
+        qa = NW * (lin0 % groups) + wv;
+    } else {
+        chunk = a.dense ? lin0 / per_chunk : 0;   // dense mode: key chunk of this wave
+        const int lin = lin0 - chunk * per_chunk;
+        qa = lin % nq;
+        bh = lin / nq;
+    }
+    // the last group of a head can have waves past its query blocks: they take
+    // part in the shared copies and barriers only
+    const bool live = qa < nq;
     const int jlo = a.dense ? static_cast<int>(static_cast<long long>(chunk) * nb / a.dense) : 0;
     const int jhi = a.dense ? static_cast<int>(static_cast<long long>(chunk + 1) * nb / a.dense) : nb;
     const int l = lane_id(), h = l >> 5, l32 = l & 31;
@@ -730,10 +781,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     const float c2 = a.scale * LOG2E;
 
     const size_t rowid = bh * nq + qa;
-    const int cntE = a.dense ? jhi - jlo : (a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0);
+    const int cntE = !live ? 0 : a.dense ? jhi - jlo : (a.cap > 0 ? min(a.cnt[rowid], a.cap) : 0);
     const int32_t* listE = a.idx + rowid * a.cap;
     const const_i32* lstE = (const const_i32*)listE;
-    const int cntM = SKIM ? min(a.cnt2[rowid], a.cap2) : 0;
+    const int cntM = SKIM && live ? min(a.cnt2[rowid], a.cap2) : 0;
     const int32_t* listM = SKIM ? a.idx2 + rowid * a.cap2 : nullptr;
 
     uint32_t dmaoff[4], oa[4], ob[4], koff[8];
@@ -942,13 +993,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
             region_cs_rb<true>(kbuf0, kbuf1, koff, qh[1], s[1], s[0], bias, 0u, st.m[0], c2, pb[0][0],
                                    pb[1][0], ls[0]);
             wave_lds_sync();
-            if (more) {
+            if (COMP != 1 && more) {
                 dma_half(rc, kbuf0, un, dmaoff);
                 dma_half(rc, kbuf1, plane + un, dmaoff);
             }
             settle_row<0>(st, s[0], 1.0f, pb[0][0], pb[1][0], ls[0]);
             // V planes of unit u: only the next unit's K planes may still be in flight
-            if (more) wait_vmcnt<16>(); else wait_vmcnt<0>();
+            // (order 1 loads the next unit's planes after its moment stream)
+            if (COMP != 1 && more) wait_vmcnt<16>(); else wait_vmcnt<0>();
             wave_lds_sync();
             region_cpv_rb<true, 0>(st, vbuf0, vbuf1, oa, ob, pb[0][0], pb[1][0], s[1], bias, st.m[1], c2,
                                        pb[0][1], pb[1][1], ls[1]);
@@ -960,7 +1012,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                                             unused0, unused1, unused_l);
             }
             wave_lds_sync();
-            if (more) {
+            // (order 1: the V plane buffers first carry the shared moment
+            // stream, and the next unit's V planes load after it)
+            if (COMP != 1 && more) {
                 dma_half(rc, vbuf0, 2 * plane + un, dmaoff);
                 dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
             }
@@ -976,27 +1030,34 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                     st.a1[rb] += acc;
                 }
             }
-            if (COMP == 1) {
+            if constexpr (COMP == 1) {
                 // O^T[., row] += w_j[row] T, T = H_j^T Q^T (fp32, 16 MFMAs per
                 // 32-wide d block), for every compensated block j of this unit,
                 // with w_j = scale 2^{L - m + e_j} / n_j (L without the count bias,
                 // e_j the exponent of the block's fp16 moment copy).
-                // Two batches of 16 centroids (their weights staged in LDS); the A
-                // operands (H_j^T in MFMA operand order) load two d blocks ahead.
+                // The workgroup's NW query blocks stream the union of their
+                // compensated blocks' H_j (32 KiB each, MFMA operand order)
+                // through the four plane buffers of all the waves, now four
+                // 32 KiB slots (the next unit's planes load after the stream):
+                // each wave copies its quarter of each H_j, copies run three
+                // blocks ahead, and a wave skips the products of the blocks it
+                // does not compensate.
+                static_assert(NW * HALFB == D * D * 2, "the NW buffers of one kind hold one H_j");
                 const uint16_t* MOM = static_cast<const uint16_t*>(a.kmom) + bh * nb * static_cast<size_t>(D) * D;
-                // H_j^T in MFMA operand order: (d block, i step) operands are 1 KiB runs
-                auto load_step = [&](int jj, int db, f16x8 op[8]) __attribute__((always_inline)) {
-                    const uint16_t* Hop = MOM + static_cast<size_t>(jj) * D * D + (db * 8 * 64 + l) * 8;
-#pragma unroll
-                    for (int ks = 0; ks < 8; ++ks) op[ks] = *reinterpret_cast<const f16x8*>(Hop + ks * 64 * 8);
+                const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+                    const_cast<uint16_t*>(MOM), 0, nb * D * D * 2, RSRC_WORD3);
+                // this wave's 8 KiB of the moment copy of block 32 u + cc into slot dst
+                auto copy_quarter = [&](uint8_t* dst, int cc) __attribute__((always_inline)) {
+                    dma_plain_8k(rm, static_cast<uint32_t>(reinterpret_cast<uintptr_t>(dst)) + wv * HALFB,
+                                 static_cast<uint32_t>(32 * u + cc) * (D * D * 2) + wv * HALFB);
                 };
-#pragma unroll
-                for (int hb = 0; hb < 2; ++hb) {
-                    // accumulator entries r = 8 hb .. 8 hb + 7 hold centroids 16 hb .. 16 hb + 15
+                // this wave's weights of the 16 centroids of batch hb into wbuf
+                auto weights = [&](int hb) __attribute__((always_inline)) {
 #pragma unroll
                     for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-                        for (int r = 8 * hb; r < 8 * hb + 8; ++r) {
+                        for (int r = 0; r < 16; ++r) {
+                            if ((r >> 3) != hb) continue;          // entries 8 hb .. 8 hb + 7
                             const int cc = 8 * (r >> 2) + 4 * h + (r & 3) - 16 * hb;
                             const float ej = static_cast<float>(__shfl(kex, 16 * hb + cc));   // every lane takes part
                             const float x = (bias[r] == -INFINITY) ? 0.f
@@ -1004,46 +1065,84 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
                             wbuf[cc * BLK + 32 * rb + l32] = x;
                         }
                     wave_lds_sync();
-                    uint32_t pend = 0;                    // compensated blocks of this batch
+                };
+                // O^T += w_c T for centroid c of the current batch, moment copy in slot src
+                auto apply = [&](const uint8_t* src, int c) __attribute__((always_inline)) {
+                    const float w0 = wbuf[c * BLK + l32], w1 = wbuf[c * BLK + 32 + l32];
 #pragma unroll
-                    for (int c = 0; c < 16; ++c) {
-                        const int cc = 16 * hb + c;
-                        if (32 * u + cc < nb && !((keptw >> cc) & 1u)) pend |= 1u << c;
-                    }
-                    if (pend) {
-                        // steps (block, d block) in order; each step's eight A
-                        // operands load two steps (32 MFMAs) ahead into one of two
-                        // operand sets
-                        int c = __builtin_ctz(pend);
-                        pend &= pend - 1;
-                        f16x8 buf[2][8];
-                        load_step(32 * u + 16 * hb + c, 0, buf[0]);
-                        load_step(32 * u + 16 * hb + c, 1, buf[1]);
-                        for (;;) {
-                            const float w0 = wbuf[c * BLK + l32], w1 = wbuf[c * BLK + 32 + l32];
-                            const int nc = pend ? __builtin_ctz(pend) : -1;
+                    for (int db = 0; db < 4; ++db) {
+                        f16x8 op[8];
 #pragma unroll
-                            for (int db = 0; db < 4; ++db) {
-                                f32x16 t[2] = {f32x16{}, f32x16{}};
+                        for (int ks = 0; ks < 8; ++ks)
+                            op[ks] = *reinterpret_cast<const f16x8*>(src + (db * 8 + ks) * 1024 + 16 * l);
+                        f32x16 t[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-                                for (int ks = 0; ks < 8; ++ks)
+                        for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-                                    for (int rb = 0; rb < 2; ++rb)
-                                        t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(buf[db & 1][ks], qh[rb][ks], t[rb], 0, 0, 0);
-                                if (db < 2) load_step(32 * u + 16 * hb + c, db + 2, buf[db & 1]);
-                                else if (nc >= 0) load_step(32 * u + 16 * hb + nc, db - 2, buf[db & 1]);
+                            for (int rb = 0; rb < 2; ++rb)
+                                t[rb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(op[ks], qh[rb][ks], t[rb], 0, 0, 0);
 #pragma unroll
-                                for (int r = 0; r < 16; ++r) {
-                                    st.o[db][0][r] = fmaf(t[0][r], w0, st.o[db][0][r]);
-                                    st.o[db][1][r] = fmaf(t[1][r], w1, st.o[db][1][r]);
-                                }
-                            }
-                            if (nc < 0) break;
-                            c = nc;
-                            pend &= pend - 1;
+                        for (int r = 0; r < 16; ++r) {
+                            st.o[db][0][r] = fmaf(t[0][r], w0, st.o[db][0][r]);
+                            st.o[db][1][r] = fmaf(t[1][r], w1, st.o[db][1][r]);
                         }
                     }
-                    wave_lds_sync();
+                };
+                uint8_t* const slots[4] = {&kbuf0_w[0][0], &kbuf1_w[0][0], &vbuf0_w[0][0], &vbuf1_w[0][0]};
+                // this wave's compensated blocks of the unit (bit cc: block 32 u + cc)
+                uint32_t pend = 0;
+                const uint32_t nvalid = 32 * u + 32 <= nb ? 0xFFFFFFFFu : ((1u << (nb - 32 * u)) - 1u);
+                if (live) pend = ~keptw & nvalid;
+                if (l == 0) pend_w[wv] = pend;
+                __syncthreads();      // every wave's list; every wave is done with the unit's planes
+                uint32_t uni = 0;
+#pragma unroll
+                for (int w2 = 0; w2 < NW; ++w2) uni |= pend_w[w2];
+                const int n = __popc(uni);
+                // the union's blocks in order: step i takes block nth(i), copied into slot i % 4
+                uint32_t ahead = uni;                 // blocks whose copies are not issued yet
+                auto issue = [&](uint8_t* dst) __attribute__((always_inline)) {
+                    const int c = __builtin_ctz(ahead);
+                    ahead &= ahead - 1;
+                    copy_quarter(dst, c);
+                };
+                if (n > 0) issue(slots[0]);
+                if (n > 1) issue(slots[1]);
+                if (n > 2) issue(slots[2]);
+                uint32_t rest = uni;                  // blocks not applied yet
+                int batch = -1;
+                // one step: refill slot (i + 3) % 4 (read at step i - 1), wait for block i's copy, apply it
+                auto step = [&](int i, const uint8_t* cur, uint8_t* refill) __attribute__((always_inline)) {
+                    const int later = min(n - 1 - i, 3);       // copies issued after block i's
+                    if (i + 3 < n) {
+                        __syncthreads();                        // step i - 1 is done with the slot
+                        issue(refill);
+                    }
+                    if (later >= 3) wait_vmcnt<24>();
+                    else if (later == 2) wait_vmcnt<16>();
+                    else if (later == 1) wait_vmcnt<8>();
+                    else wait_vmcnt<0>();
+                    __syncthreads();                            // every quarter of block i has landed
+                    const int c = __builtin_ctz(rest);
+                    rest &= rest - 1;
+                    if ((c >> 4) != batch) {
+                        batch = c >> 4;
+                        weights(batch);
+                    }
+                    if ((pend >> c) & 1u) apply(cur, c & 15);
+                };
+                for (int i = 0; i < n; i += 4) {
+                    step(i, slots[0], slots[3]);
+                    if (i + 1 < n) step(i + 1, slots[1], slots[0]);
+                    if (i + 2 < n) step(i + 2, slots[2], slots[1]);
+                    if (i + 3 < n) step(i + 3, slots[3], slots[2]);
+                }
+                __syncthreads();      // the slots are free again
+                if (more) {
+                    dma_half(rc, kbuf0, un, dmaoff);
+                    dma_half(rc, kbuf1, plane + un, dmaoff);
+                    dma_half(rc, vbuf0, 2 * plane + un, dmaoff);
+                    dma_half(rc, vbuf1, 3 * plane + un, dmaoff);
                 }
             }
         }
@@ -1092,6 +1191,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
     if constexpr (SKIM > 0) skim_tiles<SKIM>(a, st, bh, qa, listM, cntM, c2);
 
     // ---- normalise and write O (bf16) and lse ----
+    if (!live) return;
     const size_t cofs = static_cast<size_t>(chunk) * per_chunk * BLK;   // B H Nq_pad rows per chunk
     uint16_t* O = static_cast<uint16_t*>(a.out) + headq + cofs * D;
     float* OF = static_cast<float*>(a.out) + headq + cofs * D;
@@ -1125,8 +1225,11 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(1, 1))) void
 template <int COMP, int SKIM>
 hipError_t launch_t(const FwdArgs& a, hipStream_t s) {
     const int nq = a.Nq_pad / BLK;
-    dim3 grid(nq * a.H * a.B * (a.dense > 0 ? a.dense : 1));
-    hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64), 0, s, a);
+    constexpr int NW = FwdWaves<COMP>::value;
+    if (NW > 1 && a.dense > 0) return hipErrorInvalidValue;   // dense mode runs without compensation
+    const int groups = (nq + NW - 1) / NW;
+    dim3 grid(groups * a.H * a.B * (a.dense > 0 ? a.dense : 1));
+    hipLaunchKernelGGL((fwd_bf16_kernel<COMP, SKIM>), grid, dim3(64 * NW), 0, s, a);
     return hipGetLastError();
 }
 
