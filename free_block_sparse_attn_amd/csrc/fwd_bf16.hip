@@ -1111,18 +1111,16 @@ void fwd_bf16_kernel(FwdArgs a) {
                 if (n > 2) issue(slots[2]);
                 uint32_t rest = uni;                  // blocks not applied yet
                 int batch = -1;
-                // one step: refill slot (i + 3) % 4 (read at step i - 1), wait for block i's copy, apply it
+                // One step: wait for block i's copy (the two later copies may still be
+                // in flight), then refill slot (i + 3) % 4, which every wave finished
+                // reading in step i - 1 (before this step's barrier), and apply block i.
                 auto step = [&](int i, const uint8_t* cur, uint8_t* refill) __attribute__((always_inline)) {
-                    const int later = min(n - 1 - i, 3);       // copies issued after block i's
-                    if (i + 3 < n) {
-                        __syncthreads();                        // step i - 1 is done with the slot
-                        issue(refill);
-                    }
-                    if (later >= 3) wait_vmcnt<24>();
-                    else if (later == 2) wait_vmcnt<16>();
+                    const int later = min(n - 1 - i, 2);       // copies issued after block i's
+                    if (later >= 2) wait_vmcnt<16>();
                     else if (later == 1) wait_vmcnt<8>();
                     else wait_vmcnt<0>();
                     __syncthreads();                            // every quarter of block i has landed
+                    if (i + 3 < n) issue(refill);
                     const int c = __builtin_ctz(rest);
                     rest &= rest - 1;
                     if ((c >> 4) != batch) {
