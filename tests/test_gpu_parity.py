@@ -183,6 +183,27 @@ def test_parity_reduced(wid, size):
         print(f"[ok] step={step} max|err|={worst:.3e}", flush=True)
 
 
+@pytest.mark.parametrize("grid,rem", [((5, 11, 11), 2), ((6, 12, 14), 0)])
+def test_parity_order1_workgroup_tails(grid, rem):
+    """The block first-order form runs four query blocks of a head per
+    workgroup and streams the union of their compensated blocks' moments;
+    these heads leave 2 and 0 query blocks over in the last group (the small,
+    medium and full-size cases leave 1 and 3), and three heads put groups of
+    consecutive heads side by side."""
+    wl = WORKLOADS[3].small(*grid, H=3)
+    assert wl.nb % 4 == rem
+    print(f"\n[case] {wl.name} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords)
+    check_pool(wl, pooled_o, res, v)
+    check_route(wl, pooled_o, res, coords, 0)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 @pytest.mark.parametrize("sc", [0.37, 4.0])
 @pytest.mark.parametrize("kind", ["topk", "error", "cov", "triage", "order1", "global", "lvsa", "mxfp4"])
 def test_parity_softmax_scale(kind, sc):
