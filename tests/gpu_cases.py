@@ -49,8 +49,10 @@ def inputs(wl, heads=None):
     return (q, k, v), to_device(wl, q, k, v), coords
 
 
-def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
-    """pool -> route -> fwd through the C ABI; returns dict of numpy results."""
+def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0, edit=None):
+    """pool -> route -> fwd through the C ABI; returns dict of numpy results.
+
+    `edit` may replace the route's lists: (idx, cnt, idx2, cnt2) -> new ones."""
     import free_block_sparse_attn_amd as fbsa
     q, k, v = dev_qkv
     N = wl.N
@@ -79,6 +81,8 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0):
     else:
         idx, cnt, idx2, cnt2 = fbsa.sparse_attn_route(
             pooled, N, fbsa.SA_ROUTE_TRIAGE, n_keep=wl.n_keep, n_refine=wl.n_refine, scale=scale)
+    if edit is not None:
+        idx, cnt, idx2, cnt2 = edit(idx, cnt, idx2, cnt2)
     out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2,
                                     skim_fmt=fbsa.SA_SKIM_MXFP4 if wl.skim_fmt == "mxfp4" else fbsa.SA_SKIM_E4M3)
     torch.cuda.synchronize()

@@ -291,6 +291,72 @@ def test_parity_one_kept_block(kind):
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
+def _far_skim_lists(J, full):
+    """List edit: block J moves to every query block's skim list (from its
+    exact list, or in place of the last skim entry); the query blocks in
+    `full` get no exact tile and every block skimmed."""
+    def edit(idx, cnt, idx2, cnt2):
+        idx, cnt, idx2, cnt2 = (t.cpu().numpy().copy() for t in (idx, cnt, idx2, cnt2))
+        B, H, nq, _ = idx.shape
+        new2 = np.zeros((B, H, nq, nq), np.int32)
+        for b in range(B):
+            for h in range(H):
+                for a in range(nq):
+                    ex = [int(x) for x in idx[b, h, a, :cnt[b, h, a]]]
+                    sk = [int(x) for x in idx2[b, h, a, :cnt2[b, h, a]]]
+                    if (b, h, a) in full:
+                        ex, sk = [], list(range(nq))
+                    elif J in ex:
+                        ex.remove(J)
+                        sk.append(J)
+                    elif J not in sk:
+                        sk = sk[:-1] + [J]
+                    idx[b, h, a, :len(ex)] = sorted(ex)
+                    cnt[b, h, a] = len(ex)
+                    new2[b, h, a, :len(sk)] = sorted(sk)
+                    cnt2[b, h, a] = len(sk)
+        return tuple(torch.from_numpy(x).cuda() for x in (idx, cnt, new2, cnt2))
+    return edit
+
+
+def test_skim_far_above_reference():
+    """Skim tiles whose logits lie ~100 binades above every logit a row saw
+    before them (the skim tier's lazy rescale by ~2^-100), and query blocks
+    with no exact tile and every block skimmed (no centroids: a skim tile
+    sets those rows' first reference)."""
+    from dataclasses import replace
+    wl = replace(_batch2_workload("triage"), B=1)
+    q, k, v, coords = gc.make_qkv(wl)
+    J = wl.nb // 2
+    # head 0: one shared direction lowers every row's logits against all
+    # blocks but J by ~72 (~100 binades), so J's ordinary-sized logits lie far
+    # above everything else (large logits would instead measure the
+    # block-scaled MFMA's sums, whose error grows with their magnitude);
+    # head 1 unchanged
+    inJ = np.zeros(wl.N_pad, bool)
+    inJ[64 * J:64 * J + 64] = True
+    valid = np.arange(wl.N_pad) < wl.N
+    q[0, 0, :wl.N, 0] += 6.0
+    k[0, 0, valid & ~inJ, 0] -= 12.0
+    q, k = (torch.from_numpy(x).to(torch.bfloat16).float().numpy() for x in (q, k))
+    c2 = 1.4426950408889634
+    s = np.einsum("nd,md->nm", q[0, 0, :wl.N].astype(np.float64), k[0, 0, :wl.N].astype(np.float64)) * c2
+    iJ = inJ[:wl.N]
+    assert np.min(s[:, iJ].max(axis=1) - s[:, ~iJ].max(axis=1)) > 40.0
+    assert np.abs(s[:, iJ]).max() < 32.0
+    dev = gc.to_device(wl, q, k, v)
+    full = {(0, 0, 0), (0, 1, 0), (0, 1, wl.nb - 1)}
+    print(f"\n[case] {wl.name} far skim block {J} N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords, edit=_far_skim_lists(J, full))
+    assert all(J in gc.lists_of(res["idx2"], res["cnt2"], 0, h, a) for h in range(wl.H) for a in range(wl.nb))
+    assert all(res["cnt"][0, h, a] == 0 and res["cnt2"][0, h, a] == wl.nb for (_, h, a) in full)
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    assert np.all(res["out"][:, :, wl.N:] == 0)
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 def _batch2_workload(kind):
     from dataclasses import replace
     from workloads import configs as C
