@@ -13,6 +13,7 @@
 // and the spreads all read contiguous LDS runs.
 #include "common.h"
 #include "launch.h"
+#include "lds_tile.h"
 
 #include <mutex>
 
@@ -122,6 +123,43 @@ __device__ __forceinline__ int e4m3_block_exponent(float amax) {
     int k;
     float f = frexpf(amax, &k);
     return (f <= 0.875f) ? k - 9 : k - 8;
+}
+
+// The fp16 copy H_j 2^-e of one block's moment (d = 128) from the four
+// waves' accumulators (wave w: key columns 32 w .. 32 w + 31, value rows in
+// four 32-row blocks; accumulator entry r of lane l: row 8 (r/4) + 4 (l/32)
+// + r % 4, column l % 32): the block exponent e (largest entry in
+// [2^14, 2^15)) from the maxima the waves leave in red4[0..3], then every
+// element in the forward pass's MFMA A-operand order.
+__device__ __forceinline__ void store_moment(const PoolArgs& a, const f32x16 acc[4], float* red4, int w,
+                                             size_t blk) {
+    constexpr int D = 128;
+    const int l = threadIdx.x & 63, hl = l >> 5;
+    float am = 0.0f;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[ob][r]));
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    if (l == 0) red4[w] = am;
+    __syncthreads();
+    am = fmaxf(fmaxf(red4[0], red4[1]), fmaxf(red4[2], red4[3]));
+    const int ex = f16_block_exponent(am);
+    if (threadIdx.x == 0) a.kmom_exp[blk] = static_cast<int8_t>(ex);
+    // element (o, i) of H_j^T at ((o/32 * 8 + i/16) * 64 + o%32 + 32 (i/8 % 2))
+    // * 8 + i%8, so each (32-row d block, 16-wide i step) operand is 1 KiB
+    // contiguous
+    const int icol = 32 * w + (l & 31);
+    uint16_t* mom = static_cast<uint16_t*>(a.kmom) + blk * static_cast<size_t>(D) * D;
+    const int ks = icol >> 4, hi8 = (icol >> 3) & 1, e8 = icol & 7;
+#pragma unroll
+    for (int ob = 0; ob < 4; ++ob) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int o32 = 8 * (r >> 2) + 4 * hl + (r & 3);
+            mom[((ob * 8 + ks) * 64 + o32 + 32 * hi8) * 8 + e8] = f32_to_f16(ldexpf(acc[ob][r], -ex));
+        }
+    }
 }
 
 template <typename T, int D>
@@ -281,32 +319,7 @@ __global__ __launch_bounds__(THREADS) void pool_kernel(PoolArgs a) {
                     acc[ob] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[ob], 0, 0, 0);
                 }
             }
-            // fp16 copy H_j 2^-e with the block's exponent e (largest entry
-            // in [2^14, 2^15)), written to kmom_exp
-            float am = 0.0f;
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) am = fmaxf(am, fabsf(acc[ob][r]));
-            for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-            if (l == 0) red[48 + w] = am;         // slots no other phase uses
-            __syncthreads();
-            am = fmaxf(fmaxf(red[48], red[49]), fmaxf(red[50], red[51]));
-            const int ex = f16_block_exponent(am);
-            if (tid == 0) a.kmom_exp[bh * nb + j] = static_cast<int8_t>(ex);
-            // MFMA A-operand order of the forward pass: element (o, i) of H_j^T
-            // at ((o/32 * 8 + i/16) * 64 + o%32 + 32 (i/8 % 2)) * 8 + i%8, so each
-            // (32-row d block, 16-wide i step) operand is 1 KiB contiguous
-            uint16_t* mom = static_cast<uint16_t*>(a.kmom) + (bh * nb + j) * static_cast<size_t>(D) * D;
-            const int ks = icol >> 4, hi8 = (icol >> 3) & 1, e8 = icol & 7;
-#pragma unroll
-            for (int ob = 0; ob < 4; ++ob) {
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int o32 = 8 * (r >> 2) + 4 * hl + (r & 3);
-                    mom[((ob * 8 + ks) * 64 + o32 + 32 * hi8) * 8 + e8] = f32_to_f16(ldexpf(acc[ob][r], -ex));
-                }
-            }
+            store_moment(a, acc, red + 48, w, bh * nb + j);   // slots no other phase uses
         }
 
         // Phase 5 (optional): per-block power-of-two scaled e4m3 copies.
@@ -462,8 +475,6 @@ __device__ __forceinline__ double wave_sum(double x) {
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
     return x;
 }
-
-typedef __attribute__((address_space(3))) void lds_void;
 
 // Raw buffer descriptor over `bytes` bytes at p (32-bit data format).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t span_rsrc(const void* p, uint32_t bytes) {
@@ -664,6 +675,133 @@ __global__ __launch_bounds__(64 * SW_WAVES) void pool_stream_kernel(PoolArgs a) 
         const double rk = wave_sum(spread[0]), rv = wave_sum(spread[1]);
         if (lane == 0) a.klam[bh * nb + j] = static_cast<float>(0.5 * log(rk) + 0.5 * log(rv));
     }
+}
+
+// Pooling with the per-block first-order moments (bf16, d = 128): one
+// workgroup of four waves per block.  Q, K and V are copied into LDS in the
+// forward pass's swizzled 64-row tile layout (each wave copies 16 rows of
+// each; no registers held while in flight).  Waves 0-2 then take the fp64
+// column sums of Q, K and V in token order (lane l: dimensions 2l, 2l + 1,
+// as the streaming form) and wave 3 writes the fp16 copy of V.  The moment
+// H_j = sum_n v_n (k_n - k_bar)^T comes from bf16 MFMAs whose operands are
+// both column slices read with the transposed LDS reads: V^T for the value
+// rows and the centred keys (split into bf16 high + low parts) for the key
+// columns, wave w taking key columns 32 w .. 32 w + 31.
+__global__ __launch_bounds__(THREADS) void pool_moment_kernel(PoolArgs a) {
+    constexpr int D = 128;
+    __shared__ __attribute__((aligned(16))) uint8_t tile[3][TILEB];
+    __shared__ float kmean[D];
+    __shared__ float red[4];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int nb = a.N_pad / BLK;
+    const int nbc = BLK * ((nb + BLK - 1) / BLK);
+    const size_t bh = static_cast<size_t>(b) * a.H + h;
+    if (j >= nb) {
+        // centroid pad rows (launched only when cent is requested)
+        for (int x = tid; x < 4 * D; x += THREADS) cent_row(a.cent, bh, x / D, nbc, j, D)[x % D] = 0;
+        return;
+    }
+    const int n = min(BLK, a.N - BLK * j);
+    const size_t row0 = bh * a.N_pad + static_cast<size_t>(j) * BLK;      // first token row of the block
+
+    // wave w copies rows 16 w .. 16 w + 15 of each tensor (rows past n read as 0)
+    {
+        uint32_t off[4];
+        dma_offsets(off);
+        const uint32_t part = (w >> 1) * HALFB + (w & 1) * 4096;
+#pragma unroll
+        for (int t = 0; t < 3; ++t) {
+            const uint16_t* src = static_cast<const uint16_t*>(t == 0 ? a.q : t == 1 ? a.k : a.v) + row0 * D;
+            const __amdgpu_buffer_rsrc_t rs = span_rsrc(src, n * ROWB);
+            const uint32_t lds = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(tile[t])) + part;
+            dma_one<0>(rs, lds, part, off);
+            dma_one<1>(rs, lds, part, off);
+            dma_one<2>(rs, lds, part, off);
+            dma_one<3>(rs, lds, part, off);
+        }
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (n < BLK) {                                   // ragged tail block: rows n .. 63 are zero
+#pragma unroll
+        for (int t = 0; t < 3; ++t)
+            for (int x = tid; x < (BLK - n) * (ROWB / 4); x += THREADS)
+                reinterpret_cast<uint32_t*>(tile[t] + n * ROWB)[x] = 0u;
+        __syncthreads();
+    }
+
+    if (w < 3) {
+        // means of tensor w: sums in token order (pad rows add +0.0: exact)
+        const uint8_t* tb = tile[w];
+        double s0 = 0.0, s1 = 0.0;
+#pragma unroll 16
+        for (int r = 0; r < BLK; ++r) {
+            const uint32_t xr = *reinterpret_cast<const uint32_t*>(tb + r * ROWB + 16 * swz(r, lane >> 2) + 4 * (lane & 3));
+            s0 = s0 + static_cast<double>(__uint_as_float(xr << 16));
+            s1 = s1 + static_cast<double>(__uint_as_float(xr & 0xFFFF0000u));
+        }
+        const int d0 = 2 * lane;
+        const float m0 = static_cast<float>(s0 / static_cast<double>(n));
+        const float m1 = static_cast<float>(s1 / static_cast<double>(n));
+        float* dst = (w == 0) ? a.qbar : (w == 1) ? a.kbar : a.vbar;
+        *reinterpret_cast<float2*>(dst + (bh * nb + j) * D + d0) = make_float2(m0, m1);
+        if (a.cent && w > 0) {
+            uint16_t h0, l0, h1, l1;
+            split_hi_lo(m0, h0, l0);
+            split_hi_lo(m1, h1, l1);
+            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1), nbc, j, D) + d0) =
+                static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1) + 1, nbc, j, D) + d0) =
+                static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+        }
+        if (w == 1) {
+            kmean[d0] = m0;
+            kmean[d0 + 1] = m1;
+        }
+    } else if (a.v16) {
+        // fp16 copy of V, 16-byte chunks (pad rows zero)
+#pragma unroll 4
+        for (int i = 0; i < 16; ++i) {
+            const int r = 4 * i + (lane >> 4), c = lane & 15;
+            const u32x4 x = *reinterpret_cast<const u32x4*>(tile[2] + r * ROWB + 16 * swz(r, c));
+            *reinterpret_cast<u32x4*>(a.v16 + (row0 + r) * D + 8 * c) = bf16x8_to_f16x8(x);
+        }
+    }
+    if (b == 0 && h == 0 && tid == 0) a.kcount[j] = n;
+    __syncthreads();                                 // kmean
+
+    // H_j[o][i] for key columns i = 32 w + l % 32 and the four 32-row value
+    // blocks; both operands walk a 16-row step in the transposed reads' row
+    // order, so their reduction indices pair up
+    uint32_t oa[4], ob[4];
+    pv_offsets(oa, ob);
+    const float kb = kmean[32 * w + (lane & 31)];
+    f32x16 acc[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) acc[o] = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        const int step = (ks >> 1) * HALFB + (ks & 1) * 16 * ROWB;
+        const u32x4 kr = __builtin_bit_cast(u32x4, tr_read_pair(tile[1] + step + oa[w], tile[1] + step + ob[w]));
+        bf16x8 bhi, blo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t bits = (e & 1) ? (kr[e >> 1] & 0xFFFF0000u) : (kr[e >> 1] << 16);
+            const float x = __uint_as_float(bits) - kb;
+            const __bf16 hi = static_cast<__bf16>(x);
+            bhi[e] = hi;
+            blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+        }
+#pragma unroll
+        for (int o = 0; o < 4; ++o) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, tr_read_pair(tile[2] + step + oa[o], tile[2] + step + ob[o]));
+            acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[o], 0, 0, 0);
+            acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[o], 0, 0, 0);
+        }
+    }
+    store_moment(a, acc, red, w, bh * nb + j);
 }
 
 // Means-only pooling (no optional statistics): each lane owns one 16-byte
@@ -1134,9 +1272,15 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
         hipLaunchKernelGGL((pool_means_kernel<T, D>), grid, dim3(256), 0, s, a);
         return hipGetLastError();
     }
-    const size_t lds = pool_lds<T, D>();
     const int nb = a.N_pad / BLK;
     dim3 grid(a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb, a.H, a.B);
+    if constexpr (sizeof(T) == 2 && D == 128) {
+        if (a.kmom && !a.klam && !a.q8 && !a.q4) {
+            hipLaunchKernelGGL(pool_moment_kernel, grid, dim3(THREADS), 0, s, a);
+            return hipGetLastError();
+        }
+    }
+    const size_t lds = pool_lds<T, D>();
     hipLaunchKernelGGL((pool_kernel<T, D>), grid, dim3(THREADS), lds, s, a);
     return hipGetLastError();
 }
