@@ -41,6 +41,7 @@ template <> struct Elem<uint16_t> {
 };
 
 constexpr int THREADS = 256;
+constexpr int HBAR_PARTS = 64;    // partial sums of PISA's H_bar per head (blocks j = c mod 64)
 
 // Centroid planes of one (b, h): plane p row j at cent + ((bh * 4 + p) * nbc + j) * D.
 __device__ __forceinline__ uint16_t* cent_row(void* cent, size_t bh, int plane, int nbc, int j, int D) {
@@ -677,16 +678,22 @@ __global__ __launch_bounds__(64 * SW_WAVES) void pool_stream_kernel(PoolArgs a) 
     }
 }
 
-// Pooling with the per-block first-order moments (bf16, d = 128): one
-// workgroup of four waves per block.  Q, K and V are copied into LDS in the
-// forward pass's swizzled 64-row tile layout (each wave copies 16 rows of
-// each; no registers held while in flight).  Waves 0-2 then take the fp64
-// column sums of Q, K and V in token order (lane l: dimensions 2l, 2l + 1,
-// as the streaming form) and wave 3 writes the fp16 copy of V.  The moment
-// H_j = sum_n v_n (k_n - k_bar)^T comes from bf16 MFMAs whose operands are
+// Pooling with the first-order moments (bf16, d = 128): four waves per
+// 64-token block.  Q, K and V are copied into LDS in the forward pass's
+// swizzled 64-row tile layout (each wave copies 16 rows of each; no
+// registers held while in flight).  Waves 0-2 then take the fp64 column sums
+// of Q, K and V in token order (lane l: dimensions 2l, 2l + 1, as the
+// streaming form) and wave 3 writes the fp16 copy of V.  The moment
+// H_j = sum_n v_n (k_n - k_bar_j)^T comes from bf16 MFMAs whose operands are
 // both column slices read with the transposed LDS reads: V^T for the value
 // rows and the centred keys (split into bf16 high + low parts) for the key
 // columns, wave w taking key columns 32 w .. 32 w + 31.
+// HBAR false: one block per workgroup, H_j stored in fp16 (kmom).
+// HBAR true: workgroup c of a head takes blocks c, c + HBAR_PARTS, ... and
+// writes the sum of their H_j to its slot of hbar_ws (PISA's global H_bar,
+// reduced by hbar_reduce_kernel), so K and V are read once for the means and
+// the moments together.
+template <bool HBAR>
 __global__ __launch_bounds__(THREADS) void pool_moment_kernel(PoolArgs a) {
     constexpr int D = 128;
     __shared__ __attribute__((aligned(16))) uint8_t tile[3][TILEB];
@@ -694,22 +701,22 @@ __global__ __launch_bounds__(THREADS) void pool_moment_kernel(PoolArgs a) {
     __shared__ float red[4];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int j = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int h = blockIdx.y, b = blockIdx.z;
     const int nb = a.N_pad / BLK;
     const int nbc = BLK * ((nb + BLK - 1) / BLK);
     const size_t bh = static_cast<size_t>(b) * a.H + h;
-    if (j >= nb) {
-        // centroid pad rows (launched only when cent is requested)
-        for (int x = tid; x < 4 * D; x += THREADS) cent_row(a.cent, bh, x / D, nbc, j, D)[x % D] = 0;
-        return;
-    }
-    const int n = min(BLK, a.N - BLK * j);
-    const size_t row0 = bh * a.N_pad + static_cast<size_t>(j) * BLK;      // first token row of the block
+    uint32_t off[4], oa[4], ob[4];
+    dma_offsets(off);
+    pv_offsets(oa, ob);
+    f32x16 acc[4];
+#pragma unroll
+    for (int o = 0; o < 4; ++o) acc[o] = f32x16{};
 
-    // wave w copies rows 16 w .. 16 w + 15 of each tensor (rows past n read as 0)
-    {
-        uint32_t off[4];
-        dma_offsets(off);
+    // means, fp16 V copy and moment (added to acc) of block j
+    auto block = [&](int j) __attribute__((always_inline)) {
+        const int n = min(BLK, a.N - BLK * j);
+        const size_t row0 = bh * a.N_pad + static_cast<size_t>(j) * BLK;   // first token row of the block
+        // wave w copies rows 16 w .. 16 w + 15 of each tensor (rows past n read as 0)
         const uint32_t part = (w >> 1) * HALFB + (w & 1) * 4096;
 #pragma unroll
         for (int t = 0; t < 3; ++t) {
@@ -721,87 +728,108 @@ __global__ __launch_bounds__(THREADS) void pool_moment_kernel(PoolArgs a) {
             dma_one<2>(rs, lds, part, off);
             dma_one<3>(rs, lds, part, off);
         }
-    }
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (n < BLK) {                                   // ragged tail block: rows n .. 63 are zero
-#pragma unroll
-        for (int t = 0; t < 3; ++t)
-            for (int x = tid; x < (BLK - n) * (ROWB / 4); x += THREADS)
-                reinterpret_cast<uint32_t*>(tile[t] + n * ROWB)[x] = 0u;
+        wait_vmcnt<0>();
         __syncthreads();
-    }
+        if (n < BLK) {                               // ragged tail block: rows n .. 63 are zero
+#pragma unroll
+            for (int t = 0; t < 3; ++t)
+                for (int x = tid; x < (BLK - n) * (ROWB / 4); x += THREADS)
+                    reinterpret_cast<uint32_t*>(tile[t] + n * ROWB)[x] = 0u;
+            __syncthreads();
+        }
 
-    if (w < 3) {
-        // means of tensor w: sums in token order (pad rows add +0.0: exact)
-        const uint8_t* tb = tile[w];
-        double s0 = 0.0, s1 = 0.0;
+        if (w < 3) {
+            // means of tensor w: sums in token order (pad rows add +0.0: exact)
+            const uint8_t* tb = tile[w];
+            double s0 = 0.0, s1 = 0.0;
 #pragma unroll 16
-        for (int r = 0; r < BLK; ++r) {
-            const uint32_t xr = *reinterpret_cast<const uint32_t*>(tb + r * ROWB + 16 * swz(r, lane >> 2) + 4 * (lane & 3));
-            s0 = s0 + static_cast<double>(__uint_as_float(xr << 16));
-            s1 = s1 + static_cast<double>(__uint_as_float(xr & 0xFFFF0000u));
-        }
-        const int d0 = 2 * lane;
-        const float m0 = static_cast<float>(s0 / static_cast<double>(n));
-        const float m1 = static_cast<float>(s1 / static_cast<double>(n));
-        float* dst = (w == 0) ? a.qbar : (w == 1) ? a.kbar : a.vbar;
-        *reinterpret_cast<float2*>(dst + (bh * nb + j) * D + d0) = make_float2(m0, m1);
-        if (a.cent && w > 0) {
-            uint16_t h0, l0, h1, l1;
-            split_hi_lo(m0, h0, l0);
-            split_hi_lo(m1, h1, l1);
-            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1), nbc, j, D) + d0) =
-                static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
-            *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1) + 1, nbc, j, D) + d0) =
-                static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
-        }
-        if (w == 1) {
-            kmean[d0] = m0;
-            kmean[d0 + 1] = m1;
-        }
-    } else if (a.v16) {
-        // fp16 copy of V, 16-byte chunks (pad rows zero)
+            for (int r = 0; r < BLK; ++r) {
+                const uint32_t xr =
+                    *reinterpret_cast<const uint32_t*>(tb + r * ROWB + 16 * swz(r, lane >> 2) + 4 * (lane & 3));
+                s0 = s0 + static_cast<double>(__uint_as_float(xr << 16));
+                s1 = s1 + static_cast<double>(__uint_as_float(xr & 0xFFFF0000u));
+            }
+            const int d0 = 2 * lane;
+            const float m0 = static_cast<float>(s0 / static_cast<double>(n));
+            const float m1 = static_cast<float>(s1 / static_cast<double>(n));
+            float* dst = (w == 0) ? a.qbar : (w == 1) ? a.kbar : a.vbar;
+            *reinterpret_cast<float2*>(dst + (bh * nb + j) * D + d0) = make_float2(m0, m1);
+            if (a.cent && w > 0) {
+                uint16_t h0, l0, h1, l1;
+                split_hi_lo(m0, h0, l0);
+                split_hi_lo(m1, h1, l1);
+                *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1), nbc, j, D) + d0) =
+                    static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+                *reinterpret_cast<uint32_t*>(cent_row(a.cent, bh, 2 * (w - 1) + 1, nbc, j, D) + d0) =
+                    static_cast<uint32_t>(l0) | (static_cast<uint32_t>(l1) << 16);
+            }
+            if (w == 1) {
+                kmean[d0] = m0;
+                kmean[d0 + 1] = m1;
+            }
+        } else if (a.v16) {
+            // fp16 copy of V, 16-byte chunks (pad rows zero)
 #pragma unroll 4
-        for (int i = 0; i < 16; ++i) {
-            const int r = 4 * i + (lane >> 4), c = lane & 15;
-            const u32x4 x = *reinterpret_cast<const u32x4*>(tile[2] + r * ROWB + 16 * swz(r, c));
-            *reinterpret_cast<u32x4*>(a.v16 + (row0 + r) * D + 8 * c) = bf16x8_to_f16x8(x);
+            for (int i = 0; i < 16; ++i) {
+                const int r = 4 * i + (lane >> 4), c = lane & 15;
+                const u32x4 x = *reinterpret_cast<const u32x4*>(tile[2] + r * ROWB + 16 * swz(r, c));
+                *reinterpret_cast<u32x4*>(a.v16 + (row0 + r) * D + 8 * c) = bf16x8_to_f16x8(x);
+            }
         }
-    }
-    if (b == 0 && h == 0 && tid == 0) a.kcount[j] = n;
-    __syncthreads();                                 // kmean
+        if (b == 0 && h == 0 && tid == 0) a.kcount[j] = n;
+        __syncthreads();                             // kmean
 
-    // H_j[o][i] for key columns i = 32 w + l % 32 and the four 32-row value
-    // blocks; both operands walk a 16-row step in the transposed reads' row
-    // order, so their reduction indices pair up
-    uint32_t oa[4], ob[4];
-    pv_offsets(oa, ob);
-    const float kb = kmean[32 * w + (lane & 31)];
-    f32x16 acc[4];
+        // H_j[o][i] for key columns i = 32 w + l % 32 and the four 32-row
+        // value blocks; both operands walk a 16-row step in the transposed
+        // reads' row order, so their reduction indices pair up
+        const float kb = kmean[32 * w + (lane & 31)];
 #pragma unroll
-    for (int o = 0; o < 4; ++o) acc[o] = f32x16{};
+        for (int ks = 0; ks < 4; ++ks) {
+            const int step = (ks >> 1) * HALFB + (ks & 1) * 16 * ROWB;
+            const u32x4 kr = __builtin_bit_cast(u32x4, tr_read_pair(tile[1] + step + oa[w], tile[1] + step + ob[w]));
+            bf16x8 bhi, blo;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        const int step = (ks >> 1) * HALFB + (ks & 1) * 16 * ROWB;
-        const u32x4 kr = __builtin_bit_cast(u32x4, tr_read_pair(tile[1] + step + oa[w], tile[1] + step + ob[w]));
-        bf16x8 bhi, blo;
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t bits = (e & 1) ? (kr[e >> 1] & 0xFFFF0000u) : (kr[e >> 1] << 16);
+                const float x = __uint_as_float(bits) - kb;
+                const __bf16 hi = static_cast<__bf16>(x);
+                bhi[e] = hi;
+                blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+            }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t bits = (e & 1) ? (kr[e >> 1] & 0xFFFF0000u) : (kr[e >> 1] << 16);
-            const float x = __uint_as_float(bits) - kb;
-            const __bf16 hi = static_cast<__bf16>(x);
-            bhi[e] = hi;
-            blo[e] = static_cast<__bf16>(x - static_cast<float>(hi));
+            for (int o = 0; o < 4; ++o) {
+                const bf16x8 av =
+                    __builtin_bit_cast(bf16x8, tr_read_pair(tile[2] + step + oa[o], tile[2] + step + ob[o]));
+                acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[o], 0, 0, 0);
+                acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[o], 0, 0, 0);
+            }
         }
-#pragma unroll
-        for (int o = 0; o < 4; ++o) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, tr_read_pair(tile[2] + step + oa[o], tile[2] + step + ob[o]));
-            acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bhi, acc[o], 0, 0, 0);
-            acc[o] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, blo, acc[o], 0, 0, 0);
+    };
+
+    if constexpr (!HBAR) {
+        const int j = blockIdx.x;
+        if (j >= nb) {
+            // centroid pad rows (launched only when cent is requested)
+            for (int x = tid; x < 4 * D; x += THREADS) cent_row(a.cent, bh, x / D, nbc, j, D)[x % D] = 0;
+            return;
         }
+        block(j);
+        store_moment(a, acc, red, w, bh * nb + j);
+    } else {
+        const int c = blockIdx.x;
+        if (a.cent && nb + c < nbc)                  // centroid pad row nb + c
+            for (int x = tid; x < 4 * D; x += THREADS) cent_row(a.cent, bh, x / D, nbc, nb + c, D)[x % D] = 0;
+        for (int j = c; j < nb; j += HBAR_PARTS) {
+            block(j);
+            __syncthreads();                         // every wave is done with the tiles
+        }
+        float* dst = a.hbar_ws + (bh * HBAR_PARTS + c) * static_cast<size_t>(D) * D;
+        const int icol = 32 * w + (lane & 31), hl = lane >> 5;
+#pragma unroll
+        for (int o = 0; o < 4; ++o)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) dst[(32 * o + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + icol] = acc[o][r];
     }
-    store_moment(a, acc, red, w, bh * nb + j);
 }
 
 // Means-only pooling (no optional statistics): each lane owns one 16-byte
@@ -910,7 +938,6 @@ __global__ __launch_bounds__(256) void pool_means_kernel(PoolArgs a) {
 // writes its partial G[o][i] = sum_j sum_n v_n[o] (k_n[i] - kbar_j[i]).
 // Pass 2 adds the 64 partials of a head in a fixed order (fp64) and divides
 // by nb, so H_bar is bit-reproducible.
-constexpr int HBAR_PARTS = 64;
 
 // Adds block j's centred moment G[o][i] = sum_n v_n[o] (k_n[i] - kbar_j[i])
 // to the workgroup's fp32 MFMA accumulators: wave w, lane l holds column
@@ -1276,7 +1303,7 @@ hipError_t launch_pool_t(const PoolArgs& a, hipStream_t s) {
     dim3 grid(a.cent ? BLK * ((nb + BLK - 1) / BLK) : nb, a.H, a.B);
     if constexpr (sizeof(T) == 2 && D == 128) {
         if (a.kmom && !a.klam && !a.q8 && !a.q4) {
-            hipLaunchKernelGGL(pool_moment_kernel, grid, dim3(THREADS), 0, s, a);
+            hipLaunchKernelGGL(pool_moment_kernel<false>, grid, dim3(THREADS), 0, s, a);
             return hipGetLastError();
         }
     }
@@ -1312,12 +1339,18 @@ float* pool_static_scratch() {
 
 hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
     hipError_t e;
-    if (bf16) e = a.d == 128 ? launch_pool_t<uint16_t, 128>(a, s) : launch_pool_t<uint16_t, 64>(a, s);
-    else e = a.d == 128 ? launch_pool_t<float, 128>(a, s) : launch_pool_t<float, 64>(a, s);
-    if (e != hipSuccess || !a.hbar) return e;
-    // after the means (the centring uses kbar)
-    hipLaunchKernelGGL(hbar_partial_kernel, dim3(HBAR_PARTS, a.B * a.H), dim3(THREADS), 0, s, a);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (bf16 && a.d == 128 && a.hbar && !a.kmom && !a.klam && !a.q8 && !a.q4) {
+        // the means, the fp16 V copy and the H_bar partial sums in one pass over Q, K, V
+        hipLaunchKernelGGL(pool_moment_kernel<true>, dim3(HBAR_PARTS, a.H, a.B), dim3(THREADS), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    } else {
+        if (bf16) e = a.d == 128 ? launch_pool_t<uint16_t, 128>(a, s) : launch_pool_t<uint16_t, 64>(a, s);
+        else e = a.d == 128 ? launch_pool_t<float, 128>(a, s) : launch_pool_t<float, 64>(a, s);
+        if (e != hipSuccess || !a.hbar) return e;
+        // after the means (the centring uses kbar)
+        hipLaunchKernelGGL(hbar_partial_kernel, dim3(HBAR_PARTS, a.B * a.H), dim3(THREADS), 0, s, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     hipLaunchKernelGGL(hbar_reduce_kernel, dim3(a.B * a.H), dim3(THREADS), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess || !a.kcov) return e;
     hipLaunchKernelGGL(cov_norm_kernel, dim3(a.N_pad / BLK, a.B * a.H), dim3(THREADS), 0, s, a);
