@@ -47,7 +47,10 @@ MFMA_FP8_PEAK_TFLOPS = 5000.0
 FP32_PEAK_TFLOPS = 157.3
 HBM_PEAK_GBS = 8000.0
 FP64_PEAK_TFLOPS = 78.6
-FWD_SOURCE = os.path.join(ROOT, "free_block_sparse_attn_amd", "csrc", "fwd_bf16.hip")
+# the forward kernel's source and the headers it includes: counters taken on
+# other sources are stale
+FWD_SOURCES = [os.path.join(ROOT, "free_block_sparse_attn_amd", "csrc", f)
+               for f in ("fwd_bf16.hip", "lds_tile.h", "common.h", "launch.h")]
 HEADLINE = "triage-e4m3"
 
 LAYERS = {
@@ -88,6 +91,15 @@ def layer_workload(name):
     return table[key]
 
 
+def fwd_source_sha256():
+    """sha256 over the forward kernel's source files, in FWD_SOURCES order."""
+    h = hashlib.sha256()
+    for path in FWD_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
 def traffic_record(layer):
     """HBM bytes per forward launch from the committed counter summary of this
     layer, if it was taken on the current kernel source."""
@@ -95,7 +107,7 @@ def traffic_record(layer):
     try:
         with open(path) as f:
             rec = json.load(f)
-        src = hashlib.sha256(open(FWD_SOURCE, "rb").read()).hexdigest()
+        src = fwd_source_sha256()
         if rec.get("source_sha256") != src:
             return None
         return rec["bytes_per_launch"]
