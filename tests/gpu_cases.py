@@ -55,6 +55,22 @@ def inputs(wl, heads=None):
     return (q, k, v), to_device(wl, q, k, v), coords
 
 
+def pool_results(pooled, n_pad):
+    """The pooling pass's device outputs as numpy, in the oracle's layouts."""
+    res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
+    if "v8" in res:
+        res["v8"] = v8_row_major(res["v8"], n_pad)
+    if "q4" in res:
+        for n in ("q4", "k4"):
+            res[n] = unpack_nibbles(res[n])
+        for n in ("qs4", "ks4", "vs4"):
+            res[n] = res[n].astype(np.int64) - 127
+        res["v4"] = v8_row_major(unpack_nibbles(res["v4"]), n_pad)
+    if "kmom" in res:
+        res["kmom"] = kmom_value_major(res["kmom"])
+    return res
+
+
 def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0, edit=None):
     """pool -> route -> fwd through the C ABI; returns dict of numpy results.
 
@@ -92,17 +108,7 @@ def run_gpu(wl, dev_qkv, coords, step=0, scale=1.0, edit=None):
     out, lse = fbsa.sparse_attn_fwd(q, k, v, N, scale, wl.comp, pooled, idx, cnt, idx2, cnt2,
                                     skim_fmt=fbsa.SA_SKIM_MXFP4 if wl.skim_fmt == "mxfp4" else fbsa.SA_SKIM_E4M3)
     torch.cuda.synchronize()
-    res = {n: (t.cpu().float() if t.dtype == torch.bfloat16 else t.cpu()).numpy() for n, t in pooled.items()}
-    if "v8" in res:
-        res["v8"] = v8_row_major(res["v8"], wl.N_pad)
-    if "q4" in res:
-        for n in ("q4", "k4"):
-            res[n] = unpack_nibbles(res[n])
-        for n in ("qs4", "ks4", "vs4"):
-            res[n] = res[n].astype(np.int64) - 127
-        res["v4"] = v8_row_major(unpack_nibbles(res["v4"]), wl.N_pad)
-    if "kmom" in res:
-        res["kmom"] = kmom_value_major(res["kmom"])
+    res = pool_results(pooled, wl.N_pad)
     res["idx"], res["cnt"] = idx.cpu().numpy(), cnt.cpu().numpy()
     if idx2 is not None:
         res["idx2"], res["cnt2"] = idx2.cpu().numpy(), cnt2.cpu().numpy()

@@ -463,6 +463,31 @@ def test_full_tiny_is_elementwise():
     test_parity_reduced(1, "small")
 
 
+@pytest.mark.parametrize("opts", [
+    dict(moments=True, spreads=True, fp8=True),          # the general pooling kernel's moment phase
+    dict(global_moment=True, spreads=True),              # streaming means, then the H_bar partial-sum pass
+    dict(moments=True, global_moment=True, fp4=True),    # both moment forms at once
+])
+def test_pool_option_combinations(opts):
+    """Pooling options requested together, which take the kernels no
+    configured layer uses: every output against the oracle's pooling."""
+    import free_block_sparse_attn_amd as fbsa
+    from dataclasses import replace
+    wl = replace(WORKLOADS[3].small(9, 20, 45), H=2)
+    print(f"\n[case] pool {sorted(opts)} N={wl.N} nb={wl.nb}", flush=True)
+    (q, k, v), (dq, dk, dv), _ = gc.inputs(wl)
+    pooled = fbsa.sparse_attn_pool(dq, dk, dv, wl.N, **opts)
+    torch.cuda.synchronize()
+    res = gc.pool_results(pooled, wl.N_pad)
+    pooled_o = pooling.pool(q, k, v, wl.N, moments=opts.get("moments", False), spreads=opts.get("spreads", False),
+                            fp8=opts.get("fp8", False), hbar=opts.get("global_moment", False),
+                            fp4=opts.get("fp4", False))
+    for n in ("kmom", "hbar", "klam", "q8", "q4"):
+        assert (n in res) == (n in pooled_o), n
+    check_pool(wl, pooled_o, res, v)
+    print("[ok]", flush=True)
+
+
 @pytest.mark.parametrize("comp,sc", [(0, 1.0), (-1, 1.0), (0, 0.37), (0, 4.0)])
 def test_parity_fp32_ragged(comp, sc):
     """The fp32 path (d = 64) on a grid with a ragged tail (1200 tokens: 19
