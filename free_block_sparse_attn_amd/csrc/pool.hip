@@ -1052,13 +1052,18 @@ __global__ __launch_bounds__(THREADS) void hbar_partial_kernel(PoolArgs a) {
         }
 }
 
+// One workgroup per (head, D*D / HBAR_SLICES elements): each element's 64
+// partials added in a fixed order (c = 0 .. 63) whatever the split.
+constexpr int HBAR_SLICES = 16;
+
 __global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
-    constexpr int D = 128;
+    constexpr int D = 128, PER = D * D / HBAR_SLICES;
     const size_t bh = blockIdx.x;
     const int nb = a.N_pad / BLK;
     const float* part = a.hbar_ws + bh * HBAR_PARTS * static_cast<size_t>(D) * D;
-    for (int e = threadIdx.x; e < D * D; e += THREADS) {
+    for (int e = blockIdx.y * PER + threadIdx.x; e < (blockIdx.y + 1) * PER; e += THREADS) {
         double sum = 0.0;
+#pragma unroll 16
         for (int c = 0; c < HBAR_PARTS; ++c) sum += static_cast<double>(part[static_cast<size_t>(c) * D * D + e]);
         a.hbar[bh * D * D + e] = static_cast<float>(sum / static_cast<double>(nb));
     }
@@ -1351,7 +1356,7 @@ hipError_t launch_pool(const PoolArgs& a, bool bf16, hipStream_t s) {
         hipLaunchKernelGGL(hbar_partial_kernel, dim3(HBAR_PARTS, a.B * a.H), dim3(THREADS), 0, s, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(hbar_reduce_kernel, dim3(a.B * a.H), dim3(THREADS), 0, s, a);
+    hipLaunchKernelGGL(hbar_reduce_kernel, dim3(a.B * a.H, HBAR_SLICES), dim3(THREADS), 0, s, a);
     if ((e = hipGetLastError()) != hipSuccess || !a.kcov) return e;
     hipLaunchKernelGGL(cov_norm_kernel, dim3(a.N_pad / BLK, a.B * a.H), dim3(THREADS), 0, s, a);
     return hipGetLastError();
