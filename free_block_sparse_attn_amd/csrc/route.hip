@@ -533,6 +533,284 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
     }
 }
 
+// ---- scores on the fp64 matrix cores (d = 64 or 128, nb <= 2048) ----
+//
+// v_mfma_f64_16x16x4_f64 adds its four products to the accumulator one fused
+// multiply-add at a time, in k order, so a chain of them over k = 0, 4, 8, ...
+// gives the same bits as the sequential fp64 FMA contract above (the operands
+// are fp32 values, whose products fp64 holds exactly).  A workgroup takes 16
+// query blocks, the MFMA's N, and walks the key blocks 16 at a time, its M: in
+// round p wave w scores key tile 8p + w against the 16 rows, and the tiles go
+// through LDS to the waves that own the rows (wave w owns rows w and w + 8).
+// Those waves keep their rows' keys in registers, lane l holding key blocks
+// l + 64 t, so 16 rows need no LDS key arrays and the selection makes no LDS
+// traffic.  Key 0 marks a missing entry (no real key is 0).
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+constexpr int MROWS = 16;          // query blocks per workgroup (the MFMA's N)
+constexpr int MWAVES = 8;
+
+// Threshold search of threshold_select on keys already in registers; the
+// candidates are the nonzero keys (slots past nb hold 0, which no compare
+// against a candidate >= 1 counts, so every slot takes part).
+template <int KPL>
+__device__ __forceinline__ Threshold threshold_regs(const uint64_t (&kr)[KPL], int k) {
+    uint64_t kand = ~0ull, kor = 0ull;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t)
+        if (kr[t] != 0ull) { kand &= kr[t]; kor |= kr[t]; }
+    kand = wave_and64(kand);
+    kor = wave_or64(kor);
+    const uint64_t diff = kand ^ kor;
+    const int top = diff ? 63 - __builtin_clzll(diff) : -1;
+    uint64_t T = top < 0 ? kand : (top == 63 ? 0ull : (kand & ~((2ull << top) - 1ull)));
+    for (int b = top; b >= 0; --b) {
+        const uint64_t cand = T | (1ull << b);
+        int c = 0;
+#pragma unroll
+        for (int t = 0; t < KPL; ++t) c += __popcll(__ballot(kr[t] >= cand));
+        if (c == k) return Threshold{cand - 1ull, 0};
+        if (c > k) T = cand;
+    }
+    int gt = 0;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) gt += __popcll(__ballot(kr[t] > T));
+    return Threshold{T, k - gt};
+}
+
+// compact_selection over register keys (slot t covers blocks 64 t .. 64 t + 63)
+template <int KPL>
+__device__ __forceinline__ int compact_regs(const uint64_t (&kr)[KPL], Threshold t, int32_t* out, int cap, bool none) {
+    const int lane = lane_id();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int base = 0, eqseen = 0;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+        const uint64_t key = kr[s];
+        const bool cand = key != 0ull && !none;
+        const bool gt = cand && key > t.key;
+        const bool eq = cand && key == t.key;
+        const uint64_t eqm = __ballot(eq);
+        const int eqrank = eqseen + __popcll(eqm & lt);
+        const bool sel = gt || (eq && eqrank < t.need);
+        const uint64_t selm = __ballot(sel);
+        const int pos = base + __popcll(selm & lt);
+        if (sel && pos < cap) out[pos] = 64 * s + lane;
+        base += __popcll(selm);
+        eqseen += __popcll(eqm);
+    }
+    for (int p = base + lane; p < cap; p += 64) out[p] = -1;
+    return base;
+}
+
+// The selection of one row from its register keys: top-k modes take kr as
+// the order keys (0 past nb); Triage takes kr as the scaled scores ss.
+template <int KPL, int MODE>
+__device__ __forceinline__ void select_row(const RouteArgs& a, size_t bh, int row, const uint64_t (&kr)[KPL]) {
+    const int nb = a.nb, lane = lane_id();
+    const size_t rowid = bh * nb + row;
+    if constexpr (MODE != 2) {
+        const Threshold t = threshold_regs(kr, a.topk);
+        const int c = compact_regs(kr, t, a.idx + rowid * a.cap, a.cap, false);
+        if (lane == 0) a.cnt[rowid] = c;
+        return;
+    }
+    // Triage: kept = first n_keep by e_skip = fl(ss + lambda_j); of those,
+    // refine = first n_refine by w = fl(ss + ln n_j); skim = kept, not refine
+    const float* lam = a.klam + bh * nb;
+    const double lgn64 = log(64.0);
+    const double lgnl = log(static_cast<double>(a.kcount[nb - 1]));
+    uint64_t ek[KPL];
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+        const int j = 64 * s + lane;
+        ek[s] = j < nb ? order_key(__dadd_rn(__longlong_as_double(static_cast<long long>(kr[s])), static_cast<double>(lam[j])))
+                       : 0ull;
+    }
+    const Threshold tk = threshold_regs(ek, a.n_keep);
+    {
+        const uint64_t lt = (1ull << lane) - 1ull;
+        int eqseen = 0;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            const int j = 64 * s + lane;
+            const uint64_t key = ek[s];
+            const bool eq = key != 0ull && key == tk.key;
+            const uint64_t eqm = __ballot(eq);
+            const int eqrank = eqseen + __popcll(eqm & lt);
+            const bool kept = key != 0ull && (key > tk.key || (eq && eqrank < tk.need));
+            const double ss = __longlong_as_double(static_cast<long long>(kr[s]));
+            ek[s] = kept ? order_key(__dadd_rn(ss, j == nb - 1 ? lgnl : lgn64)) : 0ull;
+            eqseen += __popcll(eqm);
+        }
+    }
+    const bool none = a.n_refine == 0;
+    Threshold tr{~0ull, 0};
+    if (!none) tr = threshold_regs(ek, a.n_refine);
+    const int c1 = compact_regs(ek, tr, a.idx + rowid * a.cap, a.cap, none);
+    {
+        const uint64_t lt = (1ull << lane) - 1ull;
+        int eqseen = 0;
+#pragma unroll
+        for (int s = 0; s < KPL; ++s) {
+            const uint64_t key = ek[s];
+            const bool cand = key != 0ull && !none;
+            const bool eq = cand && key == tr.key;
+            const uint64_t eqm = __ballot(eq);
+            const int eqrank = eqseen + __popcll(eqm & lt);
+            const bool ref = cand && (key > tr.key || (eq && eqrank < tr.need));
+            if (ref) ek[s] = 0ull;
+            eqseen += __popcll(eqm);
+        }
+    }
+    const Threshold all{1ull, 0};
+    const int c2 = compact_regs(ek, all, a.idx2 + rowid * a.cap2, a.cap2, false);
+    if (lane == 0) { a.cnt[rowid] = c1; a.cnt2[rowid] = c2; }
+}
+
+template <int D, int KPL, int MODE>
+__global__ __launch_bounds__(64 * MWAVES) void route_mfma_kernel(RouteArgs a) {
+    constexpr int KP = D + 4;          // staged row pitch (floats)
+    constexpr int NS = D / 4;          // MFMA steps
+    constexpr int PL = D / 16;         // 16-byte loads per lane per 16-row tile
+    constexpr int SP = MROWS + 1;      // score staging pitch (doubles)
+    // scoring: key tiles kt[MWAVES][MROWS * KP] (fp32) and score tiles
+    // st[2][MWAVES][MROWS * SP] (fp64); selection: row B's keys while row A
+    // is selected, [MWAVES][KPL][64]
+    constexpr int KT_BYTES = MWAVES * MROWS * KP * 4;
+    constexpr int ST_BYTES = 2 * MWAVES * MROWS * SP * 8;
+    constexpr int STASH_BYTES = MWAVES * KPL * 64 * 8;
+    constexpr int LDS_BYTES = KT_BYTES + ST_BYTES > STASH_BYTES ? KT_BYTES + ST_BYTES : STASH_BYTES;
+    __shared__ __attribute__((aligned(16))) char lds[LDS_BYTES];
+    float (*kt)[MROWS * KP] = reinterpret_cast<float (*)[MROWS * KP]>(lds);
+    double (*st)[MWAVES][MROWS * SP] = reinterpret_cast<double (*)[MWAVES][MROWS * SP]>(lds + KT_BYTES);
+
+    const int nb = a.nb;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int row0 = blockIdx.x * MROWS;
+    const size_t bh = static_cast<size_t>(blockIdx.z) * a.H + blockIdx.y;
+    const float* Kb = a.kbar + bh * nb * D;
+    float* my = kt[w];
+    const double sc = static_cast<double>(a.scale);
+
+    // rows r0 .. r0 + 15 of a block-major [nb][D] array, zero past nb
+    auto load16 = [&](const float* src, int r0, f32x4 (&buf)[PL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int x = 64 * u + l, r = x / (D / 4), c4 = x % (D / 4);
+            buf[u] = (r0 + r < nb) ? *reinterpret_cast<const f32x4*>(src + static_cast<size_t>(r0 + r) * D + 4 * c4)
+                                   : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        }
+    };
+    auto put16 = [&](const f32x4 (&buf)[PL]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < PL; ++u) {
+            const int x = 64 * u + l, r = x / (D / 4), c4 = x % (D / 4);
+            *reinterpret_cast<f32x4*>(my + r * KP + 4 * c4) = buf[u];
+        }
+    };
+    // MFMA operand of step s for this lane: row l % 16, dimension 4 s + l / 16
+    const int opo = (l & 15) * KP + (l >> 4);
+
+    // B operands: the 16 query rows
+    float qv[NS];
+    f32x4 pre[PL];
+    load16(a.qbar + bh * nb * D, row0, pre);
+    put16(pre);
+    wave_sync();
+#pragma unroll
+    for (int s = 0; s < NS; ++s) qv[s] = my[opo + 4 * s];
+    wave_sync();
+
+    const int rA = w, rB = w + MWAVES;
+    uint64_t kA[KPL], kB[KPL];
+    load16(Kb, MROWS * w, pre);
+#pragma unroll
+    for (int p = 0; p < KPL / 2; ++p) {
+        kA[2 * p] = kA[2 * p + 1] = kB[2 * p] = kB[2 * p + 1] = 0ull;
+        if (128 * p >= nb) continue;                       // uniform
+        const int j0 = MROWS * (MWAVES * p + w);
+        put16(pre);
+        if (128 * (p + 1) < nb) load16(Kb, j0 + 128, pre);
+        wave_sync();
+        f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+        if (j0 < nb) {
+#pragma unroll
+            for (int s = 0; s < NS; ++s)
+                acc = __builtin_amdgcn_mfma_f64_16x16x4f64(static_cast<double>(my[opo + 4 * s]),
+                                                           static_cast<double>(qv[s]), acc, 0, 0, 0);
+        }
+        // accumulator entry i: key j0 + 4 i + l / 16, query row l % 16
+        double* sp = st[p & 1][w];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sp[(l & 15) * SP + 4 * i + (l >> 4)] = acc[i];
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int c = 64 * u + l, j = 128 * p + c;
+            if (j >= nb) continue;
+            const double* sq = st[p & 1][c >> 4];
+            const double vA = sq[rA * SP + (c & 15)], vB = sq[rB * SP + (c & 15)];
+            uint64_t xA, xB;
+            if constexpr (MODE == 2) {
+                xA = static_cast<uint64_t>(__double_as_longlong(__dmul_rn(sc, vA)));
+                xB = static_cast<uint64_t>(__double_as_longlong(__dmul_rn(sc, vB)));
+            } else if constexpr (MODE == 3) {
+                const double lm = static_cast<double>(a.klam[bh * nb + j]);
+                xA = order_key(__dadd_rn(__dmul_rn(sc, vA), lm));
+                xB = order_key(__dadd_rn(__dmul_rn(sc, vB), lm));
+            } else if constexpr (MODE == 4) {
+                // ln(E / n_j) = 2 scale s + L - ln n_j
+                const double lgn = log(static_cast<double>(a.kcount[j]));
+                const float* el = a.ekey + (bh * nb + j) * static_cast<size_t>(nb);
+                const double LA = row0 + rA < nb ? static_cast<double>(el[row0 + rA]) : 0.0;
+                const double LB = row0 + rB < nb ? static_cast<double>(el[row0 + rB]) : 0.0;
+                xA = order_key(__dadd_rn(__dadd_rn(2.0 * __dmul_rn(sc, vA), LA), -lgn));
+                xB = order_key(__dadd_rn(__dadd_rn(2.0 * __dmul_rn(sc, vB), LB), -lgn));
+            } else {
+                xA = order_key(vA);
+                xB = order_key(vB);
+            }
+            kA[2 * p + u] = xA;
+            kB[2 * p + u] = xB;
+        }
+    }
+    // row B's keys wait in LDS (the tiles are no longer read) while row A is
+    // selected; one copy of the selection code serves both rows
+    __syncthreads();
+    uint64_t* stash = reinterpret_cast<uint64_t*>(lds) + w * KPL * 64 + l;
+#pragma unroll
+    for (int t = 0; t < KPL; ++t) stash[64 * t] = kB[t];
+#pragma unroll 1
+    for (int rr = 0; rr < 2; ++rr) {
+        if (rr == 1) {
+            wave_sync();
+#pragma unroll
+            for (int t = 0; t < KPL; ++t) kA[t] = stash[64 * t];
+        }
+        const int row = row0 + w + MWAVES * rr;
+        if (row < nb) select_row<KPL, MODE>(a, bh, row, kA);
+    }
+}
+
+template <int D, int MODE>
+hipError_t launch_mfma(const RouteArgs& a, hipStream_t s) {
+    dim3 grid((a.nb + MROWS - 1) / MROWS, a.H, a.B);
+    if (a.nb <= 512) hipLaunchKernelGGL((route_mfma_kernel<D, 8, MODE>), grid, dim3(64 * MWAVES), 0, s, a);
+    else if (a.nb <= 1024) hipLaunchKernelGGL((route_mfma_kernel<D, 16, MODE>), grid, dim3(64 * MWAVES), 0, s, a);
+    else hipLaunchKernelGGL((route_mfma_kernel<D, 32, MODE>), grid, dim3(64 * MWAVES), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_mfma_modes(const RouteArgs& a, hipStream_t s) {
+    switch (a.mode) {
+        case 2: return launch_mfma<D, 2>(a, s);
+        case 3: return launch_mfma<D, 3>(a, s);
+        case 4: return launch_mfma<D, 4>(a, s);
+        default: return launch_mfma<D, 0>(a, s);
+    }
+}
+
 template <int R>
 hipError_t launch_scored(const RouteArgs& a, hipStream_t s) {
     const int nbp = (a.nb + 63) & ~63;
@@ -555,6 +833,8 @@ hipError_t launch_route(const RouteArgs& a, hipStream_t s) {
         hipLaunchKernelGGL(route_lvsa_kernel, grid, dim3(64 * LVSA_ROWS), 0, s, a);
         return hipGetLastError();
     }
+    if ((a.d == 64 || a.d == 128) && a.nb <= 2048)
+        return a.d == 128 ? launch_mfma_modes<128>(a, s) : launch_mfma_modes<64>(a, s);
     // rows per workgroup: as many as fit a 64 KiB key budget, at most 16, then
     // halved while the grid has fewer than 1024 workgroups (four per CU), so
     // that the waves' global k_bar loads overlap (Wan-size layer: 16 rows per
