@@ -566,6 +566,45 @@ def test_topk_ties_at_the_cut():
         assert np.array_equal(idx.cpu().numpy()[..., :kk], ri), kk
 
 
+@pytest.mark.parametrize("nb", [19, 300, 1100, 2100])
+def test_route_one_sign_rows(nb):
+    """Query blocks whose scores against every key block are all positive, all
+    negative, or mixed (a third each), for top-k and for Triage's two
+    selections.  All-positive rows have order keys that share the sign bit, so
+    the threshold search's first interval reaches 2^64.  The block counts take
+    the search's gathered-interval path at once (19), after some passes (300,
+    1100), and the long-row kernel past 2048 blocks (2100)."""
+    import free_block_sparse_attn_amd as fbsa
+    rng = np.random.default_rng(11)
+    d = 128
+    N = 64 * nb
+    u = rng.standard_normal(d).astype(np.float32)
+    u /= np.linalg.norm(u)
+    blk = np.arange(N) // 64
+    sign = np.where(blk % 3 == 0, 1.0, np.where(blk % 3 == 1, -1.0, 0.0)).astype(np.float32)
+    k_np = (rng.standard_normal((1, 1, N, d)) * 0.3 + 2.0 * u).astype(np.float32)
+    q_np = (rng.standard_normal((1, 1, N, d)) * 0.3 + (2.0 * sign)[None, None, :, None] * u).astype(np.float32)
+    to = lambda x: torch.from_numpy(x).to(torch.bfloat16).cuda()
+    q, k = to(q_np), to(k_np)
+    pooled = fbsa.sparse_attn_pool(q, k, k, N, spreads=True)
+    f = {x: pooled[x].cpu().numpy() for x in ("qbar", "kbar", "klam", "kcount")}
+    print(f"\n[case] one-sign rows nb={nb}", flush=True)
+    kk = max(2, nb // 5)
+    idx, cnt, _, _ = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TOPK, topk=kk)
+    ri, rc = routing.route_topk(f["qbar"], f["kbar"], kk)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(idx.cpu().numpy()[..., :kk], ri)
+    scale = d ** -0.5
+    n_keep, n_refine = max(1, 2 * nb // 5), 3 * nb // 20
+    idx, cnt, idx2, cnt2 = fbsa.sparse_attn_route(pooled, N, fbsa.SA_ROUTE_TRIAGE, n_keep=n_keep,
+                                                  n_refine=n_refine, scale=scale)
+    ri, rc, si, sc = routing.route_triage(f["qbar"], f["kbar"], f["klam"], f["kcount"], scale, n_keep, n_refine)
+    assert np.array_equal(idx.cpu().numpy()[..., :ri.shape[-1]], ri)
+    assert np.array_equal(cnt.cpu().numpy(), rc)
+    assert np.array_equal(idx2.cpu().numpy(), si)
+    assert np.array_equal(cnt2.cpu().numpy(), sc)
+
+
 def test_topk_all_blocks_matches_dense():
     wl = get_workload(2, small=True)
     (q, k, v), dev, coords = gc.inputs(wl)
