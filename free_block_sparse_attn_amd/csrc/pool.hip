@@ -17,6 +17,9 @@
 
 #include <mutex>
 
+// the device library's wavefront sum (DPP, a fixed order)
+extern "C" __device__ float __ockl_wfred_add_f32(float);
+
 namespace sa {
 
 namespace {
@@ -1072,13 +1075,14 @@ __global__ __launch_bounds__(THREADS) void hbar_reduce_kernel(PoolArgs a) {
 // PISA's covariance-aware routing statistic ("PISA ...", section 2, "Routage
 // Sensible a la Covariance"): M_j = ||H_j - H_bar||_2, written as ln M_j.
 // One workgroup per (block, head): the block's moment is rebuilt in MFMA
-// accumulators (never stored), H_bar subtracted, and the deviation parked in
-// LDS as fp32 value-major Dm[o][i], from which each thread keeps an 8 x 8 tile
-// in registers.  M_j^2 is the largest eigenvalue of A = Dm^T Dm, found by
-// at most COV_STEPS steps of the Lanczos recurrence on A (two tile products per step,
-// partial sums combined across tiles in a fixed order through LDS, so the
-// result is deterministic) and then the largest eigenvalue of the Lanczos
-// tridiagonal by 64-point multisection with Sturm counts.  Lanczos converges
+// accumulators (never stored) and H_bar subtracted, so each wave holds 32
+// columns of the deviation Dm[o][i] in that layout, plus a copy of them by
+// rows (moved through LDS).  M_j^2 is the largest eigenvalue of Dm Dm^T (that
+// of Dm^T Dm), found by at most COV_STEPS steps of the Lanczos recurrence
+// (per step Dm^T q inside each wave, then Dm y from the four waves' partial
+// sums added in a fixed order, so the result is deterministic) and then the
+// largest eigenvalue of the Lanczos tridiagonal by 64-point multisection with
+// Sturm counts.  Lanczos converges
 // with the square root of the relative gap, so blocks whose two top singular
 // values are within a few percent (where plain power iteration stalls) still
 // come out to fp32 accuracy.  The Ritz value never exceeds M_j^2 beyond
@@ -1090,7 +1094,7 @@ __device__ __forceinline__ int sturm_below(const float* al, const float* be, int
     int c = 0;
     float d = 1.0f;
     for (int k = 0; k < n; ++k) {
-        d = al[k] - x - (k > 0 ? be[k - 1] * be[k - 1] / d : 0.0f);
+        d = al[k] - x - (k > 0 ? __fdividef(be[k - 1] * be[k - 1], d) : 0.0f);
         if (fabsf(d) < 1e-30f) d = -1e-30f;
         c += d < 0.0f;
     }
@@ -1128,57 +1132,55 @@ constexpr int COV_CHECK = 8;
 
 __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3))) void cov_norm_kernel(PoolArgs a) {
     constexpr int D = 128;
-    // the block staging, then half of Dm at a time (rows 64 hf .. 64 hf + 63)
+    constexpr int RP = 36;                    // row pitch (floats) of a wave's transposing area
     __shared__ __attribute__((aligned(16))) uint16_t stage[2 * D * TPITCH];
-    constexpr int PP = D + 4;                 // padded partial-sum rows: the 16 column tiles' writes hit distinct banks
-    __shared__ float part[16 * PP];
-    __shared__ float yv_s[D], wv_s[D];
-    __shared__ float red2[2][2];              // per-step wave partials of |y|^2 and |w|^2
     __shared__ float kb_s[D];
-    __shared__ float al[COV_STEPS], be[COV_STEPS];
+    __shared__ __attribute__((aligned(16))) float qv_s[4][D];      // each wave's copy of q
+    __shared__ __attribute__((aligned(16))) float yv_s[4][32];     // each wave's entries of Dm^T q
+    __shared__ float part_s[2][4][D + 1];     // per step: Dm y over each wave's columns, then |y|^2 of them
+    __shared__ float al_s[COV_STEPS], be_s[COV_STEPS];
     __shared__ float ritz_s;
     __shared__ int stop_s;
-    float* dmh = reinterpret_cast<float*>(stage);
-    static_assert(64 * D * sizeof(float) <= sizeof(stage), "half of Dm fits the staging buffer");
+    static_assert(4 * 64 * RP * sizeof(float) <= sizeof(stage), "a 64-row half of Dm fits the staging buffer");
     const int j = blockIdx.x;
     const size_t bh = blockIdx.y;
-    const int tid = threadIdx.x, l = tid & 63, hl = l >> 5;
-    const int icol = 32 * (tid >> 6) + (l & 31);
+    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, hl = l >> 5, l32 = l & 31;
+    const int icol = 32 * w + l32;
     const int nb = a.N_pad / BLK;
     f32x16 acc[4];
 #pragma unroll
     for (int ob = 0; ob < 4; ++ob) acc[ob] = f32x16{};
     add_block_moment(a, bh, j, stage, kb_s, acc);
+    // acc[ob][r] = Dm[o][icol], o = 32 ob + 8 (r / 4) + 4 hl + r % 4: wave w holds columns 32 w .. 32 w + 31
     const float* hb = a.hbar + bh * D * D;
 #pragma unroll
     for (int ob = 0; ob < 4; ++ob)
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[ob][r] -= hb[(32 * ob + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + icol];
-    // thread tile: rows o = 8 tr + u, columns i = 8 tc + v, moved over in two row halves
-    const int tr = tid >> 4, tc = tid & 15;
-    float t[8][8];
+    // second copy of the wave's columns by rows: tr[hf][c] = Dm[l + 64 hf][32 w + c],
+    // moved through the wave's own part of the staging buffer
+    float tr[2][32];
+    float* mine = reinterpret_cast<float*>(stage) + w * 64 * RP;
+    __syncthreads();                          // every wave is done with the block staging
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-        __syncthreads();                      // the staging / previous half is consumed
 #pragma unroll
         for (int ob = 2 * hf; ob < 2 * hf + 2; ++ob)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                dmh[(32 * (ob - 2 * hf) + 8 * (r >> 2) + 4 * hl + (r & 3)) * D + icol] = acc[ob][r];
-        __syncthreads();
-        if ((tr >> 3) == hf) {
+                mine[(32 * (ob - 2 * hf) + 8 * (r >> 2) + 4 * hl + (r & 3)) * RP + l32] = acc[ob][r];
+        wave_lds_fence();
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const float* row = dmh + (8 * (tr & 7) + u) * D + 8 * tc;
-                const f32x4 lo = *reinterpret_cast<const f32x4*>(row);
-                const f32x4 hi = *reinterpret_cast<const f32x4*>(row + 4);
+        for (int c4 = 0; c4 < 8; ++c4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(mine + l * RP + 4 * c4);
 #pragma unroll
-                for (int v = 0; v < 4; ++v) { t[u][v] = lo[v]; t[u][v + 4] = hi[v]; }
-            }
+            for (int e = 0; e < 4; ++e) tr[hf][4 * c4 + e] = v[e];
         }
+        wave_lds_fence();
     }
-    // Lanczos start q_1 = x / |x|, x_i = 1 + frac(0.618034 i); q_0 = 0.  Thread
-    // i < 128 keeps q_i and q_prev_i; the new q reaches every tile through wv_s.
+    // Lanczos on A = Dm Dm^T (the same nonzero eigenvalues as Dm^T Dm), q over
+    // the 128 rows o; start q_o = x_o / |x|, x_o = 1 + frac(0.618034 o).  Lane
+    // l keeps q_o and q_prev_o for o = l and l + 64.
     float n0 = 0.0f;
     for (int i = 0; i < D; ++i) {
         const float fi = static_cast<float>(i) * 0.618034f;
@@ -1186,77 +1188,78 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
         n0 += xi * xi;
     }
     const float inv0 = rsqrtf(n0);
-    float qi = 0.0f, qpi = 0.0f;
-    if (tid < D) {
-        const float fi = static_cast<float>(tid) * 0.618034f;
-        qi = (1.0f + (fi - floorf(fi))) * inv0;
+    float q0, q1, qp0 = 0.0f, qp1 = 0.0f;
+    {
+        const float f0 = static_cast<float>(l) * 0.618034f, f1 = static_cast<float>(l + 64) * 0.618034f;
+        q0 = (1.0f + (f0 - floorf(f0))) * inv0;
+        q1 = (1.0f + (f1 - floorf(f1))) * inv0;
     }
-    float x[8];
-#pragma unroll
-    for (int v = 0; v < 8; ++v) {
-        const float fi = static_cast<float>(8 * tc + v) * 0.618034f;
-        x[v] = (1.0f + (fi - floorf(fi))) * inv0;
-    }
+    float* qs = qv_s[w];
+    qs[l] = q0;
+    qs[l + 64] = q1;
+    wave_lds_fence();
     int steps = 0;
     float beta = 0.0f;
-    // Four barriers per step (column sums, y to every tile, row sums, w to
-    // every tile); the squared norms ride on the second and fourth as wave
-    // partials.
+    // One barrier per step: y = Dm^T q stays inside each wave (its own
+    // columns); the wave partials of Dm y and |y|^2 are exchanged through LDS
+    // and every wave adds them in the same order, so all waves hold the same
+    // alpha, beta and q and take the same exits.  Every COV_CHECK steps wave 0
+    // alone finds the top Ritz value and shares the stop decision.
     for (int k = 0; k < COV_STEPS; ++k) {
-        // y = Dm q: partial sums over this tile's columns, summed over the 16 column tiles
+        float pp[4];                          // one chain per 32-row group
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            float p = 0.0f;
+        for (int ob = 0; ob < 4; ++ob) {
+            pp[ob] = 0.0f;
 #pragma unroll
-            for (int v = 0; v < 8; ++v) p = fmaf(t[u][v], x[v], p);
-            part[tc * PP + 8 * tr + u] = p;
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const f32x4 qv = *reinterpret_cast<const f32x4*>(qs + 32 * ob + 8 * r4 + 4 * hl);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) pp[ob] = fmaf(acc[ob][4 * r4 + e], qv[e], pp[ob]);
+            }
         }
-        __syncthreads();
-        float y = 0.0f;
-        if (tid < D) {
-#pragma unroll
-            for (int c = 0; c < 16; ++c) y += part[c * PP + tid];
-            yv_s[tid] = y;
-            float y2 = y * y;                 // alpha = q^T A q = |Dm q|^2: wave partials
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) y2 += __shfl_xor(y2, off);
-            if ((tid & 63) == 0) red2[0][tid >> 6] = y2;
+        const float p = (pp[0] + pp[1]) + (pp[2] + pp[3]);
+        float po;                                    // the column's other 64 rows (lane l ^ 32)
+        {
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+            po = __uint_as_float(hl ? static_cast<uint32_t>(sw[0]) : static_cast<uint32_t>(sw[1]));
         }
-        __syncthreads();
-        const float alpha = red2[0][0] + red2[0][1];
-        // w = Dm^T y - alpha q - beta q_prev: partial sums over this tile's rows
-        float yy[8];
+        const float y = hl ? po + p : p + po;
+        if (hl == 0) yv_s[w][l32] = y;
+        const float y2 = __ockl_wfred_add_f32(hl == 0 ? y * y : 0.0f);
+        wave_lds_fence();
+        float wa[2][2] = {{0.0f, 0.0f}, {0.0f, 0.0f}};   // two chains per row
 #pragma unroll
-        for (int u = 0; u < 8; ++u) yy[u] = yv_s[8 * tr + u];
+        for (int c4 = 0; c4 < 8; ++c4) {
+            const f32x4 yy = *reinterpret_cast<const f32x4*>(yv_s[w] + 4 * c4);
 #pragma unroll
-        for (int v = 0; v < 8; ++v) {
-            float p = 0.0f;
-#pragma unroll
-            for (int u = 0; u < 8; ++u) p = fmaf(t[u][v], yy[u], p);
-            part[tr * PP + 8 * tc + v] = p;
+            for (int e = 0; e < 4; ++e) {
+                wa[0][c4 & 1] = fmaf(tr[0][4 * c4 + e], yy[e], wa[0][c4 & 1]);
+                wa[1][c4 & 1] = fmaf(tr[1][4 * c4 + e], yy[e], wa[1][c4 & 1]);
+            }
         }
+        float* pt = part_s[k & 1][w];
+        pt[l] = wa[0][0] + wa[0][1];
+        pt[l + 64] = wa[1][0] + wa[1][1];
+        if (l == 0) pt[D] = y2;
         __syncthreads();
-        float w = 0.0f;
-        if (tid < D) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) w += part[r * PP + tid];
-            w = w - alpha * qi - beta * qpi;
-            wv_s[tid] = w;
-            float w2 = w * w;
-#pragma unroll
-            for (int off = 32; off >= 1; off >>= 1) w2 += __shfl_xor(w2, off);
-            if ((tid & 63) == 0) red2[1][tid >> 6] = w2;
+        const float (*ps)[D + 1] = part_s[k & 1];
+        const float alpha = ((ps[0][D] + ps[1][D]) + ps[2][D]) + ps[3][D];   // q^T A q = |Dm^T q|^2
+        float s0 = ((ps[0][l] + ps[1][l]) + ps[2][l]) + ps[3][l];
+        float s1 = ((ps[0][l + 64] + ps[1][l + 64]) + ps[2][l + 64]) + ps[3][l + 64];
+        s0 = s0 - alpha * q0 - beta * qp0;
+        s1 = s1 - alpha * q1 - beta * qp1;
+        beta = sqrtf(__ockl_wfred_add_f32(s0 * s0 + s1 * s1));
+        if (tid == 0) {
+            al_s[k] = alpha;
+            be_s[k] = beta;
         }
-        __syncthreads();
-        beta = sqrtf(red2[1][0] + red2[1][1]);
-        if (tid == 0) { al[k] = alpha; be[k] = beta; }
         steps = k + 1;
         if (!(beta > alpha * 0x1p-20f)) break;    // invariant subspace (or A = 0): T is exact
         if (steps % COV_CHECK == 0 && steps < COV_STEPS) {
-            // converged?  (al / be of this step were written by lane 0 of wave 0)
-            if (tid < 64) {
-                const float r = top_ritz(al, be, steps, l);
-                if (tid == 0) {
+            if (w == 0) {
+                wave_lds_fence();                 // al / be of this step
+                const float r = top_ritz(al_s, be_s, steps, l);
+                if (l == 0) {
                     stop_s = steps > COV_CHECK && r - ritz_s <= r * 0x1p-15f;
                     ritz_s = r;
                 }
@@ -1265,16 +1268,19 @@ __global__ __launch_bounds__(THREADS) __attribute__((amdgpu_waves_per_eu(3, 3)))
             if (stop_s) break;
         }
         const float ib = 1.0f / beta;
-        qpi = qi;
-        qi = w * ib;
-#pragma unroll
-        for (int v = 0; v < 8; ++v) x[v] = wv_s[8 * tc + v] * ib;
+        qp0 = q0;
+        qp1 = q1;
+        q0 = s0 * ib;
+        q1 = s1 * ib;
+        qs[l] = q0;
+        qs[l + 64] = q1;
+        wave_lds_fence();
     }
-    __syncthreads();
-    if (tid < 64) {
-        const float hi = top_ritz(al, be, steps, l);
-        if (tid == 0) {
-            const bool zero = al[0] == 0.0f && steps == 1;
+    if (w == 0) {
+        wave_lds_fence();
+        const float hi = top_ritz(al_s, be_s, steps, l);
+        if (l == 0) {
+            const bool zero = al_s[0] == 0.0f && steps == 1;
             a.kcov[bh * nb + j] = zero ? -INFINITY : 0.5f * logf(hi);
         }
     }
