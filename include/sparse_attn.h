@@ -144,7 +144,8 @@ typedef struct {
  *                        covariance-aware top-k (section 2, "Routage Sensible
  *                        a la Covariance").  H_j is rebuilt in fp32 (never
  *                        stored); M_j^2 is the largest eigenvalue of
- *                        A = (H_j - H_bar)^T (H_j - H_bar), taken from up to
+ *                        A = (H_j - H_bar) (H_j - H_bar)^T (that of the
+ *                        product in the other order), taken from up to
  *                        32 Lanczos steps on A (fixed start vector, partial
  *                        sums combined in a fixed order, so deterministic;
  *                        the steps stop once the top Ritz value moved by at
