@@ -50,7 +50,7 @@ FP64_PEAK_TFLOPS = 78.6
 # the forward kernel's source and the headers it includes: counters taken on
 # other sources are stale
 FWD_SOURCES = [os.path.join(ROOT, "free_block_sparse_attn_amd", "csrc", f)
-               for f in ("fwd_bf16.hip", "lds_tile.h", "common.h", "launch.h")]
+               for f in ("fwd_bf16.hip", "fwd_bf16_skim.hip", "lds_tile.h", "common.h", "launch.h")]
 HEADLINE = "triage-e4m3"
 
 LAYERS = {

@@ -13,7 +13,10 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libsparse_attn.so")
-SOURCES = ["api.cpp", "pool.hip", "route.hip", "fwd_f32.hip", "fwd_bf16.hip", "residual.hip"]
+SOURCES = ["api.cpp", "pool.hip", "route.hip", "fwd_f32.hip", "fwd_bf16.hip", "fwd_bf16_skim.hip", "residual.hip"]
+# per-source flags: the skim forms keep their MFMAs beside the softmax work
+# only without machine sinking
+SOURCE_FLAGS = {"fwd_bf16_skim.hip": ["-mllvm", "-disable-machine-sink"]}
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -32,7 +35,8 @@ def build(verbose: bool = False, lib_path: str = LIB, defines=(), extra_flags=()
     for src in SOURCES:
         obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [HIPCC] + FLAGS + list(extra_flags) + [f"-D{x}" for x in defines] + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = ([HIPCC] + FLAGS + SOURCE_FLAGS.get(src, []) + list(extra_flags) + [f"-D{x}" for x in defines] + lang
+               + ["-c", os.path.join(CSRC, src), "-o", obj])
         procs.append((src, cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
         objs.append(obj)
     for src, cmd, p in procs:

@@ -485,154 +485,229 @@ __device__ __forceinline__ void skim_tiles(const FwdArgs& a, State& st, size_t b
         }
     }
     const int sq = static_cast<int>(EX[qa * 3 + 0]) + 127;
-    auto load_tile = [&](int j, i32x8 ka[2][2], i32x8 va[4], int ksc[2][2], int vsc[4]) __attribute__((always_inline)) {
-        const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * QB;
-        const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * QB;
-        if constexpr (F4) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    const u32x4 w = *reinterpret_cast<const u32x4*>(Kj + (32 * kb + l32) * QB + 32 * ks + 16 * h);
-                    ka[kb][ks] = i32x8{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
-                                       static_cast<int>(w[3]), 0, 0, 0, 0};
-                    ksc[kb][ks] = KS[(static_cast<size_t>(j) * BLK + 32 * kb + l32) * (D / 32) + 2 * ks + h];
-                }
-            // An fp4 operand lane of half h holds reduction indices
-            // 32 (p / 16) + 16 h + p % 16 for its nibbles p (the fp8 P operand:
-            // 32 h + p), so V^T takes positions 16h .. 16h+15 and 32+16h .. 32+16h+15.
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                const uint8_t* vr = Vj + (32 * db + l32) * (BLK / 2);
-                const uint2 w0 = *reinterpret_cast<const uint2*>(vr + 8 * h);
-                const uint2 w1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * h);
-                va[db] = i32x8{static_cast<int>(w0.x), static_cast<int>(w0.y), static_cast<int>(w1.x),
-                               static_cast<int>(w1.y), 0, 0, 0, 0};
-                vsc[db] = VS[static_cast<size_t>(j) * D + 32 * db + l32];
-            }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int ks = 0; ks < 2; ++ks) {
-                    ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
-                    ksc[kb][ks] = 0;
-                }
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-                va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
-                vsc[db] = 0;
-            }
-        }
+    // K~ of tile j into a K slot, V~ into a V slot (the exponent bytes are
+    // vector loads issued before the operands, so that waiting for them leaves
+    // the operand loads in flight).  Slots past the end of the list repeat its
+    // last tile (never used), so the load sequence is straight-line.
+    struct KSlot {
+        i32x8 ka[2][2];
+        int ksc[2][2];
+        int nj, sk;          // valid keys of the tile (0: a null tile past the end of the list)
     };
-    // One skim tile: S^T = K Q^T on the scaled MFMA, quantised weights, O^T += V^T P^T.
-    auto tile = [&](int j, int sk, int sv, const i32x8 ka[2][2], const i32x8 va[4], const int ksc[2][2],
-                    const int vsc[4]) __attribute__((always_inline)) {
-        const int nj = min(BLK, a.N - BLK * j);
-        f32x16 s[2][2];
+    struct VSlot {
+        i32x8 va[4];
+        int vsc[4];
+        int sv;
+    };
+    auto load_k = [&](KSlot& sl, int e) __attribute__((always_inline)) {
+        const int j = LM[min(e, cntM - 1)];
+        sl.nj = e < cntM ? min(BLK, a.N - BLK * j) : 0;
+        sl.sk = static_cast<int>(EX[j * 3 + 1]) + 127;
+        const uint8_t* Kj = K8 + static_cast<size_t>(j) * BLK * QB;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-            for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int rb = 0; rb < 2; ++rb) {
-                    if constexpr (F4)
-                        s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            ka[kb][ks], qb8[rb][ks], s[kb][rb], 4, 4, 0, ksc[kb][ks], 0, qsc[rb][ks]);
-                    else
-                        s[kb][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            ka[kb][ks], qb8[rb][ks], s[kb][rb], 0, 0, 0, sk, 0, sq);
+            for (int ks = 0; ks < 2; ++ks) {
+                if constexpr (F4) {
+                    const u32x4 w = *reinterpret_cast<const u32x4*>(Kj + (32 * kb + l32) * QB + 32 * ks + 16 * h);
+                    sl.ka[kb][ks] = i32x8{static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]),
+                                          static_cast<int>(w[3]), 0, 0, 0, 0};
+                    sl.ksc[kb][ks] = KS[(static_cast<size_t>(j) * BLK + 32 * kb + l32) * (D / 32) + 2 * ks + h];
+                } else {
+                    sl.ka[kb][ks] = *reinterpret_cast<const i32x8*>(Kj + (32 * kb + l32) * D + 64 * ks + 32 * h);
+                    sl.ksc[kb][ks] = 0;
                 }
-        // raw logits; pad keys of the ragged tail block -inf (c2 > 0 commutes with max)
-        if (nj < BLK) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) mask_half(s[kb], 32 * kb, nj);
-        }
-        i32x8 pb[2];
-        int sb[2];
-        float mx[2];
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            float m0 = s[0][rb][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, s[kb][rb][r]);
-            mx[rb] = pair_max(m0) * c2;
-            rescale_lazy(st, rb, mx[rb]);
-        }
-#pragma unroll
-        for (int rb = 0; rb < 2; ++rb) {
-            // y = 2^{8 + L - c} is the pre-quantisation code value; the
-            // unquantised weight 2^{L - m} = y 2^{c - 8 - m}, so the denominator
-            // takes 2^{c - 8 - m} times the sum of the y.
-            const float mref = st.m[rb];
-            const float ct = (mx[rb] == -INFINITY) ? mref : ceilf(mx[rb]);
-            const float off = 8.0f - ct;
-            float ysum = 0.f;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    float y[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        y[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][rb][4 * w + u], c2, off));
-                        ysum += y[u];
-                    }
-                    const uint32_t lo = pack_fp8x2<false>(y[0], y[1], 0u);
-                    pb[rb][4 * kb + w] = static_cast<int>(pack_fp8x2<true>(y[2], y[3], lo));
-                }
-            st.l[rb] = fmaf(ysum, ldexpf(1.0f, static_cast<int>(ct - mref) - 8), st.l[rb]);
-            sb[rb] = min(max(static_cast<int>(ct - mref) - 8 + 127, 0), 254);
-        }
-#pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-            for (int rb = 0; rb < 2; ++rb) {
-                if constexpr (F4)
-                    st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        va[db], pb[rb], st.o[db][rb], 4, 0, 0, vsc[db], 0, sb[rb]);
-                else
-                    st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        va[db], pb[rb], st.o[db][rb], 0, 0, 0, sv, 0, sb[rb]);
             }
     };
-    // Three register slots: each tile's loads are issued two tiles ahead of
-    // its use (one ahead left the loads' latency exposed).  Loads past the end
-    // of the list repeat the last tile (never used), so the load sequence is
-    // straight-line and its waits stay counted.
-    struct Slot {
-        i32x8 ka[2][2], va[4];
-        int ksc[2][2], vsc[4];
-        int j, sk, sv;
+    auto load_v = [&](VSlot& sl, int e) __attribute__((always_inline)) {
+        const int j = LM[min(e, cntM - 1)];
+        sl.sv = static_cast<int>(EX[j * 3 + 2]) + 127;
+        const uint8_t* Vj = V8 + static_cast<size_t>(j) * BLK * QB;
+        // An fp4 operand lane of half h holds reduction indices
+        // 32 (p / 16) + 16 h + p % 16 for its nibbles p (the fp8 P operand:
+        // 32 h + p), so V^T takes positions 16h .. 16h+15 and 32+16h .. 32+16h+15.
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+            if constexpr (F4) {
+                const uint8_t* vr = Vj + (32 * db + l32) * (BLK / 2);
+                const uint2 w0 = *reinterpret_cast<const uint2*>(vr + 8 * h);
+                const uint2 w1 = *reinterpret_cast<const uint2*>(vr + 16 + 8 * h);
+                sl.va[db] = i32x8{static_cast<int>(w0.x), static_cast<int>(w0.y), static_cast<int>(w1.x),
+                                  static_cast<int>(w1.y), 0, 0, 0, 0};
+                sl.vsc[db] = VS[static_cast<size_t>(j) * D + 32 * db + l32];
+            } else {
+                sl.va[db] = *reinterpret_cast<const i32x8*>(Vj + (32 * db + l32) * BLK + 32 * h);
+                sl.vsc[db] = 0;
+            }
+        }
     };
-    // (the exponent bytes are vector loads: issued before the tile's own loads,
-    // so that waiting for them leaves the tile loads in flight)
-    auto fill = [&](Slot& sl, int e) __attribute__((always_inline)) {
-        sl.j = LM[min(e, cntM - 1)];
-        sl.sk = static_cast<int>(EX[sl.j * 3 + 1]) + 127;
-        sl.sv = static_cast<int>(EX[sl.j * 3 + 2]) + 127;
-        load_tile(sl.j, sl.ka, sl.va, sl.ksc, sl.vsc);
+    // One of the 4 scaled MFMAs of S^T for row block rb against a tile's K~
+    // (i = 2 ks + kb: reduction half ks of key half kb); bs = the Q~ (B)
+    // operand's scale.
+    auto qk1 = [&](int rb, const KSlot& K, f32x16 s[2], int i, int bs) __attribute__((always_inline)) {
+        const int ks = i >> 1, kb = i & 1;
+        const f32x16 acc = ks ? s[kb] : f32x16{};
+        if constexpr (F4)
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                K.ka[kb][ks], qb8[rb][ks], acc, 4, 4, 0, K.ksc[kb][ks], 0, bs);
+        else
+            s[kb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                K.ka[kb][ks], qb8[rb][ks], acc, 0, 0, 0, K.sk, 0, bs);
     };
-    auto run = [&](const Slot& sl) __attribute__((always_inline)) {
-        tile(sl.j, sl.sk, sl.sv, sl.ka, sl.va, sl.ksc, sl.vsc);
+    auto qscale = [&](int rb, int i) __attribute__((always_inline)) -> int {
+        if constexpr (F4) return qsc[rb][i >> 1];
+        return sq;
     };
-    Slot s0, s1, s2;
-    fill(s0, 0);
-    fill(s1, 1);
-    for (int e = 0; e < cntM; e += 3) {
-        fill(s2, e + 2);
-        run(s0);
-        fill(s0, e + 3);
-        if (e + 1 < cntM) run(s1);
-        fill(s1, e + 4);
-        if (e + 2 < cntM) run(s2);
+    // Row block rb's raw logits of a tile with nj valid keys: pad keys of the
+    // ragged tail block -inf (c2 > 0 commutes with max), the row max
+    // (scaled), and the lazy reference update.  A null tile (nj = 0) has no
+    // logits: max -inf, no update, zero weights.
+    auto settle = [&](int rb, f32x16 s[2], int nj) __attribute__((always_inline)) -> float {
+        if (nj < BLK) {
+            // key 32 kb + 8 (r / 4) + 4 h + r % 4 against one per-lane bound,
+            // so the key offsets stay immediates
+            const int lim = nj - 4 * h;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + (r & 3) >= lim) s[kb][r] = -INFINITY;
+        }
+        float m0 = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) m0 = fmaxf(m0, s[kb][r]);
+        const float mx = pair_max(m0) * c2;
+        rescale_lazy(st, rb, mx);
+        return mx;
+    };
+    // Quantised weights of row block rb: y = 2^{8 + L - c} is the
+    // pre-quantisation code value; the unquantised weight 2^{L - m} =
+    // y 2^{c - 8 - m}, so the denominator takes 2^{c - 8 - m} times the sum
+    // of the y, and the P operand's E8M0 scale is 2^{c - 8 - m}.  In eight
+    // chunks of 4 logits (i = 4 kb + w), one beside each MFMA of a block.
+    struct Wts {
+        float mref, ct, off, ysum;
+    };
+    auto w_begin = [&](int rb, float mx) __attribute__((always_inline)) -> Wts {
+        Wts w;
+        w.mref = st.m[rb];
+        w.ct = (mx == -INFINITY) ? w.mref : ceilf(mx);
+        w.off = 8.0f - w.ct;
+        w.ysum = 0.f;
+        return w;
+    };
+    auto w_chunk = [&](Wts& w, float off, const f32x16 s[2], i32x8& pb, int i) __attribute__((always_inline)) {
+        const int kb = i >> 2, q = i & 3;
+        float y[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            y[u] = __builtin_amdgcn_exp2f(fmaf(s[kb][4 * q + u], c2, off));
+            w.ysum += y[u];
+        }
+        const uint32_t lo = pack_fp8x2<false>(y[0], y[1], 0u);
+        pb[i] = static_cast<int>(pack_fp8x2<true>(y[2], y[3], lo));
+    };
+    auto w_end = [&](int rb, const Wts& w, int& sb) __attribute__((always_inline)) {
+        st.l[rb] = fmaf(w.ysum, ldexpf(1.0f, static_cast<int>(w.ct - w.mref) - 8), st.l[rb]);
+        sb = min(max(static_cast<int>(w.ct - w.mref) - 8 + 127, 0), 254);
+    };
+    // One of the 4 scaled MFMAs of O^T += V~^T P~^T for row block rb (d block
+    // db); sb = the P~ (B) operand's scale.
+    auto pv1 = [&](int rb, const VSlot& V, const i32x8& pb, int sb, int db) __attribute__((always_inline)) {
+        if constexpr (F4)
+            st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                V.va[db], pb, st.o[db][rb], 4, 0, 0, V.vsc[db], 0, sb);
+        else
+            st.o[db][rb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                V.va[db], pb, st.o[db][rb], 0, 0, 0, V.sv, 0, sb);
+    };
+    // Software pipeline over the two 32-row blocks of the query block, so
+    // that every block of MFMAs has the softmax VALU work of the other row
+    // block beside it (one wave issues both; the weights of a row block
+    // depend only on its own logits, the MFMAs only on earlier weights).
+    // Tile t, with s0 = rows 0-31's logits of t (issued one block earlier):
+    //   block A:  S(rows 32-63, t)    PV(rows 32-63, t - 1) | weights(rows 0-31, t)
+    //   block B:  S(rows 0-31, t + 1) PV(rows 0-31, t)      | weights(rows 32-63, t)
+    // and the reference update of a row block (a rare uniform branch) sits
+    // between the blocks.  Each row block's operations run in the same order
+    // as tile by tile.  K~ of tile t is last read in block A of t, V~ of t in
+    // block A of t + 1; after block A of t, K slot t % 2 takes tile t + 2 and
+    // V slot (t + 1) % 2 tile t + 1, both first read in block B of t + 1 (two
+    // slots each: a third V or K slot pushes the e4m3 form past 512
+    // registers).  The list is padded to an even length with a null tile
+    // (all keys masked: no update, zero weights, o + 0), and the tile after
+    // the last is null too, so every step runs the same straight-line code
+    // and the slots' roles stay static.
+    KSlot K0, K1;
+    VSlot V0, V1;
+    f32x16 s0[2], s1[2];
+    i32x8 pb0, pb1;
+    int sb0 = 0, sb1 = 0;
+    float mx0 = 0.f, mx1 = 0.f;
+    const int T = cntM + (cntM & 1);
+    load_k(K0, 0);
+    load_v(V0, 0);
+    load_k(K1, 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) qk1(0, K0, s0, i, qscale(0, i));
+    __builtin_amdgcn_sched_barrier(0);
+    mx0 = settle(0, s0, K0.nj);
+    // One block: the S MFMAs of row block rs against tile K (and, with PV,
+    // the PV MFMAs of row block rp from slot V with weights pbp), each
+    // followed by an eighth of row block rw's weights.  The MFMAs take their
+    // operands from registers, so nothing orders them against the weights:
+    // empty volatile asm statements (kept in program order) pass each MFMA's
+    // B scale and each chunk's exponent offset through, and take the previous
+    // chunk's results, so MFMA i and chunk i sit between statements i and
+    // i + 1 (and the weights cannot be sunk past the branch that follows).
+    auto block = [&](auto with_pv, int rs, const KSlot& K, f32x16 ss[2], int rp, const VSlot& V,
+                     const i32x8& pbp, int sbp, int rw, const f32x16 sw[2], float mxw, i32x8& pbw,
+                     int& sbw) __attribute__((always_inline)) {
+        constexpr bool PV = decltype(with_pv)::value;
+        Wts w = w_begin(rw, mxw);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            int bs = i < 4 ? qscale(rs, i) : sbp;
+            float off = w.off;
+            if (i == 0)
+                asm volatile("" : "+v"(bs), "+v"(off));
+            else
+                asm volatile("" : "+v"(bs), "+v"(off) : "v"(pbw[i - 1]), "v"(w.ysum));
+            if (i < 4)
+                qk1(rs, K, ss, i, bs);
+            else if constexpr (PV)
+                pv1(rp, V, pbp, bs, i - 4);
+            w_chunk(w, off, sw, pbw, i);
+        }
+        asm volatile("" ::"v"(pbw[7]), "v"(w.ysum));
+        w_end(rw, w, sbw);
+    };
+    // FIRST: no PV of a previous tile in block A.
+    auto step = [&](auto first, int t, KSlot& Kt, KSlot& Kn, VSlot& Vp, VSlot& Vt) __attribute__((always_inline)) {
+        constexpr bool FIRST = decltype(first)::value;
+        const int njt = Kt.nj;
+        // block A: S(rows 32-63, t), PV(rows 32-63, t - 1) | weights(rows 0-31, t)
+        block(std::integral_constant<bool, !FIRST>{}, 1, Kt, s1, 1, Vp, pb1, sb1, 0, s0, mx0, pb0, sb0);
+        load_k(Kt, t + 2);
+        load_v(Vp, t + 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx1 = settle(1, s1, njt);
+        // block B: S(rows 0-31, t + 1), PV(rows 0-31, t) | weights(rows 32-63, t)
+        block(std::true_type{}, 0, Kn, s0, 0, Vt, pb0, sb0, 1, s1, mx1, pb1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mx0 = settle(0, s0, Kn.nj);
+    };
+    step(std::true_type{}, 0, K0, K1, V1, V0);
+    step(std::false_type{}, 1, K1, K0, V0, V1);
+    for (int t = 2; t < T; t += 2) {
+        step(std::false_type{}, t, K0, K1, V1, V0);
+        step(std::false_type{}, t + 1, K1, K0, V0, V1);
     }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) pv1(1, V1, pb1, sb1, db);
 }
 
 // Query blocks (one wave each) per workgroup: the block first-order form
@@ -1158,10 +1233,23 @@ hipError_t launch_c(const FwdArgs& a, hipStream_t s) {
 
 }  // namespace
 
+// The forms with a skim tier are compiled in fwd_bf16_skim.hip, which
+// includes this file with SA_FWD_SKIM_TU defined and is built without
+// machine sinking: the skim pipeline's MFMAs take all their operands from
+// registers, and the sinking pass would otherwise move them out of the
+// blocks whose softmax work they are meant to run beside.
+hipError_t launch_fwd_bf16_skim(const FwdArgs& a, hipStream_t s);
+
+#ifdef SA_FWD_SKIM_TU
+hipError_t launch_fwd_bf16_skim(const FwdArgs& a, hipStream_t s) {
+    return a.skim_fmt == 1 ? launch_c<2>(a, s) : launch_c<1>(a, s);
+}
+#else
 hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t s) {
     const bool skim = a.idx2 != nullptr && a.cap2 > 0;
     if (!skim) return launch_c<0>(a, s);
-    return a.skim_fmt == 1 ? launch_c<2>(a, s) : launch_c<1>(a, s);
+    return launch_fwd_bf16_skim(a, s);
 }
+#endif
 
 }  // namespace sa
