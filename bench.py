@@ -276,9 +276,9 @@ def cpu_baseline(wl, q, k, v):
     """fp64 numpy oracle on a bounded sample of the Triage layer, scaled to the layer.
 
     Sample: pool (means, counts, spreads) of every head; the fp8 copies of
-    SAMPLE_HEADS heads; Triage routing and the compensated rule (exact,
-    skim and centroid terms) for SAMPLE_ROWS query blocks spread over those
-    heads.  Whole-layer time = pool of every head + fp8 copies per head x H +
+    SAMPLE_HEADS heads spread over the layer (every other head); Triage
+    routing and the compensated rule (exact, skim and centroid terms) for one
+    query block per sampled head, the blocks spread along the sequence.  Whole-layer time = pool of every head + fp8 copies per head x H +
     route and rule per query block x B*H*nb; value = the layer's kept flop /
     that time.
     """
@@ -289,7 +289,7 @@ def cpu_baseline(wl, q, k, v):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:
         cores = os.cpu_count()
-    SAMPLE_HEADS, SAMPLE_ROWS = 2, 8
+    SAMPLE_HEADS = max(1, wl.H // 2)
     t0 = time.perf_counter()
     po = pooling.pool(q, k, v, wl.N, spreads=True)
     t_pool = time.perf_counter() - t0
@@ -303,8 +303,7 @@ def cpu_baseline(wl, q, k, v):
             c[name + "8"], c[name + "exp"] = codes[0, 0], e[0, 0]
         fp8[h] = c
     t_fp8 = (time.perf_counter() - t0) / len(heads)
-    rows = [(h, int(a)) for i, h in enumerate(heads)
-            for a in np.linspace(0, wl.nb - 1, SAMPLE_ROWS // len(heads) + 2)[1:-1].astype(int)]
+    rows = [(h, int((i + 0.5) * wl.nb / len(heads))) for i, h in enumerate(heads)]
     kept = 0
     t0 = time.perf_counter()
     for h, a in rows:
