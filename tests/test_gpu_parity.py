@@ -359,6 +359,45 @@ def test_skim_far_above_reference():
     print(f"[ok] max|err|={worst:.3e}", flush=True)
 
 
+def _skim_length_lists(edit_len):
+    """List edit: query block a keeps only edit_len(a) of its skim blocks,
+    the lowest ones for even a and the highest (which hold the ragged last
+    block when it is skimmed) for odd a; the dropped blocks are compensated."""
+    def edit(idx, cnt, idx2, cnt2):
+        idx2, cnt2 = (t.cpu().numpy().copy() for t in (idx2, cnt2))
+        B, H, nq = cnt2.shape
+        for b in range(B):
+            for h in range(H):
+                for a in range(nq):
+                    sk = sorted(int(x) for x in idx2[b, h, a, :cnt2[b, h, a]])
+                    n = min(edit_len(a), len(sk))
+                    sk = sk[:n] if a % 2 == 0 else sk[len(sk) - n:]
+                    idx2[b, h, a, :] = 0
+                    idx2[b, h, a, :n] = sk
+                    cnt2[b, h, a] = n
+        return idx, cnt, torch.from_numpy(idx2).cuda(), torch.from_numpy(cnt2).cuda()
+    return edit
+
+
+@pytest.mark.parametrize("kind", ["triage", "mxfp4"])
+def test_skim_list_lengths(kind):
+    """Skim lists of every length from 0 to 5 (the skim loop pads odd lengths
+    with a masked null tile and runs its row-block pipeline two tiles deep),
+    with and without the ragged last block."""
+    from dataclasses import replace
+    wl = replace(_batch2_workload(kind), B=1)
+    (q, k, v), dev, coords = gc.inputs(wl)
+    print(f"\n[case] {wl.name} skim lists of length a % 6 N={wl.N} H={wl.H} nb={wl.nb}", flush=True)
+    pooled_o = gc.oracle_pool(wl, q, k, v)
+    res = gc.run_gpu(wl, dev, coords, edit=_skim_length_lists(lambda a: a % 6))
+    assert sorted(set(int(c) for c in res["cnt2"].ravel())) == list(range(6))
+    assert any(wl.nb - 1 in gc.lists_of(res["idx2"], res["cnt2"], 0, h, a)
+               for h in range(wl.H) for a in range(1, wl.nb, 2))
+    ref = gc.oracle_rows(wl, q, k, v, pooled_o, res, all_rows(wl))
+    worst = check_out(wl, res, ref, all_rows(wl))
+    print(f"[ok] max|err|={worst:.3e}", flush=True)
+
+
 def _batch2_workload(kind):
     from dataclasses import replace
     from workloads import configs as C
